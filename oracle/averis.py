@@ -1,0 +1,237 @@
+"""The Averis split-quant and quantized GEMMs, step by step (oracle side).
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
+
+All inputs are float32 numpy arrays (a bf16 tensor is widened exactly to
+float32 before it reaches the oracle).  Every FP32 intermediate that decides a
+code or a scale byte is rounded exactly as written below (numpy float32
+arithmetic is IEEE round-to-nearest-even, one rounding per operation).
+
+Readings of the pages taken here (the pages give the equations, not the
+arithmetic):
+
+* mean ([Lighthouse] §2.1): mu_j = (1/l) sum_i a_ij over the l rows (tokens)
+  of the GEMM's left operand.  Computed as float32(RN64(S_j) / l), where
+  RN64(S_j) is the exact column sum correctly rounded to float64 (math.fsum)
+  and the division is one float64 operation.
+* residual ([Lighthouse] §2.2 and [Gist] §2): r_ij = float32(a_ij - mu_j),
+  using the unquantized mean; it is quantized on its own.
+* Q4 ([Lighthouse] §1.1 and §3.1; [NVFP4-outliers]): blocks of 16 along the
+  GEMM contraction axis; a float32 tensor scale and an E4M3 scale per block:
+    amax   = max |T| over the tensor
+    S_enc  = float32(2688 / amax)  (2688 = 6 * 448), or 1 if amax == 0 or the
+             quotient is not finite;  S_dec = float32(1 / S_enc)
+    s_b    = float32(float32(amax_b / 6) * S_enc), capped at 448
+    c_b    = E4M3(s_b) (RNE), d_b its value
+    e_b    = float32(S_enc / d_b) if d_b > 0 else 0
+    v_k    = float32(T_k * e_b) -> E2M1 code by RN or SR
+  and the dequantized value is E2M1(code) * d_b * S_dec (exact in float64).
+* SR draws come from oracle.philox keyed by (seed, stream, row * cols + col);
+  streams: 0 residual / vanilla activations, 1 mean, 2 weights.
+* GEMMs ([Lighthouse] §2.2): Y = 1 (deq(mean_q) deq(B)^T) + deq(X_R,q) deq(B)^T
+  with B = W^T quantized along m (forward), and the same with D and B = W
+  quantized along n (dgrad); the vanilla arm is deq(Q4(X)) deq(B)^T.  All
+  products and sums are float64.
+* grouped (one mean and one tensor scale per expert segment): every step above
+  is applied to each segment's rows; SR indices use the global row, the mean
+  of segment s uses index s * cols + col; an empty segment has mean 0.
+"""
+
+import math
+
+import numpy as np
+
+from . import formats
+from .philox import sr_draw16
+
+BLOCK = 16
+F32 = np.float32
+
+
+# --------------------------------------------------------------------------
+# mean and residual
+# --------------------------------------------------------------------------
+
+def column_mean(a):
+    """mu_j = float32(fsum(a[:, j]) / rows) for a float32 (rows x cols) array."""
+    a = np.asarray(a, dtype=np.float32)
+    rows, cols = a.shape
+    if rows == 0:
+        return np.zeros(cols, dtype=np.float32)
+    sums = np.array([math.fsum(a[:, j].astype(np.float64)) for j in range(cols)],
+                    dtype=np.float64)
+    return (sums / np.float64(rows)).astype(np.float32)
+
+
+def residual(a, mu):
+    """r = float32(a - mu) broadcast over rows."""
+    return (np.asarray(a, dtype=np.float32) - np.asarray(mu, dtype=np.float32)[None, :]).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Q4: NVFP4-style two-level quantization
+# --------------------------------------------------------------------------
+
+def tensor_scales(amax):
+    """(S_enc, S_dec) as float32 from the tensor's float32 max magnitude."""
+    amax = F32(amax)
+    if amax == 0:
+        s_enc = F32(1.0)
+    else:
+        with np.errstate(over="ignore", divide="ignore"):
+            s_enc = F32(2688.0) / amax
+        if not np.isfinite(s_enc):
+            s_enc = F32(1.0)
+    s_dec = F32(1.0) / s_enc
+    return F32(s_enc), F32(s_dec)
+
+
+def quantize(t, rnd="sr", seed=0, stream=0, row0=0, amax=None):
+    """Q4 of a float32 (rows x cols) tensor; blocks of 16 along cols.
+
+    row0 offsets the row used in the SR index (global row of a segment).
+    amax, if given, overrides the tensor's own max magnitude (never used by the
+    method itself; kept for tests of the scale arithmetic).
+    Returns dict(codes=u8[rows, cols/2], scales=u8[rows, cols/16],
+    s_enc=f32, s_dec=f32).
+    """
+    t = np.asarray(t, dtype=np.float32)
+    rows, cols = t.shape
+    if cols % BLOCK:
+        raise ValueError("cols must be a multiple of 16")
+    if amax is None:
+        amax = np.max(np.abs(t)) if t.size else F32(0.0)
+    s_enc, s_dec = tensor_scales(amax)
+    nb = cols // BLOCK
+    blk = t.reshape(rows, nb, BLOCK)
+    amax_b = np.max(np.abs(blk), axis=-1) if rows else np.zeros((0, nb), np.float32)
+    s_b = ((amax_b / F32(6.0)).astype(np.float32) * s_enc).astype(np.float32)
+    s_b = np.minimum(s_b, F32(formats.E4M3_MAX))
+    c_b = formats.e4m3_encode(s_b)
+    d_b = formats.e4m3_decode(c_b).astype(np.float32)       # exact in float32
+    with np.errstate(divide="ignore"):
+        e_b = np.where(d_b > 0, s_enc / np.where(d_b > 0, d_b, F32(1.0)), F32(0.0)).astype(np.float32)
+    v = (blk * e_b[..., None]).astype(np.float32).reshape(rows, cols)
+    if rnd == "rn":
+        codes = formats.e2m1_round_rn(v)
+    elif rnd == "sr":
+        r_idx = (np.arange(rows, dtype=np.uint64) + np.uint64(row0))[:, None]
+        idx = r_idx * np.uint64(cols) + np.arange(cols, dtype=np.uint64)[None, :]
+        codes = formats.e2m1_round_sr(v, sr_draw16(seed, stream, idx))
+    else:
+        raise ValueError("rnd must be 'rn' or 'sr'")
+    return dict(codes=formats.pack_nibbles(codes), scales=c_b, s_enc=s_enc, s_dec=s_dec)
+
+
+def dequantize(q):
+    """float64 values of an oracle-quantized tensor (exact)."""
+    codes = formats.unpack_nibbles(q["codes"])
+    rows, cols = codes.shape
+    d = formats.e4m3_decode(q["scales"]).astype(np.float64)
+    vals = formats.e2m1_decode(codes).reshape(rows, cols // BLOCK, BLOCK) * d[..., None]
+    return vals.reshape(rows, cols) * np.float64(q["s_dec"])
+
+
+# --------------------------------------------------------------------------
+# Averis split-quant, vanilla quant, weight quant
+# --------------------------------------------------------------------------
+
+def split_quant(a, rnd="sr", seed=0):
+    """mu, X_R,q = Q4(a - 1 mu) (stream 0), mean_q = Q4(mu) (stream 1)."""
+    a = np.asarray(a, dtype=np.float32)
+    mu = column_mean(a)
+    r = residual(a, mu)
+    res_q = quantize(r, rnd, seed, stream=0)
+    mean_q = quantize(mu[None, :], rnd, seed, stream=1)
+    return dict(mu=mu, residual=res_q, mean=mean_q)
+
+
+def vanilla_quant(a, rnd="sr", seed=0):
+    """Q4 of the activation itself, no split (stream 0)."""
+    return quantize(np.asarray(a, dtype=np.float32), rnd, seed, stream=0)
+
+
+def weight_quant(w, rnd="rn", seed=0):
+    """The two quantized copies of W (m x n): forward B = Q4(W^T) (n x m, blocks
+    along m) and dgrad B = Q4(W) (m x n, blocks along n); stream 2."""
+    w = np.asarray(w, dtype=np.float32)
+    return dict(fwd=quantize(np.ascontiguousarray(w.T), rnd, seed, stream=2),
+                dgrad=quantize(w, rnd, seed, stream=2))
+
+
+# --------------------------------------------------------------------------
+# GEMMs (float64)
+# --------------------------------------------------------------------------
+
+def gemm(a_q, b_q, mean_q=None):
+    """deq(A) deq(B)^T (+ 1 (deq(mean) deq(B)^T) if a quantized mean is given)."""
+    b = dequantize(b_q)
+    c = dequantize(a_q) @ b.T
+    if mean_q is not None:
+        c = c + (dequantize(mean_q) @ b.T)[0][None, :]
+    return c
+
+
+def gemm_abs_bound(a_q, b_q, mean_q=None):
+    """|deq A| |deq B|^T (+ |deq mean| |deq B|^T): the scale the GEMM error is
+    measured against (an FP32-accumulated result is within K * 2^-24 of it)."""
+    b = np.abs(dequantize(b_q))
+    c = np.abs(dequantize(a_q)) @ b.T
+    if mean_q is not None:
+        c = c + (np.abs(dequantize(mean_q)) @ b.T)[0][None, :]
+    return c
+
+
+def averis_forward(x, w_q_fwd, rnd="sr", seed=0):
+    """Y = 1 (mean_q W_q) + X_R,q W_q ([Lighthouse] §2.2, forward)."""
+    s = split_quant(x, rnd, seed)
+    return s, gemm(s["residual"], w_q_fwd, s["mean"])
+
+
+def averis_dgrad(d, w_q_dgrad, rnd="sr", seed=0):
+    """dX = 1 (mean_q,D W_q^T) + D_R,q W_q^T ([Lighthouse] §2.2, backward)."""
+    s = split_quant(d, rnd, seed)
+    return s, gemm(s["residual"], w_q_dgrad, s["mean"])
+
+
+def vanilla_forward(x, w_q_fwd, rnd="sr", seed=0):
+    """Comparison arm ([Abstract]: vanilla NVFP4): deq(Q4(X)) deq(W_q)."""
+    q = vanilla_quant(x, rnd, seed)
+    return q, gemm(q, w_q_fwd)
+
+
+# --------------------------------------------------------------------------
+# grouped (expert segments)
+# --------------------------------------------------------------------------
+
+def split_quant_grouped(a, offsets, rnd="sr", seed=0):
+    """Per-segment split-quant over rows offsets[s]:offsets[s+1]."""
+    a = np.asarray(a, dtype=np.float32)
+    rows, cols = a.shape
+    nseg = len(offsets) - 1
+    mu = np.zeros((nseg, cols), dtype=np.float32)
+    res = []
+    means = []
+    for s in range(nseg):
+        r0, r1 = int(offsets[s]), int(offsets[s + 1])
+        seg = a[r0:r1]
+        if r1 > r0:
+            mu[s] = column_mean(seg)
+        res.append(quantize(residual(seg, mu[s]), rnd, seed, stream=0, row0=r0))
+        m = quantize(mu[s][None, :], rnd, seed, stream=1, row0=s)
+        means.append(m)
+    return dict(mu=mu, residual=res, mean=means)
+
+
+def vanilla_quant_grouped(a, offsets, rnd="sr", seed=0):
+    a = np.asarray(a, dtype=np.float32)
+    return [quantize(a[int(offsets[s]):int(offsets[s + 1])], rnd, seed, stream=0, row0=int(offsets[s]))
+            for s in range(len(offsets) - 1)]
+
+
+def gemm_grouped(a_qs, b_qs, mean_qs=None):
+    """Row-concatenation over segments of gemm(a_q[s], b_q[s], mean_q[s])."""
+    outs = []
+    for s in range(len(a_qs)):
+        outs.append(gemm(a_qs[s], b_qs[s], None if mean_qs is None else mean_qs[s]))
+    return np.concatenate(outs, axis=0)
