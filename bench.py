@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of the Averis linear hot path (forward + dgrad) on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input
+of the Qwen3-0.6B up-projection shape (l = 8192 tokens, m = 1024, n = 3072,
+bf16): both quantized copies of W, split-quant of X, the forward GEMM with
+the rank-one mean term, split-quant of the output gradient D, and the dgrad
+GEMM.  The vanilla-FP4 arm (plain quant of X / D + the same GEMMs without
+the mean term) is timed the same way to report the Averis overhead.
+
+Inputs are resident in HBM before timing starts; the timed steps rotate
+through enough copies of X and D (> 512 MB) that the 256 MB MALL cannot hold
+them, so every step reads its activations from HBM.
+
+Prints ONE JSON line (see the keys below).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from mean_residual_quantized_amd import averis as av  # noqa: E402
+from mean_residual_quantized_amd import workloads  # noqa: E402
+
+METRIC = "Averis fwd+dgrad TFLOP/s & split-quant GB/s (frac. roofline); % overhead vs vanilla FP4"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+F16_MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 MFMA, the instruction the GEMM uses
+FP4_MFMA_PEAK_TFLOPS = 10100.0  # dense fp4, for reference only
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--l", type=int, default=8192)
+    p.add_argument("--m", type=int, default=1024)
+    p.add_argument("--n", type=int, default=3072)
+    p.add_argument("--copies", type=int, default=0, help="rotating input copies (0: auto)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=1024, help="oracle sample: tokens")
+    return p.parse_args()
+
+
+class Timer:
+    """Event pairs on the current stream (the one the library launches on)."""
+
+    def __init__(self):
+        self.pairs = {}
+
+    def start(self, name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.setdefault(name, []).append([e, None])
+
+    def stop(self, name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs[name][-1][1] = e
+
+    def ms(self, name):
+        return [a.elapsed_time(b) for a, b in self.pairs.get(name, [])]
+
+
+def run_step(x, d, w, ws, t=None, vanilla=False):
+    """One pass of the hot path; returns nothing (outputs stay on device)."""
+    def tic(n):
+        if t:
+            t.start(n)
+
+    def toc(n):
+        if t:
+            t.stop(n)
+    tic("wquant")
+    wt = av.averis_quant(w, transpose=True, rnd=av.RN, sr_stream=av.STREAM_WEIGHT, ws=ws["q"])
+    wd = av.averis_quant(w, transpose=False, rnd=av.RN, sr_stream=av.STREAM_WEIGHT, ws=ws["q"])
+    toc("wquant")
+    if not vanilla:
+        tic("split_x")
+        xr, xm, _ = av.averis_split_quant(x, seed=0, ws=ws["sq_x"])
+        toc("split_x")
+        tic("gemm_fwd")
+        av.averis_gemm_fwd(xr, xm, wt, out_dtype=torch.bfloat16, out=ws["y"], ws=ws["g"])
+        toc("gemm_fwd")
+        tic("split_d")
+        dr, dm, _ = av.averis_split_quant(d, seed=1, ws=ws["sq_d"])
+        toc("split_d")
+        tic("gemm_dgrad")
+        av.averis_gemm_dgrad(dr, dm, wd, out_dtype=torch.bfloat16, out=ws["dx"], ws=ws["g"])
+        toc("gemm_dgrad")
+    else:
+        tic("vq_x")
+        xq = av.averis_quant(x, seed=0, ws=ws["sq_x"])
+        toc("vq_x")
+        tic("vgemm_fwd")
+        av.averis_gemm_vanilla(xq, wt, out_dtype=torch.bfloat16, out=ws["y"], ws=ws["g"])
+        toc("vgemm_fwd")
+        tic("vq_d")
+        dq = av.averis_quant(d, seed=1, ws=ws["sq_d"])
+        toc("vq_d")
+        tic("vgemm_dgrad")
+        av.averis_gemm_vanilla(dq, wd, out_dtype=torch.bfloat16, out=ws["dx"], ws=ws["g"])
+        toc("vgemm_dgrad")
+
+
+def timed(xs, ds, w, ws, steps, warmup, vanilla):
+    for i in range(warmup):
+        run_step(xs[i % len(xs)], ds[i % len(ds)], w, ws, None, vanilla)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        run_step(xs[i % len(xs)], ds[i % len(ds)], w, ws, None, vanilla)
+    torch.cuda.synchronize()
+    whole_ms = (time.perf_counter() - t0) * 1e3 / steps
+    # per-kernel-call durations, events on the launch stream, same rotation
+    t = Timer()
+    for i in range(steps):
+        run_step(xs[i % len(xs)], ds[i % len(ds)], w, ws, t, vanilla)
+    torch.cuda.synchronize()
+    return whole_ms, t
+
+
+def cpu_baseline(cfg_rows, m, n):
+    """The oracle as it stands on a bounded sample: cfg_rows tokens of the
+    same workload (split-quant of X and D, both weight copies, the float64
+    forward and dgrad GEMMs); reported in TFLOP/s of the sample's GEMMs."""
+    from oracle import averis as orc
+    cfg = workloads.config1(l=cfg_rows, m=m, n=n)
+    x, w, d = cfg["x"].float().numpy(), cfg["w"].float().numpy(), cfg["d"].float().numpy()
+    t0 = time.perf_counter()
+    wq = orc.weight_quant(w, "rn")
+    orc.averis_forward(x, wq["fwd"], "sr", 0)
+    orc.averis_dgrad(d, wq["dgrad"], "sr", 1)
+    dt = time.perf_counter() - t0
+    flops = 2 * (2.0 * cfg_rows * m * n)
+    try:
+        import threadpoolctl
+        blas = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        blas = 1
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=int(blas), kind="oracle",
+                sample="%d tokens of the l=8192 workload (m=%d, n=%d): split-quant X and D, "
+                       "both weight copies, float64 fwd+dgrad GEMMs; %.1f s; numpy elementwise "
+                       "work single-threaded, float64 matmul on %d BLAS threads of %d host cores"
+                       % (cfg_rows, m, n, dt, blas, len(os.sched_getaffinity(0))),
+                seconds=dt)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    av.lib()
+    l, m, n = args.l, args.m, args.n
+    log("bench: generating inputs l=%d m=%d n=%d" % (l, m, n))
+    cfg = workloads.config1(l=l, m=m, n=n)
+    x0, w0, d0 = cfg["x"].cuda(), cfg["w"].cuda(), cfg["d"].cuda()
+    bytes_per_set = (x0.numel() + d0.numel()) * 2
+    copies = args.copies or max(2, int(np.ceil(640e6 / bytes_per_set)))
+    xs = [x0] + [x0.clone() for _ in range(copies - 1)]
+    ds = [d0] + [d0.clone() for _ in range(copies - 1)]
+    dev = x0.device
+    ws = dict(
+        q=torch.empty(av.workspace_bytes(av.OP_QUANT, n, m), dtype=torch.uint8, device=dev),
+        sq_x=torch.empty(av.workspace_bytes(av.OP_SPLIT_QUANT, l, m), dtype=torch.uint8,
+                         device=dev),
+        sq_d=torch.empty(av.workspace_bytes(av.OP_SPLIT_QUANT, l, n), dtype=torch.uint8,
+                         device=dev),
+        g=torch.empty(av.workspace_bytes(av.OP_GEMM, l, max(m, n), max(m, n)), dtype=torch.uint8,
+                      device=dev),
+        y=torch.empty((l, n), dtype=torch.bfloat16, device=dev),
+        dx=torch.empty((l, m), dtype=torch.bfloat16, device=dev),
+    )
+    log("bench: %d rotating input copies; warmup %d, steps %d" % (copies, args.warmup, args.steps))
+    ms_a, ta = timed(xs, ds, w0, ws, args.steps, args.warmup, vanilla=False)
+    ms_v, tv = timed(xs, ds, w0, ws, args.steps, args.warmup, vanilla=True)
+    log("bench: averis %.3f ms/step, vanilla %.3f ms/step" % (ms_a, ms_v))
+
+    gemm_flops = 2.0 * l * m * n
+    med = lambda v: float(np.median(v)) if v else float("nan")
+    comp = {k: med(ta.ms(k)) for k in ["wquant", "split_x", "gemm_fwd", "split_d", "gemm_dgrad"]}
+    compv = {k: med(tv.ms(k)) for k in ["vq_x", "vgemm_fwd", "vq_d", "vgemm_dgrad"]}
+    sq_bytes = lambda rows, cols: rows * cols * (2 + 0.5 + 1 / 16)   # algorithmic bytes
+    gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
+    split = {
+        "x": dict(ms=comp["split_x"], gbs=gbs(sq_bytes(l, m), comp["split_x"])),
+        "d": dict(ms=comp["split_d"], gbs=gbs(sq_bytes(l, n), comp["split_d"])),
+    }
+    for v in split.values():
+        v["frac_hbm"] = v["gbs"] / HBM_PEAK_GBS
+    vq = {"x": dict(ms=compv["vq_x"], gbs=gbs(sq_bytes(l, m), compv["vq_x"])),
+          "d": dict(ms=compv["vq_d"], gbs=gbs(sq_bytes(l, n), compv["vq_d"]))}
+    gemm = {k: dict(ms=comp[k], tflops=gemm_flops / (comp[k] * 1e-3) / 1e12)
+            for k in ["gemm_fwd", "gemm_dgrad"]}
+    vgemm = {k: dict(ms=compv[k], tflops=gemm_flops / (compv[k] * 1e-3) / 1e12)
+             for k in ["vgemm_fwd", "vgemm_dgrad"]}
+    t_fwd_a = comp["split_x"] + comp["gemm_fwd"]
+    t_fwd_v = compv["vq_x"] + compv["vgemm_fwd"]
+    t_bwd_a = comp["split_d"] + comp["gemm_dgrad"]
+    t_bwd_v = compv["vq_d"] + compv["vgemm_dgrad"]
+    overhead = dict(fwd_pct=100 * (t_fwd_a / t_fwd_v - 1), dgrad_pct=100 * (t_bwd_a / t_bwd_v - 1),
+                    step_pct=100 * (ms_a / ms_v - 1))
+
+    # roofline of the dominant kernel: the forward GEMM (the vanilla call is the
+    # same NT kernel without the rank-one term; its events bracket one launch)
+    g_ms = compv["vgemm_fwd"]
+    achieved = gemm_flops / (g_ms * 1e-3) / 1e12
+    roofline = dict(bound="mfma", achieved=achieved, peak=F16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=achieved / F16_MFMA_PEAK_TFLOPS, traffic=None,
+                    kernel="k_gemm_nt (NVFP4 NT GEMM, exact fp16 dequant -> "
+                           "v_mfma_f32_32x32x16_f16), %dx%dx%d" % (l, n, m),
+                    frac_of_fp4_peak=achieved / FP4_MFMA_PEAK_TFLOPS)
+
+    out = {
+        "metric": METRIC,
+        "value": 2 * gemm_flops / (ms_a * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_a,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 (e2m1 + e4m3 scales) operands, f16 MFMA, f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3-0.6B-shaped up-proj, Averis fwd+dgrad step",
+                   "tokens": l, "m": m, "n": n, "input_dtype": "bf16", "sr": "philox4x32-10, 16 bits",
+                   "rotating_input_copies": copies},
+        "roofline": roofline,
+        "split_quant": split,
+        "vanilla_quant": vq,
+        "gemm": gemm,
+        "vanilla_gemm": vgemm,
+        "weight_quant_ms": comp["wquant"],
+        "vanilla_ms_per_step": ms_v,
+        "overhead_vs_vanilla": overhead,
+        "pages_overhead_context": "2.20% end-to-end over vanilla NVFP4 (hardware not stated)",
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle on the host (bounded sample)")
+        out["cpu_baseline"] = cpu_baseline(args.cpu_rows, m, n)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,219 @@
+/*
+ * libaveris -- C ABI of the Averis mean-residual split FP4 linear on MI355X
+ * (gfx950): split-quant, plain quant, and the quantized GEMMs of the forward
+ * and dgrad passes, plus the vanilla-FP4 comparison arm.
+ *
+ * The method (from "The Curse and Blessing of Mean Bias in FP4-Quantized LLM
+ * Training", as reviewed on the "Lighthouse" blog, §2.1-§2.2, and summarised
+ * in the paper's arXiv abstract and the gist.science technical summary §2):
+ *   mu_X   = (1/l) 1^T X                       column mean over the l tokens
+ *   X_R    = X - 1 mu_X^T                      residual (unquantized mean)
+ *   Y      = 1 (Q4(mu_X) Q4(W)) + Q4(X_R) Q4(W)          forward
+ *   dX     = 1 (Q4(mu_D) Q4(W)^T) + Q4(D_R) Q4(W)^T      dgrad (D = dL/dY)
+ * Q4 is NVFP4-style E2M1 with stochastic rounding by default (Lighthouse
+ * §3.1; two-level "hierarchical" microscaling per "Dissecting Outlier
+ * Dynamics in LLM NVFP4 Pretraining", abstract).
+ *
+ * Q4 as implemented (a reading; the pages give no bit-level recipe):
+ *   blocks of 16 along the GEMM contraction axis (the tensor's columns);
+ *   amax   = max |T| over the tensor (per segment for grouped calls)
+ *   S_enc  = fp32(2688 / amax), or 1 when amax == 0 or the quotient is not
+ *            finite;  S_dec = fp32(1 / S_enc)
+ *   s_b    = fp32(fp32(amax_b / 6) * S_enc) capped at 448 -> E4M3FN (RNE,
+ *            subnormals kept) = the block's scale byte, value d_b
+ *   e_b    = fp32(S_enc / d_b) (0 if d_b == 0);  v = fp32(t * e_b)
+ *   E2M1 code (sign << 3 | index into {0,.5,1,1.5,2,3,4,6}) by
+ *     RN: nearest, ties to the even index, |v| >= 6 -> 6, or
+ *     SR: up iff u < 2^16 (|v| - lo) / (hi - lo) with u the element's 16-bit
+ *         draw from Philox4x32-10: key = seed, counter = (g lo, g hi,
+ *         stream, 0), g = idx >> 3, word (idx >> 1) & 3, half idx & 1,
+ *         idx = row * cols + col (global row for grouped tensors).
+ *   SR streams: 0 residual and vanilla activations, 1 means, 2 weights.
+ *   The mean is fp32(RN64(exact column sum) / l); the residual is
+ *   fp32(x - mu) with the unquantized mean.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library allocates nothing and keeps no state between calls.
+ *   - Work is enqueued on `stream` (NULL = the default stream) and the call
+ *     returns without synchronising.  Scales flow device to device.
+ *   - Arguments are validated before any HIP call; a rejected call enqueues
+ *     nothing and returns the status.  Nothing aborts.
+ *   - The workspace `ws` (device, >= averis_workspace_bytes(...) bytes,
+ *     256-byte aligned) holds intermediate results only; its contents on
+ *     entry do not matter.  Calls that share a workspace must be ordered on
+ *     one stream.
+ *   - Values that are not finite in an input give unspecified codes.
+ */
+#ifndef AVERIS_H
+#define AVERIS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AVERIS_ABI_VERSION 1
+
+typedef enum {
+  AVERIS_OK = 0,
+  AVERIS_E_NULL = 1,       /* a required pointer is NULL                      */
+  AVERIS_E_SHAPE = 2,      /* negative size, cols % 16 != 0, operand mismatch */
+  AVERIS_E_DTYPE = 3,      /* unknown dtype                                   */
+  AVERIS_E_ALIGN = 4,      /* pointer or leading dimension misaligned         */
+  AVERIS_E_WORKSPACE = 5,  /* workspace missing or smaller than required      */
+  AVERIS_E_ARG = 6,        /* other invalid argument (rounding, stream, nseg) */
+  AVERIS_E_HIP = 7         /* a kernel launch failed                          */
+} averis_status_t;
+
+typedef enum { AVERIS_F32 = 0, AVERIS_BF16 = 1 } averis_dtype_t;
+typedef enum { AVERIS_RN = 0, AVERIS_SR = 1 } averis_round_t;
+
+/* Workspace queries, see averis_workspace_bytes. */
+typedef enum {
+  AVERIS_OP_SPLIT_QUANT = 0,  /* rows, cols, nseg (nseg = 0: not grouped)     */
+  AVERIS_OP_QUANT = 1,        /* rows, cols, nseg (batch for batched quant)   */
+  AVERIS_OP_GEMM = 2          /* rows = M, cols = K, n = N, nseg              */
+} averis_op_t;
+
+/* An NVFP4-style tensor of rows x cols logical elements, 16-blocks along
+ * cols.  codes: rows * cols/2 bytes, row-major, byte j of a row holds element
+ * 2j in bits 3:0 and element 2j+1 in bits 7:4; 16-byte aligned.
+ * scales: rows * cols/16 E4M3FN bytes, row-major.  tscale: 2 floats
+ * [S_enc, S_dec] per tensor (per segment / batch entry for grouped calls).
+ * All three are device pointers. */
+typedef struct {
+  uint8_t* codes;
+  uint8_t* scales;
+  float*   tscale;
+  int64_t  rows;
+  int64_t  cols;
+} averis_nvfp4_t;
+
+/* ---------------------------------------------------------------------- */
+/* Split-quant (Lighthouse §2.1 column mean; §2.2 X_R = X - 1 mu, separate */
+/* quantization of mean and residual; gist.science summary §2).            */
+/* ---------------------------------------------------------------------- */
+
+/* a: rows x cols activation or output gradient (dtype F32 or BF16), row
+ * stride lda elements (lda >= cols, lda * element size a multiple of 16
+ * bytes, a 16-byte aligned).  Writes
+ *   residual: rows x cols, Q4(a - 1 mu) with SR stream 0 (or RN),
+ *   mean:     1 x cols,    Q4(mu) with SR stream 1 (or RN),
+ *   mean_f32: the fp32 mean (optional, may be NULL), cols floats.
+ * rows == 0 gives mu = 0 and an all-zero mean tensor with S_enc = 1.
+ * Workspace: averis_workspace_bytes(AVERIS_OP_SPLIT_QUANT, rows, cols, 0, 0). */
+averis_status_t averis_split_quant(const void* a, averis_dtype_t dtype, int64_t rows, int64_t cols,
+                                   int64_t lda, uint64_t seed, averis_round_t rnd,
+                                   const averis_nvfp4_t* residual, const averis_nvfp4_t* mean,
+                                   float* mean_f32, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Grouped split-quant over expert segments (the paper's MoE runs, arXiv
+ * abstract): rows seg_offsets[s] .. seg_offsets[s+1]-1 form segment s, each
+ * with its own mean (row s of `mean`, nseg x cols, SR index s*cols + col)
+ * and its own residual tensor scale (residual->tscale holds 2*nseg floats,
+ * as does mean->tscale).  seg_offsets: DEVICE int64[nseg+1], non-decreasing,
+ * seg_offsets[0] = 0, seg_offsets[nseg] = rows (the kernels clamp values
+ * outside [0, rows]).  mean_f32 (optional): nseg x cols.  An empty segment
+ * has mean 0.  Workspace: AVERIS_OP_SPLIT_QUANT with nseg. */
+averis_status_t averis_split_quant_grouped(const void* a, averis_dtype_t dtype, int64_t rows,
+                                           int64_t cols, int64_t lda, const int64_t* seg_offsets,
+                                           int nseg, uint64_t seed, averis_round_t rnd,
+                                           const averis_nvfp4_t* residual,
+                                           const averis_nvfp4_t* mean, float* mean_f32, void* ws,
+                                           size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* Plain quant: the vanilla-FP4 arm (arXiv abstract: "vanilla NVFP4") and  */
+/* the weight operand W (Lighthouse §2.2, both equations).                 */
+/* ---------------------------------------------------------------------- */
+
+/* Q4 of the logical rows x cols tensor T, blocks along cols, one tensor
+ * scale.  transpose = 0: T[r][c] = a[r*lda + c]; transpose = 1:
+ * T[r][c] = a[c*lda + r] (a stored cols x rows; used for the forward copy
+ * of W, Q4(W^T)).  sr_stream: 0 for activations, 2 for weights.
+ * Workspace: AVERIS_OP_QUANT (rows, cols, 0). */
+averis_status_t averis_quant(const void* a, averis_dtype_t dtype, int64_t rows, int64_t cols,
+                             int64_t lda, int transpose, uint64_t seed, averis_round_t rnd,
+                             uint32_t sr_stream, const averis_nvfp4_t* out, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/* Batched plain quant: `batch` independent rows x cols tensors (matrix b at
+ * a + b*batch_stride elements), each with its own tensor scale
+ * (out->tscale: 2*batch floats); out is (batch*rows) x cols and the SR index
+ * uses the global row b*rows + r.  Used for per-expert weights.
+ * Workspace: AVERIS_OP_QUANT (rows, cols, batch). */
+averis_status_t averis_quant_batched(const void* a, averis_dtype_t dtype, int batch, int64_t rows,
+                                     int64_t cols, int64_t lda, int64_t batch_stride,
+                                     int transpose, uint64_t seed, averis_round_t rnd,
+                                     uint32_t sr_stream, const averis_nvfp4_t* out, void* ws,
+                                     size_t ws_bytes, hipStream_t stream);
+
+/* Grouped plain quant of activations: one tensor scale per segment
+ * (vanilla arm of the grouped case).  Workspace: AVERIS_OP_QUANT with nseg. */
+averis_status_t averis_quant_grouped(const void* a, averis_dtype_t dtype, int64_t rows,
+                                     int64_t cols, int64_t lda, const int64_t* seg_offsets,
+                                     int nseg, uint64_t seed, averis_round_t rnd,
+                                     uint32_t sr_stream, const averis_nvfp4_t* out, void* ws,
+                                     size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* Quantized GEMMs (Lighthouse §2.2; gist.science summary §2).             */
+/* C = deq(A) deq(B)^T (+ 1 deq(mean) deq(B)^T), FP32 accumulation.        */
+/* ---------------------------------------------------------------------- */
+
+/* Forward: y (xr->rows x wt->rows) = 1 (mean W) + X_R W with
+ *   xr:   Q4(X - 1 mu), l x m
+ *   mean: Q4(mu), 1 x m
+ *   wt:   Q4(W^T), n x m (blocks along m)
+ * y: F32 or BF16, row stride ldy >= n elements.  Workspace: AVERIS_OP_GEMM
+ * (l, m, n, 0). */
+averis_status_t averis_gemm_fwd(const averis_nvfp4_t* xr, const averis_nvfp4_t* mean,
+                                const averis_nvfp4_t* wt, void* y, averis_dtype_t ydtype,
+                                int64_t ldy, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Dgrad: dx (dr->rows x w->rows) = 1 (mean_d W^T) + D_R W^T with
+ *   dr:     Q4(D - 1 mu_D), l x n
+ *   mean_d: Q4(mu_D), 1 x n
+ *   w:      Q4(W), m x n (blocks along n)
+ * Same kernel as the forward; only the quantized copy of W differs. */
+averis_status_t averis_gemm_dgrad(const averis_nvfp4_t* dr, const averis_nvfp4_t* mean_d,
+                                  const averis_nvfp4_t* w, void* dx, averis_dtype_t dxdtype,
+                                  int64_t lddx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Vanilla arm: c = deq(a) deq(b)^T, no mean term. */
+averis_status_t averis_gemm_vanilla(const averis_nvfp4_t* a, const averis_nvfp4_t* b, void* c,
+                                    averis_dtype_t cdtype, int64_t ldc, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
+
+/* Grouped GEMM: for each segment s (rows seg_offsets[s] .. [s+1]-1 of a),
+ * c[rows of s] = deq(a_s) deq(b_s)^T (+ 1 deq(mean_s) deq(b_s)^T), where
+ * b is (nseg * N) x K (expert s = rows s*N .. s*N+N-1, its own tensor scale
+ * b->tscale[2s..2s+1]), a->tscale and mean->tscale hold 2*nseg floats,
+ * mean is nseg x K or NULL (vanilla).  Workspace: AVERIS_OP_GEMM with nseg. */
+averis_status_t averis_gemm_grouped(const averis_nvfp4_t* a, const averis_nvfp4_t* mean,
+                                    const averis_nvfp4_t* b, const int64_t* seg_offsets, int nseg,
+                                    void* c, averis_dtype_t cdtype, int64_t ldc, void* ws,
+                                    size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* Utilities                                                               */
+/* ---------------------------------------------------------------------- */
+
+/* Bytes of workspace an entry point needs (0 if none); a bad query returns
+ * 0 and the entry point then rejects the call with AVERIS_E_SHAPE. */
+size_t averis_workspace_bytes(averis_op_t op, int64_t rows, int64_t cols, int64_t n, int64_t nseg);
+
+/* Static string for a status code. */
+const char* averis_status_str(averis_status_t status);
+
+/* AVERIS_ABI_VERSION of the built library. */
+int averis_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AVERIS_H */

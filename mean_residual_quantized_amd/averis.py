@@ -1,0 +1,271 @@
+"""Thin ctypes binding of libaveris (include/averis.h), same names as the C ABI.
+
+Argument marshalling only: torch supplies device memory (outputs and
+workspace are allocated with torch.empty) and the current HIP stream; every
+step of the computation runs in the library's kernels.  The library must be
+built (``python -m mean_residual_quantized_amd.build``); if it is missing,
+loading fails with an error -- there is no fallback.
+"""
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libaveris.so")
+
+AVERIS_OK = 0
+STATUS_NAMES = {0: "OK", 1: "E_NULL", 2: "E_SHAPE", 3: "E_DTYPE", 4: "E_ALIGN",
+                5: "E_WORKSPACE", 6: "E_ARG", 7: "E_HIP"}
+F32, BF16 = 0, 1
+RN, SR = 0, 1
+OP_SPLIT_QUANT, OP_QUANT, OP_GEMM = 0, 1, 2
+STREAM_ACT, STREAM_MEAN, STREAM_WEIGHT = 0, 1, 2
+
+# every symbol include/averis.h declares
+EXPORTS = [
+    "averis_split_quant", "averis_split_quant_grouped", "averis_quant", "averis_quant_batched",
+    "averis_quant_grouped", "averis_gemm_fwd", "averis_gemm_dgrad", "averis_gemm_vanilla",
+    "averis_gemm_grouped", "averis_workspace_bytes", "averis_status_str", "averis_abi_version",
+]
+
+
+class AverisError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__("%s failed: %s (%s)" % (fn, STATUS_NAMES.get(status, status), msg))
+        self.status = status
+
+
+class _NVFP4(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("tscale", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libaveris.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libaveris.so not built at %s; run "
+                               "`python -m mean_residual_quantized_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, U64, I, U32, SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_int,
+                                   ctypes.c_uint32, ctypes.c_size_t)
+        T = ctypes.POINTER(_NVFP4)
+        sig = {
+            "averis_split_quant": [P, I, I64, I64, I64, U64, I, T, T, P, P, SZ, P],
+            "averis_split_quant_grouped": [P, I, I64, I64, I64, P, I, U64, I, T, T, P, P, SZ, P],
+            "averis_quant": [P, I, I64, I64, I64, I, U64, I, U32, T, P, SZ, P],
+            "averis_quant_batched": [P, I, I, I64, I64, I64, I64, I, U64, I, U32, T, P, SZ, P],
+            "averis_quant_grouped": [P, I, I64, I64, I64, P, I, U64, I, U32, T, P, SZ, P],
+            "averis_gemm_fwd": [T, T, T, P, I, I64, P, SZ, P],
+            "averis_gemm_dgrad": [T, T, T, P, I, I64, P, SZ, P],
+            "averis_gemm_vanilla": [T, T, P, I, I64, P, SZ, P],
+            "averis_gemm_grouped": [T, T, T, P, I, P, I, I64, P, SZ, P],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.averis_workspace_bytes.argtypes = [I, I64, I64, I64, I64]
+        L.averis_workspace_bytes.restype = SZ
+        L.averis_status_str.argtypes = [I]
+        L.averis_status_str.restype = ctypes.c_char_p
+        L.averis_abi_version.argtypes = []
+        L.averis_abi_version.restype = I
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != AVERIS_OK:
+        raise AverisError(fn, status, lib().averis_status_str(status).decode())
+
+
+def workspace_bytes(op, rows, cols, n=0, nseg=0):
+    return int(lib().averis_workspace_bytes(op, rows, cols, n, nseg))
+
+
+# --------------------------------------------------------------------------
+# tensors
+# --------------------------------------------------------------------------
+
+@dataclass
+class NVFP4:
+    """Device NVFP4-style tensor: codes u8[rows, cols/2], scales u8[rows, cols/16]
+    (E4M3), tscale f32[2*nseg] = [S_enc, S_dec] per segment."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    tscale: torch.Tensor
+    rows: int
+    cols: int
+
+    @staticmethod
+    def empty(rows, cols, nseg=1, device="cuda"):
+        return NVFP4(torch.empty((rows, cols // 2), dtype=torch.uint8, device=device),
+                     torch.empty((rows, cols // 16), dtype=torch.uint8, device=device),
+                     torch.empty((2 * nseg,), dtype=torch.float32, device=device), rows, cols)
+
+    def c(self):
+        return _NVFP4(self.codes.data_ptr(), self.scales.data_ptr(), self.tscale.data_ptr(),
+                      self.rows, self.cols)
+
+    def cpu(self):
+        return dict(codes=self.codes.cpu().numpy(), scales=self.scales.cpu().numpy(),
+                    tscale=self.tscale.cpu().numpy())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError("libaveris takes float32 or bfloat16 inputs, got %s" % t.dtype)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _workspace(nbytes, device):
+    return torch.empty((max(int(nbytes), 1),), dtype=torch.uint8, device=device)
+
+
+def _lda(a):
+    if a.dim() != 2 or a.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return a.stride(0)
+
+
+# --------------------------------------------------------------------------
+# entry points
+# --------------------------------------------------------------------------
+
+def averis_split_quant(a, seed=0, rnd=SR, ws=None):
+    """Q4(a - 1 mu) and Q4(mu); returns (residual, mean, mu_f32)."""
+    rows, cols = a.shape
+    res = NVFP4.empty(rows, cols, 1, a.device)
+    mean = NVFP4.empty(1, cols, 1, a.device)
+    mu = torch.empty((cols,), dtype=torch.float32, device=a.device)
+    need = workspace_bytes(OP_SPLIT_QUANT, rows, cols)
+    ws = ws if ws is not None else _workspace(need, a.device)
+    r, m = res.c(), mean.c()
+    _check("averis_split_quant", lib().averis_split_quant(
+        a.data_ptr(), _dtype_code(a), rows, cols, _lda(a), seed, rnd, ctypes.byref(r),
+        ctypes.byref(m), mu.data_ptr(), ws.data_ptr(), ws.numel(), _stream()))
+    return res, mean, mu
+
+
+def averis_split_quant_grouped(a, offsets, seed=0, rnd=SR, ws=None):
+    """Per-segment split-quant; offsets: int64 device tensor [nseg+1]."""
+    rows, cols = a.shape
+    nseg = offsets.numel() - 1
+    res = NVFP4.empty(rows, cols, nseg, a.device)
+    mean = NVFP4.empty(nseg, cols, nseg, a.device)
+    mu = torch.empty((nseg, cols), dtype=torch.float32, device=a.device)
+    need = workspace_bytes(OP_SPLIT_QUANT, rows, cols, 0, nseg)
+    ws = ws if ws is not None else _workspace(need, a.device)
+    r, m = res.c(), mean.c()
+    _check("averis_split_quant_grouped", lib().averis_split_quant_grouped(
+        a.data_ptr(), _dtype_code(a), rows, cols, _lda(a), offsets.data_ptr(), nseg, seed, rnd,
+        ctypes.byref(r), ctypes.byref(m), mu.data_ptr(), ws.data_ptr(), ws.numel(), _stream()))
+    return res, mean, mu
+
+
+def averis_quant(a, transpose=False, seed=0, rnd=SR, sr_stream=STREAM_ACT, ws=None):
+    """Plain Q4.  transpose=True quantizes a^T (blocks along a's rows)."""
+    srows, scols = a.shape
+    rows, cols = (scols, srows) if transpose else (srows, scols)
+    out = NVFP4.empty(rows, cols, 1, a.device)
+    need = workspace_bytes(OP_QUANT, rows, cols)
+    ws = ws if ws is not None else _workspace(need, a.device)
+    o = out.c()
+    _check("averis_quant", lib().averis_quant(
+        a.data_ptr(), _dtype_code(a), rows, cols, _lda(a), int(transpose), seed, rnd, sr_stream,
+        ctypes.byref(o), ws.data_ptr(), ws.numel(), _stream()))
+    return out
+
+
+def averis_quant_batched(a, transpose=False, seed=0, rnd=RN, sr_stream=STREAM_WEIGHT, ws=None):
+    """Plain Q4 of each matrix a[b] (3-D tensor), one tensor scale each."""
+    batch, srows, scols = a.shape
+    if a.stride(2) != 1:
+        raise ValueError("expected unit innermost stride")
+    rows, cols = (scols, srows) if transpose else (srows, scols)
+    out = NVFP4.empty(batch * rows, cols, batch, a.device)
+    need = workspace_bytes(OP_QUANT, rows, cols, 0, batch)
+    ws = ws if ws is not None else _workspace(need, a.device)
+    o = out.c()
+    _check("averis_quant_batched", lib().averis_quant_batched(
+        a.data_ptr(), _dtype_code(a), batch, rows, cols, a.stride(1), a.stride(0),
+        int(transpose), seed, rnd, sr_stream, ctypes.byref(o), ws.data_ptr(), ws.numel(),
+        _stream()))
+    return out
+
+
+def averis_quant_grouped(a, offsets, seed=0, rnd=SR, sr_stream=STREAM_ACT, ws=None):
+    rows, cols = a.shape
+    nseg = offsets.numel() - 1
+    out = NVFP4.empty(rows, cols, nseg, a.device)
+    need = workspace_bytes(OP_QUANT, rows, cols, 0, nseg)
+    ws = ws if ws is not None else _workspace(need, a.device)
+    o = out.c()
+    _check("averis_quant_grouped", lib().averis_quant_grouped(
+        a.data_ptr(), _dtype_code(a), rows, cols, _lda(a), offsets.data_ptr(), nseg, seed, rnd,
+        sr_stream, ctypes.byref(o), ws.data_ptr(), ws.numel(), _stream()))
+    return out
+
+
+def _out(m, n, dtype, device, out):
+    if out is not None:
+        return out
+    return torch.empty((m, n), dtype=dtype, device=device)
+
+
+def _gemm(fn, a, mean, b, out_dtype, out, nseg=1, offsets=None, ws=None):
+    m, k = a.rows, a.cols
+    n = b.rows // (nseg if offsets is not None else 1)
+    c = _out(m, n, out_dtype, a.codes.device, out)
+    need = workspace_bytes(OP_GEMM, m, k, n, nseg if offsets is not None else 0)
+    ws = ws if ws is not None else _workspace(need, a.codes.device)
+    ca, cb = a.c(), b.c()
+    cm = mean.c() if mean is not None else None
+    pm = ctypes.byref(cm) if cm is not None else None
+    cd = _dtype_code(c)
+    if fn == "averis_gemm_vanilla":
+        st = lib().averis_gemm_vanilla(ctypes.byref(ca), ctypes.byref(cb), c.data_ptr(), cd,
+                                       c.stride(0), ws.data_ptr(), ws.numel(), _stream())
+    elif fn == "averis_gemm_grouped":
+        st = lib().averis_gemm_grouped(ctypes.byref(ca), pm, ctypes.byref(cb),
+                                       offsets.data_ptr(), nseg, c.data_ptr(), cd, c.stride(0),
+                                       ws.data_ptr(), ws.numel(), _stream())
+    else:
+        st = getattr(lib(), fn)(ctypes.byref(ca), pm, ctypes.byref(cb), c.data_ptr(), cd,
+                                c.stride(0), ws.data_ptr(), ws.numel(), _stream())
+    _check(fn, st)
+    return c
+
+
+def averis_gemm_fwd(xr, mean, wt, out_dtype=torch.float32, out=None, ws=None):
+    """Y = 1 (mean W) + X_R W with wt = Q4(W^T) (n x m)."""
+    return _gemm("averis_gemm_fwd", xr, mean, wt, out_dtype, out, ws=ws)
+
+
+def averis_gemm_dgrad(dr, mean_d, w, out_dtype=torch.float32, out=None, ws=None):
+    """dX = 1 (mean_D W^T) + D_R W^T with w = Q4(W) (m x n)."""
+    return _gemm("averis_gemm_dgrad", dr, mean_d, w, out_dtype, out, ws=ws)
+
+
+def averis_gemm_vanilla(a, b, out_dtype=torch.float32, out=None, ws=None):
+    return _gemm("averis_gemm_vanilla", a, None, b, out_dtype, out, ws=ws)
+
+
+def averis_gemm_grouped(a, mean, b, offsets, out_dtype=torch.float32, out=None, ws=None):
+    nseg = offsets.numel() - 1
+    return _gemm("averis_gemm_grouped", a, mean, b, out_dtype, out, nseg=nseg, offsets=offsets,
+                 ws=ws)

@@ -1,0 +1,292 @@
+// libaveris C ABI: argument validation, workspace carve-up and launches.
+// Every check runs before the first HIP call, so a rejected call touches no
+// device state and the checks can be exercised on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/averis.h"
+#include "launch.hpp"
+#include "segments.hpp"
+
+using namespace averis;
+
+namespace {
+
+constexpr int kMaxSeg = 4096;
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+inline size_t elem_size(averis_dtype_t d) { return d == AVERIS_BF16 ? 2 : 4; }
+inline bool dtype_ok(averis_dtype_t d) { return d == AVERIS_F32 || d == AVERIS_BF16; }
+
+averis_status_t check_tensor(const averis_nvfp4_t* t, int64_t rows, int64_t cols) {
+  if (!t || !t->tscale) return AVERIS_E_NULL;
+  if (t->rows != rows || t->cols != cols) return AVERIS_E_SHAPE;
+  if (rows > 0 && (!t->codes || !t->scales)) return AVERIS_E_NULL;
+  if (!aligned(t->codes, 16) || !aligned(t->tscale, 4)) return AVERIS_E_ALIGN;
+  return AVERIS_OK;
+}
+
+averis_status_t check_input(const void* a, averis_dtype_t dtype, int64_t rows, int64_t cols,
+                            int64_t lda, int64_t min_lda) {
+  if (!dtype_ok(dtype)) return AVERIS_E_DTYPE;
+  if (rows < 0 || cols <= 0 || (cols % 16) != 0) return AVERIS_E_SHAPE;
+  if (lda < min_lda) return AVERIS_E_SHAPE;
+  if (rows > 0 && !a) return AVERIS_E_NULL;
+  if (!aligned(a, 16) || ((size_t)lda * elem_size(dtype)) % 16 != 0) return AVERIS_E_ALIGN;
+  return AVERIS_OK;
+}
+
+inline averis_status_t hip_status(hipError_t e) { return e == hipSuccess ? AVERIS_OK : AVERIS_E_HIP; }
+
+}  // namespace
+
+namespace averis {
+
+size_t split_ws_bytes(int64_t rows, int64_t cols, int nseg) {
+  const int ns = nseg > 0 ? nseg : 1;
+  const int64_t nch = chunk_upper_bound(rows, nseg > 0 ? nseg : 1, kStatsRows);
+  const int64_t ct_s = (cols + 511) / 512, ct_f = (cols + 255) / 256;
+  size_t b = 0;
+  b += align256((size_t)(nch * cols * 8));      // psum
+  b += align256((size_t)(nch * cols * 4)) * 2;  // pmax, pmin
+  b += align256((size_t)(nch * ct_s * 4));      // pamax
+  b += align256((size_t)(ns * cols * 4));       // mu
+  b += align256((size_t)(ns * (ct_f > 1 ? ct_f : 1) * 4)) * 2;  // tmax_r, tmax_mu
+  return b;
+}
+
+SplitWs split_ws_carve(void* ws, int64_t rows, int64_t cols, int nseg) {
+  const int ns = nseg > 0 ? nseg : 1;
+  const int64_t nch = chunk_upper_bound(rows, nseg > 0 ? nseg : 1, kStatsRows);
+  const int64_t ct_s = (cols + 511) / 512, ct_f = (cols + 255) / 256;
+  char* p = static_cast<char*>(ws);
+  SplitWs w;
+  w.psum = reinterpret_cast<double*>(p); p += align256((size_t)(nch * cols * 8));
+  w.pmax = reinterpret_cast<float*>(p);  p += align256((size_t)(nch * cols * 4));
+  w.pmin = reinterpret_cast<float*>(p);  p += align256((size_t)(nch * cols * 4));
+  w.pamax = reinterpret_cast<float*>(p); p += align256((size_t)(nch * ct_s * 4));
+  w.mu = reinterpret_cast<float*>(p);    p += align256((size_t)(ns * cols * 4));
+  w.tmax_r = reinterpret_cast<float*>(p); p += align256((size_t)(ns * (ct_f > 1 ? ct_f : 1) * 4));
+  w.tmax_mu = reinterpret_cast<float*>(p);
+  return w;
+}
+
+size_t batched_ws_bytes(int64_t, int64_t, int batch) {
+  return align256((size_t)(batch > 0 ? batch : 1) * (size_t)kAmaxBlocks * 4);
+}
+
+}  // namespace averis
+
+extern "C" {
+
+size_t averis_workspace_bytes(averis_op_t op, int64_t rows, int64_t cols, int64_t n, int64_t nseg) {
+  if (rows < 0 || cols <= 0 || cols % 16 != 0 || nseg < 0 || nseg > kMaxSeg) return 0;
+  switch (op) {
+    case AVERIS_OP_SPLIT_QUANT:
+      return split_ws_bytes(rows, cols, (int)nseg);
+    case AVERIS_OP_QUANT: {
+      const size_t a = split_ws_bytes(rows, cols, (int)nseg);
+      const size_t b = batched_ws_bytes(rows, cols, (int)nseg);
+      return a > b ? a : b;
+    }
+    case AVERIS_OP_GEMM:
+      if (n < 0) return 0;
+      return gemm_ws_bytes(n, (int)nseg);
+  }
+  return 0;
+}
+
+const char* averis_status_str(averis_status_t s) {
+  switch (s) {
+    case AVERIS_OK: return "ok";
+    case AVERIS_E_NULL: return "a required pointer is NULL";
+    case AVERIS_E_SHAPE: return "invalid or mismatched shape";
+    case AVERIS_E_DTYPE: return "unsupported dtype";
+    case AVERIS_E_ALIGN: return "misaligned pointer or leading dimension";
+    case AVERIS_E_WORKSPACE: return "workspace missing or too small";
+    case AVERIS_E_ARG: return "invalid argument";
+    case AVERIS_E_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int averis_abi_version(void) { return AVERIS_ABI_VERSION; }
+
+static averis_status_t split_common(const void* a, averis_dtype_t dtype, int64_t rows,
+                                    int64_t cols, int64_t lda, const int64_t* offs, int nseg,
+                                    uint64_t seed, averis_round_t rnd,
+                                    const averis_nvfp4_t* residual, const averis_nvfp4_t* mean,
+                                    float* mean_f32, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  averis_status_t s = check_input(a, dtype, rows, cols, lda, cols);
+  if (s != AVERIS_OK) return s;
+  if (rnd != AVERIS_RN && rnd != AVERIS_SR) return AVERIS_E_ARG;
+  if (nseg < 1 || nseg > kMaxSeg) return AVERIS_E_ARG;
+  if ((s = check_tensor(residual, rows, cols)) != AVERIS_OK) return s;
+  if ((s = check_tensor(mean, offs ? nseg : 1, cols)) != AVERIS_OK) return s;
+  if (!aligned(mean_f32, 4)) return AVERIS_E_ALIGN;
+  const size_t need = split_ws_bytes(rows, cols, nseg);
+  if (!ws || ws_bytes < need) return AVERIS_E_WORKSPACE;
+  if (!aligned(ws, 256)) return AVERIS_E_ALIGN;
+  const SplitWs w = split_ws_carve(ws, rows, cols, nseg);
+  const QuantOut ro{residual->codes, residual->scales, residual->tscale};
+  const QuantOut mo{mean->codes, mean->scales, mean->tscale};
+  return hip_status(launch_split_or_plain(a, dtype == AVERIS_BF16, rows, cols, lda, offs, nseg,
+                                          true, rnd == AVERIS_SR, seed, 0u, ro, &mo, mean_f32, w,
+                                          stream));
+}
+
+averis_status_t averis_split_quant(const void* a, averis_dtype_t dtype, int64_t rows, int64_t cols,
+                                   int64_t lda, uint64_t seed, averis_round_t rnd,
+                                   const averis_nvfp4_t* residual, const averis_nvfp4_t* mean,
+                                   float* mean_f32, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  return split_common(a, dtype, rows, cols, lda, nullptr, 1, seed, rnd, residual, mean, mean_f32,
+                      ws, ws_bytes, stream);
+}
+
+averis_status_t averis_split_quant_grouped(const void* a, averis_dtype_t dtype, int64_t rows,
+                                           int64_t cols, int64_t lda, const int64_t* seg_offsets,
+                                           int nseg, uint64_t seed, averis_round_t rnd,
+                                           const averis_nvfp4_t* residual,
+                                           const averis_nvfp4_t* mean, float* mean_f32, void* ws,
+                                           size_t ws_bytes, hipStream_t stream) {
+  if (!seg_offsets) return AVERIS_E_NULL;
+  if (!aligned(seg_offsets, 8)) return AVERIS_E_ALIGN;
+  return split_common(a, dtype, rows, cols, lda, seg_offsets, nseg, seed, rnd, residual, mean,
+                      mean_f32, ws, ws_bytes, stream);
+}
+
+static averis_status_t quant_common(const void* a, averis_dtype_t dtype, int64_t rows,
+                                    int64_t cols, int64_t lda, const int64_t* offs, int nseg,
+                                    uint64_t seed, averis_round_t rnd, uint32_t sr_stream,
+                                    const averis_nvfp4_t* out, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  averis_status_t s = check_input(a, dtype, rows, cols, lda, cols);
+  if (s != AVERIS_OK) return s;
+  if (rnd != AVERIS_RN && rnd != AVERIS_SR) return AVERIS_E_ARG;
+  if (sr_stream > 0xFFFFu || nseg < 1 || nseg > kMaxSeg) return AVERIS_E_ARG;
+  if ((s = check_tensor(out, rows, cols)) != AVERIS_OK) return s;
+  const size_t need = split_ws_bytes(rows, cols, nseg);
+  if (!ws || ws_bytes < need) return AVERIS_E_WORKSPACE;
+  if (!aligned(ws, 256)) return AVERIS_E_ALIGN;
+  const SplitWs w = split_ws_carve(ws, rows, cols, nseg);
+  const QuantOut o{out->codes, out->scales, out->tscale};
+  return hip_status(launch_split_or_plain(a, dtype == AVERIS_BF16, rows, cols, lda, offs, nseg,
+                                          false, rnd == AVERIS_SR, seed, sr_stream, o, nullptr,
+                                          nullptr, w, stream));
+}
+
+averis_status_t averis_quant_batched(const void* a, averis_dtype_t dtype, int batch, int64_t rows,
+                                     int64_t cols, int64_t lda, int64_t batch_stride,
+                                     int transpose, uint64_t seed, averis_round_t rnd,
+                                     uint32_t sr_stream, const averis_nvfp4_t* out, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return AVERIS_E_DTYPE;
+  if (batch < 1 || batch > kMaxSeg) return AVERIS_E_ARG;
+  if (transpose != 0 && transpose != 1) return AVERIS_E_ARG;
+  if (rnd != AVERIS_RN && rnd != AVERIS_SR) return AVERIS_E_ARG;
+  if (sr_stream > 0xFFFFu) return AVERIS_E_ARG;
+  if (rows < 0 || cols <= 0 || cols % 16 != 0) return AVERIS_E_SHAPE;
+  const int64_t scols = transpose ? rows : cols, srows = transpose ? cols : rows;
+  if (lda < scols || batch_stride < 0) return AVERIS_E_SHAPE;
+  if (batch > 1 && batch_stride < srows * lda) return AVERIS_E_SHAPE;
+  if (rows > 0 && !a) return AVERIS_E_NULL;
+  if (!aligned(a, elem_size(dtype))) return AVERIS_E_ALIGN;
+  averis_status_t s = check_tensor(out, (int64_t)batch * rows, cols);
+  if (s != AVERIS_OK) return s;
+  const size_t need = batched_ws_bytes(rows, cols, batch);
+  if (!ws || ws_bytes < need) return AVERIS_E_WORKSPACE;
+  if (!aligned(ws, 256)) return AVERIS_E_ALIGN;
+  const QuantOut o{out->codes, out->scales, out->tscale};
+  return hip_status(launch_quant_batched(a, dtype == AVERIS_BF16, batch, rows, cols, lda,
+                                         batch_stride, transpose, rnd == AVERIS_SR, seed,
+                                         sr_stream, o, static_cast<float*>(ws), stream));
+}
+
+averis_status_t averis_quant(const void* a, averis_dtype_t dtype, int64_t rows, int64_t cols,
+                             int64_t lda, int transpose, uint64_t seed, averis_round_t rnd,
+                             uint32_t sr_stream, const averis_nvfp4_t* out, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  if (transpose == 1)
+    return averis_quant_batched(a, dtype, 1, rows, cols, lda, 0, 1, seed, rnd, sr_stream, out, ws,
+                                ws_bytes, stream);
+  if (transpose != 0) return AVERIS_E_ARG;
+  return quant_common(a, dtype, rows, cols, lda, nullptr, 1, seed, rnd, sr_stream, out, ws,
+                      ws_bytes, stream);
+}
+
+averis_status_t averis_quant_grouped(const void* a, averis_dtype_t dtype, int64_t rows,
+                                     int64_t cols, int64_t lda, const int64_t* seg_offsets,
+                                     int nseg, uint64_t seed, averis_round_t rnd,
+                                     uint32_t sr_stream, const averis_nvfp4_t* out, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  if (!seg_offsets) return AVERIS_E_NULL;
+  if (!aligned(seg_offsets, 8)) return AVERIS_E_ALIGN;
+  return quant_common(a, dtype, rows, cols, lda, seg_offsets, nseg, seed, rnd, sr_stream, out, ws,
+                      ws_bytes, stream);
+}
+
+static averis_status_t gemm_common(const averis_nvfp4_t* a, const averis_nvfp4_t* mean,
+                                   const averis_nvfp4_t* b, const int64_t* offs, int nseg,
+                                   void* c, averis_dtype_t cdtype, int64_t ldc, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  if (!a || !b) return AVERIS_E_NULL;
+  if (!dtype_ok(cdtype)) return AVERIS_E_DTYPE;
+  if (nseg < 1 || nseg > kMaxSeg) return AVERIS_E_ARG;
+  const int64_t m = a->rows, k = a->cols;
+  if (m < 0 || k <= 0 || k % 16 != 0 || b->cols != k) return AVERIS_E_SHAPE;
+  const int64_t ns = offs ? nseg : 1;
+  if (b->rows < 0 || b->rows % ns != 0) return AVERIS_E_SHAPE;
+  const int64_t n = b->rows / ns;
+  averis_status_t s;
+  if ((s = check_tensor(a, m, k)) != AVERIS_OK) return s;
+  if ((s = check_tensor(b, b->rows, k)) != AVERIS_OK) return s;
+  if (mean && (s = check_tensor(mean, ns, k)) != AVERIS_OK) return s;
+  if (ldc < n) return AVERIS_E_SHAPE;
+  if (m > 0 && n > 0 && !c) return AVERIS_E_NULL;
+  if (!aligned(c, elem_size(cdtype))) return AVERIS_E_ALIGN;
+  const size_t need = mean ? gemm_ws_bytes(n, (int)ns) : 0;
+  if (need && (!ws || ws_bytes < need)) return AVERIS_E_WORKSPACE;
+  if (ws && !aligned(ws, 256)) return AVERIS_E_ALIGN;
+  const QOperand qa{a->codes, a->scales, a->tscale};
+  const QOperand qb{b->codes, b->scales, b->tscale};
+  QOperand qm{};
+  if (mean) qm = QOperand{mean->codes, mean->scales, mean->tscale};
+  return hip_status(launch_gemm(qa, mean ? &qm : nullptr, qb, m, n, k, offs, nseg, c,
+                                cdtype == AVERIS_BF16, ldc, static_cast<float*>(ws), stream));
+}
+
+averis_status_t averis_gemm_fwd(const averis_nvfp4_t* xr, const averis_nvfp4_t* mean,
+                                const averis_nvfp4_t* wt, void* y, averis_dtype_t ydtype,
+                                int64_t ldy, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!mean) return AVERIS_E_NULL;
+  return gemm_common(xr, mean, wt, nullptr, 1, y, ydtype, ldy, ws, ws_bytes, stream);
+}
+
+averis_status_t averis_gemm_dgrad(const averis_nvfp4_t* dr, const averis_nvfp4_t* mean_d,
+                                  const averis_nvfp4_t* w, void* dx, averis_dtype_t dxdtype,
+                                  int64_t lddx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!mean_d) return AVERIS_E_NULL;
+  return gemm_common(dr, mean_d, w, nullptr, 1, dx, dxdtype, lddx, ws, ws_bytes, stream);
+}
+
+averis_status_t averis_gemm_vanilla(const averis_nvfp4_t* a, const averis_nvfp4_t* b, void* c,
+                                    averis_dtype_t cdtype, int64_t ldc, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  return gemm_common(a, nullptr, b, nullptr, 1, c, cdtype, ldc, ws, ws_bytes, stream);
+}
+
+averis_status_t averis_gemm_grouped(const averis_nvfp4_t* a, const averis_nvfp4_t* mean,
+                                    const averis_nvfp4_t* b, const int64_t* seg_offsets, int nseg,
+                                    void* c, averis_dtype_t cdtype, int64_t ldc, void* ws,
+                                    size_t ws_bytes, hipStream_t stream) {
+  if (!seg_offsets) return AVERIS_E_NULL;
+  if (!aligned(seg_offsets, 8)) return AVERIS_E_ALIGN;
+  return gemm_common(a, mean, b, seg_offsets, nseg, c, cdtype, ldc, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

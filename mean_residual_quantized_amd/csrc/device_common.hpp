@@ -1,0 +1,148 @@
+// Device helpers shared by the libaveris kernels (gfx950): counter-based RNG,
+// the E4M3 scale codec and the E2M1 element rounding of the NVFP4-style Q4.
+//
+// Every operation that decides a code or a scale byte is a single IEEE fp32
+// operation with round-to-nearest-even, in the order the format definition
+// states (no contraction; this file is built with -ffp-contract=off).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace averis {
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon et al., "Parallel random numbers: as easy as 1, 2, 3",
+// SC'11): 10 rounds of two 32x32->64-bit multiplies and key mixing.  Each call
+// gives 128 bits = eight 16-bit draws, for elements 8g .. 8g+7.
+// ---------------------------------------------------------------------------
+struct u32x4 {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ u32x4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                           uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
+    const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return {c0, c1, c2, c3};
+}
+
+// 16-bit draw j (0..7) of a Philox block: word j >> 1, low half for even j.
+__device__ __forceinline__ uint32_t draw16(const u32x4& r, int j) {
+  const uint32_t w = (j >> 1) == 0 ? r.x : (j >> 1) == 1 ? r.y : (j >> 1) == 2 ? r.z : r.w;
+  return (j & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+// ---------------------------------------------------------------------------
+// E4M3FN scale codec: bias 7, 3 mantissa bits, max 448, subnormals m * 2^-9.
+// ---------------------------------------------------------------------------
+
+// s: finite, >= 0, already capped at 448.  Round-to-nearest-even.
+__device__ __forceinline__ uint32_t e4m3_encode(float s) {
+  if (s < 0.015625f) {                       // below 2^-6: subnormal quanta of 2^-9
+    return (uint32_t)__builtin_rintf(s * 512.0f);   // exact scaling; 8 -> 2^-6 = 0x08
+  }
+  const uint32_t b = __float_as_uint(s);
+  // round the 23-bit mantissa to 3 bits, ties to even, carrying into the exponent
+  const uint32_t r = (b + 0x7FFFFu + ((b >> 20) & 1u)) & ~0xFFFFFu;
+  const uint32_t e = (r >> 23) - 127u + 7u;
+  const uint32_t code = (e << 3) | ((r >> 20) & 7u);
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  if (e == 0) return (float)m * 0.001953125f;            // m * 2^-9
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1 + m/8) 2^(e-7)
+}
+
+// ---------------------------------------------------------------------------
+// E2M1 element rounding.  Magnitudes by index: 0, .5, 1, 1.5, 2, 3, 4, 6.
+// Input v = t * e_b (fp32); output 4-bit code sign << 3 | index.
+// ---------------------------------------------------------------------------
+
+// Round to nearest, ties to the even index, saturating at 6.
+__device__ __forceinline__ uint32_t e2m1_rn(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
+  const float a = __builtin_fminf(__builtin_fabsf(v), 6.0f);
+  uint32_t idx;
+  if (a < 1.0f) {
+    idx = (uint32_t)__builtin_rintf(a * 2.0f);      // 0, 1 or 2 (= 1.0)
+  } else {
+    const uint32_t b = __float_as_uint(a);
+    // keep one mantissa bit, ties to even; the index is bits 30:22 - 252
+    const uint32_t r = b + 0x1FFFFFu + ((b >> 22) & 1u);
+    idx = (r >> 22) - 252u;
+  }
+  return sign | idx;
+}
+
+// Stochastic rounding with a 16-bit draw u: lo is the largest grid point
+// <= |v|, hi the next; round up iff u < 2^16 (|v| - lo) / (hi - lo).
+__device__ __forceinline__ uint32_t e2m1_sr(float v, uint32_t u) {
+  const uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
+  const float a = __builtin_fminf(__builtin_fabsf(v), 6.0f);
+  uint32_t idx;
+  if (a < 1.0f) {
+    // gap 0.5: 2^16 (a - lo) / 0.5 = a * 2^17 - lo * 2^17, both exact
+    const uint32_t lo = a >= 0.5f ? 1u : 0u;
+    const float t = a * 131072.0f - (lo ? 65536.0f : 0.0f);
+    idx = lo + ((float)u < t ? 1u : 0u);
+  } else {
+    // gap = 2^(E-1): the fraction of the gap is the low 22 mantissa bits, so
+    // u < 2^16 * R / 2^22  <=>  u * 64 < R, exactly
+    const uint32_t b = __float_as_uint(a);
+    const uint32_t rem = b & 0x3FFFFFu;
+    idx = (b >> 22) - 252u + ((u << 6) < rem ? 1u : 0u);
+  }
+  return sign | idx;
+}
+
+// ---------------------------------------------------------------------------
+// Tensor scale from the tensor's max magnitude.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void tensor_scales(float amax, float& s_enc, float& s_dec) {
+  float e = 1.0f;
+  if (amax > 0.0f) {
+    e = 2688.0f / amax;
+    if (!__builtin_isfinite(e)) e = 1.0f;
+  }
+  s_enc = e;
+  s_dec = 1.0f / e;
+}
+
+// Block scale byte and element factor from the block's max magnitude.
+__device__ __forceinline__ void block_scale(float amax_b, float s_enc, uint32_t& code, float& e_b) {
+  float s = amax_b / 6.0f;
+  s = s * s_enc;
+  s = __builtin_fminf(s, 448.0f);
+  code = e4m3_encode(s);
+  const float d = e4m3_decode(code);
+  e_b = d > 0.0f ? s_enc / d : 0.0f;
+}
+
+// bf16 bits -> fp32 (exact)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Order-preserving map of fp32 to uint32 (for max/min via unsigned compares).
+__device__ __forceinline__ uint32_t f32_ordered(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float f32_from_ordered(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+}  // namespace averis

@@ -1,0 +1,62 @@
+// Internal interface between the C ABI (api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace averis {
+
+// rows per chunk of the stats and quant passes
+constexpr int64_t kStatsRows = 128;
+constexpr int64_t kQuantRows = 16;
+// cap on the blocks of the weight amax pass
+constexpr int64_t kAmaxBlocks = 1024;
+
+struct QuantOut {
+  uint8_t* codes;
+  uint8_t* scales;
+  float* tscale;
+};
+
+// Workspace carve-up of the split / plain quant passes.
+struct SplitWs {
+  double* psum;    // [chunks][cols] partial column sums
+  float* pmax;     // [chunks][cols]
+  float* pmin;     // [chunks][cols]
+  float* pamax;    // [chunks][col tiles] plain-pass max |a|
+  float* mu;       // [nseg][cols]
+  float* tmax_r;   // [nseg][col tiles] residual max |r| per column tile
+  float* tmax_mu;  // [nseg][col tiles] max |mu| per column tile
+};
+
+size_t split_ws_bytes(int64_t rows, int64_t cols, int nseg);
+SplitWs split_ws_carve(void* ws, int64_t rows, int64_t cols, int nseg);
+size_t batched_ws_bytes(int64_t rows, int64_t cols, int batch);
+
+hipError_t launch_split_or_plain(const void* a, bool bf16, int64_t rows, int64_t cols,
+                                 int64_t lda, const int64_t* offs, int nseg, bool split, bool sr,
+                                 uint64_t seed, uint32_t stream_id, const QuantOut& out,
+                                 const QuantOut* mean, float* mean_f32, const SplitWs& ws,
+                                 hipStream_t st);
+
+hipError_t launch_quant_batched(const void* a, bool bf16, int batch, int64_t rows, int64_t cols,
+                                int64_t lda, int64_t bstride, int transpose, bool sr,
+                                uint64_t seed, uint32_t stream_id, const QuantOut& out,
+                                float* part, hipStream_t st);
+
+// A quantized GEMM operand as the kernels see it.
+struct QOperand {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* tscale;
+};
+
+// C[M x N] = deq(A) deq(B)^T (+ 1 deq(mean) deq(B)^T); grouped when offs != nullptr
+// (B then holds nseg stacked N x K matrices).
+hipError_t launch_gemm(const QOperand& a, const QOperand* mean, const QOperand& b, int64_t m,
+                       int64_t n, int64_t k, const int64_t* offs, int nseg, void* c, bool c_bf16,
+                       int64_t ldc, float* rho_ws, hipStream_t st);
+
+size_t gemm_ws_bytes(int64_t n, int nseg);
+
+}  // namespace averis

@@ -1,0 +1,493 @@
+// Split-quant and plain quant kernels for gfx950.
+//
+// Averis split ("Lighthouse" review §2.1-§2.2; gist.science summary §2):
+//   mu_j = (1/l) sum_i a_ij over a segment's rows, X_R = X - 1 mu^T, and
+//   Q4(X_R), Q4(mu) quantized separately (NVFP4-style, 16-blocks along cols).
+//
+// Three launches per call:
+//   stats     one pass over A: per row-chunk partial column sums (fp64), max
+//             and min (split), or per-chunk max |a| (plain)
+//   finalize  (split) per column: mu = fp32(fp64(sum) / l), and the column's
+//             max |fp32(a - mu)| = max(fp32(max - mu), fp32(mu - min)) (fp32
+//             subtraction is monotone), reduced per column tile
+//   quant     per 16-block: residual, block amax, E4M3 scale, Philox SR or RN,
+//             packed nibbles; extra workgroups quantize the mean vectors
+// Partial sums are exact in fp64 for inputs whose column dynamic range fits
+// 53 bits (always for the bf16 workloads here), so their order does not
+// change the mean.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+#include "segments.hpp"
+
+namespace averis {
+
+// ---------------------------------------------------------------------------
+// element loads: 8 consecutive columns as fp32
+// ---------------------------------------------------------------------------
+template <typename T>
+struct Load8;
+
+template <>
+struct Load8<uint16_t> {  // bf16
+  static __device__ __forceinline__ void run(const uint16_t* p, float* v) {
+    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+    v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+    v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+  }
+};
+
+template <>
+struct Load8<float> {
+  static __device__ __forceinline__ void run(const float* p, float* v) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+  // max over the 256 threads of a block
+  for (int d = 32; d > 0; d >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, d, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+  __syncthreads();
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// stats: block = 64 column-octets (512 columns) x 4 row lanes; one row chunk
+// ---------------------------------------------------------------------------
+template <typename T, bool SPLIT>
+__global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t rows, int64_t cols,
+                                               int64_t lda, const int64_t* offs, int nseg,
+                                               double* __restrict__ psum,
+                                               float* __restrict__ pmax,
+                                               float* __restrict__ pmin,
+                                               float* __restrict__ pamax) {
+  const SegRange sr = locate_chunk(offs, nseg, rows, kStatsRows, blockIdx.y);
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int64_t c = (int64_t)blockIdx.x * 512 + tx * 8;
+  const bool active = sr.seg >= 0 && c < cols;
+
+  double s[8];
+  float mx[8], mn[8];
+  float am = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    s[k] = 0.0;
+    mx[k] = -__builtin_inff();
+    mn[k] = __builtin_inff();
+  }
+  if (active) {
+    for (int64_t r = sr.r0 + ty; r < sr.r1; r += 4) {
+      float v[8];
+      Load8<T>::run(a + r * lda + c, v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (SPLIT) {
+          s[k] += (double)v[k];
+          mx[k] = __builtin_fmaxf(mx[k], v[k]);
+          mn[k] = __builtin_fminf(mn[k], v[k]);
+        } else {
+          am = __builtin_fmaxf(am, __builtin_fabsf(v[k]));
+        }
+      }
+    }
+  }
+  if (SPLIT) {
+    __shared__ double ls[4][512];
+    __shared__ float lmx[4][512], lmn[4][512];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      ls[ty][tx * 8 + k] = s[k];
+      lmx[ty][tx * 8 + k] = mx[k];
+      lmn[ty][tx * 8 + k] = mn[k];
+    }
+    __syncthreads();
+    if (sr.seg >= 0) {
+      for (int j = threadIdx.x; j < 512; j += 256) {
+        const int64_t col = (int64_t)blockIdx.x * 512 + j;
+        if (col < cols) {
+          const double t = ls[0][j] + ls[1][j] + ls[2][j] + ls[3][j];
+          const float m1 = __builtin_fmaxf(__builtin_fmaxf(lmx[0][j], lmx[1][j]),
+                                           __builtin_fmaxf(lmx[2][j], lmx[3][j]));
+          const float m0 = __builtin_fminf(__builtin_fminf(lmn[0][j], lmn[1][j]),
+                                           __builtin_fminf(lmn[2][j], lmn[3][j]));
+          const int64_t o = (int64_t)blockIdx.y * cols + col;
+          psum[o] = t;
+          pmax[o] = m1;
+          pmin[o] = m0;
+        }
+      }
+    }
+  } else {
+    __shared__ float red[4];
+    am = block_max(am, red);
+    if (threadIdx.x == 0) pamax[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = am;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// finalize (split): thread per column, block per (256 columns, segment)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_finalize(int64_t rows, int64_t cols, const int64_t* offs,
+                                                  int nseg, const double* __restrict__ psum,
+                                                  const float* __restrict__ pmax,
+                                                  const float* __restrict__ pmin,
+                                                  float* __restrict__ mu,
+                                                  float* __restrict__ mean_out,
+                                                  float* __restrict__ tmax_r,
+                                                  float* __restrict__ tmax_mu) {
+  const int seg = blockIdx.y;
+  const SegRange sr = describe_segment(offs, nseg, rows, kStatsRows, seg);
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  float rmax = 0.0f, amu = 0.0f;
+  if (j < cols) {
+    double s = 0.0;
+    float m1 = -__builtin_inff(), m0 = __builtin_inff();
+    for (int64_t ck = sr.c0; ck < sr.c1; ++ck) {
+      s += psum[ck * cols + j];
+      m1 = __builtin_fmaxf(m1, pmax[ck * cols + j]);
+      m0 = __builtin_fminf(m0, pmin[ck * cols + j]);
+    }
+    const int64_t l = sr.seg_r1 - sr.seg_r0;
+    float m = 0.0f;
+    if (l > 0) {
+      m = (float)(s / (double)l);
+      rmax = __builtin_fmaxf(m1 - m, m - m0);
+    }
+    mu[(int64_t)seg * cols + j] = m;
+    if (mean_out) mean_out[(int64_t)seg * cols + j] = m;
+    amu = __builtin_fabsf(m);
+  }
+  __shared__ float red[4];
+  rmax = block_max(rmax, red);
+  amu = block_max(amu, red);
+  if (threadIdx.x == 0) {
+    tmax_r[(int64_t)seg * gridDim.x + blockIdx.x] = rmax;
+    tmax_mu[(int64_t)seg * gridDim.x + blockIdx.x] = amu;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// quantize one 16-block held in registers; writes 8 code bytes and 1 scale
+// ---------------------------------------------------------------------------
+template <bool SR>
+__device__ __forceinline__ void quant_block16(const float* r, float s_enc, uint64_t idx0,
+                                              uint32_t k0, uint32_t k1, uint32_t stream,
+                                              uint8_t* codes, uint8_t* scale) {
+  float amax_b = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) amax_b = __builtin_fmaxf(amax_b, __builtin_fabsf(r[k]));
+  uint32_t sc;
+  float e_b;
+  block_scale(amax_b, s_enc, sc, e_b);
+  uint32_t q[16];
+  if (SR) {
+    const uint64_t g = idx0 >> 3;   // idx0 is a multiple of 16
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint64_t gg = g + h;
+      const u32x4 rr = philox10((uint32_t)gg, (uint32_t)(gg >> 32), stream, 0u, k0, k1);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) q[h * 8 + k] = e2m1_sr(r[h * 8 + k] * e_b, draw16(rr, k));
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) q[k] = e2m1_rn(r[k] * e_b);
+  }
+  uint2 packed;
+  packed.x = q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12) | (q[4] << 16) | (q[5] << 20) |
+             (q[6] << 24) | (q[7] << 28);
+  packed.y = q[8] | (q[9] << 4) | (q[10] << 8) | (q[11] << 12) | (q[12] << 16) | (q[13] << 20) |
+             (q[14] << 24) | (q[15] << 28);
+  *reinterpret_cast<uint2*>(codes) = packed;
+  *scale = (uint8_t)sc;
+}
+
+// max over a segment's per-tile partial maxima (all threads get it)
+__device__ __forceinline__ float reduce_partials(const float* p, int64_t n) {
+  __shared__ float red[4];
+  float m = 0.0f;
+  for (int64_t i = threadIdx.x; i < n; i += 256) m = __builtin_fmaxf(m, p[i]);
+  return block_max(m, red);
+}
+
+// ---------------------------------------------------------------------------
+// quant: block = 64 column-blocks (1024 columns) x 4 row lanes over a chunk
+// of kQuantRows rows; blockIdx.y >= nchunk_ub quantizes segment means.
+// ---------------------------------------------------------------------------
+template <typename T, bool SPLIT, bool SR>
+__global__ __launch_bounds__(256) void k_quant(const T* __restrict__ a, int64_t rows, int64_t cols,
+                                               int64_t lda, const int64_t* offs, int nseg,
+                                               int64_t nchunk_ub, uint64_t seed, uint32_t stream,
+                                               const float* __restrict__ mu,
+                                               const float* __restrict__ tmax,  // per segment
+                                               int64_t ntmax,
+                                               const float* __restrict__ tmax_mu,
+                                               int64_t ntmax_mu,
+                                               uint8_t* __restrict__ codes,
+                                               uint8_t* __restrict__ scales,
+                                               float* __restrict__ tscale,
+                                               uint8_t* __restrict__ mcodes,
+                                               uint8_t* __restrict__ mscales,
+                                               float* __restrict__ mtscale) {
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int64_t nb = cols >> 4;
+  const int64_t b = (int64_t)blockIdx.x * 64 + tx;   // 16-block index within a row
+
+  if (SPLIT && (int64_t)blockIdx.y >= nchunk_ub) {
+    // mean vector of one segment: 1 x cols, SR stream 1, index seg*cols + col
+    const int seg = (int)((int64_t)blockIdx.y - nchunk_ub);
+    const float am = reduce_partials(tmax_mu + (int64_t)seg * ntmax_mu, ntmax_mu);
+    float s_enc, s_dec;
+    tensor_scales(am, s_enc, s_dec);
+    if (blockIdx.x == 0) {
+      // this segment's residual tensor scale too (written even when the
+      // segment is empty and no chunk exists)
+      const float amr = reduce_partials(tmax + (int64_t)seg * ntmax, ntmax);
+      float r_enc, r_dec;
+      tensor_scales(amr, r_enc, r_dec);
+      if (threadIdx.x == 0) {
+        mtscale[2 * seg] = s_enc;
+        mtscale[2 * seg + 1] = s_dec;
+        tscale[2 * seg] = r_enc;
+        tscale[2 * seg + 1] = r_dec;
+      }
+    }
+    if (ty == 0 && b < nb) {
+      float r[16];
+      const float* m = mu + (int64_t)seg * cols + b * 16;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) r[k] = m[k];
+      const uint64_t idx0 = (uint64_t)seg * (uint64_t)cols + (uint64_t)b * 16;
+      quant_block16<SR>(r, s_enc, idx0, k0, k1, 1u, mcodes + (int64_t)seg * (cols >> 1) + b * 8,
+                        mscales + (int64_t)seg * nb + b);
+    }
+    return;
+  }
+
+  const SegRange sr = locate_chunk(offs, nseg, rows, kQuantRows, blockIdx.y);
+  if (sr.seg < 0) return;
+  const float am = reduce_partials(tmax + (int64_t)sr.seg * ntmax, ntmax);
+  float s_enc, s_dec;
+  tensor_scales(am, s_enc, s_dec);
+  if (b >= nb) return;
+  float m[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) m[k] = 0.0f;
+  if (SPLIT) {
+    const float* mp = mu + (int64_t)sr.seg * cols + b * 16;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) m[k] = mp[k];
+  }
+  for (int64_t row = sr.r0 + ty; row < sr.r1; row += 4) {
+    float v[16];
+    const T* p = a + row * lda + b * 16;
+    Load8<T>::run(p, v);
+    Load8<T>::run(p + 8, v + 8);
+    if (SPLIT) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = v[k] - m[k];
+    }
+    const uint64_t idx0 = (uint64_t)row * (uint64_t)cols + (uint64_t)b * 16;
+    quant_block16<SR>(v, s_enc, idx0, k0, k1, stream, codes + row * (cols >> 1) + b * 8,
+                      scales + row * nb + b);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// plain quant of any-orientation, batched tensors (weights)
+//   logical T_b[r][c] = a[b*bstride + r*lda + c]     (transpose = 0)
+//                     = a[b*bstride + c*lda + r]     (transpose = 1)
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ float load1(const T* p);
+template <>
+__device__ __forceinline__ float load1<uint16_t>(const uint16_t* p) {
+  return __uint_as_float((uint32_t)(*p) << 16);
+}
+template <>
+__device__ __forceinline__ float load1<float>(const float* p) { return *p; }
+
+// amax over the stored matrix of each batch entry (stored rows x stored cols)
+template <typename T>
+__global__ __launch_bounds__(256) void k_amax_batched(const T* __restrict__ a, int64_t srows,
+                                                      int64_t scols, int64_t lda, int64_t bstride,
+                                                      float* __restrict__ part) {
+  const T* base = a + (int64_t)blockIdx.y * bstride;
+  const int64_t n = srows * scols;
+  float m = 0.0f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / scols, c = i - r * scols;
+    m = __builtin_fmaxf(m, __builtin_fabsf(load1<T>(base + r * lda + c)));
+  }
+  __shared__ float red[4];
+  m = block_max(m, red);
+  if (threadIdx.x == 0) part[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = m;
+}
+
+// thread per (logical row r, 16-block cb); blockIdx.z = batch entry
+template <typename T, bool SR>
+__global__ __launch_bounds__(256) void k_quant_batched(const T* __restrict__ a, int64_t rows,
+                                                       int64_t cols, int64_t lda, int64_t bstride,
+                                                       int transpose, uint64_t seed,
+                                                       uint32_t stream,
+                                                       const float* __restrict__ part,
+                                                       int64_t npart, uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales,
+                                                       float* __restrict__ tscale) {
+  const int bt = blockIdx.z;
+  const float am = reduce_partials(part + (int64_t)bt * npart, npart);
+  float s_enc, s_dec;
+  tensor_scales(am, s_enc, s_dec);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    tscale[2 * bt] = s_enc;
+    tscale[2 * bt + 1] = s_dec;
+  }
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t cb = blockIdx.y;
+  if (r >= rows) return;
+  const T* base = a + (int64_t)bt * bstride;
+  float v[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int64_t c = cb * 16 + k;
+    v[k] = transpose ? load1<T>(base + c * lda + r) : load1<T>(base + r * lda + c);
+  }
+  const int64_t grow = (int64_t)bt * rows + r;
+  const uint64_t idx0 = (uint64_t)grow * (uint64_t)cols + (uint64_t)cb * 16;
+  quant_block16<SR>(v, s_enc, idx0, (uint32_t)seed, (uint32_t)(seed >> 32), stream,
+                    codes + grow * (cols >> 1) + cb * 8, scales + grow * (cols >> 4) + cb);
+}
+
+// per-segment reduction of plain-stats partials: chunk range x column tiles
+__global__ __launch_bounds__(256) void k_reduce_plain_partials(int64_t rows, const int64_t* offs,
+                                                               int nseg,
+                                                               const float* __restrict__ pamax,
+                                                               int64_t nct,
+                                                               float* __restrict__ out,
+                                                               float* __restrict__ tscale) {
+  const SegRange sr = describe_segment(offs, nseg, rows, kStatsRows, blockIdx.x);
+  const float m = reduce_partials(pamax + sr.c0 * nct, (sr.c1 - sr.c0) * nct);
+  if (threadIdx.x == 0) {
+    out[blockIdx.x] = m;
+    float s_enc, s_dec;
+    tensor_scales(m, s_enc, s_dec);
+    tscale[2 * blockIdx.x] = s_enc;
+    tscale[2 * blockIdx.x + 1] = s_dec;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+template <typename T>
+static hipError_t run_split_or_plain(const void* a_, int64_t rows, int64_t cols, int64_t lda,
+                                     const int64_t* offs, int nseg, bool split, bool sr,
+                                     uint64_t seed, uint32_t stream_id, const QuantOut& out,
+                                     const QuantOut* mean, float* mean_f32, const SplitWs& ws,
+                                     hipStream_t st) {
+  const T* a = static_cast<const T*>(a_);
+  const int64_t nchs = chunk_upper_bound(rows, nseg, kStatsRows);
+  const int64_t nchq = chunk_upper_bound(rows, nseg, kQuantRows);
+  const int64_t ct_s = (cols + 511) / 512;
+  const int64_t ct_f = (cols + 255) / 256;
+  const int64_t ct_q = ((cols >> 4) + 63) / 64;
+  if (nchs > 0) {
+    dim3 g((unsigned)ct_s, (unsigned)nchs);
+    if (split)
+      k_stats<T, true><<<g, 256, 0, st>>>(a, rows, cols, lda, offs, nseg, ws.psum, ws.pmax,
+                                          ws.pmin, nullptr);
+    else
+      k_stats<T, false><<<g, 256, 0, st>>>(a, rows, cols, lda, offs, nseg, nullptr, nullptr,
+                                           nullptr, ws.pamax);
+  }
+  int64_t ntmax;
+  if (split) {
+    dim3 g((unsigned)ct_f, (unsigned)nseg);
+    k_finalize<<<g, 256, 0, st>>>(rows, cols, offs, nseg, ws.psum, ws.pmax, ws.pmin, ws.mu,
+                                  mean_f32, ws.tmax_r, ws.tmax_mu);
+    ntmax = ct_f;
+  } else {
+    // one block per segment reduces its chunks' partials and sets its scale
+    k_reduce_plain_partials<<<dim3((unsigned)nseg), 256, 0, st>>>(rows, offs, nseg, ws.pamax,
+                                                                   ct_s, ws.tmax_r, out.tscale);
+    ntmax = 1;
+  }
+  const float* tmax = ws.tmax_r;
+  dim3 gq((unsigned)ct_q, (unsigned)(nchq + (split ? nseg : 0)));
+  if (gq.y == 0) return hipGetLastError();
+#define AVERIS_QUANT_LAUNCH(SPL, SRB)                                                        \
+  k_quant<T, SPL, SRB><<<gq, 256, 0, st>>>(                                                 \
+      a, rows, cols, lda, offs, nseg, nchq, seed, stream_id, ws.mu, tmax, ntmax, ws.tmax_mu, \
+      ct_f, out.codes, out.scales, out.tscale, mean ? mean->codes : nullptr,                \
+      mean ? mean->scales : nullptr, mean ? mean->tscale : nullptr)
+  if (split) {
+    if (sr) AVERIS_QUANT_LAUNCH(true, true); else AVERIS_QUANT_LAUNCH(true, false);
+  } else {
+    if (sr) AVERIS_QUANT_LAUNCH(false, true); else AVERIS_QUANT_LAUNCH(false, false);
+  }
+#undef AVERIS_QUANT_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_split_or_plain(const void* a, bool bf16, int64_t rows, int64_t cols,
+                                 int64_t lda, const int64_t* offs, int nseg, bool split, bool sr,
+                                 uint64_t seed, uint32_t stream_id, const QuantOut& out,
+                                 const QuantOut* mean, float* mean_f32, const SplitWs& ws,
+                                 hipStream_t st) {
+  if (bf16)
+    return run_split_or_plain<uint16_t>(a, rows, cols, lda, offs, nseg, split, sr, seed,
+                                        stream_id, out, mean, mean_f32, ws, st);
+  return run_split_or_plain<float>(a, rows, cols, lda, offs, nseg, split, sr, seed, stream_id,
+                                   out, mean, mean_f32, ws, st);
+}
+
+template <typename T>
+static hipError_t run_batched(const void* a_, int batch, int64_t rows, int64_t cols, int64_t lda,
+                              int64_t bstride, int transpose, bool sr, uint64_t seed,
+                              uint32_t stream_id, const QuantOut& out, float* part,
+                              hipStream_t st) {
+  const T* a = static_cast<const T*>(a_);
+  const int64_t srows = transpose ? cols : rows, scols = transpose ? rows : cols;
+  const int64_t n = srows * scols;
+  int64_t nblk = (n + 256 * 8 - 1) / (256 * 8);
+  if (nblk > kAmaxBlocks) nblk = kAmaxBlocks;
+  if (nblk < 1) nblk = 1;
+  k_amax_batched<T><<<dim3((unsigned)nblk, (unsigned)batch), 256, 0, st>>>(a, srows, scols, lda,
+                                                                           bstride, part);
+  if (rows > 0) {
+    dim3 g((unsigned)((rows + 255) / 256), (unsigned)(cols >> 4), (unsigned)batch);
+    if (sr)
+      k_quant_batched<T, true><<<g, 256, 0, st>>>(a, rows, cols, lda, bstride, transpose, seed,
+                                                  stream_id, part, nblk, out.codes, out.scales,
+                                                  out.tscale);
+    else
+      k_quant_batched<T, false><<<g, 256, 0, st>>>(a, rows, cols, lda, bstride, transpose, seed,
+                                                   stream_id, part, nblk, out.codes, out.scales,
+                                                   out.tscale);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_batched(const void* a, bool bf16, int batch, int64_t rows, int64_t cols,
+                                int64_t lda, int64_t bstride, int transpose, bool sr,
+                                uint64_t seed, uint32_t stream_id, const QuantOut& out,
+                                float* part, hipStream_t st) {
+  if (bf16)
+    return run_batched<uint16_t>(a, batch, rows, cols, lda, bstride, transpose, sr, seed,
+                                 stream_id, out, part, st);
+  return run_batched<float>(a, batch, rows, cols, lda, bstride, transpose, sr, seed, stream_id,
+                            out, part, st);
+}
+
+}  // namespace averis

@@ -1,0 +1,140 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/averis.h declares, and rejects bad arguments before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mean_residual_quantized_amd import averis as av
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# stand-in device addresses: validation must reject the call before using them
+P = 0x10000
+P2 = 0x20000
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "averis.h")).read()
+    return sorted(set(re.findall(r"\b(averis_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return av.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(av.EXPORTS) == names
+
+
+def test_version_and_status_strings(L):
+    assert L.averis_abi_version() == 1
+    for s in range(8):
+        assert L.averis_status_str(s)
+    assert b"unknown" in L.averis_status_str(99)
+
+
+def test_workspace_queries(L):
+    wb = av.workspace_bytes
+    assert wb(av.OP_SPLIT_QUANT, 8192, 1024) > 0
+    assert wb(av.OP_SPLIT_QUANT, 8192, 24) == 0          # cols % 16
+    assert wb(av.OP_SPLIT_QUANT, -1, 32) == 0
+    assert wb(av.OP_GEMM, 8192, 1024, 3072) >= 3072 * 4
+    assert wb(av.OP_GEMM, 8192, 1024, 3072, 64) >= 64 * 3072 * 4
+    assert wb(av.OP_QUANT, 64, 128, 0, 8) > 0
+    # grows with the grouped segment count
+    assert wb(av.OP_SPLIT_QUANT, 4096, 256, 0, 64) > wb(av.OP_SPLIT_QUANT, 4096, 256, 0, 1)
+
+
+def nv(rows, cols, codes=P, scales=P2, tscale=P):
+    return av._NVFP4(codes, scales, tscale, rows, cols)
+
+
+def split(L, a=P, dtype=av.BF16, rows=64, cols=128, lda=128, rnd=av.SR, res=None, mean=None,
+          mu=None, ws=P, wsb=1 << 30):
+    res = res if res is not None else nv(rows, cols)
+    mean = mean if mean is not None else nv(1, cols)
+    return L.averis_split_quant(a, dtype, rows, cols, lda, 0, rnd, ctypes.byref(res),
+                                ctypes.byref(mean), mu, ws, wsb, None)
+
+
+def test_split_quant_rejections(L):
+    assert split(L, cols=24, lda=24) == 2                 # cols % 16
+    assert split(L, cols=0, lda=0) == 2
+    assert split(L, rows=-1) == 2
+    assert split(L, lda=64) == 2                          # lda < cols
+    assert split(L, dtype=7) == 3
+    assert split(L, a=None) == 1
+    assert split(L, a=P + 2) == 4                         # misaligned input
+    assert split(L, lda=132) == 4                         # row stride not 16-byte multiple
+    assert split(L, rnd=5) == 6
+    assert split(L, res=nv(64, 64)) == 2                  # residual shape mismatch
+    assert split(L, mean=nv(2, 128)) == 2
+    assert split(L, res=nv(64, 128, codes=None)) == 1
+    assert split(L, res=nv(64, 128, codes=P + 8)) == 4
+    assert split(L, ws=None) == 5
+    assert split(L, wsb=16) == 5
+    assert split(L, ws=P + 16) == 4                       # workspace alignment
+
+
+def test_quant_and_gemm_rejections(L):
+    out = nv(64, 128)
+    q = lambda **k: L.averis_quant(k.get("a", P), k.get("dt", av.BF16), k.get("rows", 64),
+                                   k.get("cols", 128), k.get("lda", 128), k.get("tr", 0), 0,
+                                   k.get("rnd", av.SR), k.get("stream", 0),
+                                   ctypes.byref(k.get("out", out)), P, 1 << 30, None)
+    assert q(cols=40, lda=40) == 2
+    assert q(tr=2) == 6
+    assert q(stream=1 << 20) == 6
+    assert q(tr=1, lda=32) == 2                           # transposed: lda >= rows
+    assert q(out=nv(64, 64)) == 2
+    assert q(dt=9) == 3
+
+    a, b, m = nv(64, 128), nv(32, 128), nv(1, 128)
+    g = lambda a=a, m=m, b=b, c=P, dt=av.F32, ldc=32, ws=P, wsb=1 << 20: L.averis_gemm_fwd(
+        ctypes.byref(a), None if m is None else ctypes.byref(m), ctypes.byref(b), c, dt, ldc, ws,
+        wsb, None)
+    assert g(b=nv(32, 64)) == 2                           # K mismatch
+    assert g(m=None) == 1
+    assert g(m=nv(1, 64)) == 2
+    assert g(ldc=16) == 2
+    assert g(c=None) == 1
+    assert g(dt=4) == 3
+    assert g(ws=None) == 5
+    assert g(wsb=8) == 5
+    assert g(a=nv(64, 120)) == 2                          # K % 16
+    assert L.averis_gemm_vanilla(ctypes.byref(a), ctypes.byref(b), P + 2, av.F32, 32, None, 0,
+                                 None) == 4
+    # grouped: B rows must be a multiple of nseg, offsets required
+    assert L.averis_gemm_grouped(ctypes.byref(a), None, ctypes.byref(nv(33, 128)), P, 2, P,
+                                 av.F32, 32, P, 1 << 20, None) == 2
+    assert L.averis_gemm_grouped(ctypes.byref(a), None, ctypes.byref(b), None, 2, P, av.F32, 32,
+                                 P, 1 << 20, None) == 1
+    assert L.averis_gemm_grouped(ctypes.byref(a), None, ctypes.byref(b), P, 0, P, av.F32, 32, P,
+                                 1 << 20, None) == 6
+
+
+def test_grouped_and_batched_rejections(L):
+    res, mean = nv(64, 128), nv(4, 128)
+    sg = lambda offs=P, nseg=4, mean=mean: L.averis_split_quant_grouped(
+        P, av.BF16, 64, 128, 128, offs, nseg, 0, av.SR, ctypes.byref(res), ctypes.byref(mean),
+        None, P, 1 << 30, None)
+    assert sg(offs=None) == 1
+    assert sg(offs=P + 4) == 4
+    assert sg(nseg=0) == 6
+    assert sg(nseg=5000) == 6
+    assert sg(mean=nv(3, 128)) == 2
+    out = nv(2 * 64, 128)
+    qb = lambda batch=2, bstride=64 * 128, tr=0: L.averis_quant_batched(
+        P, av.BF16, batch, 64, 128, 128, bstride, tr, 0, av.RN, 2, ctypes.byref(out), P, 1 << 20,
+        None)
+    assert qb(batch=0) == 6
+    assert qb(bstride=100) == 2                           # overlapping batch entries
+    assert qb(batch=3) == 2                               # out rows != batch * rows

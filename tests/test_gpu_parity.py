@@ -1,0 +1,246 @@
+"""GPU parity: libaveris (through the C ABI) against the CPU oracle.
+
+Quantized codes, scale bytes, tensor scales and the fp32 mean must be
+bit-exact; GEMM outputs must satisfy
+    |C_gpu - C_oracle| <= 1e-3 * (|deq A| |deq B|^T + 1 |deq mean| |deq B|^T)
+elementwise, where C_oracle is the oracle's float64 product of the same
+dequantized operands (the bound an FP32-accumulated product of exact operands
+meets with a wide margin: K * 2^-24 < 2e-4 at K = 3072)."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import averis as orc
+from mean_residual_quantized_amd import averis as av
+from mean_residual_quantized_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+GEMM_TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    av.lib()
+
+
+def f32(t):
+    return t.float().cpu().numpy()
+
+
+def assert_quant_equal(gpu, ref, seg=0, rows=None):
+    g = gpu.cpu()
+    codes, scales = g["codes"], g["scales"]
+    if rows is not None:
+        codes, scales = codes[rows], scales[rows]
+    np.testing.assert_array_equal(codes, ref["codes"])
+    np.testing.assert_array_equal(scales, ref["scales"])
+    assert g["tscale"][2 * seg] == ref["s_enc"]
+    assert g["tscale"][2 * seg + 1] == ref["s_dec"]
+
+
+def assert_gemm_close(c_gpu, c_ref, bound):
+    c = c_gpu.float().cpu().numpy().astype(np.float64) if torch.is_tensor(c_gpu) else c_gpu
+    err = np.abs(c - c_ref)
+    ok = err <= GEMM_TOL * bound
+    assert ok.all(), "max normalised error %.3g" % np.max(err / np.maximum(bound, 1e-300))
+
+
+def quant_weights(w, rnd=av.RN):
+    return (av.averis_quant(w, transpose=True, rnd=rnd, sr_stream=av.STREAM_WEIGHT),
+            av.averis_quant(w, transpose=False, rnd=rnd, sr_stream=av.STREAM_WEIGHT))
+
+
+def full_check(x, w, d, seed=0, rnd="sr"):
+    """Split-quant of X and D, weight quant, fwd/dgrad/vanilla GEMMs vs oracle."""
+    r = av.SR if rnd == "sr" else av.RN
+    xg, wg, dg = x.cuda(), w.cuda(), d.cuda()
+    xn, wn, dn = f32(x), f32(w), f32(d)
+
+    wt_g, wd_g = quant_weights(wg)
+    wq = orc.weight_quant(wn, "rn")
+    assert_quant_equal(wt_g, wq["fwd"])
+    assert_quant_equal(wd_g, wq["dgrad"])
+
+    for a_g, a_n, b_g, b_ref, fn in [(xg, xn, wt_g, wq["fwd"], av.averis_gemm_fwd),
+                                     (dg, dn, wd_g, wq["dgrad"], av.averis_gemm_dgrad)]:
+        res, mean, mu = av.averis_split_quant(a_g, seed=seed, rnd=r)
+        s = orc.split_quant(a_n, rnd, seed)
+        np.testing.assert_array_equal(mu.cpu().numpy(), s["mu"])
+        assert_quant_equal(res, s["residual"])
+        assert_quant_equal(mean, s["mean"])
+        c = fn(res, mean, b_g)
+        ref = orc.gemm(s["residual"], b_ref, s["mean"])
+        assert_gemm_close(c, ref, orc.gemm_abs_bound(s["residual"], b_ref, s["mean"]))
+
+    # vanilla arm (forward)
+    qv = av.averis_quant(xg, seed=seed, rnd=r)
+    qv_ref = orc.vanilla_quant(xn, rnd, seed)
+    assert_quant_equal(qv, qv_ref)
+    c = av.averis_gemm_vanilla(qv, wt_g)
+    assert_gemm_close(c, orc.gemm(qv_ref, wq["fwd"]), orc.gemm_abs_bound(qv_ref, wq["fwd"]))
+    torch.cuda.synchronize()
+
+
+def test_config0_tiny():
+    cfg = workloads.config0()
+    full_check(cfg["x"], cfg["w"], cfg["d"], seed=0)
+
+
+def test_config0_round_to_nearest_and_other_seed():
+    cfg = workloads.config0()
+    full_check(cfg["x"], cfg["w"], cfg["d"], seed=0, rnd="rn")
+    full_check(cfg["x"], cfg["w"], cfg["d"], seed=0xABCDEF0123456789)
+
+
+def test_ragged_shapes_several_tiles():
+    # rows not a multiple of any chunk or tile; cols not a multiple of the
+    # 512/1024-column tiles; N not a multiple of the 128-wide GEMM tile
+    cfg = workloads.config1(l=1000, m=304, n=208)
+    full_check(cfg["x"], cfg["w"], cfg["d"], seed=7)
+
+
+def test_swiglu_shapes_reduced():
+    cfg = workloads.config2(l=520, m=3072, n=1024)
+    full_check(cfg["x"], cfg["w"], cfg["d"], seed=3)
+
+
+def test_single_block_and_single_row():
+    rng = np.random.default_rng(0)
+    for rows, cols in [(1, 16), (3, 16), (1, 64), (200, 16)]:
+        x = torch.from_numpy((rng.standard_normal((rows, cols)) * 2 + 1).astype(np.float32))
+        w = torch.from_numpy((rng.standard_normal((cols, 32)) / 4).astype(np.float32))
+        d = torch.from_numpy(rng.standard_normal((rows, 32)).astype(np.float32))
+        full_check(x, w, d, seed=rows)
+
+
+def test_constant_columns_give_zero_residual_and_mean_rows():
+    mu = (3 * np.random.default_rng(1).standard_normal(128) + 1.5).astype(np.float32)
+    x = torch.from_numpy(np.tile(mu, (77, 1))).to(torch.bfloat16)
+    res, mean, m = av.averis_split_quant(x.cuda(), seed=5)
+    s = orc.split_quant(f32(x), "sr", 5)
+    assert_quant_equal(res, s["residual"])
+    assert_quant_equal(mean, s["mean"])
+    g = res.cpu()
+    assert g["tscale"][0] == 1 and not (g["codes"] & 0x77).any()
+
+
+def test_all_zero_and_empty_inputs():
+    z = torch.zeros((40, 64), dtype=torch.bfloat16, device="cuda")
+    res, mean, mu = av.averis_split_quant(z, seed=1)
+    assert not res.codes.any() and not res.scales.any() and not mean.codes.any()
+    assert res.tscale.tolist() == [1.0, 1.0] and mean.tscale.tolist() == [1.0, 1.0]
+    e = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    res, mean, mu = av.averis_split_quant(e, seed=1)
+    assert res.codes.numel() == 0 and not mu.any() and mean.tscale.tolist() == [1.0, 1.0]
+    q = av.averis_quant(e)
+    assert q.tscale.tolist() == [1.0, 1.0]
+    torch.cuda.synchronize()
+
+
+def test_bf16_output_within_rounding():
+    cfg = workloads.config1(l=256, m=256, n=128)
+    xg = cfg["x"].cuda()
+    wt_g, _ = quant_weights(cfg["w"].cuda())
+    res, mean, _ = av.averis_split_quant(xg, seed=0)
+    y32 = av.averis_gemm_fwd(res, mean, wt_g, out_dtype=torch.float32)
+    y16 = av.averis_gemm_fwd(res, mean, wt_g, out_dtype=torch.bfloat16)
+    torch.testing.assert_close(y16, y32.to(torch.bfloat16), rtol=0, atol=0)
+
+
+def test_deterministic_repeats():
+    cfg = workloads.config1(l=512, m=256, n=128)
+    xg = cfg["x"].cuda()
+    outs = [av.averis_split_quant(xg, seed=9) for _ in range(3)]
+    for r, m, mu in outs[1:]:
+        assert torch.equal(r.codes, outs[0][0].codes) and torch.equal(r.scales, outs[0][0].scales)
+        assert torch.equal(m.codes, outs[0][1].codes) and torch.equal(mu, outs[0][2])
+
+
+def sampled_rows_check(a, seed, ranges):
+    """Full-size split-quant: mean and scales exact; residual rows exact on
+    the sampled contiguous row ranges (the oracle quantizes only those)."""
+    ag = a.cuda()
+    res, mean, mu = av.averis_split_quant(ag, seed=seed)
+    an = f32(a)
+    mu_ref = orc.column_mean(an)
+    np.testing.assert_array_equal(mu.cpu().numpy(), mu_ref)
+    r = orc.residual(an, mu_ref)
+    amax = np.max(np.abs(r))
+    mean_ref = orc.quantize(mu_ref[None, :], "sr", seed, stream=1)
+    assert_quant_equal(mean, mean_ref)
+    refs = {}
+    for r0, r1 in ranges:
+        q = orc.quantize(r[r0:r1], "sr", seed, stream=0, row0=r0, amax=amax)
+        assert_quant_equal(res, q, rows=slice(r0, r1))
+        refs[(r0, r1)] = q
+    return res, mean, mean_ref, refs
+
+
+@pytest.mark.parametrize("which", ["x", "d"])
+def test_full_size_config1_sampled(which):
+    cfg = workloads.config1()
+    a = cfg[which]
+    l = a.shape[0]
+    ranges = [(0, 16), (4093, 4109), (l - 16, l)]
+    res, mean, mean_ref, refs = sampled_rows_check(a, 0, ranges)
+    w = cfg["w"].cuda()
+    wt_g, wd_g = quant_weights(w)
+    wq = orc.weight_quant(f32(cfg["w"]), "rn")
+    b_g, b_ref = (wt_g, wq["fwd"]) if which == "x" else (wd_g, wq["dgrad"])
+    fn = av.averis_gemm_fwd if which == "x" else av.averis_gemm_dgrad
+    c = fn(res, mean, b_g, out_dtype=torch.float32)
+    b_deq = orc.dequantize(b_ref)
+    m_deq = orc.dequantize(mean_ref)[0]
+    for (r0, r1), q in refs.items():
+        a_deq = orc.dequantize(q)
+        ref = a_deq @ b_deq.T + (m_deq @ b_deq.T)[None, :]
+        bound = np.abs(a_deq) @ np.abs(b_deq).T + (np.abs(m_deq) @ np.abs(b_deq).T)[None, :]
+        assert_gemm_close(c[r0:r1], ref, bound)
+
+
+def test_grouped_moe_reduced():
+    cfg = workloads.config3(tokens=256, topk=8, experts=16, hidden=128, inter=64)
+    x, w, d, offs = cfg["x"], cfg["w"], cfg["d"], cfg["offsets"]
+    nseg = len(offs) - 1
+    og = torch.from_numpy(offs).cuda()
+    xn, wn = f32(x), f32(w)
+    res, mean, mu = av.averis_split_quant_grouped(x.cuda(), og, seed=2)
+    g = orc.split_quant_grouped(xn, offs, "sr", 2)
+    np.testing.assert_array_equal(mu.cpu().numpy(), g["mu"])
+    rc = res.cpu()
+    for s in range(nseg):
+        r0, r1 = offs[s], offs[s + 1]
+        np.testing.assert_array_equal(rc["codes"][r0:r1], g["residual"][s]["codes"])
+        np.testing.assert_array_equal(rc["scales"][r0:r1], g["residual"][s]["scales"])
+        assert rc["tscale"][2 * s] == g["residual"][s]["s_enc"]
+        assert rc["tscale"][2 * s + 1] == g["residual"][s]["s_dec"]
+        mc = mean.cpu()
+        np.testing.assert_array_equal(mc["codes"][s:s + 1], g["mean"][s]["codes"])
+        assert mc["tscale"][2 * s] == g["mean"][s]["s_enc"]
+    # per-expert weights, forward copies
+    wt = av.averis_quant_batched(w.cuda(), transpose=True)
+    wrefs = [orc.weight_quant(wn[e], "rn")["fwd"] for e in range(nseg)]
+    wc = wt.cpu()
+    n = w.shape[2]
+    for e in range(nseg):
+        np.testing.assert_array_equal(wc["codes"][e * n:(e + 1) * n], wrefs[e]["codes"])
+        assert wc["tscale"][2 * e + 1] == wrefs[e]["s_dec"]
+    y = av.averis_gemm_grouped(res, mean, wt, og)
+    ref = orc.gemm_grouped(g["residual"], wrefs, g["mean"])
+    bound = np.concatenate([orc.gemm_abs_bound(g["residual"][s], wrefs[s], g["mean"][s])
+                            for s in range(nseg)])
+    assert_gemm_close(y, ref, bound)
+    # vanilla grouped
+    qv = av.averis_quant_grouped(x.cuda(), og, seed=2)
+    vrefs = orc.vanilla_quant_grouped(xn, offs, "sr", 2)
+    qc = qv.cpu()
+    for s in range(nseg):
+        np.testing.assert_array_equal(qc["codes"][offs[s]:offs[s + 1]], vrefs[s]["codes"])
+        assert qc["tscale"][2 * s] == vrefs[s]["s_enc"]
+    yv = av.averis_gemm_grouped(qv, None, wt, og)
+    assert_gemm_close(yv, orc.gemm_grouped(vrefs, wrefs),
+                      np.concatenate([orc.gemm_abs_bound(vrefs[s], wrefs[s]) for s in range(nseg)]))
