@@ -178,7 +178,8 @@ def main():
     ds = [d0] + [d0.clone() for _ in range(copies - 1)]
     dev = x0.device
     ws = dict(
-        q=torch.empty(av.workspace_bytes(av.OP_QUANT, n, m), dtype=torch.uint8, device=dev),
+        q=torch.empty(max(av.workspace_bytes(av.OP_QUANT, n, m),
+                          av.workspace_bytes(av.OP_QUANT, m, n)), dtype=torch.uint8, device=dev),
         sq_x=torch.empty(av.workspace_bytes(av.OP_SPLIT_QUANT, l, m), dtype=torch.uint8,
                          device=dev),
         sq_d=torch.empty(av.workspace_bytes(av.OP_SPLIT_QUANT, l, n), dtype=torch.uint8,

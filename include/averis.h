@@ -213,6 +213,11 @@ const char* averis_status_str(averis_status_t status);
 /* AVERIS_ABI_VERSION of the built library. */
 int averis_abi_version(void);
 
+/* Text of the last HIP error an entry point on the calling thread returned
+ * AVERIS_E_HIP for ("" if none).  The string is owned by the library and is
+ * valid until the next call on the same thread. */
+const char* averis_last_error(void);
+
 #ifdef __cplusplus
 }
 #endif

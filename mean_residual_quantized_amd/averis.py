@@ -29,6 +29,7 @@ EXPORTS = [
     "averis_split_quant", "averis_split_quant_grouped", "averis_quant", "averis_quant_batched",
     "averis_quant_grouped", "averis_gemm_fwd", "averis_gemm_dgrad", "averis_gemm_vanilla",
     "averis_gemm_grouped", "averis_workspace_bytes", "averis_status_str", "averis_abi_version",
+    "averis_last_error",
 ]
 
 
@@ -78,13 +79,18 @@ def lib():
         L.averis_status_str.restype = ctypes.c_char_p
         L.averis_abi_version.argtypes = []
         L.averis_abi_version.restype = I
+        L.averis_last_error.argtypes = []
+        L.averis_last_error.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
 
 def _check(fn, status):
     if status != AVERIS_OK:
-        raise AverisError(fn, status, lib().averis_status_str(status).decode())
+        msg = lib().averis_status_str(status).decode()
+        if status == 7:
+            msg += ": " + lib().averis_last_error().decode()
+        raise AverisError(fn, status, msg)
 
 
 def workspace_bytes(op, rows, cols, n=0, nseg=0):

@@ -5,6 +5,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <cstdio>
 
 #include "../../include/averis.h"
 #include "launch.hpp"
@@ -39,7 +40,14 @@ averis_status_t check_input(const void* a, averis_dtype_t dtype, int64_t rows, i
   return AVERIS_OK;
 }
 
-inline averis_status_t hip_status(hipError_t e) { return e == hipSuccess ? AVERIS_OK : AVERIS_E_HIP; }
+thread_local char g_last_error[256] = "";
+
+inline averis_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return AVERIS_OK;
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s", hipGetErrorName(e),
+                hipGetErrorString(e));
+  return AVERIS_E_HIP;
+}
 
 }  // namespace
 
@@ -114,6 +122,8 @@ const char* averis_status_str(averis_status_t s) {
 }
 
 int averis_abi_version(void) { return AVERIS_ABI_VERSION; }
+
+const char* averis_last_error(void) { return g_last_error; }
 
 static averis_status_t split_common(const void* a, averis_dtype_t dtype, int64_t rows,
                                     int64_t cols, int64_t lda, const int64_t* offs, int nseg,

@@ -163,6 +163,241 @@ __global__ __launch_bounds__(256) void k_gemm_nt(QOperand A, QOperand B, int64_t
     }
 }
 
+// ---------------------------------------------------------------------------
+// Fast path (K % 64 == 0): WG tile (64 TM) x (64 TN), 4 waves in a 2 x 2
+// grid, each wave 32 TM x 32 TN outputs.  Per 64-wide K stage every thread
+// loads raw codes for the next stage into registers while the waves run the
+// MFMAs of the current stage from LDS; the codes are then dequantized with
+// v_cvt_scalef32_pk_f16_fp4 (scale 1) and v_pk_mul_f16 by the E4M3 block
+// scale (both exact) into the other LDS buffer.  One barrier per stage.
+// The rank-one term is fused: the thread that stages row j of B also
+// accumulates sum_k deq'(mean)_k deq'(B)_jk with v_dot2_f32_f16 on the
+// values it has just dequantized, so no extra launch or pass over B.
+// ---------------------------------------------------------------------------
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ half2_t h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+__device__ __forceinline__ uint32_t u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
+
+// 8 codes of one dword -> 4 x (2 x fp16), times the block scale s2 = (s, s)
+__device__ __forceinline__ uint4 deq8(uint32_t w, half2_t s2) {
+  uint4 r;
+  r.x = u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2);
+  r.y = u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2);
+  r.z = u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2);
+  r.w = u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2);
+  return r;
+}
+
+__device__ __forceinline__ half2_t scale_h2(uint32_t byte) {
+  const _Float16 s = (_Float16)e4m3_value(byte & 0xFFu);
+  half2_t r = {s, s};
+  return r;
+}
+
+}  // namespace
+
+template <int TM, int TN, bool OUT_BF16, bool HAS_MEAN>
+__global__ __launch_bounds__(256, 1) void k_gemm_fast(QOperand A, QOperand B, QOperand MU,
+                                                      int64_t m, int64_t n, int64_t k,
+                                                      const int64_t* offs, int nseg, void* c,
+                                                      int64_t ldc) {
+  constexpr int BM = 64 * TM, BN = 64 * TN;
+  constexpr int CA = BM / 128, CB = BN / 128;   // 32-element chunks per thread and stage
+  extern __shared__ __attribute__((aligned(16))) _Float16 smem[];
+  _Float16* As = smem;                          // [2][BM][LDSK]
+  _Float16* Bs = As + 2 * BM * LDSK;            // [2][BN][LDSK]
+  float* rho_sh = reinterpret_cast<float*>(Bs + 2 * BN * LDSK);   // [2][BN]
+  _Float16* Ms = reinterpret_cast<_Float16*>(rho_sh + 2 * BN);    // [k] dequantized mean
+
+  const SegRange sr = locate_chunk(offs, nseg, m, BM, blockIdx.y);
+  if (sr.seg < 0) return;
+  const int seg = sr.seg;
+  const int64_t m0 = sr.r0, m_end = sr.r1;
+  const int64_t n0 = (int64_t)blockIdx.x * BN;
+  const int64_t kh = k >> 1, kb = k >> 4;
+  const uint8_t* bcodes = B.codes + (offs ? (int64_t)seg * n * kh : 0);
+  const uint8_t* bscales = B.scales + (offs ? (int64_t)seg * n * kb : 0);
+
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int wm = w >> 1, wn = w & 1;
+
+  if (HAS_MEAN) {
+    // the whole dequantized mean vector (without its tensor scale) in LDS
+    const uint8_t* mcodes = MU.codes + (int64_t)seg * kh;
+    const uint8_t* mscales = MU.scales + (int64_t)seg * kb;
+    for (int64_t q = t; q < (k >> 3); q += 256) {
+      const uint32_t wq = *reinterpret_cast<const uint32_t*>(mcodes + 4 * q);
+      reinterpret_cast<uint4*>(Ms)[q] = deq8(wq, scale_h2(mscales[q >> 1]));
+    }
+  }
+
+  // staging assignment: chunk q = t + 256 i -> row q >> 1, k-half q & 1
+  uint4 ra[CA], rb[CB];
+  uint32_t sa[CA], sb[CB];
+  float rho_acc[CB];
+#pragma unroll
+  for (int i = 0; i < CB; ++i) rho_acc[i] = 0.0f;
+
+  auto gload = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      const int q = t + 256 * i, row = q >> 1, hf = q & 1;
+      const int64_t gr = m0 + row;
+      if (gr < m_end) {
+        ra[i] = *reinterpret_cast<const uint4*>(A.codes + gr * kh + (k0 >> 1) + 16 * hf);
+        sa[i] = *reinterpret_cast<const uint16_t*>(A.scales + gr * kb + (k0 >> 4) + 2 * hf);
+      } else {
+        ra[i] = make_uint4(0, 0, 0, 0);
+        sa[i] = 0;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int q = t + 256 * i, row = q >> 1, hf = q & 1;
+      const int64_t gr = n0 + row;
+      if (gr < n) {
+        rb[i] = *reinterpret_cast<const uint4*>(bcodes + gr * kh + (k0 >> 1) + 16 * hf);
+        sb[i] = *reinterpret_cast<const uint16_t*>(bscales + gr * kb + (k0 >> 4) + 2 * hf);
+      } else {
+        rb[i] = make_uint4(0, 0, 0, 0);
+        sb[i] = 0;
+      }
+    }
+  };
+
+  // dequantize the registers of stage k0 into LDS buffer `buf`; B rows also
+  // feed the rank-one partial sums (Ms is complete: it is written before the
+  // first barrier and never changes)
+  auto stage = [&](int buf, int64_t k0) {
+    _Float16* as = As + buf * BM * LDSK;
+    _Float16* bs = Bs + buf * BN * LDSK;
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      const int q = t + 256 * i, row = q >> 1, hf = q & 1;
+      const half2_t s0 = scale_h2(sa[i]), s1 = scale_h2(sa[i] >> 8);
+      uint4* dst = reinterpret_cast<uint4*>(as + row * LDSK + 32 * hf);
+      dst[0] = deq8(ra[i].x, s0);
+      dst[1] = deq8(ra[i].y, s0);
+      dst[2] = deq8(ra[i].z, s1);
+      dst[3] = deq8(ra[i].w, s1);
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int q = t + 256 * i, row = q >> 1, hf = q & 1;
+      const half2_t s0 = scale_h2(sb[i]), s1 = scale_h2(sb[i] >> 8);
+      uint4 d[4];
+      d[0] = deq8(rb[i].x, s0);
+      d[1] = deq8(rb[i].y, s0);
+      d[2] = deq8(rb[i].z, s1);
+      d[3] = deq8(rb[i].w, s1);
+      uint4* dst = reinterpret_cast<uint4*>(bs + row * LDSK + 32 * hf);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = d[e];
+      if (HAS_MEAN) {
+        const uint4* mv = reinterpret_cast<const uint4*>(Ms + k0 + 32 * hf);
+        float a = rho_acc[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint4 m4 = mv[e];
+          a = __builtin_amdgcn_fdot2(h2(d[e].x), h2(m4.x), a, false);
+          a = __builtin_amdgcn_fdot2(h2(d[e].y), h2(m4.y), a, false);
+          a = __builtin_amdgcn_fdot2(h2(d[e].z), h2(m4.z), a, false);
+          a = __builtin_amdgcn_fdot2(h2(d[e].w), h2(m4.w), a, false);
+        }
+        rho_acc[i] = a;
+      }
+    }
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int nk = (int)(k / BK);
+  gload(0);
+  if (HAS_MEAN) __syncthreads();   // Ms visible before stage(0) reads it
+  stage(0, 0);
+  __syncthreads();
+  for (int it = 0; it < nk; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < nk) gload((int64_t)(it + 1) * BK);
+    const _Float16* as = As + buf * BM * LDSK;
+    const _Float16* bs = Bs + buf * BN * LDSK;
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      half8_t af[TM], bf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const half8_t*>(
+            as + (wm * 32 * TM + i * 32 + (lane & 31)) * LDSK + kk + (lane >> 5) * 8);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bf[j] = *reinterpret_cast<const half8_t*>(
+            bs + (wn * 32 * TN + j * 32 + (lane & 31)) * LDSK + kk + (lane >> 5) * 8);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    if (it + 1 < nk) stage(buf ^ 1, (int64_t)(it + 1) * BK);
+    __syncthreads();
+  }
+
+  float rho_col[TN];
+  if (HAS_MEAN) {
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int q = t + 256 * i, row = q >> 1, hf = q & 1;
+      rho_sh[hf * BN + row] = rho_acc[i];
+    }
+    __syncthreads();
+    const float sd = MU.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = wn * 32 * TN + j * 32 + (lane & 31);
+      rho_col[j] = (rho_sh[col] + rho_sh[BN + col]) * sd;
+    }
+  }
+
+  const float alpha = A.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int64_t col = n0 + wn * 32 * TN + j * 32 + (lane & 31);
+    if (col >= n) continue;
+    const float r1 = HAS_MEAN ? rho_col[j] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = m0 + wm * 32 * TM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        if (row >= m_end) continue;
+        const float y = acc[i][j][v] * alpha + r1;
+        if (OUT_BF16)
+          static_cast<uint16_t*>(c)[row * ldc + col] = f32_to_bf16_rne(y);
+        else
+          static_cast<float*>(c)[row * ldc + col] = y;
+      }
+    }
+  }
+}
+
+// dynamic LDS of k_gemm_fast
+static size_t fast_lds_bytes(int tm, int tn, int64_t k, bool has_mean) {
+  return (size_t)(2 * 64 * tm * LDSK + 2 * 64 * tn * LDSK) * 2 + (size_t)2 * 64 * tn * 4 +
+         (has_mean ? (size_t)k * 2 : 0);
+}
+
+// 160 KB of LDS per workgroup, less room for the kernel's static LDS (segment lookup)
+constexpr size_t kLdsLimit = 160 * 1024 - 512;
+
 // rho[seg][j] = S_dec(mean_seg) S_dec(B_seg) sum_k deq'(mean_seg)_k deq'(B_seg)_jk
 // one wavefront per output column j
 __global__ __launch_bounds__(256) void k_rank1(QOperand M, QOperand B, int64_t n, int64_t k,
@@ -203,16 +438,77 @@ size_t gemm_ws_bytes(int64_t n, int nseg) {
   return (size_t)(n * (int64_t)(nseg > 0 ? nseg : 1) * 4 + 255) & ~(size_t)255;
 }
 
+template <int TM, int TN, bool OB, bool HM>
+static hipError_t launch_fast(const QOperand& a, const QOperand& mu, const QOperand& b, int64_t m,
+                              int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
+                              int64_t ldc, hipStream_t st) {
+  const size_t lds = fast_lds_bytes(TM, TN, k, HM);
+  static bool attr_set = false;   // per instantiation; the attribute is idempotent
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_fast<TM, TN, OB, HM>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t tiles_m = chunk_upper_bound(m, offs ? nseg : 1, 64 * TM);
+  dim3 g((unsigned)((n + 64 * TN - 1) / (64 * TN)), (unsigned)tiles_m);
+  k_gemm_fast<TM, TN, OB, HM><<<g, 256, lds, st>>>(a, b, mu, m, n, k, offs, nseg, c, ldc);
+  return hipGetLastError();
+}
+
+template <int TM, int TN>
+static hipError_t launch_fast_any(const QOperand& a, const QOperand* mean, const QOperand& b,
+                                  int64_t m, int64_t n, int64_t k, const int64_t* offs, int nseg,
+                                  void* c, bool c_bf16, int64_t ldc, hipStream_t st) {
+  const QOperand mu = mean ? *mean : QOperand{nullptr, nullptr, nullptr};
+  if (c_bf16)
+    return mean ? launch_fast<TM, TN, true, true>(a, mu, b, m, n, k, offs, nseg, c, ldc, st)
+                : launch_fast<TM, TN, true, false>(a, mu, b, m, n, k, offs, nseg, c, ldc, st);
+  return mean ? launch_fast<TM, TN, false, true>(a, mu, b, m, n, k, offs, nseg, c, ldc, st)
+              : launch_fast<TM, TN, false, false>(a, mu, b, m, n, k, offs, nseg, c, ldc, st);
+}
+
+// Tile shape for the fast kernel: the fewest "tile-area rounds" over the 256
+// CUs (one workgroup per CU), with a small penalty for the narrower tiles'
+// higher LDS traffic per MFMA.  Returns 0 if the fast kernel does not apply.
+static int pick_tile(int64_t m, int64_t n, int64_t k, int nseg_eff, bool has_mean) {
+  if (k % BK != 0) return 0;
+  struct Cand { int tm, tn; double eff; };
+  const Cand cands[3] = {{4, 4, 1.0}, {4, 2, 0.85}, {2, 2, 0.7}};
+  int best = 0;
+  double best_cost = 0;
+  for (int i = 0; i < 3; ++i) {
+    const Cand& cd = cands[i];
+    if (fast_lds_bytes(cd.tm, cd.tn, k, has_mean) > kLdsLimit) continue;
+    const int64_t tiles = chunk_upper_bound(m, nseg_eff, 64 * cd.tm) * ((n + 64 * cd.tn - 1) / (64 * cd.tn));
+    const double rounds = (double)((tiles + 255) / 256);
+    const double cost = rounds * (64.0 * cd.tm) * (64.0 * cd.tn) / cd.eff;
+    if (best == 0 || cost < best_cost) {
+      best = i + 1;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 hipError_t launch_gemm(const QOperand& a, const QOperand* mean, const QOperand& b, int64_t m,
                        int64_t n, int64_t k, const int64_t* offs, int nseg, void* c, bool c_bf16,
                        int64_t ldc, float* rho_ws, hipStream_t st) {
+  if (m == 0 || n == 0) return hipGetLastError();
+  const int choice = pick_tile(m, n, k, offs ? nseg : 1, mean != nullptr);
+  switch (choice) {
+    case 1: return launch_fast_any<4, 4>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+    case 2: return launch_fast_any<4, 2>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+    case 3: return launch_fast_any<2, 2>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+    default: break;
+  }
+  // general path (K % 64 != 0, or a mean vector too long for LDS)
   const int ns = offs ? nseg : 1;
   if (mean) {
     dim3 g((unsigned)((n + 3) / 4), (unsigned)ns);
     k_rank1<<<g, 256, 0, st>>>(*mean, b, n, k, offs != nullptr, rho_ws);
   }
-  const int64_t tiles_m = chunk_upper_bound(m, offs ? nseg : 1, BM);
-  if (tiles_m == 0 || n == 0) return hipGetLastError();
+  const int64_t tiles_m = chunk_upper_bound(m, ns, BM);
   dim3 g((unsigned)((n + BN - 1) / BN), (unsigned)tiles_m);
   if (c_bf16) {
     if (mean)

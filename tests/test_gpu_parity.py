@@ -103,6 +103,12 @@ def test_ragged_shapes_several_tiles():
     full_check(cfg["x"], cfg["w"], cfg["d"], seed=7)
 
 
+def test_ragged_rows_and_cols_fast_gemm_path():
+    # K % 64 == 0 in both passes (the fast GEMM kernel) with M and N tails
+    cfg = workloads.config1(l=1000, m=320, n=192)
+    full_check(cfg["x"], cfg["w"], cfg["d"], seed=11)
+
+
 def test_swiglu_shapes_reduced():
     cfg = workloads.config2(l=520, m=3072, n=1024)
     full_check(cfg["x"], cfg["w"], cfg["d"], seed=3)
