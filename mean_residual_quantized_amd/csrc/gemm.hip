@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdlib>
+
 #include "launch.hpp"
 #include "segments.hpp"
 
@@ -41,10 +43,13 @@ __device__ __forceinline__ uint32_t e2m1_f16_bits(uint32_t code) {
   return mag | ((code & 8u) << 12);
 }
 
+// E4M3FN byte -> fp32 (exact), branch-free: normal (1 + m/8) 2^(e-7),
+// subnormal m 2^-9
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
   const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  if (e == 0) return (float)m * 0.001953125f;
-  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+  const uint32_t normal = ((e + 120u) << 23) | (m << 20);
+  const uint32_t sub = __float_as_uint((float)m * 0.001953125f);
+  return __uint_as_float(e ? normal : sub);
 }
 
 // 8 codes (one dword) times a block scale -> 8 fp16 (exact)
@@ -199,7 +204,14 @@ __device__ __forceinline__ half2_t scale_h2(uint32_t byte) {
 
 }  // namespace
 
-template <int TM, int TN, bool OUT_BF16, bool HAS_MEAN>
+constexpr int kXcds = 8;   // MI355X: 8 accelerator complex dies, one L2 each
+
+#ifndef AVERIS_GEMM_INTERLEAVE
+#define AVERIS_GEMM_INTERLEAVE 1
+#endif
+constexpr bool INTERLEAVE = AVERIS_GEMM_INTERLEAVE;
+
+template <int TM, int TN, int PF, bool OUT_BF16, bool HAS_MEAN>
 __global__ __launch_bounds__(256, 1) void k_gemm_fast(QOperand A, QOperand B, QOperand MU,
                                                       int64_t m, int64_t n, int64_t k,
                                                       const int64_t* offs, int nseg, void* c,
@@ -212,11 +224,24 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fast(QOperand A, QOperand B, QO
   float* rho_sh = reinterpret_cast<float*>(Bs + 2 * BN * LDSK);   // [2][BN]
   _Float16* Ms = reinterpret_cast<_Float16*>(rho_sh + 2 * BN);    // [k] dequantized mean
 
-  const SegRange sr = locate_chunk(offs, nseg, m, BM, blockIdx.y);
+  // Workgroups are dispatched round-robin over the 8 XCDs (linear id % 8).
+  // Renumber them so each XCD walks a contiguous, row-major run of tiles:
+  // the tiles an XCD runs together share A rows in its L2.
+  int64_t tile_x, tile_y;
+  {
+    const int64_t gx = gridDim.x, total = gx * gridDim.y;
+    const int64_t lin = (int64_t)blockIdx.y * gx + blockIdx.x;
+    const int64_t even = total - total % kXcds;
+    int64_t id = lin;
+    if (lin < even) id = (lin % kXcds) * (even / kXcds) + lin / kXcds;
+    tile_y = id / gx;
+    tile_x = id - tile_y * gx;
+  }
+  const SegRange sr = locate_chunk(offs, nseg, m, BM, tile_y);
   if (sr.seg < 0) return;
   const int seg = sr.seg;
   const int64_t m0 = sr.r0, m_end = sr.r1;
-  const int64_t n0 = (int64_t)blockIdx.x * BN;
+  const int64_t n0 = tile_x * BN;
   const int64_t kh = k >> 1, kb = k >> 4;
   const uint8_t* bcodes = B.codes + (offs ? (int64_t)seg * n * kh : 0);
   const uint8_t* bscales = B.scales + (offs ? (int64_t)seg * n * kb : 0);
@@ -234,65 +259,78 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fast(QOperand A, QOperand B, QO
     }
   }
 
-  // staging assignment: chunk q = t + 256 i -> row q >> 1, k-half q & 1
-  uint4 ra[CA], rb[CB];
-  uint32_t sa[CA], sb[CB];
+  // Staging: chunk q = t + 256 i covers row q >> 1 of the tile, k-half q & 1
+  // of each 64-wide stage.  Rows past the edge are clamped to the last valid
+  // row: their products land only in outputs that are never stored.
+  // Byte offsets are 32-bit and fixed; each stage adds a uniform k offset.
+  const uint8_t* a_c = A.codes + m0 * kh;
+  const uint8_t* a_s = A.scales + m0 * kb;
+  const uint8_t* b_c = bcodes + n0 * kh;
+  const uint8_t* b_s = bscales + n0 * kb;
+  uint32_t oac[CA], oas[CA], obc[CB], obs[CB];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    const int q = t + 256 * i, hf = q & 1;
+    const int64_t row = (q >> 1) < (m_end - m0) ? (q >> 1) : (m_end - m0 - 1);
+    oac[i] = (uint32_t)(row * kh) + 16u * hf;
+    oas[i] = (uint32_t)(row * kb) + 2u * hf;
+  }
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    const int q = t + 256 * i, hf = q & 1;
+    const int64_t row = (q >> 1) < (n - n0) ? (q >> 1) : (n - n0 - 1);
+    obc[i] = (uint32_t)(row * kh) + 16u * hf;
+    obs[i] = (uint32_t)(row * kb) + 2u * hf;
+  }
+
+  // raw codes of K stage j live in register slot j % PF
+  uint4 ra[PF][CA], rb[PF][CB];
+  uint32_t sa[PF][CA], sb[PF][CB];
   float rho_acc[CB];
 #pragma unroll
   for (int i = 0; i < CB; ++i) rho_acc[i] = 0.0f;
 
-  auto gload = [&](int64_t k0) {
+  auto gload = [&](int slot, int64_t k0) {
+    const uint8_t* ac = a_c + (k0 >> 1);
+    const uint8_t* as_ = a_s + (k0 >> 4);
+    const uint8_t* bc = b_c + (k0 >> 1);
+    const uint8_t* bs_ = b_s + (k0 >> 4);
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
-      const int q = t + 256 * i, row = q >> 1, hf = q & 1;
-      const int64_t gr = m0 + row;
-      if (gr < m_end) {
-        ra[i] = *reinterpret_cast<const uint4*>(A.codes + gr * kh + (k0 >> 1) + 16 * hf);
-        sa[i] = *reinterpret_cast<const uint16_t*>(A.scales + gr * kb + (k0 >> 4) + 2 * hf);
-      } else {
-        ra[i] = make_uint4(0, 0, 0, 0);
-        sa[i] = 0;
-      }
+      ra[slot][i] = *reinterpret_cast<const uint4*>(ac + oac[i]);
+      sa[slot][i] = *reinterpret_cast<const uint16_t*>(as_ + oas[i]);
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
-      const int q = t + 256 * i, row = q >> 1, hf = q & 1;
-      const int64_t gr = n0 + row;
-      if (gr < n) {
-        rb[i] = *reinterpret_cast<const uint4*>(bcodes + gr * kh + (k0 >> 1) + 16 * hf);
-        sb[i] = *reinterpret_cast<const uint16_t*>(bscales + gr * kb + (k0 >> 4) + 2 * hf);
-      } else {
-        rb[i] = make_uint4(0, 0, 0, 0);
-        sb[i] = 0;
-      }
+      rb[slot][i] = *reinterpret_cast<const uint4*>(bc + obc[i]);
+      sb[slot][i] = *reinterpret_cast<const uint16_t*>(bs_ + obs[i]);
     }
   };
 
-  // dequantize the registers of stage k0 into LDS buffer `buf`; B rows also
-  // feed the rank-one partial sums (Ms is complete: it is written before the
-  // first barrier and never changes)
-  auto stage = [&](int buf, int64_t k0) {
+  // dequantize the staged registers into LDS buffer `buf`; B rows also feed
+  // the rank-one partial sums (Ms is written before the first barrier)
+  auto stage = [&](int slot, int buf, int64_t k0) {
     _Float16* as = As + buf * BM * LDSK;
     _Float16* bs = Bs + buf * BN * LDSK;
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
       const int q = t + 256 * i, row = q >> 1, hf = q & 1;
-      const half2_t s0 = scale_h2(sa[i]), s1 = scale_h2(sa[i] >> 8);
+      const half2_t s0 = scale_h2(sa[slot][i]), s1 = scale_h2(sa[slot][i] >> 8);
       uint4* dst = reinterpret_cast<uint4*>(as + row * LDSK + 32 * hf);
-      dst[0] = deq8(ra[i].x, s0);
-      dst[1] = deq8(ra[i].y, s0);
-      dst[2] = deq8(ra[i].z, s1);
-      dst[3] = deq8(ra[i].w, s1);
+      dst[0] = deq8(ra[slot][i].x, s0);
+      dst[1] = deq8(ra[slot][i].y, s0);
+      dst[2] = deq8(ra[slot][i].z, s1);
+      dst[3] = deq8(ra[slot][i].w, s1);
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
       const int q = t + 256 * i, row = q >> 1, hf = q & 1;
-      const half2_t s0 = scale_h2(sb[i]), s1 = scale_h2(sb[i] >> 8);
+      const half2_t s0 = scale_h2(sb[slot][i]), s1 = scale_h2(sb[slot][i] >> 8);
       uint4 d[4];
-      d[0] = deq8(rb[i].x, s0);
-      d[1] = deq8(rb[i].y, s0);
-      d[2] = deq8(rb[i].z, s1);
-      d[3] = deq8(rb[i].w, s1);
+      d[0] = deq8(rb[slot][i].x, s0);
+      d[1] = deq8(rb[slot][i].y, s0);
+      d[2] = deq8(rb[slot][i].z, s1);
+      d[3] = deq8(rb[slot][i].w, s1);
       uint4* dst = reinterpret_cast<uint4*>(bs + row * LDSK + 32 * hf);
 #pragma unroll
       for (int e = 0; e < 4; ++e) dst[e] = d[e];
@@ -320,35 +358,71 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fast(QOperand A, QOperand B, QO
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int nk = (int)(k / BK);
-  gload(0);
-  if (HAS_MEAN) __syncthreads();   // Ms visible before stage(0) reads it
-  stage(0, 0);
-  __syncthreads();
-  for (int it = 0; it < nk; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < nk) gload((int64_t)(it + 1) * BK);
-    const _Float16* as = As + buf * BM * LDSK;
-    const _Float16* bs = Bs + buf * BN * LDSK;
+  // LDS fragment offsets (in fp16 elements) of this lane
+  const int a_frag = (wm * 32 * TM + (lane & 31)) * LDSK + (lane >> 5) * 8;
+  const int b_frag = (wn * 32 * TN + (lane & 31)) * LDSK + (lane >> 5) * 8;
+  auto mfma_stage = [&](int buf) {
+    const _Float16* as = As + buf * BM * LDSK + a_frag;
+    const _Float16* bs = Bs + buf * BN * LDSK + b_frag;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
       half8_t af[TM], bf[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const half8_t*>(
-            as + (wm * 32 * TM + i * 32 + (lane & 31)) * LDSK + kk + (lane >> 5) * 8);
+        af[i] = *reinterpret_cast<const half8_t*>(as + i * 32 * LDSK + kk);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        bf[j] = *reinterpret_cast<const half8_t*>(
-            bs + (wn * 32 * TN + j * 32 + (lane & 31)) * LDSK + kk + (lane >> 5) * 8);
+        bf[j] = *reinterpret_cast<const half8_t*>(bs + j * 32 * LDSK + kk);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-    if (it + 1 < nk) stage(buf ^ 1, (int64_t)(it + 1) * BK);
+  };
+
+  // One K stage `it`: refill slot it % PF with stage it + PF, run the MFMAs
+  // of LDS buffer it & 1, dequantize stage it + 1 into the other buffer.
+  const int nk = (int)(k / BK);
+  auto step = [&](int it, int slot, bool refill, bool next) {
+    if (refill) gload(slot, (int64_t)(it + PF) * BK);
+    mfma_stage(it & 1);
+    if (next) stage((slot + 1) % PF, (it + 1) & 1, (int64_t)(it + 1) * BK);
+    if (INTERLEAVE && refill && next) {
+      // Ask the scheduler to interleave: each MFMA leaves ~28 idle issue
+      // cycles that the next stage's dequantization (VALU), its LDS writes
+      // and this stage's fragment reads can fill.
+      // coarse groups keep the scheduler's group solver cheap
+      constexpr int NG = BK / 16;                     // one group per k-step
+      constexpr int NM = TM * TN;                     // MFMAs per k-step
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);  // fragment reads
+        __builtin_amdgcn_sched_group_barrier(0x008, NM / 2, 0);   // MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);       // VALU
+        __builtin_amdgcn_sched_group_barrier(0x008, NM / 2, 0);   // MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);        // LDS writes
+      }
+    }
     __syncthreads();
+  };
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+    if (p < nk) gload(p, (int64_t)p * BK);
+  if (HAS_MEAN) __syncthreads();   // Ms visible before stage() reads it
+  stage(0, 0, 0);
+  __syncthreads();
+  int it = 0;
+  // steady state: every refill and every next stage exists
+  for (; it + 2 * PF - 1 < nk; it += PF) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) step(it + u, u, true, true);
+  }
+  // tail: fewer than 2 PF - 1 stages left
+#pragma unroll
+  for (int u = 0; u < 2 * PF - 1; ++u) {
+    const int i2 = it + u;
+    if (i2 < nk) step(i2, u % PF, i2 + PF < nk, i2 + 1 < nk);
   }
 
   float rho_col[TN];
@@ -368,17 +442,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fast(QOperand A, QOperand B, QO
   }
 
   const float alpha = A.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
+  const bool full = (m0 + BM <= m_end) && (n0 + BN <= n);
+  const int64_t row_base = m0 + wm * 32 * TM + (lane >> 5) * 4;
+  const int64_t col_base = n0 + wn * 32 * TN + (lane & 31);
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
-    const int64_t col = n0 + wn * 32 * TN + j * 32 + (lane & 31);
-    if (col >= n) continue;
+    const int64_t col = col_base + j * 32;
     const float r1 = HAS_MEAN ? rho_col[j] : 0.0f;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + wm * 32 * TM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-        if (row >= m_end) continue;
+        const int64_t row = row_base + i * 32 + (v >> 2) * 8 + (v & 3);
+        if (!full && (row >= m_end || col >= n)) continue;
         const float y = acc[i][j][v] * alpha + r1;
         if (OUT_BF16)
           static_cast<uint16_t*>(c)[row * ldc + col] = f32_to_bf16_rne(y);
@@ -438,34 +514,34 @@ size_t gemm_ws_bytes(int64_t n, int nseg) {
   return (size_t)(n * (int64_t)(nseg > 0 ? nseg : 1) * 4 + 255) & ~(size_t)255;
 }
 
-template <int TM, int TN, bool OB, bool HM>
+template <int TM, int TN, int PF, bool OB, bool HM>
 static hipError_t launch_fast(const QOperand& a, const QOperand& mu, const QOperand& b, int64_t m,
                               int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
                               int64_t ldc, hipStream_t st) {
   const size_t lds = fast_lds_bytes(TM, TN, k, HM);
   static bool attr_set = false;   // per instantiation; the attribute is idempotent
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_fast<TM, TN, OB, HM>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_fast<TM, TN, PF, OB, HM>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t tiles_m = chunk_upper_bound(m, offs ? nseg : 1, 64 * TM);
   dim3 g((unsigned)((n + 64 * TN - 1) / (64 * TN)), (unsigned)tiles_m);
-  k_gemm_fast<TM, TN, OB, HM><<<g, 256, lds, st>>>(a, b, mu, m, n, k, offs, nseg, c, ldc);
+  k_gemm_fast<TM, TN, PF, OB, HM><<<g, 256, lds, st>>>(a, b, mu, m, n, k, offs, nseg, c, ldc);
   return hipGetLastError();
 }
 
-template <int TM, int TN>
+template <int TM, int TN, int PF>
 static hipError_t launch_fast_any(const QOperand& a, const QOperand* mean, const QOperand& b,
                                   int64_t m, int64_t n, int64_t k, const int64_t* offs, int nseg,
                                   void* c, bool c_bf16, int64_t ldc, hipStream_t st) {
   const QOperand mu = mean ? *mean : QOperand{nullptr, nullptr, nullptr};
   if (c_bf16)
-    return mean ? launch_fast<TM, TN, true, true>(a, mu, b, m, n, k, offs, nseg, c, ldc, st)
-                : launch_fast<TM, TN, true, false>(a, mu, b, m, n, k, offs, nseg, c, ldc, st);
-  return mean ? launch_fast<TM, TN, false, true>(a, mu, b, m, n, k, offs, nseg, c, ldc, st)
-              : launch_fast<TM, TN, false, false>(a, mu, b, m, n, k, offs, nseg, c, ldc, st);
+    return mean ? launch_fast<TM, TN, PF, true, true>(a, mu, b, m, n, k, offs, nseg, c, ldc, st)
+                : launch_fast<TM, TN, PF, true, false>(a, mu, b, m, n, k, offs, nseg, c, ldc, st);
+  return mean ? launch_fast<TM, TN, PF, false, true>(a, mu, b, m, n, k, offs, nseg, c, ldc, st)
+              : launch_fast<TM, TN, PF, false, false>(a, mu, b, m, n, k, offs, nseg, c, ldc, st);
 }
 
 // Tile shape for the fast kernel: the fewest "tile-area rounds" over the 256
@@ -495,13 +571,32 @@ hipError_t launch_gemm(const QOperand& a, const QOperand* mean, const QOperand& 
                        int64_t n, int64_t k, const int64_t* offs, int nseg, void* c, bool c_bf16,
                        int64_t ldc, float* rho_ws, hipStream_t st) {
   if (m == 0 || n == 0) return hipGetLastError();
-  const int choice = pick_tile(m, n, k, offs ? nseg : 1, mean != nullptr);
+  int choice = pick_tile(m, n, k, offs ? nseg : 1, mean != nullptr);
+  // tuning override: AVERIS_GEMM_TILE = 1 (256x256), 2 (256x128), 3 (128x128)
+  static const int forced = [] {
+    const char* e = std::getenv("AVERIS_GEMM_TILE");
+    return e ? std::atoi(e) : 0;
+  }();
+  if (choice != 0 && forced >= 1 && forced <= 3 &&
+      fast_lds_bytes(forced == 3 ? 2 : 4, forced == 1 ? 4 : 2, k, mean != nullptr) <= kLdsLimit)
+    choice = forced;
+  static const int pf = [] {
+    const char* e = std::getenv("AVERIS_GEMM_PF");
+    return e ? std::atoi(e) : 2;
+  }();
+#define AVERIS_FAST(TM_, TN_)                                                               \
+  switch (pf) {                                                                            \
+    case 1: return launch_fast_any<TM_, TN_, 1>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st); \
+    case 3: return launch_fast_any<TM_, TN_, 3>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st); \
+    default: return launch_fast_any<TM_, TN_, 2>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st); \
+  }
   switch (choice) {
-    case 1: return launch_fast_any<4, 4>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
-    case 2: return launch_fast_any<4, 2>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
-    case 3: return launch_fast_any<2, 2>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+    case 1: AVERIS_FAST(4, 4)
+    case 2: AVERIS_FAST(4, 2)
+    case 3: AVERIS_FAST(2, 2)
     default: break;
   }
+#undef AVERIS_FAST
   // general path (K % 64 != 0, or a mean vector too long for LDS)
   const int ns = offs ? nseg : 1;
   if (mean) {
