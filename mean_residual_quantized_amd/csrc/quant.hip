@@ -62,7 +62,8 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 }
 
 // ---------------------------------------------------------------------------
-// stats: block = 64 column-octets (512 columns) x 4 row lanes; one row chunk
+// stats: block = 32 column-octets (256 columns) x 8 row lanes over one chunk
+// of kStatsRows rows; each thread keeps 8 row loads in flight.
 // ---------------------------------------------------------------------------
 template <typename T, bool SPLIT>
 __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t rows, int64_t cols,
@@ -72,8 +73,8 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
                                                float* __restrict__ pmin,
                                                float* __restrict__ pamax) {
   const SegRange sr = locate_chunk(offs, nseg, rows, kStatsRows, blockIdx.y);
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  const int64_t c = (int64_t)blockIdx.x * 512 + tx * 8;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const int64_t c = (int64_t)blockIdx.x * 256 + tx * 8;
   const bool active = sr.seg >= 0 && c < cols;
 
   double s[8];
@@ -86,24 +87,39 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
     mn[k] = __builtin_inff();
   }
   if (active) {
-    for (int64_t r = sr.r0 + ty; r < sr.r1; r += 4) {
-      float v[8];
-      Load8<T>::run(a + r * lda + c, v);
+    constexpr int U = 8;
+    for (int64_t r0 = sr.r0 + ty; r0 < sr.r1; r0 += 8 * U) {
+      float v[U][8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        if (SPLIT) {
-          s[k] += (double)v[k];
-          mx[k] = __builtin_fmaxf(mx[k], v[k]);
-          mn[k] = __builtin_fminf(mn[k], v[k]);
+      for (int u = 0; u < U; ++u) {
+        const int64_t r = r0 + 8 * u;
+        if (r < sr.r1) {
+          Load8<T>::run(a + r * lda + c, v[u]);
         } else {
-          am = __builtin_fmaxf(am, __builtin_fabsf(v[k]));
+#pragma unroll
+          for (int k = 0; k < 8; ++k) v[u][k] = __builtin_nanf("");
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool ok = r0 + 8 * u < sr.r1;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (SPLIT) {
+            // fmax/fmin ignore the NaN fill of missing rows
+            s[k] += ok ? (double)v[u][k] : 0.0;
+            mx[k] = __builtin_fmaxf(mx[k], v[u][k]);
+            mn[k] = __builtin_fminf(mn[k], v[u][k]);
+          } else {
+            am = __builtin_fmaxf(am, __builtin_fabsf(v[u][k]));
+          }
         }
       }
     }
   }
   if (SPLIT) {
-    __shared__ double ls[4][512];
-    __shared__ float lmx[4][512], lmn[4][512];
+    __shared__ double ls[8][256];
+    __shared__ float lmx[8][256], lmn[8][256];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       ls[ty][tx * 8 + k] = s[k];
@@ -111,21 +127,21 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
       lmn[ty][tx * 8 + k] = mn[k];
     }
     __syncthreads();
-    if (sr.seg >= 0) {
-      for (int j = threadIdx.x; j < 512; j += 256) {
-        const int64_t col = (int64_t)blockIdx.x * 512 + j;
-        if (col < cols) {
-          const double t = ls[0][j] + ls[1][j] + ls[2][j] + ls[3][j];
-          const float m1 = __builtin_fmaxf(__builtin_fmaxf(lmx[0][j], lmx[1][j]),
-                                           __builtin_fmaxf(lmx[2][j], lmx[3][j]));
-          const float m0 = __builtin_fminf(__builtin_fminf(lmn[0][j], lmn[1][j]),
-                                           __builtin_fminf(lmn[2][j], lmn[3][j]));
-          const int64_t o = (int64_t)blockIdx.y * cols + col;
-          psum[o] = t;
-          pmax[o] = m1;
-          pmin[o] = m0;
-        }
+    const int j = threadIdx.x;
+    const int64_t col = (int64_t)blockIdx.x * 256 + j;
+    if (sr.seg >= 0 && col < cols) {
+      double t = 0.0;
+      float m1 = -__builtin_inff(), m0 = __builtin_inff();
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        t += ls[q][j];
+        m1 = __builtin_fmaxf(m1, lmx[q][j]);
+        m0 = __builtin_fminf(m0, lmn[q][j]);
       }
+      const int64_t o = (int64_t)blockIdx.y * cols + col;
+      psum[o] = t;
+      pmax[o] = m1;
+      pmin[o] = m0;
     }
   } else {
     __shared__ float red[4];
@@ -135,7 +151,8 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
 }
 
 // ---------------------------------------------------------------------------
-// finalize (split): thread per column, block per (256 columns, segment)
+// finalize (split): block = 64 columns x 4 chunk lanes, per segment.  The
+// fp64 partial sums are exact, so the order of the reduction is free.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_finalize(int64_t rows, int64_t cols, const int64_t* offs,
                                                   int nseg, const double* __restrict__ psum,
@@ -147,21 +164,49 @@ __global__ __launch_bounds__(256) void k_finalize(int64_t rows, int64_t cols, co
                                                   float* __restrict__ tmax_mu) {
   const int seg = blockIdx.y;
   const SegRange sr = describe_segment(offs, nseg, rows, kStatsRows, seg);
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  float rmax = 0.0f, amu = 0.0f;
+  const int jl = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int64_t j = (int64_t)blockIdx.x * 64 + jl;
+  double s = 0.0;
+  float m1 = -__builtin_inff(), m0 = __builtin_inff();
   if (j < cols) {
-    double s = 0.0;
-    float m1 = -__builtin_inff(), m0 = __builtin_inff();
-    for (int64_t ck = sr.c0; ck < sr.c1; ++ck) {
-      s += psum[ck * cols + j];
-      m1 = __builtin_fmaxf(m1, pmax[ck * cols + j]);
-      m0 = __builtin_fminf(m0, pmin[ck * cols + j]);
+    constexpr int U = 4;
+    for (int64_t ck = sr.c0 + q; ck < sr.c1; ck += 4 * U) {
+      double ps[U];
+      float px[U], pn[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t cc = ck + 4 * u;
+        const bool ok = cc < sr.c1;
+        ps[u] = ok ? psum[cc * cols + j] : 0.0;
+        px[u] = ok ? pmax[cc * cols + j] : -__builtin_inff();
+        pn[u] = ok ? pmin[cc * cols + j] : __builtin_inff();
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        s += ps[u];
+        m1 = __builtin_fmaxf(m1, px[u]);
+        m0 = __builtin_fminf(m0, pn[u]);
+      }
     }
+  }
+  __shared__ double ls[4][64];
+  __shared__ float lx[4][64], ln[4][64];
+  ls[q][jl] = s;
+  lx[q][jl] = m1;
+  ln[q][jl] = m0;
+  __syncthreads();
+  float rmax = 0.0f, amu = 0.0f;
+  if (q == 0 && j < cols) {
+    const double t = (ls[0][jl] + ls[1][jl]) + (ls[2][jl] + ls[3][jl]);
+    const float x1 = __builtin_fmaxf(__builtin_fmaxf(lx[0][jl], lx[1][jl]),
+                                     __builtin_fmaxf(lx[2][jl], lx[3][jl]));
+    const float x0 = __builtin_fminf(__builtin_fminf(ln[0][jl], ln[1][jl]),
+                                     __builtin_fminf(ln[2][jl], ln[3][jl]));
     const int64_t l = sr.seg_r1 - sr.seg_r0;
     float m = 0.0f;
     if (l > 0) {
-      m = (float)(s / (double)l);
-      rmax = __builtin_fmaxf(m1 - m, m - m0);
+      m = (float)(t / (double)l);
+      rmax = __builtin_fmaxf(x1 - m, m - x0);
     }
     mu[(int64_t)seg * cols + j] = m;
     if (mean_out) mean_out[(int64_t)seg * cols + j] = m;
@@ -189,8 +234,9 @@ __device__ __forceinline__ void quant_block16(const float* r, float s_enc, uint6
   uint32_t sc;
   float e_b;
   block_scale(amax_b, s_enc, sc, e_b);
-  uint32_t q[16];
+  uint2 packed;
   if (SR) {
+    uint32_t q[16];
     const uint64_t g = idx0 >> 3;   // idx0 is a multiple of 16
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -199,15 +245,29 @@ __device__ __forceinline__ void quant_block16(const float* r, float s_enc, uint6
 #pragma unroll
       for (int k = 0; k < 8; ++k) q[h * 8 + k] = e2m1_sr(r[h * 8 + k] * e_b, draw16(rr, k));
     }
+    packed.x = q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12) | (q[4] << 16) | (q[5] << 20) |
+               (q[6] << 24) | (q[7] << 28);
+    packed.y = q[8] | (q[9] << 4) | (q[10] << 8) | (q[11] << 12) | (q[12] << 16) | (q[13] << 20) |
+               (q[14] << 24) | (q[15] << 28);
   } else {
+    // RN: gfx950's v_cvt_scalef32_pk_fp4_f32 with scale 1 rounds to nearest,
+    // ties to the even code, saturates at 6 and keeps the sign of zero --
+    // the same rule as e2m1_rn, two elements per instruction
+    float v[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) q[k] = e2m1_rn(r[k] * e_b);
+    for (int k = 0; k < 16; ++k) v[k] = r[k] * e_b;
+    uint32_t lo = 0, hi = 0;
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[0], v[1], 1.0f, 0);
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[2], v[3], 1.0f, 1);
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[4], v[5], 1.0f, 2);
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[6], v[7], 1.0f, 3);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[8], v[9], 1.0f, 0);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[10], v[11], 1.0f, 1);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[12], v[13], 1.0f, 2);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[14], v[15], 1.0f, 3);
+    packed.x = lo;
+    packed.y = hi;
   }
-  uint2 packed;
-  packed.x = q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12) | (q[4] << 16) | (q[5] << 20) |
-             (q[6] << 24) | (q[7] << 28);
-  packed.y = q[8] | (q[9] << 4) | (q[10] << 8) | (q[11] << 12) | (q[12] << 16) | (q[13] << 20) |
-             (q[14] << 24) | (q[15] << 28);
   *reinterpret_cast<uint2*>(codes) = packed;
   *scale = (uint8_t)sc;
 }
@@ -399,8 +459,8 @@ static hipError_t run_split_or_plain(const void* a_, int64_t rows, int64_t cols,
   const T* a = static_cast<const T*>(a_);
   const int64_t nchs = chunk_upper_bound(rows, nseg, kStatsRows);
   const int64_t nchq = chunk_upper_bound(rows, nseg, kQuantRows);
-  const int64_t ct_s = (cols + 511) / 512;
-  const int64_t ct_f = (cols + 255) / 256;
+  const int64_t ct_s = (cols + 255) / 256;
+  const int64_t ct_f = (cols + 63) / 64;
   const int64_t ct_q = ((cols >> 4) + 63) / 64;
   if (nchs > 0) {
     dim3 g((unsigned)ct_s, (unsigned)nchs);
