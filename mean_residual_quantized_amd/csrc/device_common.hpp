@@ -90,23 +90,19 @@ __device__ __forceinline__ uint32_t e2m1_rn(float v) {
 
 // Stochastic rounding with a 16-bit draw u: lo is the largest grid point
 // <= |v|, hi the next; round up iff u < 2^16 (|v| - lo) / (hi - lo).
+// Branch-free: both exact tests are computed and one is selected.
 __device__ __forceinline__ uint32_t e2m1_sr(float v, uint32_t u) {
   const uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
   const float a = __builtin_fminf(__builtin_fabsf(v), 6.0f);
-  uint32_t idx;
-  if (a < 1.0f) {
-    // gap 0.5: 2^16 (a - lo) / 0.5 = a * 2^17 - lo * 2^17, both exact
-    const uint32_t lo = a >= 0.5f ? 1u : 0u;
-    const float t = a * 131072.0f - (lo ? 65536.0f : 0.0f);
-    idx = lo + ((float)u < t ? 1u : 0u);
-  } else {
-    // gap = 2^(E-1): the fraction of the gap is the low 22 mantissa bits, so
-    // u < 2^16 * R / 2^22  <=>  u * 64 < R, exactly
-    const uint32_t b = __float_as_uint(a);
-    const uint32_t rem = b & 0x3FFFFFu;
-    idx = (b >> 22) - 252u + ((u << 6) < rem ? 1u : 0u);
-  }
-  return sign | idx;
+  const uint32_t b = __float_as_uint(a);
+  // |v| >= 1: gap = 2^(E-1); the fraction of the gap is the low 22 mantissa
+  // bits R, so u < 2^16 R / 2^22  <=>  u * 64 < R
+  const uint32_t idx_n = (b >> 22) - 252u + ((u << 6) < (b & 0x3FFFFFu) ? 1u : 0u);
+  // |v| < 1: gap 0.5, lo = 0 or 0.5; 2^16 (a - lo) / 0.5 = a 2^17 - lo 2^17 (exact)
+  const uint32_t half = a >= 0.5f ? 1u : 0u;
+  const float t = a * 131072.0f - (half ? 65536.0f : 0.0f);
+  const uint32_t idx_s = half + ((float)u < t ? 1u : 0u);
+  return sign | (a < 1.0f ? idx_s : idx_n);
 }
 
 // ---------------------------------------------------------------------------

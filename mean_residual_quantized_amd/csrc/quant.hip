@@ -87,32 +87,28 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
     mn[k] = __builtin_inff();
   }
   if (active) {
-    constexpr int U = 8;
-    for (int64_t r0 = sr.r0 + ty; r0 < sr.r1; r0 += 8 * U) {
-      float v[U][8];
+    // all rows of the chunk in flight at once; rows past the segment end are
+    // clamped to its last row (loads stay legal, no branch) and masked below
+    constexpr int U = (int)(kStatsRows / 8);
+    const int64_t rlast = sr.r1 - 1;
+    float v[U][8];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t r = r0 + 8 * u;
-        if (r < sr.r1) {
-          Load8<T>::run(a + r * lda + c, v[u]);
+    for (int u = 0; u < U; ++u) {
+      const int64_t r = sr.r0 + ty + 8 * u;
+      Load8<T>::run(a + (r < rlast ? r : rlast) * lda + c, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = sr.r0 + ty + 8 * u <= rlast;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (SPLIT) {
+          // a clamped row repeats a real value: harmless for max and min
+          s[k] += ok ? (double)v[u][k] : 0.0;
+          mx[k] = __builtin_fmaxf(mx[k], v[u][k]);
+          mn[k] = __builtin_fminf(mn[k], v[u][k]);
         } else {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) v[u][k] = __builtin_nanf("");
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const bool ok = r0 + 8 * u < sr.r1;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          if (SPLIT) {
-            // fmax/fmin ignore the NaN fill of missing rows
-            s[k] += ok ? (double)v[u][k] : 0.0;
-            mx[k] = __builtin_fmaxf(mx[k], v[u][k]);
-            mn[k] = __builtin_fminf(mn[k], v[u][k]);
-          } else {
-            am = __builtin_fmaxf(am, __builtin_fabsf(v[u][k]));
-          }
+          am = __builtin_fmaxf(am, __builtin_fabsf(v[u][k]));
         }
       }
     }
@@ -168,23 +164,24 @@ __global__ __launch_bounds__(256) void k_finalize(int64_t rows, int64_t cols, co
   const int64_t j = (int64_t)blockIdx.x * 64 + jl;
   double s = 0.0;
   float m1 = -__builtin_inff(), m0 = __builtin_inff();
-  if (j < cols) {
-    constexpr int U = 4;
+  if (j < cols && sr.c1 > sr.c0) {
+    constexpr int U = 16;
+    const int64_t clast = sr.c1 - 1;
     for (int64_t ck = sr.c0 + q; ck < sr.c1; ck += 4 * U) {
       double ps[U];
       float px[U], pn[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t cc = ck + 4 * u;
-        const bool ok = cc < sr.c1;
-        ps[u] = ok ? psum[cc * cols + j] : 0.0;
-        px[u] = ok ? pmax[cc * cols + j] : -__builtin_inff();
-        pn[u] = ok ? pmin[cc * cols + j] : __builtin_inff();
+        const int64_t cc = ck + 4 * u < clast ? ck + 4 * u : clast;
+        ps[u] = psum[cc * cols + j];
+        px[u] = pmax[cc * cols + j];
+        pn[u] = pmin[cc * cols + j];
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        s += ps[u];
-        m1 = __builtin_fmaxf(m1, px[u]);
+        const bool ok = ck + 4 * u <= clast;
+        s += ok ? ps[u] : 0.0;
+        m1 = __builtin_fmaxf(m1, px[u]);   // a clamped chunk repeats a real one
         m0 = __builtin_fminf(m0, pn[u]);
       }
     }
@@ -335,9 +332,31 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ a, int64_t 
     return;
   }
 
+  if (!SPLIT && (int64_t)blockIdx.y >= nchunk_ub) {
+    // plain: one block per segment publishes the segment's tensor scale
+    // (also for empty segments, which have no chunk)
+    if (blockIdx.x != 0) return;
+    const int seg = (int)((int64_t)blockIdx.y - nchunk_ub);
+    const SegRange ss = describe_segment(offs, nseg, rows, kStatsRows, seg);
+    const float am = reduce_partials(tmax + ss.c0 * ntmax, (ss.c1 - ss.c0) * ntmax);
+    float s_enc, s_dec;
+    tensor_scales(am, s_enc, s_dec);
+    if (threadIdx.x == 0) {
+      tscale[2 * seg] = s_enc;
+      tscale[2 * seg + 1] = s_dec;
+    }
+    return;
+  }
   const SegRange sr = locate_chunk(offs, nseg, rows, kQuantRows, blockIdx.y);
   if (sr.seg < 0) return;
-  const float am = reduce_partials(tmax + (int64_t)sr.seg * ntmax, ntmax);
+  float am;
+  if (SPLIT) {
+    am = reduce_partials(tmax + (int64_t)sr.seg * ntmax, ntmax);
+  } else {
+    // plain: the segment's stats partials are its stats chunks x column tiles
+    const SegRange ss = describe_segment(offs, nseg, rows, kStatsRows, sr.seg);
+    am = reduce_partials(tmax + ss.c0 * ntmax, (ss.c1 - ss.c0) * ntmax);
+  }
   float s_enc, s_dec;
   tensor_scales(am, s_enc, s_dec);
   if (b >= nb) return;
@@ -349,17 +368,28 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ a, int64_t 
 #pragma unroll
     for (int k = 0; k < 16; ++k) m[k] = mp[k];
   }
-  for (int64_t row = sr.r0 + ty; row < sr.r1; row += 4) {
-    float v[16];
-    const T* p = a + row * lda + b * 16;
-    Load8<T>::run(p, v);
-    Load8<T>::run(p + 8, v + 8);
+  // every row of the chunk: loads first (rows past the end clamped), then
+  // quantize; the row is uniform per wavefront, so the store guard is too
+  constexpr int R = (int)(kQuantRows / 4);
+  const int64_t rlast = sr.r1 - 1;
+  float v[R][16];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int64_t row = sr.r0 + ty + 4 * u;
+    const T* p = a + (row < rlast ? row : rlast) * lda + b * 16;
+    Load8<T>::run(p, v[u]);
+    Load8<T>::run(p + 8, v[u] + 8);
+  }
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int64_t row = sr.r0 + ty + 4 * u;
+    if (row > rlast) break;
     if (SPLIT) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) v[k] = v[k] - m[k];
+      for (int k = 0; k < 16; ++k) v[u][k] = v[u][k] - m[k];
     }
     const uint64_t idx0 = (uint64_t)row * (uint64_t)cols + (uint64_t)b * 16;
-    quant_block16<SR>(v, s_enc, idx0, k0, k1, stream, codes + row * (cols >> 1) + b * 8,
+    quant_block16<SR>(v[u], s_enc, idx0, k0, k1, stream, codes + row * (cols >> 1) + b * 8,
                       scales + row * nb + b);
   }
 }
@@ -429,24 +459,6 @@ __global__ __launch_bounds__(256) void k_quant_batched(const T* __restrict__ a, 
                     codes + grow * (cols >> 1) + cb * 8, scales + grow * (cols >> 4) + cb);
 }
 
-// per-segment reduction of plain-stats partials: chunk range x column tiles
-__global__ __launch_bounds__(256) void k_reduce_plain_partials(int64_t rows, const int64_t* offs,
-                                                               int nseg,
-                                                               const float* __restrict__ pamax,
-                                                               int64_t nct,
-                                                               float* __restrict__ out,
-                                                               float* __restrict__ tscale) {
-  const SegRange sr = describe_segment(offs, nseg, rows, kStatsRows, blockIdx.x);
-  const float m = reduce_partials(pamax + sr.c0 * nct, (sr.c1 - sr.c0) * nct);
-  if (threadIdx.x == 0) {
-    out[blockIdx.x] = m;
-    float s_enc, s_dec;
-    tensor_scales(m, s_enc, s_dec);
-    tscale[2 * blockIdx.x] = s_enc;
-    tscale[2 * blockIdx.x + 1] = s_dec;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
@@ -472,20 +484,19 @@ static hipError_t run_split_or_plain(const void* a_, int64_t rows, int64_t cols,
                                            nullptr, ws.pamax);
   }
   int64_t ntmax;
+  const float* tmax;
   if (split) {
     dim3 g((unsigned)ct_f, (unsigned)nseg);
     k_finalize<<<g, 256, 0, st>>>(rows, cols, offs, nseg, ws.psum, ws.pmax, ws.pmin, ws.mu,
                                   mean_f32, ws.tmax_r, ws.tmax_mu);
+    tmax = ws.tmax_r;
     ntmax = ct_f;
   } else {
-    // one block per segment reduces its chunks' partials and sets its scale
-    k_reduce_plain_partials<<<dim3((unsigned)nseg), 256, 0, st>>>(rows, offs, nseg, ws.pamax,
-                                                                   ct_s, ws.tmax_r, out.tscale);
-    ntmax = 1;
+    // the quant blocks reduce the stats partials (chunks x column tiles) directly
+    tmax = ws.pamax;
+    ntmax = ct_s;
   }
-  const float* tmax = ws.tmax_r;
-  dim3 gq((unsigned)ct_q, (unsigned)(nchq + (split ? nseg : 0)));
-  if (gq.y == 0) return hipGetLastError();
+  dim3 gq((unsigned)ct_q, (unsigned)(nchq + nseg));
 #define AVERIS_QUANT_LAUNCH(SPL, SRB)                                                        \
   k_quant<T, SPL, SRB><<<gq, 256, 0, st>>>(                                                 \
       a, rows, cols, lda, offs, nseg, nchq, seed, stream_id, ws.mu, tmax, ntmax, ws.tmax_mu, \
