@@ -50,7 +50,11 @@ def parse():
     p.add_argument("--n", type=int, default=3072)
     p.add_argument("--copies", type=int, default=0, help="rotating input copies (0: auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=1024, help="oracle sample: tokens")
+    p.add_argument("--cpu-rows", type=int, default=0,
+                   help="oracle sample: tokens (0: the whole step, all l tokens)")
+    p.add_argument("--traffic-probe", action="store_true",
+                   help="run a 256 MiB device copy and the hot-path kernels a few times each "
+                        "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE), then exit")
     return p.parse_args()
 
 
@@ -151,15 +155,60 @@ def cpu_baseline(cfg_rows, m, n):
     except Exception:
         blas = 1
     return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=int(blas), kind="oracle",
-                sample="%d tokens of the l=8192 workload (m=%d, n=%d): split-quant X and D, "
+                sample="%d tokens of the l=8192 workload (m=%d, n=%d), one step: split-quant X and D, "
                        "both weight copies, float64 fwd+dgrad GEMMs; %.1f s; numpy elementwise "
                        "work single-threaded, float64 matmul on %d BLAS threads of %d host cores"
                        % (cfg_rows, m, n, dt, blas, len(os.sched_getaffinity(0))),
                 seconds=dt)
 
 
+COPY_BYTES = 256 << 20
+
+
+def traffic_probe(args):
+    """A device copy of known size (the scale reference for the HBM byte
+    counters) followed by three launches of each hot-path kernel."""
+    l, m, n = args.l, args.m, args.n
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    cfg = workloads.config1(l=l, m=m, n=n)
+    x, w, d = cfg["x"].cuda(), cfg["w"].cuda(), cfg["d"].cuda()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        wt = av.averis_quant(w, transpose=True, rnd=av.RN, sr_stream=av.STREAM_WEIGHT)
+        wd = av.averis_quant(w, transpose=False, rnd=av.RN, sr_stream=av.STREAM_WEIGHT)
+        xr, xm, _ = av.averis_split_quant(x, seed=0)
+        av.averis_gemm_fwd(xr, xm, wt, out_dtype=torch.bfloat16)
+        dr, dm, _ = av.averis_split_quant(d, seed=1)
+        av.averis_gemm_dgrad(dr, dm, wd, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    print("traffic probe done: copy %d bytes" % COPY_BYTES, file=sys.stderr)
+
+
+def load_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, if it was taken on the current kernel source (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+    src = os.path.join(ROOT, "mean_residual_quantized_amd", "csrc", "gemm.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("gemm_source_sha256") != sha:
+        return None
+    return rec
+
+
 def main():
     args = parse()
+    if args.traffic_probe:
+        traffic_probe(args)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -219,14 +268,18 @@ def main():
     overhead = dict(fwd_pct=100 * (t_fwd_a / t_fwd_v - 1), dgrad_pct=100 * (t_bwd_a / t_bwd_v - 1),
                     step_pct=100 * (ms_a / ms_v - 1))
 
-    # roofline of the dominant kernel: the forward GEMM (the vanilla call is the
-    # same NT kernel without the rank-one term; its events bracket one launch)
-    g_ms = compv["vgemm_fwd"]
+    # roofline of the dominant kernel: the Averis forward GEMM (one launch: the
+    # rank-one mean term is fused into it), timed by the events around the call
+    g_ms = comp["gemm_fwd"]
     achieved = gemm_flops / (g_ms * 1e-3) / 1e12
+    tr = load_traffic()
+    traffic = None
+    if tr is not None:
+        traffic = tr["gemm_fwd"]["fetch_bytes"] + tr["gemm_fwd"]["write_bytes"]
     roofline = dict(bound="mfma", achieved=achieved, peak=F16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=achieved / F16_MFMA_PEAK_TFLOPS, traffic=None,
-                    kernel="k_gemm_nt (NVFP4 NT GEMM, exact fp16 dequant -> "
-                           "v_mfma_f32_32x32x16_f16), %dx%dx%d" % (l, n, m),
+                    frac=achieved / F16_MFMA_PEAK_TFLOPS, traffic=traffic,
+                    kernel="k_gemm_fast (Averis forward: NVFP4 NT GEMM + rank-one mean term, exact "
+                           "fp16 dequant -> v_mfma_f32_32x32x16_f16), M=%d N=%d K=%d" % (l, n, m),
                     frac_of_fp4_peak=achieved / FP4_MFMA_PEAK_TFLOPS)
 
     out = {
@@ -257,7 +310,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on the host (bounded sample)")
-        out["cpu_baseline"] = cpu_baseline(args.cpu_rows, m, n)
+        out["cpu_baseline"] = cpu_baseline(args.cpu_rows or l, m, n)
     print(json.dumps(out), flush=True)
 
 

@@ -85,6 +85,16 @@ __device__ __forceinline__ void stage_rows(const uint8_t* codes, const uint8_t* 
   }
 }
 
+// After the last MFMA of a K loop: its accumulators must not be read for
+// ~18 wait states (32x32 f16 MFMA, 8 passes).  The compiler's hazard check
+// misses this when the loop exits through a branch straight into a barrier,
+// so every kernel fences explicitly before its epilogue reads them.
+__device__ __forceinline__ void mfma_drain() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   const uint32_t b = __float_as_uint(f);
   if ((b & 0x7F800000u) == 0x7F800000u) return (uint16_t)((b >> 16) | ((b & 0xFFFFu) ? 0x40u : 0u));
@@ -144,6 +154,7 @@ __global__ __launch_bounds__(256) void k_gemm_nt(QOperand A, QOperand B, int64_t
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
+    if (k0 + BK >= k) mfma_drain();   // last stage: fence in the block of the last MFMA
     __syncthreads();
   }
 
@@ -160,10 +171,12 @@ __global__ __launch_bounds__(256) void k_gemm_nt(QOperand A, QOperand B, int64_t
         const int64_t row = m0 + wm * 64 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
         if (row >= m_end) continue;
         const float y = acc[i][j][v] * alpha + r1;
+        // non-temporal: the output streams out without evicting the
+        // operand tiles the XCD's other workgroups are reading from L2
         if (OUT_BF16)
-          static_cast<uint16_t*>(c)[row * ldc + col] = f32_to_bf16_rne(y);
+          __builtin_nontemporal_store(f32_to_bf16_rne(y), static_cast<uint16_t*>(c) + row * ldc + col);
         else
-          static_cast<float*>(c)[row * ldc + col] = y;
+          __builtin_nontemporal_store(y, static_cast<float*>(c) + row * ldc + col);
       }
     }
 }
@@ -207,17 +220,20 @@ __device__ __forceinline__ half2_t scale_h2(uint32_t byte) {
 constexpr int kXcds = 8;   // MI355X: 8 accelerator complex dies, one L2 each
 
 #ifndef AVERIS_GEMM_INTERLEAVE
-#define AVERIS_GEMM_INTERLEAVE 1
+#define AVERIS_GEMM_INTERLEAVE 0
 #endif
 constexpr bool INTERLEAVE = AVERIS_GEMM_INTERLEAVE;
 
-template <int TM, int TN, int PF, bool OUT_BF16, bool HAS_MEAN>
-__global__ __launch_bounds__(256, 1) void k_gemm_fast(QOperand A, QOperand B, QOperand MU,
+template <int TM, int TN, int WM, int WN, int PF, bool OUT_BF16, bool HAS_MEAN>
+__global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_fast(QOperand A, QOperand B, QOperand MU,
                                                       int64_t m, int64_t n, int64_t k,
                                                       const int64_t* offs, int nseg, void* c,
                                                       int64_t ldc) {
-  constexpr int BM = 64 * TM, BN = 64 * TN;
-  constexpr int CA = BM / 128, CB = BN / 128;   // 32-element chunks per thread and stage
+  constexpr int NT = 64 * WM * WN;                // threads
+  constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
+  // 32-element chunks per thread and stage; when a tile has fewer chunks
+  // than threads, the surplus (whole) wavefronts skip them
+  constexpr int CA = (2 * BM + NT - 1) / NT, CB = (2 * BN + NT - 1) / NT;
   extern __shared__ __attribute__((aligned(16))) _Float16 smem[];
   _Float16* As = smem;                          // [2][BM][LDSK]
   _Float16* Bs = As + 2 * BM * LDSK;            // [2][BN][LDSK]
@@ -247,13 +263,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fast(QOperand A, QOperand B, QO
   const uint8_t* bscales = B.scales + (offs ? (int64_t)seg * n * kb : 0);
 
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / WN, wn = w % WN;
 
   if (HAS_MEAN) {
     // the whole dequantized mean vector (without its tensor scale) in LDS
     const uint8_t* mcodes = MU.codes + (int64_t)seg * kh;
     const uint8_t* mscales = MU.scales + (int64_t)seg * kb;
-    for (int64_t q = t; q < (k >> 3); q += 256) {
+    for (int64_t q = t; q < (k >> 3); q += NT) {
       const uint32_t wq = *reinterpret_cast<const uint32_t*>(mcodes + 4 * q);
       reinterpret_cast<uint4*>(Ms)[q] = deq8(wq, scale_h2(mscales[q >> 1]));
     }
@@ -270,14 +286,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fast(QOperand A, QOperand B, QO
   uint32_t oac[CA], oas[CA], obc[CB], obs[CB];
 #pragma unroll
   for (int i = 0; i < CA; ++i) {
-    const int q = t + 256 * i, hf = q & 1;
+    const int q = t + NT * i, hf = q & 1;
     const int64_t row = (q >> 1) < (m_end - m0) ? (q >> 1) : (m_end - m0 - 1);
     oac[i] = (uint32_t)(row * kh) + 16u * hf;
     oas[i] = (uint32_t)(row * kb) + 2u * hf;
   }
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
-    const int q = t + 256 * i, hf = q & 1;
+    const int q = t + NT * i, hf = q & 1;
     const int64_t row = (q >> 1) < (n - n0) ? (q >> 1) : (n - n0 - 1);
     obc[i] = (uint32_t)(row * kh) + 16u * hf;
     obs[i] = (uint32_t)(row * kb) + 2u * hf;
@@ -297,11 +313,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fast(QOperand A, QOperand B, QO
     const uint8_t* bs_ = b_s + (k0 >> 4);
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
+      if (t + NT * i >= 2 * BM) break;
       ra[slot][i] = *reinterpret_cast<const uint4*>(ac + oac[i]);
       sa[slot][i] = *reinterpret_cast<const uint16_t*>(as_ + oas[i]);
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
+      if (t + NT * i >= 2 * BN) break;
       rb[slot][i] = *reinterpret_cast<const uint4*>(bc + obc[i]);
       sb[slot][i] = *reinterpret_cast<const uint16_t*>(bs_ + obs[i]);
     }
@@ -314,7 +332,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fast(QOperand A, QOperand B, QO
     _Float16* bs = Bs + buf * BN * LDSK;
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
-      const int q = t + 256 * i, row = q >> 1, hf = q & 1;
+      const int q = t + NT * i, row = q >> 1, hf = q & 1;
+      if (q >= 2 * BM) break;
       const half2_t s0 = scale_h2(sa[slot][i]), s1 = scale_h2(sa[slot][i] >> 8);
       uint4* dst = reinterpret_cast<uint4*>(as + row * LDSK + 32 * hf);
       dst[0] = deq8(ra[slot][i].x, s0);
@@ -324,7 +343,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fast(QOperand A, QOperand B, QO
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
-      const int q = t + 256 * i, row = q >> 1, hf = q & 1;
+      const int q = t + NT * i, row = q >> 1, hf = q & 1;
+      if (q >= 2 * BN) break;
       const half2_t s0 = scale_h2(sb[slot][i]), s1 = scale_h2(sb[slot][i] >> 8);
       uint4 d[4];
       d[0] = deq8(rb[slot][i].x, s0);
@@ -386,7 +406,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fast(QOperand A, QOperand B, QO
   const int nk = (int)(k / BK);
   auto step = [&](int it, int slot, bool refill, bool next) {
     if (refill) gload(slot, (int64_t)(it + PF) * BK);
+    // keep the prefetch loads ahead of everything else in the step: vmcnt
+    // drains in issue order, so a load scheduled after the dequantization
+    // below would make it wait for this step's loads too
+    __builtin_amdgcn_sched_barrier(0);
     mfma_stage(it & 1);
+    if (!next) mfma_drain();   // last stage: fence in the block of the last MFMA
     if (next) stage((slot + 1) % PF, (it + 1) & 1, (int64_t)(it + 1) * BK);
     if (INTERLEAVE && refill && next) {
       // Ask the scheduler to interleave: each MFMA leaves ~28 idle issue
@@ -429,7 +454,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fast(QOperand A, QOperand B, QO
   if (HAS_MEAN) {
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
-      const int q = t + 256 * i, row = q >> 1, hf = q & 1;
+      const int q = t + NT * i, row = q >> 1, hf = q & 1;
+      if (q >= 2 * BN) break;
       rho_sh[hf * BN + row] = rho_acc[i];
     }
     __syncthreads();
@@ -456,13 +482,292 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fast(QOperand A, QOperand B, QO
         const int64_t row = row_base + i * 32 + (v >> 2) * 8 + (v & 3);
         if (!full && (row >= m_end || col >= n)) continue;
         const float y = acc[i][j][v] * alpha + r1;
+        // non-temporal: the output streams out without evicting the
+        // operand tiles the XCD's other workgroups are reading from L2
         if (OUT_BF16)
-          static_cast<uint16_t*>(c)[row * ldc + col] = f32_to_bf16_rne(y);
+          __builtin_nontemporal_store(f32_to_bf16_rne(y), static_cast<uint16_t*>(c) + row * ldc + col);
         else
-          static_cast<float*>(c)[row * ldc + col] = y;
+          __builtin_nontemporal_store(y, static_cast<float*>(c) + row * ldc + col);
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Raw-code variant (K % 64 == 0): the LDS stages hold the 4-bit codes and
+// E4M3 bytes as loaded (4x less LDS traffic than fp16 operands); each wave
+// dequantizes its own MFMA fragments right before use.  A lane's 8 operand
+// values per MFMA k-step are 8 consecutive codes of one 16-block: lanes
+// 0..31 take k in [0, 32) of the 64-wide stage and lanes 32..63 k in
+// [32, 64), one 16-byte LDS read per fragment and stage; A and B use the same
+// k mapping, so the products pair up exactly.  Codes are stored as two
+// half-planes (k-half h of row r at plane h, slot r) so those reads are
+// conflict-free.  The rank-one term is accumulated from the dequantized B
+// fragments by the waves of the first row of the wave grid.
+// ---------------------------------------------------------------------------
+template <int TM, int TN>
+struct RawLds {
+  static constexpr int BM = 64 * TM, BN = 64 * TN;
+  static constexpr int PLANE_A = BM * 16 + 128;   // bytes per k-half plane (+pad)
+  static constexpr int PLANE_B = BN * 16 + 128;
+  static constexpr int A_CODES = 0;
+  static constexpr int A_SC = 2 * PLANE_A;
+  static constexpr int B_CODES = A_SC + BM * 4;
+  static constexpr int B_SC = B_CODES + 2 * PLANE_B;
+  static constexpr int STAGE = B_SC + BN * 4;     // bytes per stage buffer
+};
+
+template <int TM, int TN, int PF, bool OUT_BF16, bool HAS_MEAN>
+__global__ __launch_bounds__(256, 1) void k_gemm_raw(QOperand A, QOperand B, QOperand MU,
+                                                     int64_t m, int64_t n, int64_t k,
+                                                     const int64_t* offs, int nseg, void* c,
+                                                     int64_t ldc) {
+  using L = RawLds<TM, TN>;
+  constexpr int BM = L::BM, BN = L::BN;
+  constexpr int CA = BM / 128, CB = BN / 128;   // 16-byte code chunks per thread and stage
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
+  uint8_t* stg = smem_raw;                                        // [2][STAGE]
+  float* rho_sh = reinterpret_cast<float*>(smem_raw + 2 * L::STAGE);   // [BN]
+  _Float16* Ms = reinterpret_cast<_Float16*>(rho_sh + BN);        // [k]
+
+  int64_t tile_x, tile_y;
+  {
+    const int64_t gx = gridDim.x, total = gx * gridDim.y;
+    const int64_t lin = (int64_t)blockIdx.y * gx + blockIdx.x;
+    const int64_t even = total - total % kXcds;
+    int64_t id = lin;
+    if (lin < even) id = (lin % kXcds) * (even / kXcds) + lin / kXcds;
+    tile_y = id / gx;
+    tile_x = id - tile_y * gx;
+  }
+  const SegRange sr = locate_chunk(offs, nseg, m, BM, tile_y);
+  if (sr.seg < 0) return;
+  const int seg = sr.seg;
+  const int64_t m0 = sr.r0, m_end = sr.r1;
+  const int64_t n0 = tile_x * BN;
+  const int64_t kh = k >> 1, kb = k >> 4;
+  const uint8_t* bcodes = B.codes + (offs ? (int64_t)seg * n * kh : 0);
+  const uint8_t* bscales = B.scales + (offs ? (int64_t)seg * n * kb : 0);
+
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int h = lane >> 5, lr = lane & 31;
+
+  if (HAS_MEAN) {
+    const uint8_t* mcodes = MU.codes + (int64_t)seg * kh;
+    const uint8_t* mscales = MU.scales + (int64_t)seg * kb;
+    for (int64_t q = t; q < (k >> 3); q += 256) {
+      const uint32_t wq = *reinterpret_cast<const uint32_t*>(mcodes + 4 * q);
+      reinterpret_cast<uint4*>(Ms)[q] = deq8(wq, scale_h2(mscales[q >> 1]));
+    }
+  }
+
+  // staging: code chunk q = t + 256 i -> row q >> 1, k-half q & 1 (16 bytes);
+  // scale dword of row t (and t + 256 ...) per stage
+  const uint8_t* a_c = A.codes + m0 * kh;
+  const uint8_t* a_s = A.scales + m0 * kb;
+  const uint8_t* b_c = bcodes + n0 * kh;
+  const uint8_t* b_s = bscales + n0 * kb;
+  uint32_t oac[CA], obc[CB], oas[CA], obs[CB];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    const int q = t + 256 * i, hf = q & 1;
+    const int64_t row = (q >> 1) < (m_end - m0) ? (q >> 1) : (m_end - m0 - 1);
+    oac[i] = (uint32_t)(row * kh) + 16u * hf;
+  }
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    const int q = t + 256 * i, hf = q & 1;
+    const int64_t row = (q >> 1) < (n - n0) ? (q >> 1) : (n - n0 - 1);
+    obc[i] = (uint32_t)(row * kh) + 16u * hf;
+  }
+  constexpr int SA = (BM + 255) / 256, SB = (BN + 255) / 256;   // scale dwords per thread
+#pragma unroll
+  for (int i = 0; i < SA; ++i) {
+    const int r = t + 256 * i;
+    const int64_t row = r < (m_end - m0) ? r : (m_end - m0 - 1);
+    oas[i] = (uint32_t)(row * kb);
+  }
+#pragma unroll
+  for (int i = 0; i < SB; ++i) {
+    const int r = t + 256 * i;
+    const int64_t row = r < (n - n0) ? r : (n - n0 - 1);
+    obs[i] = (uint32_t)(row * kb);
+  }
+
+  uint4 ra[PF][CA], rb[PF][CB];
+  uint32_t sa[PF][SA], sb[PF][SB];
+  auto gload = [&](int slot, int64_t k0) {
+    const uint8_t* ac = a_c + (k0 >> 1);
+    const uint8_t* bc = b_c + (k0 >> 1);
+#pragma unroll
+    for (int i = 0; i < CA; ++i) ra[slot][i] = *reinterpret_cast<const uint4*>(ac + oac[i]);
+#pragma unroll
+    for (int i = 0; i < CB; ++i) rb[slot][i] = *reinterpret_cast<const uint4*>(bc + obc[i]);
+#pragma unroll
+    for (int i = 0; i < SA; ++i)
+      if (t + 256 * i < BM) sa[slot][i] = *reinterpret_cast<const uint32_t*>(a_s + (k0 >> 4) + oas[i]);
+#pragma unroll
+    for (int i = 0; i < SB; ++i)
+      if (t + 256 * i < BN) sb[slot][i] = *reinterpret_cast<const uint32_t*>(b_s + (k0 >> 4) + obs[i]);
+  };
+  auto stage = [&](int slot, int buf) {
+    uint8_t* base = stg + buf * L::STAGE;
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      const int q = t + 256 * i, row = q >> 1, hf = q & 1;
+      *reinterpret_cast<uint4*>(base + L::A_CODES + hf * L::PLANE_A + row * 16) = ra[slot][i];
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int q = t + 256 * i, row = q >> 1, hf = q & 1;
+      *reinterpret_cast<uint4*>(base + L::B_CODES + hf * L::PLANE_B + row * 16) = rb[slot][i];
+    }
+#pragma unroll
+    for (int i = 0; i < SA; ++i)
+      if (t + 256 * i < BM)
+        *reinterpret_cast<uint32_t*>(base + L::A_SC + (t + 256 * i) * 4) = sa[slot][i];
+#pragma unroll
+    for (int i = 0; i < SB; ++i)
+      if (t + 256 * i < BN)
+        *reinterpret_cast<uint32_t*>(base + L::B_SC + (t + 256 * i) * 4) = sb[slot][i];
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  float rho_acc[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) rho_acc[j] = 0.0f;
+
+  const int a_row = wm * 32 * TM + lr, b_row = wn * 32 * TN + lr;
+  auto mfma_stage = [&](int buf, int64_t k0) {
+    const uint8_t* base = stg + buf * L::STAGE;
+    uint4 ca[TM], cb[TN];
+    half2_t xa[TM], xb[TN];   // the lane's two block scales (blocks 2h, 2h + 1), exact
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      ca[i] = *reinterpret_cast<const uint4*>(base + L::A_CODES + h * L::PLANE_A + (a_row + 32 * i) * 16);
+      xa[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+          *reinterpret_cast<const uint32_t*>(base + L::A_SC + (a_row + 32 * i) * 4) >> (16 * h),
+          1.0f, false);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      cb[j] = *reinterpret_cast<const uint4*>(base + L::B_CODES + h * L::PLANE_B + (b_row + 32 * j) * 16);
+      xb[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+          *reinterpret_cast<const uint32_t*>(base + L::B_SC + (b_row + 32 * j) * 4) >> (16 * h),
+          1.0f, false);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      half8_t af[TM], bf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const uint32_t wd = kk == 0 ? ca[i].x : kk == 1 ? ca[i].y : kk == 2 ? ca[i].z : ca[i].w;
+        const half2_t sc = kk < 2 ? half2_t{xa[i][0], xa[i][0]} : half2_t{xa[i][1], xa[i][1]};
+        const uint4 d = deq8(wd, sc);
+        af[i] = __builtin_bit_cast(half8_t, d);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const uint32_t wd = kk == 0 ? cb[j].x : kk == 1 ? cb[j].y : kk == 2 ? cb[j].z : cb[j].w;
+        const half2_t sc = kk < 2 ? half2_t{xb[j][0], xb[j][0]} : half2_t{xb[j][1], xb[j][1]};
+        const uint4 d = deq8(wd, sc);
+        bf[j] = __builtin_bit_cast(half8_t, d);
+        if (HAS_MEAN && wm == 0) {
+          const uint4 m4 = *reinterpret_cast<const uint4*>(Ms + k0 + 32 * h + 8 * kk);
+          float a = rho_acc[j];
+          a = __builtin_amdgcn_fdot2(h2(d.x), h2(m4.x), a, false);
+          a = __builtin_amdgcn_fdot2(h2(d.y), h2(m4.y), a, false);
+          a = __builtin_amdgcn_fdot2(h2(d.z), h2(m4.z), a, false);
+          a = __builtin_amdgcn_fdot2(h2(d.w), h2(m4.w), a, false);
+          rho_acc[j] = a;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  const int nk = (int)(k / BK);
+  auto step = [&](int it, int slot, bool refill, bool next) {
+    if (refill) gload(slot, (int64_t)(it + PF) * BK);
+    __builtin_amdgcn_sched_barrier(0);   // prefetch loads first (see k_gemm_fast)
+    mfma_stage(it & 1, (int64_t)it * BK);
+    if (!next) mfma_drain();
+    if (next) stage((slot + 1) % PF, (it + 1) & 1);
+    __syncthreads();
+  };
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+    if (p < nk) gload(p, (int64_t)p * BK);
+  stage(0, 0);
+  __syncthreads();
+  int it = 0;
+  for (; it + 2 * PF - 1 < nk; it += PF) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) step(it + u, u, true, true);
+  }
+#pragma unroll
+  for (int u = 0; u < 2 * PF - 1; ++u) {
+    const int i2 = it + u;
+    if (i2 < nk) step(i2, u % PF, i2 + PF < nk, i2 + 1 < nk);
+  }
+
+  float rho_col[TN];
+  if (HAS_MEAN) {
+    // lanes l and l + 32 hold the two k-halves of the same column
+    if (wm == 0) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const float o = __shfl_xor(rho_acc[j], 32, 64);
+        if (h == 0) rho_sh[b_row + 32 * j] = rho_acc[j] + o;
+      }
+    }
+    __syncthreads();
+    const float sd = MU.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) rho_col[j] = rho_sh[b_row + 32 * j] * sd;
+  }
+
+  const float alpha = A.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
+  const bool full = (m0 + BM <= m_end) && (n0 + BN <= n);
+  const int64_t row_base = m0 + wm * 32 * TM + h * 4;
+  const int64_t col_base = n0 + b_row;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int64_t col = col_base + j * 32;
+    const float r1 = HAS_MEAN ? rho_col[j] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = row_base + i * 32 + (v >> 2) * 8 + (v & 3);
+        if (!full && (row >= m_end || col >= n)) continue;
+        const float y = acc[i][j][v] * alpha + r1;
+        // non-temporal: the output streams out without evicting the
+        // operand tiles the XCD's other workgroups are reading from L2
+        if (OUT_BF16)
+          __builtin_nontemporal_store(f32_to_bf16_rne(y), static_cast<uint16_t*>(c) + row * ldc + col);
+        else
+          __builtin_nontemporal_store(y, static_cast<float*>(c) + row * ldc + col);
+      }
+    }
+  }
+}
+
+static size_t raw_lds_bytes(int tm, int tn, int64_t k, bool has_mean) {
+  const int bm = 64 * tm, bn = 64 * tn;
+  const size_t stage = (size_t)(2 * (bm * 16 + 128) + bm * 4 + 2 * (bn * 16 + 128) + bn * 4);
+  return 2 * stage + (size_t)bn * 4 + (has_mean ? (size_t)k * 2 : 0);
 }
 
 // dynamic LDS of k_gemm_fast
@@ -514,22 +819,53 @@ size_t gemm_ws_bytes(int64_t n, int nseg) {
   return (size_t)(n * (int64_t)(nseg > 0 ? nseg : 1) * 4 + 255) & ~(size_t)255;
 }
 
-template <int TM, int TN, int PF, bool OB, bool HM>
+template <int TM, int TN, int PF, bool OB, bool HM, int WM = 2, int WN = 2>
 static hipError_t launch_fast(const QOperand& a, const QOperand& mu, const QOperand& b, int64_t m,
                               int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
                               int64_t ldc, hipStream_t st) {
-  const size_t lds = fast_lds_bytes(TM, TN, k, HM);
+  constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
+  const size_t lds = fast_lds_bytes(BM / 64, BN / 64, k, HM);
   static bool attr_set = false;   // per instantiation; the attribute is idempotent
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_fast<TM, TN, PF, OB, HM>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_fast<TM, TN, WM, WN, PF, OB, HM>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t tiles_m = chunk_upper_bound(m, offs ? nseg : 1, BM);
+  dim3 g((unsigned)((n + BN - 1) / BN), (unsigned)tiles_m);
+  k_gemm_fast<TM, TN, WM, WN, PF, OB, HM><<<g, 64 * WM * WN, lds, st>>>(a, b, mu, m, n, k, offs, nseg, c, ldc);
+  return hipGetLastError();
+}
+
+template <int TM, int TN, int PF, bool OB, bool HM>
+static hipError_t launch_raw(const QOperand& a, const QOperand& mu, const QOperand& b, int64_t m,
+                             int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
+                             int64_t ldc, hipStream_t st) {
+  const size_t lds = raw_lds_bytes(TM, TN, k, HM);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_raw<TM, TN, PF, OB, HM>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t tiles_m = chunk_upper_bound(m, offs ? nseg : 1, 64 * TM);
   dim3 g((unsigned)((n + 64 * TN - 1) / (64 * TN)), (unsigned)tiles_m);
-  k_gemm_fast<TM, TN, PF, OB, HM><<<g, 256, lds, st>>>(a, b, mu, m, n, k, offs, nseg, c, ldc);
+  k_gemm_raw<TM, TN, PF, OB, HM><<<g, 256, lds, st>>>(a, b, mu, m, n, k, offs, nseg, c, ldc);
   return hipGetLastError();
+}
+
+template <int TM, int TN>
+static hipError_t launch_raw_any(const QOperand& a, const QOperand* mean, const QOperand& b,
+                                 int64_t m, int64_t n, int64_t k, const int64_t* offs, int nseg,
+                                 void* c, bool c_bf16, int64_t ldc, hipStream_t st) {
+  const QOperand mu = mean ? *mean : QOperand{nullptr, nullptr, nullptr};
+  if (c_bf16)
+    return mean ? launch_raw<TM, TN, 2, true, true>(a, mu, b, m, n, k, offs, nseg, c, ldc, st)
+                : launch_raw<TM, TN, 2, true, false>(a, mu, b, m, n, k, offs, nseg, c, ldc, st);
+  return mean ? launch_raw<TM, TN, 2, false, true>(a, mu, b, m, n, k, offs, nseg, c, ldc, st)
+              : launch_raw<TM, TN, 2, false, false>(a, mu, b, m, n, k, offs, nseg, c, ldc, st);
 }
 
 template <int TM, int TN, int PF>
@@ -544,23 +880,28 @@ static hipError_t launch_fast_any(const QOperand& a, const QOperand* mean, const
               : launch_fast<TM, TN, PF, false, false>(a, mu, b, m, n, k, offs, nseg, c, ldc, st);
 }
 
-// Tile shape for the fast kernel: the fewest "tile-area rounds" over the 256
-// CUs (one workgroup per CU), with a small penalty for the narrower tiles'
-// higher LDS traffic per MFMA.  Returns 0 if the fast kernel does not apply.
+// Tile shape for the fast kernel, by estimated time: rounds of workgroups
+// over the 256 CUs times the work of one round, with an efficiency factor per
+// variant measured on the Qwen3-0.6B shapes (the 8-wave variants run two
+// waves per SIMD and overlap one wave's dequantization with the other's
+// MFMAs).  Returns 0 if the fast kernel does not apply.
+//   1: 256x256, 4 waves   2: 256x128, 4 waves   3: 128x128, 4 waves (2 per CU)
+//   4: 256x256, 8 waves   5: 256x128, 8 waves
 static int pick_tile(int64_t m, int64_t n, int64_t k, int nseg_eff, bool has_mean) {
   if (k % BK != 0) return 0;
-  struct Cand { int tm, tn; double eff; };
-  const Cand cands[3] = {{4, 4, 1.0}, {4, 2, 0.85}, {2, 2, 0.7}};
+  struct Cand { int id, bm, bn, per_cu; double eff; };
+  const Cand cands[5] = {{5, 256, 128, 1, 1.0}, {4, 256, 256, 1, 0.95}, {3, 128, 128, 2, 0.9},
+                         {2, 256, 128, 1, 0.85}, {1, 256, 256, 1, 0.8}};
   int best = 0;
   double best_cost = 0;
-  for (int i = 0; i < 3; ++i) {
-    const Cand& cd = cands[i];
-    if (fast_lds_bytes(cd.tm, cd.tn, k, has_mean) > kLdsLimit) continue;
-    const int64_t tiles = chunk_upper_bound(m, nseg_eff, 64 * cd.tm) * ((n + 64 * cd.tn - 1) / (64 * cd.tn));
-    const double rounds = (double)((tiles + 255) / 256);
-    const double cost = rounds * (64.0 * cd.tm) * (64.0 * cd.tn) / cd.eff;
+  for (const Cand& cd : cands) {
+    if (fast_lds_bytes(cd.bm / 64, cd.bn / 64, k, has_mean) * cd.per_cu > kLdsLimit) continue;
+    const int64_t tiles = chunk_upper_bound(m, nseg_eff, cd.bm) * ((n + cd.bn - 1) / cd.bn);
+    const int64_t slots = 256 * cd.per_cu;
+    const double rounds = (double)((tiles + slots - 1) / slots);
+    const double cost = rounds * cd.bm * cd.bn * cd.per_cu / cd.eff;
     if (best == 0 || cost < best_cost) {
-      best = i + 1;
+      best = cd.id;
       best_cost = cost;
     }
   }
@@ -572,31 +913,52 @@ hipError_t launch_gemm(const QOperand& a, const QOperand* mean, const QOperand& 
                        int64_t ldc, float* rho_ws, hipStream_t st) {
   if (m == 0 || n == 0) return hipGetLastError();
   int choice = pick_tile(m, n, k, offs ? nseg : 1, mean != nullptr);
-  // tuning override: AVERIS_GEMM_TILE = 1 (256x256), 2 (256x128), 3 (128x128)
+  // tuning override: AVERIS_GEMM_TILE = 1..5 (see pick_tile)
   static const int forced = [] {
     const char* e = std::getenv("AVERIS_GEMM_TILE");
     return e ? std::atoi(e) : 0;
   }();
-  if (choice != 0 && forced >= 1 && forced <= 3 &&
-      fast_lds_bytes(forced == 3 ? 2 : 4, forced == 1 ? 4 : 2, k, mean != nullptr) <= kLdsLimit)
-    choice = forced;
+  if (choice != 0 && forced >= 1 && forced <= 5) {
+    const int tm = (forced == 3) ? 2 : 4, tn = (forced == 1 || forced == 4) ? 4 : 2;
+    if (fast_lds_bytes(tm, tn, k, mean != nullptr) <= kLdsLimit) choice = forced;
+  }
   static const int pf = [] {
     const char* e = std::getenv("AVERIS_GEMM_PF");
     return e ? std::atoi(e) : 2;
   }();
+  // raw-code kernel for the 256-wide 4-wave tiles: opt-in (AVERIS_GEMM_RAW = 1);
+  // it measured slower than the fp16-LDS kernel on the Qwen3-0.6B shapes
+  static const int raw = [] {
+    const char* e = std::getenv("AVERIS_GEMM_RAW");
+    return e ? std::atoi(e) : 0;
+  }();
+  if (raw && choice == 1 && raw_lds_bytes(4, 4, k, mean != nullptr) <= kLdsLimit)
+    return launch_raw_any<4, 4>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+  if (raw && choice == 2 && raw_lds_bytes(4, 2, k, mean != nullptr) <= kLdsLimit)
+    return launch_raw_any<4, 2>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+  const QOperand mu = mean ? *mean : QOperand{nullptr, nullptr, nullptr};
 #define AVERIS_FAST(TM_, TN_)                                                               \
   switch (pf) {                                                                            \
     case 1: return launch_fast_any<TM_, TN_, 1>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st); \
     case 3: return launch_fast_any<TM_, TN_, 3>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st); \
     default: return launch_fast_any<TM_, TN_, 2>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st); \
   }
+#define AVERIS_FAST8(TM_, TN_)                                                              \
+  if (c_bf16)                                                                              \
+    return mean ? launch_fast<TM_, TN_, 2, true, true, 4, 2>(a, mu, b, m, n, k, offs, nseg, c, ldc, st) \
+                : launch_fast<TM_, TN_, 2, true, false, 4, 2>(a, mu, b, m, n, k, offs, nseg, c, ldc, st); \
+  return mean ? launch_fast<TM_, TN_, 2, false, true, 4, 2>(a, mu, b, m, n, k, offs, nseg, c, ldc, st) \
+              : launch_fast<TM_, TN_, 2, false, false, 4, 2>(a, mu, b, m, n, k, offs, nseg, c, ldc, st);
   switch (choice) {
     case 1: AVERIS_FAST(4, 4)
     case 2: AVERIS_FAST(4, 2)
     case 3: AVERIS_FAST(2, 2)
+    case 4: AVERIS_FAST8(2, 4)
+    case 5: AVERIS_FAST8(2, 2)
     default: break;
   }
 #undef AVERIS_FAST
+#undef AVERIS_FAST8
   // general path (K % 64 != 0, or a mean vector too long for LDS)
   const int ns = offs ? nseg : 1;
   if (mean) {

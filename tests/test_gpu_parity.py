@@ -166,6 +166,32 @@ def test_deterministic_repeats():
         assert torch.equal(m.codes, outs[0][1].codes) and torch.equal(mu, outs[0][2])
 
 
+@pytest.mark.parametrize("l,m,n", [(1000, 320, 192), (300, 64, 128), (256, 128, 64),
+                                   (8192, 1024, 3072)])
+def test_gemm_bitwise_repeatable(l, m, n):
+    # Regression: on the exit path of the K loop the epilogue read the last
+    # MFMA's accumulator before it completed (missing wait states); results
+    # then varied between runs.  Repeated runs must agree bit for bit, and
+    # with the oracle.
+    cfg = workloads.config1(l=l, m=m, n=n)
+    wt, wd = quant_weights(cfg["w"].cuda())
+    xr, xm, _ = av.averis_split_quant(cfg["x"].cuda(), seed=3)
+    dr, dm, _ = av.averis_split_quant(cfg["d"].cuda(), seed=4)
+    for fn, a, mu, b in [(av.averis_gemm_fwd, xr, xm, wt), (av.averis_gemm_dgrad, dr, dm, wd)]:
+        outs = [fn(a, mu, b, out_dtype=torch.float32) for _ in range(5)]
+        for o in outs[1:]:
+            assert torch.equal(o, outs[0])
+        vo = [av.averis_gemm_vanilla(a, b, out_dtype=torch.bfloat16) for _ in range(3)]
+        for o in vo[1:]:
+            assert torch.equal(o, vo[0])
+    if l <= 1000:
+        wq = orc.weight_quant(f32(cfg["w"]), "rn")
+        s = orc.split_quant(f32(cfg["d"]), "sr", 4)
+        c = av.averis_gemm_dgrad(dr, dm, wd, out_dtype=torch.float32)
+        assert_gemm_close(c, orc.gemm(s["residual"], wq["dgrad"], s["mean"]),
+                          orc.gemm_abs_bound(s["residual"], wq["dgrad"], s["mean"]))
+
+
 def sampled_rows_check(a, seed, ranges):
     """Full-size split-quant: mean and scales exact; residual rows exact on
     the sampled contiguous row ranges (the oracle quantizes only those)."""
@@ -195,6 +221,28 @@ def test_full_size_config1_sampled(which):
     res, mean, mean_ref, refs = sampled_rows_check(a, 0, ranges)
     w = cfg["w"].cuda()
     wt_g, wd_g = quant_weights(w)
+    wq = orc.weight_quant(f32(cfg["w"]), "rn")
+    b_g, b_ref = (wt_g, wq["fwd"]) if which == "x" else (wd_g, wq["dgrad"])
+    fn = av.averis_gemm_fwd if which == "x" else av.averis_gemm_dgrad
+    c = fn(res, mean, b_g, out_dtype=torch.float32)
+    b_deq = orc.dequantize(b_ref)
+    m_deq = orc.dequantize(mean_ref)[0]
+    for (r0, r1), q in refs.items():
+        a_deq = orc.dequantize(q)
+        ref = a_deq @ b_deq.T + (m_deq @ b_deq.T)[None, :]
+        bound = np.abs(a_deq) @ np.abs(b_deq).T + (np.abs(m_deq) @ np.abs(b_deq).T)[None, :]
+        assert_gemm_close(c[r0:r1], ref, bound)
+
+
+@pytest.mark.parametrize("which", ["x", "d"])
+def test_full_size_config2_sampled(which):
+    # down-proj: SwiGLU-like positive-mean X (8192 x 3072), D 8192 x 1024
+    cfg = workloads.config2()
+    a = cfg[which]
+    l = a.shape[0]
+    ranges = [(0, 16), (5000, 5016), (l - 16, l)]
+    res, mean, mean_ref, refs = sampled_rows_check(a, 0, ranges)
+    wt_g, wd_g = quant_weights(cfg["w"].cuda())
     wq = orc.weight_quant(f32(cfg["w"]), "rn")
     b_g, b_ref = (wt_g, wq["fwd"]) if which == "x" else (wd_g, wq["dgrad"])
     fn = av.averis_gemm_fwd if which == "x" else av.averis_gemm_dgrad
