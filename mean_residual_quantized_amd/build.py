@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libaveris.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "quant.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "quant.hip", "gemm.hip", "gemm_ws.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -102,7 +102,7 @@ size_t averis_workspace_bytes(averis_op_t op, int64_t rows, int64_t cols, int64_
     }
     case AVERIS_OP_GEMM:
       if (n < 0) return 0;
-      return gemm_ws_bytes(n, (int)nseg);
+      return gemm_ws_bytes(n, cols, (int)nseg);
   }
   return 0;
 }
@@ -259,7 +259,7 @@ static averis_status_t gemm_common(const averis_nvfp4_t* a, const averis_nvfp4_t
   if (ldc < n) return AVERIS_E_SHAPE;
   if (m > 0 && n > 0 && !c) return AVERIS_E_NULL;
   if (!aligned(c, elem_size(cdtype))) return AVERIS_E_ALIGN;
-  const size_t need = mean ? gemm_ws_bytes(n, (int)ns) : 0;
+  const size_t need = mean ? gemm_ws_bytes(n, k, (int)ns) : 0;
   if (need && (!ws || ws_bytes < need)) return AVERIS_E_WORKSPACE;
   if (ws && !aligned(ws, 256)) return AVERIS_E_ALIGN;
   const QOperand qa{a->codes, a->scales, a->tscale};
@@ -267,7 +267,7 @@ static averis_status_t gemm_common(const averis_nvfp4_t* a, const averis_nvfp4_t
   QOperand qm{};
   if (mean) qm = QOperand{mean->codes, mean->scales, mean->tscale};
   return hip_status(launch_gemm(qa, mean ? &qm : nullptr, qb, m, n, k, offs, nseg, c,
-                                cdtype == AVERIS_BF16, ldc, static_cast<float*>(ws), stream));
+                                cdtype == AVERIS_BF16, ldc, ws, stream));
 }
 
 averis_status_t averis_gemm_fwd(const averis_nvfp4_t* xr, const averis_nvfp4_t* mean,

@@ -22,13 +22,12 @@
 
 #include <cstdlib>
 
+#include "gemm_common.hpp"
 #include "launch.hpp"
 #include "segments.hpp"
 
 namespace averis {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 namespace {
 
@@ -85,21 +84,8 @@ __device__ __forceinline__ void stage_rows(const uint8_t* codes, const uint8_t* 
   }
 }
 
-// After the last MFMA of a K loop: its accumulators must not be read for
-// ~18 wait states (32x32 f16 MFMA, 8 passes).  The compiler's hazard check
-// misses this when the loop exits through a branch straight into a barrier,
-// so every kernel fences explicitly before its epilogue reads them.
-__device__ __forceinline__ void mfma_drain() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  const uint32_t b = __float_as_uint(f);
-  if ((b & 0x7F800000u) == 0x7F800000u) return (uint16_t)((b >> 16) | ((b & 0xFFFFu) ? 0x40u : 0u));
-  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
-}
+
 
 }  // namespace
 
@@ -171,12 +157,10 @@ __global__ __launch_bounds__(256) void k_gemm_nt(QOperand A, QOperand B, int64_t
         const int64_t row = m0 + wm * 64 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
         if (row >= m_end) continue;
         const float y = acc[i][j][v] * alpha + r1;
-        // non-temporal: the output streams out without evicting the
-        // operand tiles the XCD's other workgroups are reading from L2
         if (OUT_BF16)
-          __builtin_nontemporal_store(f32_to_bf16_rne(y), static_cast<uint16_t*>(c) + row * ldc + col);
+          store_out(f32_to_bf16_rne(y), static_cast<uint16_t*>(c) + row * ldc + col);
         else
-          __builtin_nontemporal_store(y, static_cast<float*>(c) + row * ldc + col);
+          store_out(y, static_cast<float*>(c) + row * ldc + col);
       }
     }
 }
@@ -194,20 +178,7 @@ __global__ __launch_bounds__(256) void k_gemm_nt(QOperand A, QOperand B, int64_t
 // ---------------------------------------------------------------------------
 namespace {
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ half2_t h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
-__device__ __forceinline__ uint32_t u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
-
-// 8 codes of one dword -> 4 x (2 x fp16), times the block scale s2 = (s, s)
-__device__ __forceinline__ uint4 deq8(uint32_t w, half2_t s2) {
-  uint4 r;
-  r.x = u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2);
-  r.y = u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2);
-  r.z = u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2);
-  r.w = u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2);
-  return r;
-}
 
 __device__ __forceinline__ half2_t scale_h2(uint32_t byte) {
   const _Float16 s = (_Float16)e4m3_value(byte & 0xFFu);
@@ -215,9 +186,9 @@ __device__ __forceinline__ half2_t scale_h2(uint32_t byte) {
   return r;
 }
 
+
 }  // namespace
 
-constexpr int kXcds = 8;   // MI355X: 8 accelerator complex dies, one L2 each
 
 #ifndef AVERIS_GEMM_INTERLEAVE
 #define AVERIS_GEMM_INTERLEAVE 0
@@ -334,7 +305,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_fast(QOperand A, QOper
     for (int i = 0; i < CA; ++i) {
       const int q = t + NT * i, row = q >> 1, hf = q & 1;
       if (q >= 2 * BM) break;
-      const half2_t s0 = scale_h2(sa[slot][i]), s1 = scale_h2(sa[slot][i] >> 8);
+      const half2_t sc = scales2(sa[slot][i]);
+      const half2_t s0 = {sc.x, sc.x}, s1 = {sc.y, sc.y};
       uint4* dst = reinterpret_cast<uint4*>(as + row * LDSK + 32 * hf);
       dst[0] = deq8(ra[slot][i].x, s0);
       dst[1] = deq8(ra[slot][i].y, s0);
@@ -345,7 +317,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_fast(QOperand A, QOper
     for (int i = 0; i < CB; ++i) {
       const int q = t + NT * i, row = q >> 1, hf = q & 1;
       if (q >= 2 * BN) break;
-      const half2_t s0 = scale_h2(sb[slot][i]), s1 = scale_h2(sb[slot][i] >> 8);
+      const half2_t sc = scales2(sb[slot][i]);
+      const half2_t s0 = {sc.x, sc.x}, s1 = {sc.y, sc.y};
       uint4 d[4];
       d[0] = deq8(rb[slot][i].x, s0);
       d[1] = deq8(rb[slot][i].y, s0);
@@ -397,7 +370,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_fast(QOperand A, QOper
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
     }
   };
 
@@ -450,7 +423,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_fast(QOperand A, QOper
     if (i2 < nk) step(i2, u % PF, i2 + PF < nk, i2 + 1 < nk);
   }
 
-  float rho_col[TN];
   if (HAS_MEAN) {
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
@@ -459,315 +431,61 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_fast(QOperand A, QOper
       rho_sh[hf * BN + row] = rho_acc[i];
     }
     __syncthreads();
+    // each column's two k-half sums, times the tensor scales, in place
     const float sd = MU.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = wn * 32 * TN + j * 32 + (lane & 31);
-      rho_col[j] = (rho_sh[col] + rho_sh[BN + col]) * sd;
-    }
+    for (int cidx = t; cidx < BN; cidx += NT) rho_sh[cidx] = (rho_sh[cidx] + rho_sh[BN + cidx]) * sd;
+    __syncthreads();
   }
 
+  // The MFMAs take the B fragment first, so a lane's accumulators hold four
+  // consecutive output columns (v & 3) of one output row: 8-byte (bf16) or
+  // 16-byte (fp32) stores.
   const float alpha = A.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
   const bool full = (m0 + BM <= m_end) && (n0 + BN <= n);
-  const int64_t row_base = m0 + wm * 32 * TM + (lane >> 5) * 4;
-  const int64_t col_base = n0 + wn * 32 * TN + (lane & 31);
+  const bool vec = full && (ldc % 4 == 0) &&
+                   ((reinterpret_cast<uintptr_t>(c) & (OUT_BF16 ? 7 : 15)) == 0);
+  const int64_t row_base = m0 + wm * 32 * TM + (lane & 31);
+  const int cl_base = wn * 32 * TN + (lane >> 5) * 4;   // tile-local column of v = 0
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
-    const int64_t col = col_base + j * 32;
-    const float r1 = HAS_MEAN ? rho_col[j] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = row_base + i * 32 + (v >> 2) * 8 + (v & 3);
-        if (!full && (row >= m_end || col >= n)) continue;
-        const float y = acc[i][j][v] * alpha + r1;
-        // non-temporal: the output streams out without evicting the
-        // operand tiles the XCD's other workgroups are reading from L2
-        if (OUT_BF16)
-          __builtin_nontemporal_store(f32_to_bf16_rne(y), static_cast<uint16_t*>(c) + row * ldc + col);
-        else
-          __builtin_nontemporal_store(y, static_cast<float*>(c) + row * ldc + col);
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Raw-code variant (K % 64 == 0): the LDS stages hold the 4-bit codes and
-// E4M3 bytes as loaded (4x less LDS traffic than fp16 operands); each wave
-// dequantizes its own MFMA fragments right before use.  A lane's 8 operand
-// values per MFMA k-step are 8 consecutive codes of one 16-block: lanes
-// 0..31 take k in [0, 32) of the 64-wide stage and lanes 32..63 k in
-// [32, 64), one 16-byte LDS read per fragment and stage; A and B use the same
-// k mapping, so the products pair up exactly.  Codes are stored as two
-// half-planes (k-half h of row r at plane h, slot r) so those reads are
-// conflict-free.  The rank-one term is accumulated from the dequantized B
-// fragments by the waves of the first row of the wave grid.
-// ---------------------------------------------------------------------------
-template <int TM, int TN>
-struct RawLds {
-  static constexpr int BM = 64 * TM, BN = 64 * TN;
-  static constexpr int PLANE_A = BM * 16 + 128;   // bytes per k-half plane (+pad)
-  static constexpr int PLANE_B = BN * 16 + 128;
-  static constexpr int A_CODES = 0;
-  static constexpr int A_SC = 2 * PLANE_A;
-  static constexpr int B_CODES = A_SC + BM * 4;
-  static constexpr int B_SC = B_CODES + 2 * PLANE_B;
-  static constexpr int STAGE = B_SC + BN * 4;     // bytes per stage buffer
-};
-
-template <int TM, int TN, int PF, bool OUT_BF16, bool HAS_MEAN>
-__global__ __launch_bounds__(256, 1) void k_gemm_raw(QOperand A, QOperand B, QOperand MU,
-                                                     int64_t m, int64_t n, int64_t k,
-                                                     const int64_t* offs, int nseg, void* c,
-                                                     int64_t ldc) {
-  using L = RawLds<TM, TN>;
-  constexpr int BM = L::BM, BN = L::BN;
-  constexpr int CA = BM / 128, CB = BN / 128;   // 16-byte code chunks per thread and stage
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
-  uint8_t* stg = smem_raw;                                        // [2][STAGE]
-  float* rho_sh = reinterpret_cast<float*>(smem_raw + 2 * L::STAGE);   // [BN]
-  _Float16* Ms = reinterpret_cast<_Float16*>(rho_sh + BN);        // [k]
-
-  int64_t tile_x, tile_y;
-  {
-    const int64_t gx = gridDim.x, total = gx * gridDim.y;
-    const int64_t lin = (int64_t)blockIdx.y * gx + blockIdx.x;
-    const int64_t even = total - total % kXcds;
-    int64_t id = lin;
-    if (lin < even) id = (lin % kXcds) * (even / kXcds) + lin / kXcds;
-    tile_y = id / gx;
-    tile_x = id - tile_y * gx;
-  }
-  const SegRange sr = locate_chunk(offs, nseg, m, BM, tile_y);
-  if (sr.seg < 0) return;
-  const int seg = sr.seg;
-  const int64_t m0 = sr.r0, m_end = sr.r1;
-  const int64_t n0 = tile_x * BN;
-  const int64_t kh = k >> 1, kb = k >> 4;
-  const uint8_t* bcodes = B.codes + (offs ? (int64_t)seg * n * kh : 0);
-  const uint8_t* bscales = B.scales + (offs ? (int64_t)seg * n * kb : 0);
-
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  const int h = lane >> 5, lr = lane & 31;
-
-  if (HAS_MEAN) {
-    const uint8_t* mcodes = MU.codes + (int64_t)seg * kh;
-    const uint8_t* mscales = MU.scales + (int64_t)seg * kb;
-    for (int64_t q = t; q < (k >> 3); q += 256) {
-      const uint32_t wq = *reinterpret_cast<const uint32_t*>(mcodes + 4 * q);
-      reinterpret_cast<uint4*>(Ms)[q] = deq8(wq, scale_h2(mscales[q >> 1]));
-    }
-  }
-
-  // staging: code chunk q = t + 256 i -> row q >> 1, k-half q & 1 (16 bytes);
-  // scale dword of row t (and t + 256 ...) per stage
-  const uint8_t* a_c = A.codes + m0 * kh;
-  const uint8_t* a_s = A.scales + m0 * kb;
-  const uint8_t* b_c = bcodes + n0 * kh;
-  const uint8_t* b_s = bscales + n0 * kb;
-  uint32_t oac[CA], obc[CB], oas[CA], obs[CB];
-#pragma unroll
-  for (int i = 0; i < CA; ++i) {
-    const int q = t + 256 * i, hf = q & 1;
-    const int64_t row = (q >> 1) < (m_end - m0) ? (q >> 1) : (m_end - m0 - 1);
-    oac[i] = (uint32_t)(row * kh) + 16u * hf;
-  }
-#pragma unroll
-  for (int i = 0; i < CB; ++i) {
-    const int q = t + 256 * i, hf = q & 1;
-    const int64_t row = (q >> 1) < (n - n0) ? (q >> 1) : (n - n0 - 1);
-    obc[i] = (uint32_t)(row * kh) + 16u * hf;
-  }
-  constexpr int SA = (BM + 255) / 256, SB = (BN + 255) / 256;   // scale dwords per thread
-#pragma unroll
-  for (int i = 0; i < SA; ++i) {
-    const int r = t + 256 * i;
-    const int64_t row = r < (m_end - m0) ? r : (m_end - m0 - 1);
-    oas[i] = (uint32_t)(row * kb);
-  }
-#pragma unroll
-  for (int i = 0; i < SB; ++i) {
-    const int r = t + 256 * i;
-    const int64_t row = r < (n - n0) ? r : (n - n0 - 1);
-    obs[i] = (uint32_t)(row * kb);
-  }
-
-  uint4 ra[PF][CA], rb[PF][CB];
-  uint32_t sa[PF][SA], sb[PF][SB];
-  auto gload = [&](int slot, int64_t k0) {
-    const uint8_t* ac = a_c + (k0 >> 1);
-    const uint8_t* bc = b_c + (k0 >> 1);
-#pragma unroll
-    for (int i = 0; i < CA; ++i) ra[slot][i] = *reinterpret_cast<const uint4*>(ac + oac[i]);
-#pragma unroll
-    for (int i = 0; i < CB; ++i) rb[slot][i] = *reinterpret_cast<const uint4*>(bc + obc[i]);
-#pragma unroll
-    for (int i = 0; i < SA; ++i)
-      if (t + 256 * i < BM) sa[slot][i] = *reinterpret_cast<const uint32_t*>(a_s + (k0 >> 4) + oas[i]);
-#pragma unroll
-    for (int i = 0; i < SB; ++i)
-      if (t + 256 * i < BN) sb[slot][i] = *reinterpret_cast<const uint32_t*>(b_s + (k0 >> 4) + obs[i]);
-  };
-  auto stage = [&](int slot, int buf) {
-    uint8_t* base = stg + buf * L::STAGE;
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int q = t + 256 * i, row = q >> 1, hf = q & 1;
-      *reinterpret_cast<uint4*>(base + L::A_CODES + hf * L::PLANE_A + row * 16) = ra[slot][i];
-    }
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int q = t + 256 * i, row = q >> 1, hf = q & 1;
-      *reinterpret_cast<uint4*>(base + L::B_CODES + hf * L::PLANE_B + row * 16) = rb[slot][i];
-    }
-#pragma unroll
-    for (int i = 0; i < SA; ++i)
-      if (t + 256 * i < BM)
-        *reinterpret_cast<uint32_t*>(base + L::A_SC + (t + 256 * i) * 4) = sa[slot][i];
-#pragma unroll
-    for (int i = 0; i < SB; ++i)
-      if (t + 256 * i < BN)
-        *reinterpret_cast<uint32_t*>(base + L::B_SC + (t + 256 * i) * 4) = sb[slot][i];
-  };
-
-  f32x16_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-  float rho_acc[TN];
-#pragma unroll
-  for (int j = 0; j < TN; ++j) rho_acc[j] = 0.0f;
-
-  const int a_row = wm * 32 * TM + lr, b_row = wn * 32 * TN + lr;
-  auto mfma_stage = [&](int buf, int64_t k0) {
-    const uint8_t* base = stg + buf * L::STAGE;
-    uint4 ca[TM], cb[TN];
-    half2_t xa[TM], xb[TN];   // the lane's two block scales (blocks 2h, 2h + 1), exact
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      ca[i] = *reinterpret_cast<const uint4*>(base + L::A_CODES + h * L::PLANE_A + (a_row + 32 * i) * 16);
-      xa[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
-          *reinterpret_cast<const uint32_t*>(base + L::A_SC + (a_row + 32 * i) * 4) >> (16 * h),
-          1.0f, false);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      cb[j] = *reinterpret_cast<const uint4*>(base + L::B_CODES + h * L::PLANE_B + (b_row + 32 * j) * 16);
-      xb[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
-          *reinterpret_cast<const uint32_t*>(base + L::B_SC + (b_row + 32 * j) * 4) >> (16 * h),
-          1.0f, false);
-    }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      half8_t af[TM], bf[TN];
+    for (int q = 0; q < 4; ++q) {
+      const int cl = cl_base + j * 32 + 8 * q;
+      const int64_t col = n0 + cl;
+      f32x4_t r1 = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (HAS_MEAN) r1 = *reinterpret_cast<const f32x4_t*>(rho_sh + cl);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const uint32_t wd = kk == 0 ? ca[i].x : kk == 1 ? ca[i].y : kk == 2 ? ca[i].z : ca[i].w;
-        const half2_t sc = kk < 2 ? half2_t{xa[i][0], xa[i][0]} : half2_t{xa[i][1], xa[i][1]};
-        const uint4 d = deq8(wd, sc);
-        af[i] = __builtin_bit_cast(half8_t, d);
-      }
+        const int64_t row = row_base + i * 32;
+        float y[4];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const uint32_t wd = kk == 0 ? cb[j].x : kk == 1 ? cb[j].y : kk == 2 ? cb[j].z : cb[j].w;
-        const half2_t sc = kk < 2 ? half2_t{xb[j][0], xb[j][0]} : half2_t{xb[j][1], xb[j][1]};
-        const uint4 d = deq8(wd, sc);
-        bf[j] = __builtin_bit_cast(half8_t, d);
-        if (HAS_MEAN && wm == 0) {
-          const uint4 m4 = *reinterpret_cast<const uint4*>(Ms + k0 + 32 * h + 8 * kk);
-          float a = rho_acc[j];
-          a = __builtin_amdgcn_fdot2(h2(d.x), h2(m4.x), a, false);
-          a = __builtin_amdgcn_fdot2(h2(d.y), h2(m4.y), a, false);
-          a = __builtin_amdgcn_fdot2(h2(d.z), h2(m4.z), a, false);
-          a = __builtin_amdgcn_fdot2(h2(d.w), h2(m4.w), a, false);
-          rho_acc[j] = a;
+        for (int e = 0; e < 4; ++e) y[e] = acc[i][j][4 * q + e] * alpha + r1[e];
+        if (vec) {
+          if (OUT_BF16) {
+            const u32x2_t pk = {(uint32_t)f32_to_bf16_rne(y[0]) | ((uint32_t)f32_to_bf16_rne(y[1]) << 16),
+                                (uint32_t)f32_to_bf16_rne(y[2]) | ((uint32_t)f32_to_bf16_rne(y[3]) << 16)};
+            store_out(pk, reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(c) + row * ldc + col));
+          } else {
+            const f32x4_t v4 = {y[0], y[1], y[2], y[3]};
+            store_out(v4, reinterpret_cast<f32x4_t*>(static_cast<float*>(c) + row * ldc + col));
+          }
+        } else if (row < m_end) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (col + e >= n) break;
+            if (OUT_BF16)
+              store_out(f32_to_bf16_rne(y[e]), static_cast<uint16_t*>(c) + row * ldc + col + e);
+            else
+              store_out(y[e], static_cast<float*>(c) + row * ldc + col + e);
+          }
         }
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  const int nk = (int)(k / BK);
-  auto step = [&](int it, int slot, bool refill, bool next) {
-    if (refill) gload(slot, (int64_t)(it + PF) * BK);
-    __builtin_amdgcn_sched_barrier(0);   // prefetch loads first (see k_gemm_fast)
-    mfma_stage(it & 1, (int64_t)it * BK);
-    if (!next) mfma_drain();
-    if (next) stage((slot + 1) % PF, (it + 1) & 1);
-    __syncthreads();
-  };
-#pragma unroll
-  for (int p = 0; p < PF; ++p)
-    if (p < nk) gload(p, (int64_t)p * BK);
-  stage(0, 0);
-  __syncthreads();
-  int it = 0;
-  for (; it + 2 * PF - 1 < nk; it += PF) {
-#pragma unroll
-    for (int u = 0; u < PF; ++u) step(it + u, u, true, true);
-  }
-#pragma unroll
-  for (int u = 0; u < 2 * PF - 1; ++u) {
-    const int i2 = it + u;
-    if (i2 < nk) step(i2, u % PF, i2 + PF < nk, i2 + 1 < nk);
-  }
-
-  float rho_col[TN];
-  if (HAS_MEAN) {
-    // lanes l and l + 32 hold the two k-halves of the same column
-    if (wm == 0) {
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const float o = __shfl_xor(rho_acc[j], 32, 64);
-        if (h == 0) rho_sh[b_row + 32 * j] = rho_acc[j] + o;
-      }
-    }
-    __syncthreads();
-    const float sd = MU.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) rho_col[j] = rho_sh[b_row + 32 * j] * sd;
-  }
-
-  const float alpha = A.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
-  const bool full = (m0 + BM <= m_end) && (n0 + BN <= n);
-  const int64_t row_base = m0 + wm * 32 * TM + h * 4;
-  const int64_t col_base = n0 + b_row;
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int64_t col = col_base + j * 32;
-    const float r1 = HAS_MEAN ? rho_col[j] : 0.0f;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = row_base + i * 32 + (v >> 2) * 8 + (v & 3);
-        if (!full && (row >= m_end || col >= n)) continue;
-        const float y = acc[i][j][v] * alpha + r1;
-        // non-temporal: the output streams out without evicting the
-        // operand tiles the XCD's other workgroups are reading from L2
-        if (OUT_BF16)
-          __builtin_nontemporal_store(f32_to_bf16_rne(y), static_cast<uint16_t*>(c) + row * ldc + col);
-        else
-          __builtin_nontemporal_store(y, static_cast<float*>(c) + row * ldc + col);
       }
     }
   }
 }
 
-static size_t raw_lds_bytes(int tm, int tn, int64_t k, bool has_mean) {
-  const int bm = 64 * tm, bn = 64 * tn;
-  const size_t stage = (size_t)(2 * (bm * 16 + 128) + bm * 4 + 2 * (bn * 16 + 128) + bn * 4);
-  return 2 * stage + (size_t)bn * 4 + (has_mean ? (size_t)k * 2 : 0);
+size_t gemm_ws_bytes(int64_t n, int64_t, int nseg) {
+  return (size_t)(n * (int64_t)(nseg > 0 ? nseg : 1) * 4 + 255) & ~(size_t)255;
 }
 
 // dynamic LDS of k_gemm_fast
@@ -815,9 +533,6 @@ __global__ __launch_bounds__(256) void k_rank1(QOperand M, QOperand B, int64_t n
   }
 }
 
-size_t gemm_ws_bytes(int64_t n, int nseg) {
-  return (size_t)(n * (int64_t)(nseg > 0 ? nseg : 1) * 4 + 255) & ~(size_t)255;
-}
 
 template <int TM, int TN, int PF, bool OB, bool HM, int WM = 2, int WN = 2>
 static hipError_t launch_fast(const QOperand& a, const QOperand& mu, const QOperand& b, int64_t m,
@@ -838,36 +553,6 @@ static hipError_t launch_fast(const QOperand& a, const QOperand& mu, const QOper
   return hipGetLastError();
 }
 
-template <int TM, int TN, int PF, bool OB, bool HM>
-static hipError_t launch_raw(const QOperand& a, const QOperand& mu, const QOperand& b, int64_t m,
-                             int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
-                             int64_t ldc, hipStream_t st) {
-  const size_t lds = raw_lds_bytes(TM, TN, k, HM);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_raw<TM, TN, PF, OB, HM>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  const int64_t tiles_m = chunk_upper_bound(m, offs ? nseg : 1, 64 * TM);
-  dim3 g((unsigned)((n + 64 * TN - 1) / (64 * TN)), (unsigned)tiles_m);
-  k_gemm_raw<TM, TN, PF, OB, HM><<<g, 256, lds, st>>>(a, b, mu, m, n, k, offs, nseg, c, ldc);
-  return hipGetLastError();
-}
-
-template <int TM, int TN>
-static hipError_t launch_raw_any(const QOperand& a, const QOperand* mean, const QOperand& b,
-                                 int64_t m, int64_t n, int64_t k, const int64_t* offs, int nseg,
-                                 void* c, bool c_bf16, int64_t ldc, hipStream_t st) {
-  const QOperand mu = mean ? *mean : QOperand{nullptr, nullptr, nullptr};
-  if (c_bf16)
-    return mean ? launch_raw<TM, TN, 2, true, true>(a, mu, b, m, n, k, offs, nseg, c, ldc, st)
-                : launch_raw<TM, TN, 2, true, false>(a, mu, b, m, n, k, offs, nseg, c, ldc, st);
-  return mean ? launch_raw<TM, TN, 2, false, true>(a, mu, b, m, n, k, offs, nseg, c, ldc, st)
-              : launch_raw<TM, TN, 2, false, false>(a, mu, b, m, n, k, offs, nseg, c, ldc, st);
-}
-
 template <int TM, int TN, int PF>
 static hipError_t launch_fast_any(const QOperand& a, const QOperand* mean, const QOperand& b,
                                   int64_t m, int64_t n, int64_t k, const int64_t* offs, int nseg,
@@ -882,16 +567,16 @@ static hipError_t launch_fast_any(const QOperand& a, const QOperand* mean, const
 
 // Tile shape for the fast kernel, by estimated time: rounds of workgroups
 // over the 256 CUs times the work of one round, with an efficiency factor per
-// variant measured on the Qwen3-0.6B shapes (the 8-wave variants run two
-// waves per SIMD and overlap one wave's dequantization with the other's
-// MFMAs).  Returns 0 if the fast kernel does not apply.
+// variant (the 8-wave variants run two waves per SIMD and overlap one wave's
+// dequantization with the other's MFMAs; larger tiles dequantize fewer
+// operand values per MFMA).  Returns 0 if the fast kernel does not apply.
 //   1: 256x256, 4 waves   2: 256x128, 4 waves   3: 128x128, 4 waves (2 per CU)
-//   4: 256x256, 8 waves   5: 256x128, 8 waves
+//   4: 256x256, 8 waves   5: 256x128, 8 waves   6: 256x192, 8 waves
 static int pick_tile(int64_t m, int64_t n, int64_t k, int nseg_eff, bool has_mean) {
   if (k % BK != 0) return 0;
   struct Cand { int id, bm, bn, per_cu; double eff; };
-  const Cand cands[5] = {{5, 256, 128, 1, 1.0}, {4, 256, 256, 1, 0.95}, {3, 128, 128, 2, 0.9},
-                         {2, 256, 128, 1, 0.85}, {1, 256, 256, 1, 0.8}};
+  const Cand cands[6] = {{6, 256, 192, 1, 1.05}, {5, 256, 128, 1, 1.0}, {4, 256, 256, 1, 0.95},
+                         {3, 128, 128, 2, 0.9},  {2, 256, 128, 1, 0.85}, {1, 256, 256, 1, 0.8}};
   int best = 0;
   double best_cost = 0;
   for (const Cand& cd : cands) {
@@ -910,32 +595,39 @@ static int pick_tile(int64_t m, int64_t n, int64_t k, int nseg_eff, bool has_mea
 
 hipError_t launch_gemm(const QOperand& a, const QOperand* mean, const QOperand& b, int64_t m,
                        int64_t n, int64_t k, const int64_t* offs, int nseg, void* c, bool c_bf16,
-                       int64_t ldc, float* rho_ws, hipStream_t st) {
+                       int64_t ldc, void* ws, hipStream_t st) {
+  float* rho_ws = static_cast<float*>(ws);
   if (m == 0 || n == 0) return hipGetLastError();
+  // warp-specialized kernel (default); AVERIS_GEMM_KERNEL = 1 selects the
+  // lock-step kernel below, AVERIS_GEMM_WS_TILE = 1..2 forces a variant
+  static const int kernel_sel = [] {
+    const char* e = std::getenv("AVERIS_GEMM_KERNEL");
+    return e ? std::atoi(e) : 0;
+  }();
+  if (kernel_sel == 0) {
+    int v = ws_pick(m, n, k, offs ? nseg : 1, mean != nullptr);
+    static const int forced_ws = [] {
+      const char* e = std::getenv("AVERIS_GEMM_WS_TILE");
+      return e ? std::atoi(e) : 0;
+    }();
+    if (v != 0 && forced_ws >= 1 && forced_ws <= 2) v = forced_ws;
+    if (v != 0) return launch_gemm_ws(v, a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+  }
   int choice = pick_tile(m, n, k, offs ? nseg : 1, mean != nullptr);
-  // tuning override: AVERIS_GEMM_TILE = 1..5 (see pick_tile)
+  // tuning override: AVERIS_GEMM_TILE = 1..6 (see pick_tile)
   static const int forced = [] {
     const char* e = std::getenv("AVERIS_GEMM_TILE");
     return e ? std::atoi(e) : 0;
   }();
-  if (choice != 0 && forced >= 1 && forced <= 5) {
-    const int tm = (forced == 3) ? 2 : 4, tn = (forced == 1 || forced == 4) ? 4 : 2;
-    if (fast_lds_bytes(tm, tn, k, mean != nullptr) <= kLdsLimit) choice = forced;
+  if (choice != 0 && forced >= 1 && forced <= 6) {
+    static const int dims[7][2] = {{0, 0}, {4, 4}, {4, 2}, {2, 2}, {4, 4}, {4, 2}, {4, 3}};
+    if (fast_lds_bytes(dims[forced][0], dims[forced][1], k, mean != nullptr) <= kLdsLimit)
+      choice = forced;
   }
   static const int pf = [] {
     const char* e = std::getenv("AVERIS_GEMM_PF");
     return e ? std::atoi(e) : 2;
   }();
-  // raw-code kernel for the 256-wide 4-wave tiles: opt-in (AVERIS_GEMM_RAW = 1);
-  // it measured slower than the fp16-LDS kernel on the Qwen3-0.6B shapes
-  static const int raw = [] {
-    const char* e = std::getenv("AVERIS_GEMM_RAW");
-    return e ? std::atoi(e) : 0;
-  }();
-  if (raw && choice == 1 && raw_lds_bytes(4, 4, k, mean != nullptr) <= kLdsLimit)
-    return launch_raw_any<4, 4>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
-  if (raw && choice == 2 && raw_lds_bytes(4, 2, k, mean != nullptr) <= kLdsLimit)
-    return launch_raw_any<4, 2>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
   const QOperand mu = mean ? *mean : QOperand{nullptr, nullptr, nullptr};
 #define AVERIS_FAST(TM_, TN_)                                                               \
   switch (pf) {                                                                            \
@@ -955,6 +647,7 @@ hipError_t launch_gemm(const QOperand& a, const QOperand* mean, const QOperand& 
     case 3: AVERIS_FAST(2, 2)
     case 4: AVERIS_FAST8(2, 4)
     case 5: AVERIS_FAST8(2, 2)
+    case 6: AVERIS_FAST8(2, 3)
     default: break;
   }
 #undef AVERIS_FAST

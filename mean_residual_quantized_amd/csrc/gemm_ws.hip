@@ -1,0 +1,397 @@
+// Warp-specialized quantized NT GEMM for gfx950 (K % 64 == 0).
+//
+// Computes the Averis products of the "Lighthouse" review §2.2 (forward
+// Y = 1 (mean_q W_q) + X_R,q W_q and dgrad dX = 1 (mean_q,D W_q^T) +
+// D_R,q W_q^T) as C = deq(A) deq(B)^T + 1 rho^T with
+// rho_j = S_dec(mean) S_dec(B) sum_k deq'(mean)_k deq'(B)_jk.
+//
+// A workgroup of eight wavefronts owns a (64 TM) x (64 TN) output tile and
+// splits the work by role, so that each SIMD runs one wavefront of each:
+//   consumers (waves 0..3, a 2 x 2 grid): each owns a (32 TM) x (32 TN)
+//     sub-tile, reads fp16 operand fragments from LDS and issues
+//     v_mfma_f32_32x32x16_f16 back to back (fp32 accumulation);
+//   producers (waves 4..7): load the next stages' 4-bit codes and E4M3
+//     scales into a register ring, dequantize them exactly to fp16
+//     (v_cvt_scalef32_pk_f16_fp4, v_pk_mul_f16 by the scale that
+//     v_cvt_scalef32_pk_f16_fp8 decodes exactly) into the other LDS buffer,
+//     and accumulate the rank-one sums from the B values they write.
+// One barrier per 64-wide K stage hands the two LDS buffers over.  When all
+// waves do both jobs in lock step, the MFMA phase and the dequantization
+// phase of a stage follow each other on every SIMD; with split roles the
+// dequantization of stage s + 1 runs on the same SIMDs during the MFMAs of
+// stage s.
+//
+// The MFMA takes the B fragment first, so a lane's accumulators hold four
+// consecutive output columns of one output row: 8-byte (bf16) or 16-byte
+// (fp32) stores.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_common.hpp"
+#include "launch.hpp"
+#include "segments.hpp"
+
+namespace averis {
+namespace {
+
+constexpr int kWsBK = 64;
+constexpr int kWsLdsK = kWsBK + 8;   // fp16 per LDS row (16-byte pad against bank conflicts)
+constexpr int kProducers = 256;      // producer threads (waves 4..7)
+
+template <int V>
+struct WsIC {
+  static constexpr int value = V;
+};
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void ws_unroll(F&& f) {
+  if constexpr (I < N) {
+    f(WsIC<I>{});
+    ws_unroll<I + 1, N>(f);
+  }
+}
+
+}  // namespace
+
+template <int TM, int TN, int PF, bool OUT_BF16, bool HAS_MEAN>
+__global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOperand MU, int64_t m,
+                                                    int64_t n, int64_t k, const int64_t* offs,
+                                                    int nseg, void* c, int64_t ldc) {
+  constexpr int BM = 64 * TM, BN = 64 * TN;
+  constexpr int NCH = 2 * (BM + BN);                     // 32-element chunks per stage
+  constexpr int CP = (NCH + kProducers - 1) / kProducers;  // chunks per producer thread
+  constexpr int IA = 2 * BM / kProducers;                // chunk rounds that hold A rows
+  static_assert((2 * BM) % kProducers == 0 && (2 * BN) % 64 == 0, "whole-wave chunk rounds");
+  extern __shared__ __attribute__((aligned(16))) _Float16 smem_ws[];
+  _Float16* As = smem_ws;                                // [2][BM][LDSK]
+  _Float16* Bs = As + 2 * BM * kWsLdsK;                  // [2][BN][LDSK]
+  float* rho_sh = reinterpret_cast<float*>(Bs + 2 * BN * kWsLdsK);   // [2][BN]
+  _Float16* Ms = reinterpret_cast<_Float16*>(rho_sh + 2 * BN);       // [k]
+
+  int64_t tile_x, tile_y;
+  xcd_tile(tile_x, tile_y);
+  const SegRange sr = locate_chunk(offs, nseg, m, BM, tile_y);
+  if (sr.seg < 0) return;
+  const int seg = sr.seg;
+  const int64_t m0 = sr.r0, m_end = sr.r1;
+  const int64_t n0 = tile_x * BN;
+  const int64_t kh = k >> 1, kb = k >> 4;
+  const uint8_t* bcodes = B.codes + (offs ? (int64_t)seg * n * kh : 0);
+  const uint8_t* bscales = B.scales + (offs ? (int64_t)seg * n * kb : 0);
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const bool producer = wave >= 4;
+  const int nk = (int)(k / kWsBK);
+
+  if (HAS_MEAN) {
+    // the whole dequantized mean vector (without its tensor scale) in LDS
+    const uint8_t* mcodes = MU.codes + (int64_t)seg * kh;
+    const uint8_t* mscales = MU.scales + (int64_t)seg * kb;
+    for (int64_t q = t; q < (k >> 5); q += 512) {
+      const uint4 wq = *reinterpret_cast<const uint4*>(mcodes + 16 * q);
+      const half2_t sc = scales2(*reinterpret_cast<const uint16_t*>(mscales + 2 * q));
+      const half2_t s0 = {sc.x, sc.x}, s1 = {sc.y, sc.y};
+      uint4* dst = reinterpret_cast<uint4*>(Ms + 32 * q);
+      dst[0] = deq8(wq.x, s0);
+      dst[1] = deq8(wq.y, s0);
+      dst[2] = deq8(wq.z, s1);
+      dst[3] = deq8(wq.w, s1);
+    }
+    __syncthreads();
+  }
+
+  if (producer) {
+    // ------------------------------------------------------------------ producers
+    const int pt = t - 512 + kProducers;
+    // chunk q = pt + 256 i: A row q >> 1 (rounds i < IA) or B row
+    // (q - 2 BM) >> 1, k-half q & 1 of each stage.  Rows past the edge are
+    // clamped to the last valid row: their products only reach outputs that
+    // are never stored.  Byte offsets are 32-bit; each stage adds a uniform
+    // k offset.
+    const uint8_t* a_c = A.codes + m0 * kh;
+    const uint8_t* a_s = A.scales + m0 * kb;
+    const uint8_t* b_c = bcodes + n0 * kh;
+    const uint8_t* b_s = bscales + n0 * kb;
+    uint32_t oc[CP], os[CP];
+    int lrow[CP];
+#pragma unroll
+    for (int i = 0; i < CP; ++i) {
+      const int q = pt + kProducers * i, hf = q & 1;
+      const bool is_a = i < IA;
+      const int r = is_a ? (q >> 1) : ((q - 2 * BM) >> 1);
+      const int64_t lim = is_a ? (m_end - m0) : (n - n0);
+      const int64_t row = r < lim ? r : lim - 1;
+      lrow[i] = r;
+      oc[i] = (uint32_t)(row * kh) + 16u * hf;
+      os[i] = (uint32_t)(row * kb) + 2u * hf;
+    }
+    uint4 rc[PF][CP];
+    uint32_t rs[PF][CP];
+    float rho_acc[CP];
+#pragma unroll
+    for (int i = 0; i < CP; ++i) rho_acc[i] = 0.0f;
+
+    auto gload = [&](int slot, int st) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < CP; ++i) {
+        if (pt + kProducers * i >= NCH) break;   // whole waves
+        const uint8_t* cb = (i < IA ? a_c : b_c) + 32 * st;
+        const uint8_t* sb = (i < IA ? a_s : b_s) + 4 * st;
+        rc[slot][i] = *reinterpret_cast<const uint4*>(cb + oc[i]);
+        rs[slot][i] = *reinterpret_cast<const uint16_t*>(sb + os[i]);
+      }
+    };
+    auto dequant = [&](int slot, int buf, int st) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < CP; ++i) {
+        const int q = pt + kProducers * i, hf = q & 1;
+        if (q >= NCH) break;
+        const half2_t sc = scales2(rs[slot][i]);
+        const half2_t s0 = {sc.x, sc.x}, s1 = {sc.y, sc.y};
+        uint4 d[4];
+        d[0] = deq8(rc[slot][i].x, s0);
+        d[1] = deq8(rc[slot][i].y, s0);
+        d[2] = deq8(rc[slot][i].z, s1);
+        d[3] = deq8(rc[slot][i].w, s1);
+        _Float16* base = i < IA ? As + buf * BM * kWsLdsK : Bs + buf * BN * kWsLdsK;
+        uint4* dst = reinterpret_cast<uint4*>(base + lrow[i] * kWsLdsK + 32 * hf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[e] = d[e];
+        if (HAS_MEAN && i >= IA) {
+          const uint4* mv = reinterpret_cast<const uint4*>(Ms + kWsBK * st + 32 * hf);
+          float a = rho_acc[i];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint4 m4 = mv[e];
+            a = __builtin_amdgcn_fdot2(h2(d[e].x), h2(m4.x), a, false);
+            a = __builtin_amdgcn_fdot2(h2(d[e].y), h2(m4.y), a, false);
+            a = __builtin_amdgcn_fdot2(h2(d[e].z), h2(m4.z), a, false);
+            a = __builtin_amdgcn_fdot2(h2(d[e].w), h2(m4.w), a, false);
+          }
+          rho_acc[i] = a;
+        }
+      }
+    };
+
+    // stage j's codes live in ring slot j % PF, PF stages ahead of their
+    // dequantization; buffer j & 1 of LDS receives stage j
+    ws_unroll<0, PF>([&](auto p_c) __attribute__((always_inline)) {
+      constexpr int p = decltype(p_c)::value;
+      if (p < nk) gload(p, p);
+    });
+    dequant(0, 0, 0);
+    if (PF < nk) gload(0, PF);
+    __syncthreads();
+    // iteration it: dequantize stage it + 1 (slot (it + 1) % PF) into buffer
+    // (it + 1) & 1, refill that slot with stage it + 1 + PF
+    int it = 0;
+    for (; it + PF <= nk; it += PF) {
+      ws_unroll<0, PF>([&](auto u_c) __attribute__((always_inline)) {
+        constexpr int su = (decltype(u_c)::value + 1) % PF;
+        const int i2 = it + decltype(u_c)::value;
+        if (i2 + 1 < nk) {
+          dequant(su, (i2 + 1) & 1, i2 + 1);
+          if (i2 + 1 + PF < nk) gload(su, i2 + 1 + PF);
+        }
+        __syncthreads();
+      });
+    }
+    ws_unroll<0, PF>([&](auto u_c) __attribute__((always_inline)) {
+      constexpr int su = (decltype(u_c)::value + 1) % PF;
+      const int i2 = it + decltype(u_c)::value;
+      if (i2 < nk) {
+        if (i2 + 1 < nk) {
+          dequant(su, (i2 + 1) & 1, i2 + 1);
+          if (i2 + 1 + PF < nk) gload(su, i2 + 1 + PF);
+        }
+        __syncthreads();
+      }
+    });
+    if (HAS_MEAN) {
+#pragma unroll
+      for (int i = IA; i < CP; ++i) {
+        const int q = pt + kProducers * i;
+        if (q >= NCH) break;
+        rho_sh[(q & 1) * BN + lrow[i]] = rho_acc[i];
+      }
+      __syncthreads();
+      // each column's two k-half sums, times the tensor scales, in place
+      const float sd = MU.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
+      for (int cidx = pt; cidx < BN; cidx += kProducers)
+        rho_sh[cidx] = (rho_sh[cidx] + rho_sh[BN + cidx]) * sd;
+      __syncthreads();
+    }
+    return;
+  }
+
+  // -------------------------------------------------------------------- consumers
+  const int wm = wave >> 1, wn = wave & 1;
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  const int a_frag = (wm * 32 * TM + (lane & 31)) * kWsLdsK + (lane >> 5) * 8;
+  const int b_frag = (wn * 32 * TN + (lane & 31)) * kWsLdsK + (lane >> 5) * 8;
+  // fragments of k-step kk of the stage in buffer b; the reads for k-step
+  // kk + 1 are issued before the MFMAs of k-step kk, so the MFMAs hide the
+  // LDS latency (the first k-step of a stage waits for the barrier)
+  half8_t af[2][TM], bf[2][TN];
+  auto read_frags = [&](int slot, int b, int kk) __attribute__((always_inline)) {
+    const _Float16* as = As + b * BM * kWsLdsK + a_frag + kk;
+    const _Float16* bs = Bs + b * BN * kWsLdsK + b_frag + kk;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      af[slot][i] = *reinterpret_cast<const half8_t*>(as + i * 32 * kWsLdsK);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      bf[slot][j] = *reinterpret_cast<const half8_t*>(bs + j * 32 * kWsLdsK);
+  };
+  __syncthreads();   // stage 0 in buffer 0
+  read_frags(0, 0, 0);
+  for (int it = 0; it < nk; ++it) {
+    const int b = it & 1;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int cur = s4 & 1;
+      if (s4 < 3) read_frags(cur ^ 1, b, 16 * (s4 + 1));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (it + 1 == nk) mfma_drain();   // fence in the block of the last MFMA
+    __syncthreads();
+    if (it + 1 < nk) read_frags(0, b ^ 1, 0);
+  }
+  if (HAS_MEAN) {
+    __syncthreads();   // producers: partial sums written
+    __syncthreads();   // producers: combined and scaled
+  }
+
+  const float alpha = A.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
+  const bool full = (m0 + BM <= m_end) && (n0 + BN <= n);
+  const bool vec = full && (ldc % 4 == 0) &&
+                   ((reinterpret_cast<uintptr_t>(c) & (OUT_BF16 ? 7 : 15)) == 0);
+  const int64_t row_base = m0 + wm * 32 * TM + (lane & 31);
+  const int cl_base = wn * 32 * TN + (lane >> 5) * 4;   // tile-local column of v = 0
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int cl = cl_base + j * 32 + 8 * q;
+      const int64_t col = n0 + cl;
+      f32x4_t r1 = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (HAS_MEAN) r1 = *reinterpret_cast<const f32x4_t*>(rho_sh + cl);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int64_t row = row_base + i * 32;
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = __builtin_fmaf(acc[i][j][4 * q + e], alpha, r1[e]);
+        if (vec) {
+          if (OUT_BF16) {
+            const u32x2_t pk = {bf16x2_rne(y[0], y[1]), bf16x2_rne(y[2], y[3])};
+            store_out(pk, reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(c) + row * ldc + col));
+          } else {
+            const f32x4_t v4 = {y[0], y[1], y[2], y[3]};
+            store_out(v4, reinterpret_cast<f32x4_t*>(static_cast<float*>(c) + row * ldc + col));
+          }
+        } else if (row < m_end) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (col + e >= n) break;
+            if (OUT_BF16)
+              store_out((uint16_t)bf16x2_rne(y[e], 0.0f), static_cast<uint16_t*>(c) + row * ldc + col + e);
+            else
+              store_out(y[e], static_cast<float*>(c) + row * ldc + col + e);
+          }
+        }
+      }
+    }
+  }
+}
+
+namespace {
+
+size_t ws_lds_bytes(int tm, int tn, int64_t k, bool has_mean) {
+  const int bm = 64 * tm, bn = 64 * tn;
+  return (size_t)(2 * bm * kWsLdsK + 2 * bn * kWsLdsK) * 2 + (size_t)2 * bn * 4 +
+         (has_mean ? (size_t)k * 2 : 0);
+}
+
+constexpr size_t kWsLdsLimit = 160 * 1024 - 512;
+
+template <int TM, int TN, bool OB, bool HM>
+hipError_t launch_ws(const QOperand& a, const QOperand& mu, const QOperand& b, int64_t m, int64_t n,
+                     int64_t k, const int64_t* offs, int nseg, void* c, int64_t ldc,
+                     hipStream_t st) {
+  constexpr int PF = 2, BM = 64 * TM, BN = 64 * TN;
+  const size_t lds = ws_lds_bytes(TM, TN, k, HM);
+  static bool attr_set = false;   // per instantiation; the attribute is idempotent
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_ws<TM, TN, PF, OB, HM>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWsLdsLimit);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t tiles_m = chunk_upper_bound(m, offs ? nseg : 1, BM);
+  dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)tiles_m);
+  k_gemm_ws<TM, TN, PF, OB, HM><<<grid, 512, lds, st>>>(a, b, mu, m, n, k, offs, nseg, c, ldc);
+  return hipGetLastError();
+}
+
+template <int TM, int TN>
+hipError_t launch_ws_any(const QOperand& a, const QOperand* mean, const QOperand& b, int64_t m,
+                         int64_t n, int64_t k, const int64_t* offs, int nseg, void* c, bool c_bf16,
+                         int64_t ldc, hipStream_t st) {
+  const QOperand mu = mean ? *mean : QOperand{nullptr, nullptr, nullptr};
+  if (c_bf16)
+    return mean ? launch_ws<TM, TN, true, true>(a, mu, b, m, n, k, offs, nseg, c, ldc, st)
+                : launch_ws<TM, TN, true, false>(a, mu, b, m, n, k, offs, nseg, c, ldc, st);
+  return mean ? launch_ws<TM, TN, false, true>(a, mu, b, m, n, k, offs, nseg, c, ldc, st)
+              : launch_ws<TM, TN, false, false>(a, mu, b, m, n, k, offs, nseg, c, ldc, st);
+}
+
+}  // namespace
+
+// Variants (workgroup tile): 1: 256 x 192, 2: 256 x 128.  Chosen by rounds of
+// workgroups over the 256 CUs (one resident workgroup per CU) times the
+// tile's work.  Returns 0 when the kernel does not apply.
+int ws_pick(int64_t m, int64_t n, int64_t k, int nseg_eff, bool has_mean) {
+  if (k % kWsBK != 0) return 0;
+  struct Cand { int id, tm, tn; double eff; };
+  const Cand cands[2] = {{1, 4, 3, 1.0}, {2, 4, 2, 0.95}};
+  int best = 0;
+  double best_cost = 0;
+  for (const Cand& cd : cands) {
+    if (ws_lds_bytes(cd.tm, cd.tn, k, has_mean) > kWsLdsLimit) continue;
+    const int64_t bm = 64 * cd.tm, bn = 64 * cd.tn;
+    const int64_t tiles = chunk_upper_bound(m, nseg_eff, bm) * ((n + bn - 1) / bn);
+    const double rounds = (double)((tiles + 255) / 256);
+    const double cost = rounds * bm * bn / cd.eff;
+    if (best == 0 || cost < best_cost) {
+      best = cd.id;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+hipError_t launch_gemm_ws(int variant, const QOperand& a, const QOperand* mean, const QOperand& b,
+                          int64_t m, int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
+                          bool c_bf16, int64_t ldc, hipStream_t st) {
+  switch (variant) {
+    case 1: return launch_ws_any<4, 3>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+    case 2: return launch_ws_any<4, 2>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace averis
