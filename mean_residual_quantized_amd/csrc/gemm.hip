@@ -498,41 +498,63 @@ static size_t fast_lds_bytes(int tm, int tn, int64_t k, bool has_mean) {
 constexpr size_t kLdsLimit = 160 * 1024 - 512;
 
 // rho[seg][j] = S_dec(mean_seg) S_dec(B_seg) sum_k deq'(mean_seg)_k deq'(B_seg)_jk
-// one wavefront per output column j
+// (the rank-one term of one output column).  Sixteen lanes per column j, four
+// columns per wavefront: each lane takes 16-element blocks k = 16 (l + 16 i)
+// of its column, dequantizes B and the mean exactly to fp16 and accumulates
+// v_dot2_f32_f16 products in fp32; the sixteen partial sums are combined by a
+// fixed butterfly.
+constexpr int kRank1Cols = 16;   // columns per workgroup of 256 threads
 __global__ __launch_bounds__(256) void k_rank1(QOperand M, QOperand B, int64_t n, int64_t k,
                                                bool grouped, float* __restrict__ rho) {
   const int seg = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (j >= n) return;
-  const int64_t nb = k >> 4;
-  const uint8_t* mc = M.codes + (int64_t)seg * (k >> 1);
-  const uint8_t* ms = M.scales + (int64_t)seg * nb;
-  const int64_t brow = (grouped ? (int64_t)seg * n : 0) + j;
-  const uint8_t* bc = B.codes + brow * (k >> 1);
-  const uint8_t* bs = B.scales + brow * nb;
+  const int sub = threadIdx.x & 15;
+  const int64_t j = (int64_t)blockIdx.x * kRank1Cols + (threadIdx.x >> 4);
+  const bool live = j < n;
+  const int64_t jj = live ? j : n - 1;   // keep every lane in the butterfly
+  const int64_t kh = k >> 1, kb = k >> 4;
+  const uint8_t* mc = M.codes + (int64_t)seg * kh;
+  const uint8_t* ms = M.scales + (int64_t)seg * kb;
+  const int64_t brow = (grouped ? (int64_t)seg * n : 0) + jj;
+  const uint8_t* bc = B.codes + brow * kh;
+  const uint8_t* bs = B.scales + brow * kb;
   float acc = 0.0f;
-  for (int64_t blk = lane; blk < nb; blk += 64) {
-    const uint2 wm = *reinterpret_cast<const uint2*>(mc + blk * 8);
-    const uint2 wb = *reinterpret_cast<const uint2*>(bc + blk * 8);
-    float s = 0.0f;
+  // four blocks per pass, their loads issued before any arithmetic; blocks
+  // past the end are clamped to the last one and their products dropped
+  constexpr int U = 4;
+  for (int64_t b0 = sub; b0 < kb; b0 += 16 * U) {
+    uint2 wm[U], wb[U];
+    uint32_t sm[U], sb[U];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const uint32_t cm = ((e < 8 ? wm.x : wm.y) >> (4 * (e & 7))) & 0xFu;
-      const uint32_t cb = ((e < 8 ? wb.x : wb.y) >> (4 * (e & 7))) & 0xFu;
-      const float vm = (float)__builtin_bit_cast(_Float16, (uint16_t)e2m1_f16_bits(cm));
-      const float vb = (float)__builtin_bit_cast(_Float16, (uint16_t)e2m1_f16_bits(cb));
-      s += vm * vb;   // exact: products and partial sums of a block are small dyadics
+    for (int u = 0; u < U; ++u) {
+      const int64_t blk = b0 + 16 * u < kb ? b0 + 16 * u : kb - 1;
+      wm[u] = *reinterpret_cast<const uint2*>(mc + 8 * blk);
+      wb[u] = *reinterpret_cast<const uint2*>(bc + 8 * blk);
+      sm[u] = ms[blk];
+      sb[u] = bs[blk];
     }
-    acc += s * (e4m3_value(ms[blk]) * e4m3_value(bs[blk]));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const half2_t smh = scales2(sm[u]), sbh = scales2(sb[u]);
+      const half2_t m0 = {smh.x, smh.x}, bb = {sbh.x, sbh.x};
+      const uint4 dm[2] = {deq8(wm[u].x, m0), deq8(wm[u].y, m0)};
+      const uint4 db[2] = {deq8(wb[u].x, bb), deq8(wb[u].y, bb)};
+      float p = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        p = __builtin_amdgcn_fdot2(h2(dm[e].x), h2(db[e].x), p, false);
+        p = __builtin_amdgcn_fdot2(h2(dm[e].y), h2(db[e].y), p, false);
+        p = __builtin_amdgcn_fdot2(h2(dm[e].z), h2(db[e].z), p, false);
+        p = __builtin_amdgcn_fdot2(h2(dm[e].w), h2(db[e].w), p, false);
+      }
+      acc += b0 + 16 * u < kb ? p : 0.0f;
+    }
   }
-  for (int d = 32; d > 0; d >>= 1) acc += __shfl_xor(acc, d, 64);
-  if (lane == 0) {
+  for (int d = 8; d > 0; d >>= 1) acc += __shfl_xor(acc, d, 16);
+  if (sub == 0 && live) {
     const float sd = M.tscale[2 * seg + 1] * B.tscale[(grouped ? 2 * seg : 0) + 1];
     rho[(int64_t)seg * n + j] = acc * sd;
   }
 }
-
 
 template <int TM, int TN, int PF, bool OB, bool HM, int WM = 2, int WN = 2>
 static hipError_t launch_fast(const QOperand& a, const QOperand& mu, const QOperand& b, int64_t m,
@@ -605,13 +627,21 @@ hipError_t launch_gemm(const QOperand& a, const QOperand* mean, const QOperand& 
     return e ? std::atoi(e) : 0;
   }();
   if (kernel_sel == 0) {
-    int v = ws_pick(m, n, k, offs ? nseg : 1, mean != nullptr);
+    int v = ws_pick(m, n, k, offs ? nseg : 1);
     static const int forced_ws = [] {
       const char* e = std::getenv("AVERIS_GEMM_WS_TILE");
       return e ? std::atoi(e) : 0;
     }();
     if (v != 0 && forced_ws >= 1 && forced_ws <= 2) v = forced_ws;
-    if (v != 0) return launch_gemm_ws(v, a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+    if (v != 0) {
+      if (mean) {
+        dim3 g((unsigned)((n + kRank1Cols - 1) / kRank1Cols), (unsigned)(offs ? nseg : 1));
+        k_rank1<<<g, 256, 0, st>>>(*mean, b, n, k, offs != nullptr, rho_ws);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      return launch_gemm_ws(v, a, mean ? rho_ws : nullptr, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+    }
   }
   int choice = pick_tile(m, n, k, offs ? nseg : 1, mean != nullptr);
   // tuning override: AVERIS_GEMM_TILE = 1..6 (see pick_tile)
@@ -655,7 +685,7 @@ hipError_t launch_gemm(const QOperand& a, const QOperand* mean, const QOperand& 
   // general path (K % 64 != 0, or a mean vector too long for LDS)
   const int ns = offs ? nseg : 1;
   if (mean) {
-    dim3 g((unsigned)((n + 3) / 4), (unsigned)ns);
+    dim3 g((unsigned)((n + kRank1Cols - 1) / kRank1Cols), (unsigned)ns);
     k_rank1<<<g, 256, 0, st>>>(*mean, b, n, k, offs != nullptr, rho_ws);
   }
   const int64_t tiles_m = chunk_upper_bound(m, ns, BM);

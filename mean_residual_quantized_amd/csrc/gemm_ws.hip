@@ -11,19 +11,21 @@
 //     sub-tile, reads fp16 operand fragments from LDS and issues
 //     v_mfma_f32_32x32x16_f16 back to back (fp32 accumulation);
 //   producers (waves 4..7): load the next stages' 4-bit codes and E4M3
-//     scales into a register ring, dequantize them exactly to fp16
+//     scales into a register ring and dequantize them exactly to fp16
 //     (v_cvt_scalef32_pk_f16_fp4, v_pk_mul_f16 by the scale that
-//     v_cvt_scalef32_pk_f16_fp8 decodes exactly) into the other LDS buffer,
-//     and accumulate the rank-one sums from the B values they write.
+//     v_cvt_scalef32_pk_f16_fp8 decodes exactly) into the other LDS buffer.
 // One barrier per 64-wide K stage hands the two LDS buffers over.  When all
 // waves do both jobs in lock step, the MFMA phase and the dequantization
 // phase of a stage follow each other on every SIMD; with split roles the
 // dequantization of stage s + 1 runs on the same SIMDs during the MFMAs of
 // stage s.
 //
-// The MFMA takes the B fragment first, so a lane's accumulators hold four
-// consecutive output columns of one output row: 8-byte (bf16) or 16-byte
-// (fp32) stores.
+// The rank-one term rho (one value per output column) comes from a small
+// GEMV launched just before (every row tile of a column would otherwise
+// recompute it); the producers stage the tile's values in LDS during the
+// prologue and the consumers add them in the epilogue.  The MFMA takes the B fragment
+// first, so a lane's accumulators hold four consecutive output columns of one
+// output row: 8-byte (bf16) or 16-byte (fp32) stores.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -54,7 +56,8 @@ __device__ __forceinline__ void ws_unroll(F&& f) {
 }  // namespace
 
 template <int TM, int TN, int PF, bool OUT_BF16, bool HAS_MEAN>
-__global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOperand MU, int64_t m,
+__global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B,
+                                                    const float* __restrict__ rho, int64_t m,
                                                     int64_t n, int64_t k, const int64_t* offs,
                                                     int nseg, void* c, int64_t ldc) {
   constexpr int BM = 64 * TM, BN = 64 * TN;
@@ -65,8 +68,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
   extern __shared__ __attribute__((aligned(16))) _Float16 smem_ws[];
   _Float16* As = smem_ws;                                // [2][BM][LDSK]
   _Float16* Bs = As + 2 * BM * kWsLdsK;                  // [2][BN][LDSK]
-  float* rho_sh = reinterpret_cast<float*>(Bs + 2 * BN * kWsLdsK);   // [2][BN]
-  _Float16* Ms = reinterpret_cast<_Float16*>(rho_sh + 2 * BN);       // [k]
+  float* rho_sh = reinterpret_cast<float*>(Bs + 2 * BN * kWsLdsK);   // [BN]
 
   int64_t tile_x, tile_y;
   xcd_tile(tile_x, tile_y);
@@ -83,23 +85,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const bool producer = wave >= 4;
   const int nk = (int)(k / kWsBK);
-
-  if (HAS_MEAN) {
-    // the whole dequantized mean vector (without its tensor scale) in LDS
-    const uint8_t* mcodes = MU.codes + (int64_t)seg * kh;
-    const uint8_t* mscales = MU.scales + (int64_t)seg * kb;
-    for (int64_t q = t; q < (k >> 5); q += 512) {
-      const uint4 wq = *reinterpret_cast<const uint4*>(mcodes + 16 * q);
-      const half2_t sc = scales2(*reinterpret_cast<const uint16_t*>(mscales + 2 * q));
-      const half2_t s0 = {sc.x, sc.x}, s1 = {sc.y, sc.y};
-      uint4* dst = reinterpret_cast<uint4*>(Ms + 32 * q);
-      dst[0] = deq8(wq.x, s0);
-      dst[1] = deq8(wq.y, s0);
-      dst[2] = deq8(wq.z, s1);
-      dst[3] = deq8(wq.w, s1);
-    }
-    __syncthreads();
-  }
 
   if (producer) {
     // ------------------------------------------------------------------ producers
@@ -128,9 +113,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
     }
     uint4 rc[PF][CP];
     uint32_t rs[PF][CP];
-    float rho_acc[CP];
-#pragma unroll
-    for (int i = 0; i < CP; ++i) rho_acc[i] = 0.0f;
 
     auto gload = [&](int slot, int st) __attribute__((always_inline)) {
 #pragma unroll
@@ -158,19 +140,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
         uint4* dst = reinterpret_cast<uint4*>(base + lrow[i] * kWsLdsK + 32 * hf);
 #pragma unroll
         for (int e = 0; e < 4; ++e) dst[e] = d[e];
-        if (HAS_MEAN && i >= IA) {
-          const uint4* mv = reinterpret_cast<const uint4*>(Ms + kWsBK * st + 32 * hf);
-          float a = rho_acc[i];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint4 m4 = mv[e];
-            a = __builtin_amdgcn_fdot2(h2(d[e].x), h2(m4.x), a, false);
-            a = __builtin_amdgcn_fdot2(h2(d[e].y), h2(m4.y), a, false);
-            a = __builtin_amdgcn_fdot2(h2(d[e].z), h2(m4.z), a, false);
-            a = __builtin_amdgcn_fdot2(h2(d[e].w), h2(m4.w), a, false);
-          }
-          rho_acc[i] = a;
-        }
       }
     };
 
@@ -180,6 +149,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
       constexpr int p = decltype(p_c)::value;
       if (p < nk) gload(p, p);
     });
+    if (HAS_MEAN) {
+      // this tile's rank-one terms, for the consumers' epilogue
+      for (int cidx = pt; cidx < BN; cidx += kProducers)
+        rho_sh[cidx] = n0 + cidx < n ? rho[(int64_t)seg * n + n0 + cidx] : 0.0f;
+    }
     dequant(0, 0, 0);
     if (PF < nk) gload(0, PF);
     __syncthreads();
@@ -208,20 +182,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
         __syncthreads();
       }
     });
-    if (HAS_MEAN) {
-#pragma unroll
-      for (int i = IA; i < CP; ++i) {
-        const int q = pt + kProducers * i;
-        if (q >= NCH) break;
-        rho_sh[(q & 1) * BN + lrow[i]] = rho_acc[i];
-      }
-      __syncthreads();
-      // each column's two k-half sums, times the tensor scales, in place
-      const float sd = MU.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
-      for (int cidx = pt; cidx < BN; cidx += kProducers)
-        rho_sh[cidx] = (rho_sh[cidx] + rho_sh[BN + cidx]) * sd;
-      __syncthreads();
-    }
     return;
   }
 
@@ -270,10 +230,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
     __syncthreads();
     if (it + 1 < nk) read_frags(0, b ^ 1, 0);
   }
-  if (HAS_MEAN) {
-    __syncthreads();   // producers: partial sums written
-    __syncthreads();   // producers: combined and scaled
-  }
 
   const float alpha = A.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
   const bool full = (m0 + BM <= m_end) && (n0 + BN <= n);
@@ -320,20 +276,19 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
 
 namespace {
 
-size_t ws_lds_bytes(int tm, int tn, int64_t k, bool has_mean) {
+size_t ws_lds_bytes(int tm, int tn) {
   const int bm = 64 * tm, bn = 64 * tn;
-  return (size_t)(2 * bm * kWsLdsK + 2 * bn * kWsLdsK) * 2 + (size_t)2 * bn * 4 +
-         (has_mean ? (size_t)k * 2 : 0);
+  return (size_t)(2 * bm * kWsLdsK + 2 * bn * kWsLdsK) * 2 + (size_t)bn * 4;
 }
 
 constexpr size_t kWsLdsLimit = 160 * 1024 - 512;
 
 template <int TM, int TN, bool OB, bool HM>
-hipError_t launch_ws(const QOperand& a, const QOperand& mu, const QOperand& b, int64_t m, int64_t n,
+hipError_t launch_ws(const QOperand& a, const float* rho, const QOperand& b, int64_t m, int64_t n,
                      int64_t k, const int64_t* offs, int nseg, void* c, int64_t ldc,
                      hipStream_t st) {
   constexpr int PF = 2, BM = 64 * TM, BN = 64 * TN;
-  const size_t lds = ws_lds_bytes(TM, TN, k, HM);
+  const size_t lds = ws_lds_bytes(TM, TN);
   static bool attr_set = false;   // per instantiation; the attribute is idempotent
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_ws<TM, TN, PF, OB, HM>),
@@ -343,20 +298,19 @@ hipError_t launch_ws(const QOperand& a, const QOperand& mu, const QOperand& b, i
   }
   const int64_t tiles_m = chunk_upper_bound(m, offs ? nseg : 1, BM);
   dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)tiles_m);
-  k_gemm_ws<TM, TN, PF, OB, HM><<<grid, 512, lds, st>>>(a, b, mu, m, n, k, offs, nseg, c, ldc);
+  k_gemm_ws<TM, TN, PF, OB, HM><<<grid, 512, lds, st>>>(a, b, rho, m, n, k, offs, nseg, c, ldc);
   return hipGetLastError();
 }
 
 template <int TM, int TN>
-hipError_t launch_ws_any(const QOperand& a, const QOperand* mean, const QOperand& b, int64_t m,
+hipError_t launch_ws_any(const QOperand& a, const float* rho, const QOperand& b, int64_t m,
                          int64_t n, int64_t k, const int64_t* offs, int nseg, void* c, bool c_bf16,
                          int64_t ldc, hipStream_t st) {
-  const QOperand mu = mean ? *mean : QOperand{nullptr, nullptr, nullptr};
   if (c_bf16)
-    return mean ? launch_ws<TM, TN, true, true>(a, mu, b, m, n, k, offs, nseg, c, ldc, st)
-                : launch_ws<TM, TN, true, false>(a, mu, b, m, n, k, offs, nseg, c, ldc, st);
-  return mean ? launch_ws<TM, TN, false, true>(a, mu, b, m, n, k, offs, nseg, c, ldc, st)
-              : launch_ws<TM, TN, false, false>(a, mu, b, m, n, k, offs, nseg, c, ldc, st);
+    return rho ? launch_ws<TM, TN, true, true>(a, rho, b, m, n, k, offs, nseg, c, ldc, st)
+               : launch_ws<TM, TN, true, false>(a, rho, b, m, n, k, offs, nseg, c, ldc, st);
+  return rho ? launch_ws<TM, TN, false, true>(a, rho, b, m, n, k, offs, nseg, c, ldc, st)
+             : launch_ws<TM, TN, false, false>(a, rho, b, m, n, k, offs, nseg, c, ldc, st);
 }
 
 }  // namespace
@@ -364,14 +318,14 @@ hipError_t launch_ws_any(const QOperand& a, const QOperand* mean, const QOperand
 // Variants (workgroup tile): 1: 256 x 192, 2: 256 x 128.  Chosen by rounds of
 // workgroups over the 256 CUs (one resident workgroup per CU) times the
 // tile's work.  Returns 0 when the kernel does not apply.
-int ws_pick(int64_t m, int64_t n, int64_t k, int nseg_eff, bool has_mean) {
+int ws_pick(int64_t m, int64_t n, int64_t k, int nseg_eff) {
   if (k % kWsBK != 0) return 0;
   struct Cand { int id, tm, tn; double eff; };
   const Cand cands[2] = {{1, 4, 3, 1.0}, {2, 4, 2, 0.95}};
   int best = 0;
   double best_cost = 0;
   for (const Cand& cd : cands) {
-    if (ws_lds_bytes(cd.tm, cd.tn, k, has_mean) > kWsLdsLimit) continue;
+    if (ws_lds_bytes(cd.tm, cd.tn) > kWsLdsLimit) continue;
     const int64_t bm = 64 * cd.tm, bn = 64 * cd.tn;
     const int64_t tiles = chunk_upper_bound(m, nseg_eff, bm) * ((n + bn - 1) / bn);
     const double rounds = (double)((tiles + 255) / 256);
@@ -384,12 +338,12 @@ int ws_pick(int64_t m, int64_t n, int64_t k, int nseg_eff, bool has_mean) {
   return best;
 }
 
-hipError_t launch_gemm_ws(int variant, const QOperand& a, const QOperand* mean, const QOperand& b,
+hipError_t launch_gemm_ws(int variant, const QOperand& a, const float* rho, const QOperand& b,
                           int64_t m, int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
                           bool c_bf16, int64_t ldc, hipStream_t st) {
   switch (variant) {
-    case 1: return launch_ws_any<4, 3>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
-    case 2: return launch_ws_any<4, 2>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+    case 1: return launch_ws_any<4, 3>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+    case 2: return launch_ws_any<4, 2>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
     default: return hipErrorInvalidValue;
   }
 }
