@@ -24,7 +24,9 @@
  *   e_b    = fp32(S_enc / d_b) (0 if d_b == 0);  v = fp32(t * e_b)
  *   E2M1 code (sign << 3 | index into {0,.5,1,1.5,2,3,4,6}) by
  *     RN: nearest, ties to the even index, |v| >= 6 -> 6, or
- *     SR: up iff u < 2^16 (|v| - lo) / (hi - lo) with u the element's 16-bit
+ *     SR: with lo <= |v| < hi the neighbouring grid points and
+ *         frac = (|v| - lo) / (hi - lo), up iff floor(2^22 frac) + 64 u >= 2^22,
+ *         u the element's 16-bit
  *         draw from Philox4x32-10: key = seed, counter = (g lo, g hi,
  *         stream, 0), g = idx >> 3, word (idx >> 1) & 3, half idx & 1,
  *         idx = row * cols + col (global row for grouped tensors).

@@ -1,5 +1,6 @@
-// Device helpers shared by the libaveris kernels (gfx950): counter-based RNG,
-// the E4M3 scale codec and the E2M1 element rounding of the NVFP4-style Q4.
+// Device helpers shared by the libaveris kernels (gfx950): counter-based RNG
+// and the E4M3 scale codec of the NVFP4-style Q4 (the E2M1 element rounding,
+// RN and SR, is done by the hardware conversion instructions).
 //
 // Every operation that decides a code or a scale byte is a single IEEE fp32
 // operation with round-to-nearest-even, in the order the format definition
@@ -14,7 +15,8 @@ namespace averis {
 // ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon et al., "Parallel random numbers: as easy as 1, 2, 3",
 // SC'11): 10 rounds of two 32x32->64-bit multiplies and key mixing.  Each call
-// gives 128 bits = eight 16-bit draws, for elements 8g .. 8g+7.
+// gives 128 bits = eight 16-bit draws, for elements 8g .. 8g+7: element j
+// takes word j >> 1, its low half for even j and its high half for odd j.
 // ---------------------------------------------------------------------------
 struct u32x4 {
   uint32_t x, y, z, w;
@@ -38,12 +40,6 @@ __device__ __forceinline__ u32x4 philox10(uint32_t c0, uint32_t c1, uint32_t c2,
   return {c0, c1, c2, c3};
 }
 
-// 16-bit draw j (0..7) of a Philox block: word j >> 1, low half for even j.
-__device__ __forceinline__ uint32_t draw16(const u32x4& r, int j) {
-  const uint32_t w = (j >> 1) == 0 ? r.x : (j >> 1) == 1 ? r.y : (j >> 1) == 2 ? r.z : r.w;
-  return (j & 1) ? (w >> 16) : (w & 0xFFFFu);
-}
-
 // ---------------------------------------------------------------------------
 // E4M3FN scale codec: bias 7, 3 mantissa bits, max 448, subnormals m * 2^-9.
 // ---------------------------------------------------------------------------
@@ -65,44 +61,6 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   const uint32_t e = (c >> 3) & 15u, m = c & 7u;
   if (e == 0) return (float)m * 0.001953125f;            // m * 2^-9
   return __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1 + m/8) 2^(e-7)
-}
-
-// ---------------------------------------------------------------------------
-// E2M1 element rounding.  Magnitudes by index: 0, .5, 1, 1.5, 2, 3, 4, 6.
-// Input v = t * e_b (fp32); output 4-bit code sign << 3 | index.
-// ---------------------------------------------------------------------------
-
-// Round to nearest, ties to the even index, saturating at 6.
-__device__ __forceinline__ uint32_t e2m1_rn(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
-  const float a = __builtin_fminf(__builtin_fabsf(v), 6.0f);
-  uint32_t idx;
-  if (a < 1.0f) {
-    idx = (uint32_t)__builtin_rintf(a * 2.0f);      // 0, 1 or 2 (= 1.0)
-  } else {
-    const uint32_t b = __float_as_uint(a);
-    // keep one mantissa bit, ties to even; the index is bits 30:22 - 252
-    const uint32_t r = b + 0x1FFFFFu + ((b >> 22) & 1u);
-    idx = (r >> 22) - 252u;
-  }
-  return sign | idx;
-}
-
-// Stochastic rounding with a 16-bit draw u: lo is the largest grid point
-// <= |v|, hi the next; round up iff u < 2^16 (|v| - lo) / (hi - lo).
-// Branch-free: both exact tests are computed and one is selected.
-__device__ __forceinline__ uint32_t e2m1_sr(float v, uint32_t u) {
-  const uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
-  const float a = __builtin_fminf(__builtin_fabsf(v), 6.0f);
-  const uint32_t b = __float_as_uint(a);
-  // |v| >= 1: gap = 2^(E-1); the fraction of the gap is the low 22 mantissa
-  // bits R, so u < 2^16 R / 2^22  <=>  u * 64 < R
-  const uint32_t idx_n = (b >> 22) - 252u + ((u << 6) < (b & 0x3FFFFFu) ? 1u : 0u);
-  // |v| < 1: gap 0.5, lo = 0 or 0.5; 2^16 (a - lo) / 0.5 = a 2^17 - lo 2^17 (exact)
-  const uint32_t half = a >= 0.5f ? 1u : 0u;
-  const float t = a * 131072.0f - (half ? 65536.0f : 0.0f);
-  const uint32_t idx_s = half + ((float)u < t ? 1u : 0u);
-  return sign | (a < 1.0f ? idx_s : idx_n);
 }
 
 // ---------------------------------------------------------------------------

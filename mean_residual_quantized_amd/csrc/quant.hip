@@ -219,6 +219,24 @@ __global__ __launch_bounds__(256) void k_finalize(int64_t rows, int64_t cols, co
 }
 
 // ---------------------------------------------------------------------------
+// v_cvt_scalef32_sr_pk_fp4_f32 (scale 1) into byte P of acc, keeping its other
+// bytes.  Written as an instruction with a read-write destination: the
+// compiler's builtin for it does not keep the destination's other bytes.
+// ---------------------------------------------------------------------------
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+template <int P>
+__device__ __forceinline__ void sr_fp4_byte(uint32_t& acc, f32x2v v, uint32_t seed) {
+  if constexpr (P == 0)
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0" : "+v"(acc) : "v"(v), "v"(seed));
+  else if constexpr (P == 1)
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,0]" : "+v"(acc) : "v"(v), "v"(seed));
+  else if constexpr (P == 2)
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,0,1]" : "+v"(acc) : "v"(v), "v"(seed));
+  else
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,1]" : "+v"(acc) : "v"(v), "v"(seed));
+}
+
+// ---------------------------------------------------------------------------
 // quantize one 16-block held in registers; writes 8 code bytes and 1 scale
 // ---------------------------------------------------------------------------
 template <bool SR>
@@ -233,23 +251,40 @@ __device__ __forceinline__ void quant_block16(const float* r, float s_enc, uint6
   block_scale(amax_b, s_enc, sc, e_b);
   uint2 packed;
   if (SR) {
-    uint32_t q[16];
+    // gfx950's v_cvt_scalef32_sr_pk_fp4_f32 (scale 1) rounds element 0 up iff
+    // floor(2^22 frac) + seed[31:10] >= 2^22 and element 1 with seed[30:9]
+    // (frac: the fraction of the E2M1 step above the lower grid point).  With
+    // the 16-bit draw u in the top bits of that window -- seed = u << 16 for
+    // element 0, u << 15 for element 1 -- this is the exact SR rule: up iff
+    // floor(2^22 frac) + 64 u >= 2^22.  One instruction per element: the even
+    // element goes in as element 0 and the odd one as element 1 of separate
+    // conversions (their dither windows overlap), and the nibbles are OR-ed.
     const uint64_t g = idx0 >> 3;   // idx0 is a multiple of 16
+    uint32_t even[2] = {0u, 0u}, odd[2] = {0u, 0u};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint64_t gg = g + h;
       const u32x4 rr = philox10((uint32_t)gg, (uint32_t)(gg >> 32), stream, 0u, k0, k1);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) q[h * 8 + k] = e2m1_sr(r[h * 8 + k] * e_b, draw16(rr, k));
+      const uint32_t wd[4] = {rr.x, rr.y, rr.z, rr.w};
+#define AVERIS_SR_PAIR(P)                                               \
+  {                                                                     \
+    const f32x2v e0 = {r[8 * h + 2 * (P)] * e_b, 0.0f};                 \
+    const f32x2v e1 = {0.0f, r[8 * h + 2 * (P) + 1] * e_b};             \
+    sr_fp4_byte<P>(even[h], e0, wd[P] << 16);                           \
+    sr_fp4_byte<P>(odd[h], e1, (wd[P] & 0xFFFF0000u) >> 1);             \
+  }
+      AVERIS_SR_PAIR(0)
+      AVERIS_SR_PAIR(1)
+      AVERIS_SR_PAIR(2)
+      AVERIS_SR_PAIR(3)
+#undef AVERIS_SR_PAIR
     }
-    packed.x = q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12) | (q[4] << 16) | (q[5] << 20) |
-               (q[6] << 24) | (q[7] << 28);
-    packed.y = q[8] | (q[9] << 4) | (q[10] << 8) | (q[11] << 12) | (q[12] << 16) | (q[13] << 20) |
-               (q[14] << 24) | (q[15] << 28);
+    packed.x = even[0] | odd[0];
+    packed.y = even[1] | odd[1];
   } else {
-    // RN: gfx950's v_cvt_scalef32_pk_fp4_f32 with scale 1 rounds to nearest,
-    // ties to the even code, saturates at 6 and keeps the sign of zero --
-    // the same rule as e2m1_rn, two elements per instruction
+    // RN: gfx950's v_cvt_scalef32_pk_fp4_f32 with scale 1 rounds to the
+    // nearest E2M1 value, ties to the even code, saturates at 6 and keeps the
+    // sign of zero, two elements per instruction
     float v[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) v[k] = r[k] * e_b;

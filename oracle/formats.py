@@ -10,11 +10,13 @@ bit-level rules, so the readings below are the oracle's:
   sign << 3 | index, so a negative value that rounds to 0 keeps its sign (0x8).
 * Round-to-nearest (RN): nearest grid point; a value exactly half-way between
   two grid points goes to the even index; |v| >= 6 saturates to 6.
-* Stochastic rounding (SR): with lo the largest grid point <= |v| and hi the
-  next one, the result is lo when |v| == lo; otherwise it rounds up iff the
-  element's 16-bit draw u satisfies u < 2^16 (|v| - lo) / (hi - lo), a real
-  comparison (so P(up) = ceil(2^16 p) / 2^16, a bias below 2^-16 of a gap).
-  |v| >= 6 saturates to 6.
+* Stochastic rounding (SR): with lo the largest grid point <= |v|, hi the
+  next one and frac = (|v| - lo) / (hi - lo), the element's 16-bit draw u
+  rounds up iff floor(2^22 frac) + 2^6 u >= 2^22 (a 22-bit dither added to
+  the fraction of the step, with the draw in its top 16 bits).  Exactly
+  floor(2^16 frac) of the 2^16 draws round up (P(up) = floor(2^16 frac) /
+  2^16, a bias below 2^-16 of a gap); |v| == lo never moves; |v| >= 6
+  saturates to 6.
 * Block scales are E4M3FN (bias 7, no infinities, max 448, subnormals kept,
   smallest 2^-9), round-to-nearest-even, saturating at 448.
 """
@@ -82,7 +84,15 @@ def e2m1_round_rn(v):
 
 
 def e2m1_round_sr(v, u16):
-    """SR codes for float32 values v with per-element 16-bit draws u16."""
+    """SR codes for float32 values v with per-element 16-bit draws u16.
+
+    lo is the largest grid point <= |v|, hi the next one, and
+    frac = (|v| - lo) / (hi - lo) in [0, 1).  The 16-bit draw u rounds up iff
+        floor(2^22 frac) + 2^6 u >= 2^22,
+    i.e. iff u >= 2^16 (1 - frac): over the 2^16 draws, exactly
+    floor(2^16 frac) of them round up, so the rounding is unbiased to within
+    2^-16 of a step.  A value on the grid never moves; |v| >= 6 gives 6.
+    """
     v = np.asarray(v, dtype=np.float32)
     u = np.asarray(u16, dtype=np.float64)
     a = np.abs(v).astype(np.float64)
@@ -90,10 +100,11 @@ def e2m1_round_sr(v, u16):
     lo = np.clip(lo, 0, 7)
     hi = np.minimum(lo + 1, 7)
     g_lo = E2M1_GRID[lo]
-    gap = E2M1_GRID[hi] - g_lo
-    with np.errstate(divide="ignore", invalid="ignore"):
-        thresh = np.where(gap > 0, (a - g_lo) / np.where(gap > 0, gap, 1.0) * 65536.0, 0.0)
-    up = (a != g_lo) & (u < thresh)
+    gap = np.where(hi > lo, E2M1_GRID[hi] - g_lo, 1.0)     # a power of two
+    # (a - g_lo) is exact in float64 and the scaling by 2^22 / gap is a power
+    # of two, so f22 is the exact floor
+    f22 = np.floor((a - g_lo) * (4194304.0 / gap))
+    up = (f22 + 64.0 * u >= 4194304.0) & (hi > lo)
     idx = np.where(a >= 6.0, 7, lo + up.astype(np.int64))
     sign = np.signbit(v).astype(np.int64)
     return ((sign << 3) | idx).astype(np.uint8)

@@ -109,8 +109,37 @@ def test_sr_result_is_a_neighbour_and_threshold_rule():
     lo = np.array([max(g for g in GRID if g <= x) for x in a])
     hi = np.array([min([g for g in GRID if g > x] or [6.0]) for x in a])
     assert np.all((got == lo) | (got == hi))
-    p = (a - lo) / (hi - lo)
-    np.testing.assert_array_equal(got == hi, (u < p * 65536) & (a != lo))
+    # the draw that first rounds up: u >= 2^16 (1 - frac), compared exactly
+    # with Python fractions on the float32 inputs
+    from fractions import Fraction
+    for x, uu, g in zip(a[:4000], u[:4000], got[:4000]):
+        lo_x = max(gv for gv in GRID if gv <= x)
+        hi_x = min([gv for gv in GRID if gv > x] or [6.0])
+        if x >= 6.0 or x == lo_x:
+            assert g == lo_x or x >= 6.0
+            continue
+        frac = (Fraction(float(x)) - Fraction(lo_x)) / (Fraction(hi_x) - Fraction(lo_x))
+        assert (g == hi_x) == (int(2 ** 22 * frac) + 64 * int(uu) >= 2 ** 22), (x, uu)
+
+
+def test_sr_exact_up_count_over_all_draws():
+    # over all 2^16 draws, exactly floor(2^16 frac) round up (closed form)
+    from fractions import Fraction
+    rng = np.random.default_rng(11)
+    vals = np.concatenate([rng.uniform(0, 6, 40), [1e-6, 0.2500001, 0.74999994, 5.9999995, 3.0000002]])
+    u = np.arange(65536)
+    for x in vals.astype(np.float32):
+        c = formats.e2m1_round_sr(np.full(u.shape, x, dtype=np.float32), u)
+        lo_x = max(gv for gv in GRID if gv <= float(x))
+        hi_x = min([gv for gv in GRID if gv > float(x)] or [6.0])
+        if float(x) >= 6.0:
+            continue
+        frac = (Fraction(float(x)) - Fraction(lo_x)) / (Fraction(hi_x) - Fraction(lo_x))
+        n_up = int(np.count_nonzero(np.array(GRID)[c & 7] == hi_x)) if hi_x != lo_x else 0
+        assert n_up == int(frac * 65536), (x, n_up, frac)
+        # and the draws that round up are exactly the largest ones
+        if n_up:
+            assert np.all(np.array(GRID)[c[-n_up:] & 7] == hi_x)
 
 
 def test_sr_up_frequency_and_unbiased_over_seeds():
