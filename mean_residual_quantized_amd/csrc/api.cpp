@@ -56,7 +56,7 @@ namespace averis {
 size_t split_ws_bytes(int64_t rows, int64_t cols, int nseg) {
   const int ns = nseg > 0 ? nseg : 1;
   const int64_t nch = chunk_upper_bound(rows, nseg > 0 ? nseg : 1, kStatsRows);
-  const int64_t ct_s = (cols + 255) / 256, ct_f = (cols + 63) / 64;
+  const int64_t ct_s = (cols + 255) / 256, ct_f = (cols + kFinCols - 1) / kFinCols;
   size_t b = 0;
   b += align256((size_t)(nch * cols * 8));      // psum
   b += align256((size_t)(nch * cols * 4)) * 2;  // pmax, pmin
@@ -69,7 +69,7 @@ size_t split_ws_bytes(int64_t rows, int64_t cols, int nseg) {
 SplitWs split_ws_carve(void* ws, int64_t rows, int64_t cols, int nseg) {
   const int ns = nseg > 0 ? nseg : 1;
   const int64_t nch = chunk_upper_bound(rows, nseg > 0 ? nseg : 1, kStatsRows);
-  const int64_t ct_s = (cols + 255) / 256, ct_f = (cols + 63) / 64;
+  const int64_t ct_s = (cols + 255) / 256, ct_f = (cols + kFinCols - 1) / kFinCols;
   char* p = static_cast<char*>(ws);
   SplitWs w;
   w.psum = reinterpret_cast<double*>(p); p += align256((size_t)(nch * cols * 8));

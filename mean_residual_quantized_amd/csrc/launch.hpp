@@ -11,6 +11,8 @@ constexpr int64_t kStatsRows = 128;
 constexpr int64_t kQuantRows = 16;
 // cap on the blocks of the weight amax pass
 constexpr int64_t kAmaxBlocks = 1024;
+// columns per workgroup of the split-quant finalize pass
+constexpr int64_t kFinCols = 16;
 
 struct QuantOut {
   uint8_t* codes;

@@ -51,6 +51,35 @@ struct Load8<float> {
   }
 };
 
+// 8 consecutive elements kept as loaded (bf16: one 16-byte word) and
+// unpacked to fp32 where they are used, so many rows fit in flight
+template <typename T>
+struct Raw8;
+
+template <>
+struct Raw8<uint16_t> {
+  uint4 w;
+  __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ float get(int k) const {
+    const uint32_t x = k < 2 ? w.x : k < 4 ? w.y : k < 6 ? w.z : w.w;
+    return (k & 1) ? bf16_hi(x) : bf16_lo(x);
+  }
+};
+
+template <>
+struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ float get(int k) const {
+    const float4& h = k < 4 ? a : b;
+    const int kk = k & 3;
+    return kk == 0 ? h.x : kk == 1 ? h.y : kk == 2 ? h.z : h.w;
+  }
+};
+
 __device__ __forceinline__ float block_max(float v, float* red) {
   // max over the 256 threads of a block
   for (int d = 32; d > 0; d >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, d, 64));
@@ -91,24 +120,25 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
     // clamped to its last row (loads stay legal, no branch) and masked below
     constexpr int U = (int)(kStatsRows / 8);
     const int64_t rlast = sr.r1 - 1;
-    float v[U][8];
+    Raw8<T> v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t r = sr.r0 + ty + 8 * u;
-      Load8<T>::run(a + (r < rlast ? r : rlast) * lda + c, v[u]);
+      v[u].load(a + (r < rlast ? r : rlast) * lda + c);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool ok = sr.r0 + ty + 8 * u <= rlast;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
+        const float x = v[u].get(k);
         if (SPLIT) {
           // a clamped row repeats a real value: harmless for max and min
-          s[k] += ok ? (double)v[u][k] : 0.0;
-          mx[k] = __builtin_fmaxf(mx[k], v[u][k]);
-          mn[k] = __builtin_fminf(mn[k], v[u][k]);
+          s[k] += ok ? (double)x : 0.0;
+          mx[k] = __builtin_fmaxf(mx[k], x);
+          mn[k] = __builtin_fminf(mn[k], x);
         } else {
-          am = __builtin_fmaxf(am, __builtin_fabsf(v[u][k]));
+          am = __builtin_fmaxf(am, __builtin_fabsf(x));
         }
       }
     }
@@ -147,8 +177,9 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
 }
 
 // ---------------------------------------------------------------------------
-// finalize (split): block = 64 columns x 4 chunk lanes, per segment.  The
-// fp64 partial sums are exact, so the order of the reduction is free.
+// finalize (split): block = kFinCols (16) columns x 16 chunk lanes, per
+// segment; each lane keeps all its partial loads in flight.  The fp64 partial
+// sums are exact, so the order of the reduction is free.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_finalize(int64_t rows, int64_t cols, const int64_t* offs,
                                                   int nseg, const double* __restrict__ psum,
@@ -158,47 +189,51 @@ __global__ __launch_bounds__(256) void k_finalize(int64_t rows, int64_t cols, co
                                                   float* __restrict__ mean_out,
                                                   float* __restrict__ tmax_r,
                                                   float* __restrict__ tmax_mu) {
+  constexpr int NC = (int)kFinCols, NQ = 256 / NC;
   const int seg = blockIdx.y;
   const SegRange sr = describe_segment(offs, nseg, rows, kStatsRows, seg);
-  const int jl = threadIdx.x & 63, q = threadIdx.x >> 6;
-  const int64_t j = (int64_t)blockIdx.x * 64 + jl;
+  const int jl = threadIdx.x % NC, q = threadIdx.x / NC;
+  const int64_t j = (int64_t)blockIdx.x * NC + jl;
   double s = 0.0;
   float m1 = -__builtin_inff(), m0 = __builtin_inff();
   if (j < cols && sr.c1 > sr.c0) {
-    constexpr int U = 16;
+    constexpr int U = 8;
     const int64_t clast = sr.c1 - 1;
-    for (int64_t ck = sr.c0 + q; ck < sr.c1; ck += 4 * U) {
+    for (int64_t ck = sr.c0 + q; ck < sr.c1; ck += NQ * U) {
       double ps[U];
       float px[U], pn[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t cc = ck + 4 * u < clast ? ck + 4 * u : clast;
+        const int64_t cc = ck + NQ * u < clast ? ck + NQ * u : clast;
         ps[u] = psum[cc * cols + j];
         px[u] = pmax[cc * cols + j];
         pn[u] = pmin[cc * cols + j];
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const bool ok = ck + 4 * u <= clast;
+        const bool ok = ck + NQ * u <= clast;
         s += ok ? ps[u] : 0.0;
         m1 = __builtin_fmaxf(m1, px[u]);   // a clamped chunk repeats a real one
         m0 = __builtin_fminf(m0, pn[u]);
       }
     }
   }
-  __shared__ double ls[4][64];
-  __shared__ float lx[4][64], ln[4][64];
+  __shared__ double ls[NQ][NC];
+  __shared__ float lx[NQ][NC], ln[NQ][NC];
   ls[q][jl] = s;
   lx[q][jl] = m1;
   ln[q][jl] = m0;
   __syncthreads();
   float rmax = 0.0f, amu = 0.0f;
   if (q == 0 && j < cols) {
-    const double t = (ls[0][jl] + ls[1][jl]) + (ls[2][jl] + ls[3][jl]);
-    const float x1 = __builtin_fmaxf(__builtin_fmaxf(lx[0][jl], lx[1][jl]),
-                                     __builtin_fmaxf(lx[2][jl], lx[3][jl]));
-    const float x0 = __builtin_fminf(__builtin_fminf(ln[0][jl], ln[1][jl]),
-                                     __builtin_fminf(ln[2][jl], ln[3][jl]));
+    double t = 0.0;
+    float x1 = -__builtin_inff(), x0 = __builtin_inff();
+#pragma unroll
+    for (int p = 0; p < NQ; ++p) {
+      t += ls[p][jl];
+      x1 = __builtin_fmaxf(x1, lx[p][jl]);
+      x0 = __builtin_fminf(x0, ln[p][jl]);
+    }
     const int64_t l = sr.seg_r1 - sr.seg_r0;
     float m = 0.0f;
     if (l > 0) {
@@ -209,12 +244,16 @@ __global__ __launch_bounds__(256) void k_finalize(int64_t rows, int64_t cols, co
     if (mean_out) mean_out[(int64_t)seg * cols + j] = m;
     amu = __builtin_fabsf(m);
   }
-  __shared__ float red[4];
-  rmax = block_max(rmax, red);
-  amu = block_max(amu, red);
-  if (threadIdx.x == 0) {
-    tmax_r[(int64_t)seg * gridDim.x + blockIdx.x] = rmax;
-    tmax_mu[(int64_t)seg * gridDim.x + blockIdx.x] = amu;
+  // the column maxima of this tile: lanes 0 .. NC-1 of wave 0 hold them
+  if (threadIdx.x < 64) {
+    for (int d = NC / 2; d > 0; d >>= 1) {
+      rmax = __builtin_fmaxf(rmax, __shfl_xor(rmax, d, 64));
+      amu = __builtin_fmaxf(amu, __shfl_xor(amu, d, 64));
+    }
+    if (threadIdx.x == 0) {
+      tmax_r[(int64_t)seg * gridDim.x + blockIdx.x] = rmax;
+      tmax_mu[(int64_t)seg * gridDim.x + blockIdx.x] = amu;
+    }
   }
 }
 
@@ -507,7 +546,7 @@ static hipError_t run_split_or_plain(const void* a_, int64_t rows, int64_t cols,
   const int64_t nchs = chunk_upper_bound(rows, nseg, kStatsRows);
   const int64_t nchq = chunk_upper_bound(rows, nseg, kQuantRows);
   const int64_t ct_s = (cols + 255) / 256;
-  const int64_t ct_f = (cols + 63) / 64;
+  const int64_t ct_f = (cols + kFinCols - 1) / kFinCols;
   const int64_t ct_q = ((cols >> 4) + 63) / 64;
   if (nchs > 0) {
     dim3 g((unsigned)ct_s, (unsigned)nchs);
