@@ -10,7 +10,10 @@ the mean term) is timed the same way to report the Averis overhead.
 
 Inputs are resident in HBM before timing starts; the timed steps rotate
 through enough copies of X and D (> 512 MB) that the 256 MB MALL cannot hold
-them, so every step reads its activations from HBM.
+them, so every step reads its activations from HBM.  The step is timed
+two ways -- op by op from Python, and as one captured HIP graph per
+input copy -- and report the faster (the same kernels run either way; which
+one wins depends on the host), with both figures beside it.
 
 Prints ONE JSON line (see the keys below).
 """
@@ -119,21 +122,49 @@ def run_step(x, d, w, ws, t=None, vanilla=False):
         toc("vgemm_dgrad")
 
 
+def capture(xs, ds, w, ws, vanilla):
+    """One HIP graph per rotating input copy, each holding one whole step
+    (every launch of the step, outputs in the graphs' shared pool)."""
+    graphs = []
+    pool = None
+    for i in range(len(xs)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, pool=pool):
+            run_step(xs[i], ds[i], w, ws, None, vanilla)
+        pool = g.pool()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
 def timed(xs, ds, w, ws, steps, warmup, vanilla):
+    """(graph ms/step, eager ms/step, per-call event timer)."""
     for i in range(warmup):
         run_step(xs[i % len(xs)], ds[i % len(ds)], w, ws, None, vanilla)
     torch.cuda.synchronize()
+    # eager: one Python call per kernel group, as an op-by-op caller runs it
     t0 = time.perf_counter()
     for i in range(steps):
         run_step(xs[i % len(xs)], ds[i % len(ds)], w, ws, None, vanilla)
     torch.cuda.synchronize()
-    whole_ms = (time.perf_counter() - t0) * 1e3 / steps
+    eager_ms = (time.perf_counter() - t0) * 1e3 / steps
+    # graph replay: the same launches with the host out of the loop
+    graphs = capture(xs, ds, w, ws, vanilla)
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) * 1e3 / steps
+    del graphs
     # per-kernel-call durations, events on the launch stream, same rotation
     t = Timer()
     for i in range(steps):
         run_step(xs[i % len(xs)], ds[i % len(ds)], w, ws, t, vanilla)
     torch.cuda.synchronize()
-    return whole_ms, t
+    return graph_ms, eager_ms, t
 
 
 def cpu_baseline(cfg_rows, m, n):
@@ -188,18 +219,28 @@ def traffic_probe(args):
     print("traffic probe done: copy %d bytes" % COPY_BYTES, file=sys.stderr)
 
 
-def load_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, if it was taken on the current kernel source (else None)."""
+GEMM_SOURCES = ["gemm.hip", "gemm_ws.hip", "gemm_common.hpp"]
+
+
+def gemm_source_sha():
+    """One hash over the sources of the forward GEMM call's two kernels."""
     import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(os.path.join(ROOT, "mean_residual_quantized_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def load_traffic():
+    """HBM bytes per forward GEMM call (k_rank1 + k_gemm_ws) from the committed
+    counter summary, if it was taken on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
-    src = os.path.join(ROOT, "mean_residual_quantized_amd", "csrc", "gemm.hip")
     try:
         rec = json.load(open(path))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        sha = gemm_source_sha()
     except (OSError, ValueError):
         return None
-    if rec.get("gemm_source_sha256") != sha:
+    if rec.get("gemm_sources_sha256") != sha:
         return None
     return rec
 
@@ -239,9 +280,13 @@ def main():
         dx=torch.empty((l, m), dtype=torch.bfloat16, device=dev),
     )
     log("bench: %d rotating input copies; warmup %d, steps %d" % (copies, args.warmup, args.steps))
-    ms_a, ta = timed(xs, ds, w0, ws, args.steps, args.warmup, vanilla=False)
-    ms_v, tv = timed(xs, ds, w0, ws, args.steps, args.warmup, vanilla=True)
-    log("bench: averis %.3f ms/step, vanilla %.3f ms/step" % (ms_a, ms_v))
+    graph_a, eager_a, ta = timed(xs, ds, w0, ws, args.steps, args.warmup, vanilla=False)
+    graph_v, eager_v, tv = timed(xs, ds, w0, ws, args.steps, args.warmup, vanilla=True)
+    log("bench: averis graph %.3f / eager %.3f ms/step, vanilla graph %.3f / eager %.3f"
+        % (graph_a, eager_a, graph_v, eager_v))
+    # the step as launched the faster way on this host (both run the same kernels)
+    ms_a, mode_a = min((graph_a, "graph"), (eager_a, "eager"))
+    ms_v, mode_v = min((graph_v, "graph"), (eager_v, "eager"))
 
     gemm_flops = 2.0 * l * m * n
     med = lambda v: float(np.median(v)) if v else float("nan")
@@ -268,8 +313,11 @@ def main():
     overhead = dict(fwd_pct=100 * (t_fwd_a / t_fwd_v - 1), dgrad_pct=100 * (t_bwd_a / t_bwd_v - 1),
                     step_pct=100 * (ms_a / ms_v - 1))
 
-    # roofline of the dominant kernel: the Averis forward GEMM (one launch: the
-    # rank-one mean term is fused into it), timed by the events around the call
+    # roofline of the dominant kernel: the Averis forward GEMM call, timed by
+    # the events around it on the launch stream.  The call is two launches:
+    # k_rank1 (the mean row times W, a GEMV of 2mn flops, ~4 us) and k_gemm_ws
+    # (the NT GEMM over the residual codes, with the rank-one row added in its
+    # epilogue).  The flops counted are the GEMM's 2lmn.
     g_ms = comp["gemm_fwd"]
     achieved = gemm_flops / (g_ms * 1e-3) / 1e12
     tr = load_traffic()
@@ -278,8 +326,9 @@ def main():
         traffic = tr["gemm_fwd"]["fetch_bytes"] + tr["gemm_fwd"]["write_bytes"]
     roofline = dict(bound="mfma", achieved=achieved, peak=F16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=achieved / F16_MFMA_PEAK_TFLOPS, traffic=traffic,
-                    kernel="k_gemm_fast (Averis forward: NVFP4 NT GEMM + rank-one mean term, exact "
-                           "fp16 dequant -> v_mfma_f32_32x32x16_f16), M=%d N=%d K=%d" % (l, n, m),
+                    kernel="averis_gemm_fwd = k_rank1 (mean-row GEMV) + k_gemm_ws (warp-specialized "
+                           "NVFP4 NT GEMM, exact fp16 dequant -> v_mfma_f32_32x32x16_f16, rank-one "
+                           "row added in the epilogue), M=%d N=%d K=%d, bf16 out" % (l, n, m),
                     frac_of_fp4_peak=achieved / FP4_MFMA_PEAK_TFLOPS)
 
     out = {
@@ -305,6 +354,10 @@ def main():
         "vanilla_gemm": vgemm,
         "weight_quant_ms": comp["wquant"],
         "vanilla_ms_per_step": ms_v,
+        "step_launch": {"averis": mode_a, "vanilla": mode_v,
+                        "graph": "one HIP graph per step, replayed", "eager": "one Python call per op"},
+        "averis_ms_per_step": {"graph": graph_a, "eager": eager_a},
+        "vanilla_ms_per_step_by_launch": {"graph": graph_v, "eager": eager_v},
         "overhead_vs_vanilla": overhead,
         "pages_overhead_context": "2.20% end-to-end over vanilla NVFP4 (hardware not stated)",
     }

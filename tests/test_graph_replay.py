@@ -1,0 +1,71 @@
+"""The whole forward + dgrad step captured in one HIP graph and replayed.
+
+Every launch of the library is a plain kernel launch on the caller's stream
+(no allocation, copy or memset inside), so a captured step must reproduce the
+eager step bit for bit on every replay, also with other eager work and
+synchronizations between the replays.  The eager path itself is checked
+against the oracle in test_gpu_parity.py."""
+
+import pytest
+import torch
+
+from mean_residual_quantized_amd import averis as av
+from mean_residual_quantized_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    av.lib()
+
+
+def step(x, w, d, vanilla):
+    wt = av.averis_quant(w, transpose=True, rnd=av.RN, sr_stream=av.STREAM_WEIGHT)
+    wd = av.averis_quant(w, transpose=False, rnd=av.RN, sr_stream=av.STREAM_WEIGHT)
+    if vanilla:
+        xq = av.averis_quant(x, seed=0)
+        dq = av.averis_quant(d, seed=1)
+        y = av.averis_gemm_vanilla(xq, wt, out_dtype=torch.bfloat16)
+        dx = av.averis_gemm_vanilla(dq, wd, out_dtype=torch.bfloat16)
+        quants = [wt, wd, xq, dq]
+        extra = []
+    else:
+        xr, xm, xmu = av.averis_split_quant(x, seed=0)
+        y = av.averis_gemm_fwd(xr, xm, wt, out_dtype=torch.bfloat16)
+        dr, dm, dmu = av.averis_split_quant(d, seed=1)
+        dx = av.averis_gemm_dgrad(dr, dm, wd, out_dtype=torch.bfloat16)
+        quants = [wt, wd, xr, xm, dr, dm]
+        extra = [xmu, dmu]
+    flat = [t for q in quants for t in (q.codes, q.scales, q.tscale)]
+    return flat + extra + [y, dx]
+
+
+@pytest.mark.parametrize("vanilla", [False, True])
+@pytest.mark.parametrize("l,m,n", [(1000, 320, 192), (8192, 1024, 3072)])
+def test_graph_replays_match_eager(l, m, n, vanilla):
+    cfg = workloads.config1(l=l, m=m, n=n)
+    x, w, d = cfg["x"].cuda(), cfg["w"].cuda(), cfg["d"].cuda()
+    ref = [t.clone() for t in step(x, w, d, vanilla)]
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = step(x, w, d, vanilla)
+    torch.cuda.synchronize()
+
+    other = workloads.config1(l=256, m=m, n=n)["x"].cuda()
+    for rep in range(3):
+        # eager work of the program's own between replays
+        av.averis_split_quant(other, seed=rep)
+        torch.cuda.synchronize()
+        for t in outs:
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, ref)):
+            assert torch.equal(a, b), "replay %d, output %d differs from the eager step" % (rep, i)
+    del g
+    torch.cuda.synchronize()
