@@ -11,9 +11,11 @@ the mean term) is timed the same way to report the Averis overhead.
 Inputs are resident in HBM before timing starts; the timed steps rotate
 through enough copies of X and D (> 512 MB) that the 256 MB MALL cannot hold
 them, so every step reads its activations from HBM.  The step is timed
-two ways -- op by op from Python, and as one captured HIP graph per
-input copy -- and report the faster (the same kernels run either way; which
-one wins depends on the host), with both figures beside it.
+three ways: op by op from Python (host clock), as one captured HIP graph per
+input copy (host clock), and op by op with the launches queued behind a spin
+kernel, timed by events on the launch stream.  The last is the headline: the
+device's own step time, free of the host's launch cost; the other two are
+reported beside it.
 
 Prints ONE JSON line (see the keys below).
 """
@@ -91,8 +93,7 @@ def run_step(x, d, w, ws, t=None, vanilla=False):
         if t:
             t.stop(n)
     tic("wquant")
-    wt = av.averis_quant(w, transpose=True, rnd=av.RN, sr_stream=av.STREAM_WEIGHT, ws=ws["q"])
-    wd = av.averis_quant(w, transpose=False, rnd=av.RN, sr_stream=av.STREAM_WEIGHT, ws=ws["q"])
+    wt, wd = av.averis_quant_pair(w, rnd=av.RN, ws=ws["q"])
     toc("wquant")
     if not vanilla:
         tic("split_x")
@@ -137,18 +138,42 @@ def capture(xs, ds, w, ws, vanilla):
     return graphs
 
 
+_SLEEP_CYCLES_PER_MS = None
+
+
+def hold_gpu(ms):
+    """Enqueue a spin kernel of about `ms` milliseconds, so that the launches
+    queued behind it run back to back, with no wait on the host."""
+    global _SLEEP_CYCLES_PER_MS
+    if _SLEEP_CYCLES_PER_MS is None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        e0.record()
+        torch.cuda._sleep(20_000_000)
+        e1.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_MS = 20_000_000 / max(e0.elapsed_time(e1), 1e-3)
+    torch.cuda._sleep(int(ms * _SLEEP_CYCLES_PER_MS))
+
+
 def timed(xs, ds, w, ws, steps, warmup, vanilla):
-    """(graph ms/step, eager ms/step, per-call event timer)."""
+    """Step time three ways (ms/step) and a per-call event timer.
+
+    eager:  one Python call per op, timed on the host around the loop;
+    graph:  one captured HIP graph per input copy, replayed;
+    queued: the eager launches queued behind a spin kernel and timed with
+            events on the launch stream: the device's own step time, with the
+            host's launch cost taken out."""
     for i in range(warmup):
         run_step(xs[i % len(xs)], ds[i % len(ds)], w, ws, None, vanilla)
     torch.cuda.synchronize()
-    # eager: one Python call per kernel group, as an op-by-op caller runs it
     t0 = time.perf_counter()
     for i in range(steps):
         run_step(xs[i % len(xs)], ds[i % len(ds)], w, ws, None, vanilla)
+    enqueue_ms = (time.perf_counter() - t0) * 1e3
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / steps
-    # graph replay: the same launches with the host out of the loop
+
     graphs = capture(xs, ds, w, ws, vanilla)
     for i in range(warmup):
         graphs[i % len(graphs)].replay()
@@ -159,12 +184,29 @@ def timed(xs, ds, w, ws, steps, warmup, vanilla):
     torch.cuda.synchronize()
     graph_ms = (time.perf_counter() - t0) * 1e3 / steps
     del graphs
-    # per-kernel-call durations, events on the launch stream, same rotation
+
+    hold = 2.0 * enqueue_ms + 2.0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hold_gpu(hold)
+    e0.record()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        run_step(xs[i % len(xs)], ds[i % len(ds)], w, ws, None, vanilla)
+    e1.record()
+    queued_enqueue_ms = (time.perf_counter() - t0) * 1e3
+    torch.cuda.synchronize()
+    queued_ms = e0.elapsed_time(e1) / steps
+    if queued_enqueue_ms > 0.8 * hold:
+        log("bench: warning: enqueue took %.2f ms of a %.2f ms hold" % (queued_enqueue_ms, hold))
+
+    # per-kernel-call durations, events on the launch stream, same rotation,
+    # also queued behind a spin kernel
     t = Timer()
+    hold_gpu(hold * 1.5)
     for i in range(steps):
         run_step(xs[i % len(xs)], ds[i % len(ds)], w, ws, t, vanilla)
     torch.cuda.synchronize()
-    return graph_ms, eager_ms, t
+    return dict(eager=eager_ms, graph=graph_ms, queued=queued_ms), t
 
 
 def cpu_baseline(cfg_rows, m, n):
@@ -209,8 +251,7 @@ def traffic_probe(args):
     x, w, d = cfg["x"].cuda(), cfg["w"].cuda(), cfg["d"].cuda()
     torch.cuda.synchronize()
     for _ in range(3):
-        wt = av.averis_quant(w, transpose=True, rnd=av.RN, sr_stream=av.STREAM_WEIGHT)
-        wd = av.averis_quant(w, transpose=False, rnd=av.RN, sr_stream=av.STREAM_WEIGHT)
+        wt, wd = av.averis_quant_pair(w, rnd=av.RN)
         xr, xm, _ = av.averis_split_quant(x, seed=0)
         av.averis_gemm_fwd(xr, xm, wt, out_dtype=torch.bfloat16)
         dr, dm, _ = av.averis_split_quant(d, seed=1)
@@ -280,13 +321,13 @@ def main():
         dx=torch.empty((l, m), dtype=torch.bfloat16, device=dev),
     )
     log("bench: %d rotating input copies; warmup %d, steps %d" % (copies, args.warmup, args.steps))
-    graph_a, eager_a, ta = timed(xs, ds, w0, ws, args.steps, args.warmup, vanilla=False)
-    graph_v, eager_v, tv = timed(xs, ds, w0, ws, args.steps, args.warmup, vanilla=True)
-    log("bench: averis graph %.3f / eager %.3f ms/step, vanilla graph %.3f / eager %.3f"
-        % (graph_a, eager_a, graph_v, eager_v))
-    # the step as launched the faster way on this host (both run the same kernels)
-    ms_a, mode_a = min((graph_a, "graph"), (eager_a, "eager"))
-    ms_v, mode_v = min((graph_v, "graph"), (eager_v, "eager"))
+    ta_ms, ta = timed(xs, ds, w0, ws, args.steps, args.warmup, vanilla=False)
+    tv_ms, tv = timed(xs, ds, w0, ws, args.steps, args.warmup, vanilla=True)
+    log("bench: averis %s, vanilla %s (ms/step)" % (
+        " ".join("%s %.4f" % kv for kv in ta_ms.items()),
+        " ".join("%s %.4f" % kv for kv in tv_ms.items())))
+    # the headline is the device's step time (launches queued ahead of it)
+    ms_a, ms_v = ta_ms["queued"], tv_ms["queued"]
 
     gemm_flops = 2.0 * l * m * n
     med = lambda v: float(np.median(v)) if v else float("nan")
@@ -354,10 +395,11 @@ def main():
         "vanilla_gemm": vgemm,
         "weight_quant_ms": comp["wquant"],
         "vanilla_ms_per_step": ms_v,
-        "step_launch": {"averis": mode_a, "vanilla": mode_v,
-                        "graph": "one HIP graph per step, replayed", "eager": "one Python call per op"},
-        "averis_ms_per_step": {"graph": graph_a, "eager": eager_a},
-        "vanilla_ms_per_step_by_launch": {"graph": graph_v, "eager": eager_v},
+        "step_ms_by_launch": {"averis": ta_ms, "vanilla": tv_ms,
+                              "queued": "launches queued behind a spin kernel, events on the "
+                                        "launch stream (the headline)",
+                              "eager": "one Python call per op, host clock",
+                              "graph": "one HIP graph per step, replayed, host clock"},
         "overhead_vs_vanilla": overhead,
         "pages_overhead_context": "2.20% end-to-end over vanilla NVFP4 (hardware not stated)",
     }

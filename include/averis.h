@@ -154,6 +154,24 @@ averis_status_t averis_quant_batched(const void* a, averis_dtype_t dtype, int ba
                                      uint32_t sr_stream, const averis_nvfp4_t* out, void* ws,
                                      size_t ws_bytes, hipStream_t stream);
 
+/* Both quantized copies of a weight in one call (Lighthouse §2.2: the
+ * forward product takes Q4(W^T) with blocks along m, the dgrad product Q4(W)
+ * with blocks along n).  a holds `batch` stored rows x cols matrices W_b
+ * (row stride lda, matrix b at a + b*batch_stride elements).  Writes
+ *   out   = Q4(W_b),   (batch*rows) x cols, blocks along cols, and
+ *   out_t = Q4(W_b^T), (batch*cols) x rows, blocks along rows,
+ * with one tensor scale per matrix (max |W_b|, shared by both copies).
+ * Codes, scales and tensor scales are those of averis_quant_batched with
+ * transpose = 0 (out) and transpose = 1 (out_t), the same seed and stream,
+ * bit for bit.  Needs rows % 16 == 0, cols % 16 == 0, both > 0, 16-byte
+ * aligned a and lda * element size % 16 == 0.
+ * Workspace: AVERIS_OP_QUANT (rows, cols, batch). */
+averis_status_t averis_quant_pair(const void* a, averis_dtype_t dtype, int batch, int64_t rows,
+                                  int64_t cols, int64_t lda, int64_t batch_stride, uint64_t seed,
+                                  averis_round_t rnd, uint32_t sr_stream,
+                                  const averis_nvfp4_t* out, const averis_nvfp4_t* out_t,
+                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Grouped plain quant of activations: one tensor scale per segment
  * (vanilla arm of the grouped case).  Workspace: AVERIS_OP_QUANT with nseg. */
 averis_status_t averis_quant_grouped(const void* a, averis_dtype_t dtype, int64_t rows,

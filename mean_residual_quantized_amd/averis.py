@@ -27,9 +27,9 @@ STREAM_ACT, STREAM_MEAN, STREAM_WEIGHT = 0, 1, 2
 # every symbol include/averis.h declares
 EXPORTS = [
     "averis_split_quant", "averis_split_quant_grouped", "averis_quant", "averis_quant_batched",
-    "averis_quant_grouped", "averis_gemm_fwd", "averis_gemm_dgrad", "averis_gemm_vanilla",
-    "averis_gemm_grouped", "averis_workspace_bytes", "averis_status_str", "averis_abi_version",
-    "averis_last_error",
+    "averis_quant_grouped", "averis_quant_pair", "averis_gemm_fwd", "averis_gemm_dgrad",
+    "averis_gemm_vanilla", "averis_gemm_grouped", "averis_workspace_bytes", "averis_status_str",
+    "averis_abi_version", "averis_last_error",
 ]
 
 
@@ -64,6 +64,7 @@ def lib():
             "averis_quant": [P, I, I64, I64, I64, I, U64, I, U32, T, P, SZ, P],
             "averis_quant_batched": [P, I, I, I64, I64, I64, I64, I, U64, I, U32, T, P, SZ, P],
             "averis_quant_grouped": [P, I, I64, I64, I64, P, I, U64, I, U32, T, P, SZ, P],
+            "averis_quant_pair": [P, I, I, I64, I64, I64, I64, U64, I, U32, T, T, P, SZ, P],
             "averis_gemm_fwd": [T, T, T, P, I, I64, P, SZ, P],
             "averis_gemm_dgrad": [T, T, T, P, I, I64, P, SZ, P],
             "averis_gemm_vanilla": [T, T, P, I, I64, P, SZ, P],
@@ -212,6 +213,26 @@ def averis_quant_batched(a, transpose=False, seed=0, rnd=RN, sr_stream=STREAM_WE
         int(transpose), seed, rnd, sr_stream, ctypes.byref(o), ws.data_ptr(), ws.numel(),
         _stream()))
     return out
+
+
+def averis_quant_pair(w, seed=0, rnd=RN, sr_stream=STREAM_WEIGHT, ws=None):
+    """Both quantized copies of a weight in one call: returns (wt, wd) with
+    wt = Q4(w^T) (blocks along w's rows; the forward operand) and wd = Q4(w)
+    (blocks along w's cols; the dgrad operand).  w: 2-D, or 3-D (batch of
+    matrices, one tensor scale each)."""
+    a = w if w.dim() == 3 else w.unsqueeze(0)
+    batch, rows, cols = a.shape
+    if a.stride(2) != 1:
+        raise ValueError("expected unit innermost stride")
+    wd = NVFP4.empty(batch * rows, cols, batch, w.device)
+    wt = NVFP4.empty(batch * cols, rows, batch, w.device)
+    need = workspace_bytes(OP_QUANT, rows, cols, 0, batch)
+    ws = ws if ws is not None else _workspace(need, w.device)
+    o, ot = wd.c(), wt.c()
+    _check("averis_quant_pair", lib().averis_quant_pair(
+        a.data_ptr(), _dtype_code(a), batch, rows, cols, a.stride(1), a.stride(0), seed, rnd,
+        sr_stream, ctypes.byref(o), ctypes.byref(ot), ws.data_ptr(), ws.numel(), _stream()))
+    return wt, wd
 
 
 def averis_quant_grouped(a, offsets, seed=0, rnd=SR, sr_stream=STREAM_ACT, ws=None):

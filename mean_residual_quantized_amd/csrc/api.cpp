@@ -240,6 +240,35 @@ averis_status_t averis_quant_grouped(const void* a, averis_dtype_t dtype, int64_
                       ws_bytes, stream);
 }
 
+averis_status_t averis_quant_pair(const void* a, averis_dtype_t dtype, int batch, int64_t rows,
+                                  int64_t cols, int64_t lda, int64_t batch_stride, uint64_t seed,
+                                  averis_round_t rnd, uint32_t sr_stream,
+                                  const averis_nvfp4_t* out, const averis_nvfp4_t* out_t,
+                                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return AVERIS_E_DTYPE;
+  if (batch < 1 || batch > kMaxSeg) return AVERIS_E_ARG;
+  if (rnd != AVERIS_RN && rnd != AVERIS_SR) return AVERIS_E_ARG;
+  if (sr_stream > 0xFFFFu) return AVERIS_E_ARG;
+  if (rows <= 0 || cols <= 0 || rows % 16 != 0 || cols % 16 != 0) return AVERIS_E_SHAPE;
+  if (lda < cols || batch_stride < 0) return AVERIS_E_SHAPE;
+  if (batch > 1 && batch_stride < rows * lda) return AVERIS_E_SHAPE;
+  if (!a) return AVERIS_E_NULL;
+  const size_t es = elem_size(dtype);
+  if (!aligned(a, 16) || ((size_t)lda * es) % 16 != 0 || ((size_t)batch_stride * es) % 16 != 0)
+    return AVERIS_E_ALIGN;
+  averis_status_t s = check_tensor(out, (int64_t)batch * rows, cols);
+  if (s != AVERIS_OK) return s;
+  if ((s = check_tensor(out_t, (int64_t)batch * cols, rows)) != AVERIS_OK) return s;
+  const size_t need = batched_ws_bytes(rows, cols, batch);
+  if (!ws || ws_bytes < need) return AVERIS_E_WORKSPACE;
+  if (!aligned(ws, 256)) return AVERIS_E_ALIGN;
+  const QuantOut o{out->codes, out->scales, out->tscale};
+  const QuantOut ot{out_t->codes, out_t->scales, out_t->tscale};
+  return hip_status(launch_quant_pair(a, dtype == AVERIS_BF16, batch, rows, cols, lda,
+                                      batch_stride, rnd == AVERIS_SR, seed, sr_stream, o, ot,
+                                      static_cast<float*>(ws), stream));
+}
+
 static averis_status_t gemm_common(const averis_nvfp4_t* a, const averis_nvfp4_t* mean,
                                    const averis_nvfp4_t* b, const int64_t* offs, int nseg,
                                    void* c, averis_dtype_t cdtype, int64_t ldc, void* ws,

@@ -46,6 +46,13 @@ hipError_t launch_quant_batched(const void* a, bool bf16, int batch, int64_t row
                                 uint64_t seed, uint32_t stream_id, const QuantOut& out,
                                 float* part, hipStream_t st);
 
+// Q4(W_b) (out, blocks along cols) and Q4(W_b^T) (out_t, blocks along rows)
+// of `batch` stored rows x cols matrices; part: batch x kAmaxBlocks floats.
+hipError_t launch_quant_pair(const void* a, bool bf16, int batch, int64_t rows, int64_t cols,
+                             int64_t lda, int64_t bstride, bool sr, uint64_t seed,
+                             uint32_t stream_id, const QuantOut& out, const QuantOut& out_t,
+                             float* part, hipStream_t st);
+
 // A quantized GEMM operand as the kernels see it.
 struct QOperand {
   const uint8_t* codes;

@@ -534,6 +534,131 @@ __global__ __launch_bounds__(256) void k_quant_batched(const T* __restrict__ a, 
 }
 
 // ---------------------------------------------------------------------------
+// both orientations of a weight in one pass (Lighthouse §2.2: Q4(W^T) for the
+// forward product, Q4(W) for dgrad; one tensor scale, max |W|, for both)
+// ---------------------------------------------------------------------------
+
+// max |a| of each stored rows x cols matrix, 16-byte loads; workgroup x of
+// matrix y covers 16-byte chunks [x*per, (x+1)*per) of the row-major order
+template <typename T>
+__global__ __launch_bounds__(256) void k_amax_vec(const T* __restrict__ a, int64_t rows,
+                                                  int64_t cols, int64_t lda, int64_t bstride,
+                                                  int64_t per, float* __restrict__ part) {
+  constexpr int VE = 16 / (int)sizeof(T);   // elements per 16-byte chunk
+  constexpr int U = 4;
+  const T* base = a + (int64_t)blockIdx.y * bstride;
+  const int64_t cpr = cols / VE, total = rows * cpr;
+  const int64_t q0 = (int64_t)blockIdx.x * per;
+  const int64_t q1 = q0 + per < total ? q0 + per : total;
+  float m = 0.0f;
+  for (int64_t q = q0 + threadIdx.x; q < q1; q += 256 * U) {
+    uint4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t qq = q + 256 * u < q1 ? q + 256 * u : q;   // repeat a real chunk
+      const int64_t r = qq / cpr;
+      w[u] = *reinterpret_cast<const uint4*>(base + r * lda + (qq - r * cpr) * VE);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t x[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (sizeof(T) == 2) {
+          m = __builtin_fmaxf(m, __builtin_fabsf(bf16_lo(x[i])));
+          m = __builtin_fmaxf(m, __builtin_fabsf(bf16_hi(x[i])));
+        } else {
+          m = __builtin_fmaxf(m, __builtin_fabsf(__uint_as_float(x[i])));
+        }
+      }
+    }
+  }
+  __shared__ float red[4];
+  m = block_max(m, red);
+  if (threadIdx.x == 0) part[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = m;
+}
+
+// one 64 x 64 tile of W_b per workgroup, staged in LDS as fp32; each thread
+// quantizes one 16-block along a row (-> out) and one along a column (-> out_t)
+constexpr int kPairTile = 64;
+constexpr int kPairLd = kPairTile + 4;   // padded LDS row (floats), 16-byte aligned
+
+template <typename T, bool SR>
+__global__ __launch_bounds__(256) void k_pair(const T* __restrict__ a, int64_t rows, int64_t cols,
+                                              int64_t lda, int64_t bstride, uint64_t seed,
+                                              uint32_t stream, const float* __restrict__ part,
+                                              int64_t npart, QuantOut out, QuantOut out_t) {
+  constexpr int VE = 16 / (int)sizeof(T);
+  constexpr int NCH = kPairTile / VE;              // 16-byte chunks per tile row
+  constexpr int PER = kPairTile * NCH / 256;       // chunks per thread
+  __shared__ float tile[kPairTile][kPairLd];
+  const int bt = blockIdx.z;
+  const int64_t r0 = (int64_t)blockIdx.y * kPairTile, c0 = (int64_t)blockIdx.x * kPairTile;
+  const T* base = a + (int64_t)bt * bstride;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = tid + 256 * i;
+    const int lr = idx / NCH, ch = idx % NCH;
+    const int64_t r = r0 + lr, c = c0 + (int64_t)ch * VE;
+    uint4 w = {0u, 0u, 0u, 0u};
+    if (r < rows && c < cols) w = *reinterpret_cast<const uint4*>(base + r * lda + c);
+    float* dst = &tile[lr][ch * VE];
+    if (sizeof(T) == 2) {
+      const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dst[2 * e] = bf16_lo(x[e]);
+        dst[2 * e + 1] = bf16_hi(x[e]);
+      }
+    } else {
+      dst[0] = __uint_as_float(w.x);
+      dst[1] = __uint_as_float(w.y);
+      dst[2] = __uint_as_float(w.z);
+      dst[3] = __uint_as_float(w.w);
+    }
+  }
+  // the tensor scale (reduce_partials synchronizes the block, which also
+  // publishes the tile)
+  const float am = reduce_partials(part + (int64_t)bt * npart, npart);
+  float s_enc, s_dec;
+  tensor_scales(am, s_enc, s_dec);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
+    out.tscale[2 * bt] = s_enc;
+    out.tscale[2 * bt + 1] = s_dec;
+    out_t.tscale[2 * bt] = s_enc;
+    out_t.tscale[2 * bt + 1] = s_dec;
+  }
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  const int l = tid >> 2, q = tid & 3;
+  float v[16];
+  // a 16-block along row r0 + l: out row b*rows + r, columns c0 + 16q ..
+  {
+    const int64_t r = r0 + l, c = c0 + 16 * q;
+    if (r < rows && c < cols) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = tile[l][16 * q + k];
+      const int64_t grow = (int64_t)bt * rows + r;
+      quant_block16<SR>(v, s_enc, (uint64_t)grow * (uint64_t)cols + (uint64_t)c, k0, k1, stream,
+                        out.codes + grow * (cols >> 1) + (c >> 1),
+                        out.scales + grow * (cols >> 4) + (c >> 4));
+    }
+  }
+  // a 16-block along column c0 + l: out_t row b*cols + c, columns r0 + 16q ..
+  {
+    const int64_t c = c0 + l, r = r0 + 16 * q;
+    if (c < cols && r < rows) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = tile[16 * q + k][l];
+      const int64_t grow = (int64_t)bt * cols + c;
+      quant_block16<SR>(v, s_enc, (uint64_t)grow * (uint64_t)rows + (uint64_t)r, k0, k1, stream,
+                        out_t.codes + grow * (rows >> 1) + (r >> 1),
+                        out_t.scales + grow * (rows >> 4) + (r >> 4));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 template <typename T>
@@ -633,6 +758,42 @@ hipError_t launch_quant_batched(const void* a, bool bf16, int batch, int64_t row
                                  stream_id, out, part, st);
   return run_batched<float>(a, batch, rows, cols, lda, bstride, transpose, sr, seed, stream_id,
                             out, part, st);
+}
+
+template <typename T>
+static hipError_t run_pair(const void* a_, int batch, int64_t rows, int64_t cols, int64_t lda,
+                           int64_t bstride, bool sr, uint64_t seed, uint32_t stream_id,
+                           const QuantOut& out, const QuantOut& out_t, float* part,
+                           hipStream_t st) {
+  const T* a = static_cast<const T*>(a_);
+  constexpr int64_t VE = 16 / (int64_t)sizeof(T);
+  const int64_t total = rows * (cols / VE);
+  int64_t nblk = (total + 256 * 4 - 1) / (256 * 4);
+  if (nblk > kAmaxBlocks) nblk = kAmaxBlocks;
+  if (nblk < 1) nblk = 1;
+  const int64_t per = (total + nblk - 1) / nblk;
+  k_amax_vec<T><<<dim3((unsigned)nblk, (unsigned)batch), 256, 0, st>>>(a, rows, cols, lda, bstride,
+                                                                       per, part);
+  const dim3 g((unsigned)((cols + kPairTile - 1) / kPairTile),
+               (unsigned)((rows + kPairTile - 1) / kPairTile), (unsigned)batch);
+  if (sr)
+    k_pair<T, true><<<g, 256, 0, st>>>(a, rows, cols, lda, bstride, seed, stream_id, part, nblk,
+                                       out, out_t);
+  else
+    k_pair<T, false><<<g, 256, 0, st>>>(a, rows, cols, lda, bstride, seed, stream_id, part, nblk,
+                                        out, out_t);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_pair(const void* a, bool bf16, int batch, int64_t rows, int64_t cols,
+                             int64_t lda, int64_t bstride, bool sr, uint64_t seed,
+                             uint32_t stream_id, const QuantOut& out, const QuantOut& out_t,
+                             float* part, hipStream_t st) {
+  if (bf16)
+    return run_pair<uint16_t>(a, batch, rows, cols, lda, bstride, sr, seed, stream_id, out, out_t,
+                              part, st);
+  return run_pair<float>(a, batch, rows, cols, lda, bstride, sr, seed, stream_id, out, out_t, part,
+                         st);
 }
 
 }  // namespace averis

@@ -138,3 +138,25 @@ def test_grouped_and_batched_rejections(L):
     assert qb(batch=0) == 6
     assert qb(bstride=100) == 2                           # overlapping batch entries
     assert qb(batch=3) == 2                               # out rows != batch * rows
+
+
+def test_quant_pair_rejections(L):
+    out, out_t = nv(2 * 64, 128), nv(2 * 128, 64)
+    qp = lambda a=P, dt=av.BF16, batch=2, rows=64, cols=128, lda=128, bstride=64 * 128, rnd=av.RN, \
+        out=out, out_t=out_t, ws=P, wsb=1 << 20: L.averis_quant_pair(
+            a, dt, batch, rows, cols, lda, bstride, 0, rnd, 2, ctypes.byref(out),
+            ctypes.byref(out_t), ws, wsb, None)
+    assert qp(batch=0) == 6
+    assert qp(rnd=3) == 6
+    assert qp(dt=5) == 3
+    assert qp(rows=40) == 2                               # rows % 16 (out_t's block dim)
+    assert qp(cols=24, lda=24) == 2
+    assert qp(lda=64) == 2
+    assert qp(bstride=100) == 2                           # overlapping batch entries
+    assert qp(a=None) == 1
+    assert qp(a=P + 4) == 4                               # 16-byte vector loads
+    assert qp(lda=132, bstride=64 * 132) == 4
+    assert qp(out_t=nv(2 * 128, 32)) == 2                 # out_t is (batch*cols) x rows
+    assert qp(out=nv(64, 128)) == 2
+    assert qp(ws=None) == 5
+    assert qp(wsb=64) == 5

@@ -23,8 +23,7 @@ def _gpu():
 
 
 def step(x, w, d, vanilla):
-    wt = av.averis_quant(w, transpose=True, rnd=av.RN, sr_stream=av.STREAM_WEIGHT)
-    wd = av.averis_quant(w, transpose=False, rnd=av.RN, sr_stream=av.STREAM_WEIGHT)
+    wt, wd = av.averis_quant_pair(w, rnd=av.RN)
     if vanilla:
         xq = av.averis_quant(x, seed=0)
         dq = av.averis_quant(d, seed=1)
