@@ -84,8 +84,9 @@ typedef enum {
 /* An NVFP4-style tensor of rows x cols logical elements, 16-blocks along
  * cols.  codes: rows * cols/2 bytes, row-major, byte j of a row holds element
  * 2j in bits 3:0 and element 2j+1 in bits 7:4; 16-byte aligned.
- * scales: rows * cols/16 E4M3FN bytes, row-major.  tscale: 2 floats
- * [S_enc, S_dec] per tensor (per segment / batch entry for grouped calls).
+ * scales: rows * cols/16 E4M3FN bytes, row-major; 16-byte aligned.
+ * tscale: 2 floats [S_enc, S_dec] per tensor (per segment / batch entry for
+ * grouped calls).
  * All three are device pointers. */
 typedef struct {
   uint8_t* codes;

@@ -26,7 +26,8 @@ averis_status_t check_tensor(const averis_nvfp4_t* t, int64_t rows, int64_t cols
   if (!t || !t->tscale) return AVERIS_E_NULL;
   if (t->rows != rows || t->cols != cols) return AVERIS_E_SHAPE;
   if (rows > 0 && (!t->codes || !t->scales)) return AVERIS_E_NULL;
-  if (!aligned(t->codes, 16) || !aligned(t->tscale, 4)) return AVERIS_E_ALIGN;
+  if (!aligned(t->codes, 16) || !aligned(t->scales, 16) || !aligned(t->tscale, 4))
+    return AVERIS_E_ALIGN;
   return AVERIS_OK;
 }
 

@@ -621,7 +621,8 @@ hipError_t launch_gemm(const QOperand& a, const QOperand* mean, const QOperand& 
   float* rho_ws = static_cast<float*>(ws);
   if (m == 0 || n == 0) return hipGetLastError();
   // warp-specialized kernel (default); AVERIS_GEMM_KERNEL = 1 selects the
-  // lock-step kernel below, AVERIS_GEMM_WS_TILE = 1..2 forces a variant
+  // lock-step kernel below, AVERIS_GEMM_WS_TILE = 1..4 forces a variant,
+  // AVERIS_GEMM_BQ = 1 keeps B as codes in LDS
   static const int kernel_sel = [] {
     const char* e = std::getenv("AVERIS_GEMM_KERNEL");
     return e ? std::atoi(e) : 0;
@@ -632,7 +633,12 @@ hipError_t launch_gemm(const QOperand& a, const QOperand* mean, const QOperand& 
       const char* e = std::getenv("AVERIS_GEMM_WS_TILE");
       return e ? std::atoi(e) : 0;
     }();
-    if (v != 0 && forced_ws >= 1 && forced_ws <= 2) v = forced_ws;
+    static const int bq = [] {
+      const char* e = std::getenv("AVERIS_GEMM_BQ");
+      return e ? std::atoi(e) : 0;
+    }();
+    if (v != 0 && bq == 1) v += 2;   // the same tile with B kept as codes in LDS
+    if (v != 0 && forced_ws >= 1 && forced_ws <= 4) v = forced_ws;
     if (v != 0) {
       if (mean) {
         dim3 g((unsigned)((n + kRank1Cols - 1) / kRank1Cols), (unsigned)(offs ? nseg : 1));

@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdlib>
+
 #include "gemm_common.hpp"
 #include "launch.hpp"
 #include "segments.hpp"
@@ -39,6 +41,7 @@ namespace {
 constexpr int kWsBK = 64;
 constexpr int kWsLdsK = kWsBK + 8;   // fp16 per LDS row (16-byte pad against bank conflicts)
 constexpr int kProducers = 256;      // producer threads (waves 4..7)
+constexpr int kBqLd = 9;             // dwords per B code row in LDS (odd: no bank conflicts)
 
 template <int V>
 struct WsIC {
@@ -55,20 +58,27 @@ __device__ __forceinline__ void ws_unroll(F&& f) {
 
 }  // namespace
 
-template <int TM, int TN, int PF, bool OUT_BF16, bool HAS_MEAN>
+template <int TM, int TN, int PF, bool OUT_BF16, bool HAS_MEAN, bool BQ, bool SG>
 __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B,
                                                     const float* __restrict__ rho, int64_t m,
                                                     int64_t n, int64_t k, const int64_t* offs,
                                                     int nseg, void* c, int64_t ldc) {
   constexpr int BM = 64 * TM, BN = 64 * TN;
-  constexpr int NCH = 2 * (BM + BN);                     // 32-element chunks per stage
+  // 32-element chunks dequantized per stage: A rows (and B rows unless BQ)
+  constexpr int NCH = BQ ? 2 * BM : 2 * (BM + BN);
   constexpr int CP = (NCH + kProducers - 1) / kProducers;  // chunks per producer thread
   constexpr int IA = 2 * BM / kProducers;                // chunk rounds that hold A rows
   static_assert((2 * BM) % kProducers == 0 && (2 * BN) % 64 == 0, "whole-wave chunk rounds");
+  static_assert(!BQ || BN <= kProducers, "one B row per producer thread");
   extern __shared__ __attribute__((aligned(16))) _Float16 smem_ws[];
   _Float16* As = smem_ws;                                // [2][BM][LDSK]
-  _Float16* Bs = As + 2 * BM * kWsLdsK;                  // [2][BN][LDSK]
-  float* rho_sh = reinterpret_cast<float*>(Bs + 2 * BN * kWsLdsK);   // [BN]
+  // B as fp16 ([2][BN][LDSK]) or, with BQ, as codes ([2][BN][kBqLd] dwords)
+  // followed by the stage's four E4M3 scale bytes per row ([2][BN] dwords)
+  _Float16* Bs = As + 2 * BM * kWsLdsK;
+  uint32_t* Bq = reinterpret_cast<uint32_t*>(Bs);
+  uint32_t* Bqs = Bq + 2 * BN * kBqLd;
+  float* rho_sh = BQ ? reinterpret_cast<float*>(Bqs + 2 * BN)
+                     : reinterpret_cast<float*>(Bs + 2 * BN * kWsLdsK);   // [BN]
 
   int64_t tile_x, tile_y;
   xcd_tile(tile_x, tile_y);
@@ -109,27 +119,64 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B,
       const int64_t row = r < lim ? r : lim - 1;
       lrow[i] = r;
       oc[i] = (uint32_t)(row * kh) + 16u * hf;
-      os[i] = (uint32_t)(row * kb) + 2u * hf;
+      os[i] = (uint32_t)(row * kb) + (SG ? 0u : 2u * hf);
     }
+    // SG (K % 256 == 0): a chunk's scale bytes come 16 at a time -- its row's
+    // four stages of one 256-wide group -- into a two-group ring, instead of
+    // two bytes per stage (the loads, not their bytes, are what costs)
+    const uint32_t ssh = 16u * (uint32_t)(pt & 1);   // the chunk's k-half picks 2 of 4 bytes
     uint4 rc[PF][CP];
     uint32_t rs[PF][CP];
+    uint4 rsg[2][CP];
+    // BQ: B row pt is copied as loaded (32 code bytes and 4 scale bytes per stage)
+    const bool bcopy = BQ && pt < BN;
+    const int64_t blim = n - n0;
+    const int64_t brow = pt < blim ? pt : blim - 1;
+    const uint32_t obc = (uint32_t)(brow * kh), obs = (uint32_t)(brow * kb);
+    uint4 rb[PF][2];
+    uint32_t rbs[PF];
 
-    auto gload = [&](int slot, int st) __attribute__((always_inline)) {
+    // sw: the stage index mod 8, a compile-time constant wherever these run
+    // (the loop below advances 8 stages per iteration when SG)
+    auto gload = [&](int slot, int st, auto sw_c) __attribute__((always_inline)) {
+      constexpr int sw = decltype(sw_c)::value;
 #pragma unroll
       for (int i = 0; i < CP; ++i) {
         if (pt + kProducers * i >= NCH) break;   // whole waves
         const uint8_t* cb = (i < IA ? a_c : b_c) + 32 * st;
-        const uint8_t* sb = (i < IA ? a_s : b_s) + 4 * st;
         rc[slot][i] = *reinterpret_cast<const uint4*>(cb + oc[i]);
-        rs[slot][i] = *reinterpret_cast<const uint16_t*>(sb + os[i]);
+        if constexpr (SG) {
+          if constexpr ((sw & 3) == 0) {
+            const uint8_t* sb = (i < IA ? a_s : b_s) + 4 * st;
+            rsg[(sw >> 2) & 1][i] = *reinterpret_cast<const uint4*>(sb + os[i]);
+          }
+        } else {
+          const uint8_t* sb = (i < IA ? a_s : b_s) + 4 * st;
+          rs[slot][i] = *reinterpret_cast<const uint16_t*>(sb + os[i]);
+        }
+      }
+      if (bcopy) {
+        const uint8_t* cb = b_c + 32 * st + obc;
+        rb[slot][0] = *reinterpret_cast<const uint4*>(cb);
+        rb[slot][1] = *reinterpret_cast<const uint4*>(cb + 16);
+        rbs[slot] = *reinterpret_cast<const uint32_t*>(b_s + 4 * st + obs);
       }
     };
-    auto dequant = [&](int slot, int buf, int st) __attribute__((always_inline)) {
+    auto dequant = [&](int slot, int buf, auto sw_c) __attribute__((always_inline)) {
+      constexpr int sw = decltype(sw_c)::value;
 #pragma unroll
       for (int i = 0; i < CP; ++i) {
         const int q = pt + kProducers * i, hf = q & 1;
         if (q >= NCH) break;
-        const half2_t sc = scales2(rs[slot][i]);
+        uint32_t sbytes;
+        if constexpr (SG) {
+          const uint4 g = rsg[(sw >> 2) & 1][i];
+          const uint32_t wd = (sw & 3) == 0 ? g.x : (sw & 3) == 1 ? g.y : (sw & 3) == 2 ? g.z : g.w;
+          sbytes = wd >> ssh;
+        } else {
+          sbytes = rs[slot][i];
+        }
+        const half2_t sc = scales2(sbytes);
         const half2_t s0 = {sc.x, sc.x}, s1 = {sc.y, sc.y};
         uint4 d[4];
         d[0] = deq8(rc[slot][i].x, s0);
@@ -141,43 +188,56 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B,
 #pragma unroll
         for (int e = 0; e < 4; ++e) dst[e] = d[e];
       }
+      if (bcopy) {
+        uint32_t* dst = Bq + (buf * BN + pt) * kBqLd;
+        const uint4 c0 = rb[slot][0], c1 = rb[slot][1];
+        dst[0] = c0.x; dst[1] = c0.y; dst[2] = c0.z; dst[3] = c0.w;
+        dst[4] = c1.x; dst[5] = c1.y; dst[6] = c1.z; dst[7] = c1.w;
+        Bqs[buf * BN + pt] = rbs[slot];
+      }
     };
 
     // stage j's codes live in ring slot j % PF, PF stages ahead of their
-    // dequantization; buffer j & 1 of LDS receives stage j
+    // dequantization; buffer j & 1 of LDS receives stage j.  With SG the
+    // group ring's slot (j >> 2) & 1 is refilled when stage j = 4g is loaded,
+    // after stage 4g - 5 (the last user of that slot) was dequantized.
+    static_assert(!SG || PF == 4, "scale groups assume a 4-stage ring");
+    constexpr int UNR = SG ? 8 : PF;   // stages per loop iteration
     ws_unroll<0, PF>([&](auto p_c) __attribute__((always_inline)) {
       constexpr int p = decltype(p_c)::value;
-      if (p < nk) gload(p, p);
+      if (p < nk) gload(p, p, WsIC<p>{});
     });
     if (HAS_MEAN) {
       // this tile's rank-one terms, for the consumers' epilogue
       for (int cidx = pt; cidx < BN; cidx += kProducers)
         rho_sh[cidx] = n0 + cidx < n ? rho[(int64_t)seg * n + n0 + cidx] : 0.0f;
     }
-    dequant(0, 0, 0);
-    if (PF < nk) gload(0, PF);
+    dequant(0, 0, WsIC<0>{});
+    if (PF < nk) gload(0, PF, WsIC<PF % 8>{});
     __syncthreads();
     // iteration it: dequantize stage it + 1 (slot (it + 1) % PF) into buffer
     // (it + 1) & 1, refill that slot with stage it + 1 + PF
     int it = 0;
-    for (; it + PF <= nk; it += PF) {
-      ws_unroll<0, PF>([&](auto u_c) __attribute__((always_inline)) {
-        constexpr int su = (decltype(u_c)::value + 1) % PF;
-        const int i2 = it + decltype(u_c)::value;
+    for (; it + UNR <= nk; it += UNR) {
+      ws_unroll<0, UNR>([&](auto u_c) __attribute__((always_inline)) {
+        constexpr int u = decltype(u_c)::value;
+        constexpr int su = (u + 1) % PF;
+        const int i2 = it + u;
         if (i2 + 1 < nk) {
-          dequant(su, (i2 + 1) & 1, i2 + 1);
-          if (i2 + 1 + PF < nk) gload(su, i2 + 1 + PF);
+          dequant(su, (i2 + 1) & 1, WsIC<(u + 1) % 8>{});
+          if (i2 + 1 + PF < nk) gload(su, i2 + 1 + PF, WsIC<(u + 1 + PF) % 8>{});
         }
         __syncthreads();
       });
     }
-    ws_unroll<0, PF>([&](auto u_c) __attribute__((always_inline)) {
-      constexpr int su = (decltype(u_c)::value + 1) % PF;
-      const int i2 = it + decltype(u_c)::value;
+    ws_unroll<0, UNR>([&](auto u_c) __attribute__((always_inline)) {
+      constexpr int u = decltype(u_c)::value;
+      constexpr int su = (u + 1) % PF;
+      const int i2 = it + u;
       if (i2 < nk) {
         if (i2 + 1 < nk) {
-          dequant(su, (i2 + 1) & 1, i2 + 1);
-          if (i2 + 1 + PF < nk) gload(su, i2 + 1 + PF);
+          dequant(su, (i2 + 1) & 1, WsIC<(u + 1) % 8>{});
+          if (i2 + 1 + PF < nk) gload(su, i2 + 1 + PF, WsIC<(u + 1 + PF) % 8>{});
         }
         __syncthreads();
       }
@@ -196,22 +256,41 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B,
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   const int a_frag = (wm * 32 * TM + (lane & 31)) * kWsLdsK + (lane >> 5) * 8;
   const int b_frag = (wn * 32 * TN + (lane & 31)) * kWsLdsK + (lane >> 5) * 8;
+  // BQ: the lane's B row within the tile, and its code dword within a k-step
+  const int b_row = wn * 32 * TN + (lane & 31), b_half = lane >> 5;
   // fragments of k-step kk of the stage in buffer b; the reads for k-step
   // kk + 1 are issued before the MFMAs of k-step kk, so the MFMAs hide the
   // LDS latency (the first k-step of a stage waits for the barrier)
   half8_t af[2][TM], bf[2][TN];
+  uint32_t bw[2][TN];      // BQ: 8 codes of the lane's B row
+  half2_t bsc[TN][2];      // BQ: the stage's four block scales of that row
   auto read_frags = [&](int slot, int b, int kk) __attribute__((always_inline)) {
     const _Float16* as = As + b * BM * kWsLdsK + a_frag + kk;
-    const _Float16* bs = Bs + b * BN * kWsLdsK + b_frag + kk;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
       af[slot][i] = *reinterpret_cast<const half8_t*>(as + i * 32 * kWsLdsK);
+    if constexpr (BQ) {
+      const uint32_t* bq = Bq + (b * BN + b_row) * kBqLd + (kk >> 3) + b_half;
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-      bf[slot][j] = *reinterpret_cast<const half8_t*>(bs + j * 32 * kWsLdsK);
+      for (int j = 0; j < TN; ++j) bw[slot][j] = bq[j * 32 * kBqLd];
+    } else {
+      const _Float16* bs = Bs + b * BN * kWsLdsK + b_frag + kk;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bf[slot][j] = *reinterpret_cast<const half8_t*>(bs + j * 32 * kWsLdsK);
+    }
+  };
+  auto read_bscales = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const uint32_t v = Bqs[b * BN + b_row + 32 * j];
+      bsc[j][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false);
+      bsc[j][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, true);
+    }
   };
   __syncthreads();   // stage 0 in buffer 0
   read_frags(0, 0, 0);
+  if constexpr (BQ) read_bscales(0);
   for (int it = 0; it < nk; ++it) {
     const int b = it & 1;
 #pragma unroll
@@ -219,16 +298,31 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B,
       const int cur = s4 & 1;
       if (s4 < 3) read_frags(cur ^ 1, b, 16 * (s4 + 1));
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (BQ) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+        for (int j = 0; j < TN; ++j) {
+          const half2_t p = bsc[j][s4 >> 1];
+          const half2_t s2 = (s4 & 1) ? half2_t{p.y, p.y} : half2_t{p.x, p.x};
+          const half8_t bj = __builtin_bit_cast(half8_t, deq8(bw[cur][j], s2));
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
+          for (int i = 0; i < TM; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bj, af[cur][i], acc[i][j], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     if (it + 1 == nk) mfma_drain();   // fence in the block of the last MFMA
     __syncthreads();
-    if (it + 1 < nk) read_frags(0, b ^ 1, 0);
+    if (it + 1 < nk) {
+      read_frags(0, b ^ 1, 0);
+      if constexpr (BQ) read_bscales(b ^ 1);
+    }
   }
 
   const float alpha = A.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
@@ -237,17 +331,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B,
                    ((reinterpret_cast<uintptr_t>(c) & (OUT_BF16 ? 7 : 15)) == 0);
   const int64_t row_base = m0 + wm * 32 * TM + (lane & 31);
   const int cl_base = wn * 32 * TN + (lane >> 5) * 4;   // tile-local column of v = 0
+  // row blocks outermost: the eight partial writes that fill one 128-byte
+  // output line follow each other closely, so the line is whole in L2 before
+  // it can be evicted (written back in pieces, it costs HBM bandwidth twice)
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
+  for (int i = 0; i < TM; ++i) {
+    const int64_t row = row_base + i * 32;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int cl = cl_base + j * 32 + 8 * q;
-      const int64_t col = n0 + cl;
-      f32x4_t r1 = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (HAS_MEAN) r1 = *reinterpret_cast<const f32x4_t*>(rho_sh + cl);
+    for (int j = 0; j < TN; ++j) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int64_t row = row_base + i * 32;
+      for (int q = 0; q < 4; ++q) {
+        const int cl = cl_base + j * 32 + 8 * q;
+        const int64_t col = n0 + cl;
+        f32x4_t r1 = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (HAS_MEAN) r1 = *reinterpret_cast<const f32x4_t*>(rho_sh + cl);
         float y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) y[e] = __builtin_fmaf(acc[i][j][4 * q + e], alpha, r1[e]);
@@ -276,48 +373,65 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B,
 
 namespace {
 
-size_t ws_lds_bytes(int tm, int tn) {
+size_t ws_lds_bytes(int tm, int tn, bool bq) {
   const int bm = 64 * tm, bn = 64 * tn;
-  return (size_t)(2 * bm * kWsLdsK + 2 * bn * kWsLdsK) * 2 + (size_t)bn * 4;
+  const size_t a = (size_t)2 * bm * kWsLdsK * 2;
+  const size_t b = bq ? (size_t)2 * bn * (kBqLd + 1) * 4 : (size_t)2 * bn * kWsLdsK * 2;
+  return a + b + (size_t)bn * 4;
 }
 
 constexpr size_t kWsLdsLimit = 160 * 1024 - 512;
 
-template <int TM, int TN, bool OB, bool HM>
+template <int TM, int TN, bool OB, bool HM, bool BQ, bool SG>
 hipError_t launch_ws(const QOperand& a, const float* rho, const QOperand& b, int64_t m, int64_t n,
                      int64_t k, const int64_t* offs, int nseg, void* c, int64_t ldc,
                      hipStream_t st) {
-  constexpr int PF = 2, BM = 64 * TM, BN = 64 * TN;
-  const size_t lds = ws_lds_bytes(TM, TN);
+  constexpr int PF = SG ? 4 : 2, BM = 64 * TM, BN = 64 * TN;
+  const size_t lds = ws_lds_bytes(TM, TN, BQ);
   static bool attr_set = false;   // per instantiation; the attribute is idempotent
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_ws<TM, TN, PF, OB, HM>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_ws<TM, TN, PF, OB, HM, BQ, SG>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWsLdsLimit);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t tiles_m = chunk_upper_bound(m, offs ? nseg : 1, BM);
   dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)tiles_m);
-  k_gemm_ws<TM, TN, PF, OB, HM><<<grid, 512, lds, st>>>(a, b, rho, m, n, k, offs, nseg, c, ldc);
+  k_gemm_ws<TM, TN, PF, OB, HM, BQ, SG><<<grid, 512, lds, st>>>(a, b, rho, m, n, k, offs, nseg, c, ldc);
   return hipGetLastError();
 }
 
-template <int TM, int TN>
+template <int TM, int TN, bool BQ, bool SG>
+hipError_t launch_ws_sg(const QOperand& a, const float* rho, const QOperand& b, int64_t m,
+                        int64_t n, int64_t k, const int64_t* offs, int nseg, void* c, bool c_bf16,
+                        int64_t ldc, hipStream_t st) {
+  if (c_bf16)
+    return rho ? launch_ws<TM, TN, true, true, BQ, SG>(a, rho, b, m, n, k, offs, nseg, c, ldc, st)
+               : launch_ws<TM, TN, true, false, BQ, SG>(a, rho, b, m, n, k, offs, nseg, c, ldc, st);
+  return rho ? launch_ws<TM, TN, false, true, BQ, SG>(a, rho, b, m, n, k, offs, nseg, c, ldc, st)
+             : launch_ws<TM, TN, false, false, BQ, SG>(a, rho, b, m, n, k, offs, nseg, c, ldc, st);
+}
+
+// K % 256 == 0: scale bytes loaded a 256-wide group at a time
+template <int TM, int TN, bool BQ>
 hipError_t launch_ws_any(const QOperand& a, const float* rho, const QOperand& b, int64_t m,
                          int64_t n, int64_t k, const int64_t* offs, int nseg, void* c, bool c_bf16,
                          int64_t ldc, hipStream_t st) {
-  if (c_bf16)
-    return rho ? launch_ws<TM, TN, true, true>(a, rho, b, m, n, k, offs, nseg, c, ldc, st)
-               : launch_ws<TM, TN, true, false>(a, rho, b, m, n, k, offs, nseg, c, ldc, st);
-  return rho ? launch_ws<TM, TN, false, true>(a, rho, b, m, n, k, offs, nseg, c, ldc, st)
-             : launch_ws<TM, TN, false, false>(a, rho, b, m, n, k, offs, nseg, c, ldc, st);
+  static const bool sg_off = [] {
+    const char* e = std::getenv("AVERIS_GEMM_SG");
+    return e && std::atoi(e) == 0;
+  }();
+  if (k % 256 == 0 && !sg_off)
+    return launch_ws_sg<TM, TN, BQ, true>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+  return launch_ws_sg<TM, TN, BQ, false>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
 }
 
 }  // namespace
 
-// Variants (workgroup tile): 1: 256 x 192, 2: 256 x 128.  Chosen by rounds of
-// workgroups over the 256 CUs (one resident workgroup per CU) times the
-// tile's work.  Returns 0 when the kernel does not apply.
+// Variants (workgroup tile, B operand in LDS): 1: 256 x 192 fp16,
+// 2: 256 x 128 fp16, 3: 256 x 192 codes, 4: 256 x 128 codes.  The tile is
+// chosen by rounds of workgroups over the 256 CUs (one resident workgroup
+// per CU) times the tile's work.  Returns 0 when the kernel does not apply.
 int ws_pick(int64_t m, int64_t n, int64_t k, int nseg_eff) {
   if (k % kWsBK != 0) return 0;
   struct Cand { int id, tm, tn; double eff; };
@@ -325,7 +439,7 @@ int ws_pick(int64_t m, int64_t n, int64_t k, int nseg_eff) {
   int best = 0;
   double best_cost = 0;
   for (const Cand& cd : cands) {
-    if (ws_lds_bytes(cd.tm, cd.tn) > kWsLdsLimit) continue;
+    if (ws_lds_bytes(cd.tm, cd.tn, false) > kWsLdsLimit) continue;
     const int64_t bm = 64 * cd.tm, bn = 64 * cd.tn;
     const int64_t tiles = chunk_upper_bound(m, nseg_eff, bm) * ((n + bn - 1) / bn);
     const double rounds = (double)((tiles + 255) / 256);
@@ -342,8 +456,10 @@ hipError_t launch_gemm_ws(int variant, const QOperand& a, const float* rho, cons
                           int64_t m, int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
                           bool c_bf16, int64_t ldc, hipStream_t st) {
   switch (variant) {
-    case 1: return launch_ws_any<4, 3>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
-    case 2: return launch_ws_any<4, 2>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+    case 1: return launch_ws_any<4, 3, false>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+    case 2: return launch_ws_any<4, 2, false>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+    case 3: return launch_ws_any<4, 3, true>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+    case 4: return launch_ws_any<4, 2, true>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
     default: return hipErrorInvalidValue;
   }
 }
