@@ -628,7 +628,7 @@ hipError_t launch_gemm(const QOperand& a, const QOperand* mean, const QOperand& 
     return e ? std::atoi(e) : 0;
   }();
   if (kernel_sel == 0) {
-    int v = ws_pick(m, n, k, offs ? nseg : 1);
+    int v = ws_pick(m, n, k, offs ? nseg : 1, mean != nullptr);
     static const int forced_ws = [] {
       const char* e = std::getenv("AVERIS_GEMM_WS_TILE");
       return e ? std::atoi(e) : 0;
@@ -637,17 +637,10 @@ hipError_t launch_gemm(const QOperand& a, const QOperand* mean, const QOperand& 
       const char* e = std::getenv("AVERIS_GEMM_BQ");
       return e ? std::atoi(e) : 0;
     }();
-    if (v != 0 && bq == 1) v += 2;   // the same tile with B kept as codes in LDS
-    if (v != 0 && forced_ws >= 1 && forced_ws <= 4) v = forced_ws;
-    if (v != 0) {
-      if (mean) {
-        dim3 g((unsigned)((n + kRank1Cols - 1) / kRank1Cols), (unsigned)(offs ? nseg : 1));
-        k_rank1<<<g, 256, 0, st>>>(*mean, b, n, k, offs != nullptr, rho_ws);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-      }
-      return launch_gemm_ws(v, a, mean ? rho_ws : nullptr, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
-    }
+    // B kept as codes in LDS (variants 3, 4) has no rank-one path
+    if (v != 0 && bq == 1 && !mean) v += 2;
+    if (v != 0 && forced_ws >= 1 && forced_ws <= 4 && !(mean && forced_ws > 2)) v = forced_ws;
+    if (v != 0) return launch_gemm_ws(v, a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
   }
   int choice = pick_tile(m, n, k, offs ? nseg : 1, mean != nullptr);
   // tuning override: AVERIS_GEMM_TILE = 1..6 (see pick_tile)

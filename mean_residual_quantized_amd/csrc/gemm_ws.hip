@@ -20,12 +20,15 @@
 // dequantization of stage s + 1 runs on the same SIMDs during the MFMAs of
 // stage s.
 //
-// The rank-one term rho (one value per output column) comes from a small
-// GEMV launched just before (every row tile of a column would otherwise
-// recompute it); the producers stage the tile's values in LDS during the
-// prologue and the consumers add them in the epilogue.  The MFMA takes the B fragment
-// first, so a lane's accumulators hold four consecutive output columns of one
-// output row: 8-byte (bf16) or 16-byte (fp32) stores.
+// The rank-one term rho (one value per output column) is summed by the
+// producers while they dequantize B: each B chunk is dotted (v_dot2_f32_f16)
+// with the matching 32 values of the mean row, which the producers dequantize
+// into LDS once per tile; the two k-halves of a row are added across
+// neighbouring lanes and the result is staged in LDS for the epilogue.  Every
+// row tile of a column sums in the same order, so all of them add the same
+// rho.  The MFMA takes the B fragment first, so a lane's accumulators hold
+// four consecutive output columns of one output row: 8-byte (bf16) or
+// 16-byte (fp32) stores.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -59,8 +62,7 @@ __device__ __forceinline__ void ws_unroll(F&& f) {
 }  // namespace
 
 template <int TM, int TN, int PF, bool OUT_BF16, bool HAS_MEAN, bool BQ, bool SG>
-__global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B,
-                                                    const float* __restrict__ rho, int64_t m,
+__global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOperand M, int64_t m,
                                                     int64_t n, int64_t k, const int64_t* offs,
                                                     int nseg, void* c, int64_t ldc) {
   constexpr int BM = 64 * TM, BN = 64 * TN;
@@ -70,6 +72,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B,
   constexpr int IA = 2 * BM / kProducers;                // chunk rounds that hold A rows
   static_assert((2 * BM) % kProducers == 0 && (2 * BN) % 64 == 0, "whole-wave chunk rounds");
   static_assert(!BQ || BN <= kProducers, "one B row per producer thread");
+  static_assert(!(BQ && HAS_MEAN), "the rank-one term is summed from dequantized B chunks");
+  constexpr int CPB = CP - IA;   // chunk rounds that hold B rows
   extern __shared__ __attribute__((aligned(16))) _Float16 smem_ws[];
   _Float16* As = smem_ws;                                // [2][BM][LDSK]
   // B as fp16 ([2][BN][LDSK]) or, with BQ, as codes ([2][BN][kBqLd] dwords)
@@ -79,6 +83,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B,
   uint32_t* Bqs = Bq + 2 * BN * kBqLd;
   float* rho_sh = BQ ? reinterpret_cast<float*>(Bqs + 2 * BN)
                      : reinterpret_cast<float*>(Bs + 2 * BN * kWsLdsK);   // [BN]
+  // HAS_MEAN: the segment's mean row, dequantized to fp16 once ([k])
+  _Float16* mean_sh = reinterpret_cast<_Float16*>(rho_sh + BN);
 
   int64_t tile_x, tile_y;
   xcd_tile(tile_x, tile_y);
@@ -162,7 +168,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B,
         rbs[slot] = *reinterpret_cast<const uint32_t*>(b_s + 4 * st + obs);
       }
     };
-    auto dequant = [&](int slot, int buf, auto sw_c) __attribute__((always_inline)) {
+    // HAS_MEAN: rank-one partial sums of the chunk rows that hold B, in
+    // stage order (so every row tile of a column adds the same bits)
+    float racc[CPB > 0 ? CPB : 1];
+#pragma unroll
+    for (int i = 0; i < (CPB > 0 ? CPB : 1); ++i) racc[i] = 0.0f;
+    auto dequant = [&](int slot, int buf, int st, auto sw_c) __attribute__((always_inline)) {
       constexpr int sw = decltype(sw_c)::value;
 #pragma unroll
       for (int i = 0; i < CP; ++i) {
@@ -187,6 +198,24 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B,
         uint4* dst = reinterpret_cast<uint4*>(base + lrow[i] * kWsLdsK + 32 * hf);
 #pragma unroll
         for (int e = 0; e < 4; ++e) dst[e] = d[e];
+        if constexpr (HAS_MEAN) {
+          if (i >= IA) {
+            // the products of two exact fp16 values (<= 5 significant bits
+            // each) are exact; fp32 accumulation
+            // four independent chains (one per 8 elements), then their sum
+            const uint4* mv = reinterpret_cast<const uint4*>(mean_sh + st * kWsBK + 32 * hf);
+            float r[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint4 mm = mv[e];
+              r[e] = __builtin_amdgcn_fdot2(h2(d[e].x), h2(mm.x), 0.0f, false);
+              r[e] = __builtin_amdgcn_fdot2(h2(d[e].y), h2(mm.y), r[e], false);
+              r[e] = __builtin_amdgcn_fdot2(h2(d[e].z), h2(mm.z), r[e], false);
+              r[e] = __builtin_amdgcn_fdot2(h2(d[e].w), h2(mm.w), r[e], false);
+            }
+            racc[i - IA] += (r[0] + r[1]) + (r[2] + r[3]);
+          }
+        }
       }
       if (bcopy) {
         uint32_t* dst = Bq + (buf * BN + pt) * kBqLd;
@@ -203,16 +232,45 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B,
     // after stage 4g - 5 (the last user of that slot) was dequantized.
     static_assert(!SG || PF == 4, "scale groups assume a 4-stage ring");
     constexpr int UNR = SG ? 8 : PF;   // stages per loop iteration
+    // the mean row (HAS_MEAN) is loaded first: the in-order load counter
+    // then lets its dequantization start before the stages' loads land
+    constexpr int kMeanPer = 4;   // 32-element chunks of the mean row per thread, at most
+    uint4 mw[kMeanPer];
+    uint32_t msc[kMeanPer];
+    const int nmc = HAS_MEAN ? (int)(k >> 5) : 0;
+    if constexpr (HAS_MEAN) {
+      const uint8_t* mc = M.codes + (int64_t)seg * kh;
+      const uint8_t* ms = M.scales + (int64_t)seg * kb;
+#pragma unroll
+      for (int u = 0; u < kMeanPer; ++u) {
+        const int cidx = pt + kProducers * u;
+        if (cidx < nmc) {
+          mw[u] = *reinterpret_cast<const uint4*>(mc + 16 * cidx);
+          msc[u] = *reinterpret_cast<const uint16_t*>(ms + 2 * cidx);
+        }
+      }
+    }
     ws_unroll<0, PF>([&](auto p_c) __attribute__((always_inline)) {
       constexpr int p = decltype(p_c)::value;
       if (p < nk) gload(p, p, WsIC<p>{});
     });
-    if (HAS_MEAN) {
-      // this tile's rank-one terms, for the consumers' epilogue
-      for (int cidx = pt; cidx < BN; cidx += kProducers)
-        rho_sh[cidx] = n0 + cidx < n ? rho[(int64_t)seg * n + n0 + cidx] : 0.0f;
+    if constexpr (HAS_MEAN) {
+#pragma unroll
+      for (int u = 0; u < kMeanPer; ++u) {
+        const int cidx = pt + kProducers * u;
+        if (cidx < nmc) {
+          const half2_t sc = scales2(msc[u]);
+          const half2_t s0 = {sc.x, sc.x}, s1 = {sc.y, sc.y};
+          uint4* dst = reinterpret_cast<uint4*>(mean_sh + 32 * cidx);
+          dst[0] = deq8(mw[u].x, s0);
+          dst[1] = deq8(mw[u].y, s0);
+          dst[2] = deq8(mw[u].z, s1);
+          dst[3] = deq8(mw[u].w, s1);
+        }
+      }
+      __syncthreads();   // mean row published (the consumers wait here too)
     }
-    dequant(0, 0, WsIC<0>{});
+    dequant(0, 0, 0, WsIC<0>{});
     if (PF < nk) gload(0, PF, WsIC<PF % 8>{});
     __syncthreads();
     // iteration it: dequantize stage it + 1 (slot (it + 1) % PF) into buffer
@@ -224,7 +282,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B,
         constexpr int su = (u + 1) % PF;
         const int i2 = it + u;
         if (i2 + 1 < nk) {
-          dequant(su, (i2 + 1) & 1, WsIC<(u + 1) % 8>{});
+          dequant(su, (i2 + 1) & 1, i2 + 1, WsIC<(u + 1) % 8>{});
           if (i2 + 1 + PF < nk) gload(su, i2 + 1 + PF, WsIC<(u + 1 + PF) % 8>{});
         }
         __syncthreads();
@@ -236,12 +294,23 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B,
       const int i2 = it + u;
       if (i2 < nk) {
         if (i2 + 1 < nk) {
-          dequant(su, (i2 + 1) & 1, WsIC<(u + 1) % 8>{});
+          dequant(su, (i2 + 1) & 1, i2 + 1, WsIC<(u + 1) % 8>{});
           if (i2 + 1 + PF < nk) gload(su, i2 + 1 + PF, WsIC<(u + 1 + PF) % 8>{});
         }
         __syncthreads();
       }
     });
+    if constexpr (HAS_MEAN) {
+      // the two k-halves of a row sit in neighbouring lanes
+      const float rs_scale = M.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
+#pragma unroll
+      for (int i = IA; i < CP; ++i) {
+        if (pt + kProducers * i >= NCH) break;   // whole waves
+        const float v = racc[i - IA] + __shfl_xor(racc[i - IA], 1, 64);
+        if ((pt & 1) == 0) rho_sh[lrow[i]] = v * rs_scale;
+      }
+      __syncthreads();   // rank-one terms published for the epilogue
+    }
     return;
   }
 
@@ -288,6 +357,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B,
       bsc[j][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, true);
     }
   };
+  if constexpr (HAS_MEAN) __syncthreads();   // the producers' mean row
   __syncthreads();   // stage 0 in buffer 0
   read_frags(0, 0, 0);
   if constexpr (BQ) read_bscales(0);
@@ -325,6 +395,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B,
     }
   }
 
+  if constexpr (HAS_MEAN) __syncthreads();   // the producers' rank-one terms
   const float alpha = A.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
   const bool full = (m0 + BM <= m_end) && (n0 + BN <= n);
   const bool vec = full && (ldc % 4 == 0) &&
@@ -383,11 +454,11 @@ size_t ws_lds_bytes(int tm, int tn, bool bq) {
 constexpr size_t kWsLdsLimit = 160 * 1024 - 512;
 
 template <int TM, int TN, bool OB, bool HM, bool BQ, bool SG>
-hipError_t launch_ws(const QOperand& a, const float* rho, const QOperand& b, int64_t m, int64_t n,
+hipError_t launch_ws(const QOperand& a, const QOperand* mean, const QOperand& b, int64_t m, int64_t n,
                      int64_t k, const int64_t* offs, int nseg, void* c, int64_t ldc,
                      hipStream_t st) {
   constexpr int PF = SG ? 4 : 2, BM = 64 * TM, BN = 64 * TN;
-  const size_t lds = ws_lds_bytes(TM, TN, BQ);
+  const size_t lds = ws_lds_bytes(TM, TN, BQ) + (HM ? (size_t)k * 2 : 0);
   static bool attr_set = false;   // per instantiation; the attribute is idempotent
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_ws<TM, TN, PF, OB, HM, BQ, SG>),
@@ -397,24 +468,31 @@ hipError_t launch_ws(const QOperand& a, const float* rho, const QOperand& b, int
   }
   const int64_t tiles_m = chunk_upper_bound(m, offs ? nseg : 1, BM);
   dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)tiles_m);
-  k_gemm_ws<TM, TN, PF, OB, HM, BQ, SG><<<grid, 512, lds, st>>>(a, b, rho, m, n, k, offs, nseg, c, ldc);
+  const QOperand mu = mean ? *mean : QOperand{nullptr, nullptr, nullptr};
+  k_gemm_ws<TM, TN, PF, OB, HM, BQ, SG><<<grid, 512, lds, st>>>(a, b, mu, m, n, k, offs, nseg, c, ldc);
   return hipGetLastError();
 }
 
 template <int TM, int TN, bool BQ, bool SG>
-hipError_t launch_ws_sg(const QOperand& a, const float* rho, const QOperand& b, int64_t m,
+hipError_t launch_ws_sg(const QOperand& a, const QOperand* mean, const QOperand& b, int64_t m,
                         int64_t n, int64_t k, const int64_t* offs, int nseg, void* c, bool c_bf16,
                         int64_t ldc, hipStream_t st) {
-  if (c_bf16)
-    return rho ? launch_ws<TM, TN, true, true, BQ, SG>(a, rho, b, m, n, k, offs, nseg, c, ldc, st)
-               : launch_ws<TM, TN, true, false, BQ, SG>(a, rho, b, m, n, k, offs, nseg, c, ldc, st);
-  return rho ? launch_ws<TM, TN, false, true, BQ, SG>(a, rho, b, m, n, k, offs, nseg, c, ldc, st)
-             : launch_ws<TM, TN, false, false, BQ, SG>(a, rho, b, m, n, k, offs, nseg, c, ldc, st);
+  if constexpr (BQ) {
+    if (mean) return hipErrorInvalidValue;   // B-as-codes tiles have no rank-one path
+    if (c_bf16) return launch_ws<TM, TN, true, false, BQ, SG>(a, mean, b, m, n, k, offs, nseg, c, ldc, st);
+    return launch_ws<TM, TN, false, false, BQ, SG>(a, mean, b, m, n, k, offs, nseg, c, ldc, st);
+  } else {
+    if (c_bf16)
+      return mean ? launch_ws<TM, TN, true, true, BQ, SG>(a, mean, b, m, n, k, offs, nseg, c, ldc, st)
+                  : launch_ws<TM, TN, true, false, BQ, SG>(a, mean, b, m, n, k, offs, nseg, c, ldc, st);
+    return mean ? launch_ws<TM, TN, false, true, BQ, SG>(a, mean, b, m, n, k, offs, nseg, c, ldc, st)
+                : launch_ws<TM, TN, false, false, BQ, SG>(a, mean, b, m, n, k, offs, nseg, c, ldc, st);
+  }
 }
 
 // K % 256 == 0: scale bytes loaded a 256-wide group at a time
 template <int TM, int TN, bool BQ>
-hipError_t launch_ws_any(const QOperand& a, const float* rho, const QOperand& b, int64_t m,
+hipError_t launch_ws_any(const QOperand& a, const QOperand* mean, const QOperand& b, int64_t m,
                          int64_t n, int64_t k, const int64_t* offs, int nseg, void* c, bool c_bf16,
                          int64_t ldc, hipStream_t st) {
   static const bool sg_off = [] {
@@ -422,8 +500,8 @@ hipError_t launch_ws_any(const QOperand& a, const float* rho, const QOperand& b,
     return e && std::atoi(e) == 0;
   }();
   if (k % 256 == 0 && !sg_off)
-    return launch_ws_sg<TM, TN, BQ, true>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
-  return launch_ws_sg<TM, TN, BQ, false>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+    return launch_ws_sg<TM, TN, BQ, true>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+  return launch_ws_sg<TM, TN, BQ, false>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
 }
 
 }  // namespace
@@ -432,14 +510,16 @@ hipError_t launch_ws_any(const QOperand& a, const float* rho, const QOperand& b,
 // 2: 256 x 128 fp16, 3: 256 x 192 codes, 4: 256 x 128 codes.  The tile is
 // chosen by rounds of workgroups over the 256 CUs (one resident workgroup
 // per CU) times the tile's work.  Returns 0 when the kernel does not apply.
-int ws_pick(int64_t m, int64_t n, int64_t k, int nseg_eff) {
+int ws_pick(int64_t m, int64_t n, int64_t k, int nseg_eff, bool has_mean) {
   if (k % kWsBK != 0) return 0;
   struct Cand { int id, tm, tn; double eff; };
   const Cand cands[2] = {{1, 4, 3, 1.0}, {2, 4, 2, 0.95}};
   int best = 0;
   double best_cost = 0;
   for (const Cand& cd : cands) {
-    if (ws_lds_bytes(cd.tm, cd.tn, false) > kWsLdsLimit) continue;
+    // with a mean, its dequantized row (k fp16 values, k <= 32768) shares the LDS
+    if (has_mean && k > 4 * kProducers * 32) continue;
+    if (ws_lds_bytes(cd.tm, cd.tn, false) + (has_mean ? (size_t)k * 2 : 0) > kWsLdsLimit) continue;
     const int64_t bm = 64 * cd.tm, bn = 64 * cd.tn;
     const int64_t tiles = chunk_upper_bound(m, nseg_eff, bm) * ((n + bn - 1) / bn);
     const double rounds = (double)((tiles + 255) / 256);
@@ -452,14 +532,14 @@ int ws_pick(int64_t m, int64_t n, int64_t k, int nseg_eff) {
   return best;
 }
 
-hipError_t launch_gemm_ws(int variant, const QOperand& a, const float* rho, const QOperand& b,
+hipError_t launch_gemm_ws(int variant, const QOperand& a, const QOperand* mean, const QOperand& b,
                           int64_t m, int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
                           bool c_bf16, int64_t ldc, hipStream_t st) {
   switch (variant) {
-    case 1: return launch_ws_any<4, 3, false>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
-    case 2: return launch_ws_any<4, 2, false>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
-    case 3: return launch_ws_any<4, 3, true>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
-    case 4: return launch_ws_any<4, 2, true>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+    case 1: return launch_ws_any<4, 3, false>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+    case 2: return launch_ws_any<4, 2, false>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+    case 3: return launch_ws_any<4, 3, true>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+    case 4: return launch_ws_any<4, 2, true>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
     default: return hipErrorInvalidValue;
   }
 }

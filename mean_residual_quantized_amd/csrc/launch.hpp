@@ -70,11 +70,11 @@ hipError_t launch_gemm(const QOperand& a, const QOperand* mean, const QOperand& 
 size_t gemm_ws_bytes(int64_t n, int64_t k, int nseg);
 
 // Warp-specialized GEMM (K % 64 == 0): variant for a shape (0 = not
-// applicable) and its launch.
-// rho: the rank-one term per segment and column (nseg x n floats), or
-// nullptr for the vanilla product.
-int ws_pick(int64_t m, int64_t n, int64_t k, int nseg_eff);
-hipError_t launch_gemm_ws(int variant, const QOperand& a, const float* rho, const QOperand& b,
+// applicable) and its launch.  mean: the quantized mean rows (nseg x k),
+// whose rank-one term the kernel adds itself, or nullptr for the vanilla
+// product.
+int ws_pick(int64_t m, int64_t n, int64_t k, int nseg_eff, bool has_mean);
+hipError_t launch_gemm_ws(int variant, const QOperand& a, const QOperand* mean, const QOperand& b,
                           int64_t m, int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
                           bool c_bf16, int64_t ldc, hipStream_t st);
 
