@@ -264,7 +264,7 @@ GEMM_SOURCES = ["gemm.hip", "gemm_ws.hip", "gemm_common.hpp"]
 
 
 def gemm_source_sha():
-    """One hash over the sources of the forward GEMM call's two kernels."""
+    """One hash over the sources of the forward GEMM kernel."""
     import hashlib
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
@@ -273,8 +273,8 @@ def gemm_source_sha():
 
 
 def load_traffic():
-    """HBM bytes per forward GEMM call (k_rank1 + k_gemm_ws) from the committed
-    counter summary, if it was taken on the current kernel sources (else None)."""
+    """HBM bytes per forward GEMM launch (k_gemm_ws) from the committed counter
+    summary, if it was taken on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
     try:
         rec = json.load(open(path))
@@ -354,11 +354,11 @@ def main():
     overhead = dict(fwd_pct=100 * (t_fwd_a / t_fwd_v - 1), dgrad_pct=100 * (t_bwd_a / t_bwd_v - 1),
                     step_pct=100 * (ms_a / ms_v - 1))
 
-    # roofline of the dominant kernel: the Averis forward GEMM call, timed by
-    # the events around it on the launch stream.  The call is two launches:
-    # k_rank1 (the mean row times W, a GEMV of 2mn flops, ~4 us) and k_gemm_ws
-    # (the NT GEMM over the residual codes, with the rank-one row added in its
-    # epilogue).  The flops counted are the GEMM's 2lmn.
+    # roofline of the dominant kernel: the Averis forward GEMM, one launch of
+    # k_gemm_ws (the NT GEMM over the residual codes; its producer waves also
+    # sum the rank-one row, which the epilogue adds), timed by the events
+    # around the call on the launch stream.  The flops counted are the
+    # GEMM's 2lmn.
     g_ms = comp["gemm_fwd"]
     achieved = gemm_flops / (g_ms * 1e-3) / 1e12
     tr = load_traffic()
@@ -367,9 +367,9 @@ def main():
         traffic = tr["gemm_fwd"]["fetch_bytes"] + tr["gemm_fwd"]["write_bytes"]
     roofline = dict(bound="mfma", achieved=achieved, peak=F16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=achieved / F16_MFMA_PEAK_TFLOPS, traffic=traffic,
-                    kernel="averis_gemm_fwd = k_rank1 (mean-row GEMV) + k_gemm_ws (warp-specialized "
-                           "NVFP4 NT GEMM, exact fp16 dequant -> v_mfma_f32_32x32x16_f16, rank-one "
-                           "row added in the epilogue), M=%d N=%d K=%d, bf16 out" % (l, n, m),
+                    kernel="k_gemm_ws (averis_gemm_fwd: warp-specialized NVFP4 NT GEMM, exact fp16 "
+                           "dequant -> v_mfma_f32_32x32x16_f16, rank-one row summed by the producer "
+                           "waves and added in the epilogue), M=%d N=%d K=%d, bf16 out" % (l, n, m),
                     frac_of_fp4_peak=achieved / FP4_MFMA_PEAK_TFLOPS)
 
     out = {
