@@ -102,6 +102,43 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
   const bool producer = wave >= 4;
   const int nk = (int)(k / kWsBK);
 
+  // bf16 output of a full tile goes out through LDS: the consumers write the
+  // finished tile into the (then free) stage buffers and all eight waves
+  // store it in 16-byte pieces, eight lanes to a 128-byte output line (a
+  // direct store writes 16 bytes into each of 32 lines, and the L2's write
+  // request rate, not its bandwidth, bounds the epilogue)
+  constexpr int kStLd = 2 * BN + 16;   // staged row, bytes (16-byte aligned, staggered banks)
+  constexpr size_t kStageRoom = (size_t)2 * BM * kWsLdsK * 2 +
+                                (BQ ? (size_t)2 * BN * (kBqLd + 1) * 4 : (size_t)2 * BN * kWsLdsK * 2);
+  constexpr bool kCanStage = OUT_BF16 && (size_t)BM * kStLd <= kStageRoom;
+  constexpr bool stage_out = kCanStage;   // every tile of a bf16 output
+  // pieces that lie wholly inside the output, with 16-byte aligned rows, go
+  // out as one store; the others (edge tiles, odd strides) element by element
+  const bool st_vec = (ldc % 8 == 0) && ((reinterpret_cast<uintptr_t>(c) & 15) == 0);
+  const int rows_here = (int)(m_end - m0 < BM ? m_end - m0 : BM);
+  const int cols_here = (int)(n - n0 < BN ? n - n0 : BN);
+  unsigned char* stg = reinterpret_cast<unsigned char*>(smem_ws);
+  auto store_staged = [&]() __attribute__((always_inline)) {
+    constexpr int CPR = 2 * BN / 16;   // 16-byte pieces per tile row
+    uint16_t* cb = static_cast<uint16_t*>(c) + m0 * ldc + n0;
+#pragma unroll
+    for (int it = 0; it < BM * CPR / 512; ++it) {
+      const int cidx = t + 512 * it;
+      const int r = cidx / CPR, cc = cidx - r * CPR;
+      if (r >= rows_here) continue;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + r * kStLd + cc * 16);
+      uint16_t* dst = cb + (int64_t)r * ldc + cc * 8;
+      if (st_vec && cc * 8 + 8 <= cols_here) {
+        store_out(v, reinterpret_cast<u32x4_t*>(dst));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (cc * 8 + e < cols_here) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  };
+  static_assert((BM * (2 * BN / 16)) % 512 == 0, "whole store rounds");
+
   if (producer) {
     // ------------------------------------------------------------------ producers
     const int pt = t - 512 + kProducers;
@@ -311,6 +348,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
       }
       __syncthreads();   // rank-one terms published for the epilogue
     }
+    if constexpr (stage_out) {
+      __syncthreads();   // the consumers have staged the tile
+      store_staged();
+    }
     return;
   }
 
@@ -397,6 +438,29 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
 
   if constexpr (HAS_MEAN) __syncthreads();   // the producers' rank-one terms
   const float alpha = A.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
+  if constexpr (stage_out) {
+    const int srow = wm * 32 * TM + (lane & 31);
+    const int scol = wn * 32 * TN + (lane >> 5) * 4;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int cl = scol + j * 32 + 8 * q;
+          f32x4_t r1 = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (HAS_MEAN) r1 = *reinterpret_cast<const f32x4_t*>(rho_sh + cl);
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = __builtin_fmaf(acc[i][j][4 * q + e], alpha, r1[e]);
+          const u32x2_t pk = {bf16x2_rne(y[0], y[1]), bf16x2_rne(y[2], y[3])};
+          *reinterpret_cast<u32x2_t*>(stg + (srow + 32 * i) * kStLd + 2 * cl) = pk;
+        }
+      }
+    }
+    __syncthreads();   // tile staged (the producers store too)
+    store_staged();
+  } else {
   const bool full = (m0 + BM <= m_end) && (n0 + BN <= n);
   const bool vec = full && (ldc % 4 == 0) &&
                    ((reinterpret_cast<uintptr_t>(c) & (OUT_BF16 ? 7 : 15)) == 0);
@@ -439,6 +503,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
         }
       }
     }
+  }
   }
 }
 

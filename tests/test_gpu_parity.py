@@ -157,6 +157,30 @@ def test_bf16_output_within_rounding():
     torch.testing.assert_close(y16, y32.to(torch.bfloat16), rtol=0, atol=0)
 
 
+@pytest.mark.parametrize("l,m,n", [(1000, 320, 192), (520, 1024, 208), (8192, 1024, 3072)])
+def test_bf16_output_edges_and_strides(l, m, n):
+    # bf16 output leaves through an LDS-staged tile: full 16-byte pieces go out
+    # as one store, pieces past the tile's edge or in rows that are not
+    # 16-byte aligned element by element; both must equal fp32 -> bf16 (RNE)
+    cfg = workloads.config1(l=l, m=m, n=n)
+    xg, dg = cfg["x"].cuda(), cfg["d"].cuda()
+    wt_g, wd_g = quant_weights(cfg["w"].cuda())
+    for a_g, b_g, fn, cols in [(xg, wt_g, av.averis_gemm_fwd, n), (dg, wd_g, av.averis_gemm_dgrad, m)]:
+        res, mean, _ = av.averis_split_quant(a_g, seed=4)
+        y32 = fn(res, mean, b_g, out_dtype=torch.float32)
+        ref = y32.to(torch.bfloat16)
+        y16 = fn(res, mean, b_g, out_dtype=torch.bfloat16)
+        assert torch.equal(y16, ref)
+        # row stride cols + 3 (odd) and a base 2 bytes past 16-byte alignment
+        big = torch.zeros((l, cols + 8), dtype=torch.bfloat16, device="cuda")
+        view = big.view(-1)[1:1 + l * (cols + 3)].view(l, cols + 3)[:, :cols]
+        fn(res, mean, b_g, out_dtype=torch.bfloat16, out=view)
+        assert torch.equal(view, ref)
+        v16 = av.averis_gemm_vanilla(res, b_g, out_dtype=torch.bfloat16)
+        assert torch.equal(v16, av.averis_gemm_vanilla(res, b_g, out_dtype=torch.float32).to(torch.bfloat16))
+    torch.cuda.synchronize()
+
+
 def test_deterministic_repeats():
     cfg = workloads.config1(l=512, m=256, n=128)
     xg = cfg["x"].cuda()
