@@ -151,6 +151,35 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
     const uint8_t* a_s = A.scales + m0 * kb;
     const uint8_t* b_c = bcodes + n0 * kh;
     const uint8_t* b_s = bscales + n0 * kb;
+    // W2 (with SG): one load instruction covers 64 contiguous code bytes of a
+    // row -- two stages, four lanes to a row -- where the per-stage mapping
+    // covers 32 (two lanes to a row); a second load takes the wave's other 16
+    // rows with the two stages swapped, so each lane still holds one chunk
+    // per stage, of row lo or row hi, picked per lane when it is dequantized.
+    // The loads touch half as many cache lines per byte.  Used with three
+    // column fragments per consumer wave (48 MFMAs per stage); with two, the
+    // stage is too short for the producers' extra selects (measured slower).
+    constexpr bool W2 = SG && !BQ && TN == 3;
+    const int w2_p = pt & 3;                      // 16-byte piece of the 64-byte window
+    const bool w2_sel = (w2_p >> 1) != 0;         // row lo holds the window's second stage
+    uint32_t oc_lo[CP], oc_hi[CP], os_lo[CP], os_hi[CP];
+    int lrow_lo[CP], lrow_hi[CP];
+    if constexpr (W2) {
+#pragma unroll
+      for (int i = 0; i < CP; ++i) {
+        const bool is_a = i < IA;
+        const int base = (is_a ? 128 * i : 128 * (i - IA)) + 32 * ((pt >> 6) & 3);
+        const int64_t lim = is_a ? (m_end - m0) : (n - n0);
+        const int rl = base + ((pt & 63) >> 2), rh = rl + 16;
+        const int64_t rowl = rl < lim ? rl : lim - 1, rowh = rh < lim ? rh : lim - 1;
+        lrow_lo[i] = rl;
+        lrow_hi[i] = rh;
+        oc_lo[i] = (uint32_t)(rowl * kh) + 16u * (uint32_t)w2_p;
+        oc_hi[i] = (uint32_t)(rowh * kh) + 16u * (uint32_t)((w2_p + 2) & 3);
+        os_lo[i] = (uint32_t)(rowl * kb);
+        os_hi[i] = (uint32_t)(rowh * kb);
+      }
+    }
     uint32_t oc[CP], os[CP];
     int lrow[CP];
 #pragma unroll
@@ -171,6 +200,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
     uint4 rc[PF][CP];
     uint32_t rs[PF][CP];
     uint4 rsg[2][CP];
+    uint4 rsg_hi[2][CP];   // W2: the scale groups of row hi
     // BQ: B row pt is copied as loaded (32 code bytes and 4 scale bytes per stage)
     const bool bcopy = BQ && pt < BN;
     const int64_t blim = n - n0;
@@ -183,6 +213,22 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
     // (the loop below advances 8 stages per iteration when SG)
     auto gload = [&](int slot, int st, auto sw_c) __attribute__((always_inline)) {
       constexpr int sw = decltype(sw_c)::value;
+      if constexpr (W2) {
+        // st even: stages st and st + 1 into ring slots slot and slot + 1
+#pragma unroll
+        for (int i = 0; i < CP; ++i) {
+          if (pt + kProducers * i >= NCH) break;   // whole waves
+          const uint8_t* cb = (i < IA ? a_c : b_c) + 32 * st;
+          rc[slot][i] = *reinterpret_cast<const uint4*>(cb + oc_lo[i]);
+          rc[slot + 1][i] = *reinterpret_cast<const uint4*>(cb + oc_hi[i]);
+          if constexpr ((sw & 3) == 0) {
+            const uint8_t* sb = (i < IA ? a_s : b_s) + 4 * st;
+            rsg[(sw >> 2) & 1][i] = *reinterpret_cast<const uint4*>(sb + os_lo[i]);
+            rsg_hi[(sw >> 2) & 1][i] = *reinterpret_cast<const uint4*>(sb + os_hi[i]);
+          }
+        }
+        return;
+      }
 #pragma unroll
       for (int i = 0; i < CP; ++i) {
         if (pt + kProducers * i >= NCH) break;   // whole waves
@@ -208,8 +254,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
     // HAS_MEAN: rank-one partial sums of the chunk rows that hold B, in
     // stage order (so every row tile of a column adds the same bits)
     float racc[CPB > 0 ? CPB : 1];
+    float racc_hi[CPB > 0 ? CPB : 1];   // W2: a lane's chunks alternate between rows lo and hi
 #pragma unroll
-    for (int i = 0; i < (CPB > 0 ? CPB : 1); ++i) racc[i] = 0.0f;
+    for (int i = 0; i < (CPB > 0 ? CPB : 1); ++i) racc[i] = racc_hi[i] = 0.0f;
     auto dequant = [&](int slot, int buf, int st, auto sw_c) __attribute__((always_inline)) {
       constexpr int sw = decltype(sw_c)::value;
 #pragma unroll
@@ -217,22 +264,39 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
         const int q = pt + kProducers * i, hf = q & 1;
         if (q >= NCH) break;
         uint32_t sbytes;
-        if constexpr (SG) {
-          const uint4 g = rsg[(sw >> 2) & 1][i];
-          const uint32_t wd = (sw & 3) == 0 ? g.x : (sw & 3) == 1 ? g.y : (sw & 3) == 2 ? g.z : g.w;
-          sbytes = wd >> ssh;
+        uint4 cw;
+        int drow;
+        if constexpr (W2) {
+          // the window's chunks sit in ring slots se (from row lo) and se + 1
+          // (row hi); x picks the one that holds this stage for this lane
+          constexpr int se = sw & 2;
+          const bool x = w2_sel != ((sw & 1) != 0);
+          const uint4 glo = rsg[(sw >> 2) & 1][i], ghi = rsg_hi[(sw >> 2) & 1][i];
+          const uint32_t wlo = (sw & 3) == 0 ? glo.x : (sw & 3) == 1 ? glo.y : (sw & 3) == 2 ? glo.z : glo.w;
+          const uint32_t whi = (sw & 3) == 0 ? ghi.x : (sw & 3) == 1 ? ghi.y : (sw & 3) == 2 ? ghi.z : ghi.w;
+          sbytes = (x ? whi : wlo) >> ssh;
+          cw = x ? rc[se + 1][i] : rc[se][i];
+          drow = x ? lrow_hi[i] : lrow_lo[i];
         } else {
-          sbytes = rs[slot][i];
+          if constexpr (SG) {
+            const uint4 g = rsg[(sw >> 2) & 1][i];
+            const uint32_t wd = (sw & 3) == 0 ? g.x : (sw & 3) == 1 ? g.y : (sw & 3) == 2 ? g.z : g.w;
+            sbytes = wd >> ssh;
+          } else {
+            sbytes = rs[slot][i];
+          }
+          cw = rc[slot][i];
+          drow = lrow[i];
         }
         const half2_t sc = scales2(sbytes);
         const half2_t s0 = {sc.x, sc.x}, s1 = {sc.y, sc.y};
         uint4 d[4];
-        d[0] = deq8(rc[slot][i].x, s0);
-        d[1] = deq8(rc[slot][i].y, s0);
-        d[2] = deq8(rc[slot][i].z, s1);
-        d[3] = deq8(rc[slot][i].w, s1);
+        d[0] = deq8(cw.x, s0);
+        d[1] = deq8(cw.y, s0);
+        d[2] = deq8(cw.z, s1);
+        d[3] = deq8(cw.w, s1);
         _Float16* base = i < IA ? As + buf * BM * kWsLdsK : Bs + buf * BN * kWsLdsK;
-        uint4* dst = reinterpret_cast<uint4*>(base + lrow[i] * kWsLdsK + 32 * hf);
+        uint4* dst = reinterpret_cast<uint4*>(base + drow * kWsLdsK + 32 * hf);
 #pragma unroll
         for (int e = 0; e < 4; ++e) dst[e] = d[e];
         if constexpr (HAS_MEAN) {
@@ -250,7 +314,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
               r[e] = __builtin_amdgcn_fdot2(h2(d[e].z), h2(mm.z), r[e], false);
               r[e] = __builtin_amdgcn_fdot2(h2(d[e].w), h2(mm.w), r[e], false);
             }
-            racc[i - IA] += (r[0] + r[1]) + (r[2] + r[3]);
+            const float rsum = (r[0] + r[1]) + (r[2] + r[3]);
+            if constexpr (W2) {
+              const bool xh = drow != lrow_lo[i];
+              racc[i - IA] += xh ? 0.0f : rsum;
+              racc_hi[i - IA] += xh ? rsum : 0.0f;
+            } else {
+              racc[i - IA] += rsum;
+            }
           }
         }
       }
@@ -287,10 +358,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
         }
       }
     }
-    ws_unroll<0, PF>([&](auto p_c) __attribute__((always_inline)) {
-      constexpr int p = decltype(p_c)::value;
-      if (p < nk) gload(p, p, WsIC<p>{});
-    });
+    if constexpr (W2) {
+      // windows 0 and 1 (stages 0..3) fill the ring
+      gload(0, 0, WsIC<0>{});
+      if (2 < nk) gload(2, 2, WsIC<2>{});
+    } else {
+      ws_unroll<0, PF>([&](auto p_c) __attribute__((always_inline)) {
+        constexpr int p = decltype(p_c)::value;
+        if (p < nk) gload(p, p, WsIC<p>{});
+      });
+    }
     if constexpr (HAS_MEAN) {
 #pragma unroll
       for (int u = 0; u < kMeanPer; ++u) {
@@ -308,7 +385,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
       __syncthreads();   // mean row published (the consumers wait here too)
     }
     dequant(0, 0, 0, WsIC<0>{});
-    if (PF < nk) gload(0, PF, WsIC<PF % 8>{});
+    if constexpr (!W2) {
+      if (PF < nk) gload(0, PF, WsIC<PF % 8>{});
+    }
     __syncthreads();
     // iteration it: dequantize stage it + 1 (slot (it + 1) % PF) into buffer
     // (it + 1) & 1, refill that slot with stage it + 1 + PF
@@ -320,7 +399,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
         const int i2 = it + u;
         if (i2 + 1 < nk) {
           dequant(su, (i2 + 1) & 1, i2 + 1, WsIC<(u + 1) % 8>{});
-          if (i2 + 1 + PF < nk) gload(su, i2 + 1 + PF, WsIC<(u + 1 + PF) % 8>{});
+          if constexpr (W2) {
+            // after an odd stage both slots of the window three stages on
+            // are free: stages i2 + 4 and i2 + 5
+            if constexpr (((u + 1) & 1) == 1) {
+              if (i2 + 4 < nk) gload((u + 4) % PF, i2 + 4, WsIC<(u + 4) % 8>{});
+            }
+          } else {
+            if (i2 + 1 + PF < nk) gload(su, i2 + 1 + PF, WsIC<(u + 1 + PF) % 8>{});
+          }
         }
         __syncthreads();
       });
@@ -332,7 +419,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
       if (i2 < nk) {
         if (i2 + 1 < nk) {
           dequant(su, (i2 + 1) & 1, i2 + 1, WsIC<(u + 1) % 8>{});
-          if (i2 + 1 + PF < nk) gload(su, i2 + 1 + PF, WsIC<(u + 1 + PF) % 8>{});
+          if constexpr (W2) {
+            // after an odd stage both slots of the window three stages on
+            // are free: stages i2 + 4 and i2 + 5
+            if constexpr (((u + 1) & 1) == 1) {
+              if (i2 + 4 < nk) gload((u + 4) % PF, i2 + 4, WsIC<(u + 4) % 8>{});
+            }
+          } else {
+            if (i2 + 1 + PF < nk) gload(su, i2 + 1 + PF, WsIC<(u + 1 + PF) % 8>{});
+          }
         }
         __syncthreads();
       }
@@ -343,8 +438,21 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
 #pragma unroll
       for (int i = IA; i < CP; ++i) {
         if (pt + kProducers * i >= NCH) break;   // whole waves
-        const float v = racc[i - IA] + __shfl_xor(racc[i - IA], 1, 64);
-        if ((pt & 1) == 0) rho_sh[lrow[i]] = v * rs_scale;
+        if constexpr (W2) {
+          // rows lo and hi were each summed by the four lanes of a row group
+          float vl = racc[i - IA], vh = racc_hi[i - IA];
+          vl += __shfl_xor(vl, 1, 64);
+          vh += __shfl_xor(vh, 1, 64);
+          vl += __shfl_xor(vl, 2, 64);
+          vh += __shfl_xor(vh, 2, 64);
+          if ((pt & 3) == 0) {
+            rho_sh[lrow_lo[i]] = vl * rs_scale;
+            rho_sh[lrow_hi[i]] = vh * rs_scale;
+          }
+        } else {
+          const float v = racc[i - IA] + __shfl_xor(racc[i - IA], 1, 64);
+          if ((pt & 1) == 0) rho_sh[lrow[i]] = v * rs_scale;
+        }
       }
       __syncthreads();   // rank-one terms published for the epilogue
     }
