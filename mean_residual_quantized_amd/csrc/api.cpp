@@ -60,7 +60,7 @@ size_t split_ws_bytes(int64_t rows, int64_t cols, int nseg) {
   const int64_t ct_s = (cols + 255) / 256, ct_f = (cols + kFinCols - 1) / kFinCols;
   size_t b = 0;
   b += align256((size_t)(nch * cols * 8));      // psum
-  b += align256((size_t)(nch * cols * 4)) * 2;  // pmax, pmin
+  b += align256((size_t)(nch * cols * 4)) * 3;  // pmax, pmin, pmnz
   b += align256((size_t)(nch * ct_s * 4));      // pamax
   b += align256((size_t)(ns * cols * 4));       // mu
   b += align256((size_t)(ns * (ct_f > 1 ? ct_f : 1) * 4)) * 2;  // tmax_r, tmax_mu
@@ -76,6 +76,7 @@ SplitWs split_ws_carve(void* ws, int64_t rows, int64_t cols, int nseg) {
   w.psum = reinterpret_cast<double*>(p); p += align256((size_t)(nch * cols * 8));
   w.pmax = reinterpret_cast<float*>(p);  p += align256((size_t)(nch * cols * 4));
   w.pmin = reinterpret_cast<float*>(p);  p += align256((size_t)(nch * cols * 4));
+  w.pmnz = reinterpret_cast<float*>(p);  p += align256((size_t)(nch * cols * 4));
   w.pamax = reinterpret_cast<float*>(p); p += align256((size_t)(nch * ct_s * 4));
   w.mu = reinterpret_cast<float*>(p);    p += align256((size_t)(ns * cols * 4));
   w.tmax_r = reinterpret_cast<float*>(p); p += align256((size_t)(ns * (ct_f > 1 ? ct_f : 1) * 4));

@@ -25,6 +25,7 @@ struct SplitWs {
   double* psum;    // [chunks][cols] partial column sums
   float* pmax;     // [chunks][cols]
   float* pmin;     // [chunks][cols]
+  float* pmnz;     // [chunks][cols] smallest nonzero |a| (the exactness certificate)
   float* pamax;    // [chunks][col tiles] plain-pass max |a|
   float* mu;       // [nseg][cols]
   float* tmax_r;   // [nseg][col tiles] residual max |r| per column tile

@@ -12,9 +12,10 @@
 //             subtraction is monotone), reduced per column tile
 //   quant     per 16-block: residual, block amax, E4M3 scale, Philox SR or RN,
 //             packed nibbles; extra workgroups quantize the mean vectors
-// Partial sums are exact in fp64 for inputs whose column dynamic range fits
-// 53 bits (always for the bf16 workloads here), so their order does not
-// change the mean.
+// Partial sums are exact in fp64 when a column's values span a narrow enough
+// range (checked per column from its largest and smallest nonzero magnitude);
+// a column that fails the check is summed again exactly (320-bit integer
+// accumulation, rounded once), so the mean never depends on the order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -100,6 +101,7 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
                                                double* __restrict__ psum,
                                                float* __restrict__ pmax,
                                                float* __restrict__ pmin,
+                                               float* __restrict__ pmnz,
                                                float* __restrict__ pamax) {
   const SegRange sr = locate_chunk(offs, nseg, rows, kStatsRows, blockIdx.y);
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
@@ -107,13 +109,20 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
   const bool active = sr.seg >= 0 && c < cols;
 
   double s[8];
-  float mx[8], mn[8];
+  float mx[8], mn[8], mz[8];
   float am = 0.0f;
+  // bf16: the smallest nonzero magnitude per column as packed 16-bit
+  // (|bits| - 1), where a zero wraps to 0xFFFF and never wins the minimum
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 mzp[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) mzp[w] = u16x2{0xFFFFu, 0xFFFFu};
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     s[k] = 0.0;
     mx[k] = -__builtin_inff();
     mn[k] = __builtin_inff();
+    mz[k] = __builtin_inff();
   }
   if (active) {
     // all rows of the chunk in flight at once; rows past the segment end are
@@ -137,13 +146,39 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
           s[k] += ok ? (double)x : 0.0;
           mx[k] = __builtin_fmaxf(mx[k], x);
           mn[k] = __builtin_fminf(mn[k], x);
+          if constexpr (sizeof(T) != 2) {
+            // smallest nonzero magnitude: sets the grid every value lies on
+            const float ax = __builtin_fabsf(x);
+            mz[k] = __builtin_fminf(mz[k], ax > 0.0f ? ax : __builtin_inff());
+          }
         } else {
           am = __builtin_fmaxf(am, __builtin_fabsf(x));
         }
       }
+      if constexpr (SPLIT && sizeof(T) == 2) {
+        // a clamped row repeats a real one: harmless for the minimum
+        const uint32_t wd[4] = {v[u].w.x, v[u].w.y, v[u].w.z, v[u].w.w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const u16x2 m = __builtin_bit_cast(u16x2, wd[w] & 0x7FFF7FFFu) - u16x2{1, 1};
+          mzp[w] = __builtin_elementwise_min(mzp[w], m);
+        }
+      }
+    }
+  }
+  if constexpr (SPLIT && sizeof(T) == 2) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t m = mzp[w][h];
+        mz[2 * w + h] = m == 0xFFFFu ? __builtin_inff() : __uint_as_float((m + 1u) << 16);
+      }
     }
   }
   if (SPLIT) {
+    // 32 KB of LDS (four blocks per CU): the smallest nonzero magnitudes go
+    // through the max buffer in a second round
     __shared__ double ls[8][256];
     __shared__ float lmx[8][256], lmn[8][256];
 #pragma unroll
@@ -155,7 +190,9 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
     __syncthreads();
     const int j = threadIdx.x;
     const int64_t col = (int64_t)blockIdx.x * 256 + j;
-    if (sr.seg >= 0 && col < cols) {
+    const bool live = sr.seg >= 0 && col < cols;
+    const int64_t o = (int64_t)blockIdx.y * cols + col;
+    if (live) {
       double t = 0.0;
       float m1 = -__builtin_inff(), m0 = __builtin_inff();
 #pragma unroll
@@ -164,10 +201,19 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
         m1 = __builtin_fmaxf(m1, lmx[q][j]);
         m0 = __builtin_fminf(m0, lmn[q][j]);
       }
-      const int64_t o = (int64_t)blockIdx.y * cols + col;
       psum[o] = t;
       pmax[o] = m1;
       pmin[o] = m0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 8; ++k) lmx[ty][tx * 8 + k] = mz[k];
+    __syncthreads();
+    if (live) {
+      float mzz = __builtin_inff();
+#pragma unroll
+      for (int q = 0; q < 8; ++q) mzz = __builtin_fminf(mzz, lmx[q][j]);
+      pmnz[o] = mzz;
     }
   } else {
     __shared__ float red[4];
@@ -177,14 +223,144 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
 }
 
 // ---------------------------------------------------------------------------
+// Exact column sum for columns whose fp64 accumulation is not certified.
+// Every fp32 value is an integer multiple of 2^-149 below 2^128, so a signed
+// 320-bit integer in units of 2^-149 holds any sum of up to 2^31 of them
+// exactly.  Each thread adds its rows into its own accumulator, the block
+// adds the accumulators pairwise, and thread 0 rounds the total to the
+// nearest double (ties to even): the correctly rounded sum.
+// ---------------------------------------------------------------------------
+constexpr int kWideWords = 10;
+
+__device__ __forceinline__ void wide_add_value(uint32_t (&acc)[kWideWords], float v) {
+  const uint32_t bits = __float_as_uint(v);
+  const uint32_t e = (bits >> 23) & 0xFFu, m = bits & 0x7FFFFFu;
+  if (e == 0 && m == 0) return;
+  const uint32_t mant = e ? (m | 0x800000u) : m;   // value = mant * 2^(shift - 149)
+  const uint32_t shift = e ? e - 1 : 0;
+  const uint32_t w = shift >> 5;
+  const uint64_t part = (uint64_t)mant << (shift & 31);
+  const uint32_t lo = (uint32_t)part, hi = (uint32_t)(part >> 32);
+  if (!(bits >> 31)) {
+    uint64_t carry = 0;
+#pragma unroll
+    for (int i = 0; i < kWideWords; ++i) {
+      const uint32_t add = (uint32_t)i == w ? lo : ((uint32_t)i == w + 1 ? hi : 0u);
+      const uint64_t sum = (uint64_t)acc[i] + add + carry;
+      acc[i] = (uint32_t)sum;
+      carry = sum >> 32;
+    }
+  } else {
+    uint64_t borrow = 0;
+#pragma unroll
+    for (int i = 0; i < kWideWords; ++i) {
+      const uint32_t sub = (uint32_t)i == w ? lo : ((uint32_t)i == w + 1 ? hi : 0u);
+      const uint64_t d = (uint64_t)acc[i] - sub - borrow;
+      acc[i] = (uint32_t)d;
+      borrow = (d >> 32) ? 1u : 0u;
+    }
+  }
+}
+
+__device__ __forceinline__ void wide_add(uint32_t (&acc)[kWideWords], const uint32_t* other) {
+  uint64_t carry = 0;
+#pragma unroll
+  for (int i = 0; i < kWideWords; ++i) {
+    const uint64_t sum = (uint64_t)acc[i] + other[i] + carry;
+    acc[i] = (uint32_t)sum;
+    carry = sum >> 32;
+  }
+}
+
+// bits [lo, lo + 64) of the magnitude (bits past the top read as 0)
+__device__ __forceinline__ uint64_t wide_bits64(const uint32_t (&a)[kWideWords], int lo) {
+  uint64_t r = 0;
+#pragma unroll
+  for (int i = 0; i < kWideWords; ++i) {
+    const int off = 32 * i - lo;   // position of word i's bit 0 in the result
+    if (off >= 64 || off <= -32) continue;
+    const uint64_t wv = a[i];
+    r |= off >= 0 ? (wv << off) : (wv >> -off);
+  }
+  return r;
+}
+
+__device__ inline double wide_to_double(uint32_t (&a)[kWideWords]) {
+  const bool neg = a[kWideWords - 1] >> 31;
+  if (neg) {   // magnitude: two's complement negation
+    uint64_t carry = 1;
+#pragma unroll
+    for (int i = 0; i < kWideWords; ++i) {
+      const uint64_t v = (uint64_t)(~a[i]) + carry;
+      a[i] = (uint32_t)v;
+      carry = v >> 32;
+    }
+  }
+  int p = -1;   // highest set bit
+#pragma unroll
+  for (int i = 0; i < kWideWords; ++i)
+    if (a[i]) p = 32 * i + 31 - __builtin_clz(a[i]);
+  if (p < 0) return 0.0;
+  double r;
+  if (p < 53) {
+    r = __builtin_ldexp((double)wide_bits64(a, 0), -149);   // exact
+  } else {
+    uint64_t mant = wide_bits64(a, p - 52) & ((1ull << 53) - 1);
+    const bool round = (wide_bits64(a, p - 53) & 1ull) != 0;
+    bool sticky = false;
+    for (int b = 0; b < p - 53; b += 64) {
+      const int n = p - 53 - b;
+      const uint64_t chunk = wide_bits64(a, b);
+      sticky = sticky || (n >= 64 ? chunk != 0 : (chunk & ((1ull << n) - 1)) != 0);
+    }
+    int ex = p - 52 - 149;
+    if (round && (sticky || (mant & 1ull))) {
+      mant += 1;
+      if (mant >> 53) {
+        mant >>= 1;
+        ex += 1;
+      }
+    }
+    r = __builtin_ldexp((double)mant, ex);
+  }
+  return neg ? -r : r;
+}
+
+// the exact sum of rows [r0, r1) of column j, correctly rounded to double;
+// all 256 threads call it, thread 0 gets the result
+__device__ double exact_column_sum(const void* a, bool bf16, int64_t lda, int64_t r0, int64_t r1,
+                                   int64_t j, uint32_t (*red)[kWideWords]) {
+  uint32_t acc[kWideWords];
+#pragma unroll
+  for (int i = 0; i < kWideWords; ++i) acc[i] = 0u;
+  for (int64_t r = r0 + threadIdx.x; r < r1; r += 256) {
+    const float v = bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(a)[r * lda + j] << 16)
+                         : static_cast<const float*>(a)[r * lda + j];
+    wide_add_value(acc, v);
+  }
+  for (int stride = 128; stride > 0; stride >>= 1) {
+    if ((int)threadIdx.x >= stride && (int)threadIdx.x < 2 * stride) {
+#pragma unroll
+      for (int i = 0; i < kWideWords; ++i) red[threadIdx.x - stride][i] = acc[i];
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < stride) wide_add(acc, red[threadIdx.x]);
+    __syncthreads();
+  }
+  return threadIdx.x == 0 ? wide_to_double(acc) : 0.0;
+}
+
+// ---------------------------------------------------------------------------
 // finalize (split): block = kFinCols (16) columns x 16 chunk lanes, per
 // segment; each lane keeps all its partial loads in flight.  The fp64 partial
 // sums are exact, so the order of the reduction is free.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_finalize(int64_t rows, int64_t cols, const int64_t* offs,
+__global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, int64_t lda,
+                                                  int64_t rows, int64_t cols, const int64_t* offs,
                                                   int nseg, const double* __restrict__ psum,
                                                   const float* __restrict__ pmax,
                                                   const float* __restrict__ pmin,
+                                                  const float* __restrict__ pmnz,
                                                   float* __restrict__ mu,
                                                   float* __restrict__ mean_out,
                                                   float* __restrict__ tmax_r,
@@ -195,19 +371,20 @@ __global__ __launch_bounds__(256) void k_finalize(int64_t rows, int64_t cols, co
   const int jl = threadIdx.x % NC, q = threadIdx.x / NC;
   const int64_t j = (int64_t)blockIdx.x * NC + jl;
   double s = 0.0;
-  float m1 = -__builtin_inff(), m0 = __builtin_inff();
+  float m1 = -__builtin_inff(), m0 = __builtin_inff(), mz = __builtin_inff();
   if (j < cols && sr.c1 > sr.c0) {
     constexpr int U = 8;
     const int64_t clast = sr.c1 - 1;
     for (int64_t ck = sr.c0 + q; ck < sr.c1; ck += NQ * U) {
       double ps[U];
-      float px[U], pn[U];
+      float px[U], pn[U], pz[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t cc = ck + NQ * u < clast ? ck + NQ * u : clast;
         ps[u] = psum[cc * cols + j];
         px[u] = pmax[cc * cols + j];
         pn[u] = pmin[cc * cols + j];
+        pz[u] = pmnz[cc * cols + j];
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -215,26 +392,57 @@ __global__ __launch_bounds__(256) void k_finalize(int64_t rows, int64_t cols, co
         s += ok ? ps[u] : 0.0;
         m1 = __builtin_fmaxf(m1, px[u]);   // a clamped chunk repeats a real one
         m0 = __builtin_fminf(m0, pn[u]);
+        mz = __builtin_fminf(mz, pz[u]);
       }
     }
   }
   __shared__ double ls[NQ][NC];
-  __shared__ float lx[NQ][NC], ln[NQ][NC];
+  __shared__ float lx[NQ][NC], ln[NQ][NC], lz[NQ][NC];
+  __shared__ int need_exact[NC];
+  __shared__ double exact_s[NC];
+  __shared__ uint32_t wide_red[128][kWideWords];
   ls[q][jl] = s;
   lx[q][jl] = m1;
   ln[q][jl] = m0;
+  lz[q][jl] = mz;
   __syncthreads();
   float rmax = 0.0f, amu = 0.0f;
-  if (q == 0 && j < cols) {
-    double t = 0.0;
-    float x1 = -__builtin_inff(), x0 = __builtin_inff();
+  double t = 0.0;
+  float x1 = -__builtin_inff(), x0 = __builtin_inff();
+  const int64_t l = sr.seg_r1 - sr.seg_r0;
+  if (q == 0) {
+    float z = __builtin_inff();
 #pragma unroll
     for (int p = 0; p < NQ; ++p) {
       t += ls[p][jl];
       x1 = __builtin_fmaxf(x1, lx[p][jl]);
       x0 = __builtin_fminf(x0, ln[p][jl]);
+      z = __builtin_fminf(z, lz[p][jl]);
     }
-    const int64_t l = sr.seg_r1 - sr.seg_r0;
+    // Certificate: every value of the column is a multiple of g = 2^(ez-1-P)
+    // (ez: binary exponent of the smallest nonzero |a|; P = 7 for bf16 input,
+    // 23 for fp32), and every partial sum is at most l * max|a|.  When that
+    // bound is <= 2^52 g, every fp64 addition above was exact, in any order.
+    bool fail = false;
+    if (j < cols && l > 0 && z < __builtin_inff()) {
+      int ez;
+      (void)__builtin_frexp((double)z, &ez);
+      const double amx = __builtin_fmax(__builtin_fabs((double)x1), __builtin_fabs((double)x0));
+      fail = !((double)l * amx <= __builtin_ldexp(1.0, 52 + ez - 1 - (a_bf16 ? 7 : 23)));
+    }
+    need_exact[jl] = fail;
+  }
+  __syncthreads();
+  for (int cidx = 0; cidx < NC; ++cidx) {   // uniform: flags from LDS
+    if (need_exact[cidx]) {
+      const double v = exact_column_sum(a, a_bf16, lda, sr.seg_r0, sr.seg_r1,
+                                        (int64_t)blockIdx.x * NC + cidx, wide_red);
+      if (threadIdx.x == 0) exact_s[cidx] = v;
+    }
+  }
+  __syncthreads();
+  if (q == 0 && j < cols) {
+    if (need_exact[jl]) t = exact_s[jl];
     float m = 0.0f;
     if (l > 0) {
       m = (float)(t / (double)l);
@@ -677,17 +885,18 @@ static hipError_t run_split_or_plain(const void* a_, int64_t rows, int64_t cols,
     dim3 g((unsigned)ct_s, (unsigned)nchs);
     if (split)
       k_stats<T, true><<<g, 256, 0, st>>>(a, rows, cols, lda, offs, nseg, ws.psum, ws.pmax,
-                                          ws.pmin, nullptr);
+                                          ws.pmin, ws.pmnz, nullptr);
     else
       k_stats<T, false><<<g, 256, 0, st>>>(a, rows, cols, lda, offs, nseg, nullptr, nullptr,
-                                           nullptr, ws.pamax);
+                                           nullptr, nullptr, ws.pamax);
   }
   int64_t ntmax;
   const float* tmax;
   if (split) {
     dim3 g((unsigned)ct_f, (unsigned)nseg);
-    k_finalize<<<g, 256, 0, st>>>(rows, cols, offs, nseg, ws.psum, ws.pmax, ws.pmin, ws.mu,
-                                  mean_f32, ws.tmax_r, ws.tmax_mu);
+    k_finalize<<<g, 256, 0, st>>>(a, sizeof(T) == 2, lda, rows, cols, offs, nseg, ws.psum,
+                                  ws.pmax, ws.pmin, ws.pmnz, ws.mu, mean_f32, ws.tmax_r,
+                                  ws.tmax_mu);
     tmax = ws.tmax_r;
     ntmax = ct_f;
   } else {

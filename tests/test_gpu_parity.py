@@ -147,6 +147,41 @@ def test_all_zero_and_empty_inputs():
     torch.cuda.synchronize()
 
 
+def adversarial_columns(rows, cols, seed):
+    """Columns whose fp64 running sum is order-dependent (the kernel's
+    exactness certificate fails for them and the exact sum is taken)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    i = np.arange(rows)
+    x[:, 0] = np.resize(np.array([2.0 ** 100, 1.0, -(2.0 ** 100)], np.float32), rows)
+    x[:, 1] = np.where(i % 2 == 0, np.float32(3.0e30), np.float32(-1.0e-30))
+    x[:, 2] = np.where(i % 5 == 0, np.float32(7.0), np.float32(2.0 ** -130))   # fp32 subnormal
+    x[:, 3] = 0.0
+    x[:, 5] = np.where(i % 3 == 0, np.float32(2.0 ** 60), np.float32(0.75)) * np.where(i % 2, 1, -1)
+    return x
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_uncertified_columns_take_the_exact_sum(dtype):
+    x = torch.from_numpy(adversarial_columns(300, 64, 5)).to(dtype)
+    res, mean, mu = av.averis_split_quant(x.cuda(), seed=3)
+    s = orc.split_quant(f32(x), "sr", 3)
+    np.testing.assert_array_equal(mu.cpu().numpy(), s["mu"])
+    assert_quant_equal(res, s["residual"])
+    assert_quant_equal(mean, s["mean"])
+    # grouped: each segment's mean on its own rows
+    offs = np.array([0, 97, 97, 300], dtype=np.int64)
+    og = torch.from_numpy(offs).cuda()
+    res_g, mean_g, mu_g = av.averis_split_quant_grouped(x.cuda(), og, seed=3)
+    g = orc.split_quant_grouped(f32(x), offs, "sr", 3)
+    np.testing.assert_array_equal(mu_g.cpu().numpy(), g["mu"])
+    rc = res_g.cpu()
+    for seg in range(3):
+        r0, r1 = offs[seg], offs[seg + 1]
+        np.testing.assert_array_equal(rc["codes"][r0:r1], g["residual"][seg]["codes"])
+        assert rc["tscale"][2 * seg] == g["residual"][seg]["s_enc"]
+
+
 def test_bf16_output_within_rounding():
     cfg = workloads.config1(l=256, m=256, n=128)
     xg = cfg["x"].cuda()
