@@ -27,11 +27,23 @@ arithmetic):
     v_k    = float32(T_k * e_b) -> E2M1 code by RN or SR
   and the dequantized value is E2M1(code) * d_b * S_dec (exact in float64).
 * SR draws come from oracle.philox keyed by (seed, stream, row * cols + col);
-  streams: 0 residual / vanilla activations, 1 mean, 2 weights.
+  streams: 0 residual / vanilla activations, 1 mean, 2 weights, 3 the
+  transposed residuals of the wgrad product.
 * GEMMs ([Lighthouse] §2.2): Y = 1 (deq(mean_q) deq(B)^T) + deq(X_R,q) deq(B)^T
   with B = W^T quantized along m (forward), and the same with D and B = W
   quantized along n (dgrad); the vanilla arm is deq(Q4(X)) deq(B)^T.  All
   products and sums are float64.
+* wgrad (not among the pages' equations; reading): the same split applied to
+  both operands of dW = X^T D.  With X = X_R + 1 mu^T and D = D_R + 1 nu^T,
+  X^T D = X_R^T D_R + X_R^T 1 nu^T + mu 1^T D_R + l mu nu^T, and the two
+  middle terms vanish because the residuals have zero column sums.  So
+    dW = deq(Q4(X_R^T)) deq(Q4(D_R^T))^T + l mu_X nu_D^T,
+  with the transposed residuals quantized in blocks of 16 along the token axis
+  (the contraction axis of this product), SR stream 3, and the outer product
+  taken from the fp32 means the splits already hold.  The outer product is no
+  contraction, so no FP4 GEMM needs its operands quantized; quantizing them
+  (mean="q4", for comparison) gives one error per column that the factor l
+  multiplies coherently instead of averaging it over the tokens.
 * grouped (one mean and one tensor scale per expert segment): every step above
   is applied to each segment's rows; SR indices use the global row, the mean
   of segment s uses index s * cols + col; an empty segment has mean 0.
@@ -198,6 +210,51 @@ def vanilla_forward(x, w_q_fwd, rnd="sr", seed=0):
     """Comparison arm ([Abstract]: vanilla NVFP4): deq(Q4(X)) deq(W_q)."""
     q = vanilla_quant(x, rnd, seed)
     return q, gemm(q, w_q_fwd)
+
+
+# --------------------------------------------------------------------------
+# wgrad (reading: the split applied to both operands of X^T D)
+# --------------------------------------------------------------------------
+
+def residual_t_quant(a, mu, rnd="sr", seed=0):
+    """Q4 of the transposed residual (cols x rows, blocks of 16 along the rows,
+    i.e. the token axis), SR stream 3: the wgrad operand."""
+    r = residual(np.asarray(a, dtype=np.float32), mu)
+    return quantize(np.ascontiguousarray(r.T), rnd, seed, stream=3)
+
+
+def wgrad_combine(xt, dt, mean_x, mean_d, l):
+    """xt dt^T + l mean_x^T mean_d for float64 operands: xt (m x l), dt (n x l),
+    mean_x (m,), mean_d (n,).  The quantized wgrad feeds it dequantized values;
+    with exact residuals and means it reproduces X^T D."""
+    return xt @ dt.T + np.float64(l) * np.outer(mean_x, mean_d)
+
+
+def averis_wgrad(x, d, rnd="sr", seed_x=0, seed_d=0, mean="f32"):
+    """dW (m x n) for X (l x m) and D (l x n): the splits of X and D (seeds as
+    in the forward and dgrad passes), the transposed residuals quantized along
+    the tokens, and the outer product of the fp32 means (mean="f32") or of the
+    dequantized FP4 means (mean="q4")."""
+    x = np.asarray(x, dtype=np.float32)
+    d = np.asarray(d, dtype=np.float32)
+    sx, sd = split_quant(x, rnd, seed_x), split_quant(d, rnd, seed_d)
+    xt = residual_t_quant(x, sx["mu"], rnd, seed_x)
+    dt = residual_t_quant(d, sd["mu"], rnd, seed_d)
+    if mean == "f32":
+        mx, md = sx["mu"].astype(np.float64), sd["mu"].astype(np.float64)
+    elif mean == "q4":
+        mx, md = dequantize(sx["mean"])[0], dequantize(sd["mean"])[0]
+    else:
+        raise ValueError("mean must be 'f32' or 'q4'")
+    dw = wgrad_combine(dequantize(xt), dequantize(dt), mx, md, x.shape[0])
+    return dict(xt=xt, dt=dt, mu_x=sx["mu"], mu_d=sd["mu"], dw=dw)
+
+
+def wgrad_abs_bound(xt, dt, mu_x, mu_d, l):
+    """|deq xt| |deq dt|^T + l |mu_x| |mu_d|^T: the scale the wgrad error is
+    measured against."""
+    return wgrad_combine(np.abs(dequantize(xt)), np.abs(dequantize(dt)),
+                         np.abs(np.asarray(mu_x, np.float64)), np.abs(np.asarray(mu_d, np.float64)), l)
 
 
 # --------------------------------------------------------------------------
