@@ -30,7 +30,8 @@
  *         draw from Philox4x32-10: key = seed, counter = (g lo, g hi,
  *         stream, 0), g = idx >> 3, word (idx >> 1) & 3, half idx & 1,
  *         idx = row * cols + col (global row for grouped tensors).
- *   SR streams: 0 residual and vanilla activations, 1 means, 2 weights.
+ *   SR streams: 0 residual and vanilla activations, 1 means, 2 weights,
+ *   3 transposed residuals (wgrad).
  *   The mean is fp32(RN64(exact column sum) / l); the residual is
  *   fp32(x - mu) with the unquantized mean.
  *
@@ -78,7 +79,8 @@ typedef enum { AVERIS_RN = 0, AVERIS_SR = 1 } averis_round_t;
 typedef enum {
   AVERIS_OP_SPLIT_QUANT = 0,  /* rows, cols, nseg (nseg = 0: not grouped)     */
   AVERIS_OP_QUANT = 1,        /* rows, cols, nseg (batch for batched quant)   */
-  AVERIS_OP_GEMM = 2          /* rows = M, cols = K, n = N, nseg              */
+  AVERIS_OP_GEMM = 2,         /* rows = M, cols = K, n = N, nseg              */
+  AVERIS_OP_WGRAD = 3         /* rows = m, cols = l (tokens), n               */
 } averis_op_t;
 
 /* An NVFP4-style tensor of rows x cols logical elements, 16-blocks along
@@ -219,6 +221,46 @@ averis_status_t averis_gemm_grouped(const averis_nvfp4_t* a, const averis_nvfp4_
                                     const averis_nvfp4_t* b, const int64_t* seg_offsets, int nseg,
                                     void* c, averis_dtype_t cdtype, int64_t ldc, void* ws,
                                     size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* wgrad (the W4A4G4 setting of the arXiv abstract and Lighthouse §3.1    */
+/* keeps weights, activations and gradients in FP4; §2.2 writes out only   */
+/* the forward and dgrad products).  Reading: the split applied to both    */
+/* operands of                                                             */
+/* dW = X^T D.  The residuals' column sums vanish, so                      */
+/*   dW = deq(Q4(X_R^T)) deq(Q4(D_R^T))^T + l mu_X mu_D^T,                 */
+/* with the transposed residuals quantized in 16-blocks along the tokens   */
+/* (the contraction axis of this product) and the outer product taken from */
+/* the fp32 means (no contraction runs over them).                         */
+/* ---------------------------------------------------------------------- */
+
+/* out_t = Q4((a - 1 mu)^T): cols x rows, 16-blocks along the rows (tokens),
+ * SR stream 3, element index col * rows + row.  a: rows x cols (F32 or BF16,
+ * row stride lda, as for averis_split_quant); rows % 16 == 0 (rows may be 0).
+ * mu: the fp32 column means averis_split_quant wrote for the same a (cols
+ * floats, device, 16-byte aligned).  residual_tscale: the residual tensor's
+ * [S_enc, S_dec] from that call (device, 2 floats); the transposed residual
+ * holds the same values and takes the same tensor scale, copied to
+ * out_t->tscale.  No workspace.  Other arguments as for averis_split_quant. */
+averis_status_t averis_residual_t_quant(const void* a, averis_dtype_t dtype, int64_t rows,
+                                        int64_t cols, int64_t lda, const float* mu,
+                                        const float* residual_tscale, uint64_t seed,
+                                        averis_round_t rnd, const averis_nvfp4_t* out_t,
+                                        hipStream_t stream);
+
+/* dw (m x n, F32 or BF16, row stride lddw >= n) =
+ *   deq(xt) deq(dt)^T + l mu_x mu_d^T
+ * with xt = Q4(X_R^T) (m x l) and dt = Q4(D_R^T) (n x l) from
+ * averis_residual_t_quant, mu_x (m floats) and mu_d (n floats) the fp32
+ * means of X and D (device, 16-byte aligned); m, n, l multiples of 16 (l may
+ * be 0: dw = l mu_x mu_d^T = 0).  FP32 accumulation; the token axis is split
+ * into fp32 partials that are summed in a fixed order, so repeated calls
+ * give the same bits.  Workspace: averis_workspace_bytes(AVERIS_OP_WGRAD,
+ * m, l, n, 0). */
+averis_status_t averis_gemm_wgrad(const averis_nvfp4_t* xt, const averis_nvfp4_t* dt,
+                                  const float* mu_x, const float* mu_d, void* dw,
+                                  averis_dtype_t dwdtype, int64_t lddw, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
 
 /* ---------------------------------------------------------------------- */
 /* Utilities                                                               */

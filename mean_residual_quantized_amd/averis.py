@@ -21,14 +21,15 @@ STATUS_NAMES = {0: "OK", 1: "E_NULL", 2: "E_SHAPE", 3: "E_DTYPE", 4: "E_ALIGN",
                 5: "E_WORKSPACE", 6: "E_ARG", 7: "E_HIP"}
 F32, BF16 = 0, 1
 RN, SR = 0, 1
-OP_SPLIT_QUANT, OP_QUANT, OP_GEMM = 0, 1, 2
-STREAM_ACT, STREAM_MEAN, STREAM_WEIGHT = 0, 1, 2
+OP_SPLIT_QUANT, OP_QUANT, OP_GEMM, OP_WGRAD = 0, 1, 2, 3
+STREAM_ACT, STREAM_MEAN, STREAM_WEIGHT, STREAM_RESIDUAL_T = 0, 1, 2, 3
 
 # every symbol include/averis.h declares
 EXPORTS = [
     "averis_split_quant", "averis_split_quant_grouped", "averis_quant", "averis_quant_batched",
     "averis_quant_grouped", "averis_quant_pair", "averis_gemm_fwd", "averis_gemm_dgrad",
-    "averis_gemm_vanilla", "averis_gemm_grouped", "averis_workspace_bytes", "averis_status_str",
+    "averis_gemm_vanilla", "averis_gemm_grouped", "averis_residual_t_quant", "averis_gemm_wgrad",
+    "averis_workspace_bytes", "averis_status_str",
     "averis_abi_version", "averis_last_error",
 ]
 
@@ -69,6 +70,8 @@ def lib():
             "averis_gemm_dgrad": [T, T, T, P, I, I64, P, SZ, P],
             "averis_gemm_vanilla": [T, T, P, I, I64, P, SZ, P],
             "averis_gemm_grouped": [T, T, T, P, I, P, I, I64, P, SZ, P],
+            "averis_residual_t_quant": [P, I, I64, I64, I64, P, P, U64, I, T, P],
+            "averis_gemm_wgrad": [T, T, P, P, P, I, I64, P, SZ, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -296,3 +299,30 @@ def averis_gemm_grouped(a, mean, b, offsets, out_dtype=torch.float32, out=None, 
     nseg = offsets.numel() - 1
     return _gemm("averis_gemm_grouped", a, mean, b, out_dtype, out, nseg=nseg, offsets=offsets,
                  ws=ws)
+
+
+def averis_residual_t_quant(a, mu, residual, seed=0, rnd=SR):
+    """Q4((a - 1 mu)^T) (cols x rows, blocks along the tokens, SR stream 3);
+    mu and residual are the fp32 mean and the residual tensor
+    averis_split_quant returned for the same a."""
+    rows, cols = a.shape
+    out = NVFP4.empty(cols, rows, 1, a.device)
+    o = out.c()
+    _check("averis_residual_t_quant", lib().averis_residual_t_quant(
+        a.data_ptr(), _dtype_code(a), rows, cols, _lda(a), mu.data_ptr(),
+        residual.tscale.data_ptr(), seed, rnd, ctypes.byref(o), _stream()))
+    return out
+
+
+def averis_gemm_wgrad(xt, dt, mu_x, mu_d, out_dtype=torch.float32, out=None, ws=None):
+    """dW = deq(xt) deq(dt)^T + l mu_x mu_d^T (m x n) from the transposed
+    residuals xt (m x l) and dt (n x l) and the fp32 means."""
+    m, n, l = xt.rows, dt.rows, xt.cols
+    c = _out(m, n, out_dtype, xt.codes.device, out)
+    need = workspace_bytes(OP_WGRAD, m, l, n)
+    ws = ws if ws is not None else _workspace(need, xt.codes.device)
+    cx, cd = xt.c(), dt.c()
+    _check("averis_gemm_wgrad", lib().averis_gemm_wgrad(
+        ctypes.byref(cx), ctypes.byref(cd), mu_x.data_ptr(), mu_d.data_ptr(), c.data_ptr(),
+        _dtype_code(c), c.stride(0), ws.data_ptr(), ws.numel(), _stream()))
+    return c

@@ -25,7 +25,7 @@ inline bool dtype_ok(averis_dtype_t d) { return d == AVERIS_F32 || d == AVERIS_B
 averis_status_t check_tensor(const averis_nvfp4_t* t, int64_t rows, int64_t cols) {
   if (!t || !t->tscale) return AVERIS_E_NULL;
   if (t->rows != rows || t->cols != cols) return AVERIS_E_SHAPE;
-  if (rows > 0 && (!t->codes || !t->scales)) return AVERIS_E_NULL;
+  if (rows > 0 && cols > 0 && (!t->codes || !t->scales)) return AVERIS_E_NULL;
   if (!aligned(t->codes, 16) || !aligned(t->scales, 16) || !aligned(t->tscale, 4))
     return AVERIS_E_ALIGN;
   return AVERIS_OK;
@@ -93,6 +93,11 @@ size_t batched_ws_bytes(int64_t, int64_t, int batch) {
 extern "C" {
 
 size_t averis_workspace_bytes(averis_op_t op, int64_t rows, int64_t cols, int64_t n, int64_t nseg) {
+  if (op == AVERIS_OP_WGRAD) {
+    // cols = l may be 0 (no tokens)
+    if (rows < 0 || cols < 0 || cols % 16 != 0 || n < 0) return 0;
+    return wgrad_ws_bytes(rows, n, cols);
+  }
   if (rows < 0 || cols <= 0 || cols % 16 != 0 || nseg < 0 || nseg > kMaxSeg) return 0;
   switch (op) {
     case AVERIS_OP_SPLIT_QUANT:
@@ -105,6 +110,8 @@ size_t averis_workspace_bytes(averis_op_t op, int64_t rows, int64_t cols, int64_
     case AVERIS_OP_GEMM:
       if (n < 0) return 0;
       return gemm_ws_bytes(n, cols, (int)nseg);
+    case AVERIS_OP_WGRAD:
+      break;
   }
   return 0;
 }
@@ -328,6 +335,48 @@ averis_status_t averis_gemm_grouped(const averis_nvfp4_t* a, const averis_nvfp4_
   if (!seg_offsets) return AVERIS_E_NULL;
   if (!aligned(seg_offsets, 8)) return AVERIS_E_ALIGN;
   return gemm_common(a, mean, b, seg_offsets, nseg, c, cdtype, ldc, ws, ws_bytes, stream);
+}
+
+averis_status_t averis_residual_t_quant(const void* a, averis_dtype_t dtype, int64_t rows,
+                                        int64_t cols, int64_t lda, const float* mu,
+                                        const float* residual_tscale, uint64_t seed,
+                                        averis_round_t rnd, const averis_nvfp4_t* out_t,
+                                        hipStream_t stream) {
+  averis_status_t s = check_input(a, dtype, rows, cols, lda, cols);
+  if (s != AVERIS_OK) return s;
+  if (rows % 16 != 0) return AVERIS_E_SHAPE;
+  if (rnd != AVERIS_RN && rnd != AVERIS_SR) return AVERIS_E_ARG;
+  if (!mu || !residual_tscale) return AVERIS_E_NULL;
+  if (!aligned(mu, 16) || !aligned(residual_tscale, 4)) return AVERIS_E_ALIGN;
+  if ((s = check_tensor(out_t, cols, rows)) != AVERIS_OK) return s;
+  const QuantOut o{out_t->codes, out_t->scales, out_t->tscale};
+  return hip_status(launch_quant_rt(a, dtype == AVERIS_BF16, rows, cols, lda, mu, residual_tscale,
+                                    rnd == AVERIS_SR, seed, 3u, o, stream));
+}
+
+averis_status_t averis_gemm_wgrad(const averis_nvfp4_t* xt, const averis_nvfp4_t* dt,
+                                  const float* mu_x, const float* mu_d, void* dw,
+                                  averis_dtype_t dwdtype, int64_t lddw, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  if (!xt || !dt || !mu_x || !mu_d) return AVERIS_E_NULL;
+  if (!dtype_ok(dwdtype)) return AVERIS_E_DTYPE;
+  const int64_t m = xt->rows, n = dt->rows, l = xt->cols;
+  if (m < 0 || n < 0 || l < 0 || l % 16 != 0 || dt->cols != l) return AVERIS_E_SHAPE;
+  if (m % 16 != 0 || n % 16 != 0) return AVERIS_E_SHAPE;
+  averis_status_t s;
+  if ((s = check_tensor(xt, m, l)) != AVERIS_OK) return s;
+  if ((s = check_tensor(dt, n, l)) != AVERIS_OK) return s;
+  if (!aligned(mu_x, 16) || !aligned(mu_d, 16)) return AVERIS_E_ALIGN;
+  if (lddw < n) return AVERIS_E_SHAPE;
+  if (m > 0 && n > 0 && !dw) return AVERIS_E_NULL;
+  if (!aligned(dw, elem_size(dwdtype))) return AVERIS_E_ALIGN;
+  const size_t need = wgrad_ws_bytes(m, n, l);
+  if (need && (!ws || ws_bytes < need)) return AVERIS_E_WORKSPACE;
+  if (ws && !aligned(ws, 256)) return AVERIS_E_ALIGN;
+  const QOperand qx{xt->codes, xt->scales, xt->tscale};
+  const QOperand qd{dt->codes, dt->scales, dt->tscale};
+  return hip_status(launch_wgrad(qx, qd, mu_x, mu_d, m, n, l, dw, dwdtype == AVERIS_BF16, lddw, ws,
+                                 stream));
 }
 
 }  // extern "C"

@@ -703,4 +703,105 @@ hipError_t launch_gemm(const QOperand& a, const QOperand* mean, const QOperand& 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// wgrad: dW = deq(Q4(X_R^T)) deq(Q4(D_R^T))^T + l mu_X mu_D^T.  Its output
+// (m x n) is short and wide next to its contraction over the tokens, so the
+// product runs split-K into fp32 partials and one pass sums them in split
+// order (the same bits on every run) and adds the outer product of the means.
+// ---------------------------------------------------------------------------
+
+// splits of the token axis: enough 256 x 192 tiles for one round over the
+// 256 CUs, each split a multiple of 64 tokens and at least 512 long
+int wgrad_splits(int64_t m, int64_t n, int64_t l) {
+  if (m <= 0 || n <= 0 || l % 64 != 0) return 1;
+  const int64_t tiles = ((m + 255) / 256) * ((n + 191) / 192);
+  int s = 1;
+  while (s < 8 && tiles * 2 * s <= 256 && l % (2 * s * 64) == 0 && l / (2 * s) >= 512) s *= 2;
+  return s;
+}
+
+size_t wgrad_ws_bytes(int64_t m, int64_t n, int64_t l) {
+  if (m <= 0 || n <= 0) return 0;
+  return ((size_t)wgrad_splits(m, n, l) * (size_t)m * (size_t)n * 4 + 255) & ~(size_t)255;
+}
+
+__global__ __launch_bounds__(256) void k_fill_zero(float* p, int64_t quads) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q < quads) *reinterpret_cast<f32x4_t*>(p + 4 * q) = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+// out[i][j] = sum_z part[z][i][j] (in z order) + (l mu_x[i]) mu_d[j]; four
+// consecutive outputs per thread (n % 16 == 0)
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void k_wgrad_reduce(const float* __restrict__ part, int splits,
+                                                      int64_t m, int64_t n,
+                                                      const float* __restrict__ mu_x,
+                                                      const float* __restrict__ mu_d, float l,
+                                                      void* out, int64_t ldo) {
+  const int64_t nq = n >> 2;
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= m * nq) return;
+  const int64_t i = q / nq, j = (q - i * nq) * 4;
+  const int64_t mn = m * n;
+  f32x4_t acc = *reinterpret_cast<const f32x4_t*>(part + i * n + j);
+  for (int z = 1; z < splits; ++z) {
+    const f32x4_t p = *reinterpret_cast<const f32x4_t*>(part + z * mn + i * n + j);
+    acc += p;
+  }
+  const float li = l * mu_x[i];
+  const f32x4_t md = *reinterpret_cast<const f32x4_t*>(mu_d + j);
+  float y[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = __builtin_fmaf(li, md[e], acc[e]);
+  if constexpr (OUT_BF16) {
+    uint16_t* o = static_cast<uint16_t*>(out) + i * ldo + j;
+    if ((ldo & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 7) == 0) {
+      u32x2_t v = {bf16x2_rne(y[0], y[1]), bf16x2_rne(y[2], y[3])};
+      *reinterpret_cast<u32x2_t*>(o) = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (uint16_t)bf16x2_rne(y[e], 0.0f);
+    }
+  } else {
+    float* o = static_cast<float*>(out) + i * ldo + j;
+    if ((ldo & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+      f32x4_t v = {y[0], y[1], y[2], y[3]};
+      *reinterpret_cast<f32x4_t*>(o) = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = y[e];
+    }
+  }
+}
+
+hipError_t launch_wgrad(const QOperand& xt, const QOperand& dt, const float* mu_x,
+                        const float* mu_d, int64_t m, int64_t n, int64_t l, void* out, bool bf16,
+                        int64_t ldo, void* ws, hipStream_t st) {
+  if (m == 0 || n == 0) return hipGetLastError();
+  float* part = static_cast<float*>(ws);
+  const int splits = wgrad_splits(m, n, l);
+  hipError_t e;
+  if (l == 0) {
+    // no tokens: the product is zero; the reduce of one zero partial adds
+    // the (zero-weighted) mean term
+    e = hipSuccess;
+  } else if (splits > 1) {
+    e = launch_gemm_ws_splitk(xt, dt, m, n, l, splits, part, st);
+  } else {
+    e = launch_gemm(xt, nullptr, dt, m, n, l, nullptr, 1, part, false, n, nullptr, st);
+  }
+  if (e != hipSuccess) return e;
+  const int64_t quads = m * (n >> 2);
+  const dim3 g((unsigned)((quads + 255) / 256));
+  if (l == 0) {
+    // one partial of zeros, written by a kernel (no memset in a captured graph)
+    k_fill_zero<<<g, 256, 0, st>>>(part, quads);
+  }
+  if (bf16)
+    k_wgrad_reduce<true><<<g, 256, 0, st>>>(part, splits, m, n, mu_x, mu_d, (float)l, out, ldo);
+  else
+    k_wgrad_reduce<false><<<g, 256, 0, st>>>(part, splits, m, n, mu_x, mu_d, (float)l, out, ldo);
+  return hipGetLastError();
+}
+
 }  // namespace averis

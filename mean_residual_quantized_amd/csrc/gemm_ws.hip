@@ -64,7 +64,8 @@ __device__ __forceinline__ void ws_unroll(F&& f) {
 template <int TM, int TN, int PF, bool OUT_BF16, bool HAS_MEAN, bool BQ, bool SG>
 __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOperand M, int64_t m,
                                                     int64_t n, int64_t k, const int64_t* offs,
-                                                    int nseg, void* c, int64_t ldc) {
+                                                    int nseg, void* c, int64_t ldc, int64_t kld,
+                                                    int64_t c_split) {
   constexpr int BM = 64 * TM, BN = 64 * TN;
   // 32-element chunks dequantized per stage: A rows (and B rows unless BQ)
   constexpr int NCH = BQ ? 2 * BM : 2 * (BM + BN);
@@ -93,9 +94,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
   const int seg = sr.seg;
   const int64_t m0 = sr.r0, m_end = sr.r1;
   const int64_t n0 = tile_x * BN;
-  const int64_t kh = k >> 1, kb = k >> 4;
-  const uint8_t* bcodes = B.codes + (offs ? (int64_t)seg * n * kh : 0);
-  const uint8_t* bscales = B.scales + (offs ? (int64_t)seg * n * kb : 0);
+  // split-K (gridDim.z > 1): split z contracts k = kld / gridDim.z columns
+  // starting at z k of operands whose rows hold kld columns, and writes its
+  // partial product to c + z c_split
+  const int64_t kh = kld >> 1, kb = kld >> 4;
+  const int64_t kz = (int64_t)blockIdx.z * k;
+  c = static_cast<char*>(c) + (int64_t)blockIdx.z * c_split * (OUT_BF16 ? 2 : 4);
+  const uint8_t* bcodes = B.codes + (offs ? (int64_t)seg * n * kh : 0) + (kz >> 1);
+  const uint8_t* bscales = B.scales + (offs ? (int64_t)seg * n * kb : 0) + (kz >> 4);
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -147,8 +153,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
     // clamped to the last valid row: their products only reach outputs that
     // are never stored.  Byte offsets are 32-bit; each stage adds a uniform
     // k offset.
-    const uint8_t* a_c = A.codes + m0 * kh;
-    const uint8_t* a_s = A.scales + m0 * kb;
+    const uint8_t* a_c = A.codes + m0 * kh + (kz >> 1);
+    const uint8_t* a_s = A.scales + m0 * kb + (kz >> 4);
     const uint8_t* b_c = bcodes + n0 * kh;
     const uint8_t* b_s = bscales + n0 * kb;
     // W2 (with SG): one load instruction covers 64 contiguous code bytes of a
@@ -629,7 +635,7 @@ constexpr size_t kWsLdsLimit = 160 * 1024 - 512;
 template <int TM, int TN, bool OB, bool HM, bool BQ, bool SG>
 hipError_t launch_ws(const QOperand& a, const QOperand* mean, const QOperand& b, int64_t m, int64_t n,
                      int64_t k, const int64_t* offs, int nseg, void* c, int64_t ldc,
-                     hipStream_t st) {
+                     hipStream_t st, int splits = 1, int64_t c_split = 0) {
   constexpr int PF = SG ? 4 : 2, BM = 64 * TM, BN = 64 * TN;
   const size_t lds = ws_lds_bytes(TM, TN, BQ) + (HM ? (size_t)k * 2 : 0);
   static bool attr_set = false;   // per instantiation; the attribute is idempotent
@@ -640,9 +646,10 @@ hipError_t launch_ws(const QOperand& a, const QOperand* mean, const QOperand& b,
     attr_set = true;
   }
   const int64_t tiles_m = chunk_upper_bound(m, offs ? nseg : 1, BM);
-  dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)tiles_m);
+  dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)tiles_m, (unsigned)splits);
   const QOperand mu = mean ? *mean : QOperand{nullptr, nullptr, nullptr};
-  k_gemm_ws<TM, TN, PF, OB, HM, BQ, SG><<<grid, 512, lds, st>>>(a, b, mu, m, n, k, offs, nseg, c, ldc);
+  k_gemm_ws<TM, TN, PF, OB, HM, BQ, SG><<<grid, 512, lds, st>>>(a, b, mu, m, n, k / splits, offs,
+                                                                nseg, c, ldc, k, c_split);
   return hipGetLastError();
 }
 
@@ -703,6 +710,19 @@ int ws_pick(int64_t m, int64_t n, int64_t k, int nseg_eff, bool has_mean) {
     }
   }
   return best;
+}
+
+// Split-K product for short, wide outputs (the wgrad product): fp32
+// partials part[z] = deq(A[:, z k/S ..]) deq(B[:, z k/S ..])^T, each m x n
+// with row stride n; k / splits a multiple of 64.  256 x 192 tiles.
+hipError_t launch_gemm_ws_splitk(const QOperand& a, const QOperand& b, int64_t m, int64_t n,
+                                 int64_t k, int splits, float* part, hipStream_t st) {
+  if (splits < 1 || k % splits != 0 || (k / splits) % kWsBK != 0) return hipErrorInvalidValue;
+  if ((k / splits) % 256 == 0)
+    return launch_ws<4, 3, false, false, false, true>(a, nullptr, b, m, n, k, nullptr, 1, part, n,
+                                                      st, splits, m * n);
+  return launch_ws<4, 3, false, false, false, false>(a, nullptr, b, m, n, k, nullptr, 1, part, n,
+                                                     st, splits, m * n);
 }
 
 hipError_t launch_gemm_ws(int variant, const QOperand& a, const QOperand* mean, const QOperand& b,

@@ -54,6 +54,12 @@ hipError_t launch_quant_pair(const void* a, bool bf16, int batch, int64_t rows, 
                              uint32_t stream_id, const QuantOut& out, const QuantOut& out_t,
                              float* part, hipStream_t st);
 
+// Q4((a - 1 mu)^T) (cols x rows, blocks along the rows) with the residual's
+// tensor scale tscale_in (2 floats); rows % 16 == 0, cols % 16 == 0.
+hipError_t launch_quant_rt(const void* a, bool bf16, int64_t rows, int64_t cols, int64_t lda,
+                           const float* mu, const float* tscale_in, bool sr, uint64_t seed,
+                           uint32_t stream_id, const QuantOut& out, hipStream_t st);
+
 // A quantized GEMM operand as the kernels see it.
 struct QOperand {
   const uint8_t* codes;
@@ -78,5 +84,17 @@ int ws_pick(int64_t m, int64_t n, int64_t k, int nseg_eff, bool has_mean);
 hipError_t launch_gemm_ws(int variant, const QOperand& a, const QOperand* mean, const QOperand& b,
                           int64_t m, int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
                           bool c_bf16, int64_t ldc, hipStream_t st);
+
+// Split-K product into fp32 partials part[z] (m x n each, row stride n).
+hipError_t launch_gemm_ws_splitk(const QOperand& a, const QOperand& b, int64_t m, int64_t n,
+                                 int64_t k, int splits, float* part, hipStream_t st);
+
+// wgrad: out (m x n, row stride ldo) = deq(xt) deq(dt)^T + l mu_x mu_d^T with
+// xt m x l and dt n x l (blocks along the tokens); m, n % 16 == 0.
+int wgrad_splits(int64_t m, int64_t n, int64_t l);
+size_t wgrad_ws_bytes(int64_t m, int64_t n, int64_t l);
+hipError_t launch_wgrad(const QOperand& xt, const QOperand& dt, const float* mu_x,
+                        const float* mu_d, int64_t m, int64_t n, int64_t l, void* out, bool bf16,
+                        int64_t ldo, void* ws, hipStream_t st);
 
 }  // namespace averis

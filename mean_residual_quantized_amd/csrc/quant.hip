@@ -867,6 +867,82 @@ __global__ __launch_bounds__(256) void k_pair(const T* __restrict__ a, int64_t r
 }
 
 // ---------------------------------------------------------------------------
+// transposed residual of the wgrad product: Q4((a - 1 mu)^T), cols x rows,
+// 16-blocks along the rows (tokens).  A workgroup stages a 128-token x
+// 64-column tile of fp32 residuals in LDS (full 128-byte row reads of bf16
+// input) and quantizes 8 token blocks of each of its 64 columns, so each
+// output row gets 64 contiguous code bytes.  The tensor scale is the
+// residual's, read from the split's output (the same set of values).
+// ---------------------------------------------------------------------------
+constexpr int kRtRows = 128;
+constexpr int kRtCols = 64;
+constexpr int kRtLd = kRtCols + 4;   // padded LDS row (floats)
+
+template <typename T, bool SR>
+__global__ __launch_bounds__(256) void k_quant_rt(const T* __restrict__ a, int64_t rows,
+                                                  int64_t cols, int64_t lda,
+                                                  const float* __restrict__ mu,
+                                                  const float* __restrict__ tsc, uint64_t seed,
+                                                  uint32_t stream, QuantOut out) {
+  constexpr int VE = 16 / (int)sizeof(T);
+  constexpr int NCH = kRtCols / VE;              // 16-byte chunks per tile row
+  constexpr int PER = kRtRows * NCH / 256;       // chunks per thread
+  __shared__ float tile[kRtRows][kRtLd];
+  const int64_t c0 = (int64_t)blockIdx.x * kRtCols, r0 = (int64_t)blockIdx.y * kRtRows;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = tid + 256 * i;
+    const int lr = idx / NCH, ch = idx % NCH;
+    const int64_t r = r0 + lr, c = c0 + (int64_t)ch * VE;
+    // cols % 16 == 0, so a chunk lies wholly inside or outside the tensor
+    if (r < rows && c < cols) {
+      const uint4 w = *reinterpret_cast<const uint4*>(a + r * lda + c);
+      float* dst = &tile[lr][ch * VE];
+      const float4 m0 = *reinterpret_cast<const float4*>(mu + c);
+      if constexpr (sizeof(T) == 2) {
+        const float4 m1 = *reinterpret_cast<const float4*>(mu + c + 4);
+        dst[0] = bf16_lo(w.x) - m0.x;
+        dst[1] = bf16_hi(w.x) - m0.y;
+        dst[2] = bf16_lo(w.y) - m0.z;
+        dst[3] = bf16_hi(w.y) - m0.w;
+        dst[4] = bf16_lo(w.z) - m1.x;
+        dst[5] = bf16_hi(w.z) - m1.y;
+        dst[6] = bf16_lo(w.w) - m1.z;
+        dst[7] = bf16_hi(w.w) - m1.w;
+      } else {
+        dst[0] = __uint_as_float(w.x) - m0.x;
+        dst[1] = __uint_as_float(w.y) - m0.y;
+        dst[2] = __uint_as_float(w.z) - m0.z;
+        dst[3] = __uint_as_float(w.w) - m0.w;
+      }
+    }
+  }
+  __syncthreads();
+  const float s_enc = tsc[0];
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
+    out.tscale[0] = tsc[0];
+    out.tscale[1] = tsc[1];
+  }
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  const int cl = tid & 63;
+  const int64_t c = c0 + cl;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int q = (tid >> 6) + 4 * h;   // token block of the tile
+    const int64_t r = r0 + 16 * q;
+    if (c < cols && r < rows) {         // rows % 16 == 0: whole blocks
+      float v[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = tile[16 * q + k][cl];
+      quant_block16<SR>(v, s_enc, (uint64_t)c * (uint64_t)rows + (uint64_t)r, k0, k1, stream,
+                        out.codes + c * (rows >> 1) + (r >> 1),
+                        out.scales + c * (rows >> 4) + (r >> 4));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 template <typename T>
@@ -1003,6 +1079,29 @@ hipError_t launch_quant_pair(const void* a, bool bf16, int batch, int64_t rows, 
                               part, st);
   return run_pair<float>(a, batch, rows, cols, lda, bstride, sr, seed, stream_id, out, out_t, part,
                          st);
+}
+
+template <typename T>
+static hipError_t run_rt(const void* a_, int64_t rows, int64_t cols, int64_t lda, const float* mu,
+                         const float* tsc, bool sr, uint64_t seed, uint32_t stream_id,
+                         const QuantOut& out, hipStream_t st) {
+  const T* a = static_cast<const T*>(a_);
+  // at least one workgroup: block (0, 0) also publishes the tensor scale
+  // when there are no tokens
+  const int64_t gy = (rows + kRtRows - 1) / kRtRows;
+  const dim3 g((unsigned)((cols + kRtCols - 1) / kRtCols), (unsigned)(gy > 0 ? gy : 1));
+  if (sr)
+    k_quant_rt<T, true><<<g, 256, 0, st>>>(a, rows, cols, lda, mu, tsc, seed, stream_id, out);
+  else
+    k_quant_rt<T, false><<<g, 256, 0, st>>>(a, rows, cols, lda, mu, tsc, seed, stream_id, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rt(const void* a, bool bf16, int64_t rows, int64_t cols, int64_t lda,
+                           const float* mu, const float* tscale_in, bool sr, uint64_t seed,
+                           uint32_t stream_id, const QuantOut& out, hipStream_t st) {
+  if (bf16) return run_rt<uint16_t>(a, rows, cols, lda, mu, tscale_in, sr, seed, stream_id, out, st);
+  return run_rt<float>(a, rows, cols, lda, mu, tscale_in, sr, seed, stream_id, out, st);
 }
 
 }  // namespace averis

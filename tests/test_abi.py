@@ -160,3 +160,39 @@ def test_quant_pair_rejections(L):
     assert qp(out=nv(64, 128)) == 2
     assert qp(ws=None) == 5
     assert qp(wsb=64) == 5
+
+
+def test_wgrad_rejections(L):
+    # transposed residual quant: out_t is cols x rows, rows (tokens) % 16
+    out_t = nv(128, 64)
+    rt = lambda a=P, dt=av.BF16, rows=64, cols=128, lda=128, mu=P, tsc=P, rnd=av.SR, out=out_t: \
+        L.averis_residual_t_quant(a, dt, rows, cols, lda, mu, tsc, 0, rnd, ctypes.byref(out), None)
+    assert rt(rows=40, out=nv(128, 40)) == 2
+    assert rt(cols=24, lda=24) == 2
+    assert rt(out=nv(64, 128)) == 2                       # not transposed
+    assert rt(mu=None) == 1
+    assert rt(tsc=None) == 1
+    assert rt(mu=P + 4) == 4                              # 16-byte vector loads of mu
+    assert rt(rnd=2) == 6
+    assert rt(dt=7) == 3
+    assert rt(a=None) == 1
+    # wgrad GEMM: xt m x l, dt n x l, means, output m x n
+    xt, dtq = nv(64, 256), nv(96, 256)
+    wg = lambda xt=xt, dtq=dtq, mx=P, md=P, c=P, dt=av.F32, ld=96, ws=P, wsb=1 << 30: \
+        L.averis_gemm_wgrad(ctypes.byref(xt), ctypes.byref(dtq), mx, md, c, dt, ld, ws, wsb, None)
+    assert wg(dtq=nv(96, 128)) == 2                       # token counts differ
+    assert wg(xt=nv(64, 200)) == 2                        # l % 16
+    assert wg(dtq=nv(90, 256)) == 2                       # n % 16
+    assert wg(mx=None) == 1
+    assert wg(md=P + 8) == 4
+    assert wg(ld=64) == 2
+    assert wg(c=None) == 1
+    assert wg(dt=3) == 3
+    assert wg(ws=None) == 5
+    assert wg(wsb=1024) == 5
+    assert wg(ws=P + 64) == 4
+    wb = av.workspace_bytes
+    # one fp32 partial per split of the tokens; 64 tiles of 256 x 192 take 4
+    assert wb(av.OP_WGRAD, 1024, 8192, 3072) == 4 * 1024 * 3072 * 4
+    assert wb(av.OP_WGRAD, 64, 1008, 96) == 64 * 96 * 4  # l % 64 != 0: one partial
+    assert wb(av.OP_WGRAD, 64, 0, 96) == 64 * 96 * 4
