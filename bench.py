@@ -209,6 +209,62 @@ def timed(xs, ds, w, ws, steps, warmup, vanilla):
     return dict(eager=eager_ms, graph=graph_ms, queued=queued_ms), t
 
 
+def time_wgrad(xs, ds, ws, steps, warmup):
+    """The wgrad pieces, queued behind a spin kernel and timed per call by
+    events on the launch stream, rotating through the input copies: the
+    transposed residual quants of X and D (their means and residual tensor
+    scales come from the splits the forward and dgrad passes run) and the
+    wgrad product dW = deq(xt) deq(dt)^T + l mu_X mu_D^T (fp32 out)."""
+    l, m = xs[0].shape
+    n = ds[0].shape[1]
+    xr, _, mx = av.averis_split_quant(xs[0], seed=0, ws=ws["sq_x"])
+    dr, _, md = av.averis_split_quant(ds[0], seed=1, ws=ws["sq_d"])
+    xt = av.NVFP4.empty(m, l, 1, xs[0].device)
+    dt = av.NVFP4.empty(n, l, 1, xs[0].device)
+    dw = torch.empty((m, n), dtype=torch.float32, device=xs[0].device)
+    wws = torch.empty(av.workspace_bytes(av.OP_WGRAD, m, l, n), dtype=torch.uint8,
+                      device=xs[0].device)
+
+    def one(i, t):
+        def tic(k):
+            if t:
+                t.start(k)
+
+        def toc(k):
+            if t:
+                t.stop(k)
+        tic("rt_x")
+        av.averis_residual_t_quant(xs[i % len(xs)], mx, xr, seed=0, out=xt)
+        toc("rt_x")
+        tic("rt_d")
+        av.averis_residual_t_quant(ds[i % len(ds)], md, dr, seed=1, out=dt)
+        toc("rt_d")
+        tic("gemm_wgrad")
+        av.averis_gemm_wgrad(xt, dt, mx, md, out=dw, ws=wws)
+        toc("gemm_wgrad")
+
+    for i in range(warmup):
+        one(i, None)
+    torch.cuda.synchronize()
+    t = Timer()
+    hold_gpu(5.0 + 0.5 * steps)
+    for i in range(steps):
+        one(i, t)
+    torch.cuda.synchronize()
+    med = lambda v: float(np.median(v))
+    ms = {k: med(t.ms(k)) for k in ("rt_x", "rt_d", "gemm_wgrad")}
+    rt_bytes = lambda rows, cols: rows * cols * (2 + 0.5 + 1 / 16)
+    flops = 2.0 * l * m * n
+    return dict(
+        ms=ms,
+        rt_gbs={"x": rt_bytes(l, m) / (ms["rt_x"] * 1e-3) / 1e9,
+                "d": rt_bytes(l, n) / (ms["rt_d"] * 1e-3) / 1e9},
+        gemm_tflops=flops / (ms["gemm_wgrad"] * 1e-3) / 1e12,
+        splits_of_tokens=int(av.workspace_bytes(av.OP_WGRAD, m, l, n) // (m * n * 4)),
+        note="dW (m x n) = deq(Q4(X_R^T)) deq(Q4(D_R^T))^T + l mu_X mu_D^T, fp32 out; "
+             "gemm_wgrad covers the split-K GEMM and the reduce that adds the outer product")
+
+
 def cpu_baseline(cfg_rows, m, n):
     """The oracle as it stands on a bounded sample: cfg_rows tokens of the
     same workload (split-quant of X and D, both weight copies, the float64
@@ -252,10 +308,13 @@ def traffic_probe(args):
     torch.cuda.synchronize()
     for _ in range(3):
         wt, wd = av.averis_quant_pair(w, rnd=av.RN)
-        xr, xm, _ = av.averis_split_quant(x, seed=0)
+        xr, xm, mx = av.averis_split_quant(x, seed=0)
         av.averis_gemm_fwd(xr, xm, wt, out_dtype=torch.bfloat16)
-        dr, dm, _ = av.averis_split_quant(d, seed=1)
+        dr, dm, md = av.averis_split_quant(d, seed=1)
         av.averis_gemm_dgrad(dr, dm, wd, out_dtype=torch.bfloat16)
+        xt = av.averis_residual_t_quant(x, mx, xr, seed=0)
+        dt = av.averis_residual_t_quant(d, md, dr, seed=1)
+        av.averis_gemm_wgrad(xt, dt, mx, md)
     torch.cuda.synchronize()
     print("traffic probe done: copy %d bytes" % COPY_BYTES, file=sys.stderr)
 
@@ -326,6 +385,8 @@ def main():
     log("bench: averis %s, vanilla %s (ms/step)" % (
         " ".join("%s %.4f" % kv for kv in ta_ms.items()),
         " ".join("%s %.4f" % kv for kv in tv_ms.items())))
+    log("bench: wgrad pieces")
+    wg = time_wgrad(xs, ds, ws, args.steps, args.warmup)
     # the headline is the device's step time (launches queued ahead of it)
     ms_a, ms_v = ta_ms["queued"], tv_ms["queued"]
 
@@ -401,6 +462,7 @@ def main():
                               "eager": "one Python call per op, host clock",
                               "graph": "one HIP graph per step, replayed, host clock"},
         "overhead_vs_vanilla": overhead,
+        "wgrad": wg,
         "pages_overhead_context": "2.20% end-to-end over vanilla NVFP4 (hardware not stated)",
     }
     if not args.no_cpu_baseline:

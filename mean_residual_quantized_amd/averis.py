@@ -301,12 +301,12 @@ def averis_gemm_grouped(a, mean, b, offsets, out_dtype=torch.float32, out=None, 
                  ws=ws)
 
 
-def averis_residual_t_quant(a, mu, residual, seed=0, rnd=SR):
+def averis_residual_t_quant(a, mu, residual, seed=0, rnd=SR, out=None):
     """Q4((a - 1 mu)^T) (cols x rows, blocks along the tokens, SR stream 3);
     mu and residual are the fp32 mean and the residual tensor
     averis_split_quant returned for the same a."""
     rows, cols = a.shape
-    out = NVFP4.empty(cols, rows, 1, a.device)
+    out = out if out is not None else NVFP4.empty(cols, rows, 1, a.device)
     o = out.c()
     _check("averis_residual_t_quant", lib().averis_residual_t_quant(
         a.data_ptr(), _dtype_code(a), rows, cols, _lda(a), mu.data_ptr(),

@@ -869,14 +869,15 @@ __global__ __launch_bounds__(256) void k_pair(const T* __restrict__ a, int64_t r
 // ---------------------------------------------------------------------------
 // transposed residual of the wgrad product: Q4((a - 1 mu)^T), cols x rows,
 // 16-blocks along the rows (tokens).  A workgroup stages a 128-token x
-// 64-column tile of fp32 residuals in LDS (full 128-byte row reads of bf16
-// input) and quantizes 8 token blocks of each of its 64 columns, so each
-// output row gets 64 contiguous code bytes.  The tensor scale is the
-// residual's, read from the split's output (the same set of values).
+// 64-column tile of the input in LDS as loaded (full 128-byte row reads of
+// bf16 input; 18 KB, so eight workgroups fit a CU) and each thread
+// quantizes one token block of two neighbouring columns, forming the
+// residual fp32(a - mu) as it reads the tile.  Each output row gets 64
+// contiguous code bytes per workgroup.  The tensor scale is the residual's,
+// read from the split's output (the same set of values).
 // ---------------------------------------------------------------------------
 constexpr int kRtRows = 128;
 constexpr int kRtCols = 64;
-constexpr int kRtLd = kRtCols + 4;   // padded LDS row (floats)
 
 template <typename T, bool SR>
 __global__ __launch_bounds__(256) void k_quant_rt(const T* __restrict__ a, int64_t rows,
@@ -887,7 +888,8 @@ __global__ __launch_bounds__(256) void k_quant_rt(const T* __restrict__ a, int64
   constexpr int VE = 16 / (int)sizeof(T);
   constexpr int NCH = kRtCols / VE;              // 16-byte chunks per tile row
   constexpr int PER = kRtRows * NCH / 256;       // chunks per thread
-  __shared__ float tile[kRtRows][kRtLd];
+  constexpr int LD = kRtCols + VE;               // padded LDS row (elements, 16-byte aligned)
+  __shared__ __attribute__((aligned(16))) T tile[kRtRows][LD];
   const int64_t c0 = (int64_t)blockIdx.x * kRtCols, r0 = (int64_t)blockIdx.y * kRtRows;
   const int tid = threadIdx.x;
 #pragma unroll
@@ -896,27 +898,8 @@ __global__ __launch_bounds__(256) void k_quant_rt(const T* __restrict__ a, int64
     const int lr = idx / NCH, ch = idx % NCH;
     const int64_t r = r0 + lr, c = c0 + (int64_t)ch * VE;
     // cols % 16 == 0, so a chunk lies wholly inside or outside the tensor
-    if (r < rows && c < cols) {
-      const uint4 w = *reinterpret_cast<const uint4*>(a + r * lda + c);
-      float* dst = &tile[lr][ch * VE];
-      const float4 m0 = *reinterpret_cast<const float4*>(mu + c);
-      if constexpr (sizeof(T) == 2) {
-        const float4 m1 = *reinterpret_cast<const float4*>(mu + c + 4);
-        dst[0] = bf16_lo(w.x) - m0.x;
-        dst[1] = bf16_hi(w.x) - m0.y;
-        dst[2] = bf16_lo(w.y) - m0.z;
-        dst[3] = bf16_hi(w.y) - m0.w;
-        dst[4] = bf16_lo(w.z) - m1.x;
-        dst[5] = bf16_hi(w.z) - m1.y;
-        dst[6] = bf16_lo(w.w) - m1.z;
-        dst[7] = bf16_hi(w.w) - m1.w;
-      } else {
-        dst[0] = __uint_as_float(w.x) - m0.x;
-        dst[1] = __uint_as_float(w.y) - m0.y;
-        dst[2] = __uint_as_float(w.z) - m0.z;
-        dst[3] = __uint_as_float(w.w) - m0.w;
-      }
-    }
+    if (r < rows && c < cols)
+      *reinterpret_cast<uint4*>(&tile[lr][ch * VE]) = *reinterpret_cast<const uint4*>(a + r * lda + c);
   }
   __syncthreads();
   const float s_enc = tsc[0];
@@ -925,19 +908,68 @@ __global__ __launch_bounds__(256) void k_quant_rt(const T* __restrict__ a, int64
     out.tscale[1] = tsc[1];
   }
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-  const int cl = tid & 63;
-  const int64_t c = c0 + cl;
+  const int cp = tid & 31, q = tid >> 5;     // column pair, token block of the tile
+  const int64_t c = c0 + 2 * cp, r = r0 + 16 * q;
+  const bool live = c < cols && r < rows;    // cols % 16, rows % 16 == 0: whole pairs, blocks
+  float v0[16], v1[16];
+  if (live) {
+    const float m0 = mu[c], m1 = mu[c + 1];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int q = (tid >> 6) + 4 * h;   // token block of the tile
-    const int64_t r = r0 + 16 * q;
-    if (c < cols && r < rows) {         // rows % 16 == 0: whole blocks
-      float v[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) v[k] = tile[16 * q + k][cl];
-      quant_block16<SR>(v, s_enc, (uint64_t)c * (uint64_t)rows + (uint64_t)r, k0, k1, stream,
-                        out.codes + c * (rows >> 1) + (r >> 1),
-                        out.scales + c * (rows >> 4) + (r >> 4));
+    for (int k = 0; k < 16; ++k) {
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(&tile[16 * q + k][2 * cp]);
+        v0[k] = bf16_lo(w) - m0;
+        v1[k] = bf16_hi(w) - m1;
+      } else {
+        const float2 w = *reinterpret_cast<const float2*>(&tile[16 * q + k][2 * cp]);
+        v0[k] = w.x - m0;
+        v1[k] = w.y - m1;
+      }
+    }
+  }
+  __syncthreads();   // the tile is read: its memory stages the output
+  // codes [64 columns][64 bytes + 16 pad] (16-byte aligned rows), then
+  // scales [64 columns][8 bytes]
+  constexpr int kCodeLd = 80;
+  uint8_t* cst = reinterpret_cast<uint8_t*>(&tile[0][0]);
+  uint8_t* sst = cst + kRtCols * kCodeLd;
+  static_assert(kRtCols * (kCodeLd + 8) <= (int)sizeof(tile), "output staging fits the tile");
+  static_assert(kCodeLd % 16 == 0, "16-byte aligned staged code rows");
+  if (live) {
+    quant_block16<SR>(v0, s_enc, (uint64_t)c * (uint64_t)rows + (uint64_t)r, k0, k1, stream,
+                      cst + (2 * cp) * kCodeLd + 8 * q, sst + (2 * cp) * 8 + q);
+    quant_block16<SR>(v1, s_enc, (uint64_t)(c + 1) * (uint64_t)rows + (uint64_t)r, k0, k1, stream,
+                      cst + (2 * cp + 1) * kCodeLd + 8 * q, sst + (2 * cp + 1) * 8 + q);
+  }
+  __syncthreads();
+  // each column's 64 code bytes of this tile go out in 16-byte pieces (four
+  // lanes to a column) when the rows keep them 16-byte aligned, else in
+  // 8-byte pieces; pieces past the last token are skipped
+  {
+    const int col = tid >> 2, pc = tid & 3;
+    const int64_t gc = c0 + col, t0 = r0 + 32 * pc;   // first token of the piece
+    if (gc < cols && t0 < rows) {
+      uint8_t* dst = out.codes + gc * (rows >> 1) + (t0 >> 1);
+      const uint8_t* src = cst + col * kCodeLd + 16 * pc;
+      if ((rows & 31) == 0) {
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+      } else {
+        *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+        if (t0 + 16 < rows)
+          *reinterpret_cast<uint2*>(dst + 8) = *reinterpret_cast<const uint2*>(src + 8);
+      }
+    }
+  }
+  if (tid < kRtCols) {
+    const int64_t gc = c0 + tid;
+    if (gc < cols && r0 < rows) {
+      uint8_t* dst = out.scales + gc * (rows >> 4) + (r0 >> 4);
+      const uint8_t* src = sst + tid * 8;
+      if ((rows & 127) == 0) {
+        *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+      } else {
+        for (int b = 0; b < 8 && r0 + 16 * b < rows; ++b) dst[b] = src[b];
+      }
     }
   }
 }

@@ -86,6 +86,7 @@ def test_config0_tiny():
     (2048, 320, 192),    # four splits of 512 tokens (256-wide scale groups)
     (1152, 256, 208),    # two splits of 576 tokens (per-stage scale loads), ragged n tile
     (16, 16, 16),        # one token block
+    (1056, 64, 48),      # token count a multiple of 32, not of 128: a partial tile of tokens
 ])
 def test_shapes_and_paths(l, m, n, dtype, rnd):
     check(mean_biased(l, m, l + m, dtype), mean_biased(l, n, l + n + 1, dtype), seed_x=l,
