@@ -44,6 +44,12 @@ arithmetic):
   contraction, so no FP4 GEMM needs its operands quantized; quantizing them
   (mean="q4", for comparison) gives one error per column that the factor l
   multiplies coherently instead of averaging it over the tokens.
+* mean-energy ratio ([Lighthouse] §7 recommends monitoring R = ||mu||_2 /
+  sqrt(E||X||^2 / N) and leaves E and N open): E||X||^2 is read as the sum of
+  squares of the whole operand, ||A||_F^2, and N as its row count l, so the
+  denominator is the mean squared row norm and 0 <= R <= 1, with R = 1 exactly
+  when every row equals mu.  Computed in float64 from exact sums (fsum); R = 0
+  when l = 0 or A = 0; per segment when grouped.
 * grouped (one mean and one tensor scale per expert segment): every step above
   is applied to each segment's rows; SR indices use the global row, the mean
   of segment s uses index s * cols + col; an empty segment has mean 0.
@@ -78,6 +84,20 @@ def column_mean(a):
 def residual(a, mu):
     """r = float32(a - mu) broadcast over rows."""
     return (np.asarray(a, dtype=np.float32) - np.asarray(mu, dtype=np.float32)[None, :]).astype(np.float32)
+
+
+def mean_energy_ratio(a):
+    """R = ||mu||_2 / sqrt(||A||_F^2 / l) for a float32 (l x m) array, float64,
+    with mu the exact column mean (fsum / l); 0 for l = 0 or A = 0."""
+    a = np.asarray(a, dtype=np.float32).astype(np.float64)
+    l = a.shape[0]
+    if l == 0:
+        return 0.0
+    mu = np.array([math.fsum(a[:, j]) / l for j in range(a.shape[1])], dtype=np.float64)
+    ssq = math.fsum((a * a).ravel())    # each square is exact in float64
+    if ssq == 0.0:
+        return 0.0
+    return math.sqrt(math.fsum(mu * mu) / (ssq / l))
 
 
 # --------------------------------------------------------------------------
@@ -278,6 +298,13 @@ def split_quant_grouped(a, offsets, rnd="sr", seed=0):
         m = quantize(mu[s][None, :], rnd, seed, stream=1, row0=s)
         means.append(m)
     return dict(mu=mu, residual=res, mean=means)
+
+
+def mean_energy_ratio_grouped(a, offsets):
+    """R of each segment's rows (0 for an empty segment)."""
+    a = np.asarray(a, dtype=np.float32)
+    return np.array([mean_energy_ratio(a[int(offsets[s]):int(offsets[s + 1])])
+                     for s in range(len(offsets) - 1)], dtype=np.float64)
 
 
 def vanilla_quant_grouped(a, offsets, rnd="sr", seed=0):

@@ -68,3 +68,35 @@ def test_graph_replays_match_eager(l, m, n, vanilla):
             assert torch.equal(a, b), "replay %d, output %d differs from the eager step" % (rep, i)
     del g
     torch.cuda.synchronize()
+
+
+def test_wgrad_graph_replays_match_eager():
+    # the transposed residual quants and the split-K wgrad (partials + reduce)
+    cfg = workloads.config1(l=2048, m=320, n=192)
+    x, d = cfg["x"].cuda(), cfg["d"].cuda()
+    xr, _, mx = av.averis_split_quant(x, seed=0)
+    dr, _, md = av.averis_split_quant(d, seed=1)
+
+    def wstep():
+        xt = av.averis_residual_t_quant(x, mx, xr, seed=0)
+        dt = av.averis_residual_t_quant(d, md, dr, seed=1)
+        dw = av.averis_gemm_wgrad(xt, dt, mx, md)
+        return [xt.codes, xt.scales, xt.tscale, dt.codes, dt.scales, dt.tscale, dw]
+
+    ref = [t.clone() for t in wstep()]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = wstep()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        av.averis_split_quant(workloads.config1(l=256, m=320, n=192)["x"].cuda(), seed=rep)
+        torch.cuda.synchronize()
+        for t in outs:
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, ref)):
+            assert torch.equal(a, b), "replay %d, output %d differs from the eager step" % (rep, i)
+    del g
+    torch.cuda.synchronize()
