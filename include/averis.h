@@ -131,6 +131,23 @@ averis_status_t averis_split_quant_grouped(const void* a, averis_dtype_t dtype, 
                                            const averis_nvfp4_t* mean, float* mean_f32, void* ws,
                                            size_t ws_bytes, hipStream_t stream);
 
+/* Split-quant with the mean-energy ratio ([Lighthouse] §7 recommends
+ * monitoring R = ||mu||_2 / sqrt(E||X||^2 / N) as a free stability signal).
+ * Reading: E||X||^2 is the operand's sum of squares ||A||_F^2 and N its row
+ * count l, so R = ||mu||_2 / sqrt(||A||_F^2 / l) in [0, 1] (1 when every row
+ * equals mu), computed from fp64 column sums and sums of squares gathered in
+ * the statistics pass; R = 0 for an empty segment or an all-zero one.
+ * seg_offsets = NULL with nseg = 1 is averis_split_quant, otherwise
+ * averis_split_quant_grouped; the quantized outputs are bit for bit those of
+ * that call.  ratio: device float[nseg] (4-byte aligned), required.
+ * Workspace: AVERIS_OP_SPLIT_QUANT as for the call it extends. */
+averis_status_t averis_split_quant_ratio(const void* a, averis_dtype_t dtype, int64_t rows,
+                                         int64_t cols, int64_t lda, const int64_t* seg_offsets,
+                                         int nseg, uint64_t seed, averis_round_t rnd,
+                                         const averis_nvfp4_t* residual,
+                                         const averis_nvfp4_t* mean, float* mean_f32, float* ratio,
+                                         void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------------- */
 /* Plain quant: the vanilla-FP4 arm (arXiv abstract: "vanilla NVFP4") and  */
 /* the weight operand W (Lighthouse §2.2, both equations).                 */

@@ -29,6 +29,7 @@ EXPORTS = [
     "averis_split_quant", "averis_split_quant_grouped", "averis_quant", "averis_quant_batched",
     "averis_quant_grouped", "averis_quant_pair", "averis_gemm_fwd", "averis_gemm_dgrad",
     "averis_gemm_vanilla", "averis_gemm_grouped", "averis_residual_t_quant", "averis_gemm_wgrad",
+    "averis_split_quant_ratio",
     "averis_workspace_bytes", "averis_status_str",
     "averis_abi_version", "averis_last_error",
 ]
@@ -72,6 +73,7 @@ def lib():
             "averis_gemm_grouped": [T, T, T, P, I, P, I, I64, P, SZ, P],
             "averis_residual_t_quant": [P, I, I64, I64, I64, P, P, U64, I, T, P],
             "averis_gemm_wgrad": [T, T, P, P, P, I, I64, P, SZ, P],
+            "averis_split_quant_ratio": [P, I, I64, I64, I64, P, I, U64, I, T, T, P, P, P, SZ, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -326,3 +328,23 @@ def averis_gemm_wgrad(xt, dt, mu_x, mu_d, out_dtype=torch.float32, out=None, ws=
         ctypes.byref(cx), ctypes.byref(cd), mu_x.data_ptr(), mu_d.data_ptr(), c.data_ptr(),
         _dtype_code(c), c.stride(0), ws.data_ptr(), ws.numel(), _stream()))
     return c
+
+
+def averis_split_quant_ratio(a, seed=0, rnd=SR, offsets=None, ws=None):
+    """averis_split_quant (or its grouped form with offsets) plus the
+    mean-energy ratio of each segment; returns (residual, mean, mu_f32, ratio)."""
+    rows, cols = a.shape
+    nseg = 1 if offsets is None else offsets.numel() - 1
+    res = NVFP4.empty(rows, cols, nseg, a.device)
+    mean = NVFP4.empty(nseg, cols, nseg, a.device)
+    mu = torch.empty((nseg, cols) if offsets is not None else (cols,), dtype=torch.float32,
+                     device=a.device)
+    ratio = torch.empty((nseg,), dtype=torch.float32, device=a.device)
+    need = workspace_bytes(OP_SPLIT_QUANT, rows, cols, 0, 0 if offsets is None else nseg)
+    ws = ws if ws is not None else _workspace(need, a.device)
+    r, m = res.c(), mean.c()
+    _check("averis_split_quant_ratio", lib().averis_split_quant_ratio(
+        a.data_ptr(), _dtype_code(a), rows, cols, _lda(a),
+        offsets.data_ptr() if offsets is not None else None, nseg, seed, rnd, ctypes.byref(r),
+        ctypes.byref(m), mu.data_ptr(), ratio.data_ptr(), ws.data_ptr(), ws.numel(), _stream()))
+    return res, mean, mu, ratio

@@ -64,6 +64,8 @@ size_t split_ws_bytes(int64_t rows, int64_t cols, int nseg) {
   b += align256((size_t)(nch * ct_s * 4));      // pamax
   b += align256((size_t)(ns * cols * 4));       // mu
   b += align256((size_t)(ns * (ct_f > 1 ? ct_f : 1) * 4)) * 2;  // tmax_r, tmax_mu
+  b += align256((size_t)(nch * cols * 8));      // psq
+  b += align256((size_t)(ns * (ct_f > 1 ? ct_f : 1) * 8)) * 2;  // tssq, tmu2
   return b;
 }
 
@@ -80,7 +82,10 @@ SplitWs split_ws_carve(void* ws, int64_t rows, int64_t cols, int nseg) {
   w.pamax = reinterpret_cast<float*>(p); p += align256((size_t)(nch * ct_s * 4));
   w.mu = reinterpret_cast<float*>(p);    p += align256((size_t)(ns * cols * 4));
   w.tmax_r = reinterpret_cast<float*>(p); p += align256((size_t)(ns * (ct_f > 1 ? ct_f : 1) * 4));
-  w.tmax_mu = reinterpret_cast<float*>(p);
+  w.tmax_mu = reinterpret_cast<float*>(p); p += align256((size_t)(ns * (ct_f > 1 ? ct_f : 1) * 4));
+  w.psq = reinterpret_cast<double*>(p);  p += align256((size_t)(nch * cols * 8));
+  w.tssq = reinterpret_cast<double*>(p); p += align256((size_t)(ns * (ct_f > 1 ? ct_f : 1) * 8));
+  w.tmu2 = reinterpret_cast<double*>(p);
   return w;
 }
 
@@ -139,7 +144,7 @@ static averis_status_t split_common(const void* a, averis_dtype_t dtype, int64_t
                                     uint64_t seed, averis_round_t rnd,
                                     const averis_nvfp4_t* residual, const averis_nvfp4_t* mean,
                                     float* mean_f32, void* ws, size_t ws_bytes,
-                                    hipStream_t stream) {
+                                    hipStream_t stream, float* ratio = nullptr) {
   averis_status_t s = check_input(a, dtype, rows, cols, lda, cols);
   if (s != AVERIS_OK) return s;
   if (rnd != AVERIS_RN && rnd != AVERIS_SR) return AVERIS_E_ARG;
@@ -155,7 +160,7 @@ static averis_status_t split_common(const void* a, averis_dtype_t dtype, int64_t
   const QuantOut mo{mean->codes, mean->scales, mean->tscale};
   return hip_status(launch_split_or_plain(a, dtype == AVERIS_BF16, rows, cols, lda, offs, nseg,
                                           true, rnd == AVERIS_SR, seed, 0u, ro, &mo, mean_f32, w,
-                                          stream));
+                                          stream, ratio));
 }
 
 averis_status_t averis_split_quant(const void* a, averis_dtype_t dtype, int64_t rows, int64_t cols,
@@ -177,6 +182,20 @@ averis_status_t averis_split_quant_grouped(const void* a, averis_dtype_t dtype, 
   if (!aligned(seg_offsets, 8)) return AVERIS_E_ALIGN;
   return split_common(a, dtype, rows, cols, lda, seg_offsets, nseg, seed, rnd, residual, mean,
                       mean_f32, ws, ws_bytes, stream);
+}
+
+averis_status_t averis_split_quant_ratio(const void* a, averis_dtype_t dtype, int64_t rows,
+                                         int64_t cols, int64_t lda, const int64_t* seg_offsets,
+                                         int nseg, uint64_t seed, averis_round_t rnd,
+                                         const averis_nvfp4_t* residual,
+                                         const averis_nvfp4_t* mean, float* mean_f32, float* ratio,
+                                         void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ratio) return AVERIS_E_NULL;
+  if (!aligned(ratio, 4)) return AVERIS_E_ALIGN;
+  if (!seg_offsets && nseg != 1) return AVERIS_E_ARG;
+  if (seg_offsets && !aligned(seg_offsets, 8)) return AVERIS_E_ALIGN;
+  return split_common(a, dtype, rows, cols, lda, seg_offsets, nseg, seed, rnd, residual, mean,
+                      mean_f32, ws, ws_bytes, stream, ratio);
 }
 
 static averis_status_t quant_common(const void* a, averis_dtype_t dtype, int64_t rows,

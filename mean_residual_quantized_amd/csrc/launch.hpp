@@ -30,6 +30,9 @@ struct SplitWs {
   float* mu;       // [nseg][cols]
   float* tmax_r;   // [nseg][col tiles] residual max |r| per column tile
   float* tmax_mu;  // [nseg][col tiles] max |mu| per column tile
+  double* psq;     // [chunks][cols] partial column sums of squares (mean-energy ratio)
+  double* tssq;    // [nseg][col tiles] sum of squares per column tile
+  double* tmu2;    // [nseg][col tiles] sum of squared fp64 means per column tile
 };
 
 size_t split_ws_bytes(int64_t rows, int64_t cols, int nseg);
@@ -40,7 +43,7 @@ hipError_t launch_split_or_plain(const void* a, bool bf16, int64_t rows, int64_t
                                  int64_t lda, const int64_t* offs, int nseg, bool split, bool sr,
                                  uint64_t seed, uint32_t stream_id, const QuantOut& out,
                                  const QuantOut* mean, float* mean_f32, const SplitWs& ws,
-                                 hipStream_t st);
+                                 hipStream_t st, float* ratio = nullptr);
 
 hipError_t launch_quant_batched(const void* a, bool bf16, int batch, int64_t rows, int64_t cols,
                                 int64_t lda, int64_t bstride, int transpose, bool sr,

@@ -95,20 +95,23 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 // stats: block = 32 column-octets (256 columns) x 8 row lanes over one chunk
 // of kStatsRows rows; each thread keeps 8 row loads in flight.
 // ---------------------------------------------------------------------------
-template <typename T, bool SPLIT>
+// SSQ (with SPLIT): also the column sums of squares, for the mean-energy
+// ratio (each square is exact in fp64, one fma per element)
+template <typename T, bool SPLIT, bool SSQ = false>
 __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t rows, int64_t cols,
                                                int64_t lda, const int64_t* offs, int nseg,
                                                double* __restrict__ psum,
                                                float* __restrict__ pmax,
                                                float* __restrict__ pmin,
                                                float* __restrict__ pmnz,
-                                               float* __restrict__ pamax) {
+                                               float* __restrict__ pamax,
+                                               double* __restrict__ psq = nullptr) {
   const SegRange sr = locate_chunk(offs, nseg, rows, kStatsRows, blockIdx.y);
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   const int64_t c = (int64_t)blockIdx.x * 256 + tx * 8;
   const bool active = sr.seg >= 0 && c < cols;
 
-  double s[8];
+  double s[8], sq[8];
   float mx[8], mn[8], mz[8];
   float am = 0.0f;
   // bf16: the smallest nonzero magnitude per column as packed 16-bit
@@ -120,6 +123,7 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     s[k] = 0.0;
+    sq[k] = 0.0;
     mx[k] = -__builtin_inff();
     mn[k] = __builtin_inff();
     mz[k] = __builtin_inff();
@@ -144,6 +148,10 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
         if (SPLIT) {
           // a clamped row repeats a real value: harmless for max and min
           s[k] += ok ? (double)x : 0.0;
+          if constexpr (SSQ) {
+            const double xd = ok ? (double)x : 0.0;
+            sq[k] = __builtin_fma(xd, xd, sq[k]);
+          }
           mx[k] = __builtin_fmaxf(mx[k], x);
           mn[k] = __builtin_fminf(mn[k], x);
           if constexpr (sizeof(T) != 2) {
@@ -207,13 +215,22 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 8; ++k) lmx[ty][tx * 8 + k] = mz[k];
+    for (int k = 0; k < 8; ++k) {
+      lmx[ty][tx * 8 + k] = mz[k];
+      if constexpr (SSQ) ls[ty][tx * 8 + k] = sq[k];
+    }
     __syncthreads();
     if (live) {
       float mzz = __builtin_inff();
 #pragma unroll
       for (int q = 0; q < 8; ++q) mzz = __builtin_fminf(mzz, lmx[q][j]);
       pmnz[o] = mzz;
+      if constexpr (SSQ) {
+        double t2 = 0.0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) t2 += ls[q][j];
+        psq[o] = t2;
+      }
     }
   } else {
     __shared__ float red[4];
@@ -364,24 +381,28 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
                                                   float* __restrict__ mu,
                                                   float* __restrict__ mean_out,
                                                   float* __restrict__ tmax_r,
-                                                  float* __restrict__ tmax_mu) {
+                                                  float* __restrict__ tmax_mu,
+                                                  const double* __restrict__ psq,
+                                                  double* __restrict__ tssq,
+                                                  double* __restrict__ tmu2) {
   constexpr int NC = (int)kFinCols, NQ = 256 / NC;
   const int seg = blockIdx.y;
   const SegRange sr = describe_segment(offs, nseg, rows, kStatsRows, seg);
   const int jl = threadIdx.x % NC, q = threadIdx.x / NC;
   const int64_t j = (int64_t)blockIdx.x * NC + jl;
-  double s = 0.0;
+  double s = 0.0, s2 = 0.0;
   float m1 = -__builtin_inff(), m0 = __builtin_inff(), mz = __builtin_inff();
   if (j < cols && sr.c1 > sr.c0) {
     constexpr int U = 8;
     const int64_t clast = sr.c1 - 1;
     for (int64_t ck = sr.c0 + q; ck < sr.c1; ck += NQ * U) {
-      double ps[U];
+      double ps[U], pq[U];
       float px[U], pn[U], pz[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t cc = ck + NQ * u < clast ? ck + NQ * u : clast;
         ps[u] = psum[cc * cols + j];
+        pq[u] = psq ? psq[cc * cols + j] : 0.0;
         px[u] = pmax[cc * cols + j];
         pn[u] = pmin[cc * cols + j];
         pz[u] = pmnz[cc * cols + j];
@@ -390,24 +411,26 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
       for (int u = 0; u < U; ++u) {
         const bool ok = ck + NQ * u <= clast;
         s += ok ? ps[u] : 0.0;
+        s2 += ok ? pq[u] : 0.0;
         m1 = __builtin_fmaxf(m1, px[u]);   // a clamped chunk repeats a real one
         m0 = __builtin_fminf(m0, pn[u]);
         mz = __builtin_fminf(mz, pz[u]);
       }
     }
   }
-  __shared__ double ls[NQ][NC];
+  __shared__ double ls[NQ][NC], lq[NQ][NC];
   __shared__ float lx[NQ][NC], ln[NQ][NC], lz[NQ][NC];
   __shared__ int need_exact[NC];
   __shared__ double exact_s[NC];
   __shared__ uint32_t wide_red[128][kWideWords];
   ls[q][jl] = s;
+  lq[q][jl] = s2;
   lx[q][jl] = m1;
   ln[q][jl] = m0;
   lz[q][jl] = mz;
   __syncthreads();
   float rmax = 0.0f, amu = 0.0f;
-  double t = 0.0;
+  double t = 0.0, t2 = 0.0, mu2 = 0.0;
   float x1 = -__builtin_inff(), x0 = __builtin_inff();
   const int64_t l = sr.seg_r1 - sr.seg_r0;
   if (q == 0) {
@@ -415,6 +438,7 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
 #pragma unroll
     for (int p = 0; p < NQ; ++p) {
       t += ls[p][jl];
+      t2 += lq[p][jl];
       x1 = __builtin_fmaxf(x1, lx[p][jl]);
       x0 = __builtin_fminf(x0, ln[p][jl]);
       z = __builtin_fminf(z, lz[p][jl]);
@@ -445,8 +469,10 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
     if (need_exact[jl]) t = exact_s[jl];
     float m = 0.0f;
     if (l > 0) {
-      m = (float)(t / (double)l);
+      const double md = t / (double)l;
+      m = (float)md;
       rmax = __builtin_fmaxf(x1 - m, m - x0);
+      mu2 = md * md;
     }
     mu[(int64_t)seg * cols + j] = m;
     if (mean_out) mean_out[(int64_t)seg * cols + j] = m;
@@ -461,6 +487,18 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
     if (threadIdx.x == 0) {
       tmax_r[(int64_t)seg * gridDim.x + blockIdx.x] = rmax;
       tmax_mu[(int64_t)seg * gridDim.x + blockIdx.x] = amu;
+    }
+    if (psq) {
+      // the tile's sums for the mean-energy ratio (columns past the end
+      // hold zeros), in a fixed butterfly order
+      for (int d = NC / 2; d > 0; d >>= 1) {
+        t2 += __shfl_xor(t2, d, 64);
+        mu2 += __shfl_xor(mu2, d, 64);
+      }
+      if (threadIdx.x == 0) {
+        tssq[(int64_t)seg * gridDim.x + blockIdx.x] = t2;
+        tmu2[(int64_t)seg * gridDim.x + blockIdx.x] = mu2;
+      }
     }
   }
 }
@@ -551,6 +589,23 @@ __device__ __forceinline__ void quant_block16(const float* r, float s_enc, uint6
   *scale = (uint8_t)sc;
 }
 
+// sum of n doubles in a fixed order (thread i takes i, i + 256, ...; then a
+// fixed tree over the threads); thread 0 gets the total
+__device__ __forceinline__ double block_sum_f64(const double* p, int64_t n) {
+  __shared__ double red[256];
+  double v = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += 256) v += p[i];
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if ((int)threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+    __syncthreads();
+  }
+  const double t = red[0];
+  __syncthreads();
+  return t;
+}
+
 // max over a segment's per-tile partial maxima (all threads get it)
 __device__ __forceinline__ float reduce_partials(const float* p, int64_t n) {
   __shared__ float red[4];
@@ -577,7 +632,10 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ a, int64_t 
                                                float* __restrict__ tscale,
                                                uint8_t* __restrict__ mcodes,
                                                uint8_t* __restrict__ mscales,
-                                               float* __restrict__ mtscale) {
+                                               float* __restrict__ mtscale,
+                                               const double* __restrict__ tssq,
+                                               const double* __restrict__ tmu2,
+                                               float* __restrict__ ratio) {
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   const int64_t nb = cols >> 4;
@@ -600,6 +658,18 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ a, int64_t 
         mtscale[2 * seg + 1] = s_dec;
         tscale[2 * seg] = r_enc;
         tscale[2 * seg + 1] = r_dec;
+      }
+      if (ratio) {
+        // mean-energy ratio R = sqrt(sum mu_j^2 / (sum a_ij^2 / l)) of the
+        // segment, from the per-tile sums of the finalize pass
+        // (every thread takes part: both helpers synchronize the block)
+        const double q2 = block_sum_f64(tssq + (int64_t)seg * ntmax_mu, ntmax_mu);
+        const double m2 = block_sum_f64(tmu2 + (int64_t)seg * ntmax_mu, ntmax_mu);
+        const SegRange ss = describe_segment(offs, nseg, rows, kStatsRows, seg);
+        if (threadIdx.x == 0) {
+          const int64_t l = ss.seg_r1 - ss.seg_r0;
+          ratio[seg] = (l > 0 && q2 > 0.0) ? (float)__builtin_sqrt(m2 / (q2 / (double)l)) : 0.0f;
+        }
       }
     }
     if (ty == 0 && b < nb) {
@@ -982,7 +1052,7 @@ static hipError_t run_split_or_plain(const void* a_, int64_t rows, int64_t cols,
                                      const int64_t* offs, int nseg, bool split, bool sr,
                                      uint64_t seed, uint32_t stream_id, const QuantOut& out,
                                      const QuantOut* mean, float* mean_f32, const SplitWs& ws,
-                                     hipStream_t st) {
+                                     hipStream_t st, float* ratio) {
   const T* a = static_cast<const T*>(a_);
   const int64_t nchs = chunk_upper_bound(rows, nseg, kStatsRows);
   const int64_t nchq = chunk_upper_bound(rows, nseg, kQuantRows);
@@ -991,7 +1061,10 @@ static hipError_t run_split_or_plain(const void* a_, int64_t rows, int64_t cols,
   const int64_t ct_q = ((cols >> 4) + 63) / 64;
   if (nchs > 0) {
     dim3 g((unsigned)ct_s, (unsigned)nchs);
-    if (split)
+    if (split && ratio)
+      k_stats<T, true, true><<<g, 256, 0, st>>>(a, rows, cols, lda, offs, nseg, ws.psum, ws.pmax,
+                                                ws.pmin, ws.pmnz, nullptr, ws.psq);
+    else if (split)
       k_stats<T, true><<<g, 256, 0, st>>>(a, rows, cols, lda, offs, nseg, ws.psum, ws.pmax,
                                           ws.pmin, ws.pmnz, nullptr);
     else
@@ -1004,7 +1077,7 @@ static hipError_t run_split_or_plain(const void* a_, int64_t rows, int64_t cols,
     dim3 g((unsigned)ct_f, (unsigned)nseg);
     k_finalize<<<g, 256, 0, st>>>(a, sizeof(T) == 2, lda, rows, cols, offs, nseg, ws.psum,
                                   ws.pmax, ws.pmin, ws.pmnz, ws.mu, mean_f32, ws.tmax_r,
-                                  ws.tmax_mu);
+                                  ws.tmax_mu, ratio ? ws.psq : nullptr, ws.tssq, ws.tmu2);
     tmax = ws.tmax_r;
     ntmax = ct_f;
   } else {
@@ -1017,7 +1090,7 @@ static hipError_t run_split_or_plain(const void* a_, int64_t rows, int64_t cols,
   k_quant<T, SPL, SRB><<<gq, 256, 0, st>>>(                                                 \
       a, rows, cols, lda, offs, nseg, nchq, seed, stream_id, ws.mu, tmax, ntmax, ws.tmax_mu, \
       ct_f, out.codes, out.scales, out.tscale, mean ? mean->codes : nullptr,                \
-      mean ? mean->scales : nullptr, mean ? mean->tscale : nullptr)
+      mean ? mean->scales : nullptr, mean ? mean->tscale : nullptr, ws.tssq, ws.tmu2, ratio)
   if (split) {
     if (sr) AVERIS_QUANT_LAUNCH(true, true); else AVERIS_QUANT_LAUNCH(true, false);
   } else {
@@ -1031,12 +1104,12 @@ hipError_t launch_split_or_plain(const void* a, bool bf16, int64_t rows, int64_t
                                  int64_t lda, const int64_t* offs, int nseg, bool split, bool sr,
                                  uint64_t seed, uint32_t stream_id, const QuantOut& out,
                                  const QuantOut* mean, float* mean_f32, const SplitWs& ws,
-                                 hipStream_t st) {
+                                 hipStream_t st, float* ratio) {
   if (bf16)
     return run_split_or_plain<uint16_t>(a, rows, cols, lda, offs, nseg, split, sr, seed,
-                                        stream_id, out, mean, mean_f32, ws, st);
+                                        stream_id, out, mean, mean_f32, ws, st, ratio);
   return run_split_or_plain<float>(a, rows, cols, lda, offs, nseg, split, sr, seed, stream_id,
-                                   out, mean, mean_f32, ws, st);
+                                   out, mean, mean_f32, ws, st, ratio);
 }
 
 template <typename T>

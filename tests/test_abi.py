@@ -196,3 +196,15 @@ def test_wgrad_rejections(L):
     assert wb(av.OP_WGRAD, 1024, 8192, 3072) == 4 * 1024 * 3072 * 4
     assert wb(av.OP_WGRAD, 64, 1008, 96) == 64 * 96 * 4  # l % 64 != 0: one partial
     assert wb(av.OP_WGRAD, 64, 0, 96) == 64 * 96 * 4
+
+
+def test_split_ratio_rejections(L):
+    res, mean = nv(64, 128), nv(1, 128)
+    sr = lambda offs=None, nseg=1, ratio=P, mean=mean: L.averis_split_quant_ratio(
+        P, av.BF16, 64, 128, 128, offs, nseg, 0, av.SR, ctypes.byref(res), ctypes.byref(mean),
+        None, ratio, P, 1 << 30, None)
+    assert sr(ratio=None) == 1
+    assert sr(ratio=P + 2) == 4
+    assert sr(nseg=2) == 6                                # no offsets: one segment
+    assert sr(offs=P + 4, nseg=4, mean=nv(4, 128)) == 4
+    assert sr(offs=P, nseg=4, mean=nv(3, 128)) == 2
