@@ -265,6 +265,36 @@ def time_wgrad(xs, ds, ws, steps, warmup):
              "gemm_wgrad covers the split-K GEMM and the reduce that adds the outer product")
 
 
+def time_ratio(xs, ds, ws, steps, warmup):
+    """Split-quant of X and D with and without the mean-energy ratio, per call
+    (events on the launch stream, queued behind a spin kernel, rotating
+    copies), and the ratios themselves."""
+    def one(i, t):
+        for name, src, key in (("x", xs, "sq_x"), ("d", ds, "sq_d")):
+            a = src[i % len(src)]
+            t.start("plain_" + name)
+            av.averis_split_quant(a, seed=0, ws=ws[key])
+            t.stop("plain_" + name)
+            t.start("ratio_" + name)
+            out = av.averis_split_quant_ratio(a, seed=0, ws=ws[key])
+            t.stop("ratio_" + name)
+            ratios[name] = out[3]
+
+    ratios = {}
+    for i in range(warmup):
+        one(i, Timer())
+    torch.cuda.synchronize()
+    t = Timer()
+    hold_gpu(5.0 + 0.5 * steps)
+    for i in range(steps):
+        one(i, t)
+    torch.cuda.synchronize()
+    med = lambda v: float(np.median(v))
+    return {name: dict(split_ms=med(t.ms("plain_" + name)), split_with_ratio_ms=med(t.ms("ratio_" + name)),
+                       ratio=float(ratios[name][0].item()))
+            for name in ("x", "d")}
+
+
 def cpu_baseline(cfg_rows, m, n):
     """The oracle as it stands on a bounded sample: cfg_rows tokens of the
     same workload (split-quant of X and D, both weight copies, the float64
@@ -387,6 +417,8 @@ def main():
         " ".join("%s %.4f" % kv for kv in tv_ms.items())))
     log("bench: wgrad pieces")
     wg = time_wgrad(xs, ds, ws, args.steps, args.warmup)
+    log("bench: mean-energy ratio")
+    mer = time_ratio(xs, ds, ws, args.steps, args.warmup)
     # the headline is the device's step time (launches queued ahead of it)
     ms_a, ms_v = ta_ms["queued"], tv_ms["queued"]
 
@@ -463,6 +495,7 @@ def main():
                               "graph": "one HIP graph per step, replayed, host clock"},
         "overhead_vs_vanilla": overhead,
         "wgrad": wg,
+        "mean_energy_ratio": mer,
         "pages_overhead_context": "2.20% end-to-end over vanilla NVFP4 (hardware not stated)",
     }
     if not args.no_cpu_baseline:

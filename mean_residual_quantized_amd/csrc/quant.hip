@@ -345,7 +345,9 @@ __device__ inline double wide_to_double(uint32_t (&a)[kWideWords]) {
 
 // the exact sum of rows [r0, r1) of column j, correctly rounded to double;
 // all 256 threads call it, thread 0 gets the result
-__device__ double exact_column_sum(const void* a, bool bf16, int64_t lda, int64_t r0, int64_t r1,
+// (kept out of line: the finalize pass calls it only for a column that fails
+// the certificate, and inlined it would quadruple that kernel's code)
+__device__ __noinline__ double exact_column_sum(const void* a, bool bf16, int64_t lda, int64_t r0, int64_t r1,
                                    int64_t j, uint32_t (*red)[kWideWords]) {
   uint32_t acc[kWideWords];
 #pragma unroll
@@ -393,7 +395,7 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
   double s = 0.0, s2 = 0.0;
   float m1 = -__builtin_inff(), m0 = __builtin_inff(), mz = __builtin_inff();
   if (j < cols && sr.c1 > sr.c0) {
-    constexpr int U = 8;
+    constexpr int U = 4;
     const int64_t clast = sr.c1 - 1;
     for (int64_t ck = sr.c0 + q; ck < sr.c1; ck += NQ * U) {
       double ps[U], pq[U];
