@@ -3,9 +3,9 @@
 
 One step = one pass of the whole hot path over one batch of synthetic input
 of the Qwen3-0.6B up-projection shape (l = 8192 tokens, m = 1024, n = 3072,
-bf16): both quantized copies of W, split-quant of X, the forward GEMM with
-the rank-one mean term, split-quant of the output gradient D, and the dgrad
-GEMM.  The vanilla-FP4 arm (plain quant of X / D + the same GEMMs without
+bf16): both quantized copies of W, split-quant of X (which also forms the
+rank-one mean row for the forward GEMM), the forward GEMM, split-quant of the
+output gradient D (and its rank-one row), and the dgrad GEMM.  The vanilla-FP4 arm (plain quant of X / D + the same GEMMs without
 the mean term) is timed the same way to report the Averis overhead.
 
 Inputs are resident in HBM before timing starts; the timed steps rotate
@@ -96,17 +96,19 @@ def run_step(x, d, w, ws, t=None, vanilla=False):
     wt, wd = av.averis_quant_pair(w, rnd=av.RN, ws=ws["q"])
     toc("wquant")
     if not vanilla:
+        # the split also forms the rank-one row 1 (mean W) for the GEMM that
+        # takes it, so the GEMM adds it without a mean row of its own
         tic("split_x")
-        xr, xm, _ = av.averis_split_quant(x, seed=0, ws=ws["sq_x"])
+        xr, _, _, rho_x = av.averis_split_quant_rank1(x, wt, seed=0, ws=ws["sq_x"], rho=ws["rho_x"])
         toc("split_x")
         tic("gemm_fwd")
-        av.averis_gemm_fwd(xr, xm, wt, out_dtype=torch.bfloat16, out=ws["y"], ws=ws["g"])
+        av.averis_gemm_rank1(xr, rho_x, wt, out_dtype=torch.bfloat16, out=ws["y"])
         toc("gemm_fwd")
         tic("split_d")
-        dr, dm, _ = av.averis_split_quant(d, seed=1, ws=ws["sq_d"])
+        dr, _, _, rho_d = av.averis_split_quant_rank1(d, wd, seed=1, ws=ws["sq_d"], rho=ws["rho_d"])
         toc("split_d")
         tic("gemm_dgrad")
-        av.averis_gemm_dgrad(dr, dm, wd, out_dtype=torch.bfloat16, out=ws["dx"], ws=ws["g"])
+        av.averis_gemm_rank1(dr, rho_d, wd, out_dtype=torch.bfloat16, out=ws["dx"])
         toc("gemm_dgrad")
     else:
         tic("vq_x")
@@ -338,10 +340,10 @@ def traffic_probe(args):
     torch.cuda.synchronize()
     for _ in range(3):
         wt, wd = av.averis_quant_pair(w, rnd=av.RN)
-        xr, xm, mx = av.averis_split_quant(x, seed=0)
-        av.averis_gemm_fwd(xr, xm, wt, out_dtype=torch.bfloat16)
-        dr, dm, md = av.averis_split_quant(d, seed=1)
-        av.averis_gemm_dgrad(dr, dm, wd, out_dtype=torch.bfloat16)
+        xr, _, mx, rho_x = av.averis_split_quant_rank1(x, wt, seed=0)
+        av.averis_gemm_rank1(xr, rho_x, wt, out_dtype=torch.bfloat16)
+        dr, _, md, rho_d = av.averis_split_quant_rank1(d, wd, seed=1)
+        av.averis_gemm_rank1(dr, rho_d, wd, out_dtype=torch.bfloat16)
         xt = av.averis_residual_t_quant(x, mx, xr, seed=0)
         dt = av.averis_residual_t_quant(d, md, dr, seed=1)
         av.averis_gemm_wgrad(xt, dt, mx, md)
@@ -408,6 +410,8 @@ def main():
                       device=dev),
         y=torch.empty((l, n), dtype=torch.bfloat16, device=dev),
         dx=torch.empty((l, m), dtype=torch.bfloat16, device=dev),
+        rho_x=torch.empty((n,), dtype=torch.float32, device=dev),
+        rho_d=torch.empty((m,), dtype=torch.float32, device=dev),
     )
     log("bench: %d rotating input copies; warmup %d, steps %d" % (copies, args.warmup, args.steps))
     ta_ms, ta = timed(xs, ds, w0, ws, args.steps, args.warmup, vanilla=False)
@@ -448,10 +452,9 @@ def main():
                     step_pct=100 * (ms_a / ms_v - 1))
 
     # roofline of the dominant kernel: the Averis forward GEMM, one launch of
-    # k_gemm_ws (the NT GEMM over the residual codes; its producer waves also
-    # sum the rank-one row, which the epilogue adds), timed by the events
-    # around the call on the launch stream.  The flops counted are the
-    # GEMM's 2lmn.
+    # k_gemm_ws (the NT GEMM over the residual codes; the epilogue adds the
+    # rank-one row the split formed), timed by the events around the call on
+    # the launch stream.  The flops counted are the GEMM's 2lmn.
     g_ms = comp["gemm_fwd"]
     achieved = gemm_flops / (g_ms * 1e-3) / 1e12
     tr = load_traffic()
@@ -460,9 +463,10 @@ def main():
         traffic = tr["gemm_fwd"]["fetch_bytes"] + tr["gemm_fwd"]["write_bytes"]
     roofline = dict(bound="mfma", achieved=achieved, peak=F16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=achieved / F16_MFMA_PEAK_TFLOPS, traffic=traffic,
-                    kernel="k_gemm_ws (averis_gemm_fwd: warp-specialized NVFP4 NT GEMM, exact fp16 "
-                           "dequant -> v_mfma_f32_32x32x16_f16, rank-one row summed by the producer "
-                           "waves and added in the epilogue), M=%d N=%d K=%d, bf16 out" % (l, n, m),
+                    kernel="k_gemm_ws (averis_gemm_rank1 on the forward operands: warp-specialized "
+                           "NVFP4 NT GEMM, exact fp16 dequant -> v_mfma_f32_32x32x16_f16, the rank-one "
+                           "row from the split added in the epilogue), M=%d N=%d K=%d, bf16 out"
+                           % (l, n, m),
                     frac_of_fp4_peak=achieved / FP4_MFMA_PEAK_TFLOPS)
 
     out = {

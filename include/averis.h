@@ -224,6 +224,30 @@ averis_status_t averis_gemm_dgrad(const averis_nvfp4_t* dr, const averis_nvfp4_t
                                   const averis_nvfp4_t* w, void* dx, averis_dtype_t dxdtype,
                                   int64_t lddx, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* The rank-one row formed once, by the split ([Lighthouse] §2.2: the term
+ * 1(mu_bar W_bar) is a row vector added to every output row).
+ * averis_split_quant_rank1 is averis_split_quant (bit for bit the same
+ * residual, mean and mean_f32) that also writes
+ *   rho[j] = deq(mean) . deq(b_j),  j < b->rows,
+ * for the B operand of the GEMM that will take this split (wt for the
+ * forward, w for dgrad: b->cols == cols), fp32 accumulation of exact
+ * products, times the two tensor scales.  rho: device float[b->rows], 4-byte
+ * aligned.  cols <= 32768 (the dequantized mean is staged in on-chip memory).
+ * Workspace: AVERIS_OP_SPLIT_QUANT (rows, cols, 0, 0).
+ * averis_gemm_rank1 then computes c = deq(a) deq(b)^T + 1 rho^T (a: the
+ * residual, b as above) with no mean row of its own; it equals averis_gemm_fwd
+ * / averis_gemm_dgrad of the same operands up to fp32 summation order.  No
+ * workspace. */
+averis_status_t averis_split_quant_rank1(const void* a, averis_dtype_t dtype, int64_t rows,
+                                         int64_t cols, int64_t lda, uint64_t seed,
+                                         averis_round_t rnd, const averis_nvfp4_t* residual,
+                                         const averis_nvfp4_t* mean, float* mean_f32,
+                                         const averis_nvfp4_t* b, float* rho, void* ws,
+                                         size_t ws_bytes, hipStream_t stream);
+averis_status_t averis_gemm_rank1(const averis_nvfp4_t* a, const float* rho,
+                                  const averis_nvfp4_t* b, void* c, averis_dtype_t cdtype,
+                                  int64_t ldc, hipStream_t stream);
+
 /* Vanilla arm: c = deq(a) deq(b)^T, no mean term. */
 averis_status_t averis_gemm_vanilla(const averis_nvfp4_t* a, const averis_nvfp4_t* b, void* c,
                                     averis_dtype_t cdtype, int64_t ldc, void* ws, size_t ws_bytes,

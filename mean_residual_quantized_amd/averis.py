@@ -29,7 +29,7 @@ EXPORTS = [
     "averis_split_quant", "averis_split_quant_grouped", "averis_quant", "averis_quant_batched",
     "averis_quant_grouped", "averis_quant_pair", "averis_gemm_fwd", "averis_gemm_dgrad",
     "averis_gemm_vanilla", "averis_gemm_grouped", "averis_residual_t_quant", "averis_gemm_wgrad",
-    "averis_split_quant_ratio",
+    "averis_split_quant_ratio", "averis_split_quant_rank1", "averis_gemm_rank1",
     "averis_workspace_bytes", "averis_status_str",
     "averis_abi_version", "averis_last_error",
 ]
@@ -74,6 +74,8 @@ def lib():
             "averis_residual_t_quant": [P, I, I64, I64, I64, P, P, U64, I, T, P],
             "averis_gemm_wgrad": [T, T, P, P, P, I, I64, P, SZ, P],
             "averis_split_quant_ratio": [P, I, I64, I64, I64, P, I, U64, I, T, T, P, P, P, SZ, P],
+            "averis_split_quant_rank1": [P, I, I64, I64, I64, U64, I, T, T, P, T, P, P, SZ, P],
+            "averis_gemm_rank1": [T, P, T, P, I, I64, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -348,3 +350,31 @@ def averis_split_quant_ratio(a, seed=0, rnd=SR, offsets=None, ws=None):
         offsets.data_ptr() if offsets is not None else None, nseg, seed, rnd, ctypes.byref(r),
         ctypes.byref(m), mu.data_ptr(), ratio.data_ptr(), ws.data_ptr(), ws.numel(), _stream()))
     return res, mean, mu, ratio
+
+
+def averis_split_quant_rank1(a, b, seed=0, rnd=SR, ws=None, rho=None):
+    """averis_split_quant plus the rank-one row rho = deq(mean) deq(b)^T for
+    the GEMM's B operand b; returns (residual, mean, mu_f32, rho)."""
+    rows, cols = a.shape
+    res = NVFP4.empty(rows, cols, 1, a.device)
+    mean = NVFP4.empty(1, cols, 1, a.device)
+    mu = torch.empty((cols,), dtype=torch.float32, device=a.device)
+    rho = rho if rho is not None else torch.empty((b.rows,), dtype=torch.float32, device=a.device)
+    need = workspace_bytes(OP_SPLIT_QUANT, rows, cols)
+    ws = ws if ws is not None else _workspace(need, a.device)
+    r, m, cb = res.c(), mean.c(), b.c()
+    _check("averis_split_quant_rank1", lib().averis_split_quant_rank1(
+        a.data_ptr(), _dtype_code(a), rows, cols, _lda(a), seed, rnd, ctypes.byref(r),
+        ctypes.byref(m), mu.data_ptr(), ctypes.byref(cb), rho.data_ptr(), ws.data_ptr(),
+        ws.numel(), _stream()))
+    return res, mean, mu, rho
+
+
+def averis_gemm_rank1(a, rho, b, out_dtype=torch.float32, out=None):
+    """c = deq(a) deq(b)^T + 1 rho^T."""
+    c = _out(a.rows, b.rows, out_dtype, a.codes.device, out)
+    ca, cb = a.c(), b.c()
+    _check("averis_gemm_rank1", lib().averis_gemm_rank1(
+        ctypes.byref(ca), rho.data_ptr(), ctypes.byref(cb), c.data_ptr(), _dtype_code(c),
+        c.stride(0), _stream()))
+    return c

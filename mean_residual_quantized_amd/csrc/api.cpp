@@ -16,6 +16,9 @@ using namespace averis;
 namespace {
 
 constexpr int kMaxSeg = 4096;
+// the split stages the dequantized mean (2 bytes per column) in LDS to form
+// the rank-one row
+constexpr int64_t kRank1MaxK = 32768;
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -144,7 +147,8 @@ static averis_status_t split_common(const void* a, averis_dtype_t dtype, int64_t
                                     uint64_t seed, averis_round_t rnd,
                                     const averis_nvfp4_t* residual, const averis_nvfp4_t* mean,
                                     float* mean_f32, void* ws, size_t ws_bytes,
-                                    hipStream_t stream, float* ratio = nullptr) {
+                                    hipStream_t stream, float* ratio = nullptr,
+                                    const Rank1Out* r1 = nullptr) {
   averis_status_t s = check_input(a, dtype, rows, cols, lda, cols);
   if (s != AVERIS_OK) return s;
   if (rnd != AVERIS_RN && rnd != AVERIS_SR) return AVERIS_E_ARG;
@@ -160,7 +164,7 @@ static averis_status_t split_common(const void* a, averis_dtype_t dtype, int64_t
   const QuantOut mo{mean->codes, mean->scales, mean->tscale};
   return hip_status(launch_split_or_plain(a, dtype == AVERIS_BF16, rows, cols, lda, offs, nseg,
                                           true, rnd == AVERIS_SR, seed, 0u, ro, &mo, mean_f32, w,
-                                          stream, ratio));
+                                          stream, ratio, r1));
 }
 
 averis_status_t averis_split_quant(const void* a, averis_dtype_t dtype, int64_t rows, int64_t cols,
@@ -196,6 +200,42 @@ averis_status_t averis_split_quant_ratio(const void* a, averis_dtype_t dtype, in
   if (seg_offsets && !aligned(seg_offsets, 8)) return AVERIS_E_ALIGN;
   return split_common(a, dtype, rows, cols, lda, seg_offsets, nseg, seed, rnd, residual, mean,
                       mean_f32, ws, ws_bytes, stream, ratio);
+}
+
+averis_status_t averis_split_quant_rank1(const void* a, averis_dtype_t dtype, int64_t rows,
+                                         int64_t cols, int64_t lda, uint64_t seed,
+                                         averis_round_t rnd, const averis_nvfp4_t* residual,
+                                         const averis_nvfp4_t* mean, float* mean_f32,
+                                         const averis_nvfp4_t* b, float* rho, void* ws,
+                                         size_t ws_bytes, hipStream_t stream) {
+  if (!b || !rho) return AVERIS_E_NULL;
+  if (!aligned(rho, 4)) return AVERIS_E_ALIGN;
+  if (cols > kRank1MaxK) return AVERIS_E_SHAPE;
+  averis_status_t s = check_tensor(b, b->rows, cols);
+  if (s != AVERIS_OK) return s;
+  if (b->rows <= 0) return AVERIS_E_SHAPE;
+  const Rank1Out r1{QOperand{b->codes, b->scales, b->tscale}, b->rows, rho};
+  return split_common(a, dtype, rows, cols, lda, nullptr, 1, seed, rnd, residual, mean, mean_f32,
+                      ws, ws_bytes, stream, nullptr, &r1);
+}
+
+averis_status_t averis_gemm_rank1(const averis_nvfp4_t* a, const float* rho,
+                                  const averis_nvfp4_t* b, void* c, averis_dtype_t cdtype,
+                                  int64_t ldc, hipStream_t stream) {
+  if (!a || !b || !rho) return AVERIS_E_NULL;
+  if (!dtype_ok(cdtype)) return AVERIS_E_DTYPE;
+  const int64_t m = a->rows, k = a->cols, n = b->rows;
+  if (m < 0 || n < 0 || k <= 0 || k % 16 != 0 || b->cols != k) return AVERIS_E_SHAPE;
+  averis_status_t s;
+  if ((s = check_tensor(a, m, k)) != AVERIS_OK) return s;
+  if ((s = check_tensor(b, n, k)) != AVERIS_OK) return s;
+  if (!aligned(rho, 4)) return AVERIS_E_ALIGN;
+  if (ldc < n) return AVERIS_E_SHAPE;
+  if (m > 0 && n > 0 && !c) return AVERIS_E_NULL;
+  if (!aligned(c, elem_size(cdtype))) return AVERIS_E_ALIGN;
+  const QOperand qa{a->codes, a->scales, a->tscale};
+  const QOperand qb{b->codes, b->scales, b->tscale};
+  return hip_status(launch_gemm_rho(qa, rho, qb, m, n, k, c, cdtype == AVERIS_BF16, ldc, stream));
 }
 
 static averis_status_t quant_common(const void* a, averis_dtype_t dtype, int64_t rows,

@@ -61,11 +61,13 @@ __device__ __forceinline__ void ws_unroll(F&& f) {
 
 }  // namespace
 
-template <int TM, int TN, int PF, bool OUT_BF16, bool HAS_MEAN, bool BQ, bool SG>
+// RG (with HAS_MEAN): the rank-one row comes precomputed (rho_g, one float
+// per column of B) instead of being summed by the producers from the mean row
+template <int TM, int TN, int PF, bool OUT_BF16, bool HAS_MEAN, bool BQ, bool SG, bool RG = false>
 __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOperand M, int64_t m,
                                                     int64_t n, int64_t k, const int64_t* offs,
                                                     int nseg, void* c, int64_t ldc, int64_t kld,
-                                                    int64_t c_split) {
+                                                    int64_t c_split, const float* rho_g) {
   constexpr int BM = 64 * TM, BN = 64 * TN;
   // 32-element chunks dequantized per stage: A rows (and B rows unless BQ)
   constexpr int NCH = BQ ? 2 * BM : 2 * (BM + BN);
@@ -74,6 +76,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
   static_assert((2 * BM) % kProducers == 0 && (2 * BN) % 64 == 0, "whole-wave chunk rounds");
   static_assert(!BQ || BN <= kProducers, "one B row per producer thread");
   static_assert(!(BQ && HAS_MEAN), "the rank-one term is summed from dequantized B chunks");
+  static_assert(!RG || HAS_MEAN, "a precomputed rank-one row is a mean term");
+  constexpr bool DOTS = HAS_MEAN && !RG;   // the producers sum the rank-one row
   constexpr int CPB = CP - IA;   // chunk rounds that hold B rows
   extern __shared__ __attribute__((aligned(16))) _Float16 smem_ws[];
   _Float16* As = smem_ws;                                // [2][BM][LDSK]
@@ -305,7 +309,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
         uint4* dst = reinterpret_cast<uint4*>(base + drow * kWsLdsK + 32 * hf);
 #pragma unroll
         for (int e = 0; e < 4; ++e) dst[e] = d[e];
-        if constexpr (HAS_MEAN) {
+        if constexpr (DOTS) {
           if (i >= IA) {
             // the products of two exact fp16 values (<= 5 significant bits
             // each) are exact; fp32 accumulation
@@ -351,8 +355,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
     constexpr int kMeanPer = 4;   // 32-element chunks of the mean row per thread, at most
     uint4 mw[kMeanPer];
     uint32_t msc[kMeanPer];
-    const int nmc = HAS_MEAN ? (int)(k >> 5) : 0;
-    if constexpr (HAS_MEAN) {
+    const int nmc = DOTS ? (int)(k >> 5) : 0;
+    if constexpr (DOTS) {
       const uint8_t* mc = M.codes + (int64_t)seg * kh;
       const uint8_t* ms = M.scales + (int64_t)seg * kb;
 #pragma unroll
@@ -374,7 +378,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
         if (p < nk) gload(p, p, WsIC<p>{});
       });
     }
-    if constexpr (HAS_MEAN) {
+    if constexpr (RG) {
+      // published by the stage-0 barrier below
+      if (pt < BN) rho_sh[pt] = n0 + pt < n ? rho_g[n0 + pt] : 0.0f;
+    } else if constexpr (HAS_MEAN) {
 #pragma unroll
       for (int u = 0; u < kMeanPer; ++u) {
         const int cidx = pt + kProducers * u;
@@ -438,7 +445,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
         __syncthreads();
       }
     });
-    if constexpr (HAS_MEAN) {
+    if constexpr (DOTS) {
       // the two k-halves of a row sit in neighbouring lanes
       const float rs_scale = M.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
 #pragma unroll
@@ -512,7 +519,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
       bsc[j][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, true);
     }
   };
-  if constexpr (HAS_MEAN) __syncthreads();   // the producers' mean row
+  if constexpr (DOTS) __syncthreads();   // the producers' mean row
   __syncthreads();   // stage 0 in buffer 0
   read_frags(0, 0, 0);
   if constexpr (BQ) read_bscales(0);
@@ -550,7 +557,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
     }
   }
 
-  if constexpr (HAS_MEAN) __syncthreads();   // the producers' rank-one terms
+  if constexpr (DOTS) __syncthreads();   // the producers' rank-one terms
   const float alpha = A.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
   if constexpr (stage_out) {
     const int srow = wm * 32 * TM + (lane & 31);
@@ -632,15 +639,16 @@ size_t ws_lds_bytes(int tm, int tn, bool bq) {
 
 constexpr size_t kWsLdsLimit = 160 * 1024 - 512;
 
-template <int TM, int TN, bool OB, bool HM, bool BQ, bool SG>
+template <int TM, int TN, bool OB, bool HM, bool BQ, bool SG, bool RG = false>
 hipError_t launch_ws(const QOperand& a, const QOperand* mean, const QOperand& b, int64_t m, int64_t n,
                      int64_t k, const int64_t* offs, int nseg, void* c, int64_t ldc,
-                     hipStream_t st, int splits = 1, int64_t c_split = 0) {
+                     hipStream_t st, int splits = 1, int64_t c_split = 0,
+                     const float* rho = nullptr) {
   constexpr int PF = SG ? 4 : 2, BM = 64 * TM, BN = 64 * TN;
-  const size_t lds = ws_lds_bytes(TM, TN, BQ) + (HM ? (size_t)k * 2 : 0);
+  const size_t lds = ws_lds_bytes(TM, TN, BQ) + (HM && !RG ? (size_t)k * 2 : 0);
   static bool attr_set = false;   // per instantiation; the attribute is idempotent
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_ws<TM, TN, PF, OB, HM, BQ, SG>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_ws<TM, TN, PF, OB, HM, BQ, SG, RG>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWsLdsLimit);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -648,8 +656,8 @@ hipError_t launch_ws(const QOperand& a, const QOperand* mean, const QOperand& b,
   const int64_t tiles_m = chunk_upper_bound(m, offs ? nseg : 1, BM);
   dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)tiles_m, (unsigned)splits);
   const QOperand mu = mean ? *mean : QOperand{nullptr, nullptr, nullptr};
-  k_gemm_ws<TM, TN, PF, OB, HM, BQ, SG><<<grid, 512, lds, st>>>(a, b, mu, m, n, k / splits, offs,
-                                                                nseg, c, ldc, k, c_split);
+  k_gemm_ws<TM, TN, PF, OB, HM, BQ, SG, RG><<<grid, 512, lds, st>>>(a, b, mu, m, n, k / splits, offs,
+                                                                    nseg, c, ldc, k, c_split, rho);
   return hipGetLastError();
 }
 
@@ -723,6 +731,32 @@ hipError_t launch_gemm_ws_splitk(const QOperand& a, const QOperand& b, int64_t m
                                                       st, splits, m * n);
   return launch_ws<4, 3, false, false, false, false>(a, nullptr, b, m, n, k, nullptr, 1, part, n,
                                                      st, splits, m * n);
+}
+
+// rank-one row precomputed: 256 x 192 (variant 1) or 256 x 128 (variant 2) tiles
+template <int TM, int TN>
+hipError_t launch_ws_rho(const QOperand& a, const float* rho, const QOperand& b, int64_t m,
+                         int64_t n, int64_t k, void* c, bool c_bf16, int64_t ldc, hipStream_t st) {
+  if (k % 256 == 0) {
+    if (c_bf16)
+      return launch_ws<TM, TN, true, true, false, true, true>(a, nullptr, b, m, n, k, nullptr, 1, c,
+                                                              ldc, st, 1, 0, rho);
+    return launch_ws<TM, TN, false, true, false, true, true>(a, nullptr, b, m, n, k, nullptr, 1, c,
+                                                             ldc, st, 1, 0, rho);
+  }
+  if (c_bf16)
+    return launch_ws<TM, TN, true, true, false, false, true>(a, nullptr, b, m, n, k, nullptr, 1, c,
+                                                             ldc, st, 1, 0, rho);
+  return launch_ws<TM, TN, false, true, false, false, true>(a, nullptr, b, m, n, k, nullptr, 1, c,
+                                                            ldc, st, 1, 0, rho);
+}
+
+hipError_t launch_gemm_ws_rho(int variant, const QOperand& a, const float* rho, const QOperand& b,
+                              int64_t m, int64_t n, int64_t k, void* c, bool c_bf16, int64_t ldc,
+                              hipStream_t st) {
+  if (variant == 1) return launch_ws_rho<4, 3>(a, rho, b, m, n, k, c, c_bf16, ldc, st);
+  if (variant == 2) return launch_ws_rho<4, 2>(a, rho, b, m, n, k, c, c_bf16, ldc, st);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_ws(int variant, const QOperand& a, const QOperand* mean, const QOperand& b,

@@ -35,6 +35,21 @@ struct SplitWs {
   double* tmu2;    // [nseg][col tiles] sum of squared fp64 means per column tile
 };
 
+// A quantized GEMM operand as the kernels see it.
+struct QOperand {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* tscale;
+};
+
+// The rank-one row a split can compute for the GEMM that takes it:
+// rho[j] = deq(Q4(mu)) . deq(b_j) for the n rows of b (one segment).
+struct Rank1Out {
+  QOperand b;
+  int64_t n;
+  float* rho;
+};
+
 size_t split_ws_bytes(int64_t rows, int64_t cols, int nseg);
 SplitWs split_ws_carve(void* ws, int64_t rows, int64_t cols, int nseg);
 size_t batched_ws_bytes(int64_t rows, int64_t cols, int batch);
@@ -43,7 +58,8 @@ hipError_t launch_split_or_plain(const void* a, bool bf16, int64_t rows, int64_t
                                  int64_t lda, const int64_t* offs, int nseg, bool split, bool sr,
                                  uint64_t seed, uint32_t stream_id, const QuantOut& out,
                                  const QuantOut* mean, float* mean_f32, const SplitWs& ws,
-                                 hipStream_t st, float* ratio = nullptr);
+                                 hipStream_t st, float* ratio = nullptr,
+                                 const Rank1Out* r1 = nullptr);
 
 hipError_t launch_quant_batched(const void* a, bool bf16, int batch, int64_t rows, int64_t cols,
                                 int64_t lda, int64_t bstride, int transpose, bool sr,
@@ -63,18 +79,16 @@ hipError_t launch_quant_rt(const void* a, bool bf16, int64_t rows, int64_t cols,
                            const float* mu, const float* tscale_in, bool sr, uint64_t seed,
                            uint32_t stream_id, const QuantOut& out, hipStream_t st);
 
-// A quantized GEMM operand as the kernels see it.
-struct QOperand {
-  const uint8_t* codes;
-  const uint8_t* scales;
-  const float* tscale;
-};
-
 // C[M x N] = deq(A) deq(B)^T (+ 1 deq(mean) deq(B)^T); grouped when offs != nullptr
 // (B then holds nseg stacked N x K matrices).
 hipError_t launch_gemm(const QOperand& a, const QOperand* mean, const QOperand& b, int64_t m,
                        int64_t n, int64_t k, const int64_t* offs, int nseg, void* c, bool c_bf16,
                        int64_t ldc, void* ws, hipStream_t st);
+
+// C = deq(A) deq(B)^T + 1 rho^T with rho (n floats) precomputed (one segment).
+hipError_t launch_gemm_rho(const QOperand& a, const float* rho, const QOperand& b, int64_t m,
+                           int64_t n, int64_t k, void* c, bool c_bf16, int64_t ldc,
+                           hipStream_t st);
 
 // Workspace of a GEMM call (rho, the rank-one term per segment and column).
 size_t gemm_ws_bytes(int64_t n, int64_t k, int nseg);
@@ -87,6 +101,9 @@ int ws_pick(int64_t m, int64_t n, int64_t k, int nseg_eff, bool has_mean);
 hipError_t launch_gemm_ws(int variant, const QOperand& a, const QOperand* mean, const QOperand& b,
                           int64_t m, int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
                           bool c_bf16, int64_t ldc, hipStream_t st);
+hipError_t launch_gemm_ws_rho(int variant, const QOperand& a, const float* rho, const QOperand& b,
+                              int64_t m, int64_t n, int64_t k, void* c, bool c_bf16, int64_t ldc,
+                              hipStream_t st);
 
 // Split-K product into fp32 partials part[z] (m x n each, row stride n).
 hipError_t launch_gemm_ws_splitk(const QOperand& a, const QOperand& b, int64_t m, int64_t n,

@@ -20,6 +20,7 @@
 #include <stdint.h>
 
 #include "device_common.hpp"
+#include "gemm_common.hpp"
 #include "launch.hpp"
 #include "segments.hpp"
 
@@ -527,16 +528,14 @@ __device__ __forceinline__ void sr_fp4_byte(uint32_t& acc, f32x2v v, uint32_t se
 // quantize one 16-block held in registers; writes 8 code bytes and 1 scale
 // ---------------------------------------------------------------------------
 template <bool SR>
-__device__ __forceinline__ void quant_block16(const float* r, float s_enc, uint64_t idx0,
-                                              uint32_t k0, uint32_t k1, uint32_t stream,
-                                              uint8_t* codes, uint8_t* scale) {
+__device__ __forceinline__ void quant_block16_regs(const float* r, float s_enc, uint64_t idx0,
+                                                   uint32_t k0, uint32_t k1, uint32_t stream,
+                                                   uint2& packed, uint32_t& sc) {
   float amax_b = 0.0f;
 #pragma unroll
   for (int k = 0; k < 16; ++k) amax_b = __builtin_fmaxf(amax_b, __builtin_fabsf(r[k]));
-  uint32_t sc;
   float e_b;
   block_scale(amax_b, s_enc, sc, e_b);
-  uint2 packed;
   if (SR) {
     // gfx950's v_cvt_scalef32_sr_pk_fp4_f32 (scale 1) rounds element 0 up iff
     // floor(2^22 frac) + seed[31:10] >= 2^22 and element 1 with seed[30:9]
@@ -587,6 +586,15 @@ __device__ __forceinline__ void quant_block16(const float* r, float s_enc, uint6
     packed.x = lo;
     packed.y = hi;
   }
+}
+
+template <bool SR>
+__device__ __forceinline__ void quant_block16(const float* r, float s_enc, uint64_t idx0,
+                                              uint32_t k0, uint32_t k1, uint32_t stream,
+                                              uint8_t* codes, uint8_t* scale) {
+  uint2 packed;
+  uint32_t sc;
+  quant_block16_regs<SR>(r, s_enc, idx0, k0, k1, stream, packed, sc);
   *reinterpret_cast<uint2*>(codes) = packed;
   *scale = (uint8_t)sc;
 }
@@ -637,15 +645,90 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ a, int64_t 
                                                float* __restrict__ mtscale,
                                                const double* __restrict__ tssq,
                                                const double* __restrict__ tmu2,
-                                               float* __restrict__ ratio) {
+                                               float* __restrict__ ratio,
+                                               QOperand B, int64_t bn,
+                                               float* __restrict__ rho, int64_t rho_rows) {
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   const int64_t nb = cols >> 4;
   const int64_t b = (int64_t)blockIdx.x * 64 + tx;   // 16-block index within a row
+  int64_t by = blockIdx.y;
 
-  if (SPLIT && (int64_t)blockIdx.y >= nchunk_ub) {
+  if (SPLIT && rho) {
+    // leading rows of the grid: the rank-one row of the GEMM that takes this
+    // split, rho_j = deq(Q4(mu)) . deq(B_j) (one segment).  The mean is
+    // quantized here as the mean block below quantizes it (same tensor scale,
+    // same draws), dequantized to fp16 in LDS (exact), and each group of 16
+    // lanes sums one row of B against it.
+    if (by < rho_rows) {
+      extern __shared__ __attribute__((aligned(16))) _Float16 r1_mean[];   // [cols]
+      const float am = reduce_partials(tmax_mu, ntmax_mu);
+      float s_enc, s_dec;
+      tensor_scales(am, s_enc, s_dec);
+      for (int64_t mb = threadIdx.x; mb < nb; mb += 256) {
+        float r[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) r[k] = mu[mb * 16 + k];
+        uint2 packed;
+        uint32_t sc;
+        quant_block16_regs<SR>(r, s_enc, (uint64_t)mb * 16, k0, k1, 1u, packed, sc);
+        const half2_t sv = scales2(sc);
+        const half2_t s2 = {sv.x, sv.x};
+        *reinterpret_cast<uint4*>(r1_mean + mb * 16) = deq8(packed.x, s2);
+        *reinterpret_cast<uint4*>(r1_mean + mb * 16 + 8) = deq8(packed.y, s2);
+      }
+      __syncthreads();
+      const int64_t rb = by * gridDim.x + blockIdx.x;   // 16 rows of B per workgroup
+      const int sub = threadIdx.x & 15;
+      const int64_t j = rb * 16 + (threadIdx.x >> 4);
+      const int64_t jj = j < bn ? j : bn - 1;            // every lane joins the butterfly
+      const uint8_t* bc = B.codes + jj * (cols >> 1);
+      const uint8_t* bs = B.scales + jj * nb;
+      float acc = 0.0f;
+      // four blocks per pass, their loads issued before any arithmetic;
+      // blocks past the end are clamped to the last one and dropped
+      constexpr int U = 4;
+      for (int64_t b0 = sub; b0 < nb; b0 += 16 * U) {
+        uint2 w[U];
+        uint32_t sb[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t blk = b0 + 16 * u < nb ? b0 + 16 * u : nb - 1;
+          w[u] = *reinterpret_cast<const uint2*>(bc + 8 * blk);
+          sb[u] = bs[blk];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t blk = b0 + 16 * u < nb ? b0 + 16 * u : nb - 1;
+          const half2_t sv = scales2(sb[u]);
+          const half2_t s2 = {sv.x, sv.x};
+          const uint4 d0 = deq8(w[u].x, s2), d1 = deq8(w[u].y, s2);
+          const uint4 m0 = *reinterpret_cast<const uint4*>(r1_mean + blk * 16);
+          const uint4 m1 = *reinterpret_cast<const uint4*>(r1_mean + blk * 16 + 8);
+          // products of exact fp16 values (<= 6 significant bits each) are
+          // exact; fp32 accumulation
+          float p = 0.0f;
+          p = __builtin_amdgcn_fdot2(h2(d0.x), h2(m0.x), p, false);
+          p = __builtin_amdgcn_fdot2(h2(d0.y), h2(m0.y), p, false);
+          p = __builtin_amdgcn_fdot2(h2(d0.z), h2(m0.z), p, false);
+          p = __builtin_amdgcn_fdot2(h2(d0.w), h2(m0.w), p, false);
+          p = __builtin_amdgcn_fdot2(h2(d1.x), h2(m1.x), p, false);
+          p = __builtin_amdgcn_fdot2(h2(d1.y), h2(m1.y), p, false);
+          p = __builtin_amdgcn_fdot2(h2(d1.z), h2(m1.z), p, false);
+          p = __builtin_amdgcn_fdot2(h2(d1.w), h2(m1.w), p, false);
+          acc += b0 + 16 * u < nb ? p : 0.0f;
+        }
+      }
+      for (int d = 8; d > 0; d >>= 1) acc += __shfl_xor(acc, d, 16);
+      if (sub == 0 && j < bn) rho[j] = acc * (s_dec * B.tscale[1]);
+      return;
+    }
+    by -= rho_rows;
+  }
+
+  if (SPLIT && by >= nchunk_ub) {
     // mean vector of one segment: 1 x cols, SR stream 1, index seg*cols + col
-    const int seg = (int)((int64_t)blockIdx.y - nchunk_ub);
+    const int seg = (int)(by - nchunk_ub);
     const float am = reduce_partials(tmax_mu + (int64_t)seg * ntmax_mu, ntmax_mu);
     float s_enc, s_dec;
     tensor_scales(am, s_enc, s_dec);
@@ -686,11 +769,11 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ a, int64_t 
     return;
   }
 
-  if (!SPLIT && (int64_t)blockIdx.y >= nchunk_ub) {
+  if (!SPLIT && by >= nchunk_ub) {
     // plain: one block per segment publishes the segment's tensor scale
     // (also for empty segments, which have no chunk)
     if (blockIdx.x != 0) return;
-    const int seg = (int)((int64_t)blockIdx.y - nchunk_ub);
+    const int seg = (int)(by - nchunk_ub);
     const SegRange ss = describe_segment(offs, nseg, rows, kStatsRows, seg);
     const float am = reduce_partials(tmax + ss.c0 * ntmax, (ss.c1 - ss.c0) * ntmax);
     float s_enc, s_dec;
@@ -701,7 +784,7 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ a, int64_t 
     }
     return;
   }
-  const SegRange sr = locate_chunk(offs, nseg, rows, kQuantRows, blockIdx.y);
+  const SegRange sr = locate_chunk(offs, nseg, rows, kQuantRows, by);
   if (sr.seg < 0) return;
   float am;
   if (SPLIT) {
@@ -1054,7 +1137,7 @@ static hipError_t run_split_or_plain(const void* a_, int64_t rows, int64_t cols,
                                      const int64_t* offs, int nseg, bool split, bool sr,
                                      uint64_t seed, uint32_t stream_id, const QuantOut& out,
                                      const QuantOut* mean, float* mean_f32, const SplitWs& ws,
-                                     hipStream_t st, float* ratio) {
+                                     hipStream_t st, float* ratio, const Rank1Out* r1) {
   const T* a = static_cast<const T*>(a_);
   const int64_t nchs = chunk_upper_bound(rows, nseg, kStatsRows);
   const int64_t nchq = chunk_upper_bound(rows, nseg, kQuantRows);
@@ -1087,12 +1170,17 @@ static hipError_t run_split_or_plain(const void* a_, int64_t rows, int64_t cols,
     tmax = ws.pamax;
     ntmax = ct_s;
   }
-  dim3 gq((unsigned)ct_q, (unsigned)(nchq + nseg));
+  // rank-one workgroups (16 rows of B each) take the leading grid rows
+  const int64_t rho_rows = r1 ? ((r1->n + 15) / 16 + ct_q - 1) / ct_q : 0;
+  const size_t lds_r1 = r1 ? (size_t)cols * 2 : 0;
+  const QOperand rb = r1 ? r1->b : QOperand{nullptr, nullptr, nullptr};
+  dim3 gq((unsigned)ct_q, (unsigned)(rho_rows + nchq + nseg));
 #define AVERIS_QUANT_LAUNCH(SPL, SRB)                                                        \
-  k_quant<T, SPL, SRB><<<gq, 256, 0, st>>>(                                                 \
+  k_quant<T, SPL, SRB><<<gq, 256, lds_r1, st>>>(                                            \
       a, rows, cols, lda, offs, nseg, nchq, seed, stream_id, ws.mu, tmax, ntmax, ws.tmax_mu, \
       ct_f, out.codes, out.scales, out.tscale, mean ? mean->codes : nullptr,                \
-      mean ? mean->scales : nullptr, mean ? mean->tscale : nullptr, ws.tssq, ws.tmu2, ratio)
+      mean ? mean->scales : nullptr, mean ? mean->tscale : nullptr, ws.tssq, ws.tmu2, ratio, \
+      rb, r1 ? r1->n : 0, r1 ? r1->rho : nullptr, rho_rows)
   if (split) {
     if (sr) AVERIS_QUANT_LAUNCH(true, true); else AVERIS_QUANT_LAUNCH(true, false);
   } else {
@@ -1106,12 +1194,12 @@ hipError_t launch_split_or_plain(const void* a, bool bf16, int64_t rows, int64_t
                                  int64_t lda, const int64_t* offs, int nseg, bool split, bool sr,
                                  uint64_t seed, uint32_t stream_id, const QuantOut& out,
                                  const QuantOut* mean, float* mean_f32, const SplitWs& ws,
-                                 hipStream_t st, float* ratio) {
+                                 hipStream_t st, float* ratio, const Rank1Out* r1) {
   if (bf16)
     return run_split_or_plain<uint16_t>(a, rows, cols, lda, offs, nseg, split, sr, seed,
-                                        stream_id, out, mean, mean_f32, ws, st, ratio);
+                                        stream_id, out, mean, mean_f32, ws, st, ratio, r1);
   return run_split_or_plain<float>(a, rows, cols, lda, offs, nseg, split, sr, seed, stream_id,
-                                   out, mean, mean_f32, ws, st, ratio);
+                                   out, mean, mean_f32, ws, st, ratio, r1);
 }
 
 template <typename T>

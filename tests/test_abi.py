@@ -208,3 +208,25 @@ def test_split_ratio_rejections(L):
     assert sr(nseg=2) == 6                                # no offsets: one segment
     assert sr(offs=P + 4, nseg=4, mean=nv(4, 128)) == 4
     assert sr(offs=P, nseg=4, mean=nv(3, 128)) == 2
+
+
+def test_rank1_rejections(L):
+    res, mean = nv(64, 128), nv(1, 128)
+    b = nv(96, 128)
+    sq = lambda b=b, rho=P, cols=128: L.averis_split_quant_rank1(
+        P, av.BF16, 64, cols, cols, 0, av.SR, ctypes.byref(res), ctypes.byref(mean), None,
+        ctypes.byref(b) if b is not None else None, rho, P, 1 << 30, None)
+    assert sq(b=None) == 1
+    assert sq(rho=None) == 1
+    assert sq(rho=P + 2) == 4
+    assert sq(b=nv(96, 64)) == 2                          # B's K differs
+    assert sq(b=nv(0, 128)) == 2
+    a = nv(64, 128)
+    g = lambda a=a, b=b, rho=P, c=P, ldc=96, dt=av.F32: L.averis_gemm_rank1(
+        ctypes.byref(a), rho, ctypes.byref(b), c, dt, ldc, None)
+    assert g(rho=None) == 1
+    assert g(b=nv(96, 64)) == 2
+    assert g(ldc=32) == 2
+    assert g(dt=2) == 3
+    assert g(c=None) == 1
+    assert g(rho=P + 1) == 4

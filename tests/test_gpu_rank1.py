@@ -1,0 +1,104 @@
+"""GPU parity of the rank-one row formed by the split (averis_split_quant_rank1)
+and of the GEMM that adds it (averis_gemm_rank1): the split's outputs are
+bit for bit those of averis_split_quant; rho = deq(mean) deq(B)^T and
+C = deq(A_R) deq(B)^T + 1 rho^T are within 1e-3 of their bounds against the
+oracle's float64 values from its own quantized operands."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import averis as orc
+from mean_residual_quantized_amd import averis as av
+from mean_residual_quantized_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    av.lib()
+
+
+def check(a, w, which, seed=0, rnd="sr", out_dtype=torch.float32):
+    """which = 'x' (forward: b = Q4(W^T)) or 'd' (dgrad: b = Q4(W))."""
+    r = av.SR if rnd == "sr" else av.RN
+    ag, wg = a.cuda(), w.cuda()
+    b = av.averis_quant(wg, transpose=(which == "x"), rnd=av.RN, sr_stream=av.STREAM_WEIGHT)
+    res, mean, mu, rho = av.averis_split_quant_rank1(ag, b, seed=seed, rnd=r)
+    r2, m2, mu2 = av.averis_split_quant(ag, seed=seed, rnd=r)
+    for x, y in ((res, r2), (mean, m2)):
+        for t in ("codes", "scales", "tscale"):
+            assert torch.equal(getattr(x, t), getattr(y, t)), t
+    assert torch.equal(mu, mu2)
+    wq = orc.weight_quant(w.float().numpy(), "rn")
+    b_ref = wq["fwd"] if which == "x" else wq["dgrad"]
+    s = orc.split_quant(a.float().numpy(), rnd, seed)
+    m_deq, b_deq = orc.dequantize(s["mean"])[0], orc.dequantize(b_ref)
+    rho_ref = b_deq @ m_deq
+    rho_bound = np.abs(b_deq) @ np.abs(m_deq)
+    err = np.abs(rho.cpu().numpy().astype(np.float64) - rho_ref)
+    assert (err <= TOL * rho_bound + 1e-30).all(), np.max(err / np.maximum(rho_bound, 1e-300))
+    c = av.averis_gemm_rank1(res, rho, b, out_dtype=out_dtype)
+    ref = orc.gemm(s["residual"], b_ref, s["mean"])
+    bound = orc.gemm_abs_bound(s["residual"], b_ref, s["mean"])
+    extra = 2.0 ** -8 if out_dtype == torch.bfloat16 else 0.0
+    cc = c.float().cpu().numpy().astype(np.float64)
+    ok = np.abs(cc - ref) <= TOL * bound + extra * np.abs(ref)
+    assert ok.all(), np.max(np.abs(cc - ref) / np.maximum(bound, 1e-300))
+    # the same product as the GEMM that sums the rank-one row itself
+    fn = av.averis_gemm_fwd if which == "x" else av.averis_gemm_dgrad
+    c2 = fn(res, mean, b, out_dtype=torch.float32).cpu().numpy().astype(np.float64)
+    assert (np.abs(c2 - cc) <= 2 * TOL * bound + extra * np.abs(ref)).all()
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("which", ["x", "d"])
+def test_config0(which):
+    cfg = workloads.config0()
+    check(cfg[which], cfg["w"], which)
+
+
+@pytest.mark.parametrize("which", ["x", "d"])
+@pytest.mark.parametrize("l,m,n", [
+    (2048, 320, 192),    # K % 256 != 0 (per-stage scale loads), ragged tiles
+    (1000, 256, 208),    # K % 256 == 0, ragged rows
+    (300, 208, 96),      # K % 64 != 0: the general kernel
+])
+def test_shapes(l, m, n, which):
+    cfg = workloads.config1(l=l, m=m, n=n)
+    check(cfg[which], cfg["w"], which, seed=l)
+
+
+def test_round_to_nearest_and_bf16_output():
+    cfg = workloads.config1(l=1024, m=512, n=384)
+    check(cfg["x"], cfg["w"], "x", rnd="rn", out_dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("which", ["x", "d"])
+def test_full_size_config1(which):
+    # up-proj: forward K = 1024 (256 x 192 tiles, two rounds), dgrad K = 3072;
+    # rho exact against the oracle; the GEMM against the fused-mean GEMM
+    cfg = workloads.config1()
+    a, w = cfg[which], cfg["w"]
+    ag = a.cuda()
+    b = av.averis_quant(w.cuda(), transpose=(which == "x"), rnd=av.RN, sr_stream=av.STREAM_WEIGHT)
+    res, mean, mu, rho = av.averis_split_quant_rank1(ag, b)
+    r2, m2, _ = av.averis_split_quant(ag)
+    assert torch.equal(res.codes, r2.codes) and torch.equal(mean.codes, m2.codes)
+    an = a.float().numpy()
+    mu_ref = orc.column_mean(an)
+    m_deq = orc.dequantize(orc.quantize(mu_ref[None, :], "sr", 0, stream=1))[0]
+    wq = orc.weight_quant(w.float().numpy(), "rn")
+    b_deq = orc.dequantize(wq["fwd"] if which == "x" else wq["dgrad"])
+    err = np.abs(rho.cpu().numpy() - b_deq @ m_deq)
+    assert (err <= TOL * (np.abs(b_deq) @ np.abs(m_deq))).all()
+    c = av.averis_gemm_rank1(res, rho, b, out_dtype=torch.float32)
+    fn = av.averis_gemm_fwd if which == "x" else av.averis_gemm_dgrad
+    c2 = fn(res, mean, b, out_dtype=torch.float32)
+    rel = ((c - c2).abs().max() / c2.abs().max()).item()
+    assert rel < 1e-5, rel

@@ -22,9 +22,16 @@ def _gpu():
     av.lib()
 
 
-def step(x, w, d, vanilla):
+def step(x, w, d, vanilla, rank1=False):
     wt, wd = av.averis_quant_pair(w, rnd=av.RN)
-    if vanilla:
+    if rank1:
+        xr, xm, xmu, rx = av.averis_split_quant_rank1(x, wt, seed=0)
+        y = av.averis_gemm_rank1(xr, rx, wt, out_dtype=torch.bfloat16)
+        dr, dm, dmu, rd = av.averis_split_quant_rank1(d, wd, seed=1)
+        dx = av.averis_gemm_rank1(dr, rd, wd, out_dtype=torch.bfloat16)
+        quants = [wt, wd, xr, xm, dr, dm]
+        extra = [xmu, dmu, rx, rd]
+    elif vanilla:
         xq = av.averis_quant(x, seed=0)
         dq = av.averis_quant(d, seed=1)
         y = av.averis_gemm_vanilla(xq, wt, out_dtype=torch.bfloat16)
@@ -42,17 +49,18 @@ def step(x, w, d, vanilla):
     return flat + extra + [y, dx]
 
 
-@pytest.mark.parametrize("vanilla", [False, True])
+@pytest.mark.parametrize("mode", ["fused", "rank1", "vanilla"])
 @pytest.mark.parametrize("l,m,n", [(1000, 320, 192), (8192, 1024, 3072)])
-def test_graph_replays_match_eager(l, m, n, vanilla):
+def test_graph_replays_match_eager(l, m, n, mode):
     cfg = workloads.config1(l=l, m=m, n=n)
     x, w, d = cfg["x"].cuda(), cfg["w"].cuda(), cfg["d"].cuda()
-    ref = [t.clone() for t in step(x, w, d, vanilla)]
+    vanilla, rank1 = mode == "vanilla", mode == "rank1"
+    ref = [t.clone() for t in step(x, w, d, vanilla, rank1)]
     torch.cuda.synchronize()
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        outs = step(x, w, d, vanilla)
+        outs = step(x, w, d, vanilla, rank1)
     torch.cuda.synchronize()
 
     other = workloads.config1(l=256, m=m, n=n)["x"].cuda()
