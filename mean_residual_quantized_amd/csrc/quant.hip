@@ -423,7 +423,7 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
   }
   __shared__ double ls[NQ][NC], lq[NQ][NC];
   __shared__ float lx[NQ][NC], ln[NQ][NC], lz[NQ][NC];
-  __shared__ int need_exact[NC];
+  __shared__ uint32_t need_mask;   // bit c: column c of the tile failed the certificate
   __shared__ double exact_s[NC];
   __shared__ uint32_t wide_red[128][kWideWords];
   ls[q][jl] = s;
@@ -436,6 +436,7 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
   double t = 0.0, t2 = 0.0, mu2 = 0.0;
   float x1 = -__builtin_inff(), x0 = __builtin_inff();
   const int64_t l = sr.seg_r1 - sr.seg_r0;
+  bool fail = false;
   if (q == 0) {
     float z = __builtin_inff();
 #pragma unroll
@@ -450,26 +451,29 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
     // (ez: binary exponent of the smallest nonzero |a|; P = 7 for bf16 input,
     // 23 for fp32), and every partial sum is at most l * max|a|.  When that
     // bound is <= 2^52 g, every fp64 addition above was exact, in any order.
-    bool fail = false;
     if (j < cols && l > 0 && z < __builtin_inff()) {
       int ez;
       (void)__builtin_frexp((double)z, &ez);
       const double amx = __builtin_fmax(__builtin_fabs((double)x1), __builtin_fabs((double)x0));
       fail = !((double)l * amx <= __builtin_ldexp(1.0, 52 + ez - 1 - (a_bf16 ? 7 : 23)));
     }
-    need_exact[jl] = fail;
+  }
+  // the q == 0 lanes are lanes 0 .. NC-1 of wave 0
+  if (threadIdx.x < 64) {
+    const uint64_t bal = __ballot(fail);
+    if (threadIdx.x == 0) need_mask = (uint32_t)bal;
   }
   __syncthreads();
-  for (int cidx = 0; cidx < NC; ++cidx) {   // uniform: flags from LDS
-    if (need_exact[cidx]) {
-      const double v = exact_column_sum(a, a_bf16, lda, sr.seg_r0, sr.seg_r1,
-                                        (int64_t)blockIdx.x * NC + cidx, wide_red);
-      if (threadIdx.x == 0) exact_s[cidx] = v;
-    }
+  const uint32_t mask = need_mask;   // uniform
+  for (uint32_t mrest = mask; mrest != 0; mrest &= mrest - 1) {
+    const int cidx = __builtin_ctz(mrest);
+    const double v = exact_column_sum(a, a_bf16, lda, sr.seg_r0, sr.seg_r1,
+                                      (int64_t)blockIdx.x * NC + cidx, wide_red);
+    if (threadIdx.x == 0) exact_s[cidx] = v;
   }
-  __syncthreads();
+  if (mask) __syncthreads();
   if (q == 0 && j < cols) {
-    if (need_exact[jl]) t = exact_s[jl];
+    if ((mask >> jl) & 1u) t = exact_s[jl];
     float m = 0.0f;
     if (l > 0) {
       const double md = t / (double)l;

@@ -33,6 +33,20 @@ __device__ __forceinline__ void seg_bounds(const int64_t* offs, int s, int64_t r
   if (b < a) b = a;
 }
 
+// One segment of all rows (offsets == nullptr): the range in closed form.
+__device__ __forceinline__ SegRange plain_range(int64_t rows, int64_t ch, int64_t key, int mode) {
+  const int64_t n = (rows + ch - 1) / ch;
+  SegRange r;
+  r.seg = (mode == 1) ? (key == 0 ? 0 : -1) : (key < n ? 0 : -1);
+  r.seg_r0 = 0;
+  r.seg_r1 = rows;
+  r.c0 = 0;
+  r.c1 = n;
+  r.r0 = mode == 1 ? 0 : key * ch;
+  r.r1 = mode == 1 ? rows : (key * ch + ch < rows ? key * ch + ch : rows);
+  return r;
+}
+
 // Wave-level scan.  Must be called by all 64 lanes of one wavefront; the lane
 // that finds the answer writes it to *out.  mode 0: locate chunk `key`;
 // mode 1: describe segment `key`.
@@ -40,18 +54,7 @@ __device__ inline void seg_scan(const int64_t* offs, int nseg, int64_t rows, int
                                 int64_t key, int mode, SegRange* out) {
   const int lane = threadIdx.x & 63;
   if (offs == nullptr) {
-    if (lane == 0) {
-      const int64_t n = (rows + ch - 1) / ch;
-      SegRange r;
-      r.seg = (mode == 1) ? (key == 0 ? 0 : -1) : (key < n ? 0 : -1);
-      r.seg_r0 = 0;
-      r.seg_r1 = rows;
-      r.c0 = 0;
-      r.c1 = n;
-      r.r0 = mode == 1 ? 0 : key * ch;
-      r.r1 = mode == 1 ? rows : (key * ch + ch < rows ? key * ch + ch : rows);
-      *out = r;
-    }
+    if (lane == 0) *out = plain_range(rows, ch, key, mode);
     return;
   }
   int64_t carry = 0;
@@ -98,9 +101,11 @@ __device__ inline void seg_scan(const int64_t* offs, int nseg, int64_t rows, int
   }
 }
 
-// Block-level wrappers: every thread of the block gets the result.
+// Block-level wrappers: every thread of the block gets the result (without
+// offsets in closed form, with no block synchronization).
 __device__ inline SegRange locate_chunk(const int64_t* offs, int nseg, int64_t rows, int64_t ch,
                                         int64_t chunk) {
+  if (offs == nullptr) return plain_range(rows, ch, chunk, 0);
   __shared__ SegRange sr;
   if (threadIdx.x < 64) seg_scan(offs, nseg, rows, ch, chunk, 0, &sr);
   __syncthreads();
@@ -111,6 +116,7 @@ __device__ inline SegRange locate_chunk(const int64_t* offs, int nseg, int64_t r
 
 __device__ inline SegRange describe_segment(const int64_t* offs, int nseg, int64_t rows,
                                             int64_t ch, int seg) {
+  if (offs == nullptr) return plain_range(rows, ch, seg, 1);
   __shared__ SegRange sr;
   if (threadIdx.x < 64) seg_scan(offs, nseg, rows, ch, seg, 1, &sr);
   __syncthreads();
