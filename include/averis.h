@@ -248,6 +248,25 @@ averis_status_t averis_gemm_rank1(const averis_nvfp4_t* a, const float* rho,
                                   const averis_nvfp4_t* b, void* c, averis_dtype_t cdtype,
                                   int64_t ldc, hipStream_t stream);
 
+/* Grouped forms (expert segments, as averis_split_quant_grouped and
+ * averis_gemm_grouped): b holds nseg stacked N x cols matrices (expert s =
+ * rows s*N .. s*N+N-1, its own tensor scale b->tscale[2s..2s+1]) and
+ *   rho[s*N + j] = deq(mean_s) . deq(b_s,j)   (device float[nseg*N]);
+ * an empty segment has mean 0 and so rho_s = 0.  averis_gemm_grouped_rank1:
+ * c[rows of s] = deq(a_s) deq(b_s)^T + 1 rho_s^T. */
+averis_status_t averis_split_quant_grouped_rank1(const void* a, averis_dtype_t dtype,
+                                                 int64_t rows, int64_t cols, int64_t lda,
+                                                 const int64_t* seg_offsets, int nseg,
+                                                 uint64_t seed, averis_round_t rnd,
+                                                 const averis_nvfp4_t* residual,
+                                                 const averis_nvfp4_t* mean, float* mean_f32,
+                                                 const averis_nvfp4_t* b, float* rho, void* ws,
+                                                 size_t ws_bytes, hipStream_t stream);
+averis_status_t averis_gemm_grouped_rank1(const averis_nvfp4_t* a, const float* rho,
+                                          const averis_nvfp4_t* b, const int64_t* seg_offsets,
+                                          int nseg, void* c, averis_dtype_t cdtype, int64_t ldc,
+                                          hipStream_t stream);
+
 /* Vanilla arm: c = deq(a) deq(b)^T, no mean term. */
 averis_status_t averis_gemm_vanilla(const averis_nvfp4_t* a, const averis_nvfp4_t* b, void* c,
                                     averis_dtype_t cdtype, int64_t ldc, void* ws, size_t ws_bytes,

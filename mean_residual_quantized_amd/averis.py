@@ -30,6 +30,7 @@ EXPORTS = [
     "averis_quant_grouped", "averis_quant_pair", "averis_gemm_fwd", "averis_gemm_dgrad",
     "averis_gemm_vanilla", "averis_gemm_grouped", "averis_residual_t_quant", "averis_gemm_wgrad",
     "averis_split_quant_ratio", "averis_split_quant_rank1", "averis_gemm_rank1",
+    "averis_split_quant_grouped_rank1", "averis_gemm_grouped_rank1",
     "averis_workspace_bytes", "averis_status_str",
     "averis_abi_version", "averis_last_error",
 ]
@@ -76,6 +77,9 @@ def lib():
             "averis_split_quant_ratio": [P, I, I64, I64, I64, P, I, U64, I, T, T, P, P, P, SZ, P],
             "averis_split_quant_rank1": [P, I, I64, I64, I64, U64, I, T, T, P, T, P, P, SZ, P],
             "averis_gemm_rank1": [T, P, T, P, I, I64, P],
+            "averis_split_quant_grouped_rank1": [P, I, I64, I64, I64, P, I, U64, I, T, T, P, T, P,
+                                                 P, SZ, P],
+            "averis_gemm_grouped_rank1": [T, P, T, P, I, P, I, I64, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -377,4 +381,34 @@ def averis_gemm_rank1(a, rho, b, out_dtype=torch.float32, out=None):
     _check("averis_gemm_rank1", lib().averis_gemm_rank1(
         ctypes.byref(ca), rho.data_ptr(), ctypes.byref(cb), c.data_ptr(), _dtype_code(c),
         c.stride(0), _stream()))
+    return c
+
+
+def averis_split_quant_grouped_rank1(a, offsets, b, seed=0, rnd=SR, ws=None):
+    """Grouped split-quant plus rho[s] = deq(mean_s) deq(b_s)^T per segment
+    (b: nseg stacked matrices); returns (residual, mean, mu_f32, rho)."""
+    rows, cols = a.shape
+    nseg = offsets.numel() - 1
+    res = NVFP4.empty(rows, cols, nseg, a.device)
+    mean = NVFP4.empty(nseg, cols, nseg, a.device)
+    mu = torch.empty((nseg, cols), dtype=torch.float32, device=a.device)
+    rho = torch.empty((b.rows,), dtype=torch.float32, device=a.device)
+    need = workspace_bytes(OP_SPLIT_QUANT, rows, cols, 0, nseg)
+    ws = ws if ws is not None else _workspace(need, a.device)
+    r, m, cb = res.c(), mean.c(), b.c()
+    _check("averis_split_quant_grouped_rank1", lib().averis_split_quant_grouped_rank1(
+        a.data_ptr(), _dtype_code(a), rows, cols, _lda(a), offsets.data_ptr(), nseg, seed, rnd,
+        ctypes.byref(r), ctypes.byref(m), mu.data_ptr(), ctypes.byref(cb), rho.data_ptr(),
+        ws.data_ptr(), ws.numel(), _stream()))
+    return res, mean, mu, rho
+
+
+def averis_gemm_grouped_rank1(a, rho, b, offsets, out_dtype=torch.float32, out=None):
+    """c[rows of s] = deq(a_s) deq(b_s)^T + 1 rho_s^T."""
+    nseg = offsets.numel() - 1
+    c = _out(a.rows, b.rows // nseg, out_dtype, a.codes.device, out)
+    ca, cb = a.c(), b.c()
+    _check("averis_gemm_grouped_rank1", lib().averis_gemm_grouped_rank1(
+        ctypes.byref(ca), rho.data_ptr(), ctypes.byref(cb), offsets.data_ptr(), nseg,
+        c.data_ptr(), _dtype_code(c), c.stride(0), _stream()))
     return c

@@ -202,40 +202,88 @@ averis_status_t averis_split_quant_ratio(const void* a, averis_dtype_t dtype, in
                       mean_f32, ws, ws_bytes, stream, ratio);
 }
 
+static averis_status_t split_rank1_common(const void* a, averis_dtype_t dtype, int64_t rows,
+                                          int64_t cols, int64_t lda, const int64_t* offs,
+                                          int nseg, uint64_t seed, averis_round_t rnd,
+                                          const averis_nvfp4_t* residual,
+                                          const averis_nvfp4_t* mean, float* mean_f32,
+                                          const averis_nvfp4_t* b, float* rho, void* ws,
+                                          size_t ws_bytes, hipStream_t stream) {
+  if (!b || !rho) return AVERIS_E_NULL;
+  if (!aligned(rho, 4)) return AVERIS_E_ALIGN;
+  if (cols > kRank1MaxK) return AVERIS_E_SHAPE;
+  if (nseg < 1 || nseg > kMaxSeg) return AVERIS_E_ARG;
+  averis_status_t s = check_tensor(b, b->rows, cols);
+  if (s != AVERIS_OK) return s;
+  const int64_t ns = offs ? nseg : 1;
+  if (b->rows <= 0 || b->rows % ns != 0) return AVERIS_E_SHAPE;
+  const Rank1Out r1{QOperand{b->codes, b->scales, b->tscale}, b->rows / ns, rho};
+  return split_common(a, dtype, rows, cols, lda, offs, nseg, seed, rnd, residual, mean, mean_f32,
+                      ws, ws_bytes, stream, nullptr, &r1);
+}
+
 averis_status_t averis_split_quant_rank1(const void* a, averis_dtype_t dtype, int64_t rows,
                                          int64_t cols, int64_t lda, uint64_t seed,
                                          averis_round_t rnd, const averis_nvfp4_t* residual,
                                          const averis_nvfp4_t* mean, float* mean_f32,
                                          const averis_nvfp4_t* b, float* rho, void* ws,
                                          size_t ws_bytes, hipStream_t stream) {
-  if (!b || !rho) return AVERIS_E_NULL;
-  if (!aligned(rho, 4)) return AVERIS_E_ALIGN;
-  if (cols > kRank1MaxK) return AVERIS_E_SHAPE;
-  averis_status_t s = check_tensor(b, b->rows, cols);
-  if (s != AVERIS_OK) return s;
-  if (b->rows <= 0) return AVERIS_E_SHAPE;
-  const Rank1Out r1{QOperand{b->codes, b->scales, b->tscale}, b->rows, rho};
-  return split_common(a, dtype, rows, cols, lda, nullptr, 1, seed, rnd, residual, mean, mean_f32,
-                      ws, ws_bytes, stream, nullptr, &r1);
+  return split_rank1_common(a, dtype, rows, cols, lda, nullptr, 1, seed, rnd, residual, mean,
+                            mean_f32, b, rho, ws, ws_bytes, stream);
 }
 
-averis_status_t averis_gemm_rank1(const averis_nvfp4_t* a, const float* rho,
-                                  const averis_nvfp4_t* b, void* c, averis_dtype_t cdtype,
-                                  int64_t ldc, hipStream_t stream) {
+averis_status_t averis_split_quant_grouped_rank1(const void* a, averis_dtype_t dtype,
+                                                 int64_t rows, int64_t cols, int64_t lda,
+                                                 const int64_t* seg_offsets, int nseg,
+                                                 uint64_t seed, averis_round_t rnd,
+                                                 const averis_nvfp4_t* residual,
+                                                 const averis_nvfp4_t* mean, float* mean_f32,
+                                                 const averis_nvfp4_t* b, float* rho, void* ws,
+                                                 size_t ws_bytes, hipStream_t stream) {
+  if (!seg_offsets) return AVERIS_E_NULL;
+  if (!aligned(seg_offsets, 8)) return AVERIS_E_ALIGN;
+  return split_rank1_common(a, dtype, rows, cols, lda, seg_offsets, nseg, seed, rnd, residual,
+                            mean, mean_f32, b, rho, ws, ws_bytes, stream);
+}
+
+static averis_status_t gemm_rank1_common(const averis_nvfp4_t* a, const float* rho,
+                                         const averis_nvfp4_t* b, const int64_t* offs, int nseg,
+                                         void* c, averis_dtype_t cdtype, int64_t ldc,
+                                         hipStream_t stream) {
   if (!a || !b || !rho) return AVERIS_E_NULL;
   if (!dtype_ok(cdtype)) return AVERIS_E_DTYPE;
-  const int64_t m = a->rows, k = a->cols, n = b->rows;
-  if (m < 0 || n < 0 || k <= 0 || k % 16 != 0 || b->cols != k) return AVERIS_E_SHAPE;
+  if (nseg < 1 || nseg > kMaxSeg) return AVERIS_E_ARG;
+  const int64_t m = a->rows, k = a->cols;
+  const int64_t ns = offs ? nseg : 1;
+  if (m < 0 || k <= 0 || k % 16 != 0 || b->cols != k) return AVERIS_E_SHAPE;
+  if (b->rows < 0 || b->rows % ns != 0) return AVERIS_E_SHAPE;
+  const int64_t n = b->rows / ns;
   averis_status_t s;
   if ((s = check_tensor(a, m, k)) != AVERIS_OK) return s;
-  if ((s = check_tensor(b, n, k)) != AVERIS_OK) return s;
+  if ((s = check_tensor(b, b->rows, k)) != AVERIS_OK) return s;
   if (!aligned(rho, 4)) return AVERIS_E_ALIGN;
   if (ldc < n) return AVERIS_E_SHAPE;
   if (m > 0 && n > 0 && !c) return AVERIS_E_NULL;
   if (!aligned(c, elem_size(cdtype))) return AVERIS_E_ALIGN;
   const QOperand qa{a->codes, a->scales, a->tscale};
   const QOperand qb{b->codes, b->scales, b->tscale};
-  return hip_status(launch_gemm_rho(qa, rho, qb, m, n, k, c, cdtype == AVERIS_BF16, ldc, stream));
+  return hip_status(launch_gemm_rho(qa, rho, qb, m, n, k, offs, nseg, c, cdtype == AVERIS_BF16, ldc,
+                                    stream));
+}
+
+averis_status_t averis_gemm_rank1(const averis_nvfp4_t* a, const float* rho,
+                                  const averis_nvfp4_t* b, void* c, averis_dtype_t cdtype,
+                                  int64_t ldc, hipStream_t stream) {
+  return gemm_rank1_common(a, rho, b, nullptr, 1, c, cdtype, ldc, stream);
+}
+
+averis_status_t averis_gemm_grouped_rank1(const averis_nvfp4_t* a, const float* rho,
+                                          const averis_nvfp4_t* b, const int64_t* seg_offsets,
+                                          int nseg, void* c, averis_dtype_t cdtype, int64_t ldc,
+                                          hipStream_t stream) {
+  if (!seg_offsets) return AVERIS_E_NULL;
+  if (!aligned(seg_offsets, 8)) return AVERIS_E_ALIGN;
+  return gemm_rank1_common(a, rho, b, seg_offsets, nseg, c, cdtype, ldc, stream);
 }
 
 static averis_status_t quant_common(const void* a, averis_dtype_t dtype, int64_t rows,

@@ -704,18 +704,20 @@ hipError_t launch_gemm(const QOperand& a, const QOperand* mean, const QOperand& 
 }
 
 // C = deq(A) deq(B)^T + 1 rho^T, rho precomputed by the split that made A
+// (per segment when grouped)
 hipError_t launch_gemm_rho(const QOperand& a, const float* rho, const QOperand& b, int64_t m,
-                           int64_t n, int64_t k, void* c, bool c_bf16, int64_t ldc,
-                           hipStream_t st) {
+                           int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
+                           bool c_bf16, int64_t ldc, hipStream_t st) {
   if (m == 0 || n == 0) return hipGetLastError();
-  const int v = ws_pick(m, n, k, 1, false);
-  if (v == 1 || v == 2) return launch_gemm_ws_rho(v, a, rho, b, m, n, k, c, c_bf16, ldc, st);
+  const int v = ws_pick(m, n, k, offs ? nseg : 1, false);
+  if (v == 1 || v == 2)
+    return launch_gemm_ws_rho(v, a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
   // general path (K % 64 != 0): the simple kernel reads rho from global memory
-  dim3 g((unsigned)((n + BN - 1) / BN), (unsigned)chunk_upper_bound(m, 1, BM));
+  dim3 g((unsigned)((n + BN - 1) / BN), (unsigned)chunk_upper_bound(m, offs ? nseg : 1, BM));
   if (c_bf16)
-    k_gemm_nt<true, true><<<g, 256, 0, st>>>(a, b, m, n, k, nullptr, 1, rho, c, ldc);
+    k_gemm_nt<true, true><<<g, 256, 0, st>>>(a, b, m, n, k, offs, nseg, rho, c, ldc);
   else
-    k_gemm_nt<false, true><<<g, 256, 0, st>>>(a, b, m, n, k, nullptr, 1, rho, c, ldc);
+    k_gemm_nt<false, true><<<g, 256, 0, st>>>(a, b, m, n, k, offs, nseg, rho, c, ldc);
   return hipGetLastError();
 }
 

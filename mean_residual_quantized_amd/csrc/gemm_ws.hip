@@ -380,7 +380,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
     }
     if constexpr (RG) {
       // published by the stage-0 barrier below
-      if (pt < BN) rho_sh[pt] = n0 + pt < n ? rho_g[n0 + pt] : 0.0f;
+      if (pt < BN) rho_sh[pt] = n0 + pt < n ? rho_g[(offs ? (int64_t)seg * n : 0) + n0 + pt] : 0.0f;
     } else if constexpr (HAS_MEAN) {
 #pragma unroll
       for (int u = 0; u < kMeanPer; ++u) {
@@ -736,26 +736,27 @@ hipError_t launch_gemm_ws_splitk(const QOperand& a, const QOperand& b, int64_t m
 // rank-one row precomputed: 256 x 192 (variant 1) or 256 x 128 (variant 2) tiles
 template <int TM, int TN>
 hipError_t launch_ws_rho(const QOperand& a, const float* rho, const QOperand& b, int64_t m,
-                         int64_t n, int64_t k, void* c, bool c_bf16, int64_t ldc, hipStream_t st) {
+                         int64_t n, int64_t k, const int64_t* offs, int nseg, void* c, bool c_bf16,
+                         int64_t ldc, hipStream_t st) {
   if (k % 256 == 0) {
     if (c_bf16)
-      return launch_ws<TM, TN, true, true, false, true, true>(a, nullptr, b, m, n, k, nullptr, 1, c,
+      return launch_ws<TM, TN, true, true, false, true, true>(a, nullptr, b, m, n, k, offs, nseg, c,
                                                               ldc, st, 1, 0, rho);
-    return launch_ws<TM, TN, false, true, false, true, true>(a, nullptr, b, m, n, k, nullptr, 1, c,
+    return launch_ws<TM, TN, false, true, false, true, true>(a, nullptr, b, m, n, k, offs, nseg, c,
                                                              ldc, st, 1, 0, rho);
   }
   if (c_bf16)
-    return launch_ws<TM, TN, true, true, false, false, true>(a, nullptr, b, m, n, k, nullptr, 1, c,
+    return launch_ws<TM, TN, true, true, false, false, true>(a, nullptr, b, m, n, k, offs, nseg, c,
                                                              ldc, st, 1, 0, rho);
-  return launch_ws<TM, TN, false, true, false, false, true>(a, nullptr, b, m, n, k, nullptr, 1, c,
+  return launch_ws<TM, TN, false, true, false, false, true>(a, nullptr, b, m, n, k, offs, nseg, c,
                                                             ldc, st, 1, 0, rho);
 }
 
 hipError_t launch_gemm_ws_rho(int variant, const QOperand& a, const float* rho, const QOperand& b,
-                              int64_t m, int64_t n, int64_t k, void* c, bool c_bf16, int64_t ldc,
-                              hipStream_t st) {
-  if (variant == 1) return launch_ws_rho<4, 3>(a, rho, b, m, n, k, c, c_bf16, ldc, st);
-  if (variant == 2) return launch_ws_rho<4, 2>(a, rho, b, m, n, k, c, c_bf16, ldc, st);
+                              int64_t m, int64_t n, int64_t k, const int64_t* offs, int nseg,
+                              void* c, bool c_bf16, int64_t ldc, hipStream_t st) {
+  if (variant == 1) return launch_ws_rho<4, 3>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+  if (variant == 2) return launch_ws_rho<4, 2>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
   return hipErrorInvalidValue;
 }
 

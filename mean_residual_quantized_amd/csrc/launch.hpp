@@ -43,7 +43,8 @@ struct QOperand {
 };
 
 // The rank-one row a split can compute for the GEMM that takes it:
-// rho[j] = deq(Q4(mu)) . deq(b_j) for the n rows of b (one segment).
+// rho[s][j] = deq(Q4(mu_s)) . deq(b_s,j) for the n rows of each segment's b
+// (b holds nseg stacked n x cols matrices).
 struct Rank1Out {
   QOperand b;
   int64_t n;
@@ -85,10 +86,11 @@ hipError_t launch_gemm(const QOperand& a, const QOperand* mean, const QOperand& 
                        int64_t n, int64_t k, const int64_t* offs, int nseg, void* c, bool c_bf16,
                        int64_t ldc, void* ws, hipStream_t st);
 
-// C = deq(A) deq(B)^T + 1 rho^T with rho (n floats) precomputed (one segment).
+// C = deq(A) deq(B)^T + 1 rho^T with rho precomputed (n floats per segment;
+// grouped when offs != nullptr, B then holding nseg stacked N x K matrices).
 hipError_t launch_gemm_rho(const QOperand& a, const float* rho, const QOperand& b, int64_t m,
-                           int64_t n, int64_t k, void* c, bool c_bf16, int64_t ldc,
-                           hipStream_t st);
+                           int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
+                           bool c_bf16, int64_t ldc, hipStream_t st);
 
 // Workspace of a GEMM call (rho, the rank-one term per segment and column).
 size_t gemm_ws_bytes(int64_t n, int64_t k, int nseg);
@@ -102,8 +104,8 @@ hipError_t launch_gemm_ws(int variant, const QOperand& a, const QOperand* mean, 
                           int64_t m, int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
                           bool c_bf16, int64_t ldc, hipStream_t st);
 hipError_t launch_gemm_ws_rho(int variant, const QOperand& a, const float* rho, const QOperand& b,
-                              int64_t m, int64_t n, int64_t k, void* c, bool c_bf16, int64_t ldc,
-                              hipStream_t st);
+                              int64_t m, int64_t n, int64_t k, const int64_t* offs, int nseg,
+                              void* c, bool c_bf16, int64_t ldc, hipStream_t st);
 
 // Split-K product into fp32 partials part[z] (m x n each, row stride n).
 hipError_t launch_gemm_ws_splitk(const QOperand& a, const QOperand& b, int64_t m, int64_t n,

@@ -660,34 +660,42 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ a, int64_t 
 
   if (SPLIT && rho) {
     // leading rows of the grid: the rank-one row of the GEMM that takes this
-    // split, rho_j = deq(Q4(mu)) . deq(B_j) (one segment).  The mean is
-    // quantized here as the mean block below quantizes it (same tensor scale,
-    // same draws), dequantized to fp16 in LDS (exact), and each group of 16
-    // lanes sums one row of B against it.
+    // split, rho[s][j] = deq(Q4(mu_s)) . deq(B_s,j) for each segment s (B
+    // holds one bn x cols matrix per segment).  Each workgroup takes 16 rows
+    // of one segment's B: it quantizes that segment's mean as the mean block
+    // below does (same tensor scale, same draws), dequantizes it to fp16 in
+    // LDS (exact), and each group of 16 lanes sums one row of B against it.
     if (by < rho_rows) {
       extern __shared__ __attribute__((aligned(16))) _Float16 r1_mean[];   // [cols]
-      const float am = reduce_partials(tmax_mu, ntmax_mu);
+      const int64_t groups = (bn + 15) / 16;
+      const int64_t rbi = by * gridDim.x + blockIdx.x;
+      const int rseg = (int)(rbi / groups);
+      if (rseg >= nseg) return;                          // uniform
+      const float am = reduce_partials(tmax_mu + (int64_t)rseg * ntmax_mu, ntmax_mu);
       float s_enc, s_dec;
       tensor_scales(am, s_enc, s_dec);
+      const float* mu_s = mu + (int64_t)rseg * cols;
       for (int64_t mb = threadIdx.x; mb < nb; mb += 256) {
         float r[16];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) r[k] = mu[mb * 16 + k];
+        for (int k = 0; k < 16; ++k) r[k] = mu_s[mb * 16 + k];
         uint2 packed;
         uint32_t sc;
-        quant_block16_regs<SR>(r, s_enc, (uint64_t)mb * 16, k0, k1, 1u, packed, sc);
+        quant_block16_regs<SR>(r, s_enc, (uint64_t)rseg * (uint64_t)cols + (uint64_t)mb * 16, k0,
+                               k1, 1u, packed, sc);
         const half2_t sv = scales2(sc);
         const half2_t s2 = {sv.x, sv.x};
         *reinterpret_cast<uint4*>(r1_mean + mb * 16) = deq8(packed.x, s2);
         *reinterpret_cast<uint4*>(r1_mean + mb * 16 + 8) = deq8(packed.y, s2);
       }
       __syncthreads();
-      const int64_t rb = by * gridDim.x + blockIdx.x;   // 16 rows of B per workgroup
+      const int64_t rb = rbi - (int64_t)rseg * groups;   // 16 rows of the segment's B
       const int sub = threadIdx.x & 15;
       const int64_t j = rb * 16 + (threadIdx.x >> 4);
       const int64_t jj = j < bn ? j : bn - 1;            // every lane joins the butterfly
-      const uint8_t* bc = B.codes + jj * (cols >> 1);
-      const uint8_t* bs = B.scales + jj * nb;
+      const int64_t brow = (int64_t)rseg * bn + jj;
+      const uint8_t* bc = B.codes + brow * (cols >> 1);
+      const uint8_t* bs = B.scales + brow * nb;
       float acc = 0.0f;
       // four blocks per pass, their loads issued before any arithmetic;
       // blocks past the end are clamped to the last one and dropped
@@ -724,7 +732,8 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ a, int64_t 
         }
       }
       for (int d = 8; d > 0; d >>= 1) acc += __shfl_xor(acc, d, 16);
-      if (sub == 0 && j < bn) rho[j] = acc * (s_dec * B.tscale[1]);
+      if (sub == 0 && j < bn)
+        rho[(int64_t)rseg * bn + j] = acc * (s_dec * B.tscale[(offs ? 2 * rseg : 0) + 1]);
       return;
     }
     by -= rho_rows;
@@ -1174,8 +1183,8 @@ static hipError_t run_split_or_plain(const void* a_, int64_t rows, int64_t cols,
     tmax = ws.pamax;
     ntmax = ct_s;
   }
-  // rank-one workgroups (16 rows of B each) take the leading grid rows
-  const int64_t rho_rows = r1 ? ((r1->n + 15) / 16 + ct_q - 1) / ct_q : 0;
+  // rank-one workgroups (16 rows of one segment's B each) take the leading grid rows
+  const int64_t rho_rows = r1 ? ((r1->n + 15) / 16 * nseg + ct_q - 1) / ct_q : 0;
   const size_t lds_r1 = r1 ? (size_t)cols * 2 : 0;
   const QOperand rb = r1 ? r1->b : QOperand{nullptr, nullptr, nullptr};
   dim3 gq((unsigned)ct_q, (unsigned)(rho_rows + nchq + nseg));

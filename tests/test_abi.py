@@ -230,3 +230,21 @@ def test_rank1_rejections(L):
     assert g(dt=2) == 3
     assert g(c=None) == 1
     assert g(rho=P + 1) == 4
+
+
+def test_grouped_rank1_rejections(L):
+    res, mean, b = nv(64, 128), nv(4, 128), nv(4 * 96, 128)
+    sq = lambda offs=P, nseg=4, b=b: L.averis_split_quant_grouped_rank1(
+        P, av.BF16, 64, 128, 128, offs, nseg, 0, av.SR, ctypes.byref(res), ctypes.byref(mean),
+        None, ctypes.byref(b), P, P, 1 << 30, None)
+    assert sq(offs=None) == 1
+    assert sq(offs=P + 4) == 4
+    assert sq(b=nv(4 * 96 + 1, 128)) == 2                 # B rows a multiple of nseg
+    assert sq(nseg=0) == 6
+    a = nv(64, 128)
+    g = lambda offs=P, nseg=4, b=b, ldc=96: L.averis_gemm_grouped_rank1(
+        ctypes.byref(a), P, ctypes.byref(b), offs, nseg, P, av.F32, ldc, None)
+    assert g(offs=None) == 1
+    assert g(nseg=5) == 2
+    assert g(ldc=64) == 2
+    assert g(nseg=0) == 6

@@ -102,3 +102,37 @@ def test_full_size_config1(which):
     c2 = fn(res, mean, b, out_dtype=torch.float32)
     rel = ((c - c2).abs().max() / c2.abs().max()).item()
     assert rel < 1e-5, rel
+
+
+@pytest.mark.parametrize("hidden,inter", [(128, 64), (208, 96)])
+def test_grouped_with_an_empty_segment(hidden, inter):
+    # per-expert rank-one rows; hidden 208 (K % 64 != 0) takes the general kernel
+    cfg = workloads.config3(tokens=256, topk=8, experts=16, hidden=hidden, inter=inter)
+    x, w, offs = cfg["x"], cfg["w"], np.array(cfg["offsets"], dtype=np.int64)
+    x = torch.cat([x[:offs[2]], x[offs[3]:]])        # segment 2 empty
+    offs[3:] -= offs[3] - offs[2]
+    nseg = len(offs) - 1
+    og = torch.from_numpy(offs).cuda()
+    wt = av.averis_quant_batched(w.cuda(), transpose=True)
+    res, mean, mu, rho = av.averis_split_quant_grouped_rank1(x.cuda(), og, wt, seed=5)
+    r2, m2, mu2 = av.averis_split_quant_grouped(x.cuda(), og, seed=5)
+    for a, b in ((res, r2), (mean, m2)):
+        for t in ("codes", "scales", "tscale"):
+            assert torch.equal(getattr(a, t), getattr(b, t)), t
+    assert torch.equal(mu, mu2)
+    c = av.averis_gemm_grouped_rank1(res, rho, wt, og)
+    g = orc.split_quant_grouped(x.float().numpy(), offs, "sr", 5)
+    wrefs = [orc.weight_quant(w[e].float().numpy(), "rn")["fwd"] for e in range(nseg)]
+    n = w.shape[2]
+    rho_c = rho.cpu().numpy().reshape(nseg, n)
+    for s in range(nseg):
+        m_deq, b_deq = orc.dequantize(g["mean"][s])[0], orc.dequantize(wrefs[s])
+        err = np.abs(rho_c[s] - b_deq @ m_deq)
+        assert (err <= TOL * (np.abs(b_deq) @ np.abs(m_deq)) + 1e-30).all(), s
+    assert not rho_c[2].any()
+    ref = orc.gemm_grouped(g["residual"], wrefs, g["mean"])
+    bound = np.concatenate([orc.gemm_abs_bound(g["residual"][s], wrefs[s], g["mean"][s])
+                            for s in range(nseg)])
+    cc = c.cpu().numpy().astype(np.float64)
+    assert (np.abs(cc - ref) <= TOL * bound).all(), np.max(np.abs(cc - ref) / np.maximum(bound, 1e-300))
+    torch.cuda.synchronize()
