@@ -302,7 +302,7 @@ def cpu_baseline(cfg_rows, m, n):
     same workload (split-quant of X and D, both weight copies, the float64
     forward and dgrad GEMMs); reported in TFLOP/s of the sample's GEMMs."""
     from oracle import averis as orc
-    cfg = workloads.config1(l=cfg_rows, m=m, n=n)
+    cfg = workloads.up_proj(l=cfg_rows, m=m, n=n)
     x, w, d = cfg["x"].float().numpy(), cfg["w"].float().numpy(), cfg["d"].float().numpy()
     t0 = time.perf_counter()
     wq = orc.weight_quant(w, "rn")
@@ -335,7 +335,7 @@ def traffic_probe(args):
     torch.cuda.synchronize()
     for _ in range(3):
         dst.copy_(src)
-    cfg = workloads.config1(l=l, m=m, n=n)
+    cfg = workloads.up_proj(l=l, m=m, n=n)
     x, w, d = cfg["x"].cuda(), cfg["w"].cuda(), cfg["d"].cuda()
     torch.cuda.synchronize()
     for _ in range(3):
@@ -392,7 +392,7 @@ def main():
     av.lib()
     l, m, n = args.l, args.m, args.n
     log("bench: generating inputs l=%d m=%d n=%d" % (l, m, n))
-    cfg = workloads.config1(l=l, m=m, n=n)
+    cfg = workloads.up_proj(l=l, m=m, n=n)
     x0, w0, d0 = cfg["x"].cuda(), cfg["w"].cuda(), cfg["d"].cuda()
     bytes_per_set = (x0.numel() + d0.numel()) * 2
     copies = args.copies or max(2, int(np.ceil(640e6 / bytes_per_set)))

@@ -8,7 +8,7 @@ follow the Qwen3-0.6B linears (hidden 1024, intermediate 3072, q 2048).
 
 Conventions: N(a, b) is mean a and variance b; values are drawn in float64,
 rounded to float32, then to bfloat16 by torch (round-to-nearest-even).  Every
-tensor has its own generator seeded by (config, tensor id, linear id).
+tensor has its own generator seeded by (workload, tensor id, linear id).
 """
 
 import numpy as np
@@ -76,7 +76,7 @@ def weight(rng, m, n, dtype=torch.bfloat16):
 # the five workloads
 # --------------------------------------------------------------------------
 
-def config0():
+def tiny():
     """Tiny case: X f32 64x128 (rank-2 spike), W 128x64, D 64x64 = 0.2 + N(0,1)."""
     f32 = torch.float32
     x = mean_biased_activation(rng_for(0, T_X), 64, 128, spike=(4.0, 2.0), tail_sigma=0.5, dtype=f32)
@@ -85,7 +85,7 @@ def config0():
     return dict(x=x, w=w, d=d)
 
 
-def config1(l=8192, m=1024, n=3072):
+def up_proj(l=8192, m=1024, n=3072):
     """Up-proj: X bf16 l x m (mu scale 3, rank-4 spike, tail sigma 0.5), W m x n, D l x n."""
     x = mean_biased_activation(rng_for(1, T_X), l, m)
     w = weight(rng_for(1, T_W), m, n)
@@ -93,7 +93,7 @@ def config1(l=8192, m=1024, n=3072):
     return dict(x=x, w=w, d=d)
 
 
-def config2(l=8192, m=3072, n=1024):
+def down_proj(l=8192, m=3072, n=1024):
     """Down-proj: X = silu(A) * B (positive heavy mean), W m x n, D l x n."""
     x = swiglu_activation(rng_for(2, T_X), l, m)
     w = weight(rng_for(2, T_W), m, n)
@@ -111,7 +111,7 @@ def moe_routing(rng, tokens, experts, topk, zipf_s=1.1):
     return np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
 
 
-def config3(tokens=4096, topk=8, experts=64, hidden=2048, inter=768):
+def moe(tokens=4096, topk=8, experts=64, hidden=2048, inter=768):
     """MoE grouped case: tokens * topk routed rows sorted by expert; per-expert
     mean (scale 2) + N(0, 0.25) rows; W_e hidden x inter; D rows x inter."""
     offsets = moe_routing(rng_for(3, T_ROUTE), tokens, experts, topk)
@@ -134,7 +134,7 @@ def config3(tokens=4096, topk=8, experts=64, hidden=2048, inter=768):
     return dict(x=_cast(x, bf), w=_cast(w, bf), d=_cast(d, bf), offsets=offsets)
 
 
-def config4_linear(name, l=16384):
+def block_linear(name, l=16384):
     """One linear of the Qwen3-0.6B-like block sweep at l tokens."""
     k_in, n_out = QWEN3_06B_LINEARS[name]
     lid = list(QWEN3_06B_LINEARS).index(name)

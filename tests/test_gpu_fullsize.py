@@ -50,12 +50,12 @@ def close(c_rows, ref, bound, bf16):
 
 
 @pytest.mark.parametrize("name", list(workloads.QWEN3_06B_LINEARS))
-def test_config4_linear_sampled(name):
-    cfg = workloads.config4_linear(name)
+def test_block_linear_sampled(name):
+    cfg = workloads.block_linear(name)
     x, w, d = cfg["x"], cfg["w"], cfg["d"]
     l = x.shape[0]
     seed = list(workloads.QWEN3_06B_LINEARS).index(name)
-    print("config 4 linear %s: l=%d, %s -> %s" % (name, l, x.shape[1], d.shape[1]), flush=True)
+    print("block linear %s: l=%d, %s -> %s" % (name, l, x.shape[1], d.shape[1]), flush=True)
     wt, wd = av.averis_quant_pair(w.cuda(), rnd=av.RN)
     wq = orc.weight_quant(f32(w), "rn")
     same(wt, wq["fwd"])
@@ -85,11 +85,11 @@ def test_config4_linear_sampled(name):
     torch.cuda.synchronize()
 
 
-def test_config3_moe_full_size_sampled():
-    cfg = workloads.config3()       # 4096 tokens x top-8 over 64 experts, hidden 2048, inter 768
+def test_moe_full_size_sampled():
+    cfg = workloads.moe()       # 4096 tokens x top-8 over 64 experts, hidden 2048, inter 768
     x, w, d, offs = cfg["x"], cfg["w"], cfg["d"], cfg["offsets"]
     nseg = len(offs) - 1
-    print("config 3: %d rows, %d experts" % (x.shape[0], nseg), flush=True)
+    print("the MoE case: %d rows, %d experts" % (x.shape[0], nseg), flush=True)
     og = torch.from_numpy(offs).cuda()
     counts = np.diff(offs)
     live = [e for e in range(nseg) if counts[e] > 0]

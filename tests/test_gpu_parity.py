@@ -85,13 +85,13 @@ def full_check(x, w, d, seed=0, rnd="sr"):
     torch.cuda.synchronize()
 
 
-def test_config0_tiny():
-    cfg = workloads.config0()
+def test_tiny():
+    cfg = workloads.tiny()
     full_check(cfg["x"], cfg["w"], cfg["d"], seed=0)
 
 
-def test_config0_round_to_nearest_and_other_seed():
-    cfg = workloads.config0()
+def test_tiny_round_to_nearest_and_other_seed():
+    cfg = workloads.tiny()
     full_check(cfg["x"], cfg["w"], cfg["d"], seed=0, rnd="rn")
     full_check(cfg["x"], cfg["w"], cfg["d"], seed=0xABCDEF0123456789)
 
@@ -99,18 +99,18 @@ def test_config0_round_to_nearest_and_other_seed():
 def test_ragged_shapes_several_tiles():
     # rows not a multiple of any chunk or tile; cols not a multiple of the
     # 512/1024-column tiles; N not a multiple of the 128-wide GEMM tile
-    cfg = workloads.config1(l=1000, m=304, n=208)
+    cfg = workloads.up_proj(l=1000, m=304, n=208)
     full_check(cfg["x"], cfg["w"], cfg["d"], seed=7)
 
 
 def test_ragged_rows_and_cols_fast_gemm_path():
     # K % 64 == 0 in both passes (the fast GEMM kernel) with M and N tails
-    cfg = workloads.config1(l=1000, m=320, n=192)
+    cfg = workloads.up_proj(l=1000, m=320, n=192)
     full_check(cfg["x"], cfg["w"], cfg["d"], seed=11)
 
 
 def test_swiglu_shapes_reduced():
-    cfg = workloads.config2(l=520, m=3072, n=1024)
+    cfg = workloads.down_proj(l=520, m=3072, n=1024)
     full_check(cfg["x"], cfg["w"], cfg["d"], seed=3)
 
 
@@ -183,7 +183,7 @@ def test_uncertified_columns_take_the_exact_sum(dtype):
 
 
 def test_bf16_output_within_rounding():
-    cfg = workloads.config1(l=256, m=256, n=128)
+    cfg = workloads.up_proj(l=256, m=256, n=128)
     xg = cfg["x"].cuda()
     wt_g, _ = quant_weights(cfg["w"].cuda())
     res, mean, _ = av.averis_split_quant(xg, seed=0)
@@ -197,7 +197,7 @@ def test_bf16_output_edges_and_strides(l, m, n):
     # bf16 output leaves through an LDS-staged tile: full 16-byte pieces go out
     # as one store, pieces past the tile's edge or in rows that are not
     # 16-byte aligned element by element; both must equal fp32 -> bf16 (RNE)
-    cfg = workloads.config1(l=l, m=m, n=n)
+    cfg = workloads.up_proj(l=l, m=m, n=n)
     xg, dg = cfg["x"].cuda(), cfg["d"].cuda()
     wt_g, wd_g = quant_weights(cfg["w"].cuda())
     for a_g, b_g, fn, cols in [(xg, wt_g, av.averis_gemm_fwd, n), (dg, wd_g, av.averis_gemm_dgrad, m)]:
@@ -217,7 +217,7 @@ def test_bf16_output_edges_and_strides(l, m, n):
 
 
 def test_deterministic_repeats():
-    cfg = workloads.config1(l=512, m=256, n=128)
+    cfg = workloads.up_proj(l=512, m=256, n=128)
     xg = cfg["x"].cuda()
     outs = [av.averis_split_quant(xg, seed=9) for _ in range(3)]
     for r, m, mu in outs[1:]:
@@ -232,7 +232,7 @@ def test_gemm_bitwise_repeatable(l, m, n):
     # MFMA's accumulator before it completed (missing wait states); results
     # then varied between runs.  Repeated runs must agree bit for bit, and
     # with the oracle.
-    cfg = workloads.config1(l=l, m=m, n=n)
+    cfg = workloads.up_proj(l=l, m=m, n=n)
     wt, wd = quant_weights(cfg["w"].cuda())
     xr, xm, _ = av.averis_split_quant(cfg["x"].cuda(), seed=3)
     dr, dm, _ = av.averis_split_quant(cfg["d"].cuda(), seed=4)
@@ -272,8 +272,8 @@ def sampled_rows_check(a, seed, ranges):
 
 
 @pytest.mark.parametrize("which", ["x", "d"])
-def test_full_size_config1_sampled(which):
-    cfg = workloads.config1()
+def test_full_size_up_proj_sampled(which):
+    cfg = workloads.up_proj()
     a = cfg[which]
     l = a.shape[0]
     ranges = [(0, 16), (4093, 4109), (l - 16, l)]
@@ -294,9 +294,9 @@ def test_full_size_config1_sampled(which):
 
 
 @pytest.mark.parametrize("which", ["x", "d"])
-def test_full_size_config2_sampled(which):
+def test_full_size_down_proj_sampled(which):
     # down-proj: SwiGLU-like positive-mean X (8192 x 3072), D 8192 x 1024
-    cfg = workloads.config2()
+    cfg = workloads.down_proj()
     a = cfg[which]
     l = a.shape[0]
     ranges = [(0, 16), (5000, 5016), (l - 16, l)]
@@ -316,7 +316,7 @@ def test_full_size_config2_sampled(which):
 
 
 def test_grouped_moe_reduced():
-    cfg = workloads.config3(tokens=256, topk=8, experts=16, hidden=128, inter=64)
+    cfg = workloads.moe(tokens=256, topk=8, experts=16, hidden=128, inter=64)
     x, w, d, offs = cfg["x"], cfg["w"], cfg["d"], cfg["offsets"]
     nseg = len(offs) - 1
     og = torch.from_numpy(offs).cuda()

@@ -37,7 +37,7 @@ def same_gpu(a, b):
 
 @pytest.mark.parametrize("rnd", ["rn", "sr"])
 def test_full_size_weight_matches_oracle_and_one_copy_calls(rnd):
-    w = workloads.config1()["w"]                 # 1024 x 3072 bf16
+    w = workloads.up_proj()["w"]                 # 1024 x 3072 bf16
     r = av.RN if rnd == "rn" else av.SR
     wg = w.cuda()
     wt, wd = av.averis_quant_pair(wg, seed=3, rnd=r)

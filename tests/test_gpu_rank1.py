@@ -58,8 +58,8 @@ def check(a, w, which, seed=0, rnd="sr", out_dtype=torch.float32):
 
 
 @pytest.mark.parametrize("which", ["x", "d"])
-def test_config0(which):
-    cfg = workloads.config0()
+def test_tiny(which):
+    cfg = workloads.tiny()
     check(cfg[which], cfg["w"], which)
 
 
@@ -70,20 +70,20 @@ def test_config0(which):
     (300, 208, 96),      # K % 64 != 0: the general kernel
 ])
 def test_shapes(l, m, n, which):
-    cfg = workloads.config1(l=l, m=m, n=n)
+    cfg = workloads.up_proj(l=l, m=m, n=n)
     check(cfg[which], cfg["w"], which, seed=l)
 
 
 def test_round_to_nearest_and_bf16_output():
-    cfg = workloads.config1(l=1024, m=512, n=384)
+    cfg = workloads.up_proj(l=1024, m=512, n=384)
     check(cfg["x"], cfg["w"], "x", rnd="rn", out_dtype=torch.bfloat16)
 
 
 @pytest.mark.parametrize("which", ["x", "d"])
-def test_full_size_config1(which):
+def test_full_size_up_proj(which):
     # up-proj: forward K = 1024 (256 x 192 tiles, two rounds), dgrad K = 3072;
     # rho exact against the oracle; the GEMM against the fused-mean GEMM
-    cfg = workloads.config1()
+    cfg = workloads.up_proj()
     a, w = cfg[which], cfg["w"]
     ag = a.cuda()
     b = av.averis_quant(w.cuda(), transpose=(which == "x"), rnd=av.RN, sr_stream=av.STREAM_WEIGHT)
@@ -107,7 +107,7 @@ def test_full_size_config1(which):
 @pytest.mark.parametrize("hidden,inter", [(128, 64), (208, 96)])
 def test_grouped_with_an_empty_segment(hidden, inter):
     # per-expert rank-one rows; hidden 208 (K % 64 != 0) takes the general kernel
-    cfg = workloads.config3(tokens=256, topk=8, experts=16, hidden=hidden, inter=inter)
+    cfg = workloads.moe(tokens=256, topk=8, experts=16, hidden=hidden, inter=inter)
     x, w, offs = cfg["x"], cfg["w"], np.array(cfg["offsets"], dtype=np.int64)
     x = torch.cat([x[:offs[2]], x[offs[3]:]])        # segment 2 empty
     offs[3:] -= offs[3] - offs[2]

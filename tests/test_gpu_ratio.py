@@ -39,8 +39,8 @@ def same_split(a_g, seed=0):
 
 
 @pytest.mark.parametrize("which", ["x", "d"])
-def test_config0(which):
-    a = workloads.config0()[which]
+def test_tiny(which):
+    a = workloads.tiny()[which]
     ratio = same_split(a.cuda())
     close(ratio[0], orc.mean_energy_ratio(a.float().numpy()))
 
@@ -56,8 +56,8 @@ def test_shapes(l, m, dtype):
 
 
 @pytest.mark.parametrize("which", ["x", "d"])
-def test_full_size_config1(which):
-    a = workloads.config1()[which]
+def test_full_size_up_proj(which):
+    a = workloads.up_proj()[which]
     ratio = same_split(a.cuda())
     close(ratio[0], orc.mean_energy_ratio(a.float().numpy()))
 
@@ -71,7 +71,7 @@ def test_degenerate_inputs():
 
 
 def test_grouped_with_an_empty_segment():
-    cfg = workloads.config3(tokens=256, topk=8, experts=16, hidden=128, inter=64)
+    cfg = workloads.moe(tokens=256, topk=8, experts=16, hidden=128, inter=64)
     x, offs = cfg["x"], np.array(cfg["offsets"], dtype=np.int64)
     x = torch.cat([x[:offs[2]], x[offs[3]:]])     # drop segment 2's rows: it is empty
     offs[3:] -= offs[3] - offs[2]

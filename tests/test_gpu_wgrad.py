@@ -74,8 +74,8 @@ def mean_biased(l, m, seed, dtype=torch.bfloat16):
     return torch.from_numpy(a.astype(np.float32)).to(dtype)
 
 
-def test_config0_tiny():
-    cfg = workloads.config0()
+def test_tiny():
+    cfg = workloads.tiny()
     check(cfg["x"], cfg["d"])
 
 
@@ -132,11 +132,11 @@ def test_repeat_calls_give_the_same_bits():
         assert torch.equal(av.averis_gemm_wgrad(xt, dt, mx, md), dw)
 
 
-def test_full_size_config1_sampled():
+def test_full_size_up_proj_sampled():
     # up-proj shapes: X 8192 x 1024, D 8192 x 3072, dW 1024 x 3072 (four
     # splits of 2048 tokens); sampled rows of the transposed residuals are
     # exact, and dW on the sampled rows and columns is within tolerance
-    cfg = workloads.config1()
+    cfg = workloads.up_proj()
     x, d = cfg["x"], cfg["d"]
     l = x.shape[0]
     xt, dt, mx, md, dw = gpu_side(x, d, 0, 1, av.SR)

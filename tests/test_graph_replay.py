@@ -52,7 +52,7 @@ def step(x, w, d, vanilla, rank1=False):
 @pytest.mark.parametrize("mode", ["fused", "rank1", "vanilla"])
 @pytest.mark.parametrize("l,m,n", [(1000, 320, 192), (8192, 1024, 3072)])
 def test_graph_replays_match_eager(l, m, n, mode):
-    cfg = workloads.config1(l=l, m=m, n=n)
+    cfg = workloads.up_proj(l=l, m=m, n=n)
     x, w, d = cfg["x"].cuda(), cfg["w"].cuda(), cfg["d"].cuda()
     vanilla, rank1 = mode == "vanilla", mode == "rank1"
     ref = [t.clone() for t in step(x, w, d, vanilla, rank1)]
@@ -63,7 +63,7 @@ def test_graph_replays_match_eager(l, m, n, mode):
         outs = step(x, w, d, vanilla, rank1)
     torch.cuda.synchronize()
 
-    other = workloads.config1(l=256, m=m, n=n)["x"].cuda()
+    other = workloads.up_proj(l=256, m=m, n=n)["x"].cuda()
     for rep in range(3):
         # eager work of the program's own between replays
         av.averis_split_quant(other, seed=rep)
@@ -80,7 +80,7 @@ def test_graph_replays_match_eager(l, m, n, mode):
 
 def test_wgrad_graph_replays_match_eager():
     # the transposed residual quants and the split-K wgrad (partials + reduce)
-    cfg = workloads.config1(l=2048, m=320, n=192)
+    cfg = workloads.up_proj(l=2048, m=320, n=192)
     x, d = cfg["x"].cuda(), cfg["d"].cuda()
     xr, _, mx = av.averis_split_quant(x, seed=0)
     dr, _, md = av.averis_split_quant(d, seed=1)
@@ -98,7 +98,7 @@ def test_wgrad_graph_replays_match_eager():
         outs = wstep()
     torch.cuda.synchronize()
     for rep in range(3):
-        av.averis_split_quant(workloads.config1(l=256, m=320, n=192)["x"].cuda(), seed=rep)
+        av.averis_split_quant(workloads.up_proj(l=256, m=320, n=192)["x"].cuda(), seed=rep)
         torch.cuda.synchronize()
         for t in outs:
             t.zero_()

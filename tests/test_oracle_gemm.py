@@ -21,8 +21,8 @@ def decode_by_hand(q, i, k):
     return (-mag if code & 8 else mag) * scale * float(q["s_dec"])
 
 
-def test_split_gemm_brute_force_config0():
-    cfg = workloads.config0()
+def test_split_gemm_brute_force_tiny():
+    cfg = workloads.tiny()
     x, w = cfg["x"].numpy(), cfg["w"].numpy()          # 64x128, 128x64
     wq = averis.weight_quant(w, "rn")
     s, y = averis.averis_forward(x, wq["fwd"], "sr", seed=0)
@@ -38,8 +38,8 @@ def test_split_gemm_brute_force_config0():
         assert abs(acc - y[i, j]) <= 1e-12 * max(1.0, abs(acc)), (i, j)
 
 
-def test_dgrad_brute_force_config0():
-    cfg = workloads.config0()
+def test_dgrad_brute_force_tiny():
+    cfg = workloads.tiny()
     d, w = cfg["d"].numpy(), cfg["w"].numpy()          # D 64x64, W 128x64
     wq = averis.weight_quant(w, "rn")
     s, dx = averis.averis_dgrad(d, wq["dgrad"], "sr", seed=0)
@@ -65,8 +65,8 @@ def test_weight_copies_have_the_right_orientation():
 
 def test_unquantized_split_equals_plain_matmul():
     # the split itself is exact algebra: 1 mu^T W + (X - 1 mu^T) W = X W
-    x = workloads.config0()["x"].numpy().astype(np.float64)
-    w = workloads.config0()["w"].numpy().astype(np.float64)
+    x = workloads.tiny()["x"].numpy().astype(np.float64)
+    w = workloads.tiny()["w"].numpy().astype(np.float64)
     mu = x.mean(axis=0)
     y = np.ones((x.shape[0], 1)) @ (mu[None, :] @ w) + (x - mu[None, :]) @ w
     np.testing.assert_allclose(y, x @ w, rtol=1e-12, atol=1e-12 * np.abs(x @ w).max())
@@ -88,7 +88,7 @@ def test_split_preserves_the_tail_better_than_vanilla():
     # mean-driven extremes compress the tail; quantizing X - 1 mu^T instead
     # keeps it.  The residual's quantization error is far below the error of
     # quantizing X itself.
-    cfg = workloads.config1(l=512, m=256, n=128)
+    cfg = workloads.up_proj(l=512, m=256, n=128)
     x = cfg["x"].float().numpy()
     s = averis.split_quant(x, "sr", seed=0)
     xr = averis.residual(x, s["mu"]).astype(np.float64)

@@ -63,7 +63,7 @@ def test_roundtrip_exact_on_grid_times_power_of_two():
 
 
 def test_column_mean_equals_exact_rational_mean():
-    x = workloads.config0()["x"].numpy()
+    x = workloads.tiny()["x"].numpy()
     mu = averis.column_mean(x)
     for j in range(x.shape[1]):
         exact = sum(Fraction(float(v)) for v in x[:, j]) / x.shape[0]
@@ -105,7 +105,7 @@ def test_single_token_is_a_constant_column_case():
 
 
 def test_residual_column_mean_is_zero_before_quantization():
-    x = workloads.config0()["x"].numpy()
+    x = workloads.tiny()["x"].numpy()
     mu = averis.column_mean(x)
     r = averis.residual(x, mu)
     l = x.shape[0]
@@ -119,7 +119,7 @@ def test_residual_column_mean_is_zero_before_quantization():
 
 
 def test_split_shrinks_the_tensor_scale_on_mean_biased_input():
-    x = workloads.config0()["x"].numpy()
+    x = workloads.tiny()["x"].numpy()
     s = averis.split_quant(x, "rn")
     v = averis.vanilla_quant(x, "rn")
     # residual amax is smaller than the raw amax, so S_enc is larger

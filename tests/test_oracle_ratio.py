@@ -37,7 +37,7 @@ def test_pythagorean_split_and_scale_invariance():
     # zero), so R^2 = ||mu||^2 / (||mu||^2 + ||A_R||_F^2 / l); checked with the
     # residual formed in float64 from the exact rational mean of each column
     from fractions import Fraction
-    cfg = workloads.config0()
+    cfg = workloads.tiny()
     x = cfg["x"].float().numpy()
     l = x.shape[0]
     mu = [Fraction(sum(Fraction(float(v)) for v in x[:, j])) / l for j in range(x.shape[1])]
@@ -46,7 +46,7 @@ def test_pythagorean_split_and_scale_invariance():
     ref = math.sqrt(mu2 / (mu2 + res2 / l))
     r = orc.mean_energy_ratio(x)
     assert abs(r - ref) < 1e-14
-    assert 0.5 < r < 1.0               # config 0 is mean-dominated
+    assert 0.5 < r < 1.0               # the tiny case is mean-dominated
     # a power-of-two scale leaves every float exact, so R is unchanged
     assert orc.mean_energy_ratio(x * np.float32(8)) == r
     # the mean-free residual of the split has R near zero
@@ -54,7 +54,7 @@ def test_pythagorean_split_and_scale_invariance():
 
 
 def test_grouped_is_per_segment():
-    cfg = workloads.config0()
+    cfg = workloads.tiny()
     x = cfg["x"].float().numpy()
     offs = [0, 10, 10, 64]
     r = orc.mean_energy_ratio_grouped(x, offs)

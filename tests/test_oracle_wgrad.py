@@ -36,7 +36,7 @@ def test_combination_without_quantization_is_xt_d():
 def test_constant_columns_leave_only_the_mean_term():
     # X with constant columns: X_R = 0, so Q4(X_R^T) is all zero codes and
     # dW = l mu nu^T from the fp32 means (or from the dequantized FP4 means)
-    cfg = workloads.config0()
+    cfg = workloads.tiny()
     mu = (3 * np.random.default_rng(1).standard_normal(128) + 1.5).astype(np.float32)
     x = np.tile(mu, (64, 1))
     d = cfg["d"].float().numpy()
@@ -54,7 +54,7 @@ def test_transposed_residual_quant_is_per_column_quant_of_the_residual():
     # row j of Q4(X_R^T) holds column j of the residual, blocked along the
     # tokens, with one tensor scale for the whole residual (the same amax as
     # the forward's residual)
-    cfg = workloads.config0()
+    cfg = workloads.tiny()
     x = cfg["x"].float().numpy()
     s = orc.split_quant(x, "sr", 2)
     xt = orc.residual_t_quant(x, s["mu"], "sr", 2)
@@ -72,10 +72,10 @@ def test_transposed_residual_quant_is_per_column_quant_of_the_residual():
 
 
 def test_quantized_wgrad_close_to_exact_product():
-    # Q4 error is bounded: the quantized wgrad of config 0 stays near X^T D;
+    # Q4 error is bounded: the quantized wgrad of the tiny case stays near X^T D;
     # FP4 means in the outer product do worse than the fp32 ones on this
     # mean-biased input (their error is not averaged over the tokens)
-    cfg = workloads.config0()
+    cfg = workloads.tiny()
     x, d = cfg["x"].float().numpy(), cfg["d"].float().numpy()
     exact = x.astype(np.float64).T @ d.astype(np.float64)
     rel = lambda a: np.linalg.norm(a - exact) / np.linalg.norm(exact)
@@ -93,7 +93,7 @@ def test_sr_wgrad_is_unbiased_over_seeds():
     # seed average of dW tends to X^T D, up to the small bias of the clamp at
     # 6 (it acts only where a block's E4M3 scale rounded down); with RN in
     # place of SR the average would stay as far off as one sample
-    cfg = workloads.config0()
+    cfg = workloads.tiny()
     x, d = cfg["x"].float().numpy(), cfg["d"].float().numpy()
     exact = x.astype(np.float64).T @ d.astype(np.float64)
     one = orc.averis_wgrad(x, d, "sr", 0, 1000)["dw"]
