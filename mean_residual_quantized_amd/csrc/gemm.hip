@@ -562,12 +562,9 @@ static hipError_t launch_fast(const QOperand& a, const QOperand& mu, const QOper
                               int64_t ldc, hipStream_t st) {
   constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
   const size_t lds = fast_lds_bytes(BM / 64, BN / 64, k, HM);
-  static bool attr_set = false;   // per instantiation; the attribute is idempotent
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_fast<TM, TN, WM, WN, PF, OB, HM>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
+  {
+    const hipError_t e = lds_attr_once<&k_gemm_fast<TM, TN, WM, WN, PF, OB, HM>>((int)kLdsLimit);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int64_t tiles_m = chunk_upper_bound(m, offs ? nseg : 1, BM);
   dim3 g((unsigned)((n + BN - 1) / BN), (unsigned)tiles_m);

@@ -646,12 +646,9 @@ hipError_t launch_ws(const QOperand& a, const QOperand* mean, const QOperand& b,
                      const float* rho = nullptr) {
   constexpr int PF = SG ? 4 : 2, BM = 64 * TM, BN = 64 * TN;
   const size_t lds = ws_lds_bytes(TM, TN, BQ) + (HM && !RG ? (size_t)k * 2 : 0);
-  static bool attr_set = false;   // per instantiation; the attribute is idempotent
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_ws<TM, TN, PF, OB, HM, BQ, SG, RG>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWsLdsLimit);
+  {
+    const hipError_t e = lds_attr_once<&k_gemm_ws<TM, TN, PF, OB, HM, BQ, SG, RG>>((int)kWsLdsLimit);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int64_t tiles_m = chunk_upper_bound(m, offs ? nseg : 1, BM);
   dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)tiles_m, (unsigned)splits);

@@ -1188,16 +1188,21 @@ static hipError_t run_split_or_plain(const void* a_, int64_t rows, int64_t cols,
   const size_t lds_r1 = r1 ? (size_t)cols * 2 : 0;
   const QOperand rb = r1 ? r1->b : QOperand{nullptr, nullptr, nullptr};
   dim3 gq((unsigned)ct_q, (unsigned)(rho_rows + nchq + nseg));
+  // the staged mean of the rank-one workgroups (at most 64 KB)
 #define AVERIS_QUANT_LAUNCH(SPL, SRB)                                                        \
+  if (lds_r1) {                                                                             \
+    const hipError_t e = lds_attr_once<&k_quant<T, SPL, SRB>>(64 * 1024);                   \
+    if (e != hipSuccess) return e;                                                          \
+  }                                                                                         \
   k_quant<T, SPL, SRB><<<gq, 256, lds_r1, st>>>(                                            \
       a, rows, cols, lda, offs, nseg, nchq, seed, stream_id, ws.mu, tmax, ntmax, ws.tmax_mu, \
       ct_f, out.codes, out.scales, out.tscale, mean ? mean->codes : nullptr,                \
       mean ? mean->scales : nullptr, mean ? mean->tscale : nullptr, ws.tssq, ws.tmu2, ratio, \
       rb, r1 ? r1->n : 0, r1 ? r1->rho : nullptr, rho_rows)
   if (split) {
-    if (sr) AVERIS_QUANT_LAUNCH(true, true); else AVERIS_QUANT_LAUNCH(true, false);
+    if (sr) { AVERIS_QUANT_LAUNCH(true, true); } else { AVERIS_QUANT_LAUNCH(true, false); }
   } else {
-    if (sr) AVERIS_QUANT_LAUNCH(false, true); else AVERIS_QUANT_LAUNCH(false, false);
+    if (sr) { AVERIS_QUANT_LAUNCH(false, true); } else { AVERIS_QUANT_LAUNCH(false, false); }
   }
 #undef AVERIS_QUANT_LAUNCH
   return hipGetLastError();
