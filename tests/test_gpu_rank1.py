@@ -136,3 +136,27 @@ def test_grouped_with_an_empty_segment(hidden, inter):
     cc = c.cpu().numpy().astype(np.float64)
     assert (np.abs(cc - ref) <= TOL * bound).all(), np.max(np.abs(cc - ref) / np.maximum(bound, 1e-300))
     torch.cuda.synchronize()
+
+
+def test_no_tokens_gives_a_zero_row():
+    x = torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda")
+    w = workloads.tiny()["w"].cuda()
+    b = av.averis_quant(w, transpose=True, rnd=av.RN, sr_stream=av.STREAM_WEIGHT)
+    res, mean, mu, rho = av.averis_split_quant_rank1(x, b)
+    assert rho.shape == (64,) and not rho.any() and not mu.any()
+    c = av.averis_gemm_rank1(res, rho, b)
+    assert c.shape == (0, 64)
+
+
+@pytest.mark.parametrize("l,m,n", [(1000, 256, 200), (512, 512, 384)])
+def test_bf16_output_strides_and_ragged_columns(l, m, n):
+    # the staged epilogue's element-wise stores (odd strides, ragged last tile)
+    cfg = workloads.up_proj(l=l, m=m, n=n)
+    ag, wg = cfg["x"].cuda(), cfg["w"].cuda()
+    b = av.averis_quant(wg, transpose=True, rnd=av.RN, sr_stream=av.STREAM_WEIGHT)
+    res, mean, mu, rho = av.averis_split_quant_rank1(ag, b, seed=3)
+    ref = av.averis_gemm_rank1(res, rho, b, out_dtype=torch.bfloat16)
+    big = torch.full((l, n + 3), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = av.averis_gemm_rank1(res, rho, b, out_dtype=torch.bfloat16, out=big[:, 1:n + 1])
+    assert torch.equal(out, ref)
+    assert torch.isnan(big[:, 0]).all() and torch.isnan(big[:, n + 1:]).all()
