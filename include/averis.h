@@ -37,7 +37,9 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
- *     library allocates nothing and keeps no state between calls.
+ *     library allocates nothing and keeps no state between calls beyond a
+ *     per-device record that a kernel's LDS limit was raised (set once,
+ *     atomically); calls may come from several threads.
  *   - Work is enqueued on `stream` (NULL = the default stream) and the call
  *     returns without synchronising.  Scales flow device to device.
  *   - Arguments are validated before any HIP call; a rejected call enqueues
