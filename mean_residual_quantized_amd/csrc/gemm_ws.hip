@@ -220,14 +220,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
     uint32_t rbs[PF];
 
     // sw: the stage index mod 8, a compile-time constant wherever these run
-    // (the loop below advances 8 stages per iteration when SG)
+    // (the loop below advances 8 stages per iteration when SG).
+    // Every lane issues every load of the ring, also in the chunk round that
+    // only part of the waves dequantize (their rows are clamped) and past the
+    // last stage (see ld_stage): the compiler counts outstanding loads
+    // exactly only through straight-line code, and a load under a branch makes
+    // it wait for all of them (vmcnt(0)) at the next use, which drains the ring.
     auto gload = [&](int slot, int st, auto sw_c) __attribute__((always_inline)) {
       constexpr int sw = decltype(sw_c)::value;
       if constexpr (W2) {
         // st even: stages st and st + 1 into ring slots slot and slot + 1
 #pragma unroll
         for (int i = 0; i < CP; ++i) {
-          if (pt + kProducers * i >= NCH) break;   // whole waves
           const uint8_t* cb = (i < IA ? a_c : b_c) + 32 * st;
           rc[slot][i] = *reinterpret_cast<const uint4*>(cb + oc_lo[i]);
           rc[slot + 1][i] = *reinterpret_cast<const uint4*>(cb + oc_hi[i]);
@@ -241,7 +245,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
       }
 #pragma unroll
       for (int i = 0; i < CP; ++i) {
-        if (pt + kProducers * i >= NCH) break;   // whole waves
         const uint8_t* cb = (i < IA ? a_c : b_c) + 32 * st;
         rc[slot][i] = *reinterpret_cast<const uint4*>(cb + oc[i]);
         if constexpr (SG) {
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
           rs[slot][i] = *reinterpret_cast<const uint16_t*>(sb + os[i]);
         }
       }
-      if (bcopy) {
+      if constexpr (BQ) {
         const uint8_t* cb = b_c + 32 * st + obc;
         rb[slot][0] = *reinterpret_cast<const uint4*>(cb);
         rb[slot][1] = *reinterpret_cast<const uint4*>(cb + 16);
@@ -368,19 +371,35 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
         }
       }
     }
+    // a load for a stage past the end fetches an in-bounds stage instead
+    // (never dequantized): the last stage, or the last 256-wide scale group
+    // with SG (nk % 4 == 0 there, so nk - 4 >= 0 is a group's first stage)
+    auto ld_stage = [&](int st) __attribute__((always_inline)) {
+      return st < nk ? st : (SG ? nk - 4 : nk - 1);
+    };
+    // RG: every lane loads a value of the rank-one row ahead of the ring (an
+    // in-bounds column for lanes past the tile), so that waiting for it does
+    // not wait for the ring's loads
+    float rho_v = 0.0f;
+    if constexpr (RG) {
+      const int64_t cj = n0 + (pt < BN ? pt : BN - 1);
+      rho_v = rho_g[(offs ? (int64_t)seg * n : 0) + (cj < n ? cj : n - 1)];
+    }
     if constexpr (W2) {
-      // windows 0 and 1 (stages 0..3) fill the ring
+      // windows 0 and 1 (stages 0..3) fill the ring (nk >= 4 with SG)
       gload(0, 0, WsIC<0>{});
-      if (2 < nk) gload(2, 2, WsIC<2>{});
+      gload(2, 2, WsIC<2>{});
     } else {
       ws_unroll<0, PF>([&](auto p_c) __attribute__((always_inline)) {
         constexpr int p = decltype(p_c)::value;
-        if (p < nk) gload(p, p, WsIC<p>{});
+        gload(p, ld_stage(p), WsIC<p>{});
       });
     }
     if constexpr (RG) {
-      // published by the stage-0 barrier below
-      if (pt < BN) rho_sh[pt] = n0 + pt < n ? rho_g[(offs ? (int64_t)seg * n : 0) + n0 + pt] : 0.0f;
+      // published by the stage-0 barrier below; lanes past the tile store
+      // the last column's value again (no branch around the load's use)
+      const int pc = pt < BN ? pt : BN - 1;
+      rho_sh[pc] = n0 + pc < n ? rho_v : 0.0f;
     } else if constexpr (HAS_MEAN) {
 #pragma unroll
       for (int u = 0; u < kMeanPer; ++u) {
@@ -398,9 +417,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
       __syncthreads();   // mean row published (the consumers wait here too)
     }
     dequant(0, 0, 0, WsIC<0>{});
-    if constexpr (!W2) {
-      if (PF < nk) gload(0, PF, WsIC<PF % 8>{});
-    }
+    if constexpr (!W2) gload(0, ld_stage(PF), WsIC<PF % 8>{});
     __syncthreads();
     // iteration it: dequantize stage it + 1 (slot (it + 1) % PF) into buffer
     // (it + 1) & 1, refill that slot with stage it + 1 + PF
@@ -410,17 +427,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
         constexpr int u = decltype(u_c)::value;
         constexpr int su = (u + 1) % PF;
         const int i2 = it + u;
-        if (i2 + 1 < nk) {
-          dequant(su, (i2 + 1) & 1, i2 + 1, WsIC<(u + 1) % 8>{});
-          if constexpr (W2) {
-            // after an odd stage both slots of the window three stages on
-            // are free: stages i2 + 4 and i2 + 5
-            if constexpr (((u + 1) & 1) == 1) {
-              if (i2 + 4 < nk) gload((u + 4) % PF, i2 + 4, WsIC<(u + 4) % 8>{});
-            }
-          } else {
-            if (i2 + 1 + PF < nk) gload(su, i2 + 1 + PF, WsIC<(u + 1 + PF) % 8>{});
-          }
+        if (i2 + 1 < nk) dequant(su, (i2 + 1) & 1, i2 + 1, WsIC<(u + 1) % 8>{});
+        if constexpr (W2) {
+          // after an odd stage both slots of the window three stages on
+          // are free: stages i2 + 4 and i2 + 5
+          if constexpr (((u + 1) & 1) == 1) gload((u + 4) % PF, ld_stage(i2 + 4), WsIC<(u + 4) % 8>{});
+        } else {
+          gload(su, ld_stage(i2 + 1 + PF), WsIC<(u + 1 + PF) % 8>{});
         }
         __syncthreads();
       });
@@ -430,17 +443,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
       constexpr int su = (u + 1) % PF;
       const int i2 = it + u;
       if (i2 < nk) {
-        if (i2 + 1 < nk) {
-          dequant(su, (i2 + 1) & 1, i2 + 1, WsIC<(u + 1) % 8>{});
-          if constexpr (W2) {
-            // after an odd stage both slots of the window three stages on
-            // are free: stages i2 + 4 and i2 + 5
-            if constexpr (((u + 1) & 1) == 1) {
-              if (i2 + 4 < nk) gload((u + 4) % PF, i2 + 4, WsIC<(u + 4) % 8>{});
-            }
-          } else {
-            if (i2 + 1 + PF < nk) gload(su, i2 + 1 + PF, WsIC<(u + 1 + PF) % 8>{});
-          }
+        if (i2 + 1 < nk) dequant(su, (i2 + 1) & 1, i2 + 1, WsIC<(u + 1) % 8>{});
+        if constexpr (W2) {
+          if constexpr (((u + 1) & 1) == 1) gload((u + 4) % PF, ld_stage(i2 + 4), WsIC<(u + 4) % 8>{});
+        } else {
+          gload(su, ld_stage(i2 + 1 + PF), WsIC<(u + 1 + PF) % 8>{});
         }
         __syncthreads();
       }
