@@ -530,12 +530,22 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
   __syncthreads();   // stage 0 in buffer 0
   read_frags(0, 0, 0);
   if constexpr (BQ) read_bscales(0);
+  // EB: a consumer meets the stage barrier as soon as its last fragment
+  // reads of the stage have landed, before the last k-step's MFMAs, and
+  // reads the next stage's first fragments while those MFMAs run (with BQ
+  // the scales of the stage are still in use there: barrier at the end)
+  constexpr bool EB = !BQ;
   for (int it = 0; it < nk; ++it) {
     const int b = it & 1;
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       const int cur = s4 & 1;
-      if (s4 < 3) read_frags(cur ^ 1, b, 16 * (s4 + 1));
+      if (s4 < 3) {
+        read_frags(cur ^ 1, b, 16 * (s4 + 1));
+      } else if constexpr (EB) {
+        __syncthreads();   // buffer b read out; stage it + 1 in buffer b ^ 1
+        if (it + 1 < nk) read_frags(0, b ^ 1, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (BQ) {
 #pragma unroll
@@ -557,10 +567,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
       __builtin_amdgcn_sched_barrier(0);
     }
     if (it + 1 == nk) mfma_drain();   // fence in the block of the last MFMA
-    __syncthreads();
-    if (it + 1 < nk) {
-      read_frags(0, b ^ 1, 0);
-      if constexpr (BQ) read_bscales(b ^ 1);
+    if constexpr (!EB) {
+      __syncthreads();
+      if (it + 1 < nk) {
+        read_frags(0, b ^ 1, 0);
+        if constexpr (BQ) read_bscales(b ^ 1);
+      }
     }
   }
 
