@@ -180,7 +180,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
         const bool is_a = i < IA;
         const int base = (is_a ? 128 * i : 128 * (i - IA)) + 32 * ((pt >> 6) & 3);
         const int64_t lim = is_a ? (m_end - m0) : (n - n0);
-        const int rl = base + ((pt & 63) >> 2), rh = rl + 16;
+        // the four lanes of group g take rows 2g (lo) and 2g + 1 (hi): the
+        // eight lanes of a 128-byte LDS write cycle then write four
+        // consecutive rows, in distinct banks (rows 16 apart share banks)
+        const int rl = base + 2 * ((pt & 63) >> 2), rh = rl + 1;
         const int64_t rowl = rl < lim ? rl : lim - 1, rowh = rh < lim ? rh : lim - 1;
         lrow_lo[i] = rl;
         lrow_hi[i] = rh;
