@@ -75,9 +75,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
   constexpr int IA = 2 * BM / kProducers;                // chunk rounds that hold A rows
   static_assert((2 * BM) % kProducers == 0 && (2 * BN) % 64 == 0, "whole-wave chunk rounds");
   static_assert(!BQ || BN <= kProducers, "one B row per producer thread");
-  static_assert(!(BQ && HAS_MEAN), "the rank-one term is summed from dequantized B chunks");
   static_assert(!RG || HAS_MEAN, "a precomputed rank-one row is a mean term");
   constexpr bool DOTS = HAS_MEAN && !RG;   // the producers sum the rank-one row
+  static_assert(!(BQ && DOTS), "the rank-one term is summed from dequantized B chunks");
   constexpr int CPB = CP - IA;   // chunk rounds that hold B rows
   extern __shared__ __attribute__((aligned(16))) _Float16 smem_ws[];
   _Float16* As = smem_ws;                                // [2][BM][LDSK]
@@ -505,6 +505,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
   half8_t af[2][TM], bf[2][TN];
   uint32_t bw[2][TN];      // BQ: 8 codes of the lane's B row
   half2_t bsc[TN][2];      // BQ: the stage's four block scales of that row
+  uint32_t bsraw[TN];      // BQ: the next stage's scale bytes, read ahead of their conversion
   auto read_frags = [&](int slot, int b, int kk) __attribute__((always_inline)) {
     const _Float16* as = As + b * BM * kWsLdsK + a_frag + kk;
 #pragma unroll
@@ -523,21 +524,27 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
   };
   auto read_bscales = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
+    for (int j = 0; j < TN; ++j) bsraw[j] = Bqs[b * BN + b_row + 32 * j];
+  };
+  auto cvt_bscales = [&]() __attribute__((always_inline)) {
+#pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const uint32_t v = Bqs[b * BN + b_row + 32 * j];
-      bsc[j][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false);
-      bsc[j][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, true);
+      bsc[j][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bsraw[j], 1.0f, false);
+      bsc[j][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bsraw[j], 1.0f, true);
     }
   };
   if constexpr (DOTS) __syncthreads();   // the producers' mean row
   __syncthreads();   // stage 0 in buffer 0
   read_frags(0, 0, 0);
-  if constexpr (BQ) read_bscales(0);
+  if constexpr (BQ) {
+    read_bscales(0);
+    cvt_bscales();
+  }
   // EB: a consumer meets the stage barrier as soon as its last fragment
   // reads of the stage have landed, before the last k-step's MFMAs, and
-  // reads the next stage's first fragments while those MFMAs run (with BQ
-  // the scales of the stage are still in use there: barrier at the end)
-  constexpr bool EB = !BQ;
+  // reads the next stage's first fragments (with BQ: and its scale bytes,
+  // converted once the stage's last MFMAs are issued) while those MFMAs run
+  constexpr bool EB = true;
   for (int it = 0; it < nk; ++it) {
     const int b = it & 1;
 #pragma unroll
@@ -547,7 +554,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
         read_frags(cur ^ 1, b, 16 * (s4 + 1));
       } else if constexpr (EB) {
         __syncthreads();   // buffer b read out; stage it + 1 in buffer b ^ 1
-        if (it + 1 < nk) read_frags(0, b ^ 1, 0);
+        if (it + 1 < nk) {
+          read_frags(0, b ^ 1, 0);
+          if constexpr (BQ) read_bscales(b ^ 1);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (BQ) {
@@ -576,6 +586,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
         read_frags(0, b ^ 1, 0);
         if constexpr (BQ) read_bscales(b ^ 1);
       }
+    }
+    if constexpr (BQ) {
+      if (it + 1 < nk) cvt_bscales();
     }
   }
 
