@@ -50,6 +50,14 @@ arithmetic):
   denominator is the mean squared row norm and 0 <= R <= 1, with R = 1 exactly
   when every row equals mu.  Computed in float64 from exact sums (fsum); R = 0
   when l = 0 or A = 0; per segment when grouped.
+* shared 16x16-block weight (the next step [Lighthouse] §2.2 suggests by
+  writing the dgrad operand as the transpose of the forward one; reading):
+  one quantization of W (m x n) in 16 x 16 tiles, each with one E4M3 scale
+  from the tile's largest magnitude (s_b, c_b, e_b as in Q4; tensor scale from
+  max |W|; SR index i * n + j, stream 2).  Both GEMM copies hold these same
+  codes: the dgrad operand (m x n, blocks of 16 along n) and its transpose,
+  the forward operand (n x m, blocks of 16 along m), each 16-run carrying its
+  tile's scale byte, so deq(forward) = deq(dgrad)^T exactly.
 * grouped (one mean and one tensor scale per expert segment): every step above
   is applied to each segment's rows; SR indices use the global row, the mean
   of segment s uses index s * cols + col; an empty segment has mean 0.
@@ -189,6 +197,41 @@ def weight_quant(w, rnd="rn", seed=0):
     w = np.asarray(w, dtype=np.float32)
     return dict(fwd=quantize(np.ascontiguousarray(w.T), rnd, seed, stream=2),
                 dgrad=quantize(w, rnd, seed, stream=2))
+
+
+def weight_quant_2d(w, rnd="rn", seed=0, stream=2, row0=0):
+    """The shared 16x16-block quantization of W (m x n): returns dict(fwd=...,
+    dgrad=...) in the format of quantize(), fwd = n x m (the transpose) and
+    dgrad = m x n, with the same codes and one scale per 16 x 16 tile.  row0
+    offsets the row in the SR index (matrix b of a batch: b * m)."""
+    w = np.asarray(w, dtype=np.float32)
+    m, n = w.shape
+    if m % BLOCK or n % BLOCK:
+        raise ValueError("rows and cols must be multiples of 16")
+    amax = np.max(np.abs(w)) if w.size else F32(0.0)
+    s_enc, s_dec = tensor_scales(amax)
+    tiles = w.reshape(m // BLOCK, BLOCK, n // BLOCK, BLOCK)
+    amax_t = np.max(np.abs(tiles), axis=(1, 3))                       # (m/16, n/16)
+    s_t = ((amax_t / F32(6.0)).astype(np.float32) * s_enc).astype(np.float32)
+    s_t = np.minimum(s_t, F32(formats.E4M3_MAX))
+    c_t = formats.e4m3_encode(s_t)
+    d_t = formats.e4m3_decode(c_t).astype(np.float32)
+    with np.errstate(divide="ignore"):
+        e_t = np.where(d_t > 0, s_enc / np.where(d_t > 0, d_t, F32(1.0)), F32(0.0)).astype(np.float32)
+    v = (tiles * e_t[:, None, :, None]).astype(np.float32).reshape(m, n)
+    if rnd == "rn":
+        codes = formats.e2m1_round_rn(v)
+    elif rnd == "sr":
+        r_idx = (np.arange(m, dtype=np.uint64) + np.uint64(row0))[:, None]
+        idx = r_idx * np.uint64(n) + np.arange(n, dtype=np.uint64)[None, :]
+        codes = formats.e2m1_round_sr(v, sr_draw16(seed, stream, idx))
+    else:
+        raise ValueError("rnd must be 'rn' or 'sr'")
+    dgrad = dict(codes=formats.pack_nibbles(codes), scales=np.repeat(c_t, BLOCK, axis=0),
+                 s_enc=s_enc, s_dec=s_dec)
+    fwd = dict(codes=formats.pack_nibbles(np.ascontiguousarray(codes.T)),
+               scales=np.repeat(np.ascontiguousarray(c_t.T), BLOCK, axis=0), s_enc=s_enc, s_dec=s_dec)
+    return dict(fwd=fwd, dgrad=dgrad)
 
 
 # --------------------------------------------------------------------------
