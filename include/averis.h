@@ -194,6 +194,22 @@ averis_status_t averis_quant_pair(const void* a, averis_dtype_t dtype, int batch
                                   const averis_nvfp4_t* out, const averis_nvfp4_t* out_t,
                                   void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Both GEMM copies of a weight from ONE quantization in 16 x 16 tiles (the
+ * shared weight that Lighthouse §2.2 implies by writing the dgrad operand as
+ * the transpose of the forward one).  Same arguments, shapes, layouts and
+ * workspace as averis_quant_pair; the difference: each 16 x 16 tile of W_b
+ * has one E4M3 scale, from the tile's largest magnitude, and the codes are
+ * encoded once (SR draw of element (r, c) of W_b: index (b*rows + r) * cols
+ * + c, stream sr_stream) and written in both layouts, so that
+ * deq(out_t) = deq(out)^T exactly.  Every 16-run of out and of out_t carries
+ * its tile's scale byte; the GEMM calls take both copies unchanged.
+ * Errors as averis_quant_pair. */
+averis_status_t averis_quant_pair_2d(const void* a, averis_dtype_t dtype, int batch, int64_t rows,
+                                     int64_t cols, int64_t lda, int64_t batch_stride,
+                                     uint64_t seed, averis_round_t rnd, uint32_t sr_stream,
+                                     const averis_nvfp4_t* out, const averis_nvfp4_t* out_t,
+                                     void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Grouped plain quant of activations: one tensor scale per segment
  * (vanilla arm of the grouped case).  Workspace: AVERIS_OP_QUANT with nseg. */
 averis_status_t averis_quant_grouped(const void* a, averis_dtype_t dtype, int64_t rows,

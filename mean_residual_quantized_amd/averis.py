@@ -27,7 +27,7 @@ STREAM_ACT, STREAM_MEAN, STREAM_WEIGHT, STREAM_RESIDUAL_T = 0, 1, 2, 3
 # every symbol include/averis.h declares
 EXPORTS = [
     "averis_split_quant", "averis_split_quant_grouped", "averis_quant", "averis_quant_batched",
-    "averis_quant_grouped", "averis_quant_pair", "averis_gemm_fwd", "averis_gemm_dgrad",
+    "averis_quant_grouped", "averis_quant_pair", "averis_quant_pair_2d", "averis_gemm_fwd", "averis_gemm_dgrad",
     "averis_gemm_vanilla", "averis_gemm_grouped", "averis_residual_t_quant", "averis_gemm_wgrad",
     "averis_split_quant_ratio", "averis_split_quant_rank1", "averis_gemm_rank1",
     "averis_split_quant_grouped_rank1", "averis_gemm_grouped_rank1",
@@ -68,6 +68,7 @@ def lib():
             "averis_quant_batched": [P, I, I, I64, I64, I64, I64, I, U64, I, U32, T, P, SZ, P],
             "averis_quant_grouped": [P, I, I64, I64, I64, P, I, U64, I, U32, T, P, SZ, P],
             "averis_quant_pair": [P, I, I, I64, I64, I64, I64, U64, I, U32, T, T, P, SZ, P],
+            "averis_quant_pair_2d": [P, I, I, I64, I64, I64, I64, U64, I, U32, T, T, P, SZ, P],
             "averis_gemm_fwd": [T, T, T, P, I, I64, P, SZ, P],
             "averis_gemm_dgrad": [T, T, T, P, I, I64, P, SZ, P],
             "averis_gemm_vanilla": [T, T, P, I, I64, P, SZ, P],
@@ -241,6 +242,24 @@ def averis_quant_pair(w, seed=0, rnd=RN, sr_stream=STREAM_WEIGHT, ws=None):
     ws = ws if ws is not None else _workspace(need, w.device)
     o, ot = wd.c(), wt.c()
     _check("averis_quant_pair", lib().averis_quant_pair(
+        a.data_ptr(), _dtype_code(a), batch, rows, cols, a.stride(1), a.stride(0), seed, rnd,
+        sr_stream, ctypes.byref(o), ctypes.byref(ot), ws.data_ptr(), ws.numel(), _stream()))
+    return wt, wd
+
+
+def averis_quant_pair_2d(w, seed=0, rnd=RN, sr_stream=STREAM_WEIGHT, ws=None):
+    """Both GEMM copies of a weight from one quantization in 16 x 16 tiles:
+    returns (wt, wd) as averis_quant_pair does, with deq(wt) = deq(wd)^T."""
+    a = w if w.dim() == 3 else w.unsqueeze(0)
+    batch, rows, cols = a.shape
+    if a.stride(2) != 1:
+        raise ValueError("expected unit innermost stride")
+    wd = NVFP4.empty(batch * rows, cols, batch, w.device)
+    wt = NVFP4.empty(batch * cols, rows, batch, w.device)
+    need = workspace_bytes(OP_QUANT, rows, cols, 0, batch)
+    ws = ws if ws is not None else _workspace(need, w.device)
+    o, ot = wd.c(), wt.c()
+    _check("averis_quant_pair_2d", lib().averis_quant_pair_2d(
         a.data_ptr(), _dtype_code(a), batch, rows, cols, a.stride(1), a.stride(0), seed, rnd,
         sr_stream, ctypes.byref(o), ctypes.byref(ot), ws.data_ptr(), ws.numel(), _stream()))
     return wt, wd

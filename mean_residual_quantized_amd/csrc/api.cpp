@@ -356,11 +356,11 @@ averis_status_t averis_quant_grouped(const void* a, averis_dtype_t dtype, int64_
                       ws_bytes, stream);
 }
 
-averis_status_t averis_quant_pair(const void* a, averis_dtype_t dtype, int batch, int64_t rows,
-                                  int64_t cols, int64_t lda, int64_t batch_stride, uint64_t seed,
-                                  averis_round_t rnd, uint32_t sr_stream,
-                                  const averis_nvfp4_t* out, const averis_nvfp4_t* out_t,
-                                  void* ws, size_t ws_bytes, hipStream_t stream) {
+static averis_status_t pair_common(bool tiles2d, const void* a, averis_dtype_t dtype, int batch,
+                                   int64_t rows, int64_t cols, int64_t lda, int64_t batch_stride,
+                                   uint64_t seed, averis_round_t rnd, uint32_t sr_stream,
+                                   const averis_nvfp4_t* out, const averis_nvfp4_t* out_t,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!dtype_ok(dtype)) return AVERIS_E_DTYPE;
   if (batch < 1 || batch > kMaxSeg) return AVERIS_E_ARG;
   if (rnd != AVERIS_RN && rnd != AVERIS_SR) return AVERIS_E_ARG;
@@ -380,9 +380,31 @@ averis_status_t averis_quant_pair(const void* a, averis_dtype_t dtype, int batch
   if (!aligned(ws, 256)) return AVERIS_E_ALIGN;
   const QuantOut o{out->codes, out->scales, out->tscale};
   const QuantOut ot{out_t->codes, out_t->scales, out_t->tscale};
+  if (tiles2d)
+    return hip_status(launch_quant_pair2d(a, dtype == AVERIS_BF16, batch, rows, cols, lda,
+                                          batch_stride, rnd == AVERIS_SR, seed, sr_stream, o, ot,
+                                          static_cast<float*>(ws), stream));
   return hip_status(launch_quant_pair(a, dtype == AVERIS_BF16, batch, rows, cols, lda,
                                       batch_stride, rnd == AVERIS_SR, seed, sr_stream, o, ot,
                                       static_cast<float*>(ws), stream));
+}
+
+averis_status_t averis_quant_pair(const void* a, averis_dtype_t dtype, int batch, int64_t rows,
+                                  int64_t cols, int64_t lda, int64_t batch_stride, uint64_t seed,
+                                  averis_round_t rnd, uint32_t sr_stream,
+                                  const averis_nvfp4_t* out, const averis_nvfp4_t* out_t,
+                                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  return pair_common(false, a, dtype, batch, rows, cols, lda, batch_stride, seed, rnd, sr_stream,
+                     out, out_t, ws, ws_bytes, stream);
+}
+
+averis_status_t averis_quant_pair_2d(const void* a, averis_dtype_t dtype, int batch, int64_t rows,
+                                     int64_t cols, int64_t lda, int64_t batch_stride,
+                                     uint64_t seed, averis_round_t rnd, uint32_t sr_stream,
+                                     const averis_nvfp4_t* out, const averis_nvfp4_t* out_t,
+                                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  return pair_common(true, a, dtype, batch, rows, cols, lda, batch_stride, seed, rnd, sr_stream,
+                     out, out_t, ws, ws_bytes, stream);
 }
 
 static averis_status_t gemm_common(const averis_nvfp4_t* a, const averis_nvfp4_t* mean,

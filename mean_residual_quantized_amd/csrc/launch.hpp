@@ -73,6 +73,10 @@ hipError_t launch_quant_pair(const void* a, bool bf16, int batch, int64_t rows, 
                              int64_t lda, int64_t bstride, bool sr, uint64_t seed,
                              uint32_t stream_id, const QuantOut& out, const QuantOut& out_t,
                              float* part, hipStream_t st);
+hipError_t launch_quant_pair2d(const void* a, bool bf16, int batch, int64_t rows, int64_t cols,
+                               int64_t lda, int64_t bstride, bool sr, uint64_t seed,
+                               uint32_t stream_id, const QuantOut& out, const QuantOut& out_t,
+                               float* part, hipStream_t st);
 
 // Q4((a - 1 mu)^T) (cols x rows, blocks along the rows) with the residual's
 // tensor scale tscale_in (2 floats); rows % 16 == 0, cols % 16 == 0.

@@ -162,6 +162,26 @@ def test_quant_pair_rejections(L):
     assert qp(wsb=64) == 5
 
 
+def test_quant_pair_2d_rejections(L):
+    out, out_t = nv(2 * 64, 128), nv(2 * 128, 64)
+    qp = lambda a=P, dt=av.BF16, batch=2, rows=64, cols=128, lda=128, bstride=64 * 128, rnd=av.RN, \
+        out=out, out_t=out_t, ws=P, wsb=1 << 20: L.averis_quant_pair_2d(
+            a, dt, batch, rows, cols, lda, bstride, 0, rnd, 2, ctypes.byref(out),
+            ctypes.byref(out_t), ws, wsb, None)
+    assert qp(batch=0) == 6
+    assert qp(rnd=3) == 6
+    assert qp(dt=5) == 3
+    assert qp(rows=40) == 2                               # 16 x 16 tiles
+    assert qp(cols=24, lda=24) == 2
+    assert qp(bstride=100) == 2
+    assert qp(a=None) == 1
+    assert qp(a=P + 4) == 4
+    assert qp(out_t=nv(2 * 128, 32)) == 2
+    assert qp(out=nv(64, 128)) == 2
+    assert qp(ws=None) == 5
+    assert qp(wsb=64) == 5
+
+
 def test_wgrad_rejections(L):
     # transposed residual quant: out_t is cols x rows, rows (tokens) % 16
     out_t = nv(128, 64)
