@@ -297,6 +297,29 @@ def time_ratio(xs, ds, ws, steps, warmup):
             for name in ("x", "d")}
 
 
+def time_weight_copies(w, ws, steps, warmup):
+    """Both weight copies per call (events on the launch stream, queued behind
+    a spin kernel): the two 1-D quantizations (averis_quant_pair) and the
+    shared 16x16-tile quantization (averis_quant_pair_2d)."""
+    def one(t):
+        t.start("pair")
+        av.averis_quant_pair(w, rnd=av.RN, ws=ws["q"])
+        t.stop("pair")
+        t.start("pair_2d")
+        av.averis_quant_pair_2d(w, rnd=av.RN, ws=ws["q"])
+        t.stop("pair_2d")
+
+    for _ in range(warmup):
+        one(Timer())
+    torch.cuda.synchronize()
+    t = Timer()
+    hold_gpu(5.0 + 0.2 * steps)
+    for _ in range(steps):
+        one(t)
+    torch.cuda.synchronize()
+    return dict(pair_ms=float(np.median(t.ms("pair"))), pair_2d_ms=float(np.median(t.ms("pair_2d"))))
+
+
 def cpu_baseline(cfg_rows, m, n):
     """The oracle as it stands on a bounded sample: cfg_rows tokens of the
     same workload (split-quant of X and D, both weight copies, the float64
@@ -423,6 +446,8 @@ def main():
     wg = time_wgrad(xs, ds, ws, args.steps, args.warmup)
     log("bench: mean-energy ratio")
     mer = time_ratio(xs, ds, ws, args.steps, args.warmup)
+    log("bench: weight copies")
+    wc = time_weight_copies(w0, ws, args.steps, args.warmup)
     # the headline is the device's step time (launches queued ahead of it)
     ms_a, ms_v = ta_ms["queued"], tv_ms["queued"]
 
@@ -500,6 +525,7 @@ def main():
         "overhead_vs_vanilla": overhead,
         "wgrad": wg,
         "mean_energy_ratio": mer,
+        "weight_copies": wc,
         "pages_overhead_context": "2.20% end-to-end over vanilla NVFP4 (hardware not stated)",
     }
     if not args.no_cpu_baseline:
