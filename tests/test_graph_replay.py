@@ -22,8 +22,9 @@ def _gpu():
     av.lib()
 
 
-def step(x, w, d, vanilla, rank1=False):
-    wt, wd = av.averis_quant_pair(w, rnd=av.RN)
+def step(x, w, d, vanilla, rank1=False, shared=False):
+    pair = av.averis_quant_pair_2d if shared else av.averis_quant_pair
+    wt, wd = pair(w, rnd=av.RN)
     if rank1:
         xr, xm, xmu, rx = av.averis_split_quant_rank1(x, wt, seed=0)
         y = av.averis_gemm_rank1(xr, rx, wt, out_dtype=torch.bfloat16)
@@ -49,18 +50,19 @@ def step(x, w, d, vanilla, rank1=False):
     return flat + extra + [y, dx]
 
 
-@pytest.mark.parametrize("mode", ["fused", "rank1", "vanilla"])
+@pytest.mark.parametrize("mode", ["fused", "rank1", "vanilla", "rank1_shared_weight"])
 @pytest.mark.parametrize("l,m,n", [(1000, 320, 192), (8192, 1024, 3072)])
 def test_graph_replays_match_eager(l, m, n, mode):
     cfg = workloads.up_proj(l=l, m=m, n=n)
     x, w, d = cfg["x"].cuda(), cfg["w"].cuda(), cfg["d"].cuda()
-    vanilla, rank1 = mode == "vanilla", mode == "rank1"
-    ref = [t.clone() for t in step(x, w, d, vanilla, rank1)]
+    vanilla, rank1 = mode == "vanilla", mode.startswith("rank1")
+    shared = mode == "rank1_shared_weight"
+    ref = [t.clone() for t in step(x, w, d, vanilla, rank1, shared)]
     torch.cuda.synchronize()
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        outs = step(x, w, d, vanilla, rank1)
+        outs = step(x, w, d, vanilla, rank1, shared)
     torch.cuda.synchronize()
 
     other = workloads.up_proj(l=256, m=m, n=n)["x"].cuda()
