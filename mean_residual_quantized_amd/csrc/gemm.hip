@@ -20,8 +20,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <cstdlib>
-
 #include "gemm_common.hpp"
 #include "launch.hpp"
 #include "segments.hpp"
@@ -165,337 +163,11 @@ __global__ __launch_bounds__(256) void k_gemm_nt(QOperand A, QOperand B, int64_t
     }
 }
 
-// ---------------------------------------------------------------------------
-// Fast path (K % 64 == 0): WG tile (64 TM) x (64 TN), 4 waves in a 2 x 2
-// grid, each wave 32 TM x 32 TN outputs.  Per 64-wide K stage every thread
-// loads raw codes for the next stage into registers while the waves run the
-// MFMAs of the current stage from LDS; the codes are then dequantized with
-// v_cvt_scalef32_pk_f16_fp4 (scale 1) and v_pk_mul_f16 by the E4M3 block
-// scale (both exact) into the other LDS buffer.  One barrier per stage.
-// The rank-one term is fused: the thread that stages row j of B also
-// accumulates sum_k deq'(mean)_k deq'(B)_jk with v_dot2_f32_f16 on the
-// values it has just dequantized, so no extra launch or pass over B.
-// ---------------------------------------------------------------------------
-namespace {
-
-
-
-__device__ __forceinline__ half2_t scale_h2(uint32_t byte) {
-  const _Float16 s = (_Float16)e4m3_value(byte & 0xFFu);
-  half2_t r = {s, s};
-  return r;
-}
-
-
-}  // namespace
-
-
-#ifndef AVERIS_GEMM_INTERLEAVE
-#define AVERIS_GEMM_INTERLEAVE 0
-#endif
-constexpr bool INTERLEAVE = AVERIS_GEMM_INTERLEAVE;
-
-template <int TM, int TN, int WM, int WN, int PF, bool OUT_BF16, bool HAS_MEAN>
-__global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_fast(QOperand A, QOperand B, QOperand MU,
-                                                      int64_t m, int64_t n, int64_t k,
-                                                      const int64_t* offs, int nseg, void* c,
-                                                      int64_t ldc) {
-  constexpr int NT = 64 * WM * WN;                // threads
-  constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
-  // 32-element chunks per thread and stage; when a tile has fewer chunks
-  // than threads, the surplus (whole) wavefronts skip them
-  constexpr int CA = (2 * BM + NT - 1) / NT, CB = (2 * BN + NT - 1) / NT;
-  extern __shared__ __attribute__((aligned(16))) _Float16 smem[];
-  _Float16* As = smem;                          // [2][BM][LDSK]
-  _Float16* Bs = As + 2 * BM * LDSK;            // [2][BN][LDSK]
-  float* rho_sh = reinterpret_cast<float*>(Bs + 2 * BN * LDSK);   // [2][BN]
-  _Float16* Ms = reinterpret_cast<_Float16*>(rho_sh + 2 * BN);    // [k] dequantized mean
-
-  // Workgroups are dispatched round-robin over the 8 XCDs (linear id % 8).
-  // Renumber them so each XCD walks a contiguous, row-major run of tiles:
-  // the tiles an XCD runs together share A rows in its L2.
-  int64_t tile_x, tile_y;
-  {
-    const int64_t gx = gridDim.x, total = gx * gridDim.y;
-    const int64_t lin = (int64_t)blockIdx.y * gx + blockIdx.x;
-    const int64_t even = total - total % kXcds;
-    int64_t id = lin;
-    if (lin < even) id = (lin % kXcds) * (even / kXcds) + lin / kXcds;
-    tile_y = id / gx;
-    tile_x = id - tile_y * gx;
-  }
-  const SegRange sr = locate_chunk(offs, nseg, m, BM, tile_y);
-  if (sr.seg < 0) return;
-  const int seg = sr.seg;
-  const int64_t m0 = sr.r0, m_end = sr.r1;
-  const int64_t n0 = tile_x * BN;
-  const int64_t kh = k >> 1, kb = k >> 4;
-  const uint8_t* bcodes = B.codes + (offs ? (int64_t)seg * n * kh : 0);
-  const uint8_t* bscales = B.scales + (offs ? (int64_t)seg * n * kb : 0);
-
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int wm = w / WN, wn = w % WN;
-
-  if (HAS_MEAN) {
-    // the whole dequantized mean vector (without its tensor scale) in LDS
-    const uint8_t* mcodes = MU.codes + (int64_t)seg * kh;
-    const uint8_t* mscales = MU.scales + (int64_t)seg * kb;
-    for (int64_t q = t; q < (k >> 3); q += NT) {
-      const uint32_t wq = *reinterpret_cast<const uint32_t*>(mcodes + 4 * q);
-      reinterpret_cast<uint4*>(Ms)[q] = deq8(wq, scale_h2(mscales[q >> 1]));
-    }
-  }
-
-  // Staging: chunk q = t + 256 i covers row q >> 1 of the tile, k-half q & 1
-  // of each 64-wide stage.  Rows past the edge are clamped to the last valid
-  // row: their products land only in outputs that are never stored.
-  // Byte offsets are 32-bit and fixed; each stage adds a uniform k offset.
-  const uint8_t* a_c = A.codes + m0 * kh;
-  const uint8_t* a_s = A.scales + m0 * kb;
-  const uint8_t* b_c = bcodes + n0 * kh;
-  const uint8_t* b_s = bscales + n0 * kb;
-  uint32_t oac[CA], oas[CA], obc[CB], obs[CB];
-#pragma unroll
-  for (int i = 0; i < CA; ++i) {
-    const int q = t + NT * i, hf = q & 1;
-    const int64_t row = (q >> 1) < (m_end - m0) ? (q >> 1) : (m_end - m0 - 1);
-    oac[i] = (uint32_t)(row * kh) + 16u * hf;
-    oas[i] = (uint32_t)(row * kb) + 2u * hf;
-  }
-#pragma unroll
-  for (int i = 0; i < CB; ++i) {
-    const int q = t + NT * i, hf = q & 1;
-    const int64_t row = (q >> 1) < (n - n0) ? (q >> 1) : (n - n0 - 1);
-    obc[i] = (uint32_t)(row * kh) + 16u * hf;
-    obs[i] = (uint32_t)(row * kb) + 2u * hf;
-  }
-
-  // raw codes of K stage j live in register slot j % PF
-  uint4 ra[PF][CA], rb[PF][CB];
-  uint32_t sa[PF][CA], sb[PF][CB];
-  float rho_acc[CB];
-#pragma unroll
-  for (int i = 0; i < CB; ++i) rho_acc[i] = 0.0f;
-
-  auto gload = [&](int slot, int64_t k0) {
-    const uint8_t* ac = a_c + (k0 >> 1);
-    const uint8_t* as_ = a_s + (k0 >> 4);
-    const uint8_t* bc = b_c + (k0 >> 1);
-    const uint8_t* bs_ = b_s + (k0 >> 4);
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      if (t + NT * i >= 2 * BM) break;
-      ra[slot][i] = *reinterpret_cast<const uint4*>(ac + oac[i]);
-      sa[slot][i] = *reinterpret_cast<const uint16_t*>(as_ + oas[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      if (t + NT * i >= 2 * BN) break;
-      rb[slot][i] = *reinterpret_cast<const uint4*>(bc + obc[i]);
-      sb[slot][i] = *reinterpret_cast<const uint16_t*>(bs_ + obs[i]);
-    }
-  };
-
-  // dequantize the staged registers into LDS buffer `buf`; B rows also feed
-  // the rank-one partial sums (Ms is written before the first barrier)
-  auto stage = [&](int slot, int buf, int64_t k0) {
-    _Float16* as = As + buf * BM * LDSK;
-    _Float16* bs = Bs + buf * BN * LDSK;
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int q = t + NT * i, row = q >> 1, hf = q & 1;
-      if (q >= 2 * BM) break;
-      const half2_t sc = scales2(sa[slot][i]);
-      const half2_t s0 = {sc.x, sc.x}, s1 = {sc.y, sc.y};
-      uint4* dst = reinterpret_cast<uint4*>(as + row * LDSK + 32 * hf);
-      dst[0] = deq8(ra[slot][i].x, s0);
-      dst[1] = deq8(ra[slot][i].y, s0);
-      dst[2] = deq8(ra[slot][i].z, s1);
-      dst[3] = deq8(ra[slot][i].w, s1);
-    }
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int q = t + NT * i, row = q >> 1, hf = q & 1;
-      if (q >= 2 * BN) break;
-      const half2_t sc = scales2(sb[slot][i]);
-      const half2_t s0 = {sc.x, sc.x}, s1 = {sc.y, sc.y};
-      uint4 d[4];
-      d[0] = deq8(rb[slot][i].x, s0);
-      d[1] = deq8(rb[slot][i].y, s0);
-      d[2] = deq8(rb[slot][i].z, s1);
-      d[3] = deq8(rb[slot][i].w, s1);
-      uint4* dst = reinterpret_cast<uint4*>(bs + row * LDSK + 32 * hf);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dst[e] = d[e];
-      if (HAS_MEAN) {
-        const uint4* mv = reinterpret_cast<const uint4*>(Ms + k0 + 32 * hf);
-        float a = rho_acc[i];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint4 m4 = mv[e];
-          a = __builtin_amdgcn_fdot2(h2(d[e].x), h2(m4.x), a, false);
-          a = __builtin_amdgcn_fdot2(h2(d[e].y), h2(m4.y), a, false);
-          a = __builtin_amdgcn_fdot2(h2(d[e].z), h2(m4.z), a, false);
-          a = __builtin_amdgcn_fdot2(h2(d[e].w), h2(m4.w), a, false);
-        }
-        rho_acc[i] = a;
-      }
-    }
-  };
-
-  f32x16_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  // LDS fragment offsets (in fp16 elements) of this lane
-  const int a_frag = (wm * 32 * TM + (lane & 31)) * LDSK + (lane >> 5) * 8;
-  const int b_frag = (wn * 32 * TN + (lane & 31)) * LDSK + (lane >> 5) * 8;
-  auto mfma_stage = [&](int buf) {
-    const _Float16* as = As + buf * BM * LDSK + a_frag;
-    const _Float16* bs = Bs + buf * BN * LDSK + b_frag;
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      half8_t af[TM], bf[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const half8_t*>(as + i * 32 * LDSK + kk);
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bf[j] = *reinterpret_cast<const half8_t*>(bs + j * 32 * LDSK + kk);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  // One K stage `it`: refill slot it % PF with stage it + PF, run the MFMAs
-  // of LDS buffer it & 1, dequantize stage it + 1 into the other buffer.
-  const int nk = (int)(k / BK);
-  auto step = [&](int it, int slot, bool refill, bool next) {
-    if (refill) gload(slot, (int64_t)(it + PF) * BK);
-    // keep the prefetch loads ahead of everything else in the step: vmcnt
-    // drains in issue order, so a load scheduled after the dequantization
-    // below would make it wait for this step's loads too
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_stage(it & 1);
-    if (!next) mfma_drain();   // last stage: fence in the block of the last MFMA
-    if (next) stage((slot + 1) % PF, (it + 1) & 1, (int64_t)(it + 1) * BK);
-    if (INTERLEAVE && refill && next) {
-      // Ask the scheduler to interleave: each MFMA leaves ~28 idle issue
-      // cycles that the next stage's dequantization (VALU), its LDS writes
-      // and this stage's fragment reads can fill.
-      // coarse groups keep the scheduler's group solver cheap
-      constexpr int NG = BK / 16;                     // one group per k-step
-      constexpr int NM = TM * TN;                     // MFMAs per k-step
-#pragma unroll
-      for (int i = 0; i < NG; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);  // fragment reads
-        __builtin_amdgcn_sched_group_barrier(0x008, NM / 2, 0);   // MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);       // VALU
-        __builtin_amdgcn_sched_group_barrier(0x008, NM / 2, 0);   // MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);        // LDS writes
-      }
-    }
-    __syncthreads();
-  };
-#pragma unroll
-  for (int p = 0; p < PF; ++p)
-    if (p < nk) gload(p, (int64_t)p * BK);
-  if (HAS_MEAN) __syncthreads();   // Ms visible before stage() reads it
-  stage(0, 0, 0);
-  __syncthreads();
-  int it = 0;
-  // steady state: every refill and every next stage exists
-  for (; it + 2 * PF - 1 < nk; it += PF) {
-#pragma unroll
-    for (int u = 0; u < PF; ++u) step(it + u, u, true, true);
-  }
-  // tail: fewer than 2 PF - 1 stages left
-#pragma unroll
-  for (int u = 0; u < 2 * PF - 1; ++u) {
-    const int i2 = it + u;
-    if (i2 < nk) step(i2, u % PF, i2 + PF < nk, i2 + 1 < nk);
-  }
-
-  if (HAS_MEAN) {
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int q = t + NT * i, row = q >> 1, hf = q & 1;
-      if (q >= 2 * BN) break;
-      rho_sh[hf * BN + row] = rho_acc[i];
-    }
-    __syncthreads();
-    // each column's two k-half sums, times the tensor scales, in place
-    const float sd = MU.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
-    for (int cidx = t; cidx < BN; cidx += NT) rho_sh[cidx] = (rho_sh[cidx] + rho_sh[BN + cidx]) * sd;
-    __syncthreads();
-  }
-
-  // The MFMAs take the B fragment first, so a lane's accumulators hold four
-  // consecutive output columns (v & 3) of one output row: 8-byte (bf16) or
-  // 16-byte (fp32) stores.
-  const float alpha = A.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
-  const bool full = (m0 + BM <= m_end) && (n0 + BN <= n);
-  const bool vec = full && (ldc % 4 == 0) &&
-                   ((reinterpret_cast<uintptr_t>(c) & (OUT_BF16 ? 7 : 15)) == 0);
-  const int64_t row_base = m0 + wm * 32 * TM + (lane & 31);
-  const int cl_base = wn * 32 * TN + (lane >> 5) * 4;   // tile-local column of v = 0
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int cl = cl_base + j * 32 + 8 * q;
-      const int64_t col = n0 + cl;
-      f32x4_t r1 = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (HAS_MEAN) r1 = *reinterpret_cast<const f32x4_t*>(rho_sh + cl);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int64_t row = row_base + i * 32;
-        float y[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = acc[i][j][4 * q + e] * alpha + r1[e];
-        if (vec) {
-          if (OUT_BF16) {
-            const u32x2_t pk = {(uint32_t)f32_to_bf16_rne(y[0]) | ((uint32_t)f32_to_bf16_rne(y[1]) << 16),
-                                (uint32_t)f32_to_bf16_rne(y[2]) | ((uint32_t)f32_to_bf16_rne(y[3]) << 16)};
-            store_out(pk, reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(c) + row * ldc + col));
-          } else {
-            const f32x4_t v4 = {y[0], y[1], y[2], y[3]};
-            store_out(v4, reinterpret_cast<f32x4_t*>(static_cast<float*>(c) + row * ldc + col));
-          }
-        } else if (row < m_end) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (col + e >= n) break;
-            if (OUT_BF16)
-              store_out(f32_to_bf16_rne(y[e]), static_cast<uint16_t*>(c) + row * ldc + col + e);
-            else
-              store_out(y[e], static_cast<float*>(c) + row * ldc + col + e);
-          }
-        }
-      }
-    }
-  }
-}
 
 size_t gemm_ws_bytes(int64_t n, int64_t, int nseg) {
   return (size_t)(n * (int64_t)(nseg > 0 ? nseg : 1) * 4 + 255) & ~(size_t)255;
 }
 
-// dynamic LDS of k_gemm_fast
-static size_t fast_lds_bytes(int tm, int tn, int64_t k, bool has_mean) {
-  return (size_t)(2 * 64 * tm * LDSK + 2 * 64 * tn * LDSK) * 2 + (size_t)2 * 64 * tn * 4 +
-         (has_mean ? (size_t)k * 2 : 0);
-}
-
-// 160 KB of LDS per workgroup, less room for the kernel's static LDS (segment lookup)
-constexpr size_t kLdsLimit = 160 * 1024 - 512;
 
 // rho[seg][j] = S_dec(mean_seg) S_dec(B_seg) sum_k deq'(mean_seg)_k deq'(B_seg)_jk
 // (the rank-one term of one output column).  Sixteen lanes per column j, four
@@ -556,129 +228,18 @@ __global__ __launch_bounds__(256) void k_rank1(QOperand M, QOperand B, int64_t n
   }
 }
 
-template <int TM, int TN, int PF, bool OB, bool HM, int WM = 2, int WN = 2>
-static hipError_t launch_fast(const QOperand& a, const QOperand& mu, const QOperand& b, int64_t m,
-                              int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
-                              int64_t ldc, hipStream_t st) {
-  constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
-  const size_t lds = fast_lds_bytes(BM / 64, BN / 64, k, HM);
-  {
-    const hipError_t e = lds_attr_once<&k_gemm_fast<TM, TN, WM, WN, PF, OB, HM>>((int)kLdsLimit);
-    if (e != hipSuccess) return e;
-  }
-  const int64_t tiles_m = chunk_upper_bound(m, offs ? nseg : 1, BM);
-  dim3 g((unsigned)((n + BN - 1) / BN), (unsigned)tiles_m);
-  k_gemm_fast<TM, TN, WM, WN, PF, OB, HM><<<g, 64 * WM * WN, lds, st>>>(a, b, mu, m, n, k, offs, nseg, c, ldc);
-  return hipGetLastError();
-}
-
-template <int TM, int TN, int PF>
-static hipError_t launch_fast_any(const QOperand& a, const QOperand* mean, const QOperand& b,
-                                  int64_t m, int64_t n, int64_t k, const int64_t* offs, int nseg,
-                                  void* c, bool c_bf16, int64_t ldc, hipStream_t st) {
-  const QOperand mu = mean ? *mean : QOperand{nullptr, nullptr, nullptr};
-  if (c_bf16)
-    return mean ? launch_fast<TM, TN, PF, true, true>(a, mu, b, m, n, k, offs, nseg, c, ldc, st)
-                : launch_fast<TM, TN, PF, true, false>(a, mu, b, m, n, k, offs, nseg, c, ldc, st);
-  return mean ? launch_fast<TM, TN, PF, false, true>(a, mu, b, m, n, k, offs, nseg, c, ldc, st)
-              : launch_fast<TM, TN, PF, false, false>(a, mu, b, m, n, k, offs, nseg, c, ldc, st);
-}
-
-// Tile shape for the fast kernel, by estimated time: rounds of workgroups
-// over the 256 CUs times the work of one round, with an efficiency factor per
-// variant (the 8-wave variants run two waves per SIMD and overlap one wave's
-// dequantization with the other's MFMAs; larger tiles dequantize fewer
-// operand values per MFMA).  Returns 0 if the fast kernel does not apply.
-//   1: 256x256, 4 waves   2: 256x128, 4 waves   3: 128x128, 4 waves (2 per CU)
-//   4: 256x256, 8 waves   5: 256x128, 8 waves   6: 256x192, 8 waves
-static int pick_tile(int64_t m, int64_t n, int64_t k, int nseg_eff, bool has_mean) {
-  if (k % BK != 0) return 0;
-  struct Cand { int id, bm, bn, per_cu; double eff; };
-  const Cand cands[6] = {{6, 256, 192, 1, 1.05}, {5, 256, 128, 1, 1.0}, {4, 256, 256, 1, 0.95},
-                         {3, 128, 128, 2, 0.9},  {2, 256, 128, 1, 0.85}, {1, 256, 256, 1, 0.8}};
-  int best = 0;
-  double best_cost = 0;
-  for (const Cand& cd : cands) {
-    if (fast_lds_bytes(cd.bm / 64, cd.bn / 64, k, has_mean) * cd.per_cu > kLdsLimit) continue;
-    const int64_t tiles = chunk_upper_bound(m, nseg_eff, cd.bm) * ((n + cd.bn - 1) / cd.bn);
-    const int64_t slots = 256 * cd.per_cu;
-    const double rounds = (double)((tiles + slots - 1) / slots);
-    const double cost = rounds * cd.bm * cd.bn * cd.per_cu / cd.eff;
-    if (best == 0 || cost < best_cost) {
-      best = cd.id;
-      best_cost = cost;
-    }
-  }
-  return best;
-}
 
 hipError_t launch_gemm(const QOperand& a, const QOperand* mean, const QOperand& b, int64_t m,
                        int64_t n, int64_t k, const int64_t* offs, int nseg, void* c, bool c_bf16,
                        int64_t ldc, void* ws, hipStream_t st) {
   float* rho_ws = static_cast<float*>(ws);
   if (m == 0 || n == 0) return hipGetLastError();
-  // warp-specialized kernel (default); AVERIS_GEMM_KERNEL = 1 selects the
-  // lock-step kernel below, AVERIS_GEMM_WS_TILE = 1..4 forces a variant,
-  // AVERIS_GEMM_BQ = 1 keeps B as codes in LDS
-  static const int kernel_sel = [] {
-    const char* e = std::getenv("AVERIS_GEMM_KERNEL");
-    return e ? std::atoi(e) : 0;
-  }();
-  if (kernel_sel == 0) {
-    int v = ws_pick(m, n, k, offs ? nseg : 1, mean != nullptr);
-    static const int forced_ws = [] {
-      const char* e = std::getenv("AVERIS_GEMM_WS_TILE");
-      return e ? std::atoi(e) : 0;
-    }();
-    static const int bq = [] {
-      const char* e = std::getenv("AVERIS_GEMM_BQ");
-      return e ? std::atoi(e) : 0;
-    }();
-    // B kept as codes in LDS (variants 3, 4) has no rank-one path
-    if (v != 0 && bq == 1 && !mean) v += 2;
-    if (v != 0 && forced_ws >= 1 && forced_ws <= 4 && !(mean && forced_ws > 2)) v = forced_ws;
-    if (v != 0) return launch_gemm_ws(v, a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
-  }
-  int choice = pick_tile(m, n, k, offs ? nseg : 1, mean != nullptr);
-  // tuning override: AVERIS_GEMM_TILE = 1..6 (see pick_tile)
-  static const int forced = [] {
-    const char* e = std::getenv("AVERIS_GEMM_TILE");
-    return e ? std::atoi(e) : 0;
-  }();
-  if (choice != 0 && forced >= 1 && forced <= 6) {
-    static const int dims[7][2] = {{0, 0}, {4, 4}, {4, 2}, {2, 2}, {4, 4}, {4, 2}, {4, 3}};
-    if (fast_lds_bytes(dims[forced][0], dims[forced][1], k, mean != nullptr) <= kLdsLimit)
-      choice = forced;
-  }
-  static const int pf = [] {
-    const char* e = std::getenv("AVERIS_GEMM_PF");
-    return e ? std::atoi(e) : 2;
-  }();
-  const QOperand mu = mean ? *mean : QOperand{nullptr, nullptr, nullptr};
-#define AVERIS_FAST(TM_, TN_)                                                               \
-  switch (pf) {                                                                            \
-    case 1: return launch_fast_any<TM_, TN_, 1>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st); \
-    case 3: return launch_fast_any<TM_, TN_, 3>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st); \
-    default: return launch_fast_any<TM_, TN_, 2>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st); \
-  }
-#define AVERIS_FAST8(TM_, TN_)                                                              \
-  if (c_bf16)                                                                              \
-    return mean ? launch_fast<TM_, TN_, 2, true, true, 4, 2>(a, mu, b, m, n, k, offs, nseg, c, ldc, st) \
-                : launch_fast<TM_, TN_, 2, true, false, 4, 2>(a, mu, b, m, n, k, offs, nseg, c, ldc, st); \
-  return mean ? launch_fast<TM_, TN_, 2, false, true, 4, 2>(a, mu, b, m, n, k, offs, nseg, c, ldc, st) \
-              : launch_fast<TM_, TN_, 2, false, false, 4, 2>(a, mu, b, m, n, k, offs, nseg, c, ldc, st);
-  switch (choice) {
-    case 1: AVERIS_FAST(4, 4)
-    case 2: AVERIS_FAST(4, 2)
-    case 3: AVERIS_FAST(2, 2)
-    case 4: AVERIS_FAST8(2, 4)
-    case 5: AVERIS_FAST8(2, 2)
-    case 6: AVERIS_FAST8(2, 3)
-    default: break;
-  }
-#undef AVERIS_FAST
-#undef AVERIS_FAST8
-  // general path (K % 64 != 0, or a mean vector too long for LDS)
+  // warp-specialized kernel wherever it applies (K % 64 == 0, a mean row that
+  // fits its LDS)
+  const int v = ws_pick(m, n, k, offs ? nseg : 1, mean != nullptr);
+  if (v != 0) return launch_gemm_ws(v, a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+  // general path (K % 64 != 0, or a mean vector too long for LDS): the
+  // rank-one row from its own GEMV, then the simple tiled kernel
   const int ns = offs ? nseg : 1;
   if (mean) {
     dim3 g((unsigned)((n + kRank1Cols - 1) / kRank1Cols), (unsigned)ns);

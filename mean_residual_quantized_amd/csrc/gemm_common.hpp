@@ -68,17 +68,10 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-// output stores: plain by default (L2 merges the partial lines of a row
-// segment); AVERIS_GEMM_NT = 1 makes them non-temporal
-#ifndef AVERIS_GEMM_NT
-#define AVERIS_GEMM_NT 0
-#endif
+// output stores: plain (L2 merges the partial lines of a row segment)
 template <typename T>
 __device__ __forceinline__ void store_out(T v, T* p) {
-  if (AVERIS_GEMM_NT)
-    __builtin_nontemporal_store(v, p);
-  else
-    *p = v;
+  *p = v;
 }
 
 constexpr int kXcds = 8;   // MI355X: 8 accelerator complex dies, one L2 each

@@ -32,8 +32,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <cstdlib>
-
 #include "gemm_common.hpp"
 #include "launch.hpp"
 #include "segments.hpp"
@@ -44,7 +42,6 @@ namespace {
 constexpr int kWsBK = 64;
 constexpr int kWsLdsK = kWsBK + 8;   // fp16 per LDS row (16-byte pad against bank conflicts)
 constexpr int kProducers = 256;      // producer threads (waves 4..7)
-constexpr int kBqLd = 9;             // dwords per B code row in LDS (odd: no bank conflicts)
 
 template <int V>
 struct WsIC {
@@ -63,31 +60,24 @@ __device__ __forceinline__ void ws_unroll(F&& f) {
 
 // RG (with HAS_MEAN): the rank-one row comes precomputed (rho_g, one float
 // per column of B) instead of being summed by the producers from the mean row
-template <int TM, int TN, int PF, bool OUT_BF16, bool HAS_MEAN, bool BQ, bool SG, bool RG = false>
+template <int TM, int TN, int PF, bool OUT_BF16, bool HAS_MEAN, bool SG, bool RG = false>
 __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOperand M, int64_t m,
                                                     int64_t n, int64_t k, const int64_t* offs,
                                                     int nseg, void* c, int64_t ldc, int64_t kld,
                                                     int64_t c_split, const float* rho_g) {
   constexpr int BM = 64 * TM, BN = 64 * TN;
-  // 32-element chunks dequantized per stage: A rows (and B rows unless BQ)
-  constexpr int NCH = BQ ? 2 * BM : 2 * (BM + BN);
+  // 32-element chunks dequantized per stage: A rows and B rows
+  constexpr int NCH = 2 * (BM + BN);
   constexpr int CP = (NCH + kProducers - 1) / kProducers;  // chunks per producer thread
   constexpr int IA = 2 * BM / kProducers;                // chunk rounds that hold A rows
   static_assert((2 * BM) % kProducers == 0 && (2 * BN) % 64 == 0, "whole-wave chunk rounds");
-  static_assert(!BQ || BN <= kProducers, "one B row per producer thread");
   static_assert(!RG || HAS_MEAN, "a precomputed rank-one row is a mean term");
   constexpr bool DOTS = HAS_MEAN && !RG;   // the producers sum the rank-one row
-  static_assert(!(BQ && DOTS), "the rank-one term is summed from dequantized B chunks");
   constexpr int CPB = CP - IA;   // chunk rounds that hold B rows
   extern __shared__ __attribute__((aligned(16))) _Float16 smem_ws[];
   _Float16* As = smem_ws;                                // [2][BM][LDSK]
-  // B as fp16 ([2][BN][LDSK]) or, with BQ, as codes ([2][BN][kBqLd] dwords)
-  // followed by the stage's four E4M3 scale bytes per row ([2][BN] dwords)
-  _Float16* Bs = As + 2 * BM * kWsLdsK;
-  uint32_t* Bq = reinterpret_cast<uint32_t*>(Bs);
-  uint32_t* Bqs = Bq + 2 * BN * kBqLd;
-  float* rho_sh = BQ ? reinterpret_cast<float*>(Bqs + 2 * BN)
-                     : reinterpret_cast<float*>(Bs + 2 * BN * kWsLdsK);   // [BN]
+  _Float16* Bs = As + 2 * BM * kWsLdsK;                  // [2][BN][LDSK]
+  float* rho_sh = reinterpret_cast<float*>(Bs + 2 * BN * kWsLdsK);   // [BN]
   // HAS_MEAN: the segment's mean row, dequantized to fp16 once ([k])
   _Float16* mean_sh = reinterpret_cast<_Float16*>(rho_sh + BN);
 
@@ -118,8 +108,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
   // direct store writes 16 bytes into each of 32 lines, and the L2's write
   // request rate, not its bandwidth, bounds the epilogue)
   constexpr int kStLd = 2 * BN + 16;   // staged row, bytes (16-byte aligned, staggered banks)
-  constexpr size_t kStageRoom = (size_t)2 * BM * kWsLdsK * 2 +
-                                (BQ ? (size_t)2 * BN * (kBqLd + 1) * 4 : (size_t)2 * BN * kWsLdsK * 2);
+  constexpr size_t kStageRoom = (size_t)2 * (BM + BN) * kWsLdsK * 2;
   constexpr bool kCanStage = OUT_BF16 && (size_t)BM * kStLd <= kStageRoom;
   constexpr bool stage_out = kCanStage;   // every tile of a bf16 output
   // pieces that lie wholly inside the output, with 16-byte aligned rows, go
@@ -169,7 +158,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
     // The loads touch half as many cache lines per byte.  Used with three
     // column fragments per consumer wave (48 MFMAs per stage); with two, the
     // stage is too short for the producers' extra selects (measured slower).
-    constexpr bool W2 = SG && !BQ && TN == 3;
+    constexpr bool W2 = SG && TN == 3;
     const int w2_p = pt & 3;                      // 16-byte piece of the 64-byte window
     const bool w2_sel = (w2_p >> 1) != 0;         // row lo holds the window's second stage
     uint32_t oc_lo[CP], oc_hi[CP], os_lo[CP], os_hi[CP];
@@ -214,13 +203,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
     uint32_t rs[PF][CP];
     uint4 rsg[2][CP];
     uint4 rsg_hi[2][CP];   // W2: the scale groups of row hi
-    // BQ: B row pt is copied as loaded (32 code bytes and 4 scale bytes per stage)
-    const bool bcopy = BQ && pt < BN;
-    const int64_t blim = n - n0;
-    const int64_t brow = pt < blim ? pt : blim - 1;
-    const uint32_t obc = (uint32_t)(brow * kh), obs = (uint32_t)(brow * kb);
-    uint4 rb[PF][2];
-    uint32_t rbs[PF];
 
     // sw: the stage index mod 8, a compile-time constant wherever these run
     // (the loop below advances 8 stages per iteration when SG).
@@ -259,12 +241,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
           const uint8_t* sb = (i < IA ? a_s : b_s) + 4 * st;
           rs[slot][i] = *reinterpret_cast<const uint16_t*>(sb + os[i]);
         }
-      }
-      if constexpr (BQ) {
-        const uint8_t* cb = b_c + 32 * st + obc;
-        rb[slot][0] = *reinterpret_cast<const uint4*>(cb);
-        rb[slot][1] = *reinterpret_cast<const uint4*>(cb + 16);
-        rbs[slot] = *reinterpret_cast<const uint32_t*>(b_s + 4 * st + obs);
       }
     };
     // HAS_MEAN: rank-one partial sums of the chunk rows that hold B, in
@@ -340,13 +316,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
             }
           }
         }
-      }
-      if (bcopy) {
-        uint32_t* dst = Bq + (buf * BN + pt) * kBqLd;
-        const uint4 c0 = rb[slot][0], c1 = rb[slot][1];
-        dst[0] = c0.x; dst[1] = c0.y; dst[2] = c0.z; dst[3] = c0.w;
-        dst[4] = c1.x; dst[5] = c1.y; dst[6] = c1.z; dst[7] = c1.w;
-        Bqs[buf * BN + pt] = rbs[slot];
       }
     };
 
@@ -497,54 +466,26 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   const int a_frag = (wm * 32 * TM + (lane & 31)) * kWsLdsK + (lane >> 5) * 8;
   const int b_frag = (wn * 32 * TN + (lane & 31)) * kWsLdsK + (lane >> 5) * 8;
-  // BQ: the lane's B row within the tile, and its code dword within a k-step
-  const int b_row = wn * 32 * TN + (lane & 31), b_half = lane >> 5;
   // fragments of k-step kk of the stage in buffer b; the reads for k-step
   // kk + 1 are issued before the MFMAs of k-step kk, so the MFMAs hide the
   // LDS latency (the first k-step of a stage waits for the barrier)
   half8_t af[2][TM], bf[2][TN];
-  uint32_t bw[2][TN];      // BQ: 8 codes of the lane's B row
-  half2_t bsc[TN][2];      // BQ: the stage's four block scales of that row
-  uint32_t bsraw[TN];      // BQ: the next stage's scale bytes, read ahead of their conversion
   auto read_frags = [&](int slot, int b, int kk) __attribute__((always_inline)) {
     const _Float16* as = As + b * BM * kWsLdsK + a_frag + kk;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
       af[slot][i] = *reinterpret_cast<const half8_t*>(as + i * 32 * kWsLdsK);
-    if constexpr (BQ) {
-      const uint32_t* bq = Bq + (b * BN + b_row) * kBqLd + (kk >> 3) + b_half;
+    const _Float16* bs = Bs + b * BN * kWsLdsK + b_frag + kk;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bw[slot][j] = bq[j * 32 * kBqLd];
-    } else {
-      const _Float16* bs = Bs + b * BN * kWsLdsK + b_frag + kk;
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bf[slot][j] = *reinterpret_cast<const half8_t*>(bs + j * 32 * kWsLdsK);
-    }
-  };
-  auto read_bscales = [&](int b) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j) bsraw[j] = Bqs[b * BN + b_row + 32 * j];
-  };
-  auto cvt_bscales = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      bsc[j][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bsraw[j], 1.0f, false);
-      bsc[j][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bsraw[j], 1.0f, true);
-    }
+    for (int j = 0; j < TN; ++j)
+      bf[slot][j] = *reinterpret_cast<const half8_t*>(bs + j * 32 * kWsLdsK);
   };
   if constexpr (DOTS) __syncthreads();   // the producers' mean row
   __syncthreads();   // stage 0 in buffer 0
   read_frags(0, 0, 0);
-  if constexpr (BQ) {
-    read_bscales(0);
-    cvt_bscales();
-  }
-  // EB: a consumer meets the stage barrier as soon as its last fragment
-  // reads of the stage have landed, before the last k-step's MFMAs, and
-  // reads the next stage's first fragments (with BQ: and its scale bytes,
-  // converted once the stage's last MFMAs are issued) while those MFMAs run
-  constexpr bool EB = true;
+  // a consumer meets the stage barrier as soon as its last fragment reads of
+  // the stage have landed, before the last k-step's MFMAs, and reads the next
+  // stage's first fragments while those MFMAs run
   for (int it = 0; it < nk; ++it) {
     const int b = it & 1;
 #pragma unroll
@@ -552,44 +493,19 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
       const int cur = s4 & 1;
       if (s4 < 3) {
         read_frags(cur ^ 1, b, 16 * (s4 + 1));
-      } else if constexpr (EB) {
+      } else {
         __syncthreads();   // buffer b read out; stage it + 1 in buffer b ^ 1
-        if (it + 1 < nk) {
-          read_frags(0, b ^ 1, 0);
-          if constexpr (BQ) read_bscales(b ^ 1);
-        }
+        if (it + 1 < nk) read_frags(0, b ^ 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (BQ) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const half2_t p = bsc[j][s4 >> 1];
-          const half2_t s2 = (s4 & 1) ? half2_t{p.y, p.y} : half2_t{p.x, p.x};
-          const half8_t bj = __builtin_bit_cast(half8_t, deq8(bw[cur][j], s2));
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int i = 0; i < TM; ++i)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bj, af[cur][i], acc[i][j], 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
-      }
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (it + 1 == nk) mfma_drain();   // fence in the block of the last MFMA
-    if constexpr (!EB) {
-      __syncthreads();
-      if (it + 1 < nk) {
-        read_frags(0, b ^ 1, 0);
-        if constexpr (BQ) read_bscales(b ^ 1);
-      }
-    }
-    if constexpr (BQ) {
-      if (it + 1 < nk) cvt_bscales();
-    }
   }
 
   if constexpr (DOTS) __syncthreads();   // the producers' rank-one terms
@@ -665,69 +581,55 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
 
 namespace {
 
-size_t ws_lds_bytes(int tm, int tn, bool bq) {
-  const int bm = 64 * tm, bn = 64 * tn;
-  const size_t a = (size_t)2 * bm * kWsLdsK * 2;
-  const size_t b = bq ? (size_t)2 * bn * (kBqLd + 1) * 4 : (size_t)2 * bn * kWsLdsK * 2;
-  return a + b + (size_t)bn * 4;
+size_t ws_lds_bytes(int tm, int tn) {
+  return (size_t)2 * 64 * (tm + tn) * kWsLdsK * 2 + (size_t)64 * tn * 4;
 }
 
 constexpr size_t kWsLdsLimit = 160 * 1024 - 512;
 
-template <int TM, int TN, bool OB, bool HM, bool BQ, bool SG, bool RG = false>
+// SG: K % 256 == 0, scale bytes loaded a 256-wide group at a time
+template <int TM, int TN, bool OB, bool HM, bool SG, bool RG = false>
 hipError_t launch_ws(const QOperand& a, const QOperand* mean, const QOperand& b, int64_t m, int64_t n,
                      int64_t k, const int64_t* offs, int nseg, void* c, int64_t ldc,
                      hipStream_t st, int splits = 1, int64_t c_split = 0,
                      const float* rho = nullptr) {
   constexpr int PF = SG ? 4 : 2, BM = 64 * TM, BN = 64 * TN;
-  const size_t lds = ws_lds_bytes(TM, TN, BQ) + (HM && !RG ? (size_t)k * 2 : 0);
+  const size_t lds = ws_lds_bytes(TM, TN) + (HM && !RG ? (size_t)k * 2 : 0);
   {
-    const hipError_t e = lds_attr_once<&k_gemm_ws<TM, TN, PF, OB, HM, BQ, SG, RG>>((int)kWsLdsLimit);
+    const hipError_t e = lds_attr_once<&k_gemm_ws<TM, TN, PF, OB, HM, SG, RG>>((int)kWsLdsLimit);
     if (e != hipSuccess) return e;
   }
   const int64_t tiles_m = chunk_upper_bound(m, offs ? nseg : 1, BM);
   dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)tiles_m, (unsigned)splits);
   const QOperand mu = mean ? *mean : QOperand{nullptr, nullptr, nullptr};
-  k_gemm_ws<TM, TN, PF, OB, HM, BQ, SG, RG><<<grid, 512, lds, st>>>(a, b, mu, m, n, k / splits, offs,
-                                                                    nseg, c, ldc, k, c_split, rho);
+  k_gemm_ws<TM, TN, PF, OB, HM, SG, RG><<<grid, 512, lds, st>>>(a, b, mu, m, n, k / splits, offs,
+                                                                nseg, c, ldc, k, c_split, rho);
   return hipGetLastError();
 }
 
-template <int TM, int TN, bool BQ, bool SG>
+template <int TM, int TN, bool SG>
 hipError_t launch_ws_sg(const QOperand& a, const QOperand* mean, const QOperand& b, int64_t m,
                         int64_t n, int64_t k, const int64_t* offs, int nseg, void* c, bool c_bf16,
                         int64_t ldc, hipStream_t st) {
-  if constexpr (BQ) {
-    if (mean) return hipErrorInvalidValue;   // B-as-codes tiles have no rank-one path
-    if (c_bf16) return launch_ws<TM, TN, true, false, BQ, SG>(a, mean, b, m, n, k, offs, nseg, c, ldc, st);
-    return launch_ws<TM, TN, false, false, BQ, SG>(a, mean, b, m, n, k, offs, nseg, c, ldc, st);
-  } else {
-    if (c_bf16)
-      return mean ? launch_ws<TM, TN, true, true, BQ, SG>(a, mean, b, m, n, k, offs, nseg, c, ldc, st)
-                  : launch_ws<TM, TN, true, false, BQ, SG>(a, mean, b, m, n, k, offs, nseg, c, ldc, st);
-    return mean ? launch_ws<TM, TN, false, true, BQ, SG>(a, mean, b, m, n, k, offs, nseg, c, ldc, st)
-                : launch_ws<TM, TN, false, false, BQ, SG>(a, mean, b, m, n, k, offs, nseg, c, ldc, st);
-  }
+  if (c_bf16)
+    return mean ? launch_ws<TM, TN, true, true, SG>(a, mean, b, m, n, k, offs, nseg, c, ldc, st)
+                : launch_ws<TM, TN, true, false, SG>(a, mean, b, m, n, k, offs, nseg, c, ldc, st);
+  return mean ? launch_ws<TM, TN, false, true, SG>(a, mean, b, m, n, k, offs, nseg, c, ldc, st)
+              : launch_ws<TM, TN, false, false, SG>(a, mean, b, m, n, k, offs, nseg, c, ldc, st);
 }
 
-// K % 256 == 0: scale bytes loaded a 256-wide group at a time
-template <int TM, int TN, bool BQ>
+template <int TM, int TN>
 hipError_t launch_ws_any(const QOperand& a, const QOperand* mean, const QOperand& b, int64_t m,
                          int64_t n, int64_t k, const int64_t* offs, int nseg, void* c, bool c_bf16,
                          int64_t ldc, hipStream_t st) {
-  static const bool sg_off = [] {
-    const char* e = std::getenv("AVERIS_GEMM_SG");
-    return e && std::atoi(e) == 0;
-  }();
-  if (k % 256 == 0 && !sg_off)
-    return launch_ws_sg<TM, TN, BQ, true>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
-  return launch_ws_sg<TM, TN, BQ, false>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+  if (k % 256 == 0)
+    return launch_ws_sg<TM, TN, true>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+  return launch_ws_sg<TM, TN, false>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
 }
 
 }  // namespace
 
-// Variants (workgroup tile, B operand in LDS): 1: 256 x 192 fp16,
-// 2: 256 x 128 fp16, 3: 256 x 192 codes, 4: 256 x 128 codes.  The tile is
+// Variants (workgroup tile): 1: 256 x 192, 2: 256 x 128.  The tile is
 // chosen by rounds of workgroups over the 256 CUs (one resident workgroup
 // per CU) times the tile's work.  Returns 0 when the kernel does not apply.
 int ws_pick(int64_t m, int64_t n, int64_t k, int nseg_eff, bool has_mean) {
@@ -739,7 +641,7 @@ int ws_pick(int64_t m, int64_t n, int64_t k, int nseg_eff, bool has_mean) {
   for (const Cand& cd : cands) {
     // with a mean, its dequantized row (k fp16 values, k <= 32768) shares the LDS
     if (has_mean && k > 4 * kProducers * 32) continue;
-    if (ws_lds_bytes(cd.tm, cd.tn, false) + (has_mean ? (size_t)k * 2 : 0) > kWsLdsLimit) continue;
+    if (ws_lds_bytes(cd.tm, cd.tn) + (has_mean ? (size_t)k * 2 : 0) > kWsLdsLimit) continue;
     const int64_t bm = 64 * cd.tm, bn = 64 * cd.tn;
     const int64_t tiles = chunk_upper_bound(m, nseg_eff, bm) * ((n + bn - 1) / bn);
     const double rounds = (double)((tiles + 255) / 256);
@@ -759,9 +661,9 @@ hipError_t launch_gemm_ws_splitk(const QOperand& a, const QOperand& b, int64_t m
                                  int64_t k, int splits, float* part, hipStream_t st) {
   if (splits < 1 || k % splits != 0 || (k / splits) % kWsBK != 0) return hipErrorInvalidValue;
   if ((k / splits) % 256 == 0)
-    return launch_ws<4, 3, false, false, false, true>(a, nullptr, b, m, n, k, nullptr, 1, part, n,
+    return launch_ws<4, 3, false, false, true>(a, nullptr, b, m, n, k, nullptr, 1, part, n,
                                                       st, splits, m * n);
-  return launch_ws<4, 3, false, false, false, false>(a, nullptr, b, m, n, k, nullptr, 1, part, n,
+  return launch_ws<4, 3, false, false, false>(a, nullptr, b, m, n, k, nullptr, 1, part, n,
                                                      st, splits, m * n);
 }
 
@@ -772,15 +674,15 @@ hipError_t launch_ws_rho(const QOperand& a, const float* rho, const QOperand& b,
                          int64_t ldc, hipStream_t st) {
   if (k % 256 == 0) {
     if (c_bf16)
-      return launch_ws<TM, TN, true, true, false, true, true>(a, nullptr, b, m, n, k, offs, nseg, c,
+      return launch_ws<TM, TN, true, true, true, true>(a, nullptr, b, m, n, k, offs, nseg, c,
                                                               ldc, st, 1, 0, rho);
-    return launch_ws<TM, TN, false, true, false, true, true>(a, nullptr, b, m, n, k, offs, nseg, c,
+    return launch_ws<TM, TN, false, true, true, true>(a, nullptr, b, m, n, k, offs, nseg, c,
                                                              ldc, st, 1, 0, rho);
   }
   if (c_bf16)
-    return launch_ws<TM, TN, true, true, false, false, true>(a, nullptr, b, m, n, k, offs, nseg, c,
+    return launch_ws<TM, TN, true, true, false, true>(a, nullptr, b, m, n, k, offs, nseg, c,
                                                              ldc, st, 1, 0, rho);
-  return launch_ws<TM, TN, false, true, false, false, true>(a, nullptr, b, m, n, k, offs, nseg, c,
+  return launch_ws<TM, TN, false, true, false, true>(a, nullptr, b, m, n, k, offs, nseg, c,
                                                             ldc, st, 1, 0, rho);
 }
 
@@ -796,10 +698,8 @@ hipError_t launch_gemm_ws(int variant, const QOperand& a, const QOperand* mean, 
                           int64_t m, int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
                           bool c_bf16, int64_t ldc, hipStream_t st) {
   switch (variant) {
-    case 1: return launch_ws_any<4, 3, false>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
-    case 2: return launch_ws_any<4, 2, false>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
-    case 3: return launch_ws_any<4, 3, true>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
-    case 4: return launch_ws_any<4, 2, true>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+    case 1: return launch_ws_any<4, 3>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+    case 2: return launch_ws_any<4, 2>(a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
     default: return hipErrorInvalidValue;
   }
 }
