@@ -1,21 +1,31 @@
 #!/usr/bin/env python3
 """Benchmark of the Averis linear hot path (forward + dgrad) on one MI355X.
 
-One step = one pass of the whole hot path over one batch of synthetic input
-of the Qwen3-0.6B up-projection shape (l = 8192 tokens, m = 1024, n = 3072,
-bf16): both quantized copies of W, split-quant of X (which also forms the
-rank-one mean row for the forward GEMM), the forward GEMM, split-quant of the
-output gradient D (and its rank-one row), and the dgrad GEMM.  The vanilla-FP4 arm (plain quant of X / D + the same GEMMs without
-the mean term) is timed the same way to report the Averis overhead.
+One step = one pass of the whole hot path over one batch of synthetic input:
+for every linear of the workload, both quantized copies of W, split-quant of
+X (which also forms the rank-one mean row for the forward GEMM), the forward
+GEMM, split-quant of the output gradient D (and its rank-one row), and the
+dgrad GEMM.  The vanilla-FP4 arm (plain quant of X / D + the same GEMMs
+without the mean term) is timed the same way to report the Averis overhead.
 
-Inputs are resident in HBM before timing starts; the timed steps rotate
-through enough copies of X and D (> 512 MB) that the 256 MB MALL cannot hold
-them, so every step reads its activations from HBM.  The step is timed
-three ways: op by op from Python (host clock), as one captured HIP graph per
-input copy (host clock), and op by op with the launches queued behind a spin
-kernel, timed by events on the launch stream.  The last is the headline: the
-device's own step time, free of the host's launch cost; the other two are
-reported beside it.
+Workloads (--config):
+  4  the Qwen3-0.6B-like block sweep at l = 16384 tokens: q, k, v, o, gate,
+     up, down (the headline: the largest workload that fits one GPU)
+  1  the up-projection, l = 8192, m = 1024, n = 3072
+  2  the down-projection with SwiGLU-like inputs, l = 8192, m = 3072, n = 1024
+  3  the MoE-shaped grouped case: 32768 routed rows over 64 experts (Zipf
+     popularity), hidden 2048, expert width 768
+The headline config is timed first; the others follow as extra fields
+(--only-headline skips them).
+
+Inputs are resident in HBM before timing starts; where one step's
+activations are smaller than 640 MB the timed steps rotate through enough
+copies of them that the 256 MB MALL cannot hold them, so every step reads its
+activations from HBM.  The step is timed three ways: op by op from Python
+(host clock), as one captured HIP graph per input copy (host clock), and op by
+op with the launches queued behind a spin kernel, timed by events on the
+launch stream.  The last is the headline: the device's own step time, free of
+the host's launch cost.
 
 Prints ONE JSON line (see the keys below).
 """
@@ -39,6 +49,16 @@ METRIC = "Averis fwd+dgrad TFLOP/s & split-quant GB/s (frac. roofline); % overhe
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 F16_MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 MFMA, the instruction the GEMM uses
 FP4_MFMA_PEAK_TFLOPS = 10100.0  # dense fp4, for reference only
+ROTATE_BYTES = 640e6           # > the 256 MB MALL
+SQ_BYTES_PER_ELEM = 2 + 0.5 + 1 / 16   # split-quant: bf16 read, codes + scales written
+
+WORKLOAD_NAMES = {
+    1: "Qwen3-0.6B-shaped up-proj (l=8192, 1024->3072), Averis fwd+dgrad step",
+    2: "Qwen3-0.6B-shaped down-proj with SwiGLU-like inputs (l=8192, 3072->1024), Averis fwd+dgrad step",
+    3: "MoE-shaped grouped linear: 32768 routed rows over 64 experts (Zipf 1.1), 2048->768, "
+       "Averis fwd+dgrad step",
+    4: "Qwen3-0.6B-like block sweep at l=16384: q, k, v, o, gate, up, down, Averis fwd+dgrad step",
+}
 
 
 def log(msg):
@@ -50,18 +70,91 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--l", type=int, default=8192)
-    p.add_argument("--m", type=int, default=1024)
-    p.add_argument("--n", type=int, default=3072)
+    p.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4],
+                   help="headline workload (default 4, the seven-linear block sweep)")
+    p.add_argument("--only-headline", action="store_true",
+                   help="time the headline config only (no other configs, wgrad, ratio, weight copies)")
     p.add_argument("--copies", type=int, default=0, help="rotating input copies (0: auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=0,
-                   help="oracle sample: tokens (0: the whole step, all l tokens)")
+    p.add_argument("--cpu-rows", type=int, default=1024,
+                   help="oracle sample: tokens of every linear of the headline workload")
     p.add_argument("--traffic-probe", action="store_true",
-                   help="run a 256 MiB device copy and the hot-path kernels a few times each "
+                   help="run a 256 MiB device copy and three Averis steps of the headline config "
                         "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE), then exit")
     return p.parse_args()
 
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+
+class Linear:
+    """One linear of a workload: inputs on the device and preallocated
+    outputs and workspaces (so the timed steps allocate nothing new)."""
+
+    def __init__(self, name, x, w, d, offsets=None):
+        dev = torch.device("cuda")
+        self.name = name
+        self.x0, self.w, self.d0 = x.to(dev), w.to(dev), d.to(dev)
+        self.l, self.m = self.x0.shape
+        self.n = self.d0.shape[1]
+        self.offsets = None if offsets is None else torch.as_tensor(offsets, dtype=torch.int64,
+                                                                    device=dev)
+        self.nseg = 1 if offsets is None else len(offsets) - 1
+        ns = 0 if offsets is None else self.nseg
+        l, m, n = self.l, self.m, self.n
+        wm, wn = (self.w.shape[1], self.w.shape[2]) if self.w.dim() == 3 else self.w.shape
+        self.ws = dict(
+            q=torch.empty(av.workspace_bytes(av.OP_QUANT, wm, wn, 0, self.w.shape[0]
+                                             if self.w.dim() == 3 else 0) + 256,
+                          dtype=torch.uint8, device=dev),
+            sq_x=torch.empty(max(av.workspace_bytes(av.OP_SPLIT_QUANT, l, m, 0, ns),
+                                 av.workspace_bytes(av.OP_QUANT, l, m, 0, ns)),
+                             dtype=torch.uint8, device=dev),
+            sq_d=torch.empty(max(av.workspace_bytes(av.OP_SPLIT_QUANT, l, n, 0, ns),
+                                 av.workspace_bytes(av.OP_QUANT, l, n, 0, ns)),
+                             dtype=torch.uint8, device=dev),
+            g=torch.empty(av.workspace_bytes(av.OP_GEMM, l, max(m, n), max(m, n), ns),
+                          dtype=torch.uint8, device=dev),
+            y=torch.empty((l, n), dtype=torch.bfloat16, device=dev),
+            dx=torch.empty((l, m), dtype=torch.bfloat16, device=dev),
+            rho_x=torch.empty((self.nseg * n,), dtype=torch.float32, device=dev),
+            rho_d=torch.empty((self.nseg * m,), dtype=torch.float32, device=dev),
+        )
+        self.xs, self.ds = [self.x0], [self.d0]
+
+    def act_bytes(self):
+        return (self.x0.numel() + self.d0.numel()) * 2
+
+    def rotate(self, copies):
+        self.xs = [self.x0] + [self.x0.clone() for _ in range(copies - 1)]
+        self.ds = [self.d0] + [self.d0.clone() for _ in range(copies - 1)]
+
+    def flops(self):
+        """GEMM flops of one pass (fwd or dgrad): 2 l m n."""
+        return 2.0 * self.l * self.m * self.n
+
+
+def make_linears(cfg):
+    if cfg == 1:
+        c = workloads.up_proj()
+        return [Linear("up_proj", c["x"], c["w"], c["d"])]
+    if cfg == 2:
+        c = workloads.down_proj()
+        return [Linear("down_proj", c["x"], c["w"], c["d"])]
+    if cfg == 3:
+        c = workloads.moe()
+        return [Linear("moe", c["x"], c["w"], c["d"], offsets=c["offsets"])]
+    out = []
+    for name in workloads.QWEN3_06B_LINEARS:
+        c = workloads.block_linear(name)
+        out.append(Linear(name, c["x"], c["w"], c["d"]))
+    return out
+
+
+# --------------------------------------------------------------------------
+# timing
+# --------------------------------------------------------------------------
 
 class Timer:
     """Event pairs on the current stream (the one the library launches on)."""
@@ -83,61 +176,86 @@ class Timer:
         return [a.elapsed_time(b) for a, b in self.pairs.get(name, [])]
 
 
-def run_step(x, d, w, ws, t=None, vanilla=False):
-    """One pass of the hot path; returns nothing (outputs stay on device)."""
-    def tic(n):
+def run_linear(L, i, t, vanilla):
+    """One linear's forward + dgrad with input copy i."""
+    def tic(k):
         if t:
-            t.start(n)
+            t.start(L.name + "/" + k)
 
-    def toc(n):
+    def toc(k):
         if t:
-            t.stop(n)
+            t.stop(L.name + "/" + k)
+    ws = L.ws
+    x, d = L.xs[i % len(L.xs)], L.ds[i % len(L.ds)]
     tic("wquant")
-    wt, wd = av.averis_quant_pair(w, rnd=av.RN, ws=ws["q"])
+    wt, wd = av.averis_quant_pair(L.w, rnd=av.RN, ws=ws["q"])
     toc("wquant")
+    if L.offsets is None:
+        if not vanilla:
+            # the split also forms the rank-one row 1 (mean W) for the GEMM
+            # that takes it, so the GEMM adds it without a mean row of its own
+            tic("split_x")
+            xr, _, _, rho_x = av.averis_split_quant_rank1(x, wt, seed=0, ws=ws["sq_x"],
+                                                          rho=ws["rho_x"])
+            toc("split_x")
+            tic("gemm_fwd")
+            av.averis_gemm_rank1(xr, rho_x, wt, out_dtype=torch.bfloat16, out=ws["y"])
+            toc("gemm_fwd")
+            tic("split_d")
+            dr, _, _, rho_d = av.averis_split_quant_rank1(d, wd, seed=1, ws=ws["sq_d"],
+                                                          rho=ws["rho_d"])
+            toc("split_d")
+            tic("gemm_dgrad")
+            av.averis_gemm_rank1(dr, rho_d, wd, out_dtype=torch.bfloat16, out=ws["dx"])
+            toc("gemm_dgrad")
+        else:
+            tic("split_x")
+            xq = av.averis_quant(x, seed=0, ws=ws["sq_x"])
+            toc("split_x")
+            tic("gemm_fwd")
+            av.averis_gemm_vanilla(xq, wt, out_dtype=torch.bfloat16, out=ws["y"], ws=ws["g"])
+            toc("gemm_fwd")
+            tic("split_d")
+            dq = av.averis_quant(d, seed=1, ws=ws["sq_d"])
+            toc("split_d")
+            tic("gemm_dgrad")
+            av.averis_gemm_vanilla(dq, wd, out_dtype=torch.bfloat16, out=ws["dx"], ws=ws["g"])
+            toc("gemm_dgrad")
+        return
+    offs = L.offsets
     if not vanilla:
-        # the split also forms the rank-one row 1 (mean W) for the GEMM that
-        # takes it, so the GEMM adds it without a mean row of its own
         tic("split_x")
-        xr, _, _, rho_x = av.averis_split_quant_rank1(x, wt, seed=0, ws=ws["sq_x"], rho=ws["rho_x"])
+        xr, _, _, rho_x = av.averis_split_quant_grouped_rank1(x, offs, wt, seed=0, ws=ws["sq_x"])
         toc("split_x")
         tic("gemm_fwd")
-        av.averis_gemm_rank1(xr, rho_x, wt, out_dtype=torch.bfloat16, out=ws["y"])
+        av.averis_gemm_grouped_rank1(xr, rho_x, wt, offs, out_dtype=torch.bfloat16, out=ws["y"])
         toc("gemm_fwd")
         tic("split_d")
-        dr, _, _, rho_d = av.averis_split_quant_rank1(d, wd, seed=1, ws=ws["sq_d"], rho=ws["rho_d"])
+        dr, _, _, rho_d = av.averis_split_quant_grouped_rank1(d, offs, wd, seed=1, ws=ws["sq_d"])
         toc("split_d")
         tic("gemm_dgrad")
-        av.averis_gemm_rank1(dr, rho_d, wd, out_dtype=torch.bfloat16, out=ws["dx"])
+        av.averis_gemm_grouped_rank1(dr, rho_d, wd, offs, out_dtype=torch.bfloat16, out=ws["dx"])
         toc("gemm_dgrad")
     else:
-        tic("vq_x")
-        xq = av.averis_quant(x, seed=0, ws=ws["sq_x"])
-        toc("vq_x")
-        tic("vgemm_fwd")
-        av.averis_gemm_vanilla(xq, wt, out_dtype=torch.bfloat16, out=ws["y"], ws=ws["g"])
-        toc("vgemm_fwd")
-        tic("vq_d")
-        dq = av.averis_quant(d, seed=1, ws=ws["sq_d"])
-        toc("vq_d")
-        tic("vgemm_dgrad")
-        av.averis_gemm_vanilla(dq, wd, out_dtype=torch.bfloat16, out=ws["dx"], ws=ws["g"])
-        toc("vgemm_dgrad")
+        tic("split_x")
+        xq = av.averis_quant_grouped(x, offs, seed=0, ws=ws["sq_x"])
+        toc("split_x")
+        tic("gemm_fwd")
+        av.averis_gemm_grouped(xq, None, wt, offs, out_dtype=torch.bfloat16, out=ws["y"],
+                               ws=ws["g"])
+        toc("gemm_fwd")
+        tic("split_d")
+        dq = av.averis_quant_grouped(d, offs, seed=1, ws=ws["sq_d"])
+        toc("split_d")
+        tic("gemm_dgrad")
+        av.averis_gemm_grouped(dq, None, wd, offs, out_dtype=torch.bfloat16, out=ws["dx"],
+                               ws=ws["g"])
+        toc("gemm_dgrad")
 
 
-def capture(xs, ds, w, ws, vanilla):
-    """One HIP graph per rotating input copy, each holding one whole step
-    (every launch of the step, outputs in the graphs' shared pool)."""
-    graphs = []
-    pool = None
-    for i in range(len(xs)):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, pool=pool):
-            run_step(xs[i], ds[i], w, ws, None, vanilla)
-        pool = g.pool()
-        graphs.append(g)
-    torch.cuda.synchronize()
-    return graphs
+def run_step(linears, i, t=None, vanilla=False):
+    for L in linears:
+        run_linear(L, i, t, vanilla)
 
 
 _SLEEP_CYCLES_PER_MS = None
@@ -158,25 +276,40 @@ def hold_gpu(ms):
     torch.cuda._sleep(int(ms * _SLEEP_CYCLES_PER_MS))
 
 
-def timed(xs, ds, w, ws, steps, warmup, vanilla):
-    """Step time three ways (ms/step) and a per-call event timer.
+def pct(v, q):
+    return float(np.percentile(v, q)) if len(v) else float("nan")
+
+
+def timed(linears, steps, warmup, vanilla):
+    """Step time three ways (ms/step), the per-step device times of the
+    queued run, and a per-call event timer.
 
     eager:  one Python call per op, timed on the host around the loop;
     graph:  one captured HIP graph per input copy, replayed;
     queued: the eager launches queued behind a spin kernel and timed with
             events on the launch stream: the device's own step time, with the
-            host's launch cost taken out."""
+            host's launch cost taken out (an event between steps gives each
+            step's own time)."""
+    ncopy = max(len(L.xs) for L in linears)
     for i in range(warmup):
-        run_step(xs[i % len(xs)], ds[i % len(ds)], w, ws, None, vanilla)
+        run_step(linears, i, None, vanilla)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        run_step(xs[i % len(xs)], ds[i % len(ds)], w, ws, None, vanilla)
+        run_step(linears, i, None, vanilla)
     enqueue_ms = (time.perf_counter() - t0) * 1e3
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / steps
 
-    graphs = capture(xs, ds, w, ws, vanilla)
+    graphs = []
+    pool = None
+    for i in range(ncopy):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, pool=pool):
+            run_step(linears, i, None, vanilla)
+        pool = g.pool()
+        graphs.append(g)
+    torch.cuda.synchronize()
     for i in range(warmup):
         graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
@@ -188,101 +321,174 @@ def timed(xs, ds, w, ws, steps, warmup, vanilla):
     del graphs
 
     hold = 2.0 * enqueue_ms + 2.0
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     hold_gpu(hold)
-    e0.record()
     t0 = time.perf_counter()
     for i in range(steps):
-        run_step(xs[i % len(xs)], ds[i % len(ds)], w, ws, None, vanilla)
-    e1.record()
+        evs[i].record()
+        run_step(linears, i, None, vanilla)
+    evs[steps].record()
     queued_enqueue_ms = (time.perf_counter() - t0) * 1e3
     torch.cuda.synchronize()
-    queued_ms = e0.elapsed_time(e1) / steps
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    queued_ms = evs[0].elapsed_time(evs[steps]) / steps
     if queued_enqueue_ms > 0.8 * hold:
         log("bench: warning: enqueue took %.2f ms of a %.2f ms hold" % (queued_enqueue_ms, hold))
 
-    # per-kernel-call durations, events on the launch stream, same rotation,
-    # also queued behind a spin kernel
+    # per-call durations, events on the launch stream, same rotation, also
+    # queued behind a spin kernel
     t = Timer()
-    hold_gpu(hold * 1.5)
+    hold_gpu(hold * 2.0)
     for i in range(steps):
-        run_step(xs[i % len(xs)], ds[i % len(ds)], w, ws, t, vanilla)
+        run_step(linears, i, t, vanilla)
     torch.cuda.synchronize()
-    return dict(eager=eager_ms, graph=graph_ms, queued=queued_ms), t
+    return dict(eager=eager_ms, graph=graph_ms, queued=queued_ms,
+                queued_p10=pct(per_step, 10), queued_p90=pct(per_step, 90)), t
 
 
-def time_wgrad(xs, ds, ws, steps, warmup):
-    """The wgrad pieces, queued behind a spin kernel and timed per call by
-    events on the launch stream, rotating through the input copies: the
-    transposed residual quants of X and D (their means and residual tensor
-    scales come from the splits the forward and dgrad passes run) and the
-    wgrad product dW = deq(xt) deq(dt)^T + l mu_X mu_D^T (fp32 out)."""
-    l, m = xs[0].shape
-    n = ds[0].shape[1]
-    xr, _, mx = av.averis_split_quant(xs[0], seed=0, ws=ws["sq_x"])
-    dr, _, md = av.averis_split_quant(ds[0], seed=1, ws=ws["sq_d"])
-    xt = av.NVFP4.empty(m, l, 1, xs[0].device)
-    dt = av.NVFP4.empty(n, l, 1, xs[0].device)
-    dw = torch.empty((m, n), dtype=torch.float32, device=xs[0].device)
+def stats(v):
+    return dict(ms=float(np.median(v)), p10=pct(v, 10), p90=pct(v, 90))
+
+
+def measure(cfg, linears, steps, warmup):
+    """Both arms of one workload; returns the summary dict and the timers."""
+    act = sum(L.act_bytes() for L in linears)
+    copies = max(1, int(np.ceil(ROTATE_BYTES / act)))
+    for L in linears:
+        L.rotate(copies)
+    log("bench: config %d: %d linear(s), %.0f MB of activations per step, %d rotating copies"
+        % (cfg, len(linears), act / 1e6, copies))
+    ta_ms, ta = timed(linears, steps, warmup, vanilla=False)
+    tv_ms, tv = timed(linears, steps, warmup, vanilla=True)
+    log("bench: config %d: averis %s | vanilla %s (ms/step)" % (
+        cfg, " ".join("%s %.4f" % kv for kv in ta_ms.items()),
+        " ".join("%s %.4f" % kv for kv in tv_ms.items())))
+    flops_step = sum(2 * L.flops() for L in linears)
+    per = {}
+    tot = {"averis": {}, "vanilla": {}}
+    for L in linears:
+        rec = {}
+        for arm, t in (("averis", ta), ("vanilla", tv)):
+            r = {k: stats(t.ms(L.name + "/" + k))
+                 for k in ("wquant", "split_x", "gemm_fwd", "split_d", "gemm_dgrad")}
+            for k, v in r.items():
+                tot[arm][k] = tot[arm].get(k, 0.0) + v["ms"]
+            rec[arm] = r
+        a, v = rec["averis"], rec["vanilla"]
+        fa = a["split_x"]["ms"] + a["gemm_fwd"]["ms"]
+        fv = v["split_x"]["ms"] + v["gemm_fwd"]["ms"]
+        ba = a["split_d"]["ms"] + a["gemm_dgrad"]["ms"]
+        bv = v["split_d"]["ms"] + v["gemm_dgrad"]["ms"]
+        sqx = L.l * L.m * SQ_BYTES_PER_ELEM
+        sqd = L.l * L.n * SQ_BYTES_PER_ELEM
+        per[L.name] = dict(
+            shape=dict(tokens=L.l, k_in=L.m, n_out=L.n, segments=L.nseg),
+            averis={k: vv for k, vv in a.items()}, vanilla={k: vv for k, vv in v.items()},
+            split_quant_gbs=dict(x=sqx / (a["split_x"]["ms"] * 1e-3) / 1e9,
+                                 d=sqd / (a["split_d"]["ms"] * 1e-3) / 1e9),
+            vanilla_quant_gbs=dict(x=sqx / (v["split_x"]["ms"] * 1e-3) / 1e9,
+                                   d=sqd / (v["split_d"]["ms"] * 1e-3) / 1e9),
+            gemm_tflops=dict(fwd=L.flops() / (a["gemm_fwd"]["ms"] * 1e-3) / 1e12,
+                             dgrad=L.flops() / (a["gemm_dgrad"]["ms"] * 1e-3) / 1e12,
+                             vanilla_fwd=L.flops() / (v["gemm_fwd"]["ms"] * 1e-3) / 1e12,
+                             vanilla_dgrad=L.flops() / (v["gemm_dgrad"]["ms"] * 1e-3) / 1e12),
+            overhead_pct=dict(fwd=100 * (fa / fv - 1), dgrad=100 * (ba / bv - 1)))
+    sq_x = sum(L.l * L.m for L in linears) * SQ_BYTES_PER_ELEM
+    sq_d = sum(L.l * L.n for L in linears) * SQ_BYTES_PER_ELEM
+    A, V = tot["averis"], tot["vanilla"]
+    summary = dict(
+        workload=WORKLOAD_NAMES[cfg],
+        ms_per_step=ta_ms["queued"], vanilla_ms_per_step=tv_ms["queued"],
+        step_p10_p90_ms=[ta_ms["queued_p10"], ta_ms["queued_p90"]],
+        vanilla_step_p10_p90_ms=[tv_ms["queued_p10"], tv_ms["queued_p90"]],
+        tflops=flops_step / (ta_ms["queued"] * 1e-3) / 1e12,
+        vanilla_tflops=flops_step / (tv_ms["queued"] * 1e-3) / 1e12,
+        step_ms_by_launch={"averis": ta_ms, "vanilla": tv_ms},
+        overhead_pct=dict(
+            step=100 * (ta_ms["queued"] / tv_ms["queued"] - 1),
+            fwd=100 * ((A["split_x"] + A["gemm_fwd"]) / (V["split_x"] + V["gemm_fwd"]) - 1),
+            dgrad=100 * ((A["split_d"] + A["gemm_dgrad"]) / (V["split_d"] + V["gemm_dgrad"]) - 1)),
+        split_quant=dict(
+            x=dict(ms=A["split_x"], gbs=sq_x / (A["split_x"] * 1e-3) / 1e9),
+            d=dict(ms=A["split_d"], gbs=sq_d / (A["split_d"] * 1e-3) / 1e9)),
+        vanilla_quant=dict(
+            x=dict(ms=V["split_x"], gbs=sq_x / (V["split_x"] * 1e-3) / 1e9),
+            d=dict(ms=V["split_d"], gbs=sq_d / (V["split_d"] * 1e-3) / 1e9)),
+        gemm=dict(fwd_ms=A["gemm_fwd"], dgrad_ms=A["gemm_dgrad"],
+                  tflops=flops_step / ((A["gemm_fwd"] + A["gemm_dgrad"]) * 1e-3) / 1e12,
+                  vanilla_tflops=flops_step / ((V["gemm_fwd"] + V["gemm_dgrad"]) * 1e-3) / 1e12),
+        weight_quant_ms=A["wquant"],
+        per_linear=per,
+        rotating_input_copies=copies,
+        sum_of_calls_ms=dict(averis=sum(A.values()), vanilla=sum(V.values())),
+    )
+    for s in (summary["split_quant"], summary["vanilla_quant"]):
+        for v in s.values():
+            v["frac_hbm"] = v["gbs"] / HBM_PEAK_GBS
+    return summary, ta, flops_step
+
+
+def time_wgrad(L, steps, warmup):
+    """The wgrad pieces of one linear, queued behind a spin kernel and timed
+    per call by events on the launch stream, rotating through the input
+    copies: the transposed residual quants of X and D (their means and
+    residual tensor scales come from the splits the forward and dgrad passes
+    run) and dW = deq(xt) deq(dt)^T + l mu_X mu_D^T (fp32 out)."""
+    l, m, n = L.l, L.m, L.n
+    xr, _, mx = av.averis_split_quant(L.xs[0], seed=0, ws=L.ws["sq_x"])
+    dr, _, md = av.averis_split_quant(L.ds[0], seed=1, ws=L.ws["sq_d"])
+    xt = av.NVFP4.empty(m, l, 1, L.x0.device)
+    dt = av.NVFP4.empty(n, l, 1, L.x0.device)
+    dw = torch.empty((m, n), dtype=torch.float32, device=L.x0.device)
     wws = torch.empty(av.workspace_bytes(av.OP_WGRAD, m, l, n), dtype=torch.uint8,
-                      device=xs[0].device)
+                      device=L.x0.device)
 
     def one(i, t):
-        def tic(k):
-            if t:
-                t.start(k)
-
-        def toc(k):
-            if t:
-                t.stop(k)
-        tic("rt_x")
-        av.averis_residual_t_quant(xs[i % len(xs)], mx, xr, seed=0, out=xt)
-        toc("rt_x")
-        tic("rt_d")
-        av.averis_residual_t_quant(ds[i % len(ds)], md, dr, seed=1, out=dt)
-        toc("rt_d")
-        tic("gemm_wgrad")
+        t.start("rt_x")
+        av.averis_residual_t_quant(L.xs[i % len(L.xs)], mx, xr, seed=0, out=xt)
+        t.stop("rt_x")
+        t.start("rt_d")
+        av.averis_residual_t_quant(L.ds[i % len(L.ds)], md, dr, seed=1, out=dt)
+        t.stop("rt_d")
+        t.start("gemm_wgrad")
         av.averis_gemm_wgrad(xt, dt, mx, md, out=dw, ws=wws)
-        toc("gemm_wgrad")
+        t.stop("gemm_wgrad")
 
     for i in range(warmup):
-        one(i, None)
+        one(i, Timer())
     torch.cuda.synchronize()
     t = Timer()
     hold_gpu(5.0 + 0.5 * steps)
     for i in range(steps):
         one(i, t)
     torch.cuda.synchronize()
-    med = lambda v: float(np.median(v))
-    ms = {k: med(t.ms(k)) for k in ("rt_x", "rt_d", "gemm_wgrad")}
-    rt_bytes = lambda rows, cols: rows * cols * (2 + 0.5 + 1 / 16)
-    flops = 2.0 * l * m * n
-    return dict(
-        ms=ms,
-        rt_gbs={"x": rt_bytes(l, m) / (ms["rt_x"] * 1e-3) / 1e9,
-                "d": rt_bytes(l, n) / (ms["rt_d"] * 1e-3) / 1e9},
-        gemm_tflops=flops / (ms["gemm_wgrad"] * 1e-3) / 1e12,
-        splits_of_tokens=int(av.workspace_bytes(av.OP_WGRAD, m, l, n) // (m * n * 4)),
-        note="dW (m x n) = deq(Q4(X_R^T)) deq(Q4(D_R^T))^T + l mu_X mu_D^T, fp32 out; "
-             "gemm_wgrad covers the split-K GEMM and the reduce that adds the outer product")
+    ms = {k: stats(t.ms(k)) for k in ("rt_x", "rt_d", "gemm_wgrad")}
+    rt = lambda rows, cols, k: rows * cols * SQ_BYTES_PER_ELEM / (ms[k]["ms"] * 1e-3) / 1e9
+    return dict(linear=L.name, tokens=l, m=m, n=n, ms=ms,
+                rt_gbs={"x": rt(l, m, "rt_x"), "d": rt(l, n, "rt_d")},
+                gemm_tflops=2.0 * l * m * n / (ms["gemm_wgrad"]["ms"] * 1e-3) / 1e12,
+                note="dW (m x n) = deq(Q4(X_R^T)) deq(Q4(D_R^T))^T + l mu_X mu_D^T, fp32 out; "
+                     "gemm_wgrad covers the split-K GEMM and the reduce that adds the outer "
+                     "product")
 
 
-def time_ratio(xs, ds, ws, steps, warmup):
+def time_ratio(L, steps, warmup):
     """Split-quant of X and D with and without the mean-energy ratio, per call
     (events on the launch stream, queued behind a spin kernel, rotating
     copies), and the ratios themselves."""
+    ratios = {}
+
     def one(i, t):
-        for name, src, key in (("x", xs, "sq_x"), ("d", ds, "sq_d")):
+        for name, src, key in (("x", L.xs, "sq_x"), ("d", L.ds, "sq_d")):
             a = src[i % len(src)]
             t.start("plain_" + name)
-            av.averis_split_quant(a, seed=0, ws=ws[key])
+            av.averis_split_quant(a, seed=0, ws=L.ws[key])
             t.stop("plain_" + name)
             t.start("ratio_" + name)
-            out = av.averis_split_quant_ratio(a, seed=0, ws=ws[key])
+            out = av.averis_split_quant_ratio(a, seed=0, ws=L.ws[key])
             t.stop("ratio_" + name)
             ratios[name] = out[3]
 
-    ratios = {}
     for i in range(warmup):
         one(i, Timer())
     torch.cuda.synchronize()
@@ -292,21 +498,23 @@ def time_ratio(xs, ds, ws, steps, warmup):
         one(i, t)
     torch.cuda.synchronize()
     med = lambda v: float(np.median(v))
-    return {name: dict(split_ms=med(t.ms("plain_" + name)), split_with_ratio_ms=med(t.ms("ratio_" + name)),
-                       ratio=float(ratios[name][0].item()))
-            for name in ("x", "d")}
+    return dict(linear=L.name, **{
+        name: dict(split_ms=med(t.ms("plain_" + name)),
+                   split_with_ratio_ms=med(t.ms("ratio_" + name)),
+                   ratio=float(ratios[name][0].item()))
+        for name in ("x", "d")})
 
 
-def time_weight_copies(w, ws, steps, warmup):
+def time_weight_copies(L, steps, warmup):
     """Both weight copies per call (events on the launch stream, queued behind
     a spin kernel): the two 1-D quantizations (averis_quant_pair) and the
     shared 16x16-tile quantization (averis_quant_pair_2d)."""
     def one(t):
         t.start("pair")
-        av.averis_quant_pair(w, rnd=av.RN, ws=ws["q"])
+        av.averis_quant_pair(L.w, rnd=av.RN, ws=L.ws["q"])
         t.stop("pair")
         t.start("pair_2d")
-        av.averis_quant_pair_2d(w, rnd=av.RN, ws=ws["q"])
+        av.averis_quant_pair_2d(L.w, rnd=av.RN, ws=L.ws["q"])
         t.stop("pair_2d")
 
     for _ in range(warmup):
@@ -317,68 +525,80 @@ def time_weight_copies(w, ws, steps, warmup):
     for _ in range(steps):
         one(t)
     torch.cuda.synchronize()
-    return dict(pair_ms=float(np.median(t.ms("pair"))), pair_2d_ms=float(np.median(t.ms("pair_2d"))))
+    return dict(linear=L.name, pair_ms=float(np.median(t.ms("pair"))),
+                pair_2d_ms=float(np.median(t.ms("pair_2d"))))
 
 
-def cpu_baseline(cfg_rows, m, n):
-    """The oracle as it stands on a bounded sample: cfg_rows tokens of the
-    same workload (split-quant of X and D, both weight copies, the float64
-    forward and dgrad GEMMs); reported in TFLOP/s of the sample's GEMMs."""
+# --------------------------------------------------------------------------
+# the oracle on the host (reported baseline)
+# --------------------------------------------------------------------------
+
+def cpu_baseline(cfg, rows):
+    """The oracle as it stands on a bounded sample of the headline workload:
+    `rows` tokens of every linear (all other sizes as in the workload):
+    split-quant of X and D, both weight copies, the float64 forward and dgrad
+    GEMMs.  Reported in TFLOP/s of the sample's GEMMs."""
     from oracle import averis as orc
-    cfg = workloads.up_proj(l=cfg_rows, m=m, n=n)
-    x, w, d = cfg["x"].float().numpy(), cfg["w"].float().numpy(), cfg["d"].float().numpy()
+    if cfg == 4:
+        cases = [workloads.block_linear(name, l=rows) for name in workloads.QWEN3_06B_LINEARS]
+    elif cfg == 1:
+        cases = [workloads.up_proj(l=rows)]
+    elif cfg == 2:
+        cases = [workloads.down_proj(l=rows)]
+    else:
+        raise ValueError("the CPU sample covers the dense workloads")
+    flops = 0.0
     t0 = time.perf_counter()
-    wq = orc.weight_quant(w, "rn")
-    orc.averis_forward(x, wq["fwd"], "sr", 0)
-    orc.averis_dgrad(d, wq["dgrad"], "sr", 1)
+    for c in cases:
+        x, w, d = c["x"].float().numpy(), c["w"].float().numpy(), c["d"].float().numpy()
+        wq = orc.weight_quant(w, "rn")
+        orc.averis_forward(x, wq["fwd"], "sr", 0)
+        orc.averis_dgrad(d, wq["dgrad"], "sr", 1)
+        flops += 2 * 2.0 * x.shape[0] * x.shape[1] * d.shape[1]
     dt = time.perf_counter() - t0
-    flops = 2 * (2.0 * cfg_rows * m * n)
     try:
         import threadpoolctl
         blas = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
     except Exception:
         blas = 1
     return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=int(blas), kind="oracle",
-                sample="%d tokens of the l=8192 workload (m=%d, n=%d), one step: split-quant X and D, "
-                       "both weight copies, float64 fwd+dgrad GEMMs; %.1f s; numpy elementwise "
-                       "work single-threaded, float64 matmul on %d BLAS threads of %d host cores"
-                       % (cfg_rows, m, n, dt, blas, len(os.sched_getaffinity(0))),
+                sample="%d tokens of each of the %d linear(s) of the headline workload (full "
+                       "weights), one step: split-quant X and D, both weight copies, float64 "
+                       "fwd+dgrad GEMMs; %.1f s; numpy elementwise work single-threaded, float64 "
+                       "matmul on %d BLAS threads of %d host cores"
+                       % (rows, len(cases), dt, blas, len(os.sched_getaffinity(0))),
                 seconds=dt)
 
+
+# --------------------------------------------------------------------------
+# HBM counters (rocprofv3 --pmc) and the roofline record
+# --------------------------------------------------------------------------
 
 COPY_BYTES = 256 << 20
 
 
 def traffic_probe(args):
     """A device copy of known size (the scale reference for the HBM byte
-    counters) followed by three launches of each hot-path kernel."""
-    l, m, n = args.l, args.m, args.n
+    counters) followed by three Averis steps of the headline config."""
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for _ in range(3):
         dst.copy_(src)
-    cfg = workloads.up_proj(l=l, m=m, n=n)
-    x, w, d = cfg["x"].cuda(), cfg["w"].cuda(), cfg["d"].cuda()
+    linears = make_linears(args.config)
     torch.cuda.synchronize()
-    for _ in range(3):
-        wt, wd = av.averis_quant_pair(w, rnd=av.RN)
-        xr, _, mx, rho_x = av.averis_split_quant_rank1(x, wt, seed=0)
-        av.averis_gemm_rank1(xr, rho_x, wt, out_dtype=torch.bfloat16)
-        dr, _, md, rho_d = av.averis_split_quant_rank1(d, wd, seed=1)
-        av.averis_gemm_rank1(dr, rho_d, wd, out_dtype=torch.bfloat16)
-        xt = av.averis_residual_t_quant(x, mx, xr, seed=0)
-        dt = av.averis_residual_t_quant(d, md, dr, seed=1)
-        av.averis_gemm_wgrad(xt, dt, mx, md)
+    for i in range(3):
+        run_step(linears, 0, None, vanilla=False)
     torch.cuda.synchronize()
-    print("traffic probe done: copy %d bytes" % COPY_BYTES, file=sys.stderr)
+    print("traffic probe done: copy %d bytes, config %d" % (COPY_BYTES, args.config),
+          file=sys.stderr)
 
 
 GEMM_SOURCES = ["gemm.hip", "gemm_ws.hip", "gemm_common.hpp"]
 
 
 def gemm_source_sha():
-    """One hash over the sources of the forward GEMM kernel."""
+    """One hash over the sources of the GEMM kernel."""
     import hashlib
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
@@ -386,25 +606,23 @@ def gemm_source_sha():
     return h.hexdigest()
 
 
-def load_traffic():
-    """HBM bytes per forward GEMM launch (k_gemm_ws) from the committed counter
-    summary, if it was taken on the current kernel sources (else None)."""
+def load_traffic(cfg):
+    """HBM bytes per Averis GEMM launch (k_gemm_ws) from the committed counter
+    summary, if it was taken on the current kernel sources for this workload
+    (else None)."""
     path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
     try:
         rec = json.load(open(path))
         sha = gemm_source_sha()
     except (OSError, ValueError):
         return None
-    if rec.get("gemm_sources_sha256") != sha:
+    if rec.get("gemm_sources_sha256") != sha or rec.get("config") != cfg:
         return None
     return rec
 
 
 def main():
     args = parse()
-    if args.traffic_probe:
-        traffic_probe(args)
-        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -413,124 +631,89 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     av.lib()
-    l, m, n = args.l, args.m, args.n
-    log("bench: generating inputs l=%d m=%d n=%d" % (l, m, n))
-    cfg = workloads.up_proj(l=l, m=m, n=n)
-    x0, w0, d0 = cfg["x"].cuda(), cfg["w"].cuda(), cfg["d"].cuda()
-    bytes_per_set = (x0.numel() + d0.numel()) * 2
-    copies = args.copies or max(2, int(np.ceil(640e6 / bytes_per_set)))
-    xs = [x0] + [x0.clone() for _ in range(copies - 1)]
-    ds = [d0] + [d0.clone() for _ in range(copies - 1)]
-    dev = x0.device
-    ws = dict(
-        q=torch.empty(max(av.workspace_bytes(av.OP_QUANT, n, m),
-                          av.workspace_bytes(av.OP_QUANT, m, n)), dtype=torch.uint8, device=dev),
-        sq_x=torch.empty(av.workspace_bytes(av.OP_SPLIT_QUANT, l, m), dtype=torch.uint8,
-                         device=dev),
-        sq_d=torch.empty(av.workspace_bytes(av.OP_SPLIT_QUANT, l, n), dtype=torch.uint8,
-                         device=dev),
-        g=torch.empty(av.workspace_bytes(av.OP_GEMM, l, max(m, n), max(m, n)), dtype=torch.uint8,
-                      device=dev),
-        y=torch.empty((l, n), dtype=torch.bfloat16, device=dev),
-        dx=torch.empty((l, m), dtype=torch.bfloat16, device=dev),
-        rho_x=torch.empty((n,), dtype=torch.float32, device=dev),
-        rho_d=torch.empty((m,), dtype=torch.float32, device=dev),
-    )
-    log("bench: %d rotating input copies; warmup %d, steps %d" % (copies, args.warmup, args.steps))
-    ta_ms, ta = timed(xs, ds, w0, ws, args.steps, args.warmup, vanilla=False)
-    tv_ms, tv = timed(xs, ds, w0, ws, args.steps, args.warmup, vanilla=True)
-    log("bench: averis %s, vanilla %s (ms/step)" % (
-        " ".join("%s %.4f" % kv for kv in ta_ms.items()),
-        " ".join("%s %.4f" % kv for kv in tv_ms.items())))
-    log("bench: wgrad pieces")
-    wg = time_wgrad(xs, ds, ws, args.steps, args.warmup)
-    log("bench: mean-energy ratio")
-    mer = time_ratio(xs, ds, ws, args.steps, args.warmup)
-    log("bench: weight copies")
-    wc = time_weight_copies(w0, ws, args.steps, args.warmup)
-    # the headline is the device's step time (launches queued ahead of it)
-    ms_a, ms_v = ta_ms["queued"], tv_ms["queued"]
+    if args.traffic_probe:
+        traffic_probe(args)
+        return
+    cfg = args.config
+    log("bench: generating config %d" % cfg)
+    linears = make_linears(cfg)
+    head, ta, flops_step = measure(cfg, linears, args.steps, args.warmup)
 
-    gemm_flops = 2.0 * l * m * n
-    med = lambda v: float(np.median(v)) if v else float("nan")
-    comp = {k: med(ta.ms(k)) for k in ["wquant", "split_x", "gemm_fwd", "split_d", "gemm_dgrad"]}
-    compv = {k: med(tv.ms(k)) for k in ["vq_x", "vgemm_fwd", "vq_d", "vgemm_dgrad"]}
-    sq_bytes = lambda rows, cols: rows * cols * (2 + 0.5 + 1 / 16)   # algorithmic bytes
-    gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
-    split = {
-        "x": dict(ms=comp["split_x"], gbs=gbs(sq_bytes(l, m), comp["split_x"])),
-        "d": dict(ms=comp["split_d"], gbs=gbs(sq_bytes(l, n), comp["split_d"])),
-    }
-    for v in split.values():
-        v["frac_hbm"] = v["gbs"] / HBM_PEAK_GBS
-    vq = {"x": dict(ms=compv["vq_x"], gbs=gbs(sq_bytes(l, m), compv["vq_x"])),
-          "d": dict(ms=compv["vq_d"], gbs=gbs(sq_bytes(l, n), compv["vq_d"]))}
-    gemm = {k: dict(ms=comp[k], tflops=gemm_flops / (comp[k] * 1e-3) / 1e12)
-            for k in ["gemm_fwd", "gemm_dgrad"]}
-    vgemm = {k: dict(ms=compv[k], tflops=gemm_flops / (compv[k] * 1e-3) / 1e12)
-             for k in ["vgemm_fwd", "vgemm_dgrad"]}
-    t_fwd_a = comp["split_x"] + comp["gemm_fwd"]
-    t_fwd_v = compv["vq_x"] + compv["vgemm_fwd"]
-    t_bwd_a = comp["split_d"] + comp["gemm_dgrad"]
-    t_bwd_v = compv["vq_d"] + compv["vgemm_dgrad"]
-    overhead = dict(fwd_pct=100 * (t_fwd_a / t_fwd_v - 1), dgrad_pct=100 * (t_bwd_a / t_bwd_v - 1),
-                    step_pct=100 * (ms_a / ms_v - 1))
-
-    # roofline of the dominant kernel: the Averis forward GEMM, one launch of
-    # k_gemm_ws (the NT GEMM over the residual codes; the epilogue adds the
-    # rank-one row the split formed), timed by the events around the call on
-    # the launch stream.  The flops counted are the GEMM's 2lmn.
-    g_ms = comp["gemm_fwd"]
-    achieved = gemm_flops / (g_ms * 1e-3) / 1e12
-    tr = load_traffic()
-    traffic = None
-    if tr is not None:
-        traffic = tr["gemm_fwd"]["fetch_bytes"] + tr["gemm_fwd"]["write_bytes"]
+    # roofline of the dominant kernel: k_gemm_ws, the Averis GEMM (the
+    # warp-specialized NVFP4 NT GEMM adding the split's rank-one row), over
+    # all of its launches in a step: mean flops per launch / mean launch time
+    # (events around each call on the launch stream)
+    g_calls = [(L, k) for L in linears for k in ("gemm_fwd", "gemm_dgrad")]
+    g_ms = sum(float(np.mean(ta.ms(L.name + "/" + k))) for L, k in g_calls)
+    nlaunch = len(g_calls)
+    achieved = (flops_step / nlaunch) / (g_ms / nlaunch * 1e-3) / 1e12
+    tr = load_traffic(cfg)
+    traffic = None if tr is None else tr["averis_gemm"]["bytes_per_launch"]
     roofline = dict(bound="mfma", achieved=achieved, peak=F16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=achieved / F16_MFMA_PEAK_TFLOPS, traffic=traffic,
-                    kernel="k_gemm_ws (averis_gemm_rank1 on the forward operands: warp-specialized "
-                           "NVFP4 NT GEMM, exact fp16 dequant -> v_mfma_f32_32x32x16_f16, the rank-one "
-                           "row from the split added in the epilogue), M=%d N=%d K=%d, bf16 out"
-                           % (l, n, m),
+                    kernel="k_gemm_ws (averis_gemm_rank1: warp-specialized NVFP4 NT GEMM, exact "
+                           "fp16 dequant -> v_mfma_f32_32x32x16_f16, the rank-one row from the "
+                           "split added in the epilogue, bf16 out), all %d launches of one step "
+                           "(forward and dgrad of every linear)" % nlaunch,
+                    launches_per_step=nlaunch, mean_flops_per_launch=flops_step / nlaunch,
+                    mean_launch_ms=g_ms / nlaunch,
                     frac_of_fp4_peak=achieved / FP4_MFMA_PEAK_TFLOPS)
 
     out = {
         "metric": METRIC,
-        "value": 2 * gemm_flops / (ms_a * 1e-3) / 1e12,
+        "value": head["tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_a,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "nvfp4 (e2m1 + e4m3 scales) operands, f16 MFMA, f32 accumulate",
         "data": "synthetic",
-        "config": {"workload": "Qwen3-0.6B-shaped up-proj, Averis fwd+dgrad step",
-                   "tokens": l, "m": m, "n": n, "input_dtype": "bf16", "sr": "philox4x32-10, 16 bits",
-                   "rotating_input_copies": copies},
+        "config": {"workload": head["workload"], "config_id": cfg,
+                   "linears": {L.name: [L.l, L.m, L.n] for L in linears},
+                   "input_dtype": "bf16", "sr": "philox4x32-10, 16 bits"},
         "roofline": roofline,
-        "split_quant": split,
-        "vanilla_quant": vq,
-        "gemm": gemm,
-        "vanilla_gemm": vgemm,
-        "weight_quant_ms": comp["wquant"],
-        "vanilla_ms_per_step": ms_v,
-        "step_ms_by_launch": {"averis": ta_ms, "vanilla": tv_ms,
-                              "queued": "launches queued behind a spin kernel, events on the "
-                                        "launch stream (the headline)",
-                              "eager": "one Python call per op, host clock",
-                              "graph": "one HIP graph per step, replayed, host clock"},
-        "overhead_vs_vanilla": overhead,
-        "wgrad": wg,
-        "mean_energy_ratio": mer,
-        "weight_copies": wc,
+        "headline": head,
         "pages_overhead_context": "2.20% end-to-end over vanilla NVFP4 (hardware not stated)",
     }
-    if not args.no_cpu_baseline:
+    if not args.only_headline:
+        others = {}
+        for c in (1, 2, 3, 4):
+            if c == cfg:
+                continue
+            for L in linears:
+                L.xs, L.ds = [], []
+            del linears
+            torch.cuda.empty_cache()
+            log("bench: generating config %d" % c)
+            linears = make_linears(c)
+            others[str(c)] = measure(c, linears, args.steps, args.warmup)[0]
+        out["other_configs"] = others
+        # the (f) rows on one linear of the headline workload
+        for L in linears:
+            L.xs, L.ds = [], []
+        del linears
+        torch.cuda.empty_cache()
+        if cfg == 4:
+            c = workloads.block_linear("up")
+        elif cfg == 2:
+            c = workloads.down_proj()
+        else:
+            c = workloads.up_proj()
+        L = Linear("up" if cfg == 4 else "down_proj" if cfg == 2 else "up_proj",
+                   c["x"], c["w"], c["d"])
+        act = L.act_bytes()
+        L.rotate(max(1, int(np.ceil(ROTATE_BYTES / act))))
+        log("bench: wgrad, mean-energy ratio and weight copies on %s" % L.name)
+        out["wgrad"] = time_wgrad(L, args.steps, args.warmup)
+        out["mean_energy_ratio"] = time_ratio(L, args.steps, args.warmup)
+        out["weight_copies"] = time_weight_copies(L, args.steps, args.warmup)
+    if not args.no_cpu_baseline and cfg != 3:
         log("bench: timing the oracle on the host (bounded sample)")
-        out["cpu_baseline"] = cpu_baseline(args.cpu_rows or l, m, n)
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_rows)
     print(json.dumps(out), flush=True)
 
 

@@ -8,6 +8,7 @@ import pytest
 import torch
 
 from oracle import averis as orc
+from tests.parity import assert_gemm_close
 from mean_residual_quantized_amd import averis as av
 from mean_residual_quantized_amd import workloads
 
@@ -95,4 +96,4 @@ def test_averis_gemms_take_the_shared_copies(which):
     ref = orc.gemm(s["residual"], b_ref, s["mean"])
     bound = orc.gemm_abs_bound(s["residual"], b_ref, s["mean"])
     cc = c.cpu().numpy().astype(np.float64)
-    assert (np.abs(cc - ref) <= TOL * bound).all(), np.max(np.abs(cc - ref) / np.maximum(bound, 1e-300))
+    assert_gemm_close(cc, ref, bound)

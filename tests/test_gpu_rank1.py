@@ -9,6 +9,7 @@ import pytest
 import torch
 
 from oracle import averis as orc
+from tests.parity import assert_gemm_close
 from mean_residual_quantized_amd import averis as av
 from mean_residual_quantized_amd import workloads
 
@@ -48,8 +49,7 @@ def check(a, w, which, seed=0, rnd="sr", out_dtype=torch.float32):
     bound = orc.gemm_abs_bound(s["residual"], b_ref, s["mean"])
     extra = 2.0 ** -8 if out_dtype == torch.bfloat16 else 0.0
     cc = c.float().cpu().numpy().astype(np.float64)
-    ok = np.abs(cc - ref) <= TOL * bound + extra * np.abs(ref)
-    assert ok.all(), np.max(np.abs(cc - ref) / np.maximum(bound, 1e-300))
+    assert_gemm_close(cc, ref, bound, bf16=out_dtype == torch.bfloat16)
     # the same product as the GEMM that sums the rank-one row itself
     fn = av.averis_gemm_fwd if which == "x" else av.averis_gemm_dgrad
     c2 = fn(res, mean, b, out_dtype=torch.float32).cpu().numpy().astype(np.float64)
@@ -134,7 +134,7 @@ def test_grouped_with_an_empty_segment(hidden, inter):
     bound = np.concatenate([orc.gemm_abs_bound(g["residual"][s], wrefs[s], g["mean"][s])
                             for s in range(nseg)])
     cc = c.cpu().numpy().astype(np.float64)
-    assert (np.abs(cc - ref) <= TOL * bound).all(), np.max(np.abs(cc - ref) / np.maximum(bound, 1e-300))
+    assert_gemm_close(cc, ref, bound)
     torch.cuda.synchronize()
 
 

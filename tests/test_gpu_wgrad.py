@@ -8,6 +8,7 @@ import pytest
 import torch
 
 from oracle import averis as orc
+from tests.parity import assert_gemm_close
 from mean_residual_quantized_amd import averis as av
 from mean_residual_quantized_amd import workloads
 
@@ -38,10 +39,8 @@ def assert_quant_equal(gpu, ref, rows=None):
 
 
 def assert_close(c_gpu, ref, bound, extra=0.0):
-    c = c_gpu.float().cpu().numpy().astype(np.float64)
-    err = np.abs(c - ref)
-    ok = err <= GEMM_TOL * bound + extra * np.abs(ref)
-    assert ok.all(), "max normalised error %.3g" % np.max(err / np.maximum(bound, 1e-300))
+    # elementwise against the bound, and normwise for fp32 output
+    assert_gemm_close(c_gpu, ref, bound, bf16=extra > 0)
 
 
 def gpu_side(x, d, seed_x, seed_d, r, out_dtype=torch.float32):

@@ -63,13 +63,97 @@ def test_weight_copies_have_the_right_orientation():
         assert np.corrcoef(deq.ravel(), ref.ravel())[0, 1] > 0.98
 
 
-def test_unquantized_split_equals_plain_matmul():
-    # the split itself is exact algebra: 1 mu^T W + (X - 1 mu^T) W = X W
-    x = workloads.tiny()["x"].numpy().astype(np.float64)
-    w = workloads.tiny()["w"].numpy().astype(np.float64)
-    mu = x.mean(axis=0)
-    y = np.ones((x.shape[0], 1)) @ (mu[None, :] @ w) + (x - mu[None, :]) @ w
-    np.testing.assert_allclose(y, x @ w, rtol=1e-12, atol=1e-12 * np.abs(x @ w).max())
+def q4_exact_rows(rng, rows, cols, t, anchor_p):
+    """A (rows x cols) float64 matrix that Q4 (blocks of 16 along the rows)
+    maps to itself, RN or SR: element (0, 0) is the anchor 2688 * 2^-p, alone
+    in its block, which makes the tensor's amax 2688 * 2^-p and so S_enc = 2^p
+    and S_dec = 2^-p exactly; every other element is g * 2^t with g on the
+    E2M1 grid, and each other 16-run along a row holds one +-6 * 2^t (on the
+    diagonal i = j mod 16), so its scale is the E4M3 power of two 2^(t + p) and
+    its factor e_b = 2^-t is exact.  Needs -9 <= t + p <= 8.  Columns hold the
+    same pattern (the diagonal runs down them too), so the transpose is Q4-exact
+    along its rows as well, except for the anchor's column run, which is zero
+    apart from the anchor."""
+    g = np.array(GRID)[rng.integers(0, 7, size=(rows, cols))]   # |g| <= 4 off the diagonal
+    g *= np.where(rng.random((rows, cols)) < 0.5, -1.0, 1.0)
+    i, j = np.indices((rows, cols))
+    g[(i % 16) == (j % 16)] = np.where(rng.random(((i % 16) == (j % 16)).sum()) < 0.5, -6.0, 6.0)
+    m = g * 2.0 ** t
+    m[0, :16] = 0.0
+    m[:16, 0] = 0.0
+    m[0, 0] = 2688.0 * 2.0 ** -anchor_p
+    return m
+
+
+def test_split_gemm_is_exact_when_q4_is_the_identity():
+    # [Lighthouse] §2.2: Y = 1 (mean_q W_q) + X_R,q W_q.  On inputs whose mean,
+    # residual and weight Q4 maps to themselves (and whose every product and
+    # sum is exact in float64) the oracle's split forward and dgrad must equal
+    # X W and D W^T exactly: this pins, through the oracle's own functions, the
+    # mean, the residual, the rank-one row added to every output row, and the
+    # orientation of both weight copies.
+    rng = np.random.default_rng(11)
+    l, m, n = 64, 64, 48
+    w = q4_exact_rows(rng, m, n, -1, 9)                       # anchor 5.25, others <= 3
+    # residual: row pairs +v, -v, so every column sums to exactly zero
+    v = q4_exact_rows(rng, l // 2, m, -2, 8)                  # anchor 10.5, others <= 1.5
+    r = np.empty((l, m))
+    r[0::2], r[1::2] = v, -v
+    mu = q4_exact_rows(rng, 1, m, 0, 7)[0]                    # anchor 21, others <= 6
+    x = (r + mu[None, :]).astype(np.float32)
+    assert np.array_equal(x.astype(np.float64), r + mu[None, :])   # exact in float32
+    for rnd in ("rn", "sr"):
+        wq = averis.weight_quant(w.astype(np.float32), rnd)
+        np.testing.assert_array_equal(averis.dequantize(wq["fwd"]), w.T)
+        np.testing.assert_array_equal(averis.dequantize(wq["dgrad"]), w)
+        s, y = averis.averis_forward(x, wq["fwd"], rnd, seed=5)
+        np.testing.assert_array_equal(s["mu"], mu.astype(np.float32))
+        np.testing.assert_array_equal(averis.dequantize(s["residual"]), r)
+        np.testing.assert_array_equal(averis.dequantize(s["mean"])[0], mu)
+        np.testing.assert_array_equal(y, x.astype(np.float64) @ w)
+        # dgrad: D (l x n) = its residual + 1 nu^T, dX = D W^T
+        vd = q4_exact_rows(rng, l // 2, n, -3, 9)
+        rd = np.empty((l, n))
+        rd[0::2], rd[1::2] = vd, -vd
+        nu = q4_exact_rows(rng, 1, n, -1, 8)[0]
+        d = (rd + nu[None, :]).astype(np.float32)
+        sd, dx = averis.averis_dgrad(d, wq["dgrad"], rnd, seed=6)
+        np.testing.assert_array_equal(averis.dequantize(sd["residual"]), rd)
+        np.testing.assert_array_equal(dx, d.astype(np.float64) @ w.T)
+    # dropping the rank-one row (or adding it twice) breaks the equality
+    wq = averis.weight_quant(w.astype(np.float32), "rn")
+    s, y = averis.averis_forward(x, wq["fwd"], "rn", seed=5)
+    no_mean = averis.gemm(s["residual"], wq["fwd"])
+    assert not np.array_equal(no_mean, x.astype(np.float64) @ w)
+
+
+def test_gemm_abs_bound_brute_force_tiny():
+    # every GEMM parity test divides the error by this bound: pin it to a
+    # triple loop over hand-decoded bytes, sum_k |a_ik| |b_jk| + |mean_k| |b_jk|
+    cfg = workloads.tiny()
+    x, d, w = cfg["x"].numpy(), cfg["d"].numpy(), cfg["w"].numpy()
+    wq = averis.weight_quant(w, "rn")
+    rng = np.random.default_rng(7)
+    for a_in, b in ((x, wq["fwd"]), (d, wq["dgrad"])):
+        s = averis.split_quant(a_in, "sr", seed=3)
+        a, mu = s["residual"], s["mean"]
+        bound = averis.gemm_abs_bound(a, b, mu)
+        plain = averis.gemm_abs_bound(a, b)
+        rows, k = a_in.shape
+        n = b["codes"].shape[0]
+        assert bound.shape == (rows, n)
+        for i, j in zip(rng.integers(0, rows, 25), rng.integers(0, n, 25)):
+            with_mean = no_mean = 0.0
+            for kk in range(k):
+                bjk = abs(decode_by_hand(b, j, kk))
+                no_mean += abs(decode_by_hand(a, i, kk)) * bjk
+                with_mean += abs(decode_by_hand(mu, 0, kk)) * bjk
+            with_mean += no_mean
+            assert abs(bound[i, j] - with_mean) <= 1e-12 * with_mean, (i, j)
+            assert abs(plain[i, j] - no_mean) <= 1e-12 * no_mean, (i, j)
+        # the bound dominates the product it measures
+        c = averis.gemm(a, b, mu)
+        assert (np.abs(c) <= bound * (1 + 1e-12)).all()
 
 
 def test_constant_columns_rows_equal_mean_times_weight():

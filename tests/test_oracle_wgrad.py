@@ -105,3 +105,26 @@ def test_sr_wgrad_is_unbiased_over_seeds():
     err_avg = np.linalg.norm(acc / n - exact)
     # independent errors shrink as 1/sqrt(n) = 1/8; allow for the spread
     assert err_avg < 0.25 * err_one
+
+
+def test_wgrad_abs_bound_brute_force_tiny():
+    # the wgrad parity tests divide the error by this bound: pin it to a
+    # triple loop over hand-decoded bytes of the transposed residuals,
+    # sum_t |xt_it| |dt_jt| + l |mu_x,i| |mu_d,j|
+    from tests.test_oracle_gemm import decode_by_hand
+    cfg = workloads.tiny()
+    x, d = cfg["x"].float().numpy(), cfg["d"].float().numpy()
+    l = x.shape[0]
+    out = orc.averis_wgrad(x, d, "sr", 0, 1)
+    xt, dt = out["xt"], out["dt"]
+    bound = orc.wgrad_abs_bound(xt, dt, out["mu_x"], out["mu_d"], l)
+    assert bound.shape == (x.shape[1], d.shape[1])
+    rng = np.random.default_rng(9)
+    for i, j in zip(rng.integers(0, x.shape[1], 25), rng.integers(0, d.shape[1], 25)):
+        ref = sum(abs(decode_by_hand(xt, i, t)) * abs(decode_by_hand(dt, j, t)) for t in range(l))
+        ref += l * abs(float(out["mu_x"][i])) * abs(float(out["mu_d"][j]))
+        assert abs(bound[i, j] - ref) <= 1e-12 * ref, (i, j)
+        # and the product it bounds, from the same bytes
+        val = sum(decode_by_hand(xt, i, t) * decode_by_hand(dt, j, t) for t in range(l))
+        val += l * float(out["mu_x"][i]) * float(out["mu_d"][j])
+        assert abs(out["dw"][i, j] - val) <= 1e-12 * ref, (i, j)
