@@ -14,12 +14,14 @@
 //             packed nibbles; extra workgroups quantize the mean vectors
 // Partial sums are exact in fp64 when a column's values span a narrow enough
 // range (checked per column from its largest and smallest nonzero magnitude);
-// a column that fails the check is summed again exactly (320-bit integer
-// accumulation, rounded once), so the mean never depends on the order.
+// a column that fails the check is summed again exactly (its chunks' partials
+// that are exact on their own, and the rows of the others, in a 320-bit
+// integer, rounded once), so the mean never depends on the order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "device_common.hpp"
+#include "exact_sum.hpp"
 #include "gemm_common.hpp"
 #include "launch.hpp"
 #include "segments.hpp"
@@ -241,122 +243,54 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
 }
 
 // ---------------------------------------------------------------------------
-// Exact column sum for columns whose fp64 accumulation is not certified.
-// Every fp32 value is an integer multiple of 2^-149 below 2^128, so a signed
-// 320-bit integer in units of 2^-149 holds any sum of up to 2^31 of them
-// exactly.  Each thread adds its rows into its own accumulator, the block
-// adds the accumulators pairwise, and thread 0 rounds the total to the
-// nearest double (ties to even): the correctly rounded sum.
+// The correctly rounded sum of column j of one segment whose fp64 running sum
+// is not certified (certificate below).  The chunks' fp64 partial sums that
+// are exact by their own certificate (a chunk spans far fewer rows and
+// usually a far narrower range of values) are added exactly, the rows of the
+// other chunks one by one, into a 320-bit integer in units of 2^-149
+// (exact_sum.hpp), which is rounded once to the nearest double.  Chunk c of
+// the segment goes to thread c mod 256; the block then adds the accumulators
+// pairwise and thread 0 gets the result.  Kept out of line: the finalize
+// pass calls it only for a column that fails the certificate.
 // ---------------------------------------------------------------------------
-constexpr int kWideWords = 10;
 
-__device__ __forceinline__ void wide_add_value(uint32_t (&acc)[kWideWords], float v) {
-  const uint32_t bits = __float_as_uint(v);
-  const uint32_t e = (bits >> 23) & 0xFFu, m = bits & 0x7FFFFFu;
-  if (e == 0 && m == 0) return;
-  const uint32_t mant = e ? (m | 0x800000u) : m;   // value = mant * 2^(shift - 149)
-  const uint32_t shift = e ? e - 1 : 0;
-  const uint32_t w = shift >> 5;
-  const uint64_t part = (uint64_t)mant << (shift & 31);
-  const uint32_t lo = (uint32_t)part, hi = (uint32_t)(part >> 32);
-  if (!(bits >> 31)) {
-    uint64_t carry = 0;
-#pragma unroll
-    for (int i = 0; i < kWideWords; ++i) {
-      const uint32_t add = (uint32_t)i == w ? lo : ((uint32_t)i == w + 1 ? hi : 0u);
-      const uint64_t sum = (uint64_t)acc[i] + add + carry;
-      acc[i] = (uint32_t)sum;
-      carry = sum >> 32;
-    }
-  } else {
-    uint64_t borrow = 0;
-#pragma unroll
-    for (int i = 0; i < kWideWords; ++i) {
-      const uint32_t sub = (uint32_t)i == w ? lo : ((uint32_t)i == w + 1 ? hi : 0u);
-      const uint64_t d = (uint64_t)acc[i] - sub - borrow;
-      acc[i] = (uint32_t)d;
-      borrow = (d >> 32) ? 1u : 0u;
-    }
-  }
+// Certificate of an fp64 sum of n values of one column: every value is a
+// multiple of g = 2^(ez - 1 - P) (ez: binary exponent of the smallest nonzero
+// |a|, mnz; P = 7 for bf16 input, 23 for fp32) and every partial sum is at
+// most n max|a|, so when that is at most 2^52 g every fp64 addition was exact,
+// in any order.  No nonzero value: the sum is 0.
+__device__ __forceinline__ bool sum_certified(double n, double amax, float mnz, bool bf16) {
+  if (!(mnz < __builtin_inff())) return true;
+  int ez;
+  (void)__builtin_frexp((double)mnz, &ez);
+  return n * amax <= __builtin_ldexp(1.0, 52 + ez - 1 - (bf16 ? 7 : 23));
 }
 
-__device__ __forceinline__ void wide_add(uint32_t (&acc)[kWideWords], const uint32_t* other) {
-  uint64_t carry = 0;
-#pragma unroll
-  for (int i = 0; i < kWideWords; ++i) {
-    const uint64_t sum = (uint64_t)acc[i] + other[i] + carry;
-    acc[i] = (uint32_t)sum;
-    carry = sum >> 32;
-  }
-}
-
-// bits [lo, lo + 64) of the magnitude (bits past the top read as 0)
-__device__ __forceinline__ uint64_t wide_bits64(const uint32_t (&a)[kWideWords], int lo) {
-  uint64_t r = 0;
-#pragma unroll
-  for (int i = 0; i < kWideWords; ++i) {
-    const int off = 32 * i - lo;   // position of word i's bit 0 in the result
-    if (off >= 64 || off <= -32) continue;
-    const uint64_t wv = a[i];
-    r |= off >= 0 ? (wv << off) : (wv >> -off);
-  }
-  return r;
-}
-
-__device__ inline double wide_to_double(uint32_t (&a)[kWideWords]) {
-  const bool neg = a[kWideWords - 1] >> 31;
-  if (neg) {   // magnitude: two's complement negation
-    uint64_t carry = 1;
-#pragma unroll
-    for (int i = 0; i < kWideWords; ++i) {
-      const uint64_t v = (uint64_t)(~a[i]) + carry;
-      a[i] = (uint32_t)v;
-      carry = v >> 32;
-    }
-  }
-  int p = -1;   // highest set bit
-#pragma unroll
-  for (int i = 0; i < kWideWords; ++i)
-    if (a[i]) p = 32 * i + 31 - __builtin_clz(a[i]);
-  if (p < 0) return 0.0;
-  double r;
-  if (p < 53) {
-    r = __builtin_ldexp((double)wide_bits64(a, 0), -149);   // exact
-  } else {
-    uint64_t mant = wide_bits64(a, p - 52) & ((1ull << 53) - 1);
-    const bool round = (wide_bits64(a, p - 53) & 1ull) != 0;
-    bool sticky = false;
-    for (int b = 0; b < p - 53; b += 64) {
-      const int n = p - 53 - b;
-      const uint64_t chunk = wide_bits64(a, b);
-      sticky = sticky || (n >= 64 ? chunk != 0 : (chunk & ((1ull << n) - 1)) != 0);
-    }
-    int ex = p - 52 - 149;
-    if (round && (sticky || (mant & 1ull))) {
-      mant += 1;
-      if (mant >> 53) {
-        mant >>= 1;
-        ex += 1;
-      }
-    }
-    r = __builtin_ldexp((double)mant, ex);
-  }
-  return neg ? -r : r;
-}
-
-// the exact sum of rows [r0, r1) of column j, correctly rounded to double;
-// all 256 threads call it, thread 0 gets the result
-// (kept out of line: the finalize pass calls it only for a column that fails
-// the certificate, and inlined it would quadruple that kernel's code)
-__device__ __noinline__ double exact_column_sum(const void* a, bool bf16, int64_t lda, int64_t r0, int64_t r1,
-                                   int64_t j, uint32_t (*red)[kWideWords]) {
+__device__ __noinline__ double exact_column_sum(const void* a, bool bf16, int64_t lda,
+                                                int64_t cols, int64_t seg_r0, int64_t seg_r1,
+                                                int64_t c0, int64_t c1, int64_t j,
+                                                const double* __restrict__ psum,
+                                                const float* __restrict__ pmax,
+                                                const float* __restrict__ pmin,
+                                                const float* __restrict__ pmnz,
+                                                uint32_t (*red)[kWideWords]) {
   uint32_t acc[kWideWords];
 #pragma unroll
   for (int i = 0; i < kWideWords; ++i) acc[i] = 0u;
-  for (int64_t r = r0 + threadIdx.x; r < r1; r += 256) {
-    const float v = bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(a)[r * lda + j] << 16)
-                         : static_cast<const float*>(a)[r * lda + j];
-    wide_add_value(acc, v);
+  for (int64_t c = c0 + threadIdx.x; c < c1; c += 256) {
+    const int64_t r0 = seg_r0 + (c - c0) * kStatsRows;
+    const int64_t r1 = r0 + kStatsRows < seg_r1 ? r0 + kStatsRows : seg_r1;
+    const int64_t o = c * cols + j;
+    const double am = __builtin_fmax(__builtin_fabs((double)pmax[o]), __builtin_fabs((double)pmin[o]));
+    if (sum_certified((double)(r1 - r0), am, pmnz[o], bf16)) {
+      wide_add_f64(acc, psum[o]);
+    } else {
+      for (int64_t r = r0; r < r1; ++r) {
+        const float v = bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(a)[r * lda + j] << 16)
+                             : static_cast<const float*>(a)[r * lda + j];
+        wide_add_f32(acc, v);
+      }
+    }
   }
   for (int stride = 128; stride > 0; stride >>= 1) {
     if ((int)threadIdx.x >= stride && (int)threadIdx.x < 2 * stride) {
@@ -396,7 +330,7 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
   double s = 0.0, s2 = 0.0;
   float m1 = -__builtin_inff(), m0 = __builtin_inff(), mz = __builtin_inff();
   if (j < cols && sr.c1 > sr.c0) {
-    constexpr int U = 4;
+    constexpr int U = 8;   // up to 128 chunks in one round of loads
     const int64_t clast = sr.c1 - 1;
     for (int64_t ck = sr.c0 + q; ck < sr.c1; ck += NQ * U) {
       double ps[U], pq[U];
@@ -451,11 +385,9 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
     // (ez: binary exponent of the smallest nonzero |a|; P = 7 for bf16 input,
     // 23 for fp32), and every partial sum is at most l * max|a|.  When that
     // bound is <= 2^52 g, every fp64 addition above was exact, in any order.
-    if (j < cols && l > 0 && z < __builtin_inff()) {
-      int ez;
-      (void)__builtin_frexp((double)z, &ez);
+    if (j < cols && l > 0) {
       const double amx = __builtin_fmax(__builtin_fabs((double)x1), __builtin_fabs((double)x0));
-      fail = !((double)l * amx <= __builtin_ldexp(1.0, 52 + ez - 1 - (a_bf16 ? 7 : 23)));
+      fail = !sum_certified((double)l, amx, z, a_bf16);
     }
   }
   // the q == 0 lanes are lanes 0 .. NC-1 of wave 0
@@ -467,8 +399,9 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
   const uint32_t mask = need_mask;   // uniform
   for (uint32_t mrest = mask; mrest != 0; mrest &= mrest - 1) {
     const int cidx = __builtin_ctz(mrest);
-    const double v = exact_column_sum(a, a_bf16, lda, sr.seg_r0, sr.seg_r1,
-                                      (int64_t)blockIdx.x * NC + cidx, wide_red);
+    const double v = exact_column_sum(a, a_bf16, lda, cols, sr.seg_r0, sr.seg_r1, sr.c0, sr.c1,
+                                      (int64_t)blockIdx.x * NC + cidx, psum, pmax, pmin, pmnz,
+                                      wide_red);
     if (threadIdx.x == 0) exact_s[cidx] = v;
   }
   if (mask) __syncthreads();

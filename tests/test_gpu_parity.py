@@ -142,19 +142,27 @@ def adversarial_columns(rows, cols, seed):
     x[:, 2] = np.where(i % 5 == 0, np.float32(7.0), np.float32(2.0 ** -130))   # fp32 subnormal
     x[:, 3] = 0.0
     x[:, 5] = np.where(i % 3 == 0, np.float32(2.0 ** 60), np.float32(0.75)) * np.where(i % 2, 1, -1)
+    # chunks of 128 rows that are each exact on their own while the column as
+    # a whole is not: tiny values in the first chunk, huge ones after it (the
+    # exact sum then adds the chunks' exact partials)
+    small = rng.integers(-100, 100, rows) * np.float32(2.0 ** -60)
+    large = rng.integers(-100, 100, rows) * np.float32(2.0 ** 40)
+    x[:, 6] = np.where(i < 128, small, large).astype(np.float32)
+    x[:, 7] = np.where((i // 128) % 2 == 0, large, small).astype(np.float32)
     return x
 
 
+@pytest.mark.parametrize("rows", [300, 4000])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_uncertified_columns_take_the_exact_sum(dtype):
-    x = torch.from_numpy(adversarial_columns(300, 64, 5)).to(dtype)
+def test_uncertified_columns_take_the_exact_sum(dtype, rows):
+    x = torch.from_numpy(adversarial_columns(rows, 64, 5)).to(dtype)
     res, mean, mu = av.averis_split_quant(x.cuda(), seed=3)
     s = orc.split_quant(f32(x), "sr", 3)
     np.testing.assert_array_equal(mu.cpu().numpy(), s["mu"])
     assert_quant_equal(res, s["residual"])
     assert_quant_equal(mean, s["mean"])
     # grouped: each segment's mean on its own rows
-    offs = np.array([0, 97, 97, 300], dtype=np.int64)
+    offs = np.array([0, 97, 97, rows], dtype=np.int64)
     og = torch.from_numpy(offs).cuda()
     res_g, mean_g, mu_g = av.averis_split_quant_grouped(x.cuda(), og, seed=3)
     g = orc.split_quant_grouped(f32(x), offs, "sr", 3)
@@ -277,3 +285,39 @@ def test_grouped_moe_reduced():
     yv = av.averis_gemm_grouped(qv, None, wt, og)
     assert_gemm_close(yv, orc.gemm_grouped(vrefs, wrefs),
                       np.concatenate([orc.gemm_abs_bound(vrefs[s], wrefs[s]) for s in range(nseg)]))
+
+
+def test_workspace_reused_across_calls():
+    # the workspace holds intermediate results only: one workspace per shape
+    # serves many calls in a row (the plain, ratio and rank-one forms of the
+    # split, plain quant in between; the grouped split with plain grouped
+    # quant) and every result equals the result of a fresh workspace.
+    rows, cols = 1000, 320
+    cfg = workloads.up_proj(l=rows, m=cols, n=192)
+    offs = torch.tensor([0, 100, 100, 999, 1000], dtype=torch.int64, device="cuda")
+    nseg = offs.numel() - 1
+    filled = lambda n: torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")
+    ws1 = filled(max(av.workspace_bytes(av.OP_SPLIT_QUANT, rows, cols),
+                    av.workspace_bytes(av.OP_QUANT, rows, cols)))
+    wsg = filled(max(av.workspace_bytes(av.OP_SPLIT_QUANT, rows, cols, 0, nseg),
+                    av.workspace_bytes(av.OP_QUANT, rows, cols, 0, nseg)))
+    wq = av.averis_quant(cfg["w"].cuda(), transpose=True, rnd=av.RN, sr_stream=av.STREAM_WEIGHT)
+    flat = lambda outs: [t for o in outs for t in ((o.codes, o.scales, o.tscale)
+                                                   if isinstance(o, av.NVFP4) else (o,))]
+    for it in range(4):
+        x = (cfg["x"].float() * (1 + it) + it).to(torch.bfloat16).cuda()
+        runs = [
+            (ws1, lambda w: av.averis_split_quant(x, seed=it, ws=w)),
+            (ws1, lambda w: (av.averis_quant(x, seed=it, ws=w),)),
+            (ws1, lambda w: av.averis_split_quant_ratio(x, seed=it, ws=w)),
+            (ws1, lambda w: av.averis_split_quant_rank1(x, wq, seed=it, ws=w)),
+            (wsg, lambda w: av.averis_split_quant_grouped(x, offs, seed=it, ws=w)),
+            (wsg, lambda w: (av.averis_quant_grouped(x, offs, seed=it, ws=w),)),
+            (wsg, lambda w: av.averis_split_quant_ratio(x, seed=it, offsets=offs, ws=w)),
+        ]
+        for ws, run in runs:
+            got = flat(run(ws))
+            ref = flat(run(None))            # a fresh workspace
+            for g, r in zip(got, ref):
+                assert torch.equal(g, r)
+    torch.cuda.synchronize()
