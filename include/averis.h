@@ -341,6 +341,34 @@ averis_status_t averis_gemm_wgrad(const averis_nvfp4_t* xt, const averis_nvfp4_t
                                   hipStream_t stream);
 
 /* ---------------------------------------------------------------------- */
+/* Allocation-free split-quant                                             */
+/* ---------------------------------------------------------------------- */
+
+/* Bytes of the device array that averis_split_quant_noalloc uses as its
+ * workspace (one copy per device). */
+#define AVERIS_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  averis_split_quant with the same arguments and results, bit for
+ * bit, whose workspace is a file-scope device array of
+ * AVERIS_NOALLOC_SCRATCH_BYTES inside the library: the call allocates
+ * nothing.  The array holds the split's intermediate results, which depend on
+ * the shape: averis_workspace_bytes(AVERIS_OP_SPLIT_QUANT, rows, cols, 0, 0)
+ * must not exceed AVERIS_NOALLOC_SCRATCH_BYTES (about rows / 128 * cols * 28
+ * bytes: a 16384 x 3072 input fits), else the call returns
+ * AVERIS_E_WORKSPACE, enqueues nothing, and averis_last_error() names both
+ * sizes.  Every call on one device shares that device's array: calls that
+ * overlap on one device (several streams or threads at once) race and give
+ * wrong results; order them on one stream.  The first call on a device looks
+ * up the array's address there (once; the lookup is not captured). */
+averis_status_t averis_split_quant_noalloc(const void* a, averis_dtype_t dtype, int64_t rows,
+                                           int64_t cols, int64_t lda, uint64_t seed,
+                                           averis_round_t rnd, const averis_nvfp4_t* residual,
+                                           const averis_nvfp4_t* mean, float* mean_f32,
+                                           hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
 /* Utilities                                                               */
 /* ---------------------------------------------------------------------- */
 
@@ -355,7 +383,8 @@ const char* averis_status_str(averis_status_t status);
 int averis_abi_version(void);
 
 /* Text of the last HIP error an entry point on the calling thread returned
- * AVERIS_E_HIP for ("" if none).  The string is owned by the library and is
+ * AVERIS_E_HIP for, or of the size check averis_split_quant_noalloc returned
+ * AVERIS_E_WORKSPACE for ("" if none).  The string is owned by the library and is
  * valid until the next call on the same thread. */
 const char* averis_last_error(void);
 

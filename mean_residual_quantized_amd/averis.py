@@ -31,7 +31,7 @@ EXPORTS = [
     "averis_gemm_vanilla", "averis_gemm_grouped", "averis_residual_t_quant", "averis_gemm_wgrad",
     "averis_split_quant_ratio", "averis_split_quant_rank1", "averis_gemm_rank1",
     "averis_split_quant_grouped_rank1", "averis_gemm_grouped_rank1",
-    "averis_workspace_bytes", "averis_status_str",
+    "averis_split_quant_noalloc", "averis_workspace_bytes", "averis_status_str",
     "averis_abi_version", "averis_last_error",
 ]
 
@@ -81,6 +81,7 @@ def lib():
             "averis_split_quant_grouped_rank1": [P, I, I64, I64, I64, P, I, U64, I, T, T, P, T, P,
                                                  P, SZ, P],
             "averis_gemm_grouped_rank1": [T, P, T, P, I, P, I, I64, P],
+            "averis_split_quant_noalloc": [P, I, I64, I64, I64, U64, I, T, T, P, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -177,6 +178,20 @@ def averis_split_quant(a, seed=0, rnd=SR, ws=None):
     _check("averis_split_quant", lib().averis_split_quant(
         a.data_ptr(), _dtype_code(a), rows, cols, _lda(a), seed, rnd, ctypes.byref(r),
         ctypes.byref(m), mu.data_ptr(), ws.data_ptr(), ws.numel(), _stream()))
+    return res, mean, mu
+
+
+def averis_split_quant_noalloc(a, seed=0, rnd=SR):
+    """averis_split_quant with the library's own device array as the
+    workspace (no workspace argument); returns (residual, mean, mu_f32)."""
+    rows, cols = a.shape
+    res = NVFP4.empty(rows, cols, 1, a.device)
+    mean = NVFP4.empty(1, cols, 1, a.device)
+    mu = torch.empty((cols,), dtype=torch.float32, device=a.device)
+    r, m = res.c(), mean.c()
+    _check("averis_split_quant_noalloc", lib().averis_split_quant_noalloc(
+        a.data_ptr(), _dtype_code(a), rows, cols, _lda(a), seed, rnd, ctypes.byref(r),
+        ctypes.byref(m), mu.data_ptr(), _stream()))
     return res, mean, mu
 
 

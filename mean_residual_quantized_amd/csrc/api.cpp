@@ -3,6 +3,7 @@
 // device state and the checks can be exercised on a machine without a GPU.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstddef>
 #include <cstdint>
 #include <cstdio>
@@ -51,6 +52,34 @@ inline averis_status_t hip_status(hipError_t e) {
   std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s", hipGetErrorName(e),
                 hipGetErrorString(e));
   return AVERIS_E_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// The allocation-free split-quant keeps its workspace in this file-scope
+// device array (one copy per device, allocated with the code object).  Host
+// code never passes the array's name to a kernel: the name is a host-side
+// stand-in, not a device address.  The device address is looked up once per
+// device with hipGetSymbolAddress, with that device current, and kept.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = AVERIS_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // concurrent first calls on one device look up the same address
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 }  // namespace
@@ -506,6 +535,34 @@ averis_status_t averis_gemm_wgrad(const averis_nvfp4_t* xt, const averis_nvfp4_t
   const QOperand qd{dt->codes, dt->scales, dt->tscale};
   return hip_status(launch_wgrad(qx, qd, mu_x, mu_d, m, n, l, dw, dwdtype == AVERIS_BF16, lddw, ws,
                                  stream));
+}
+
+averis_status_t averis_split_quant_noalloc(const void* a, averis_dtype_t dtype, int64_t rows,
+                                           int64_t cols, int64_t lda, uint64_t seed,
+                                           averis_round_t rnd, const averis_nvfp4_t* residual,
+                                           const averis_nvfp4_t* mean, float* mean_f32,
+                                           hipStream_t stream) {
+  // the argument checks of averis_split_quant and the scratch limit, before
+  // any HIP call
+  averis_status_t s = check_input(a, dtype, rows, cols, lda, cols);
+  if (s != AVERIS_OK) return s;
+  if (rnd != AVERIS_RN && rnd != AVERIS_SR) return AVERIS_E_ARG;
+  if ((s = check_tensor(residual, rows, cols)) != AVERIS_OK) return s;
+  if ((s = check_tensor(mean, 1, cols)) != AVERIS_OK) return s;
+  if (!aligned(mean_f32, 4)) return AVERIS_E_ALIGN;
+  const size_t need = split_ws_bytes(rows, cols, 1);
+  if (need > kScratchBytes) {
+    std::snprintf(g_last_error, sizeof(g_last_error),
+                  "averis_split_quant_noalloc: a %lld x %lld input needs %zu bytes of scratch; "
+                  "the library's device array holds %zu",
+                  (long long)rows, (long long)cols, need, kScratchBytes);
+    return AVERIS_E_WORKSPACE;
+  }
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  return split_common(a, dtype, rows, cols, lda, nullptr, 1, seed, rnd, residual, mean, mean_f32,
+                      ws, kScratchBytes, stream);
 }
 
 }  // extern "C"

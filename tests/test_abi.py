@@ -84,6 +84,30 @@ def test_split_quant_rejections(L):
     assert split(L, ws=P + 16) == 4                       # workspace alignment
 
 
+def test_noalloc_split_rejections(L):
+    # the argument checks of averis_split_quant, and inputs whose
+    # intermediate results do not fit the library's device array, all before
+    # any HIP call (this host has no GPU)
+    sq = lambda a=P, dtype=av.BF16, rows=64, cols=128, lda=128, rnd=av.SR, res=None, mean=None: \
+        L.averis_split_quant_noalloc(a, dtype, rows, cols, lda, 0, rnd,
+                                     ctypes.byref(res if res is not None else nv(rows, cols)),
+                                     ctypes.byref(mean if mean is not None else nv(1, cols)),
+                                     None, None)
+    assert sq(cols=24, lda=24) == 2
+    assert sq(dtype=7) == 3
+    assert sq(a=None) == 1
+    assert sq(a=P + 2) == 4
+    assert sq(rnd=5) == 6
+    assert sq(res=nv(64, 64)) == 2
+    limit = 16 << 20
+    rows, cols = 32768, 3072
+    assert av.workspace_bytes(av.OP_SPLIT_QUANT, rows, cols) > limit
+    assert sq(rows=rows, cols=cols, lda=cols) == 5
+    msg = L.averis_last_error().decode()
+    assert "noalloc" in msg and str(limit) in msg, msg
+    assert av.workspace_bytes(av.OP_SPLIT_QUANT, 16384, 3072) <= limit
+
+
 def test_quant_and_gemm_rejections(L):
     out = nv(64, 128)
     q = lambda **k: L.averis_quant(k.get("a", P), k.get("dt", av.BF16), k.get("rows", 64),
