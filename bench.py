@@ -505,6 +505,52 @@ def time_ratio(L, steps, warmup):
         for name in ("x", "d")})
 
 
+def time_fused_statistics(L, steps, warmup):
+    """Column statistics fused into the producer, on one linear: the forward
+    GEMM with and without writing the statistics of its bf16 output Y, and
+    the split of Y with its own statistics pass (two reads of Y) and from the
+    GEMM's statistics (one read), per call (events on the launch stream,
+    queued behind a spin kernel)."""
+    x = L.xs[0]
+    wt, _ = av.averis_quant_pair(L.w, rnd=av.RN)
+    xr, _, _, rho = av.averis_split_quant_rank1(x, wt, seed=0)
+    y = torch.empty((L.l, L.n), dtype=torch.bfloat16, device=x.device)
+    wsy = torch.empty(av.workspace_bytes(av.OP_SPLIT_QUANT, L.l, L.n), dtype=torch.uint8,
+                      device=x.device)
+
+    def one(t):
+        t.start("gemm")
+        av.averis_gemm_rank1(xr, rho, wt, out_dtype=torch.bfloat16, out=y)
+        t.stop("gemm")
+        t.start("split_two_reads")
+        av.averis_split_quant(y, seed=2, ws=wsy)
+        t.stop("split_two_reads")
+        t.start("gemm_with_stats")
+        av.averis_gemm_rank1_stats(xr, rho, wt, ws=wsy, out=y)
+        t.stop("gemm_with_stats")
+        t.start("split_one_read")
+        av.averis_split_quant_from_stats(y, wsy, seed=2)
+        t.stop("split_one_read")
+
+    for _ in range(warmup):
+        one(Timer())
+    torch.cuda.synchronize()
+    t = Timer()
+    hold_gpu(5.0 + 0.5 * steps)
+    for _ in range(steps):
+        one(t)
+    torch.cuda.synchronize()
+    ms = {k: stats(t.ms(k)) for k in ("gemm", "gemm_with_stats", "split_two_reads",
+                                      "split_one_read")}
+    sq = L.l * L.n * SQ_BYTES_PER_ELEM
+    return dict(linear=L.name, y_shape=[L.l, L.n], ms=ms,
+                split_gbs={"two_reads": sq / (ms["split_two_reads"]["ms"] * 1e-3) / 1e9,
+                           "one_read": sq / (ms["split_one_read"]["ms"] * 1e-3) / 1e9},
+                producer_plus_split_ms={
+                    "separate": ms["gemm"]["ms"] + ms["split_two_reads"]["ms"],
+                    "fused": ms["gemm_with_stats"]["ms"] + ms["split_one_read"]["ms"]})
+
+
 def time_weight_copies(L, steps, warmup):
     """Both weight copies per call (events on the launch stream, queued behind
     a spin kernel): the two 1-D quantizations (averis_quant_pair) and the
@@ -711,6 +757,7 @@ def main():
         out["wgrad"] = time_wgrad(L, args.steps, args.warmup)
         out["mean_energy_ratio"] = time_ratio(L, args.steps, args.warmup)
         out["weight_copies"] = time_weight_copies(L, args.steps, args.warmup)
+        out["fused_statistics"] = time_fused_statistics(L, args.steps, args.warmup)
     if not args.no_cpu_baseline and cfg != 3:
         log("bench: timing the oracle on the host (bounded sample)")
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_rows)

@@ -341,6 +341,42 @@ averis_status_t averis_gemm_wgrad(const averis_nvfp4_t* xt, const averis_nvfp4_t
                                   hipStream_t stream);
 
 /* ---------------------------------------------------------------------- */
+/* Column statistics fused into the producer (Lighthouse §2.2 cost note:   */
+/* the split adds two column reductions and two subtractions; §4.2: it     */
+/* changes the quantization kernel's pre-processing).  The GEMM that makes */
+/* the next split's input gathers that input's column statistics in its   */
+/* epilogue, so the split reads its input once.                            */
+/* ---------------------------------------------------------------------- */
+
+/* averis_gemm_rank1 with bf16 output c (n = b->rows columns, row stride ldc)
+ * that also writes the column statistics of c, as stored, into ws: per
+ * 256-row tile and column, the fp64 sum, max, min and smallest nonzero
+ * magnitude.  ws is the split-quant workspace of c:
+ * averis_workspace_bytes(AVERIS_OP_SPLIT_QUANT, a->rows, n, 0, 0) bytes, to
+ * be passed unchanged to averis_split_quant_from_stats for this c (nothing
+ * else may use it in between).  Needs a->cols % 64 == 0, n % 16 == 0, c
+ * 16-byte aligned and ldc * 2 % 16 == 0 (c is then a valid split input).
+ * c equals averis_gemm_rank1's bf16 output bit for bit. */
+averis_status_t averis_gemm_rank1_stats(const averis_nvfp4_t* a, const float* rho,
+                                        const averis_nvfp4_t* b, void* c, int64_t ldc, void* ws,
+                                        size_t ws_bytes, hipStream_t stream);
+
+/* averis_split_quant of the bf16 rows x cols tensor a (row stride lda) from
+ * the column statistics that averis_gemm_rank1_stats wrote into ws when it
+ * produced a: the mean, the tensor scales and the quantized outputs are
+ * averis_split_quant's bit for bit, and a is read once (by the quant pass;
+ * a column whose sum is not certified exact is re-summed from its tiles'
+ * partials and, for a tile not exact on its own, from its rows).  b and rho:
+ * both NULL, or the rank-one row of the GEMM that takes this split, as for
+ * averis_split_quant_rank1.  Order this call after that GEMM (same stream). */
+averis_status_t averis_split_quant_from_stats(const void* a, int64_t rows, int64_t cols,
+                                              int64_t lda, uint64_t seed, averis_round_t rnd,
+                                              const averis_nvfp4_t* residual,
+                                              const averis_nvfp4_t* mean, float* mean_f32,
+                                              const averis_nvfp4_t* b, float* rho, void* ws,
+                                              size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
 /* Allocation-free split-quant                                             */
 /* ---------------------------------------------------------------------- */
 

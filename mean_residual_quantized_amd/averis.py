@@ -31,7 +31,8 @@ EXPORTS = [
     "averis_gemm_vanilla", "averis_gemm_grouped", "averis_residual_t_quant", "averis_gemm_wgrad",
     "averis_split_quant_ratio", "averis_split_quant_rank1", "averis_gemm_rank1",
     "averis_split_quant_grouped_rank1", "averis_gemm_grouped_rank1",
-    "averis_split_quant_noalloc", "averis_workspace_bytes", "averis_status_str",
+    "averis_split_quant_noalloc", "averis_gemm_rank1_stats", "averis_split_quant_from_stats",
+    "averis_workspace_bytes", "averis_status_str",
     "averis_abi_version", "averis_last_error",
 ]
 
@@ -82,6 +83,8 @@ def lib():
                                                  P, SZ, P],
             "averis_gemm_grouped_rank1": [T, P, T, P, I, P, I, I64, P],
             "averis_split_quant_noalloc": [P, I, I64, I64, I64, U64, I, T, T, P, P],
+            "averis_gemm_rank1_stats": [T, P, T, P, I64, P, SZ, P],
+            "averis_split_quant_from_stats": [P, I64, I64, I64, U64, I, T, T, P, T, P, P, SZ, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -446,3 +449,38 @@ def averis_gemm_grouped_rank1(a, rho, b, offsets, out_dtype=torch.float32, out=N
         ctypes.byref(ca), rho.data_ptr(), ctypes.byref(cb), offsets.data_ptr(), nseg,
         c.data_ptr(), _dtype_code(c), c.stride(0), _stream()))
     return c
+
+
+def averis_gemm_rank1_stats(a, rho, b, ws=None, out=None):
+    """averis_gemm_rank1 with bf16 output that also writes the column
+    statistics of the output into ws, the split workspace of that output;
+    returns (c, ws) for averis_split_quant_from_stats."""
+    m, n = a.rows, b.rows
+    c = _out(m, n, torch.bfloat16, a.codes.device, out)
+    need = workspace_bytes(OP_SPLIT_QUANT, m, n)
+    ws = ws if ws is not None else _workspace(need, a.codes.device)
+    ca, cb = a.c(), b.c()
+    _check("averis_gemm_rank1_stats", lib().averis_gemm_rank1_stats(
+        ctypes.byref(ca), rho.data_ptr(), ctypes.byref(cb), c.data_ptr(), c.stride(0),
+        ws.data_ptr(), ws.numel(), _stream()))
+    return c, ws
+
+
+def averis_split_quant_from_stats(c, ws, seed=0, rnd=SR, b=None, rho=None):
+    """averis_split_quant of the bf16 output c of averis_gemm_rank1_stats from
+    the statistics it left in ws; with b, also the rank-one row for the GEMM
+    that takes this split.  Returns (residual, mean, mu_f32) or, with b,
+    (residual, mean, mu_f32, rho)."""
+    rows, cols = c.shape
+    res = NVFP4.empty(rows, cols, 1, c.device)
+    mean = NVFP4.empty(1, cols, 1, c.device)
+    mu = torch.empty((cols,), dtype=torch.float32, device=c.device)
+    if b is not None and rho is None:
+        rho = torch.empty((b.rows,), dtype=torch.float32, device=c.device)
+    r, m = res.c(), mean.c()
+    cb = b.c() if b is not None else None
+    _check("averis_split_quant_from_stats", lib().averis_split_quant_from_stats(
+        c.data_ptr(), rows, cols, _lda(c), seed, rnd, ctypes.byref(r), ctypes.byref(m),
+        mu.data_ptr(), ctypes.byref(cb) if cb is not None else None,
+        rho.data_ptr() if rho is not None else None, ws.data_ptr(), ws.numel(), _stream()))
+    return (res, mean, mu) if b is None else (res, mean, mu, rho)

@@ -537,6 +537,62 @@ averis_status_t averis_gemm_wgrad(const averis_nvfp4_t* xt, const averis_nvfp4_t
                                  stream));
 }
 
+averis_status_t averis_gemm_rank1_stats(const averis_nvfp4_t* a, const float* rho,
+                                        const averis_nvfp4_t* b, void* c, int64_t ldc, void* ws,
+                                        size_t ws_bytes, hipStream_t stream) {
+  if (!a || !b || !rho) return AVERIS_E_NULL;
+  const int64_t m = a->rows, k = a->cols, n = b->rows;
+  // the warp-specialized kernel (K % 64 == 0); c must be a valid split input
+  if (m < 0 || k <= 0 || k % 64 != 0 || b->cols != k) return AVERIS_E_SHAPE;
+  if (n <= 0 || n % 16 != 0 || ldc < n) return AVERIS_E_SHAPE;
+  averis_status_t s;
+  if ((s = check_tensor(a, m, k)) != AVERIS_OK) return s;
+  if ((s = check_tensor(b, n, k)) != AVERIS_OK) return s;
+  if (!aligned(rho, 4)) return AVERIS_E_ALIGN;
+  if (m > 0 && !c) return AVERIS_E_NULL;
+  if (!aligned(c, 16) || (ldc * 2) % 16 != 0) return AVERIS_E_ALIGN;
+  const size_t need = split_ws_bytes(m, n, 1);
+  if (!ws || ws_bytes < need) return AVERIS_E_WORKSPACE;
+  if (!aligned(ws, 256)) return AVERIS_E_ALIGN;
+  const SplitWs w = split_ws_carve(ws, m, n, 1);
+  const ColStats cs{w.psum, w.pmax, w.pmin, w.pmnz};
+  const QOperand qa{a->codes, a->scales, a->tscale};
+  const QOperand qb{b->codes, b->scales, b->tscale};
+  return hip_status(launch_gemm_rho_stats(qa, rho, qb, m, n, k, nullptr, 1, c, ldc, cs, stream));
+}
+
+averis_status_t averis_split_quant_from_stats(const void* a, int64_t rows, int64_t cols,
+                                              int64_t lda, uint64_t seed, averis_round_t rnd,
+                                              const averis_nvfp4_t* residual,
+                                              const averis_nvfp4_t* mean, float* mean_f32,
+                                              const averis_nvfp4_t* b, float* rho, void* ws,
+                                              size_t ws_bytes, hipStream_t stream) {
+  averis_status_t s = check_input(a, AVERIS_BF16, rows, cols, lda, cols);
+  if (s != AVERIS_OK) return s;
+  if (rnd != AVERIS_RN && rnd != AVERIS_SR) return AVERIS_E_ARG;
+  if ((s = check_tensor(residual, rows, cols)) != AVERIS_OK) return s;
+  if ((s = check_tensor(mean, 1, cols)) != AVERIS_OK) return s;
+  if (!aligned(mean_f32, 4)) return AVERIS_E_ALIGN;
+  Rank1Out r1{QOperand{nullptr, nullptr, nullptr}, 0, nullptr};
+  if (b || rho) {
+    if (!b || !rho) return AVERIS_E_NULL;
+    if (!aligned(rho, 4)) return AVERIS_E_ALIGN;
+    if (cols > kRank1MaxK) return AVERIS_E_SHAPE;
+    if ((s = check_tensor(b, b->rows, cols)) != AVERIS_OK) return s;
+    if (b->rows <= 0) return AVERIS_E_SHAPE;
+    r1 = Rank1Out{QOperand{b->codes, b->scales, b->tscale}, b->rows, rho};
+  }
+  const size_t need = split_ws_bytes(rows, cols, 1);
+  if (!ws || ws_bytes < need) return AVERIS_E_WORKSPACE;
+  if (!aligned(ws, 256)) return AVERIS_E_ALIGN;
+  const SplitWs w = split_ws_carve(ws, rows, cols, 1);
+  const QuantOut ro{residual->codes, residual->scales, residual->tscale};
+  const QuantOut mo{mean->codes, mean->scales, mean->tscale};
+  return hip_status(launch_split_from_stats(a, true, rows, cols, lda, nullptr, 1, kGemmRows,
+                                            rnd == AVERIS_SR, seed, ro, mo, mean_f32, w, stream,
+                                            b ? &r1 : nullptr));
+}
+
 averis_status_t averis_split_quant_noalloc(const void* a, averis_dtype_t dtype, int64_t rows,
                                            int64_t cols, int64_t lda, uint64_t seed,
                                            averis_round_t rnd, const averis_nvfp4_t* residual,

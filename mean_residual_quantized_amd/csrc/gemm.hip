@@ -279,6 +279,17 @@ hipError_t launch_gemm_rho(const QOperand& a, const float* rho, const QOperand& 
   return hipGetLastError();
 }
 
+// the same with the column statistics of the (bf16) output written for the
+// split that will read it; only the warp-specialized kernel (K % 64 == 0)
+hipError_t launch_gemm_rho_stats(const QOperand& a, const float* rho, const QOperand& b, int64_t m,
+                                 int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
+                                 int64_t ldc, const ColStats& cs, hipStream_t st) {
+  if (m == 0 || n == 0) return hipGetLastError();
+  const int v = ws_pick(m, n, k, offs ? nseg : 1, false);
+  if (v != 1 && v != 2) return hipErrorInvalidValue;
+  return launch_gemm_ws_rho(v, a, rho, b, m, n, k, offs, nseg, c, true, ldc, st, cs);
+}
+
 // ---------------------------------------------------------------------------
 // wgrad: dW = deq(Q4(X_R^T)) deq(Q4(D_R^T))^T + l mu_X mu_D^T.  Its output
 // (m x n) is short and wide next to its contraction over the tokens, so the

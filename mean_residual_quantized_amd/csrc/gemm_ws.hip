@@ -64,7 +64,8 @@ template <int TM, int TN, int PF, bool OUT_BF16, bool HAS_MEAN, bool SG, bool RG
 __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOperand M, int64_t m,
                                                     int64_t n, int64_t k, const int64_t* offs,
                                                     int nseg, void* c, int64_t ldc, int64_t kld,
-                                                    int64_t c_split, const float* rho_g) {
+                                                    int64_t c_split, const float* rho_g,
+                                                    ColStats cs) {
   constexpr int BM = 64 * TM, BN = 64 * TN;
   // 32-element chunks dequantized per stage: A rows and B rows
   constexpr int NCH = 2 * (BM + BN);
@@ -137,6 +138,66 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
     }
   };
   static_assert((BM * (2 * BN / 16)) % 512 == 0, "whole store rounds");
+  // column statistics of the staged bf16 tile, as stored (cs.psum set): per
+  // column of the tile the fp64 sum, max, min and smallest nonzero magnitude
+  // of its rows_here values -> the chunk's partials [tile_y][col] of the split
+  // that will read this output.  Thread (p, g) takes column pair p and rows
+  // g, g + G, ...; the G row groups meet in the stage room past the tile.
+  auto col_stats = [&]() __attribute__((always_inline)) {
+    constexpr int P = BN / 2, G = 512 / P;
+    static_assert((size_t)BM * kStLd + (size_t)G * BN * 16 + (size_t)G * P * 4 <= kStageRoom,
+                  "room for the row groups' partials");
+    double* gs = reinterpret_cast<double*>(stg + BM * kStLd);   // [G][BN]
+    float* gmx = reinterpret_cast<float*>(gs + G * BN);         // [G][BN]
+    float* gmn = gmx + G * BN;                                  // [G][BN]
+    uint32_t* gmz = reinterpret_cast<uint32_t*>(gmn + G * BN);  // [G][P] packed 16-bit minima
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    const int p = t % P, g = t / P;
+    if (g < G) {
+      double s0 = 0.0, s1 = 0.0;
+      float x0 = -__builtin_inff(), x1 = -__builtin_inff();
+      float n0v = __builtin_inff(), n1v = __builtin_inff();
+      // smallest nonzero |bf16| as (|bits| - 1) per half: a zero wraps to
+      // 0xFFFF and never wins the minimum
+      u16x2 mz = {0xFFFFu, 0xFFFFu};
+      for (int r = g; r < rows_here; r += G) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(stg + r * kStLd + 4 * p);
+        const float a0 = __uint_as_float(w << 16), a1 = __uint_as_float(w & 0xFFFF0000u);
+        s0 += (double)a0;
+        s1 += (double)a1;
+        x0 = __builtin_fmaxf(x0, a0);
+        x1 = __builtin_fmaxf(x1, a1);
+        n0v = __builtin_fminf(n0v, a0);
+        n1v = __builtin_fminf(n1v, a1);
+        mz = __builtin_elementwise_min(mz, __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu) - u16x2{1, 1});
+      }
+      gs[g * BN + 2 * p] = s0;
+      gs[g * BN + 2 * p + 1] = s1;
+      gmx[g * BN + 2 * p] = x0;
+      gmx[g * BN + 2 * p + 1] = x1;
+      gmn[g * BN + 2 * p] = n0v;
+      gmn[g * BN + 2 * p + 1] = n1v;
+      gmz[g * P + p] = __builtin_bit_cast(uint32_t, mz);
+    }
+    __syncthreads();
+    if (t < BN && n0 + t < n) {
+      double s = 0.0;
+      float x = -__builtin_inff(), y = __builtin_inff();
+      uint32_t z = 0xFFFFu;
+      for (int gg = 0; gg < G; ++gg) {
+        s += gs[gg * BN + t];
+        x = __builtin_fmaxf(x, gmx[gg * BN + t]);
+        y = __builtin_fminf(y, gmn[gg * BN + t]);
+        const uint32_t q = (gmz[gg * P + (t >> 1)] >> (16 * (t & 1))) & 0xFFFFu;
+        z = q < z ? q : z;
+      }
+      const int64_t o = tile_y * n + n0 + t;
+      cs.psum[o] = s;
+      cs.pmax[o] = x;
+      cs.pmin[o] = y;
+      cs.pmnz[o] = z == 0xFFFFu ? __builtin_inff() : __uint_as_float((z + 1u) << 16);
+    }
+  };
 
   if (producer) {
     // ------------------------------------------------------------------ producers
@@ -451,6 +512,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
     if constexpr (stage_out) {
       __syncthreads();   // the consumers have staged the tile
       store_staged();
+      if (cs.psum) col_stats();   // uniform
     }
     return;
   }
@@ -532,6 +594,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
     }
     __syncthreads();   // tile staged (the producers store too)
     store_staged();
+    if (cs.psum) col_stats();   // uniform
   } else {
   const bool full = (m0 + BM <= m_end) && (n0 + BN <= n);
   const bool vec = full && (ldc % 4 == 0) &&
@@ -592,7 +655,8 @@ template <int TM, int TN, bool OB, bool HM, bool SG, bool RG = false>
 hipError_t launch_ws(const QOperand& a, const QOperand* mean, const QOperand& b, int64_t m, int64_t n,
                      int64_t k, const int64_t* offs, int nseg, void* c, int64_t ldc,
                      hipStream_t st, int splits = 1, int64_t c_split = 0,
-                     const float* rho = nullptr) {
+                     const float* rho = nullptr,
+                     const ColStats& cs = ColStats{nullptr, nullptr, nullptr, nullptr}) {
   constexpr int PF = SG ? 4 : 2, BM = 64 * TM, BN = 64 * TN;
   const size_t lds = ws_lds_bytes(TM, TN) + (HM && !RG ? (size_t)k * 2 : 0);
   {
@@ -603,7 +667,7 @@ hipError_t launch_ws(const QOperand& a, const QOperand* mean, const QOperand& b,
   dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)tiles_m, (unsigned)splits);
   const QOperand mu = mean ? *mean : QOperand{nullptr, nullptr, nullptr};
   k_gemm_ws<TM, TN, PF, OB, HM, SG, RG><<<grid, 512, lds, st>>>(a, b, mu, m, n, k / splits, offs,
-                                                                nseg, c, ldc, k, c_split, rho);
+                                                                nseg, c, ldc, k, c_split, rho, cs);
   return hipGetLastError();
 }
 
@@ -667,30 +731,37 @@ hipError_t launch_gemm_ws_splitk(const QOperand& a, const QOperand& b, int64_t m
                                                      st, splits, m * n);
 }
 
-// rank-one row precomputed: 256 x 192 (variant 1) or 256 x 128 (variant 2) tiles
+// rank-one row precomputed: 256 x 192 (variant 1) or 256 x 128 (variant 2)
+// tiles; with cs set (bf16 output only) the epilogue also writes the column
+// statistics of the output
 template <int TM, int TN>
 hipError_t launch_ws_rho(const QOperand& a, const float* rho, const QOperand& b, int64_t m,
                          int64_t n, int64_t k, const int64_t* offs, int nseg, void* c, bool c_bf16,
-                         int64_t ldc, hipStream_t st) {
+                         int64_t ldc, hipStream_t st, const ColStats& cs) {
+  static_assert(64 * TM == kGemmRows, "the statistics' chunks are the row tiles");
+  if (cs.psum && !c_bf16) return hipErrorInvalidValue;
   if (k % 256 == 0) {
     if (c_bf16)
       return launch_ws<TM, TN, true, true, true, true>(a, nullptr, b, m, n, k, offs, nseg, c,
-                                                              ldc, st, 1, 0, rho);
+                                                       ldc, st, 1, 0, rho, cs);
     return launch_ws<TM, TN, false, true, true, true>(a, nullptr, b, m, n, k, offs, nseg, c,
-                                                             ldc, st, 1, 0, rho);
+                                                      ldc, st, 1, 0, rho);
   }
   if (c_bf16)
     return launch_ws<TM, TN, true, true, false, true>(a, nullptr, b, m, n, k, offs, nseg, c,
-                                                             ldc, st, 1, 0, rho);
+                                                      ldc, st, 1, 0, rho, cs);
   return launch_ws<TM, TN, false, true, false, true>(a, nullptr, b, m, n, k, offs, nseg, c,
-                                                            ldc, st, 1, 0, rho);
+                                                     ldc, st, 1, 0, rho);
 }
 
 hipError_t launch_gemm_ws_rho(int variant, const QOperand& a, const float* rho, const QOperand& b,
                               int64_t m, int64_t n, int64_t k, const int64_t* offs, int nseg,
-                              void* c, bool c_bf16, int64_t ldc, hipStream_t st) {
-  if (variant == 1) return launch_ws_rho<4, 3>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
-  if (variant == 2) return launch_ws_rho<4, 2>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+                              void* c, bool c_bf16, int64_t ldc, hipStream_t st,
+                              const ColStats& cs) {
+  if (variant == 1)
+    return launch_ws_rho<4, 3>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st, cs);
+  if (variant == 2)
+    return launch_ws_rho<4, 2>(a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st, cs);
   return hipErrorInvalidValue;
 }
 

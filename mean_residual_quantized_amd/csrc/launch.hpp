@@ -42,6 +42,19 @@ struct QOperand {
   const float* tscale;
 };
 
+// Column statistics of a GEMM's bf16 output, written by its epilogue for the
+// split that will read that output: per row tile of kGemmRows rows (a chunk
+// of that split) and column, the fp64 sum, max, min and smallest nonzero
+// magnitude of the stored values, in the split workspace's partial arrays
+// ([chunk][cols]).  psum == nullptr: none.
+constexpr int64_t kGemmRows = 256;
+struct ColStats {
+  double* psum;
+  float* pmax;
+  float* pmin;
+  float* pmnz;
+};
+
 // The rank-one row a split can compute for the GEMM that takes it:
 // rho[s][j] = deq(Q4(mu_s)) . deq(b_s,j) for the n rows of each segment's b
 // (b holds nseg stacked n x cols matrices).
@@ -96,6 +109,20 @@ hipError_t launch_gemm_rho(const QOperand& a, const float* rho, const QOperand& 
                            int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
                            bool c_bf16, int64_t ldc, hipStream_t st);
 
+// The same GEMM (bf16 output, K % 64 == 0) also writing the column statistics
+// of its output into cs (kGemmRows-row chunks).
+hipError_t launch_gemm_rho_stats(const QOperand& a, const float* rho, const QOperand& b, int64_t m,
+                                 int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
+                                 int64_t ldc, const ColStats& cs, hipStream_t st);
+
+// Split-quant from the column statistics a producer wrote (chunks of ch rows)
+// into ws's partial arrays: the finalize and quant passes only (one read of a).
+hipError_t launch_split_from_stats(const void* a, bool bf16, int64_t rows, int64_t cols,
+                                   int64_t lda, const int64_t* offs, int nseg, int64_t ch, bool sr,
+                                   uint64_t seed, const QuantOut& out, const QuantOut& mean,
+                                   float* mean_f32, const SplitWs& ws, hipStream_t st,
+                                   const Rank1Out* r1 = nullptr);
+
 // Workspace of a GEMM call (rho, the rank-one term per segment and column).
 size_t gemm_ws_bytes(int64_t n, int64_t k, int nseg);
 
@@ -109,7 +136,8 @@ hipError_t launch_gemm_ws(int variant, const QOperand& a, const QOperand* mean, 
                           bool c_bf16, int64_t ldc, hipStream_t st);
 hipError_t launch_gemm_ws_rho(int variant, const QOperand& a, const float* rho, const QOperand& b,
                               int64_t m, int64_t n, int64_t k, const int64_t* offs, int nseg,
-                              void* c, bool c_bf16, int64_t ldc, hipStream_t st);
+                              void* c, bool c_bf16, int64_t ldc, hipStream_t st,
+                              const ColStats& cs = ColStats{nullptr, nullptr, nullptr, nullptr});
 
 // Split-K product into fp32 partials part[z] (m x n each, row stride n).
 hipError_t launch_gemm_ws_splitk(const QOperand& a, const QOperand& b, int64_t m, int64_t n,

@@ -268,7 +268,7 @@ __device__ __forceinline__ bool sum_certified(double n, double amax, float mnz, 
 
 __device__ __noinline__ double exact_column_sum(const void* a, bool bf16, int64_t lda,
                                                 int64_t cols, int64_t seg_r0, int64_t seg_r1,
-                                                int64_t c0, int64_t c1, int64_t j,
+                                                int64_t c0, int64_t c1, int64_t ch, int64_t j,
                                                 const double* __restrict__ psum,
                                                 const float* __restrict__ pmax,
                                                 const float* __restrict__ pmin,
@@ -278,8 +278,8 @@ __device__ __noinline__ double exact_column_sum(const void* a, bool bf16, int64_
 #pragma unroll
   for (int i = 0; i < kWideWords; ++i) acc[i] = 0u;
   for (int64_t c = c0 + threadIdx.x; c < c1; c += 256) {
-    const int64_t r0 = seg_r0 + (c - c0) * kStatsRows;
-    const int64_t r1 = r0 + kStatsRows < seg_r1 ? r0 + kStatsRows : seg_r1;
+    const int64_t r0 = seg_r0 + (c - c0) * ch;
+    const int64_t r1 = r0 + ch < seg_r1 ? r0 + ch : seg_r1;
     const int64_t o = c * cols + j;
     const double am = __builtin_fmax(__builtin_fabs((double)pmax[o]), __builtin_fabs((double)pmin[o]));
     if (sum_certified((double)(r1 - r0), am, pmnz[o], bf16)) {
@@ -306,7 +306,9 @@ __device__ __noinline__ double exact_column_sum(const void* a, bool bf16, int64_
 
 // ---------------------------------------------------------------------------
 // finalize (split): block = kFinCols (16) columns x 16 chunk lanes, per
-// segment; each lane keeps all its partial loads in flight.  The fp64 partial
+// segment, over the partials of chunks of `ch` rows (the statistics pass's
+// kStatsRows, or the row tiles of a GEMM that wrote the statistics of its
+// output); each lane keeps all its partial loads in flight.  The fp64 partial
 // sums are exact, so the order of the reduction is free.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, int64_t lda,
@@ -321,10 +323,10 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
                                                   float* __restrict__ tmax_mu,
                                                   const double* __restrict__ psq,
                                                   double* __restrict__ tssq,
-                                                  double* __restrict__ tmu2) {
+                                                  double* __restrict__ tmu2, int64_t ch) {
   constexpr int NC = (int)kFinCols, NQ = 256 / NC;
   const int seg = blockIdx.y;
-  const SegRange sr = describe_segment(offs, nseg, rows, kStatsRows, seg);
+  const SegRange sr = describe_segment(offs, nseg, rows, ch, seg);
   const int jl = threadIdx.x % NC, q = threadIdx.x / NC;
   const int64_t j = (int64_t)blockIdx.x * NC + jl;
   double s = 0.0, s2 = 0.0;
@@ -400,7 +402,7 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
   for (uint32_t mrest = mask; mrest != 0; mrest &= mrest - 1) {
     const int cidx = __builtin_ctz(mrest);
     const double v = exact_column_sum(a, a_bf16, lda, cols, sr.seg_r0, sr.seg_r1, sr.c0, sr.c1,
-                                      (int64_t)blockIdx.x * NC + cidx, psum, pmax, pmin, pmnz,
+                                      ch, (int64_t)blockIdx.x * NC + cidx, psum, pmax, pmin, pmnz,
                                       wide_red);
     if (threadIdx.x == 0) exact_s[cidx] = v;
   }
@@ -1196,37 +1198,25 @@ __global__ __launch_bounds__(256) void k_quant_rt(const T* __restrict__ a, int64
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
+// finalize (split, over chunks of ch rows) and quant passes
 template <typename T>
-static hipError_t run_split_or_plain(const void* a_, int64_t rows, int64_t cols, int64_t lda,
+static hipError_t run_finalize_quant(const T* a, int64_t rows, int64_t cols, int64_t lda,
                                      const int64_t* offs, int nseg, bool split, bool sr,
                                      uint64_t seed, uint32_t stream_id, const QuantOut& out,
                                      const QuantOut* mean, float* mean_f32, const SplitWs& ws,
-                                     hipStream_t st, float* ratio, const Rank1Out* r1) {
-  const T* a = static_cast<const T*>(a_);
-  const int64_t nchs = chunk_upper_bound(rows, nseg, kStatsRows);
+                                     hipStream_t st, float* ratio, const Rank1Out* r1,
+                                     int64_t ch) {
   const int64_t nchq = chunk_upper_bound(rows, nseg, kQuantRows);
   const int64_t ct_s = (cols + 255) / 256;
   const int64_t ct_f = (cols + kFinCols - 1) / kFinCols;
   const int64_t ct_q = ((cols >> 4) + 63) / 64;
-  if (nchs > 0) {
-    dim3 g((unsigned)ct_s, (unsigned)nchs);
-    if (split && ratio)
-      k_stats<T, true, true><<<g, 256, 0, st>>>(a, rows, cols, lda, offs, nseg, ws.psum, ws.pmax,
-                                                ws.pmin, ws.pmnz, nullptr, ws.psq);
-    else if (split)
-      k_stats<T, true><<<g, 256, 0, st>>>(a, rows, cols, lda, offs, nseg, ws.psum, ws.pmax,
-                                          ws.pmin, ws.pmnz, nullptr);
-    else
-      k_stats<T, false><<<g, 256, 0, st>>>(a, rows, cols, lda, offs, nseg, nullptr, nullptr,
-                                           nullptr, nullptr, ws.pamax);
-  }
   int64_t ntmax;
   const float* tmax;
   if (split) {
     dim3 g((unsigned)ct_f, (unsigned)nseg);
     k_finalize<<<g, 256, 0, st>>>(a, sizeof(T) == 2, lda, rows, cols, offs, nseg, ws.psum,
                                   ws.pmax, ws.pmin, ws.pmnz, ws.mu, mean_f32, ws.tmax_r,
-                                  ws.tmax_mu, ratio ? ws.psq : nullptr, ws.tssq, ws.tmu2);
+                                  ws.tmax_mu, ratio ? ws.psq : nullptr, ws.tssq, ws.tmu2, ch);
     tmax = ws.tmax_r;
     ntmax = ct_f;
   } else {
@@ -1257,6 +1247,45 @@ static hipError_t run_split_or_plain(const void* a_, int64_t rows, int64_t cols,
   }
 #undef AVERIS_QUANT_LAUNCH
   return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t run_split_or_plain(const void* a_, int64_t rows, int64_t cols, int64_t lda,
+                                     const int64_t* offs, int nseg, bool split, bool sr,
+                                     uint64_t seed, uint32_t stream_id, const QuantOut& out,
+                                     const QuantOut* mean, float* mean_f32, const SplitWs& ws,
+                                     hipStream_t st, float* ratio, const Rank1Out* r1) {
+  const T* a = static_cast<const T*>(a_);
+  const int64_t nchs = chunk_upper_bound(rows, nseg, kStatsRows);
+  const int64_t ct_s = (cols + 255) / 256;
+  if (nchs > 0) {
+    dim3 g((unsigned)ct_s, (unsigned)nchs);
+    if (split && ratio)
+      k_stats<T, true, true><<<g, 256, 0, st>>>(a, rows, cols, lda, offs, nseg, ws.psum, ws.pmax,
+                                                ws.pmin, ws.pmnz, nullptr, ws.psq);
+    else if (split)
+      k_stats<T, true><<<g, 256, 0, st>>>(a, rows, cols, lda, offs, nseg, ws.psum, ws.pmax,
+                                          ws.pmin, ws.pmnz, nullptr);
+    else
+      k_stats<T, false><<<g, 256, 0, st>>>(a, rows, cols, lda, offs, nseg, nullptr, nullptr,
+                                           nullptr, nullptr, ws.pamax);
+  }
+  return run_finalize_quant<T>(a, rows, cols, lda, offs, nseg, split, sr, seed, stream_id, out,
+                               mean, mean_f32, ws, st, ratio, r1, kStatsRows);
+}
+
+hipError_t launch_split_from_stats(const void* a, bool bf16, int64_t rows, int64_t cols,
+                                   int64_t lda, const int64_t* offs, int nseg, int64_t ch, bool sr,
+                                   uint64_t seed, const QuantOut& out, const QuantOut& mean,
+                                   float* mean_f32, const SplitWs& ws, hipStream_t st,
+                                   const Rank1Out* r1) {
+  if (bf16)
+    return run_finalize_quant<uint16_t>(static_cast<const uint16_t*>(a), rows, cols, lda, offs,
+                                        nseg, true, sr, seed, 0u, out, &mean, mean_f32, ws, st,
+                                        nullptr, r1, ch);
+  return run_finalize_quant<float>(static_cast<const float*>(a), rows, cols, lda, offs, nseg,
+                                   true, sr, seed, 0u, out, &mean, mean_f32, ws, st, nullptr, r1,
+                                   ch);
 }
 
 hipError_t launch_split_or_plain(const void* a, bool bf16, int64_t rows, int64_t cols,

@@ -108,6 +108,35 @@ def test_noalloc_split_rejections(L):
     assert av.workspace_bytes(av.OP_SPLIT_QUANT, 16384, 3072) <= limit
 
 
+def test_fused_statistics_rejections(L):
+    a, b = nv(1000, 128), nv(208, 128)
+    g = lambda a=a, rho=P, b=b, c=P, ldc=208, ws=P, wsb=1 << 30: L.averis_gemm_rank1_stats(
+        ctypes.byref(a) if a is not None else None, rho, ctypes.byref(b), c, ldc, ws, wsb, None)
+    assert g(a=None) == 1
+    assert g(rho=None) == 1
+    assert g(a=nv(1000, 96), b=nv(208, 96)) == 2          # K % 64 (the fused epilogue's kernel)
+    assert g(b=nv(200, 128)) == 2                          # output cols % 16 (a split input)
+    assert g(ldc=100) == 2
+    assert g(c=None) == 1
+    assert g(c=P + 4) == 4                                 # a split input is 16-byte aligned
+    assert g(ldc=212) == 4                                 # ... with 16-byte rows
+    assert g(ws=None) == 5
+    assert g(wsb=64) == 5
+    res, mean = nv(1000, 208), nv(1, 208)
+    sq = lambda a=P, rows=1000, cols=208, lda=208, rnd=av.SR, res=res, b=None, rho=None, ws=P, \
+        wsb=1 << 30: L.averis_split_quant_from_stats(
+            a, rows, cols, lda, 0, rnd, ctypes.byref(res), ctypes.byref(mean), None,
+            ctypes.byref(b) if b is not None else None, rho, ws, wsb, None)
+    assert sq(cols=200, lda=200) == 2
+    assert sq(a=None) == 1
+    assert sq(rnd=4) == 6
+    assert sq(res=nv(999, 208)) == 2
+    assert sq(b=nv(96, 208)) == 1                          # b without rho
+    assert sq(rho=P) == 1                                  # rho without b
+    assert sq(b=nv(96, 200), rho=P) == 2
+    assert sq(ws=None) == 5
+
+
 def test_quant_and_gemm_rejections(L):
     out = nv(64, 128)
     q = lambda **k: L.averis_quant(k.get("a", P), k.get("dt", av.BF16), k.get("rows", 64),
