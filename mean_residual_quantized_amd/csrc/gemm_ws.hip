@@ -152,31 +152,59 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
     float* gmn = gmx + G * BN;                                  // [G][BN]
     uint32_t* gmz = reinterpret_cast<uint32_t*>(gmn + G * BN);  // [G][P] packed 16-bit minima
     typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    typedef short i16x2 __attribute__((ext_vector_type(2)));
+    // bf16 bits -> 16-bit integers in the order of the values (a negative
+    // value's magnitude bits flipped), so one packed integer max or min
+    // covers both columns of a pair; the map is its own inverse
+    auto ordered = [](uint32_t w) __attribute__((always_inline)) {
+      const i16x2 x = __builtin_bit_cast(i16x2, w);
+      return x ^ ((x >> 15) & i16x2{0x7FFF, 0x7FFF});
+    };
     const int p = t % P, g = t / P;
     if (g < G) {
       double s0 = 0.0, s1 = 0.0;
-      float x0 = -__builtin_inff(), x1 = -__builtin_inff();
-      float n0v = __builtin_inff(), n1v = __builtin_inff();
+      i16x2 mx = {-32768, -32768}, mn = {32767, 32767};
       // smallest nonzero |bf16| as (|bits| - 1) per half: a zero wraps to
       // 0xFFFF and never wins the minimum
       u16x2 mz = {0xFFFFu, 0xFFFFu};
-      for (int r = g; r < rows_here; r += G) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(stg + r * kStLd + 4 * p);
-        const float a0 = __uint_as_float(w << 16), a1 = __uint_as_float(w & 0xFFFF0000u);
-        s0 += (double)a0;
-        s1 += (double)a1;
-        x0 = __builtin_fmaxf(x0, a0);
-        x1 = __builtin_fmaxf(x1, a1);
-        n0v = __builtin_fminf(n0v, a0);
-        n1v = __builtin_fminf(n1v, a1);
+      auto add_row = [&](uint32_t w) __attribute__((always_inline)) {
+        const i16x2 o = ordered(w);
+        mx = __builtin_elementwise_max(mx, o);
+        mn = __builtin_elementwise_min(mn, o);
         mz = __builtin_elementwise_min(mz, __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu) - u16x2{1, 1});
+      };
+      // full rounds of U rows (their reads issued together, at constant
+      // offsets from one pointer), then the remaining rows one by one
+      constexpr int U = 4;
+      const unsigned char* q = stg + g * kStLd + 4 * p;
+      int r = g;
+      for (; r + (U - 1) * G < rows_here; r += U * G, q += U * G * kStLd) {
+        uint32_t w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) w[u] = *reinterpret_cast<const uint32_t*>(q + u * G * kStLd);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          s0 += (double)__uint_as_float(w[u] << 16);
+          s1 += (double)__uint_as_float(w[u] & 0xFFFF0000u);
+          add_row(w[u]);
+        }
       }
+      for (; r < rows_here; r += G, q += G * kStLd) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(q);
+        s0 += (double)__uint_as_float(w << 16);
+        s1 += (double)__uint_as_float(w & 0xFFFF0000u);
+        add_row(w);
+      }
+      const uint32_t bx = __builtin_bit_cast(uint32_t, ordered(__builtin_bit_cast(uint32_t, mx)));
+      const uint32_t bn = __builtin_bit_cast(uint32_t, ordered(__builtin_bit_cast(uint32_t, mn)));
+      // a thread without rows keeps -inf / +inf
+      const bool any = g < rows_here;
       gs[g * BN + 2 * p] = s0;
       gs[g * BN + 2 * p + 1] = s1;
-      gmx[g * BN + 2 * p] = x0;
-      gmx[g * BN + 2 * p + 1] = x1;
-      gmn[g * BN + 2 * p] = n0v;
-      gmn[g * BN + 2 * p + 1] = n1v;
+      gmx[g * BN + 2 * p] = any ? __uint_as_float(bx << 16) : -__builtin_inff();
+      gmx[g * BN + 2 * p + 1] = any ? __uint_as_float(bx & 0xFFFF0000u) : -__builtin_inff();
+      gmn[g * BN + 2 * p] = any ? __uint_as_float(bn << 16) : __builtin_inff();
+      gmn[g * BN + 2 * p + 1] = any ? __uint_as_float(bn & 0xFFFF0000u) : __builtin_inff();
       gmz[g * P + p] = __builtin_bit_cast(uint32_t, mz);
     }
     __syncthreads();
