@@ -603,15 +603,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm_ws(QOperand A, QOperand B, QOpe
   if constexpr (stage_out) {
     const int srow = wm * 32 * TM + (lane & 31);
     const int scol = wn * 32 * TN + (lane >> 5) * 4;
+    // a lane's four columns of a (j, q) group are the same in every row
+    // fragment i: their rank-one values are read once for all of them
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int j = 0; j < TN; ++j) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
+      for (int q = 0; q < 4; ++q) {
+        const int cl = scol + j * 32 + 8 * q;
+        f32x4_t r1 = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (HAS_MEAN) r1 = *reinterpret_cast<const f32x4_t*>(rho_sh + cl);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int cl = scol + j * 32 + 8 * q;
-          f32x4_t r1 = {0.0f, 0.0f, 0.0f, 0.0f};
-          if (HAS_MEAN) r1 = *reinterpret_cast<const f32x4_t*>(rho_sh + cl);
+        for (int i = 0; i < TM; ++i) {
           float y[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) y[e] = __builtin_fmaf(acc[i][j][4 * q + e], alpha, r1[e]);
