@@ -640,7 +640,7 @@ def traffic_probe(args):
           file=sys.stderr)
 
 
-GEMM_SOURCES = ["gemm.hip", "gemm_ws.hip", "gemm_common.hpp"]
+GEMM_SOURCES = ["gemm.hip", "gemm_ws.hip", "gemm_win.hip", "gemm_common.hpp"]
 
 
 def gemm_source_sha():
@@ -653,7 +653,7 @@ def gemm_source_sha():
 
 
 def load_traffic(cfg):
-    """HBM bytes per Averis GEMM launch (k_gemm_ws) from the committed counter
+    """HBM bytes per Averis GEMM launch (k_gemm_win) from the committed counter
     summary, if it was taken on the current kernel sources for this workload
     (else None)."""
     path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
@@ -685,8 +685,9 @@ def main():
     linears = make_linears(cfg)
     head, ta, flops_step = measure(cfg, linears, args.steps, args.warmup)
 
-    # roofline of the dominant kernel: k_gemm_ws, the Averis GEMM (the
-    # warp-specialized NVFP4 NT GEMM adding the split's rank-one row), over
+    # roofline of the dominant kernel: k_gemm_win, the Averis GEMM (the
+    # NVFP4 NT GEMM with the codes staged in LDS, adding the split's rank-one
+    # row), over
     # all of its launches in a step: mean flops per launch / mean launch time
     # (events around each call on the launch stream)
     g_calls = [(L, k) for L in linears for k in ("gemm_fwd", "gemm_dgrad")]
@@ -697,8 +698,9 @@ def main():
     traffic = None if tr is None else tr["averis_gemm"]["bytes_per_launch"]
     roofline = dict(bound="mfma", achieved=achieved, peak=F16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=achieved / F16_MFMA_PEAK_TFLOPS, traffic=traffic,
-                    kernel="k_gemm_ws (averis_gemm_rank1: warp-specialized NVFP4 NT GEMM, exact "
-                           "fp16 dequant -> v_mfma_f32_32x32x16_f16, the rank-one row from the "
+                    kernel="k_gemm_win (averis_gemm_rank1: NVFP4 NT GEMM, 4-bit codes staged in LDS, "
+                           "exact fp16 dequant by the MFMA waves -> v_mfma_f32_32x32x16_f16, the "
+                           "rank-one row from the "
                            "split added in the epilogue, bf16 out), all %d launches of one step "
                            "(forward and dgrad of every linear)" % nlaunch,
                     launches_per_step=nlaunch, mean_flops_per_launch=flops_step / nlaunch,

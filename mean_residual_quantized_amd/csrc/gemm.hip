@@ -234,13 +234,23 @@ hipError_t launch_gemm(const QOperand& a, const QOperand* mean, const QOperand& 
                        int64_t ldc, void* ws, hipStream_t st) {
   float* rho_ws = static_cast<float*>(ws);
   if (m == 0 || n == 0) return hipGetLastError();
+  const int ns = offs ? nseg : 1;
+  // codes-in-LDS kernel wherever it applies (K % 256 == 0); with a mean, the
+  // rank-one row from its own GEMV first
+  const int fn = win_pick(m, n, k, ns, 1);
+  if (fn != 0) {
+    if (mean) {
+      dim3 g((unsigned)((n + kRank1Cols - 1) / kRank1Cols), (unsigned)ns);
+      k_rank1<<<g, 256, 0, st>>>(*mean, b, n, k, offs != nullptr, rho_ws);
+    }
+    return launch_gemm_win(fn, a, mean ? rho_ws : nullptr, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
+  }
   // warp-specialized kernel wherever it applies (K % 64 == 0, a mean row that
   // fits its LDS)
-  const int v = ws_pick(m, n, k, offs ? nseg : 1, mean != nullptr);
+  const int v = ws_pick(m, n, k, ns, mean != nullptr);
   if (v != 0) return launch_gemm_ws(v, a, mean, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
   // general path (K % 64 != 0, or a mean vector too long for LDS): the
   // rank-one row from its own GEMV, then the simple tiled kernel
-  const int ns = offs ? nseg : 1;
   if (mean) {
     dim3 g((unsigned)((n + kRank1Cols - 1) / kRank1Cols), (unsigned)ns);
     k_rank1<<<g, 256, 0, st>>>(*mean, b, n, k, offs != nullptr, rho_ws);
@@ -267,6 +277,8 @@ hipError_t launch_gemm_rho(const QOperand& a, const float* rho, const QOperand& 
                            int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
                            bool c_bf16, int64_t ldc, hipStream_t st) {
   if (m == 0 || n == 0) return hipGetLastError();
+  const int fn = win_pick(m, n, k, offs ? nseg : 1, 1);
+  if (fn != 0) return launch_gemm_win(fn, a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
   const int v = ws_pick(m, n, k, offs ? nseg : 1, false);
   if (v == 1 || v == 2)
     return launch_gemm_ws_rho(v, a, rho, b, m, n, k, offs, nseg, c, c_bf16, ldc, st);
@@ -285,6 +297,9 @@ hipError_t launch_gemm_rho_stats(const QOperand& a, const float* rho, const QOpe
                                  int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
                                  int64_t ldc, const ColStats& cs, hipStream_t st) {
   if (m == 0 || n == 0) return hipGetLastError();
+  const int fn = win_pick(m, n, k, offs ? nseg : 1, 1);
+  if (fn != 0)
+    return launch_gemm_win(fn, a, rho, b, m, n, k, offs, nseg, c, true, ldc, st, 1, 0, cs);
   const int v = ws_pick(m, n, k, offs ? nseg : 1, false);
   if (v != 1 && v != 2) return hipErrorInvalidValue;
   return launch_gemm_ws_rho(v, a, rho, b, m, n, k, offs, nseg, c, true, ldc, st, cs);
@@ -373,7 +388,10 @@ hipError_t launch_wgrad(const QOperand& xt, const QOperand& dt, const float* mu_
     // the (zero-weighted) mean term
     e = hipSuccess;
   } else if (splits > 1) {
-    e = launch_gemm_ws_splitk(xt, dt, m, n, l, splits, part, st);
+    const int fn = win_pick(m, n, l / splits, 1, splits);
+    e = fn != 0 ? launch_gemm_win(fn, xt, nullptr, dt, m, n, l, nullptr, 1, part, false, n, st,
+                                  splits, m * n)
+                : launch_gemm_ws_splitk(xt, dt, m, n, l, splits, part, st);
   } else {
     e = launch_gemm(xt, nullptr, dt, m, n, l, nullptr, 1, part, false, n, nullptr, st);
   }

@@ -139,6 +139,18 @@ hipError_t launch_gemm_ws_rho(int variant, const QOperand& a, const float* rho, 
                               void* c, bool c_bf16, int64_t ldc, hipStream_t st,
                               const ColStats& cs = ColStats{nullptr, nullptr, nullptr, nullptr});
 
+// GEMM with the operands staged in LDS as codes (K per split % 256 == 0):
+// tile width 64 fn for a shape (0 = not applicable) and its launch.  rho:
+// the rank-one row (n floats per segment) or nullptr; splits > 1: split-K
+// into c + z c_split (fp32); cs.psum set: bf16 output with its column
+// statistics (kGemmRows-row chunks).
+int win_pick(int64_t m, int64_t n, int64_t k_split, int nseg_eff, int splits);
+hipError_t launch_gemm_win(int fn, const QOperand& a, const float* rho, const QOperand& b,
+                           int64_t m, int64_t n, int64_t k, const int64_t* offs, int nseg,
+                           void* c, bool c_bf16, int64_t ldc, hipStream_t st, int splits = 1,
+                           int64_t c_split = 0,
+                           const ColStats& cs = ColStats{nullptr, nullptr, nullptr, nullptr});
+
 // Split-K product into fp32 partials part[z] (m x n each, row stride n).
 hipError_t launch_gemm_ws_splitk(const QOperand& a, const QOperand& b, int64_t m, int64_t n,
                                  int64_t k, int splits, float* part, hipStream_t st);
