@@ -76,9 +76,40 @@ __device__ __forceinline__ void tensor_scales(float amax, float& s_enc, float& s
   s_dec = 1.0f / e;
 }
 
+// amax / 6 rounded to nearest even, as the IEEE division gives it: from the
+// rounded reciprocal and one FMA correction, which reproduces the quotient
+// for every finite amax >= 2^-125 (checked against the division for every
+// fp32 value); smaller inputs (subnormal quotients) take the division.
+__device__ __forceinline__ float div6(float amax) {
+  if (__builtin_expect(amax < 0x1p-125f, 0)) return amax / 6.0f;
+  const float c = 1.0f / 6.0f;
+  const float q = amax * c;
+  return __builtin_fmaf(__builtin_fmaf(-q, 6.0f, amax), c, q);
+}
+
+// E4M3 scale byte of a block (no element factor): the first steps of
+// block_scale
+__device__ __forceinline__ uint32_t block_scale_code(float amax_b, float s_enc) {
+  float s = div6(amax_b);
+  s = s * s_enc;
+  s = __builtin_fminf(s, 448.0f);
+  return e4m3_encode(s);
+}
+
+// Element factors of a tensor scale: tab[code] = s_enc / e4m3_decode(code)
+// (0 for code 0), the division block_scale does, for every code a block can
+// get (0 .. 0x7E); filled by the first 127 threads of a workgroup.
+__device__ __forceinline__ void fill_eb_table(float s_enc, float* tab) {
+  const uint32_t t = threadIdx.x;
+  if (t < 127) {
+    const float d = e4m3_decode(t);
+    tab[t] = d > 0.0f ? s_enc / d : 0.0f;
+  }
+}
+
 // Block scale byte and element factor from the block's max magnitude.
 __device__ __forceinline__ void block_scale(float amax_b, float s_enc, uint32_t& code, float& e_b) {
-  float s = amax_b / 6.0f;
+  float s = div6(amax_b);
   s = s * s_enc;
   s = __builtin_fminf(s, 448.0f);
   code = e4m3_encode(s);

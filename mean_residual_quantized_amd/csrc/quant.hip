@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "exact_sum.hpp"
 #include "gemm_common.hpp"
@@ -95,9 +97,21 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 }
 
 // ---------------------------------------------------------------------------
-// stats: block = 32 column-octets (256 columns) x 8 row lanes over one chunk
-// of kStatsRows rows; each thread keeps 8 row loads in flight.
+// stats over one chunk of kStatsRows rows.  Split: a block covers 128 columns
+// (16 column-octets x 16 row lanes, 8 rows per thread); plain: 256 columns
+// (32 x 8, 16 rows per thread).  Every row load of a thread is issued before
+// its arithmetic.  A chunk that ends before kStatsRows rows (the last one of
+// a segment) clamps its loads to the segment's last row and masks them; a
+// full chunk takes the same code without the masks.
 // ---------------------------------------------------------------------------
+template <bool SPLIT>
+struct StatsShape {
+  static constexpr int TX = SPLIT ? 16 : 32;         // threads across the columns
+  static constexpr int TY = 256 / TX;                // row lanes
+  static constexpr int CW = TX * 8;                  // columns per block
+  static constexpr int U = (int)(kStatsRows / TY);   // rows per thread
+};
+
 // SSQ (with SPLIT): also the column sums of squares, for the mean-energy
 // ratio (each square is exact in fp64, one fma per element)
 template <typename T, bool SPLIT, bool SSQ = false>
@@ -109,9 +123,11 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
                                                float* __restrict__ pmnz,
                                                float* __restrict__ pamax,
                                                double* __restrict__ psq = nullptr) {
+  using SH = StatsShape<SPLIT>;
+  constexpr int TX = SH::TX, TY = SH::TY, CW = SH::CW, U = SH::U;
   const SegRange sr = locate_chunk(offs, nseg, rows, kStatsRows, blockIdx.y);
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  const int64_t c = (int64_t)blockIdx.x * 256 + tx * 8;
+  const int tx = threadIdx.x % TX, ty = threadIdx.x / TX;
+  const int64_t c = (int64_t)blockIdx.x * CW + tx * 8;
   const bool active = sr.seg >= 0 && c < cols;
 
   double s[8], sq[8];
@@ -131,26 +147,31 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
     mn[k] = __builtin_inff();
     mz[k] = __builtin_inff();
   }
-  if (active) {
-    // all rows of the chunk in flight at once; rows past the segment end are
-    // clamped to its last row (loads stay legal, no branch) and masked below
-    constexpr int U = (int)(kStatsRows / 8);
+  // the chunk's rows of this thread: loads first, then the arithmetic; MASK:
+  // rows past the segment end (clamped to its last row, so the loads stay
+  // legal) are left out of the sums -- a repeated real value is harmless for
+  // the max, min and smallest magnitude
+  auto accumulate = [&](auto maskc) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(maskc)::value;
     const int64_t rlast = sr.r1 - 1;
     Raw8<T> v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t r = sr.r0 + ty + 8 * u;
-      v[u].load(a + (r < rlast ? r : rlast) * lda + c);
+      const int64_t r = sr.r0 + ty + TY * u;
+      v[u].load(a + (MASK && r > rlast ? rlast : r) * lda + c);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool ok = sr.r0 + ty + 8 * u <= rlast;
+      const bool ok = !MASK || sr.r0 + ty + TY * u <= rlast;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const float x = v[u].get(k);
         if (SPLIT) {
-          // a clamped row repeats a real value: harmless for max and min
-          s[k] += ok ? (double)x : 0.0;
+          if (MASK) {
+            s[k] += ok ? (double)x : 0.0;
+          } else {
+            s[k] += (double)x;
+          }
           if constexpr (SSQ) {
             const double xd = ok ? (double)x : 0.0;
             sq[k] = __builtin_fma(xd, xd, sq[k]);
@@ -167,7 +188,6 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
         }
       }
       if constexpr (SPLIT && sizeof(T) == 2) {
-        // a clamped row repeats a real one: harmless for the minimum
         const uint32_t wd[4] = {v[u].w.x, v[u].w.y, v[u].w.z, v[u].w.w};
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -176,6 +196,12 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
         }
       }
     }
+  };
+  if (active) {
+    if (sr.r1 - sr.r0 == kStatsRows)
+      accumulate(std::integral_constant<bool, false>{});
+    else
+      accumulate(std::integral_constant<bool, true>{});
   }
   if constexpr (SPLIT && sizeof(T) == 2) {
 #pragma unroll
@@ -187,11 +213,11 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
       }
     }
   }
-  if (SPLIT) {
-    // 32 KB of LDS (four blocks per CU): the smallest nonzero magnitudes go
-    // through the max buffer in a second round
-    __shared__ double ls[8][256];
-    __shared__ float lmx[8][256], lmn[8][256];
+  if constexpr (SPLIT) {
+    // 32 KB of LDS: the smallest nonzero magnitudes go through the max buffer
+    // in a second round
+    __shared__ double ls[TY][CW];
+    __shared__ float lmx[TY][CW], lmn[TY][CW];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       ls[ty][tx * 8 + k] = s[k];
@@ -199,22 +225,26 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
       lmn[ty][tx * 8 + k] = mn[k];
     }
     __syncthreads();
-    const int j = threadIdx.x;
-    const int64_t col = (int64_t)blockIdx.x * 256 + j;
+    // the row lanes of column j: two threads per column, halves then combined
+    const int j = threadIdx.x % CW, hf = threadIdx.x / CW;
+    static_assert(2 * CW == 256, "two threads per column");
+    const int64_t col = (int64_t)blockIdx.x * CW + j;
     const bool live = sr.seg >= 0 && col < cols;
     const int64_t o = (int64_t)blockIdx.y * cols + col;
-    if (live) {
-      double t = 0.0;
-      float m1 = -__builtin_inff(), m0 = __builtin_inff();
+    double t = 0.0;
+    float m1 = -__builtin_inff(), m0 = __builtin_inff();
+    if (hf == 0) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < TY; ++q) {
         t += ls[q][j];
         m1 = __builtin_fmaxf(m1, lmx[q][j]);
         m0 = __builtin_fminf(m0, lmn[q][j]);
       }
-      psum[o] = t;
-      pmax[o] = m1;
-      pmin[o] = m0;
+      if (live) {
+        psum[o] = t;
+        pmax[o] = m1;
+        pmin[o] = m0;
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -223,15 +253,17 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
       if constexpr (SSQ) ls[ty][tx * 8 + k] = sq[k];
     }
     __syncthreads();
-    if (live) {
+    if (live && hf == 1) {
       float mzz = __builtin_inff();
 #pragma unroll
-      for (int q = 0; q < 8; ++q) mzz = __builtin_fminf(mzz, lmx[q][j]);
+      for (int q = 0; q < TY; ++q) mzz = __builtin_fminf(mzz, lmx[q][j]);
       pmnz[o] = mzz;
-      if constexpr (SSQ) {
+    }
+    if constexpr (SSQ) {
+      if (live && hf == 0) {
         double t2 = 0.0;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) t2 += ls[q][j];
+        for (int q = 0; q < TY; ++q) t2 += ls[q][j];
         psq[o] = t2;
       }
     }
@@ -537,6 +569,22 @@ __device__ __forceinline__ void quant_block16_regs(const float* r, float s_enc, 
   encode_block16<SR>(r, e_b, idx0, k0, k1, stream, packed);
 }
 
+// the same with the element factor from the workgroup's table of s_enc /
+// decode(code) (fill_eb_table): the same bits without a division per block
+template <bool SR>
+__device__ __forceinline__ void quant_block16_tab(const float* r, float s_enc, const float* eb_tab,
+                                                  uint64_t idx0, uint32_t k0, uint32_t k1,
+                                                  uint32_t stream, uint8_t* codes, uint8_t* scale) {
+  float amax_b = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) amax_b = __builtin_fmaxf(amax_b, __builtin_fabsf(r[k]));
+  const uint32_t sc = block_scale_code(amax_b, s_enc);
+  uint2 packed;
+  encode_block16<SR>(r, eb_tab[sc], idx0, k0, k1, stream, packed);
+  *reinterpret_cast<uint2*>(codes) = packed;
+  *scale = (uint8_t)sc;
+}
+
 template <bool SR>
 __device__ __forceinline__ void quant_block16(const float* r, float s_enc, uint64_t idx0,
                                               uint32_t k0, uint32_t k1, uint32_t stream,
@@ -754,6 +802,9 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ a, int64_t 
   }
   float s_enc, s_dec;
   tensor_scales(am, s_enc, s_dec);
+  __shared__ float eb_tab[128];
+  fill_eb_table(s_enc, eb_tab);
+  __syncthreads();
   if (b >= nb) return;
   float m[16];
 #pragma unroll
@@ -784,8 +835,8 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ a, int64_t 
       for (int k = 0; k < 16; ++k) v[u][k] = v[u][k] - m[k];
     }
     const uint64_t idx0 = (uint64_t)row * (uint64_t)cols + (uint64_t)b * 16;
-    quant_block16<SR>(v[u], s_enc, idx0, k0, k1, stream, codes + row * (cols >> 1) + b * 8,
-                      scales + row * nb + b);
+    quant_block16_tab<SR>(v[u], s_enc, eb_tab, idx0, k0, k1, stream,
+                          codes + row * (cols >> 1) + b * 8, scales + row * nb + b);
   }
 }
 
@@ -1257,7 +1308,9 @@ static hipError_t run_split_or_plain(const void* a_, int64_t rows, int64_t cols,
                                      hipStream_t st, float* ratio, const Rank1Out* r1) {
   const T* a = static_cast<const T*>(a_);
   const int64_t nchs = chunk_upper_bound(rows, nseg, kStatsRows);
-  const int64_t ct_s = (cols + 255) / 256;
+  // column blocks of the stats kernel (the plain one's also index its maxima)
+  const int64_t cw = split ? StatsShape<true>::CW : StatsShape<false>::CW;
+  const int64_t ct_s = (cols + cw - 1) / cw;
   if (nchs > 0) {
     dim3 g((unsigned)ct_s, (unsigned)nchs);
     if (split && ratio)
