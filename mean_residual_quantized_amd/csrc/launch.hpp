@@ -8,6 +8,9 @@ namespace averis {
 
 // rows per chunk of the stats and quant passes
 constexpr int64_t kStatsRows = 128;
+// columns per block of the plain statistics pass (its per-chunk maxima are
+// kept per block of columns)
+constexpr int64_t kPlainStatsCols = 128;
 constexpr int64_t kQuantRows = 16;
 // cap on the blocks of the weight amax pass
 constexpr int64_t kAmaxBlocks = 1024;

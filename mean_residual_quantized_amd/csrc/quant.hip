@@ -97,19 +97,20 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 }
 
 // ---------------------------------------------------------------------------
-// stats over one chunk of kStatsRows rows.  Split: a block covers 128 columns
-// (16 column-octets x 16 row lanes, 8 rows per thread); plain: 256 columns
-// (32 x 8, 16 rows per thread).  Every row load of a thread is issued before
+// stats over one chunk of kStatsRows rows: a block covers 128 columns (16
+// column-octets x 16 row lanes, 8 rows per thread; the plain pass's maxima are
+// kept per kPlainStatsCols-column block).  Every row load of a thread is issued before
 // its arithmetic.  A chunk that ends before kStatsRows rows (the last one of
 // a segment) clamps its loads to the segment's last row and masks them; a
 // full chunk takes the same code without the masks.
 // ---------------------------------------------------------------------------
 template <bool SPLIT>
 struct StatsShape {
-  static constexpr int TX = SPLIT ? 16 : 32;         // threads across the columns
+  static constexpr int TX = 16;                      // threads across the columns
   static constexpr int TY = 256 / TX;                // row lanes
   static constexpr int CW = TX * 8;                  // columns per block
   static constexpr int U = (int)(kStatsRows / TY);   // rows per thread
+  static_assert(SPLIT || CW == kPlainStatsCols, "the plain pass's maxima blocks");
 };
 
 // SSQ (with SPLIT): also the column sums of squares, for the mean-energy
@@ -509,9 +510,11 @@ __device__ __forceinline__ void encode_block16(const float* r, float e_b, uint64
     // (frac: the fraction of the E2M1 step above the lower grid point).  With
     // the 16-bit draw u in the top bits of that window -- seed = u << 16 for
     // element 0, u << 15 for element 1 -- this is the exact SR rule: up iff
-    // floor(2^22 frac) + 64 u >= 2^22.  One instruction per element: the even
-    // element goes in as element 0 and the odd one as element 1 of separate
-    // conversions (their dither windows overlap), and the nibbles are OR-ed.
+    // floor(2^22 frac) + 64 u >= 2^22.  One instruction per element (the two
+    // elements' dither windows overlap): both conversions of a pair take the
+    // pair, the one seeded for element 0 keeps the even element's nibble
+    // (low), the one seeded for element 1 the odd element's (high); the other
+    // nibble of each is masked off.
     const uint64_t g = idx0 >> 3;   // idx0 is a multiple of 16
     uint32_t even[2] = {0u, 0u}, odd[2] = {0u, 0u};
 #pragma unroll
@@ -519,12 +522,11 @@ __device__ __forceinline__ void encode_block16(const float* r, float e_b, uint64
       const uint64_t gg = g + h;
       const u32x4 rr = philox10((uint32_t)gg, (uint32_t)(gg >> 32), stream, 0u, k0, k1);
       const uint32_t wd[4] = {rr.x, rr.y, rr.z, rr.w};
-#define AVERIS_SR_PAIR(P)                                               \
-  {                                                                     \
-    const f32x2v e0 = {r[8 * h + 2 * (P)] * e_b, 0.0f};                 \
-    const f32x2v e1 = {0.0f, r[8 * h + 2 * (P) + 1] * e_b};             \
-    sr_fp4_byte<P>(even[h], e0, wd[P] << 16);                           \
-    sr_fp4_byte<P>(odd[h], e1, (wd[P] & 0xFFFF0000u) >> 1);             \
+#define AVERIS_SR_PAIR(P)                                                        \
+  {                                                                              \
+    const f32x2v e = {r[8 * h + 2 * (P)] * e_b, r[8 * h + 2 * (P) + 1] * e_b};   \
+    sr_fp4_byte<P>(even[h], e, wd[P] << 16);                                     \
+    sr_fp4_byte<P>(odd[h], e, (wd[P] & 0xFFFF0000u) >> 1);                       \
   }
       AVERIS_SR_PAIR(0)
       AVERIS_SR_PAIR(1)
@@ -532,8 +534,8 @@ __device__ __forceinline__ void encode_block16(const float* r, float e_b, uint64
       AVERIS_SR_PAIR(3)
 #undef AVERIS_SR_PAIR
     }
-    packed.x = even[0] | odd[0];
-    packed.y = even[1] | odd[1];
+    packed.x = (even[0] & 0x0F0F0F0Fu) | (odd[0] & 0xF0F0F0F0u);
+    packed.y = (even[1] & 0x0F0F0F0Fu) | (odd[1] & 0xF0F0F0F0u);
   } else {
     // RN: gfx950's v_cvt_scalef32_pk_fp4_f32 with scale 1 rounds to the
     // nearest E2M1 value, ties to the even code, saturates at 6 and keeps the
@@ -1258,7 +1260,7 @@ static hipError_t run_finalize_quant(const T* a, int64_t rows, int64_t cols, int
                                      hipStream_t st, float* ratio, const Rank1Out* r1,
                                      int64_t ch) {
   const int64_t nchq = chunk_upper_bound(rows, nseg, kQuantRows);
-  const int64_t ct_s = (cols + 255) / 256;
+  const int64_t ct_s = (cols + kPlainStatsCols - 1) / kPlainStatsCols;
   const int64_t ct_f = (cols + kFinCols - 1) / kFinCols;
   const int64_t ct_q = ((cols >> 4) + 63) / 64;
   int64_t ntmax;
