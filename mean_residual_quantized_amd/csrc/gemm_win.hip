@@ -75,14 +75,17 @@ constexpr size_t win_ring_bytes(int fn) {
   return (size_t)(kWinBM + 64 * fn) * (2 * 128 + 2 * 16);
 }
 constexpr size_t win_stage_row(int fn) { return (size_t)2 * 64 * fn + 16; }
-// staged tile + rank-one row + the statistics' row-group partials
+// staged tile + the statistics' row-group partials
 constexpr size_t win_epi_bytes(int fn) {
-  return (size_t)kWinBM * win_stage_row(fn) + (size_t)64 * fn * 4 +
+  return (size_t)kWinBM * win_stage_row(fn) +
          (size_t)(kWinThreads / (32 * fn) > 0 ? kWinThreads / (32 * fn) : 1) * 64 * fn * 16 +
          (size_t)(kWinThreads / (32 * fn) > 0 ? kWinThreads / (32 * fn) : 1) * 32 * fn * 4;
 }
+// the rank-one row (64 fn floats) lives past the ring: it is loaded with the
+// first window and read in the epilogue
 constexpr size_t win_lds_bytes(int fn) {
-  return win_ring_bytes(fn) > win_epi_bytes(fn) ? win_ring_bytes(fn) : win_epi_bytes(fn);
+  return (win_ring_bytes(fn) > win_epi_bytes(fn) ? win_ring_bytes(fn) : win_epi_bytes(fn)) +
+         (size_t)64 * fn * 4;
 }
 
 }  // namespace
@@ -191,6 +194,20 @@ __global__ __launch_bounds__(kWinThreads, 1) void k_gemm_win(
                                        (lds_void*)(ring + slot * WSLOT + j * 1024), 16, 0, 0);
     }
   };
+
+  // the rank-one row goes to LDS by a direct-to-LDS load (4 bytes a lane,
+  // column n0 + t; columns past n repeat the last one, never stored), issued
+  // before the first window's loads, so the prologue's counted wait covers it
+  // and its latency hides under them
+  constexpr size_t kRhoOff = win_lds_bytes(FN) - (size_t)BN * 4;
+  float* rho_sh = reinterpret_cast<float*>(smem_win + kRhoOff);
+  if constexpr (RHO) {
+    if (64 * wave < BN) {   // uniform per wave
+      const int64_t cj = n0 + 64 * wave + lane;
+      __builtin_amdgcn_global_load_lds((const void*)(rho_g + boff + (cj < n ? cj : n - 1)),
+                                       (lds_void*)(smem_win + kRhoOff + 256 * wave), 4, 0, 0);
+    }
+  }
 
   u32x4_t cw[2][NF];     // a stage's codes per fragment, two stages
   u32x4_t sraw[NF];      // a window's scale bytes per fragment row (read once)
@@ -370,11 +387,6 @@ __global__ __launch_bounds__(kWinThreads, 1) void k_gemm_win(
   const float alpha = A.tscale[2 * seg + 1] * B.tscale[(offs ? 2 * seg : 0) + 1];
   constexpr int kStLd = (int)win_stage_row(FN);
   unsigned char* stg = smem_win;
-  float* rho_sh = reinterpret_cast<float*>(smem_win + (size_t)BM * kStLd);
-  if constexpr (RHO) {
-    if (t < BN) rho_sh[t] = n0 + t < n ? rho_g[boff + n0 + t] : 0.0f;
-    __syncthreads();
-  }
   const int srow = wm * 128 + lrow;
   const int scol = wn * 32 * FN + lh * 4;
   if constexpr (OUT_BF16) {
@@ -422,10 +434,10 @@ __global__ __launch_bounds__(kWinThreads, 1) void k_gemm_win(
       // sum, max, min and smallest nonzero magnitude of its rows_here values
       // -> the chunk's partials [tile_y][col].  Thread (pp, g) takes column
       // pair pp and rows g, g + G, ...; the G row groups meet in LDS past the
-      // rank-one row.
+      // staged tile.
       constexpr int P = BN / 2, G = kWinThreads / P;
       static_assert(G >= 1, "a row group per column pair");
-      double* gs = reinterpret_cast<double*>(smem_win + (size_t)BM * kStLd + BN * 4);   // [G][BN]
+      double* gs = reinterpret_cast<double*>(smem_win + (size_t)BM * kStLd);   // [G][BN]
       float* gmx = reinterpret_cast<float*>(gs + G * BN);          // [G][BN]
       float* gmn = gmx + G * BN;                                   // [G][BN]
       uint32_t* gmz = reinterpret_cast<uint32_t*>(gmn + G * BN);   // [G][P]
