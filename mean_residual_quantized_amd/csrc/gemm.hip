@@ -15,8 +15,14 @@
 // cannot apply E4M3 scales per 16; the exact operands therefore run on
 // v_mfma_f32_32x32x16_f16.
 //
-// rho_j = S_dec(mean) S_dec(B) sum_k deq'(mean)_k deq'(B)_jk comes from a
-// small GEMV kernel and is added in the GEMM epilogue as a broadcast row.
+// rho_j = S_dec(mean) S_dec(B) sum_k deq'(mean)_k deq'(B)_jk is added in the
+// GEMM epilogue as a broadcast row.  It comes from the split that made A
+// (the rank-one entry points), else from the small GEMV kernel k_rank1 below,
+// or, in the warp-specialized kernel, from its producer waves' dot products.
+//
+// Dispatch: the codes-in-LDS kernel (gemm_win.hip) wherever K % 256 == 0;
+// the warp-specialized kernel (gemm_ws.hip) for the remaining K % 64 == 0;
+// the simple tiled kernel k_gemm_nt below for any other K.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -292,7 +298,8 @@ hipError_t launch_gemm_rho(const QOperand& a, const float* rho, const QOperand& 
 }
 
 // the same with the column statistics of the (bf16) output written for the
-// split that will read it; only the warp-specialized kernel (K % 64 == 0)
+// split that will read it: the codes-in-LDS kernel where K % 256 == 0, else
+// the warp-specialized one (K % 64 == 0); other K are rejected
 hipError_t launch_gemm_rho_stats(const QOperand& a, const float* rho, const QOperand& b, int64_t m,
                                  int64_t n, int64_t k, const int64_t* offs, int nseg, void* c,
                                  int64_t ldc, const ColStats& cs, hipStream_t st) {

@@ -391,19 +391,25 @@ __global__ __launch_bounds__(kWinThreads, 1) void k_gemm_win(
   const int scol = wn * 32 * FN + lh * 4;
   if constexpr (OUT_BF16) {
     // a lane's four columns of a (j, q) group are the same in every row
-    // fragment i: their rank-one values are read once for all of them
+    // fragment i: their rank-one values are read once for all of them, the
+    // four groups of a fragment column j together (one wait for the four
+    // LDS reads, not one per group)
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
+      f32x4_t r1[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        r1[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (RHO) r1[q] = *reinterpret_cast<const f32x4_t*>(rho_sh + scol + j * 32 + 8 * q);
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int cl = scol + j * 32 + 8 * q;
-        f32x4_t r1 = {0.0f, 0.0f, 0.0f, 0.0f};
-        if constexpr (RHO) r1 = *reinterpret_cast<const f32x4_t*>(rho_sh + cl);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float y[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = __builtin_fmaf(acc[i][j][4 * q + e], alpha, r1[e]);
+          for (int e = 0; e < 4; ++e) y[e] = __builtin_fmaf(acc[i][j][4 * q + e], alpha, r1[q][e]);
           const u32x2_t pk = {bf16x2_rne(y[0], y[1]), bf16x2_rne(y[2], y[3])};
           *reinterpret_cast<u32x2_t*>(stg + (srow + 32 * i) * kStLd + 2 * cl) = pk;
         }

@@ -338,12 +338,16 @@ __device__ __noinline__ double exact_column_sum(const void* a, bool bf16, int64_
 }
 
 // ---------------------------------------------------------------------------
-// finalize (split): block = kFinCols (16) columns x 16 chunk lanes, per
-// segment, over the partials of chunks of `ch` rows (the statistics pass's
+// finalize (split): block = NC columns x 256 / NC chunk lanes, per segment,
+// over the partials of chunks of `ch` rows (the statistics pass's
 // kStatsRows, or the row tiles of a GEMM that wrote the statistics of its
-// output); each lane keeps all its partial loads in flight.  The fp64 partial
-// sums are exact, so the order of the reduction is free.
+// output); each lane keeps U partial loads of each kind in flight.  NC = 16
+// for long segments (128 chunks per round of loads), NC = 64 for many short
+// ones (grouped experts: a few chunks each, so wider column tiles and a
+// quarter of the workgroups).  The fp64 partial sums are exact, so the order
+// of the reduction is free.
 // ---------------------------------------------------------------------------
+template <int NC>
 __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, int64_t lda,
                                                   int64_t rows, int64_t cols, const int64_t* offs,
                                                   int nseg, const double* __restrict__ psum,
@@ -357,7 +361,9 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
                                                   const double* __restrict__ psq,
                                                   double* __restrict__ tssq,
                                                   double* __restrict__ tmu2, int64_t ch) {
-  constexpr int NC = (int)kFinCols, NQ = 256 / NC;
+  static_assert(NC >= (int)kFinCols && NC <= 64 && 256 % NC == 0, "column tile");
+  constexpr int NQ = 256 / NC;
+  using Mask = typename std::conditional<(NC > 32), uint64_t, uint32_t>::type;
   const int seg = blockIdx.y;
   const SegRange sr = describe_segment(offs, nseg, rows, ch, seg);
   const int jl = threadIdx.x % NC, q = threadIdx.x / NC;
@@ -365,7 +371,7 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
   double s = 0.0, s2 = 0.0;
   float m1 = -__builtin_inff(), m0 = __builtin_inff(), mz = __builtin_inff();
   if (j < cols && sr.c1 > sr.c0) {
-    constexpr int U = 8;   // up to 128 chunks in one round of loads
+    constexpr int U = NC > 16 ? 4 : 8;   // NQ * U chunks in one round of loads
     const int64_t clast = sr.c1 - 1;
     for (int64_t ck = sr.c0 + q; ck < sr.c1; ck += NQ * U) {
       double ps[U], pq[U];
@@ -392,7 +398,7 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
   }
   __shared__ double ls[NQ][NC], lq[NQ][NC];
   __shared__ float lx[NQ][NC], ln[NQ][NC], lz[NQ][NC];
-  __shared__ uint32_t need_mask;   // bit c: column c of the tile failed the certificate
+  __shared__ Mask need_mask;       // bit c: column c of the tile failed the certificate
   __shared__ double exact_s[NC];
   __shared__ uint32_t wide_red[128][kWideWords];
   ls[q][jl] = s;
@@ -428,12 +434,12 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
   // the q == 0 lanes are lanes 0 .. NC-1 of wave 0
   if (threadIdx.x < 64) {
     const uint64_t bal = __ballot(fail);
-    if (threadIdx.x == 0) need_mask = (uint32_t)bal;
+    if (threadIdx.x == 0) need_mask = (Mask)bal;
   }
   __syncthreads();
-  const uint32_t mask = need_mask;   // uniform
-  for (uint32_t mrest = mask; mrest != 0; mrest &= mrest - 1) {
-    const int cidx = __builtin_ctz(mrest);
+  const Mask mask = need_mask;   // uniform
+  for (Mask mrest = mask; mrest != 0; mrest &= mrest - 1) {
+    const int cidx = __builtin_ctzll((uint64_t)mrest);
     const double v = exact_column_sum(a, a_bf16, lda, cols, sr.seg_r0, sr.seg_r1, sr.c0, sr.c1,
                                       ch, (int64_t)blockIdx.x * NC + cidx, psum, pmax, pmin, pmnz,
                                       wide_red);
@@ -441,7 +447,7 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
   }
   if (mask) __syncthreads();
   if (q == 0 && j < cols) {
-    if ((mask >> jl) & 1u) t = exact_s[jl];
+    if ((mask >> jl) & 1u) t = exact_s[jl];   // jl < NC <= mask bits
     float m = 0.0f;
     if (l > 0) {
       const double md = t / (double)l;
@@ -646,7 +652,8 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ a, int64_t 
                                                const double* __restrict__ tmu2,
                                                float* __restrict__ ratio,
                                                QOperand B, int64_t bn,
-                                               float* __restrict__ rho, int64_t rho_rows) {
+                                               float* __restrict__ rho, int64_t rho_rows,
+                                               int r1_rows) {
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   const int64_t nb = cols >> 4;
@@ -656,13 +663,14 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ a, int64_t 
   if (SPLIT && rho) {
     // leading rows of the grid: the rank-one row of the GEMM that takes this
     // split, rho[s][j] = deq(Q4(mu_s)) . deq(B_s,j) for each segment s (B
-    // holds one bn x cols matrix per segment).  Each workgroup takes 16 rows
-    // of one segment's B: it quantizes that segment's mean as the mean block
-    // below does (same tensor scale, same draws), dequantizes it to fp16 in
-    // LDS (exact), and each group of 16 lanes sums one row of B against it.
+    // holds one bn x cols matrix per segment).  Each workgroup takes r1_rows
+    // (a multiple of 16) rows of one segment's B: it quantizes that segment's
+    // mean as the mean block below does (same tensor scale, same draws),
+    // dequantizes it to fp16 in LDS (exact), and each group of 16 lanes sums
+    // one row of B against it, 16 rows per pass.
     if (by < rho_rows) {
       extern __shared__ __attribute__((aligned(16))) _Float16 r1_mean[];   // [cols]
-      const int64_t groups = (bn + 15) / 16;
+      const int64_t groups = (bn + r1_rows - 1) / r1_rows;
       const int64_t rbi = by * gridDim.x + blockIdx.x;
       const int rseg = (int)(rbi / groups);
       if (rseg >= nseg) return;                          // uniform
@@ -684,51 +692,53 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ a, int64_t 
         *reinterpret_cast<uint4*>(r1_mean + mb * 16 + 8) = deq8(packed.y, s2);
       }
       __syncthreads();
-      const int64_t rb = rbi - (int64_t)rseg * groups;   // 16 rows of the segment's B
+      const int64_t rb = rbi - (int64_t)rseg * groups;   // r1_rows rows of the segment's B
       const int sub = threadIdx.x & 15;
-      const int64_t j = rb * 16 + (threadIdx.x >> 4);
-      const int64_t jj = j < bn ? j : bn - 1;            // every lane joins the butterfly
-      const int64_t brow = (int64_t)rseg * bn + jj;
-      const uint8_t* bc = B.codes + brow * (cols >> 1);
-      const uint8_t* bs = B.scales + brow * nb;
-      float acc = 0.0f;
-      // four blocks per pass, their loads issued before any arithmetic;
-      // blocks past the end are clamped to the last one and dropped
-      constexpr int U = 4;
-      for (int64_t b0 = sub; b0 < nb; b0 += 16 * U) {
-        uint2 w[U];
-        uint32_t sb[U];
+      const float r_dec = s_dec * B.tscale[(offs ? 2 * rseg : 0) + 1];
+      for (int64_t j = rb * r1_rows + (threadIdx.x >> 4); j < (rb + 1) * r1_rows; j += 16) {
+        if (j - (threadIdx.x >> 4) >= bn) break;          // uniform: the pass starts past B
+        const int64_t jj = j < bn ? j : bn - 1;            // every lane joins the butterfly
+        const int64_t brow = (int64_t)rseg * bn + jj;
+        const uint8_t* bc = B.codes + brow * (cols >> 1);
+        const uint8_t* bs = B.scales + brow * nb;
+        float acc = 0.0f;
+        // four blocks per pass, their loads issued before any arithmetic;
+        // blocks past the end are clamped to the last one and dropped
+        constexpr int U = 4;
+        for (int64_t b0 = sub; b0 < nb; b0 += 16 * U) {
+          uint2 w[U];
+          uint32_t sb[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int64_t blk = b0 + 16 * u < nb ? b0 + 16 * u : nb - 1;
-          w[u] = *reinterpret_cast<const uint2*>(bc + 8 * blk);
-          sb[u] = bs[blk];
-        }
+          for (int u = 0; u < U; ++u) {
+            const int64_t blk = b0 + 16 * u < nb ? b0 + 16 * u : nb - 1;
+            w[u] = *reinterpret_cast<const uint2*>(bc + 8 * blk);
+            sb[u] = bs[blk];
+          }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int64_t blk = b0 + 16 * u < nb ? b0 + 16 * u : nb - 1;
-          const half2_t sv = scales2(sb[u]);
-          const half2_t s2 = {sv.x, sv.x};
-          const uint4 d0 = deq8(w[u].x, s2), d1 = deq8(w[u].y, s2);
-          const uint4 m0 = *reinterpret_cast<const uint4*>(r1_mean + blk * 16);
-          const uint4 m1 = *reinterpret_cast<const uint4*>(r1_mean + blk * 16 + 8);
-          // products of exact fp16 values (<= 6 significant bits each) are
-          // exact; fp32 accumulation
-          float p = 0.0f;
-          p = __builtin_amdgcn_fdot2(h2(d0.x), h2(m0.x), p, false);
-          p = __builtin_amdgcn_fdot2(h2(d0.y), h2(m0.y), p, false);
-          p = __builtin_amdgcn_fdot2(h2(d0.z), h2(m0.z), p, false);
-          p = __builtin_amdgcn_fdot2(h2(d0.w), h2(m0.w), p, false);
-          p = __builtin_amdgcn_fdot2(h2(d1.x), h2(m1.x), p, false);
-          p = __builtin_amdgcn_fdot2(h2(d1.y), h2(m1.y), p, false);
-          p = __builtin_amdgcn_fdot2(h2(d1.z), h2(m1.z), p, false);
-          p = __builtin_amdgcn_fdot2(h2(d1.w), h2(m1.w), p, false);
-          acc += b0 + 16 * u < nb ? p : 0.0f;
+          for (int u = 0; u < U; ++u) {
+            const int64_t blk = b0 + 16 * u < nb ? b0 + 16 * u : nb - 1;
+            const half2_t sv = scales2(sb[u]);
+            const half2_t s2 = {sv.x, sv.x};
+            const uint4 d0 = deq8(w[u].x, s2), d1 = deq8(w[u].y, s2);
+            const uint4 m0 = *reinterpret_cast<const uint4*>(r1_mean + blk * 16);
+            const uint4 m1 = *reinterpret_cast<const uint4*>(r1_mean + blk * 16 + 8);
+            // products of exact fp16 values (<= 6 significant bits each) are
+            // exact; fp32 accumulation
+            float p = 0.0f;
+            p = __builtin_amdgcn_fdot2(h2(d0.x), h2(m0.x), p, false);
+            p = __builtin_amdgcn_fdot2(h2(d0.y), h2(m0.y), p, false);
+            p = __builtin_amdgcn_fdot2(h2(d0.z), h2(m0.z), p, false);
+            p = __builtin_amdgcn_fdot2(h2(d0.w), h2(m0.w), p, false);
+            p = __builtin_amdgcn_fdot2(h2(d1.x), h2(m1.x), p, false);
+            p = __builtin_amdgcn_fdot2(h2(d1.y), h2(m1.y), p, false);
+            p = __builtin_amdgcn_fdot2(h2(d1.z), h2(m1.z), p, false);
+            p = __builtin_amdgcn_fdot2(h2(d1.w), h2(m1.w), p, false);
+            acc += b0 + 16 * u < nb ? p : 0.0f;
+          }
         }
+        for (int d = 8; d > 0; d >>= 1) acc += __shfl_xor(acc, d, 16);
+        if (sub == 0 && j < bn) rho[(int64_t)rseg * bn + j] = acc * r_dec;
       }
-      for (int d = 8; d > 0; d >>= 1) acc += __shfl_xor(acc, d, 16);
-      if (sub == 0 && j < bn)
-        rho[(int64_t)rseg * bn + j] = acc * (s_dec * B.tscale[(offs ? 2 * rseg : 0) + 1]);
       return;
     }
     by -= rho_rows;
@@ -1261,15 +1271,27 @@ static hipError_t run_finalize_quant(const T* a, int64_t rows, int64_t cols, int
                                      int64_t ch) {
   const int64_t nchq = chunk_upper_bound(rows, nseg, kQuantRows);
   const int64_t ct_s = (cols + kPlainStatsCols - 1) / kPlainStatsCols;
-  const int64_t ct_f = (cols + kFinCols - 1) / kFinCols;
+  // finalize column tiles: 64 columns when the segments are short (on average
+  // at most 16 chunks, one round of the wide kernel's loads), else 16
+  const bool fin_wide = chunk_upper_bound(rows, nseg, ch) <= 16 * (int64_t)nseg;
+  const int64_t fin_cols = fin_wide ? 64 : kFinCols;
+  const int64_t ct_f = (cols + fin_cols - 1) / fin_cols;   // <= the workspace's tiles
   const int64_t ct_q = ((cols >> 4) + 63) / 64;
   int64_t ntmax;
   const float* tmax;
   if (split) {
     dim3 g((unsigned)ct_f, (unsigned)nseg);
-    k_finalize<<<g, 256, 0, st>>>(a, sizeof(T) == 2, lda, rows, cols, offs, nseg, ws.psum,
-                                  ws.pmax, ws.pmin, ws.pmnz, ws.mu, mean_f32, ws.tmax_r,
-                                  ws.tmax_mu, ratio ? ws.psq : nullptr, ws.tssq, ws.tmu2, ch);
+#define AVERIS_FIN_LAUNCH(NCOL)                                                              \
+  k_finalize<NCOL><<<g, 256, 0, st>>>(a, sizeof(T) == 2, lda, rows, cols, offs, nseg, ws.psum, \
+                                      ws.pmax, ws.pmin, ws.pmnz, ws.mu, mean_f32, ws.tmax_r,   \
+                                      ws.tmax_mu, ratio ? ws.psq : nullptr, ws.tssq, ws.tmu2,  \
+                                      ch)
+    if (fin_wide) {
+      AVERIS_FIN_LAUNCH(64);
+    } else {
+      AVERIS_FIN_LAUNCH((int)kFinCols);
+    }
+#undef AVERIS_FIN_LAUNCH
     tmax = ws.tmax_r;
     ntmax = ct_f;
   } else {
@@ -1277,8 +1299,14 @@ static hipError_t run_finalize_quant(const T* a, int64_t rows, int64_t cols, int
     tmax = ws.pamax;
     ntmax = ct_s;
   }
-  // rank-one workgroups (16 rows of one segment's B each) take the leading grid rows
-  const int64_t rho_rows = r1 ? ((r1->n + 15) / 16 * nseg + ct_q - 1) / ct_q : 0;
+  // rank-one workgroups take the leading grid rows: r1_rows rows of one
+  // segment's B each, 16 while that gives at most 512 workgroups, else up to
+  // 128 (many experts' weights: the mean's quantization and staging, which
+  // every such workgroup repeats, spread over more rows)
+  int r1_rows = 16;
+  while (r1 && r1_rows < 128 && (r1->n + r1_rows - 1) / r1_rows * nseg > 512) r1_rows *= 2;
+  const int64_t rho_rows =
+      r1 ? ((r1->n + r1_rows - 1) / r1_rows * nseg + ct_q - 1) / ct_q : 0;
   const size_t lds_r1 = r1 ? (size_t)cols * 2 : 0;
   const QOperand rb = r1 ? r1->b : QOperand{nullptr, nullptr, nullptr};
   dim3 gq((unsigned)ct_q, (unsigned)(rho_rows + nchq + nseg));
@@ -1292,7 +1320,7 @@ static hipError_t run_finalize_quant(const T* a, int64_t rows, int64_t cols, int
       a, rows, cols, lda, offs, nseg, nchq, seed, stream_id, ws.mu, tmax, ntmax, ws.tmax_mu, \
       ct_f, out.codes, out.scales, out.tscale, mean ? mean->codes : nullptr,                \
       mean ? mean->scales : nullptr, mean ? mean->tscale : nullptr, ws.tssq, ws.tmu2, ratio, \
-      rb, r1 ? r1->n : 0, r1 ? r1->rho : nullptr, rho_rows)
+      rb, r1 ? r1->n : 0, r1 ? r1->rho : nullptr, rho_rows, r1_rows)
   if (split) {
     if (sr) { AVERIS_QUANT_LAUNCH(true, true); } else { AVERIS_QUANT_LAUNCH(true, false); }
   } else {
