@@ -76,7 +76,7 @@ def parse():
                    help="time the headline config only (no other configs, wgrad, ratio, weight copies)")
     p.add_argument("--copies", type=int, default=0, help="rotating input copies (0: auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=1024,
+    p.add_argument("--cpu-rows", type=int, default=3072,
                    help="oracle sample: tokens of every linear of the headline workload")
     p.add_argument("--traffic-probe", action="store_true",
                    help="run a 256 MiB device copy and three Averis steps of the headline config "
