@@ -379,6 +379,8 @@ __global__ __launch_bounds__(kWinThreads, 1) void k_gemm_win(
     stage(w, WIC<2>{});
     stage(w, WIC<3>{});
   }
+  // the accumulator copies the compiler hoists onto the loop's exit path
+  // come before this fence; it pads those itself (s_nop ahead of the first)
   mfma_drain();
 
   // ------------------------------------------------------------------ epilogue
