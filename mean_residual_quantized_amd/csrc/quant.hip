@@ -338,16 +338,12 @@ __device__ __noinline__ double exact_column_sum(const void* a, bool bf16, int64_
 }
 
 // ---------------------------------------------------------------------------
-// finalize (split): block = NC columns x 256 / NC chunk lanes, per segment,
-// over the partials of chunks of `ch` rows (the statistics pass's
+// finalize (split): block = kFinCols (16) columns x 16 chunk lanes, per
+// segment, over the partials of chunks of `ch` rows (the statistics pass's
 // kStatsRows, or the row tiles of a GEMM that wrote the statistics of its
-// output); each lane keeps U partial loads of each kind in flight.  NC = 16
-// for long segments (128 chunks per round of loads), NC = 64 for many short
-// ones (grouped experts: a few chunks each, so wider column tiles and a
-// quarter of the workgroups).  The fp64 partial sums are exact, so the order
-// of the reduction is free.
+// output); each lane keeps all its partial loads in flight.  The fp64 partial
+// sums are exact, so the order of the reduction is free.
 // ---------------------------------------------------------------------------
-template <int NC>
 __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, int64_t lda,
                                                   int64_t rows, int64_t cols, const int64_t* offs,
                                                   int nseg, const double* __restrict__ psum,
@@ -361,9 +357,7 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
                                                   const double* __restrict__ psq,
                                                   double* __restrict__ tssq,
                                                   double* __restrict__ tmu2, int64_t ch) {
-  static_assert(NC >= (int)kFinCols && NC <= 64 && 256 % NC == 0, "column tile");
-  constexpr int NQ = 256 / NC;
-  using Mask = typename std::conditional<(NC > 32), uint64_t, uint32_t>::type;
+  constexpr int NC = (int)kFinCols, NQ = 256 / NC;
   const int seg = blockIdx.y;
   const SegRange sr = describe_segment(offs, nseg, rows, ch, seg);
   const int jl = threadIdx.x % NC, q = threadIdx.x / NC;
@@ -371,7 +365,7 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
   double s = 0.0, s2 = 0.0;
   float m1 = -__builtin_inff(), m0 = __builtin_inff(), mz = __builtin_inff();
   if (j < cols && sr.c1 > sr.c0) {
-    constexpr int U = NC > 16 ? 4 : 8;   // NQ * U chunks in one round of loads
+    constexpr int U = 8;   // up to 128 chunks in one round of loads
     const int64_t clast = sr.c1 - 1;
     for (int64_t ck = sr.c0 + q; ck < sr.c1; ck += NQ * U) {
       double ps[U], pq[U];
@@ -398,7 +392,7 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
   }
   __shared__ double ls[NQ][NC], lq[NQ][NC];
   __shared__ float lx[NQ][NC], ln[NQ][NC], lz[NQ][NC];
-  __shared__ Mask need_mask;       // bit c: column c of the tile failed the certificate
+  __shared__ uint32_t need_mask;   // bit c: column c of the tile failed the certificate
   __shared__ double exact_s[NC];
   __shared__ uint32_t wide_red[128][kWideWords];
   ls[q][jl] = s;
@@ -434,12 +428,12 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
   // the q == 0 lanes are lanes 0 .. NC-1 of wave 0
   if (threadIdx.x < 64) {
     const uint64_t bal = __ballot(fail);
-    if (threadIdx.x == 0) need_mask = (Mask)bal;
+    if (threadIdx.x == 0) need_mask = (uint32_t)bal;
   }
   __syncthreads();
-  const Mask mask = need_mask;   // uniform
-  for (Mask mrest = mask; mrest != 0; mrest &= mrest - 1) {
-    const int cidx = __builtin_ctzll((uint64_t)mrest);
+  const uint32_t mask = need_mask;   // uniform
+  for (uint32_t mrest = mask; mrest != 0; mrest &= mrest - 1) {
+    const int cidx = __builtin_ctz(mrest);
     const double v = exact_column_sum(a, a_bf16, lda, cols, sr.seg_r0, sr.seg_r1, sr.c0, sr.c1,
                                       ch, (int64_t)blockIdx.x * NC + cidx, psum, pmax, pmin, pmnz,
                                       wide_red);
@@ -447,7 +441,7 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
   }
   if (mask) __syncthreads();
   if (q == 0 && j < cols) {
-    if ((mask >> jl) & 1u) t = exact_s[jl];   // jl < NC <= mask bits
+    if ((mask >> jl) & 1u) t = exact_s[jl];
     float m = 0.0f;
     if (l > 0) {
       const double md = t / (double)l;
@@ -480,6 +474,133 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
         tssq[(int64_t)seg * gridDim.x + blockIdx.x] = t2;
         tmu2[(int64_t)seg * gridDim.x + blockIdx.x] = mu2;
       }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// finalize for many short segments (grouped experts, a few chunks each):
+// wave w of the block takes segment 4 blockIdx.y + w and lane l column
+// 64 blockIdx.x + l, so each lane sums its column over its segment's chunks
+// by itself (kSegFinU chunks' partials in flight) and only the tile maxima
+// need the wave.  Same outputs as k_finalize, per 64-column tile.
+// ---------------------------------------------------------------------------
+constexpr int kSegFinU = 16;
+__global__ __launch_bounds__(256) void k_finalize_seg(const void* a, bool a_bf16, int64_t lda,
+                                                      int64_t rows, int64_t cols,
+                                                      const int64_t* offs, int nseg,
+                                                      const double* __restrict__ psum,
+                                                      const float* __restrict__ pmax,
+                                                      const float* __restrict__ pmin,
+                                                      const float* __restrict__ pmnz,
+                                                      float* __restrict__ mu,
+                                                      float* __restrict__ mean_out,
+                                                      float* __restrict__ tmax_r,
+                                                      float* __restrict__ tmax_mu,
+                                                      const double* __restrict__ psq,
+                                                      double* __restrict__ tssq,
+                                                      double* __restrict__ tmu2, int64_t ch) {
+  __shared__ SegRange srs[4];
+  __shared__ uint64_t fail_mask[4];
+  __shared__ double exact_s[4][64];
+  __shared__ uint32_t wide_red[128][kWideWords];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int seg_w = (int)blockIdx.y * 4 + wave;
+  if (seg_w < nseg) {   // wave-uniform
+    seg_scan(offs, nseg, rows, ch, seg_w, 1, &srs[wave]);
+  } else if (lane == 0) {
+    SegRange none;
+    none.seg = -1;
+    none.r0 = none.r1 = none.seg_r0 = none.seg_r1 = 0;
+    none.c0 = none.c1 = 0;
+    srs[wave] = none;
+  }
+  __syncthreads();
+  const SegRange sr = srs[wave];
+  const int64_t j = (int64_t)blockIdx.x * 64 + lane;
+  const bool live = sr.seg >= 0 && j < cols;
+  double t = 0.0, t2 = 0.0;
+  float x1 = -__builtin_inff(), x0 = __builtin_inff(), z = __builtin_inff();
+  if (live && sr.c1 > sr.c0) {
+    const int64_t clast = sr.c1 - 1;
+    for (int64_t c = sr.c0; c < sr.c1; c += kSegFinU) {
+      double ps[kSegFinU], pq[kSegFinU];
+      float px[kSegFinU], pn[kSegFinU], pz[kSegFinU];
+#pragma unroll
+      for (int u = 0; u < kSegFinU; ++u) {
+        const int64_t cc = c + u < clast ? c + u : clast;
+        ps[u] = psum[cc * cols + j];
+        pq[u] = psq ? psq[cc * cols + j] : 0.0;
+        px[u] = pmax[cc * cols + j];
+        pn[u] = pmin[cc * cols + j];
+        pz[u] = pmnz[cc * cols + j];
+      }
+#pragma unroll
+      for (int u = 0; u < kSegFinU; ++u) {
+        const bool ok = c + u <= clast;
+        t += ok ? ps[u] : 0.0;
+        t2 += ok ? pq[u] : 0.0;
+        x1 = __builtin_fmaxf(x1, px[u]);   // a clamped chunk repeats a real one
+        x0 = __builtin_fminf(x0, pn[u]);
+        z = __builtin_fminf(z, pz[u]);
+      }
+    }
+  }
+  const int64_t l = sr.seg_r1 - sr.seg_r0;
+  bool fail = false;
+  if (live && l > 0) {
+    // the certificate of k_finalize: every fp64 addition above was exact
+    const double amx = __builtin_fmax(__builtin_fabs((double)x1), __builtin_fabs((double)x0));
+    fail = !sum_certified((double)l, amx, z, a_bf16);
+  }
+  const uint64_t bal = __ballot(fail);
+  if (lane == 0) fail_mask[wave] = bal;
+  __syncthreads();
+  bool any = false;
+  for (int w = 0; w < 4; ++w) {
+    const SegRange sw = srs[w];
+    for (uint64_t mrest = fail_mask[w]; mrest != 0; mrest &= mrest - 1) {
+      const int cidx = __builtin_ctzll(mrest);
+      const double v = exact_column_sum(a, a_bf16, lda, cols, sw.seg_r0, sw.seg_r1, sw.c0, sw.c1,
+                                        ch, (int64_t)blockIdx.x * 64 + cidx, psum, pmax, pmin,
+                                        pmnz, wide_red);
+      if (threadIdx.x == 0) exact_s[w][cidx] = v;
+      any = true;
+    }
+  }
+  if (any) __syncthreads();
+  float rmax = 0.0f, amu = 0.0f;
+  double mu2 = 0.0;
+  if (live) {
+    if (fail) t = exact_s[wave][lane];
+    float m = 0.0f;
+    if (l > 0) {
+      const double md = t / (double)l;
+      m = (float)md;
+      rmax = __builtin_fmaxf(x1 - m, m - x0);
+      mu2 = md * md;
+    }
+    mu[(int64_t)sr.seg * cols + j] = m;
+    if (mean_out) mean_out[(int64_t)sr.seg * cols + j] = m;
+    amu = __builtin_fabsf(m);
+  }
+  // the tile's maxima (and ratio sums) over the wave's 64 columns
+  for (int d = 32; d > 0; d >>= 1) {
+    rmax = __builtin_fmaxf(rmax, __shfl_xor(rmax, d, 64));
+    amu = __builtin_fmaxf(amu, __shfl_xor(amu, d, 64));
+  }
+  if (sr.seg >= 0 && lane == 0) {
+    tmax_r[(int64_t)sr.seg * gridDim.x + blockIdx.x] = rmax;
+    tmax_mu[(int64_t)sr.seg * gridDim.x + blockIdx.x] = amu;
+  }
+  if (psq) {
+    for (int d = 32; d > 0; d >>= 1) {
+      t2 += __shfl_xor(t2, d, 64);
+      mu2 += __shfl_xor(mu2, d, 64);
+    }
+    if (sr.seg >= 0 && lane == 0) {
+      tssq[(int64_t)sr.seg * gridDim.x + blockIdx.x] = t2;
+      tmu2[(int64_t)sr.seg * gridDim.x + blockIdx.x] = mu2;
     }
   }
 }
@@ -1271,27 +1392,28 @@ static hipError_t run_finalize_quant(const T* a, int64_t rows, int64_t cols, int
                                      int64_t ch) {
   const int64_t nchq = chunk_upper_bound(rows, nseg, kQuantRows);
   const int64_t ct_s = (cols + kPlainStatsCols - 1) / kPlainStatsCols;
-  // finalize column tiles: 64 columns when the segments are short (on average
-  // at most 16 chunks, one round of the wide kernel's loads), else 16
-  const bool fin_wide = chunk_upper_bound(rows, nseg, ch) <= 16 * (int64_t)nseg;
-  const int64_t fin_cols = fin_wide ? 64 : kFinCols;
+  // finalize: many short segments (on average at most 16 chunks) take the
+  // per-segment-wave kernel in 64-column tiles, else 16-column tiles with
+  // the chunks spread over the lanes
+  const bool fin_seg = nseg > 1 && chunk_upper_bound(rows, nseg, ch) <= 16 * (int64_t)nseg;
+  const int64_t fin_cols = fin_seg ? 64 : kFinCols;
   const int64_t ct_f = (cols + fin_cols - 1) / fin_cols;   // <= the workspace's tiles
   const int64_t ct_q = ((cols >> 4) + 63) / 64;
   int64_t ntmax;
   const float* tmax;
   if (split) {
-    dim3 g((unsigned)ct_f, (unsigned)nseg);
-#define AVERIS_FIN_LAUNCH(NCOL)                                                              \
-  k_finalize<NCOL><<<g, 256, 0, st>>>(a, sizeof(T) == 2, lda, rows, cols, offs, nseg, ws.psum, \
-                                      ws.pmax, ws.pmin, ws.pmnz, ws.mu, mean_f32, ws.tmax_r,   \
-                                      ws.tmax_mu, ratio ? ws.psq : nullptr, ws.tssq, ws.tmu2,  \
-                                      ch)
-    if (fin_wide) {
-      AVERIS_FIN_LAUNCH(64);
+    if (fin_seg) {
+      dim3 g((unsigned)ct_f, (unsigned)((nseg + 3) / 4));
+      k_finalize_seg<<<g, 256, 0, st>>>(a, sizeof(T) == 2, lda, rows, cols, offs, nseg, ws.psum,
+                                        ws.pmax, ws.pmin, ws.pmnz, ws.mu, mean_f32, ws.tmax_r,
+                                        ws.tmax_mu, ratio ? ws.psq : nullptr, ws.tssq, ws.tmu2,
+                                        ch);
     } else {
-      AVERIS_FIN_LAUNCH((int)kFinCols);
+      dim3 g((unsigned)ct_f, (unsigned)nseg);
+      k_finalize<<<g, 256, 0, st>>>(a, sizeof(T) == 2, lda, rows, cols, offs, nseg, ws.psum,
+                                    ws.pmax, ws.pmin, ws.pmnz, ws.mu, mean_f32, ws.tmax_r,
+                                    ws.tmax_mu, ratio ? ws.psq : nullptr, ws.tssq, ws.tmu2, ch);
     }
-#undef AVERIS_FIN_LAUNCH
     tmax = ws.tmax_r;
     ntmax = ct_f;
   } else {
