@@ -174,6 +174,34 @@ def test_uncertified_columns_take_the_exact_sum(dtype, rows):
         assert rc["tscale"][2 * seg] == g["residual"][seg]["s_enc"]
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_uncertified_columns_in_many_short_segments(dtype):
+    # nine segments (two empty) over 2000 rows: the finalize for short
+    # segments takes four segments per workgroup, so the columns that fail the
+    # certificate sit in segments of the second and third workgroup rows and
+    # in waves other than the first; 130 columns leave a ragged last tile
+    rows, cols = 2000, 130 + 14
+    x = adversarial_columns(rows, cols, 9)
+    x[:, 64:72] = x[:, 0:8]            # failing columns in the second 64-column tile too
+    x = torch.from_numpy(x).to(dtype)
+    offs = np.array([0, 100, 100, 350, 700, 700, 900, 1300, 1500, 2000], dtype=np.int64)
+    nseg = len(offs) - 1
+    res_g, mean_g, mu_g = av.averis_split_quant_grouped(x.cuda(), torch.from_numpy(offs).cuda(),
+                                                        seed=4)
+    g = orc.split_quant_grouped(f32(x), offs, "sr", 4)
+    np.testing.assert_array_equal(mu_g.cpu().numpy(), g["mu"])
+    rc, mc = res_g.cpu(), mean_g.cpu()
+    for seg in range(nseg):
+        r0, r1 = offs[seg], offs[seg + 1]
+        print("segment %d rows %d..%d" % (seg, r0, r1), flush=True)
+        np.testing.assert_array_equal(rc["codes"][r0:r1], g["residual"][seg]["codes"])
+        np.testing.assert_array_equal(rc["scales"][r0:r1], g["residual"][seg]["scales"])
+        assert rc["tscale"][2 * seg] == g["residual"][seg]["s_enc"]
+        np.testing.assert_array_equal(mc["codes"][seg], g["mean"][seg]["codes"][0])
+        np.testing.assert_array_equal(mc["scales"][seg], g["mean"][seg]["scales"][0])
+        assert mc["tscale"][2 * seg] == g["mean"][seg]["s_enc"]
+
+
 def test_bf16_output_within_rounding():
     cfg = workloads.up_proj(l=256, m=256, n=128)
     xg = cfg["x"].cuda()
