@@ -74,6 +74,18 @@ __device__ __forceinline__ void store_out(T v, T* p) {
   *p = v;
 }
 
+// streaming output stores (nontemporal: whole 128-byte lines written by
+// eight lanes go to memory without staying dirty in L2).  A GEMM's bf16
+// output is not read again soon, and left dirty in L2 it is written back
+// while the next kernels on the stream run: measured 1-2 us less per launch
+// of the codes-in-LDS GEMM and about 25 us less for the splits that follow
+// the GEMMs of the seven-linear step.  (Split-K partials, which the reduce
+// reads right away, keep plain stores: streamed, that reduce got slower.)
+template <typename T>
+__device__ __forceinline__ void store_stream(T v, T* p) {
+  __builtin_nontemporal_store(v, p);
+}
+
 constexpr int kXcds = 8;   // MI355X: 8 accelerator complex dies, one L2 each
 
 // After the last MFMA of a K loop its accumulators must not be read for

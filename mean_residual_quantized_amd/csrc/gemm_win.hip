@@ -39,10 +39,12 @@
 // epilogue.
 //
 // Epilogue: y = fma(acc, alpha, rho_j).  bf16 output is staged in the freed
-// LDS and stored in 16-byte pieces, eight lanes to a 128-byte line; with
+// LDS and stored in 16-byte pieces, eight lanes to a 128-byte line, with
+// streaming (nontemporal) stores; with
 // column statistics requested the staged tile's per-column fp64 sum, max,
 // min and smallest nonzero magnitude go out too.  fp32 output (split-K
-// partials) is stored directly, 16 bytes per lane.
+// partials) is stored directly, 16 bytes per lane, with plain stores: the
+// reduce that follows reads the partials back while they are still cached.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -430,7 +432,7 @@ __global__ __launch_bounds__(kWinThreads, 1) void k_gemm_win(
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + r * kStLd + cc * 16);
       uint16_t* dst = cb + (int64_t)r * ldc + cc * 8;
       if (st_vec && cc * 8 + 8 <= cols_here) {
-        store_out(v, reinterpret_cast<u32x4_t*>(dst));
+        store_stream(v, reinterpret_cast<u32x4_t*>(dst));
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
