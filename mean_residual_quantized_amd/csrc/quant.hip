@@ -684,6 +684,12 @@ __device__ __forceinline__ void encode_block16(const float* r, float e_b, uint64
   }
 }
 
+// a value the optimizer cannot see through (kept in a register pair as is)
+__device__ __forceinline__ uint64_t opaque_u64(uint64_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // quantize one 16-block held in registers: its scale from its own largest
 // magnitude, then its codes
 template <bool SR>
@@ -948,28 +954,35 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ a, int64_t 
     for (int k = 0; k < 16; ++k) m[k] = mp[k];
   }
   // every row of the chunk: loads first (rows past the end clamped), then
-  // quantize; the row is uniform per wavefront, so the store guard is too
+  // quantize; the row is uniform per wavefront, so the store guard is too.
+  // Row u of the thread is row0 + 4 u: its addresses and element index are
+  // the first row's plus a uniform stride (no 64-bit multiply per row).
   constexpr int R = (int)(kQuantRows / 4);
   const int64_t rlast = sr.r1 - 1;
+  const int64_t row0 = sr.r0 + ty;
+  const T* a_row0 = a + row0 * lda + b * 16;
+  const T* a_last = a + rlast * lda + b * 16;
   float v[R][16];
 #pragma unroll
   for (int u = 0; u < R; ++u) {
-    const int64_t row = sr.r0 + ty + 4 * u;
-    const T* p = a + (row < rlast ? row : rlast) * lda + b * 16;
+    const T* p = row0 + 4 * u <= rlast ? a_row0 + 4 * u * lda : a_last;
     Load8<T>::run(p, v[u]);
     Load8<T>::run(p + 8, v[u] + 8);
   }
+  // (kept opaque to the optimizer, which would otherwise fold the strides
+  // back into one 64-bit multiply per row)
+  const uint64_t idx_row0 = opaque_u64((uint64_t)row0 * (uint64_t)cols + (uint64_t)b * 16);
+  uint8_t* c_row0 = codes + (int64_t)opaque_u64((uint64_t)(row0 * (cols >> 1) + b * 8));
+  uint8_t* s_row0 = scales + (int64_t)opaque_u64((uint64_t)(row0 * nb + b));
 #pragma unroll
   for (int u = 0; u < R; ++u) {
-    const int64_t row = sr.r0 + ty + 4 * u;
-    if (row > rlast) break;
+    if (row0 + 4 * u > rlast) break;
     if (SPLIT) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) v[u][k] = v[u][k] - m[k];
     }
-    const uint64_t idx0 = (uint64_t)row * (uint64_t)cols + (uint64_t)b * 16;
-    quant_block16_tab<SR>(v[u], s_enc, eb_tab, idx0, k0, k1, stream,
-                          codes + row * (cols >> 1) + b * 8, scales + row * nb + b);
+    quant_block16_tab<SR>(v[u], s_enc, eb_tab, idx_row0 + (uint64_t)(4 * u) * (uint64_t)cols, k0,
+                          k1, stream, c_row0 + 4 * u * (cols >> 1), s_row0 + 4 * u * nb);
   }
 }
 
