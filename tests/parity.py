@@ -1,11 +1,11 @@
 """Shared parity criteria of the GPU tests, and a process pool that runs the
 oracle's quantization over row blocks of a large tensor in parallel.
 
-GEMM acceptance (the north-star criterion, "max relative error 1e-3 against
-the oracle's float64 product of the same dequantized operands", read two
-ways, both required for fp32 output):
+GEMM acceptance: a relative error of at most 1e-3 against the oracle's
+float64 product of the same dequantized operands, read two ways, both
+required for fp32 output:
   * elementwise: |C - C_ref| <= 1e-3 (|deq A| |deq B|^T + 1 |deq mean| |deq B|^T),
-    the scale an FP32-accumulated product of exact operands is judged on
+    the scale on which an FP32-accumulated product of exact operands is measured
     where C_ref cancels to ~0;
   * normwise: max |C - C_ref| <= 1e-3 max |C_ref|.
 bf16 output adds its own rounding (half an ulp, at most 2^-9 relative) to the
