@@ -101,6 +101,11 @@ class Linear:
         self.offsets = None if offsets is None else torch.as_tensor(offsets, dtype=torch.int64,
                                                                     device=dev)
         self.nseg = 1 if offsets is None else len(offsets) - 1
+        # the linear whose input this one shares in a transformer block (k and
+        # v take q's, up takes gate's): with --shared-input-steps its split is
+        # reused, not recomputed
+        self.share_src = None
+        self.last_split = None
         ns = 0 if offsets is None else self.nseg
         l, m, n = self.l, self.m, self.n
         wm, wn = (self.w.shape[1], self.w.shape[2]) if self.w.dim() == 3 else self.w.shape
@@ -149,7 +154,14 @@ def make_linears(cfg):
     for name in workloads.QWEN3_06B_LINEARS:
         c = workloads.block_linear(name)
         out.append(Linear(name, c["x"], c["w"], c["d"]))
+    by_name = {L.name: L for L in out}
+    for dst, src in SHARED_INPUTS.items():
+        by_name[dst].share_src = by_name[src]
     return out
+
+
+# in a transformer block q, k, v read one input, gate and up another
+SHARED_INPUTS = {"k": "q", "v": "q", "up": "gate"}
 
 
 # --------------------------------------------------------------------------
@@ -176,8 +188,11 @@ class Timer:
         return [a.elapsed_time(b) for a, b in self.pairs.get(name, [])]
 
 
-def run_linear(L, i, t, vanilla):
-    """One linear's forward + dgrad with input copy i."""
+def run_linear(L, i, t, vanilla, shared=False):
+    """One linear's forward + dgrad with input copy i.  shared: a linear
+    whose input is another's (L.share_src) reuses that linear's split (or
+    plain quant) of it from the same step; the Averis GEMM then takes the
+    mean and forms its own rank-one row (averis_gemm_fwd)."""
     def tic(k):
         if t:
             t.start(L.name + "/" + k)
@@ -190,37 +205,37 @@ def run_linear(L, i, t, vanilla):
     tic("wquant")
     wt, wd = av.averis_quant_pair(L.w, rnd=av.RN, ws=ws["q"])
     toc("wquant")
+    if L.offsets is None and shared and L.share_src is not None:
+        xr, xmean = L.share_src.last_split
+        tic("gemm_fwd")
+        if not vanilla:
+            av.averis_gemm_fwd(xr, xmean, wt, out_dtype=torch.bfloat16, out=ws["y"], ws=ws["g"])
+        else:
+            av.averis_gemm_vanilla(xr, wt, out_dtype=torch.bfloat16, out=ws["y"], ws=ws["g"])
+        toc("gemm_fwd")
+        run_dgrad(L, d, wd, t, vanilla)
+        return
     if L.offsets is None:
         if not vanilla:
             # the split also forms the rank-one row 1 (mean W) for the GEMM
             # that takes it, so the GEMM adds it without a mean row of its own
             tic("split_x")
-            xr, _, _, rho_x = av.averis_split_quant_rank1(x, wt, seed=0, ws=ws["sq_x"],
-                                                          rho=ws["rho_x"])
+            xr, xmean, _, rho_x = av.averis_split_quant_rank1(x, wt, seed=0, ws=ws["sq_x"],
+                                                              rho=ws["rho_x"])
             toc("split_x")
+            L.last_split = (xr, xmean)
             tic("gemm_fwd")
             av.averis_gemm_rank1(xr, rho_x, wt, out_dtype=torch.bfloat16, out=ws["y"])
             toc("gemm_fwd")
-            tic("split_d")
-            dr, _, _, rho_d = av.averis_split_quant_rank1(d, wd, seed=1, ws=ws["sq_d"],
-                                                          rho=ws["rho_d"])
-            toc("split_d")
-            tic("gemm_dgrad")
-            av.averis_gemm_rank1(dr, rho_d, wd, out_dtype=torch.bfloat16, out=ws["dx"])
-            toc("gemm_dgrad")
         else:
             tic("split_x")
             xq = av.averis_quant(x, seed=0, ws=ws["sq_x"])
             toc("split_x")
+            L.last_split = (xq, None)
             tic("gemm_fwd")
             av.averis_gemm_vanilla(xq, wt, out_dtype=torch.bfloat16, out=ws["y"], ws=ws["g"])
             toc("gemm_fwd")
-            tic("split_d")
-            dq = av.averis_quant(d, seed=1, ws=ws["sq_d"])
-            toc("split_d")
-            tic("gemm_dgrad")
-            av.averis_gemm_vanilla(dq, wd, out_dtype=torch.bfloat16, out=ws["dx"], ws=ws["g"])
-            toc("gemm_dgrad")
+        run_dgrad(L, d, wd, t, vanilla)
         return
     offs = L.offsets
     if not vanilla:
@@ -253,9 +268,30 @@ def run_linear(L, i, t, vanilla):
         toc("gemm_dgrad")
 
 
-def run_step(linears, i, t=None, vanilla=False):
+def run_dgrad(L, d, wd, t, vanilla):
+    """The dgrad pass of a dense linear (split or plain quant of D, GEMM)."""
+    ws = L.ws
+    if t:
+        t.start(L.name + "/split_d")
+    if not vanilla:
+        dr, _, _, rho_d = av.averis_split_quant_rank1(d, wd, seed=1, ws=ws["sq_d"],
+                                                      rho=ws["rho_d"])
+    else:
+        dq = av.averis_quant(d, seed=1, ws=ws["sq_d"])
+    if t:
+        t.stop(L.name + "/split_d")
+        t.start(L.name + "/gemm_dgrad")
+    if not vanilla:
+        av.averis_gemm_rank1(dr, rho_d, wd, out_dtype=torch.bfloat16, out=ws["dx"])
+    else:
+        av.averis_gemm_vanilla(dq, wd, out_dtype=torch.bfloat16, out=ws["dx"], ws=ws["g"])
+    if t:
+        t.stop(L.name + "/gemm_dgrad")
+
+
+def run_step(linears, i, t=None, vanilla=False, shared=False):
     for L in linears:
-        run_linear(L, i, t, vanilla)
+        run_linear(L, i, t, vanilla, shared)
 
 
 _SLEEP_CYCLES_PER_MS = None
@@ -280,7 +316,7 @@ def pct(v, q):
     return float(np.percentile(v, q)) if len(v) else float("nan")
 
 
-def timed(linears, steps, warmup, vanilla):
+def timed(linears, steps, warmup, vanilla, shared=False, per_call=True):
     """Step time three ways (ms/step), the per-step device times of the
     queued run, and a per-call event timer.
 
@@ -292,11 +328,11 @@ def timed(linears, steps, warmup, vanilla):
             step's own time)."""
     ncopy = max(len(L.xs) for L in linears)
     for i in range(warmup):
-        run_step(linears, i, None, vanilla)
+        run_step(linears, i, None, vanilla, shared)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        run_step(linears, i, None, vanilla)
+        run_step(linears, i, None, vanilla, shared)
     enqueue_ms = (time.perf_counter() - t0) * 1e3
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / steps
@@ -306,7 +342,7 @@ def timed(linears, steps, warmup, vanilla):
     for i in range(ncopy):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, pool=pool):
-            run_step(linears, i, None, vanilla)
+            run_step(linears, i, None, vanilla, shared)
         pool = g.pool()
         graphs.append(g)
     torch.cuda.synchronize()
@@ -326,7 +362,7 @@ def timed(linears, steps, warmup, vanilla):
     t0 = time.perf_counter()
     for i in range(steps):
         evs[i].record()
-        run_step(linears, i, None, vanilla)
+        run_step(linears, i, None, vanilla, shared)
     evs[steps].record()
     queued_enqueue_ms = (time.perf_counter() - t0) * 1e3
     torch.cuda.synchronize()
@@ -338,10 +374,11 @@ def timed(linears, steps, warmup, vanilla):
     # per-call durations, events on the launch stream, same rotation, also
     # queued behind a spin kernel
     t = Timer()
-    hold_gpu(hold * 2.0)
-    for i in range(steps):
-        run_step(linears, i, t, vanilla)
-    torch.cuda.synchronize()
+    if per_call:
+        hold_gpu(hold * 2.0)
+        for i in range(steps):
+            run_step(linears, i, t, vanilla, shared)
+        torch.cuda.synchronize()
     return dict(eager=eager_ms, graph=graph_ms, queued=queued_ms,
                 queued_p10=pct(per_step, 10), queued_p90=pct(per_step, 90)), t
 
@@ -425,6 +462,23 @@ def measure(cfg, linears, steps, warmup):
     for s in (summary["split_quant"], summary["vanilla_quant"]):
         for v in s.values():
             v["frac_hbm"] = v["gbs"] / HBM_PEAK_GBS
+    if any(L.share_src is not None for L in linears):
+        # the same step with each shared input split (or quantized) once: k
+        # and v reuse q's, up reuses gate's; their Averis GEMMs take the mean
+        # and form their rank-one rows themselves
+        sa, _ = timed(linears, steps, warmup, vanilla=False, shared=True, per_call=False)
+        sv, _ = timed(linears, steps, warmup, vanilla=True, shared=True, per_call=False)
+        log("bench: config %d, shared inputs: averis %.4f | vanilla %.4f (ms/step)"
+            % (cfg, sa["queued"], sv["queued"]))
+        summary["shared_input_once"] = dict(
+            shared={L.name: L.share_src.name for L in linears if L.share_src is not None},
+            ms_per_step=sa["queued"], vanilla_ms_per_step=sv["queued"],
+            step_p10_p90_ms=[sa["queued_p10"], sa["queued_p90"]],
+            vanilla_step_p10_p90_ms=[sv["queued_p10"], sv["queued_p90"]],
+            tflops=flops_step / (sa["queued"] * 1e-3) / 1e12,
+            vanilla_tflops=flops_step / (sv["queued"] * 1e-3) / 1e12,
+            overhead_pct=100 * (sa["queued"] / sv["queued"] - 1),
+            step_ms_by_launch={"averis": sa, "vanilla": sv})
     return summary, ta, flops_step
 
 
