@@ -28,8 +28,9 @@ __device__ __forceinline__ u32x4 philox10(uint32_t c0, uint32_t c1, uint32_t c2,
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
     const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    // three-input xors as one v_bitop3_b32 each (truth table 0x96 = a ^ b ^ c)
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;
