@@ -157,6 +157,8 @@ def make_linears(cfg):
     by_name = {L.name: L for L in out}
     for dst, src in SHARED_INPUTS.items():
         by_name[dst].share_src = by_name[src]
+    out[0].ws["qm"] = torch.empty(av.workspace_bytes(av.OP_QUANT_PAIR_MULTI, 0, 0, len(out)),
+                                  dtype=torch.uint8, device="cuda")
     return out
 
 
@@ -188,11 +190,12 @@ class Timer:
         return [a.elapsed_time(b) for a, b in self.pairs.get(name, [])]
 
 
-def run_linear(L, i, t, vanilla, shared=False):
+def run_linear(L, i, t, vanilla, shared=False, wq=None):
     """One linear's forward + dgrad with input copy i.  shared: a linear
     whose input is another's (L.share_src) reuses that linear's split (or
     plain quant) of it from the same step; the Averis GEMM then takes the
-    mean and forms its own rank-one row (averis_gemm_fwd)."""
+    mean and forms its own rank-one row (averis_gemm_fwd).  wq: both copies
+    of the weight, when the step quantized all weights at once."""
     def tic(k):
         if t:
             t.start(L.name + "/" + k)
@@ -202,9 +205,12 @@ def run_linear(L, i, t, vanilla, shared=False):
             t.stop(L.name + "/" + k)
     ws = L.ws
     x, d = L.xs[i % len(L.xs)], L.ds[i % len(L.ds)]
-    tic("wquant")
-    wt, wd = av.averis_quant_pair(L.w, rnd=av.RN, ws=ws["q"])
-    toc("wquant")
+    if wq is None:
+        tic("wquant")
+        wt, wd = av.averis_quant_pair(L.w, rnd=av.RN, ws=ws["q"])
+        toc("wquant")
+    else:
+        wt, wd = wq
     if L.offsets is None and shared and L.share_src is not None:
         xr, xmean = L.share_src.last_split
         tic("gemm_fwd")
@@ -289,9 +295,25 @@ def run_dgrad(L, d, wd, t, vanilla):
         t.stop(L.name + "/gemm_dgrad")
 
 
+def block_weights(linears):
+    """Whether a step quantizes all of its weights in one call: the dense
+    linears of a transformer block (all weights are known when a step
+    starts)."""
+    return len(linears) > 1 and all(L.offsets is None and L.w.dim() == 2 for L in linears)
+
+
 def run_step(linears, i, t=None, vanilla=False, shared=False):
-    for L in linears:
-        run_linear(L, i, t, vanilla, shared)
+    wq = [None] * len(linears)
+    if block_weights(linears):
+        # both copies of every weight of the block in two launches
+        if t:
+            t.start("block/wquant")
+        wq = av.averis_quant_pair_multi([L.w for L in linears], rnd=av.RN,
+                                        ws=linears[0].ws["qm"])
+        if t:
+            t.stop("block/wquant")
+    for L, w in zip(linears, wq):
+        run_linear(L, i, t, vanilla, shared, w)
 
 
 _SLEEP_CYCLES_PER_MS = None
@@ -407,7 +429,8 @@ def measure(cfg, linears, steps, warmup):
         rec = {}
         for arm, t in (("averis", ta), ("vanilla", tv)):
             r = {k: stats(t.ms(L.name + "/" + k))
-                 for k in ("wquant", "split_x", "gemm_fwd", "split_d", "gemm_dgrad")}
+                 for k in ("wquant", "split_x", "gemm_fwd", "split_d", "gemm_dgrad")
+                 if t.ms(L.name + "/" + k)}
             for k, v in r.items():
                 tot[arm][k] = tot[arm].get(k, 0.0) + v["ms"]
             rec[arm] = r
@@ -430,6 +453,9 @@ def measure(cfg, linears, steps, warmup):
                              vanilla_fwd=L.flops() / (v["gemm_fwd"]["ms"] * 1e-3) / 1e12,
                              vanilla_dgrad=L.flops() / (v["gemm_dgrad"]["ms"] * 1e-3) / 1e12),
             overhead_pct=dict(fwd=100 * (fa / fv - 1), dgrad=100 * (ba / bv - 1)))
+    for arm, t in (("averis", ta), ("vanilla", tv)):
+        if t.ms("block/wquant"):
+            tot[arm]["wquant"] = stats(t.ms("block/wquant"))["ms"]
     sq_x = sum(L.l * L.m for L in linears) * SQ_BYTES_PER_ELEM
     sq_d = sum(L.l * L.n for L in linears) * SQ_BYTES_PER_ELEM
     A, V = tot["averis"], tot["vanilla"]
@@ -455,6 +481,8 @@ def measure(cfg, linears, steps, warmup):
                   tflops=flops_step / ((A["gemm_fwd"] + A["gemm_dgrad"]) * 1e-3) / 1e12,
                   vanilla_tflops=flops_step / ((V["gemm_fwd"] + V["gemm_dgrad"]) * 1e-3) / 1e12),
         weight_quant_ms=A["wquant"],
+        weight_quant_calls="one call for all weights (averis_quant_pair_multi)"
+        if block_weights(linears) else "one call per weight (averis_quant_pair)",
         per_linear=per,
         rotating_input_copies=copies,
         sum_of_calls_ms=dict(averis=sum(A.values()), vanilla=sum(V.values())),
@@ -462,6 +490,8 @@ def measure(cfg, linears, steps, warmup):
     for s in (summary["split_quant"], summary["vanilla_quant"]):
         for v in s.values():
             v["frac_hbm"] = v["gbs"] / HBM_PEAK_GBS
+    if block_weights(linears):
+        summary["block_weight_copies"] = time_block_weight_copies(linears, steps, warmup)
     if any(L.share_src is not None for L in linears):
         # the same step with each shared input split (or quantized) once: k
         # and v reuse q's, up reuses gate's; their Averis GEMMs take the mean
@@ -603,6 +633,31 @@ def time_fused_statistics(L, steps, warmup):
                 producer_plus_split_ms={
                     "separate": ms["gemm"]["ms"] + ms["split_two_reads"]["ms"],
                     "fused": ms["gemm_with_stats"]["ms"] + ms["split_one_read"]["ms"]})
+
+
+def time_block_weight_copies(linears, steps, warmup):
+    """Both copies of every weight of a block: one averis_quant_pair_multi call
+    against one averis_quant_pair call per weight (events on the launch
+    stream, queued behind a spin kernel)."""
+    def one(t):
+        t.start("multi")
+        av.averis_quant_pair_multi([L.w for L in linears], rnd=av.RN, ws=linears[0].ws["qm"])
+        t.stop("multi")
+        t.start("per_weight")
+        for L in linears:
+            av.averis_quant_pair(L.w, rnd=av.RN, ws=L.ws["q"])
+        t.stop("per_weight")
+
+    for _ in range(warmup):
+        one(Timer())
+    torch.cuda.synchronize()
+    t = Timer()
+    hold_gpu(5.0 + 0.5 * steps)
+    for _ in range(steps):
+        one(t)
+    torch.cuda.synchronize()
+    return dict(multi_ms=float(np.median(t.ms("multi"))),
+                per_weight_calls_ms=float(np.median(t.ms("per_weight"))))
 
 
 def time_weight_copies(L, steps, warmup):

@@ -82,7 +82,8 @@ typedef enum {
   AVERIS_OP_SPLIT_QUANT = 0,  /* rows, cols, nseg (nseg = 0: not grouped)     */
   AVERIS_OP_QUANT = 1,        /* rows, cols, nseg (batch for batched quant)   */
   AVERIS_OP_GEMM = 2,         /* rows = M, cols = K, n = N, nseg              */
-  AVERIS_OP_WGRAD = 3         /* rows = m, cols = l (tokens), n               */
+  AVERIS_OP_WGRAD = 3,        /* rows = m, cols = l (tokens), n               */
+  AVERIS_OP_QUANT_PAIR_MULTI = 4  /* n = number of weights (rows, cols unused) */
 } averis_op_t;
 
 /* An NVFP4-style tensor of rows x cols logical elements, 16-blocks along
@@ -209,6 +210,37 @@ averis_status_t averis_quant_pair_2d(const void* a, averis_dtype_t dtype, int ba
                                      uint64_t seed, averis_round_t rnd, uint32_t sr_stream,
                                      const averis_nvfp4_t* out, const averis_nvfp4_t* out_t,
                                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* One weight of averis_quant_pair_multi: the stored rows x cols matrix W at
+ * a (device, row stride lda elements), its seed and its two outputs (host
+ * pointers to descriptors of device buffers): out = Q4(W), rows x cols, and
+ * out_t = Q4(W^T), cols x rows, as averis_quant_pair writes them with
+ * batch 1. */
+typedef struct {
+  const void* a;
+  int64_t rows;
+  int64_t cols;
+  int64_t lda;
+  uint64_t seed;
+  const averis_nvfp4_t* out;
+  const averis_nvfp4_t* out_t;
+} averis_weight_t;
+
+#define AVERIS_MAX_WEIGHTS 16
+
+/* Both quantized copies of each of n weights of their own shapes (Lighthouse
+ * §2.2, as averis_quant_pair; e.g. the seven linears of a transformer block,
+ * all known when a step starts) in two launches instead of two per weight.
+ * For every i the codes, scales and tensor scales are those of
+ * averis_quant_pair(w[i].a, dtype, 1, w[i].rows, w[i].cols, w[i].lda, 0,
+ * w[i].seed, rnd, sr_stream, w[i].out, w[i].out_t, ...), bit for bit.
+ * w: host array of n entries (1 <= n <= AVERIS_MAX_WEIGHTS), read during the
+ * call only; every entry must meet averis_quant_pair's requirements (else
+ * that call's status, nothing launched).  The outputs of different entries
+ * must not overlap.  Workspace: AVERIS_OP_QUANT_PAIR_MULTI with n. */
+averis_status_t averis_quant_pair_multi(int n, const averis_weight_t* w, averis_dtype_t dtype,
+                                        averis_round_t rnd, uint32_t sr_stream, void* ws,
+                                        size_t ws_bytes, hipStream_t stream);
 
 /* Grouped plain quant of activations: one tensor scale per segment
  * (vanilla arm of the grouped case).  Workspace: AVERIS_OP_QUANT with nseg. */

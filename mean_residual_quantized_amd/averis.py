@@ -21,13 +21,15 @@ STATUS_NAMES = {0: "OK", 1: "E_NULL", 2: "E_SHAPE", 3: "E_DTYPE", 4: "E_ALIGN",
                 5: "E_WORKSPACE", 6: "E_ARG", 7: "E_HIP"}
 F32, BF16 = 0, 1
 RN, SR = 0, 1
-OP_SPLIT_QUANT, OP_QUANT, OP_GEMM, OP_WGRAD = 0, 1, 2, 3
+OP_SPLIT_QUANT, OP_QUANT, OP_GEMM, OP_WGRAD, OP_QUANT_PAIR_MULTI = 0, 1, 2, 3, 4
+MAX_WEIGHTS = 16
 STREAM_ACT, STREAM_MEAN, STREAM_WEIGHT, STREAM_RESIDUAL_T = 0, 1, 2, 3
 
 # every symbol include/averis.h declares
 EXPORTS = [
     "averis_split_quant", "averis_split_quant_grouped", "averis_quant", "averis_quant_batched",
-    "averis_quant_grouped", "averis_quant_pair", "averis_quant_pair_2d", "averis_gemm_fwd", "averis_gemm_dgrad",
+    "averis_quant_grouped", "averis_quant_pair", "averis_quant_pair_2d",
+    "averis_quant_pair_multi", "averis_gemm_fwd", "averis_gemm_dgrad",
     "averis_gemm_vanilla", "averis_gemm_grouped", "averis_residual_t_quant", "averis_gemm_wgrad",
     "averis_split_quant_ratio", "averis_split_quant_rank1", "averis_gemm_rank1",
     "averis_split_quant_grouped_rank1", "averis_gemm_grouped_rank1",
@@ -46,6 +48,12 @@ class AverisError(RuntimeError):
 class _NVFP4(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("tscale", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class _Weight(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("lda", ctypes.c_int64), ("seed", ctypes.c_uint64),
+                ("out", ctypes.POINTER(_NVFP4)), ("out_t", ctypes.POINTER(_NVFP4))]
 
 
 _lib = None
@@ -70,6 +78,7 @@ def lib():
             "averis_quant_grouped": [P, I, I64, I64, I64, P, I, U64, I, U32, T, P, SZ, P],
             "averis_quant_pair": [P, I, I, I64, I64, I64, I64, U64, I, U32, T, T, P, SZ, P],
             "averis_quant_pair_2d": [P, I, I, I64, I64, I64, I64, U64, I, U32, T, T, P, SZ, P],
+            "averis_quant_pair_multi": [I, P, I, I, U32, P, SZ, P],
             "averis_gemm_fwd": [T, T, T, P, I, I64, P, SZ, P],
             "averis_gemm_dgrad": [T, T, T, P, I, I64, P, SZ, P],
             "averis_gemm_vanilla": [T, T, P, I, I64, P, SZ, P],
@@ -263,6 +272,39 @@ def averis_quant_pair(w, seed=0, rnd=RN, sr_stream=STREAM_WEIGHT, ws=None):
         a.data_ptr(), _dtype_code(a), batch, rows, cols, a.stride(1), a.stride(0), seed, rnd,
         sr_stream, ctypes.byref(o), ctypes.byref(ot), ws.data_ptr(), ws.numel(), _stream()))
     return wt, wd
+
+
+def averis_quant_pair_multi(ws_list, seeds=None, rnd=RN, sr_stream=STREAM_WEIGHT, ws=None):
+    """Both quantized copies of several 2-D weights (one dtype, shapes of their
+    own) in two launches: returns [(wt, wd), ...] in order, each as
+    averis_quant_pair(w, seed) returns it."""
+    n = len(ws_list)
+    if not 1 <= n <= MAX_WEIGHTS:
+        raise ValueError("expected 1 .. %d weights" % MAX_WEIGHTS)
+    seeds = [0] * n if seeds is None else list(seeds)
+    dev = ws_list[0].device
+    dt = _dtype_code(ws_list[0])
+    outs, keep = [], []
+    arr = (_Weight * n)()
+    for i, w in enumerate(ws_list):
+        if w.dim() != 2 or w.stride(1) != 1:
+            raise ValueError("expected 2-D weights with unit innermost stride")
+        if _dtype_code(w) != dt:
+            raise ValueError("expected weights of one dtype")
+        rows, cols = w.shape
+        wd = NVFP4.empty(rows, cols, 1, dev)
+        wt = NVFP4.empty(cols, rows, 1, dev)
+        o, ot = wd.c(), wt.c()
+        keep += [o, ot]
+        arr[i] = _Weight(w.data_ptr(), rows, cols, w.stride(0), seeds[i],
+                         ctypes.pointer(o), ctypes.pointer(ot))
+        outs.append((wt, wd))
+    need = workspace_bytes(OP_QUANT_PAIR_MULTI, 0, 0, n)
+    ws = ws if ws is not None else _workspace(need, dev)
+    _check("averis_quant_pair_multi", lib().averis_quant_pair_multi(
+        n, ctypes.cast(arr, ctypes.c_void_p), dt, rnd, sr_stream, ws.data_ptr(), ws.numel(),
+        _stream()))
+    return outs
 
 
 def averis_quant_pair_2d(w, seed=0, rnd=RN, sr_stream=STREAM_WEIGHT, ws=None):

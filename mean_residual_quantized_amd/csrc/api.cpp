@@ -132,6 +132,8 @@ size_t batched_ws_bytes(int64_t, int64_t, int batch) {
 extern "C" {
 
 size_t averis_workspace_bytes(averis_op_t op, int64_t rows, int64_t cols, int64_t n, int64_t nseg) {
+  if (op == AVERIS_OP_QUANT_PAIR_MULTI)
+    return (n >= 1 && n <= kMaxWeights) ? (size_t)n * kAmaxBlocks * sizeof(float) : 0;
   if (op == AVERIS_OP_WGRAD) {
     // cols = l may be 0 (no tokens)
     if (rows < 0 || cols < 0 || cols % 16 != 0 || n < 0) return 0;
@@ -150,6 +152,7 @@ size_t averis_workspace_bytes(averis_op_t op, int64_t rows, int64_t cols, int64_
       if (n < 0) return 0;
       return gemm_ws_bytes(n, cols, (int)nseg);
     case AVERIS_OP_WGRAD:
+    case AVERIS_OP_QUANT_PAIR_MULTI:
       break;
   }
   return 0;
@@ -436,6 +439,39 @@ averis_status_t averis_quant_pair_2d(const void* a, averis_dtype_t dtype, int ba
                                      void* ws, size_t ws_bytes, hipStream_t stream) {
   return pair_common(true, a, dtype, batch, rows, cols, lda, batch_stride, seed, rnd, sr_stream,
                      out, out_t, ws, ws_bytes, stream);
+}
+
+static_assert(AVERIS_MAX_WEIGHTS == kMaxWeights, "weights per multi-weight call");
+
+averis_status_t averis_quant_pair_multi(int n, const averis_weight_t* w, averis_dtype_t dtype,
+                                        averis_round_t rnd, uint32_t sr_stream, void* ws,
+                                        size_t ws_bytes, hipStream_t stream) {
+  if (!w) return AVERIS_E_NULL;
+  if (n < 1 || n > kMaxWeights) return AVERIS_E_ARG;
+  if (!dtype_ok(dtype)) return AVERIS_E_DTYPE;
+  if (rnd != AVERIS_RN && rnd != AVERIS_SR) return AVERIS_E_ARG;
+  if (sr_stream > 0xFFFFu) return AVERIS_E_ARG;
+  const size_t es = elem_size(dtype);
+  WeightPair wp[kMaxWeights];
+  for (int i = 0; i < n; ++i) {
+    const averis_weight_t& e = w[i];
+    if (e.rows <= 0 || e.cols <= 0 || e.rows % 16 != 0 || e.cols % 16 != 0)
+      return AVERIS_E_SHAPE;
+    if (e.lda < e.cols) return AVERIS_E_SHAPE;
+    if (!e.a) return AVERIS_E_NULL;
+    if (!aligned(e.a, 16) || ((size_t)e.lda * es) % 16 != 0) return AVERIS_E_ALIGN;
+    averis_status_t s = check_tensor(e.out, e.rows, e.cols);
+    if (s != AVERIS_OK) return s;
+    if ((s = check_tensor(e.out_t, e.cols, e.rows)) != AVERIS_OK) return s;
+    wp[i] = WeightPair{e.a, e.rows, e.cols, e.lda, e.seed,
+                       QuantOut{e.out->codes, e.out->scales, e.out->tscale},
+                       QuantOut{e.out_t->codes, e.out_t->scales, e.out_t->tscale}};
+  }
+  const size_t need = (size_t)n * kAmaxBlocks * sizeof(float);
+  if (!ws || ws_bytes < need) return AVERIS_E_WORKSPACE;
+  if (!aligned(ws, 256)) return AVERIS_E_ALIGN;
+  return hip_status(launch_quant_pair_multi(n, wp, dtype == AVERIS_BF16, rnd == AVERIS_SR,
+                                            sr_stream, static_cast<float*>(ws), stream));
 }
 
 static averis_status_t gemm_common(const averis_nvfp4_t* a, const averis_nvfp4_t* mean,

@@ -89,6 +89,18 @@ hipError_t launch_quant_pair(const void* a, bool bf16, int batch, int64_t rows, 
                              int64_t lda, int64_t bstride, bool sr, uint64_t seed,
                              uint32_t stream_id, const QuantOut& out, const QuantOut& out_t,
                              float* part, hipStream_t st);
+// Both copies (as launch_quant_pair with batch 1) of each of n <= kMaxWeights
+// stored matrices of their own shapes, in one amax and one pair launch;
+// part: n x kAmaxBlocks floats.
+constexpr int kMaxWeights = 16;
+struct WeightPair {
+  const void* a;
+  int64_t rows, cols, lda;
+  uint64_t seed;
+  QuantOut out, out_t;
+};
+hipError_t launch_quant_pair_multi(int n, const WeightPair* w, bool bf16, bool sr,
+                                   uint32_t stream_id, float* part, hipStream_t st);
 hipError_t launch_quant_pair2d(const void* a, bool bf16, int batch, int64_t rows, int64_t cols,
                                int64_t lda, int64_t bstride, bool sr, uint64_t seed,
                                uint32_t stream_id, const QuantOut& out, const QuantOut& out_t,

@@ -1058,16 +1058,14 @@ __global__ __launch_bounds__(256) void k_quant_batched(const T* __restrict__ a, 
 
 // max |a| of each stored rows x cols matrix, 16-byte loads; workgroup x of
 // matrix y covers 16-byte chunks [x*per, (x+1)*per) of the row-major order
+// a thread's max |a| over the 16-byte chunks q0 + threadIdx.x, + 256, ... < q1
+// of one stored rows x cols matrix (chunk q: row q / (cols / VE))
 template <typename T>
-__global__ __launch_bounds__(256) void k_amax_vec(const T* __restrict__ a, int64_t rows,
-                                                  int64_t cols, int64_t lda, int64_t bstride,
-                                                  int64_t per, float* __restrict__ part) {
+__device__ __forceinline__ float amax_chunks(const T* base, int64_t cols, int64_t lda, int64_t q0,
+                                             int64_t q1) {
   constexpr int VE = 16 / (int)sizeof(T);   // elements per 16-byte chunk
   constexpr int U = 4;
-  const T* base = a + (int64_t)blockIdx.y * bstride;
-  const int64_t cpr = cols / VE, total = rows * cpr;
-  const int64_t q0 = (int64_t)blockIdx.x * per;
-  const int64_t q1 = q0 + per < total ? q0 + per : total;
+  const int64_t cpr = cols / VE;
   float m = 0.0f;
   for (int64_t q = q0 + threadIdx.x; q < q1; q += 256 * U) {
     uint4 w[U];
@@ -1091,6 +1089,18 @@ __global__ __launch_bounds__(256) void k_amax_vec(const T* __restrict__ a, int64
       }
     }
   }
+  return m;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_amax_vec(const T* __restrict__ a, int64_t rows,
+                                                  int64_t cols, int64_t lda, int64_t bstride,
+                                                  int64_t per, float* __restrict__ part) {
+  constexpr int VE = 16 / (int)sizeof(T);
+  const int64_t total = rows * (cols / VE);
+  const int64_t q0 = (int64_t)blockIdx.x * per;
+  const int64_t q1 = q0 + per < total ? q0 + per : total;
+  float m = amax_chunks<T>(a + (int64_t)blockIdx.y * bstride, cols, lda, q0, q1);
   __shared__ float red[4];
   m = block_max(m, red);
   if (threadIdx.x == 0) part[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = m;
@@ -1101,18 +1111,19 @@ __global__ __launch_bounds__(256) void k_amax_vec(const T* __restrict__ a, int64
 constexpr int kPairTile = 64;
 constexpr int kPairLd = kPairTile + 4;   // padded LDS row (floats), 16-byte aligned
 
+// the 64 x 64 tile at (r0, c0) of the stored rows x cols matrix W_b at base:
+// global rows of out and out_t from matrix index bt; the tensor scale from
+// W_b's npart amax partials at part (written by the tile at (0, 0))
 template <typename T, bool SR>
-__global__ __launch_bounds__(256) void k_pair(const T* __restrict__ a, int64_t rows, int64_t cols,
-                                              int64_t lda, int64_t bstride, uint64_t seed,
-                                              uint32_t stream, const float* __restrict__ part,
-                                              int64_t npart, QuantOut out, QuantOut out_t) {
+__device__ __forceinline__ void pair_tile(const T* __restrict__ base, int64_t rows, int64_t cols,
+                                          int64_t lda, int bt, int64_t r0, int64_t c0,
+                                          uint64_t seed, uint32_t stream,
+                                          const float* __restrict__ part, int64_t npart,
+                                          const QuantOut& out, const QuantOut& out_t) {
   constexpr int VE = 16 / (int)sizeof(T);
   constexpr int NCH = kPairTile / VE;              // 16-byte chunks per tile row
   constexpr int PER = kPairTile * NCH / 256;       // chunks per thread
   __shared__ float tile[kPairTile][kPairLd];
-  const int bt = blockIdx.z;
-  const int64_t r0 = (int64_t)blockIdx.y * kPairTile, c0 = (int64_t)blockIdx.x * kPairTile;
-  const T* base = a + (int64_t)bt * bstride;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -1138,10 +1149,10 @@ __global__ __launch_bounds__(256) void k_pair(const T* __restrict__ a, int64_t r
   }
   // the tensor scale (reduce_partials synchronizes the block, which also
   // publishes the tile)
-  const float am = reduce_partials(part + (int64_t)bt * npart, npart);
+  const float am = reduce_partials(part, npart);
   float s_enc, s_dec;
   tensor_scales(am, s_enc, s_dec);
-  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
+  if (r0 == 0 && c0 == 0 && tid == 0) {
     out.tscale[2 * bt] = s_enc;
     out.tscale[2 * bt + 1] = s_dec;
     out_t.tscale[2 * bt] = s_enc;
@@ -1174,6 +1185,70 @@ __global__ __launch_bounds__(256) void k_pair(const T* __restrict__ a, int64_t r
                         out_t.scales + grow * (rows >> 4) + (r >> 4));
     }
   }
+}
+
+template <typename T, bool SR>
+__global__ __launch_bounds__(256) void k_pair(const T* __restrict__ a, int64_t rows, int64_t cols,
+                                              int64_t lda, int64_t bstride, uint64_t seed,
+                                              uint32_t stream, const float* __restrict__ part,
+                                              int64_t npart, QuantOut out, QuantOut out_t) {
+  const int bt = blockIdx.z;
+  pair_tile<T, SR>(a + (int64_t)bt * bstride, rows, cols, lda, bt,
+                   (int64_t)blockIdx.y * kPairTile, (int64_t)blockIdx.x * kPairTile, seed, stream,
+                   part + (int64_t)bt * npart, npart, out, out_t);
+}
+
+// ---------------------------------------------------------------------------
+// Both copies of several weights of different shapes in two launches, one
+// grid over all of them for each pass, weight i owning a contiguous range of
+// the workgroups (the ranges' ends in the argument block; each workgroup
+// finds its weight by a uniform scan).  Per weight the same partials (a
+// partition of the same maximum) and the same tile code as k_amax_vec and
+// k_pair, so the bits are those of the single-weight launches.
+// ---------------------------------------------------------------------------
+struct PairMultiArgs {
+  WeightPair w[kMaxWeights];
+  int64_t per[kMaxWeights];        // amax pass: 16-byte chunks per workgroup
+  int64_t nblk[kMaxWeights];       // amax pass: workgroups (= partials)
+  int64_t amax_end[kMaxWeights];   // amax pass: workgroups through weight i
+  int64_t tiles_x[kMaxWeights];    // pair pass: 64 x 64 tiles across the columns
+  int64_t tile_end[kMaxWeights];   // pair pass: tiles through weight i
+  int n;
+};
+
+__device__ __forceinline__ int find_weight(const int64_t* end, int n, int64_t bid) {
+  int i = 0;
+  while (i + 1 < n && bid >= end[i]) ++i;
+  return i;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_amax_multi(PairMultiArgs args, float* __restrict__ part) {
+  constexpr int VE = 16 / (int)sizeof(T);
+  const int64_t bid = blockIdx.x;
+  const int i = find_weight(args.amax_end, args.n, bid);
+  const WeightPair& w = args.w[i];
+  const int64_t blk = bid - (i > 0 ? args.amax_end[i - 1] : 0);
+  const int64_t total = w.rows * (w.cols / VE);
+  const int64_t q0 = blk * args.per[i];
+  const int64_t q1 = q0 + args.per[i] < total ? q0 + args.per[i] : total;
+  float m = amax_chunks<T>(static_cast<const T*>(w.a), w.cols, w.lda, q0, q1);
+  __shared__ float red[4];
+  m = block_max(m, red);
+  if (threadIdx.x == 0) part[(int64_t)i * kAmaxBlocks + blk] = m;
+}
+
+template <typename T, bool SR>
+__global__ __launch_bounds__(256) void k_pair_multi(PairMultiArgs args, uint32_t stream,
+                                                    const float* __restrict__ part) {
+  const int64_t bid = blockIdx.x;
+  const int i = find_weight(args.tile_end, args.n, bid);
+  const WeightPair& w = args.w[i];
+  const int64_t t = bid - (i > 0 ? args.tile_end[i - 1] : 0);
+  const int64_t ty = t / args.tiles_x[i], tx = t - ty * args.tiles_x[i];
+  pair_tile<T, SR>(static_cast<const T*>(w.a), w.rows, w.cols, w.lda, 0, ty * kPairTile,
+                   tx * kPairTile, w.seed, stream, part + (int64_t)i * kAmaxBlocks, args.nblk[i],
+                   w.out, w.out_t);
 }
 
 // ---------------------------------------------------------------------------
@@ -1626,6 +1701,42 @@ hipError_t launch_quant_pair(const void* a, bool bf16, int batch, int64_t rows, 
                               part, st);
   return run_pair<float>(a, batch, rows, cols, lda, bstride, sr, seed, stream_id, out, out_t, part,
                          st);
+}
+
+template <typename T>
+static hipError_t run_pair_multi(int n, const WeightPair* w, bool sr, uint32_t stream_id,
+                                 float* part, hipStream_t st) {
+  constexpr int64_t VE = 16 / (int64_t)sizeof(T);
+  PairMultiArgs args{};
+  args.n = n;
+  int64_t amax_wgs = 0, tiles = 0;
+  for (int i = 0; i < n; ++i) {
+    args.w[i] = w[i];
+    // the single-weight launch's partition of the amax pass
+    const int64_t total = w[i].rows * (w[i].cols / VE);
+    int64_t nblk = (total + 256 * 4 - 1) / (256 * 4);
+    if (nblk > kAmaxBlocks) nblk = kAmaxBlocks;
+    if (nblk < 1) nblk = 1;
+    args.per[i] = (total + nblk - 1) / nblk;
+    args.nblk[i] = nblk;
+    amax_wgs += nblk;
+    args.amax_end[i] = amax_wgs;
+    args.tiles_x[i] = (w[i].cols + kPairTile - 1) / kPairTile;
+    tiles += args.tiles_x[i] * ((w[i].rows + kPairTile - 1) / kPairTile);
+    args.tile_end[i] = tiles;
+  }
+  k_amax_multi<T><<<(unsigned)amax_wgs, 256, 0, st>>>(args, part);
+  if (sr)
+    k_pair_multi<T, true><<<(unsigned)tiles, 256, 0, st>>>(args, stream_id, part);
+  else
+    k_pair_multi<T, false><<<(unsigned)tiles, 256, 0, st>>>(args, stream_id, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_pair_multi(int n, const WeightPair* w, bool bf16, bool sr,
+                                   uint32_t stream_id, float* part, hipStream_t st) {
+  if (bf16) return run_pair_multi<uint16_t>(n, w, sr, stream_id, part, st);
+  return run_pair_multi<float>(n, w, sr, stream_id, part, st);
 }
 
 template <typename T>

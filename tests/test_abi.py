@@ -49,6 +49,9 @@ def test_workspace_queries(L):
     assert wb(av.OP_GEMM, 8192, 1024, 3072) >= 3072 * 4
     assert wb(av.OP_GEMM, 8192, 1024, 3072, 64) >= 64 * 3072 * 4
     assert wb(av.OP_QUANT, 64, 128, 0, 8) > 0
+    assert wb(av.OP_QUANT_PAIR_MULTI, 0, 0, 7) == 7 * 1024 * 4
+    assert wb(av.OP_QUANT_PAIR_MULTI, 0, 0, 0) == 0
+    assert wb(av.OP_QUANT_PAIR_MULTI, 0, 0, av.MAX_WEIGHTS + 1) == 0
     # grows with the grouped segment count
     assert wb(av.OP_SPLIT_QUANT, 4096, 256, 0, 64) > wb(av.OP_SPLIT_QUANT, 4096, 256, 0, 1)
 
@@ -233,6 +236,41 @@ def test_quant_pair_2d_rejections(L):
     assert qp(out=nv(64, 128)) == 2
     assert qp(ws=None) == 5
     assert qp(wsb=64) == 5
+
+
+def test_quant_pair_multi_rejections(L):
+    outs = [(nv(64, 128), nv(128, 64)), (nv(32, 48), nv(48, 32))]
+
+    def qm(n=2, dt=av.BF16, rnd=av.RN, stream=2, ws=P, wsb=1 << 20, **bad):
+        arr = (av._Weight * 2)()
+        for i, (rows, cols) in enumerate(((64, 128), (32, 48))):
+            o, ot = outs[i]
+            e = dict(a=P, rows=rows, cols=cols, lda=cols, out=ctypes.pointer(o),
+                     out_t=ctypes.pointer(ot))
+            if i == 1:
+                e.update(bad)
+            arr[i] = av._Weight(e["a"], e["rows"], e["cols"], e["lda"], 0, e["out"], e["out_t"])
+        return L.averis_quant_pair_multi(n, ctypes.cast(arr, ctypes.c_void_p), dt, rnd, stream,
+                                         ws, wsb, None)
+    assert L.averis_quant_pair_multi(2, None, av.BF16, av.RN, 2, P, 1 << 20, None) == 1
+    assert qm(n=0) == 6
+    assert qm(n=17) == 6                                  # AVERIS_MAX_WEIGHTS
+    assert qm(dt=5) == 3
+    assert qm(rnd=3) == 6
+    assert qm(stream=1 << 16) == 6
+    # any entry's fault rejects the whole call (the second one here)
+    assert qm(rows=40) == 2                               # rows % 16
+    assert qm(cols=24, lda=24) == 2
+    assert qm(lda=16) == 2                                # lda < cols
+    assert qm(a=None) == 1
+    assert qm(a=P + 4) == 4
+    assert qm(lda=52) == 4                                # 16-byte rows
+    assert qm(out=ctypes.pointer(nv(32, 64))) == 2        # out is rows x cols
+    assert qm(out_t=ctypes.pointer(nv(32, 48))) == 2      # out_t is cols x rows
+    assert qm(out=None) == 1
+    assert qm(ws=None) == 5
+    assert qm(wsb=2 * 1024 * 4 - 4) == 5                  # n x 1024 floats
+    assert qm(ws=P + 16) == 4
 
 
 def test_wgrad_rejections(L):

@@ -83,3 +83,47 @@ def test_zero_weight():
     for q in (wt, wd):
         assert not q.codes.any() and not q.scales.any()
         assert q.tscale.tolist() == [1.0, 1.0]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("rnd", ["rn", "sr"])
+def test_multi_weight_call_matches_oracle_and_single_calls(dtype, rnd):
+    """averis_quant_pair_multi: each weight's two copies equal the oracle's and
+    averis_quant_pair's with that weight's seed, over shapes of their own
+    (ragged 64 x 64 tiles, one weight with a row stride above its width)."""
+    rng = np.random.default_rng(5)
+    r = av.RN if rnd == "rn" else av.SR
+    shapes = [(304, 208), (16, 16), (80, 1040), (2000, 48), (128, 96)]
+    ws_cpu = [torch.from_numpy((rng.standard_normal(s) * 0.05 * (i + 1)).astype(np.float32))
+              .to(dtype) for i, s in enumerate(shapes)]
+    wg = [w.cuda() for w in ws_cpu]
+    wide = torch.zeros((128, 96 + 32), dtype=dtype, device="cuda")
+    wide[:, :96] = wg[4]
+    wg[4] = wide[:, :96]                         # row stride 128
+    seeds = [3, 11, 0, 7, 2 ** 40 + 5]
+    outs = av.averis_quant_pair_multi(wg, seeds=seeds, rnd=r)
+    for i, (w, (wt, wd)) in enumerate(zip(wg, outs)):
+        ref = orc.weight_quant(ws_cpu[i].float().numpy(), rnd, seeds[i])
+        same(wt, ref["fwd"])
+        same(wd, ref["dgrad"])
+        st, sd = av.averis_quant_pair(w, seed=seeds[i], rnd=r)
+        same_gpu(wt, st)
+        same_gpu(wd, sd)
+
+
+def test_multi_weight_call_block_shapes_and_repeat():
+    """The seven Qwen3-0.6B-like weights in one call, twice in a row (the
+    workspace's partials are rewritten, not accumulated), against the
+    single-weight calls; one zero weight among them."""
+    shapes = [(1024, 2048), (1024, 1024), (1024, 1024), (2048, 1024), (1024, 3072),
+              (1024, 3072), (3072, 1024)]
+    g = torch.Generator(device="cuda").manual_seed(1)
+    wg = [(torch.randn(s, generator=g, device="cuda") * 0.02).to(torch.bfloat16) for s in shapes]
+    wg[2].zero_()
+    for _ in range(2):
+        outs = av.averis_quant_pair_multi(wg, rnd=av.SR, seeds=list(range(7)))
+        for i, w in enumerate(wg):
+            st, sd = av.averis_quant_pair(w, seed=i, rnd=av.SR)
+            same_gpu(outs[i][0], st)
+            same_gpu(outs[i][1], sd)
+    assert outs[2][0].tscale.tolist() == [1.0, 1.0]
