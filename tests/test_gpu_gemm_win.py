@@ -129,3 +129,43 @@ def test_repeat_is_bitwise_and_matches_a_fresh_output_buffer():
     av.averis_gemm_rank1(a, rho, b, out_dtype=torch.bfloat16, out=c1)
     av.averis_gemm_rank1(a, rho, b, out_dtype=torch.bfloat16, out=c2)
     assert torch.equal(c1, c2)
+
+
+# more tiles than CUs (two or more rounds of workgroups), bf16 output: full
+# 256 x 256 tiles, ragged rows and columns at another tile width, and an
+# output row stride that rules out 16-byte stores
+ROUND_SHAPES = {
+    "full": (16384, 2048, 256, 0),
+    "ragged": (16400, 1040, 512, 0),
+    "strided": (8448, 2048, 256, 4),
+}
+
+
+@pytest.mark.parametrize("case", list(ROUND_SHAPES))
+def test_multi_round_bf16(case):
+    m, n, k, pad = ROUND_SHAPES[case]
+    print("%s: m %d n %d k %d ldc %d" % (case, m, n, k, n + pad), flush=True)
+    g = np.random.default_rng(17)
+    sa, sb = 0.6875, 1.4375
+    a, ac, asc = operand(g, m, k, sa)
+    b, bc, bsc = operand(g, n, k, sb)
+    qa, qb = q(ac, asc, sa), q(bc, bsc, sb)
+    rho = torch.from_numpy(g.standard_normal(n).astype(np.float32) * 4.0)
+    rho64 = rho.numpy().astype(np.float64)
+    ab = orc.gemm(qa, qb)
+    ab_bound = orc.gemm_abs_bound(qa, qb)
+    buf = torch.full((m, n + pad), float("nan"), dtype=torch.bfloat16, device="cuda")
+    c = buf[:, :n]
+    av.averis_gemm_rank1(a, rho.cuda(), b, out_dtype=torch.bfloat16, out=c)
+    assert_gemm_close(c, ab + rho64[None, :], ab_bound + np.abs(rho64)[None, :], bf16=True,
+                      label="%s rank1" % case)
+    # the fp32 output holds the same values before rounding: the bf16 output
+    # is their round-to-nearest-even, bit for bit
+    c32 = av.averis_gemm_rank1(a, rho.cuda(), b, out_dtype=torch.float32)
+    assert torch.equal(c, c32.to(torch.bfloat16))
+    if pad:
+        assert torch.isnan(buf[:, n:].float()).all()     # nothing past the row
+    cv = av.averis_gemm_vanilla(a, b, out_dtype=torch.bfloat16)
+    assert_gemm_close(cv, ab, ab_bound, bf16=True, label="%s vanilla" % case)
+    assert torch.equal(cv, av.averis_gemm_vanilla(a, b, out_dtype=torch.float32).to(torch.bfloat16))
+    torch.cuda.synchronize()
