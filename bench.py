@@ -105,7 +105,9 @@ class Linear:
         # v take q's, up takes gate's): with --shared-input-steps its split is
         # reused, not recomputed
         self.share_src = None
+        self.dependents = []   # the linears that take this one's input
         self.last_split = None
+        self.cur_w = None      # this step's two weight copies
         ns = 0 if offsets is None else self.nseg
         l, m, n = self.l, self.m, self.n
         wm, wn = (self.w.shape[1], self.w.shape[2]) if self.w.dim() == 3 else self.w.shape
@@ -157,6 +159,7 @@ def make_linears(cfg):
     by_name = {L.name: L for L in out}
     for dst, src in SHARED_INPUTS.items():
         by_name[dst].share_src = by_name[src]
+        by_name[src].dependents.append(by_name[dst])
     out[0].ws["qm"] = torch.empty(av.workspace_bytes(av.OP_QUANT_PAIR_MULTI, 0, 0, len(out)),
                                   dtype=torch.uint8, device="cuda")
     return out
@@ -194,8 +197,9 @@ def run_linear(L, i, t, vanilla, shared=False, wq=None):
     """One linear's forward + dgrad with input copy i.  shared: a linear
     whose input is another's (L.share_src) reuses that linear's split (or
     plain quant) of it from the same step; the Averis GEMM then takes the
-    mean and forms its own rank-one row (averis_gemm_fwd).  wq: both copies
-    of the weight, when the step quantized all weights at once."""
+    rank-one row the source's split formed for it
+    (averis_split_quant_rank1_multi).  wq: both copies of the weight, when
+    the step quantized all weights at once."""
     def tic(k):
         if t:
             t.start(L.name + "/" + k)
@@ -215,7 +219,7 @@ def run_linear(L, i, t, vanilla, shared=False, wq=None):
         xr, xmean = L.share_src.last_split
         tic("gemm_fwd")
         if not vanilla:
-            av.averis_gemm_fwd(xr, xmean, wt, out_dtype=torch.bfloat16, out=ws["y"], ws=ws["g"])
+            av.averis_gemm_rank1(xr, ws["rho_x"], wt, out_dtype=torch.bfloat16, out=ws["y"])
         else:
             av.averis_gemm_vanilla(xr, wt, out_dtype=torch.bfloat16, out=ws["y"], ws=ws["g"])
         toc("gemm_fwd")
@@ -224,10 +228,18 @@ def run_linear(L, i, t, vanilla, shared=False, wq=None):
     if L.offsets is None:
         if not vanilla:
             # the split also forms the rank-one row 1 (mean W) for the GEMM
-            # that takes it, so the GEMM adds it without a mean row of its own
+            # that takes it (and, with shared inputs, for the GEMMs of the
+            # linears that read the same input), so no GEMM adds a mean row
             tic("split_x")
-            xr, xmean, _, rho_x = av.averis_split_quant_rank1(x, wt, seed=0, ws=ws["sq_x"],
-                                                              rho=ws["rho_x"])
+            deps = L.dependents if shared else []
+            if deps:
+                xr, xmean, _, _ = av.averis_split_quant_rank1_multi(
+                    x, [wt] + [D.cur_w[0] for D in deps], seed=0, ws=ws["sq_x"],
+                    rhos=[ws["rho_x"]] + [D.ws["rho_x"] for D in deps])
+                rho_x = ws["rho_x"]
+            else:
+                xr, xmean, _, rho_x = av.averis_split_quant_rank1(x, wt, seed=0, ws=ws["sq_x"],
+                                                                  rho=ws["rho_x"])
             toc("split_x")
             L.last_split = (xr, xmean)
             tic("gemm_fwd")
@@ -312,6 +324,8 @@ def run_step(linears, i, t=None, vanilla=False, shared=False):
                                         ws=linears[0].ws["qm"])
         if t:
             t.stop("block/wquant")
+    for L, w in zip(linears, wq):
+        L.cur_w = w
     for L, w in zip(linears, wq):
         run_linear(L, i, t, vanilla, shared, w)
 
@@ -494,8 +508,8 @@ def measure(cfg, linears, steps, warmup):
         summary["block_weight_copies"] = time_block_weight_copies(linears, steps, warmup)
     if any(L.share_src is not None for L in linears):
         # the same step with each shared input split (or quantized) once: k
-        # and v reuse q's, up reuses gate's; their Averis GEMMs take the mean
-        # and form their rank-one rows themselves
+        # and v reuse q's, up reuses gate's; the one split forms the rank-one
+        # rows of all the GEMMs that take it
         sa, _ = timed(linears, steps, warmup, vanilla=False, shared=True, per_call=False)
         sv, _ = timed(linears, steps, warmup, vanilla=True, shared=True, per_call=False)
         log("bench: config %d, shared inputs: averis %.4f | vanilla %.4f (ms/step)"

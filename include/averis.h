@@ -298,6 +298,25 @@ averis_status_t averis_gemm_rank1(const averis_nvfp4_t* a, const float* rho,
                                   const averis_nvfp4_t* b, void* c, averis_dtype_t cdtype,
                                   int64_t ldc, hipStream_t stream);
 
+/* The rank-one rows of several GEMMs that take the same split (the
+ * projections that read one input, e.g. q, k and v of a transformer block;
+ * [Lighthouse] §2.2 as above): averis_split_quant_rank1 with nb B operands
+ * (1 <= nb <= AVERIS_MAX_RANK1), b[i]->cols == cols, writing
+ *   rho[i][j] = deq(mean) . deq(b[i]_j),  j < b[i]->rows,
+ * each bit for bit the row averis_split_quant_rank1 with b[i] alone writes,
+ * and the same residual, mean and mean_f32.  b, rho: host arrays of nb
+ * pointers (descriptors of device tensors; device float[b[i]->rows], 4-byte
+ * aligned), read during the call only.  Workspace as averis_split_quant_rank1.
+ * Errors as averis_split_quant_rank1, for any entry. */
+#define AVERIS_MAX_RANK1 4
+averis_status_t averis_split_quant_rank1_multi(const void* a, averis_dtype_t dtype, int64_t rows,
+                                               int64_t cols, int64_t lda, uint64_t seed,
+                                               averis_round_t rnd, const averis_nvfp4_t* residual,
+                                               const averis_nvfp4_t* mean, float* mean_f32,
+                                               int nb, const averis_nvfp4_t* const* b,
+                                               float* const* rho, void* ws, size_t ws_bytes,
+                                               hipStream_t stream);
+
 /* Grouped forms (expert segments, as averis_split_quant_grouped and
  * averis_gemm_grouped): b holds nseg stacked N x cols matrices (expert s =
  * rows s*N .. s*N+N-1, its own tensor scale b->tscale[2s..2s+1]) and

@@ -23,6 +23,7 @@ F32, BF16 = 0, 1
 RN, SR = 0, 1
 OP_SPLIT_QUANT, OP_QUANT, OP_GEMM, OP_WGRAD, OP_QUANT_PAIR_MULTI = 0, 1, 2, 3, 4
 MAX_WEIGHTS = 16
+MAX_RANK1 = 4
 STREAM_ACT, STREAM_MEAN, STREAM_WEIGHT, STREAM_RESIDUAL_T = 0, 1, 2, 3
 
 # every symbol include/averis.h declares
@@ -31,7 +32,8 @@ EXPORTS = [
     "averis_quant_grouped", "averis_quant_pair", "averis_quant_pair_2d",
     "averis_quant_pair_multi", "averis_gemm_fwd", "averis_gemm_dgrad",
     "averis_gemm_vanilla", "averis_gemm_grouped", "averis_residual_t_quant", "averis_gemm_wgrad",
-    "averis_split_quant_ratio", "averis_split_quant_rank1", "averis_gemm_rank1",
+    "averis_split_quant_ratio", "averis_split_quant_rank1", "averis_split_quant_rank1_multi",
+    "averis_gemm_rank1",
     "averis_split_quant_grouped_rank1", "averis_gemm_grouped_rank1",
     "averis_split_quant_noalloc", "averis_gemm_rank1_stats", "averis_split_quant_from_stats",
     "averis_workspace_bytes", "averis_status_str",
@@ -88,6 +90,8 @@ def lib():
             "averis_split_quant_ratio": [P, I, I64, I64, I64, P, I, U64, I, T, T, P, P, P, SZ, P],
             "averis_split_quant_rank1": [P, I, I64, I64, I64, U64, I, T, T, P, T, P, P, SZ, P],
             "averis_gemm_rank1": [T, P, T, P, I, I64, P],
+            "averis_split_quant_rank1_multi": [P, I, I64, I64, I64, U64, I, T, T, P, I, P, P, P,
+                                               SZ, P],
             "averis_split_quant_grouped_rank1": [P, I, I64, I64, I64, P, I, U64, I, T, T, P, T, P,
                                                  P, SZ, P],
             "averis_gemm_grouped_rank1": [T, P, T, P, I, P, I, I64, P],
@@ -451,6 +455,32 @@ def averis_split_quant_rank1(a, b, seed=0, rnd=SR, ws=None, rho=None):
         ctypes.byref(m), mu.data_ptr(), ctypes.byref(cb), rho.data_ptr(), ws.data_ptr(),
         ws.numel(), _stream()))
     return res, mean, mu, rho
+
+
+def averis_split_quant_rank1_multi(a, bs, seed=0, rnd=SR, ws=None, rhos=None):
+    """averis_split_quant plus the rank-one rows of several GEMMs that take
+    the split (B operands bs, at most MAX_RANK1); returns (residual, mean,
+    mu_f32, [rho per operand])."""
+    nb = len(bs)
+    if not 1 <= nb <= MAX_RANK1:
+        raise ValueError("expected 1 .. %d B operands" % MAX_RANK1)
+    rows, cols = a.shape
+    res = NVFP4.empty(rows, cols, 1, a.device)
+    mean = NVFP4.empty(1, cols, 1, a.device)
+    mu = torch.empty((cols,), dtype=torch.float32, device=a.device)
+    rhos = list(rhos) if rhos is not None else [
+        torch.empty((b.rows,), dtype=torch.float32, device=a.device) for b in bs]
+    need = workspace_bytes(OP_SPLIT_QUANT, rows, cols)
+    ws = ws if ws is not None else _workspace(need, a.device)
+    r, m = res.c(), mean.c()
+    cbs = [b.c() for b in bs]
+    barr = (ctypes.POINTER(_NVFP4) * nb)(*[ctypes.pointer(cb) for cb in cbs])
+    rarr = (ctypes.c_void_p * nb)(*[rho.data_ptr() for rho in rhos])
+    _check("averis_split_quant_rank1_multi", lib().averis_split_quant_rank1_multi(
+        a.data_ptr(), _dtype_code(a), rows, cols, _lda(a), seed, rnd, ctypes.byref(r),
+        ctypes.byref(m), mu.data_ptr(), nb, ctypes.cast(barr, ctypes.c_void_p),
+        ctypes.cast(rarr, ctypes.c_void_p), ws.data_ptr(), ws.numel(), _stream()))
+    return res, mean, mu, rhos
 
 
 def averis_gemm_rank1(a, rho, b, out_dtype=torch.float32, out=None):

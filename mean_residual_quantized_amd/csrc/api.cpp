@@ -251,7 +251,7 @@ static averis_status_t split_rank1_common(const void* a, averis_dtype_t dtype, i
   if (s != AVERIS_OK) return s;
   const int64_t ns = offs ? nseg : 1;
   if (b->rows <= 0 || b->rows % ns != 0) return AVERIS_E_SHAPE;
-  const Rank1Out r1{QOperand{b->codes, b->scales, b->tscale}, b->rows / ns, rho};
+  const Rank1Out r1 = rank1_one(QOperand{b->codes, b->scales, b->tscale}, b->rows / ns, rho);
   return split_common(a, dtype, rows, cols, lda, offs, nseg, seed, rnd, residual, mean, mean_f32,
                       ws, ws_bytes, stream, nullptr, &r1);
 }
@@ -264,6 +264,34 @@ averis_status_t averis_split_quant_rank1(const void* a, averis_dtype_t dtype, in
                                          size_t ws_bytes, hipStream_t stream) {
   return split_rank1_common(a, dtype, rows, cols, lda, nullptr, 1, seed, rnd, residual, mean,
                             mean_f32, b, rho, ws, ws_bytes, stream);
+}
+
+static_assert(AVERIS_MAX_RANK1 == kMaxRank1, "rank-one operands per split");
+
+averis_status_t averis_split_quant_rank1_multi(const void* a, averis_dtype_t dtype, int64_t rows,
+                                               int64_t cols, int64_t lda, uint64_t seed,
+                                               averis_round_t rnd, const averis_nvfp4_t* residual,
+                                               const averis_nvfp4_t* mean, float* mean_f32,
+                                               int nb, const averis_nvfp4_t* const* b,
+                                               float* const* rho, void* ws, size_t ws_bytes,
+                                               hipStream_t stream) {
+  if (!b || !rho) return AVERIS_E_NULL;
+  if (nb < 1 || nb > kMaxRank1) return AVERIS_E_ARG;
+  if (cols > kRank1MaxK) return AVERIS_E_SHAPE;
+  Rank1Out r1{};
+  for (int i = 0; i < nb; ++i) {
+    if (!b[i] || !rho[i]) return AVERIS_E_NULL;
+    if (!aligned(rho[i], 4)) return AVERIS_E_ALIGN;
+    const averis_status_t s = check_tensor(b[i], b[i]->rows, cols);
+    if (s != AVERIS_OK) return s;
+    if (b[i]->rows <= 0) return AVERIS_E_SHAPE;
+    r1.b[i] = QOperand{b[i]->codes, b[i]->scales, b[i]->tscale};
+    r1.n[i] = b[i]->rows;
+    r1.rho[i] = rho[i];
+  }
+  r1.count = nb;
+  return split_common(a, dtype, rows, cols, lda, nullptr, 1, seed, rnd, residual, mean, mean_f32,
+                      ws, ws_bytes, stream, nullptr, &r1);
 }
 
 averis_status_t averis_split_quant_grouped_rank1(const void* a, averis_dtype_t dtype,
@@ -611,14 +639,14 @@ averis_status_t averis_split_quant_from_stats(const void* a, int64_t rows, int64
   if ((s = check_tensor(residual, rows, cols)) != AVERIS_OK) return s;
   if ((s = check_tensor(mean, 1, cols)) != AVERIS_OK) return s;
   if (!aligned(mean_f32, 4)) return AVERIS_E_ALIGN;
-  Rank1Out r1{QOperand{nullptr, nullptr, nullptr}, 0, nullptr};
+  Rank1Out r1{};
   if (b || rho) {
     if (!b || !rho) return AVERIS_E_NULL;
     if (!aligned(rho, 4)) return AVERIS_E_ALIGN;
     if (cols > kRank1MaxK) return AVERIS_E_SHAPE;
     if ((s = check_tensor(b, b->rows, cols)) != AVERIS_OK) return s;
     if (b->rows <= 0) return AVERIS_E_SHAPE;
-    r1 = Rank1Out{QOperand{b->codes, b->scales, b->tscale}, b->rows, rho};
+    r1 = rank1_one(QOperand{b->codes, b->scales, b->tscale}, b->rows, rho);
   }
   const size_t need = split_ws_bytes(rows, cols, 1);
   if (!ws || ws_bytes < need) return AVERIS_E_WORKSPACE;

@@ -58,14 +58,25 @@ struct ColStats {
   float* pmnz;
 };
 
-// The rank-one row a split can compute for the GEMM that takes it:
-// rho[s][j] = deq(Q4(mu_s)) . deq(b_s,j) for the n rows of each segment's b
-// (b holds nseg stacked n x cols matrices).
+// The rank-one rows a split can compute for the GEMMs that take it: for
+// each of `count` B operands, rho_i[s][j] = deq(Q4(mu_s)) . deq(b_i,s,j) for
+// the n_i rows of each segment's b_i (b_i holds nseg stacked n_i x cols
+// matrices).  More than one B operand: one segment (GEMMs of one input).
+constexpr int kMaxRank1 = 4;
 struct Rank1Out {
-  QOperand b;
-  int64_t n;
-  float* rho;
+  QOperand b[kMaxRank1];
+  int64_t n[kMaxRank1];
+  float* rho[kMaxRank1];
+  int count;
 };
+inline Rank1Out rank1_one(const QOperand& b, int64_t n, float* rho) {
+  Rank1Out r{};
+  r.b[0] = b;
+  r.n[0] = n;
+  r.rho[0] = rho;
+  r.count = 1;
+  return r;
+}
 
 size_t split_ws_bytes(int64_t rows, int64_t cols, int nseg);
 SplitWs split_ws_carve(void* ws, int64_t rows, int64_t cols, int nseg);

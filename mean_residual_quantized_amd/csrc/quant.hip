@@ -756,6 +756,16 @@ __device__ __forceinline__ float reduce_partials(const float* p, int64_t n) {
   return block_max(m, red);
 }
 
+// The rank-one operands of a split as the quant kernel takes them: up to
+// kMaxRank1 B operands, operand i's workgroups ending at gend[i]
+struct Rank1Set {
+  QOperand b[kMaxRank1];
+  int64_t n[kMaxRank1];
+  float* rho[kMaxRank1];
+  int64_t gend[kMaxRank1];
+  int count;
+};
+
 // ---------------------------------------------------------------------------
 // quant: block = 64 column-blocks (1024 columns) x 4 row lanes over a chunk
 // of kQuantRows rows; blockIdx.y >= nchunk_ub quantizes segment means.
@@ -778,29 +788,34 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ a, int64_t 
                                                const double* __restrict__ tssq,
                                                const double* __restrict__ tmu2,
                                                float* __restrict__ ratio,
-                                               QOperand B, int64_t bn,
-                                               float* __restrict__ rho, int64_t rho_rows,
-                                               int r1_rows) {
+                                               Rank1Set r1s, int64_t rho_rows, int r1_rows) {
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   const int64_t nb = cols >> 4;
   const int64_t b = (int64_t)blockIdx.x * 64 + tx;   // 16-block index within a row
   int64_t by = blockIdx.y;
 
-  if (SPLIT && rho) {
-    // leading rows of the grid: the rank-one row of the GEMM that takes this
-    // split, rho[s][j] = deq(Q4(mu_s)) . deq(B_s,j) for each segment s (B
-    // holds one bn x cols matrix per segment).  Each workgroup takes r1_rows
-    // (a multiple of 16) rows of one segment's B: it quantizes that segment's
-    // mean as the mean block below does (same tensor scale, same draws),
-    // dequantizes it to fp16 in LDS (exact), and each group of 16 lanes sums
-    // one row of B against it, 16 rows per pass.
+  if (SPLIT && r1s.count > 0) {
+    // leading rows of the grid: the rank-one rows of the GEMMs that take this
+    // split, rho_i[s][j] = deq(Q4(mu_s)) . deq(B_i,s,j) for each B operand i
+    // and segment s (B_i holds one n_i x cols matrix per segment).  Operand
+    // i owns the workgroups r1s.gend[i-1] .. r1s.gend[i]-1, r1_rows (a multiple
+    // of 16) rows of one segment's B_i each: a workgroup quantizes that
+    // segment's mean as the mean block below does (same tensor scale, same
+    // draws), dequantizes it to fp16 in LDS (exact), and each group of 16
+    // lanes sums one row of B_i against it, 16 rows per pass.
     if (by < rho_rows) {
       extern __shared__ __attribute__((aligned(16))) _Float16 r1_mean[];   // [cols]
-      const int64_t groups = (bn + r1_rows - 1) / r1_rows;
       const int64_t rbi = by * gridDim.x + blockIdx.x;
-      const int rseg = (int)(rbi / groups);
-      if (rseg >= nseg) return;                          // uniform
+      int bi = 0;
+      while (bi + 1 < r1s.count && rbi >= r1s.gend[bi]) ++bi;   // uniform
+      if (rbi >= r1s.gend[bi]) return;                        // past the last operand's rows
+      const QOperand B = r1s.b[bi];
+      const int64_t bn = r1s.n[bi];
+      float* __restrict__ rho = r1s.rho[bi];
+      const int64_t groups = (bn + r1_rows - 1) / r1_rows;
+      const int64_t rloc = rbi - (bi > 0 ? r1s.gend[bi - 1] : 0);
+      const int rseg = (int)(rloc / groups);
       const float am = reduce_partials(tmax_mu + (int64_t)rseg * ntmax_mu, ntmax_mu);
       float s_enc, s_dec;
       tensor_scales(am, s_enc, s_dec);
@@ -819,7 +834,7 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ a, int64_t 
         *reinterpret_cast<uint4*>(r1_mean + mb * 16 + 8) = deq8(packed.y, s2);
       }
       __syncthreads();
-      const int64_t rb = rbi - (int64_t)rseg * groups;   // r1_rows rows of the segment's B
+      const int64_t rb = rloc - (int64_t)rseg * groups;   // r1_rows rows of the segment's B
       const int sub = threadIdx.x & 15;
       const float r_dec = s_dec * B.tscale[(offs ? 2 * rseg : 0) + 1];
       for (int64_t j = rb * r1_rows + (threadIdx.x >> 4); j < (rb + 1) * r1_rows; j += 16) {
@@ -1513,12 +1528,25 @@ static hipError_t run_finalize_quant(const T* a, int64_t rows, int64_t cols, int
   // segment's B each, 16 while that gives at most 512 workgroups, else up to
   // 128 (many experts' weights: the mean's quantization and staging, which
   // every such workgroup repeats, spread over more rows)
+  Rank1Set rs{};
+  auto r1_wgs = [&](int rows_per) {
+    int64_t g = 0;
+    for (int i = 0; i < (r1 ? r1->count : 0); ++i) g += (r1->n[i] + rows_per - 1) / rows_per * nseg;
+    return g;
+  };
   int r1_rows = 16;
-  while (r1 && r1_rows < 128 && (r1->n + r1_rows - 1) / r1_rows * nseg > 512) r1_rows *= 2;
-  const int64_t rho_rows =
-      r1 ? ((r1->n + r1_rows - 1) / r1_rows * nseg + ct_q - 1) / ct_q : 0;
-  const size_t lds_r1 = r1 ? (size_t)cols * 2 : 0;
-  const QOperand rb = r1 ? r1->b : QOperand{nullptr, nullptr, nullptr};
+  while (r1 && r1_rows < 128 && r1_wgs(r1_rows) > 512) r1_rows *= 2;
+  int64_t gend = 0;
+  for (int i = 0; i < (r1 ? r1->count : 0); ++i) {
+    rs.b[i] = r1->b[i];
+    rs.n[i] = r1->n[i];
+    rs.rho[i] = r1->rho[i];
+    gend += (r1->n[i] + r1_rows - 1) / r1_rows * nseg;
+    rs.gend[i] = gend;
+  }
+  rs.count = r1 ? r1->count : 0;
+  const int64_t rho_rows = (gend + ct_q - 1) / ct_q;
+  const size_t lds_r1 = rs.count ? (size_t)cols * 2 : 0;
   dim3 gq((unsigned)ct_q, (unsigned)(rho_rows + nchq + nseg));
   // the staged mean of the rank-one workgroups (at most 64 KB)
 #define AVERIS_QUANT_LAUNCH(SPL, SRB)                                                        \
@@ -1530,7 +1558,7 @@ static hipError_t run_finalize_quant(const T* a, int64_t rows, int64_t cols, int
       a, rows, cols, lda, offs, nseg, nchq, seed, stream_id, ws.mu, tmax, ntmax, ws.tmax_mu, \
       ct_f, out.codes, out.scales, out.tscale, mean ? mean->codes : nullptr,                \
       mean ? mean->scales : nullptr, mean ? mean->tscale : nullptr, ws.tssq, ws.tmu2, ratio, \
-      rb, r1 ? r1->n : 0, r1 ? r1->rho : nullptr, rho_rows, r1_rows)
+      rs, rho_rows, r1_rows)
   if (split) {
     if (sr) { AVERIS_QUANT_LAUNCH(true, true); } else { AVERIS_QUANT_LAUNCH(true, false); }
   } else {

@@ -87,6 +87,36 @@ def test_split_quant_rejections(L):
     assert split(L, ws=P + 16) == 4                       # workspace alignment
 
 
+def test_split_rank1_multi_rejections(L):
+    res, mean = nv(64, 128), nv(1, 128)
+
+    def rm(nb=2, bs=None, rhos=None, cols=128, lda=128, **kw):
+        bs = bs if bs is not None else [nv(96, cols), nv(32, cols)]
+        rhos = rhos if rhos is not None else [P, P2]
+        barr = (ctypes.POINTER(av._NVFP4) * len(bs))(
+            *[ctypes.pointer(b) if b is not None else None for b in bs])
+        rarr = (ctypes.c_void_p * len(rhos))(*rhos)
+        return L.averis_split_quant_rank1_multi(
+            kw.get("a", P), av.BF16, 64, cols, lda, 0, av.SR, ctypes.byref(res),
+            ctypes.byref(mean), P, nb, ctypes.cast(barr, ctypes.c_void_p),
+            ctypes.cast(rarr, ctypes.c_void_p), kw.get("ws", P), 1 << 30, None)
+    nul = ctypes.c_void_p(None)
+    assert L.averis_split_quant_rank1_multi(P, av.BF16, 64, 128, 128, 0, av.SR, ctypes.byref(res),
+                                            ctypes.byref(mean), P, 2, None, P, P, 1 << 30,
+                                            None) == 1
+    assert rm(nb=0) == 6
+    assert rm(nb=5, bs=[nv(16, 128)] * 5, rhos=[P] * 5) == 6   # AVERIS_MAX_RANK1
+    assert rm(bs=[nv(96, 128), None]) == 1                    # every entry checked
+    assert rm(rhos=[P, 0]) == 1
+    assert rm(rhos=[P, P + 2]) == 4                           # 4-byte rho
+    assert rm(bs=[nv(96, 128), nv(32, 64)]) == 2              # b[i]->cols == cols
+    assert rm(bs=[nv(96, 128), nv(0, 128)]) == 2              # an empty b
+    assert rm(bs=[nv(96, 128), nv(32, 128, codes=P + 8)]) == 4
+    assert rm(a=P + 2) == 4                                   # then the split's own checks
+    assert rm(ws=None) == 5
+    del nul
+
+
 def test_noalloc_split_rejections(L):
     # the argument checks of averis_split_quant, and inputs whose
     # intermediate results do not fit the library's device array, all before

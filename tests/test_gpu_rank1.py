@@ -160,3 +160,30 @@ def test_bf16_output_strides_and_ragged_columns(l, m, n):
     out = av.averis_gemm_rank1(res, rho, b, out_dtype=torch.bfloat16, out=big[:, 1:n + 1])
     assert torch.equal(out, ref)
     assert torch.isnan(big[:, 0]).all() and torch.isnan(big[:, n + 1:]).all()
+
+
+@pytest.mark.parametrize("case", ["qkv", "four_small"])
+def test_several_rank1_operands_in_one_split(case):
+    """averis_split_quant_rank1_multi: the split and each operand's rank-one
+    row are those of averis_split_quant_rank1 with that operand alone, bit for
+    bit (q, k and v of a block at a ragged token count; four small operands
+    with ragged row counts, the mean's columns not a multiple of 1024)."""
+    g = np.random.default_rng(23)
+    if case == "qkv":
+        l, m, ns = 1000, 1024, (2048, 1024, 1024)
+    else:
+        l, m, ns = 300, 144, (16, 48, 32, 80)
+    a = workloads.mean_biased_activation(np.random.default_rng(5), l, m).cuda()
+    bs = []
+    for i, n in enumerate(ns):
+        w = torch.from_numpy((g.standard_normal((m, n)) * (i + 1) / np.sqrt(m)).astype(np.float32))
+        bs.append(av.averis_quant(w.cuda(), transpose=True, rnd=av.RN, sr_stream=av.STREAM_WEIGHT))
+    res, mean, mu, rhos = av.averis_split_quant_rank1_multi(a, bs, seed=3)
+    for b, rho in zip(bs, rhos):
+        r1, m1, mu1, rho1 = av.averis_split_quant_rank1(a, b, seed=3)
+        for x, y in ((res, r1), (mean, m1)):
+            for t in ("codes", "scales", "tscale"):
+                assert torch.equal(getattr(x, t), getattr(y, t)), t
+        assert torch.equal(mu, mu1)
+        assert torch.equal(rho, rho1)
+    torch.cuda.synchronize()
