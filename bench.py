@@ -75,6 +75,9 @@ def parse():
     p.add_argument("--only-headline", action="store_true",
                    help="time the headline config only (no other configs, wgrad, ratio, weight copies)")
     p.add_argument("--copies", type=int, default=0, help="rotating input copies (0: auto)")
+    p.add_argument("--streams", type=int, default=2, choices=[1, 2],
+                   help="2: each dense linear's dgrad split runs on a second stream, beside "
+                        "the forward pass (both arms); 1: every op on the launch stream")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=3072,
                    help="oracle sample: tokens of every linear of the headline workload")
@@ -128,6 +131,11 @@ class Linear:
             rho_x=torch.empty((self.nseg * n,), dtype=torch.float32, device=dev),
             rho_d=torch.empty((self.nseg * m,), dtype=torch.float32, device=dev),
         )
+        if offsets is None:
+            # the dgrad split's outputs (written on the side stream)
+            self.ws.update(d_res=av.NVFP4.empty(l, n, 1, dev), d_mean=av.NVFP4.empty(1, n, 1, dev),
+                           d_mu=torch.empty((n,), dtype=torch.float32, device=dev),
+                           d_q=av.NVFP4.empty(l, n, 1, dev))
         self.xs, self.ds = [self.x0], [self.d0]
 
     def act_bytes(self):
@@ -193,13 +201,15 @@ class Timer:
         return [a.elapsed_time(b) for a, b in self.pairs.get(name, [])]
 
 
-def run_linear(L, i, t, vanilla, shared=False, wq=None):
+def run_linear(L, i, t, vanilla, shared=False, wq=None, side=None):
     """One linear's forward + dgrad with input copy i.  shared: a linear
     whose input is another's (L.share_src) reuses that linear's split (or
     plain quant) of it from the same step; the Averis GEMM then takes the
     rank-one row the source's split formed for it
     (averis_split_quant_rank1_multi).  wq: both copies of the weight, when
-    the step quantized all weights at once."""
+    the step quantized all weights at once.  side: a second stream on which
+    the dgrad pass's split of D (independent of the forward pass) runs while
+    the main stream does the forward pass; the dgrad GEMM waits for it."""
     def tic(k):
         if t:
             t.start(L.name + "/" + k)
@@ -215,6 +225,16 @@ def run_linear(L, i, t, vanilla, shared=False, wq=None):
         toc("wquant")
     else:
         wt, wd = wq
+    pending = None
+    if side is not None and L.offsets is None:
+        fork = torch.cuda.Event()
+        fork.record()
+        side.wait_event(fork)
+        with torch.cuda.stream(side):
+            dq, rho_d = split_d(L, d, wd, vanilla)
+            join = torch.cuda.Event()
+            join.record()
+        pending = (join, dq, rho_d)
     if L.offsets is None and shared and L.share_src is not None:
         xr, xmean = L.share_src.last_split
         tic("gemm_fwd")
@@ -223,7 +243,7 @@ def run_linear(L, i, t, vanilla, shared=False, wq=None):
         else:
             av.averis_gemm_vanilla(xr, wt, out_dtype=torch.bfloat16, out=ws["y"], ws=ws["g"])
         toc("gemm_fwd")
-        run_dgrad(L, d, wd, t, vanilla)
+        run_dgrad(L, d, wd, t, vanilla, pending)
         return
     if L.offsets is None:
         if not vanilla:
@@ -253,7 +273,7 @@ def run_linear(L, i, t, vanilla, shared=False, wq=None):
             tic("gemm_fwd")
             av.averis_gemm_vanilla(xq, wt, out_dtype=torch.bfloat16, out=ws["y"], ws=ws["g"])
             toc("gemm_fwd")
-        run_dgrad(L, d, wd, t, vanilla)
+        run_dgrad(L, d, wd, t, vanilla, pending)
         return
     offs = L.offsets
     if not vanilla:
@@ -286,23 +306,42 @@ def run_linear(L, i, t, vanilla, shared=False, wq=None):
         toc("gemm_dgrad")
 
 
-def run_dgrad(L, d, wd, t, vanilla):
-    """The dgrad pass of a dense linear (split or plain quant of D, GEMM)."""
+def split_d(L, d, wd, vanilla):
+    """The dgrad pass's split (or plain quant) of D into the linear's own
+    output buffers; returns (quantized D, rank-one row or None)."""
     ws = L.ws
+    if not vanilla:
+        dr, _, _, rho_d = av.averis_split_quant_rank1(
+            d, wd, seed=1, ws=ws["sq_d"], rho=ws["rho_d"],
+            out=(ws["d_res"], ws["d_mean"], ws["d_mu"]))
+        return dr, rho_d
+    return av.averis_quant(d, seed=1, ws=ws["sq_d"], out=ws["d_q"]), None
+
+
+def gemm_d(L, dq, rho_d, wd, vanilla):
+    ws = L.ws
+    if not vanilla:
+        av.averis_gemm_rank1(dq, rho_d, wd, out_dtype=torch.bfloat16, out=ws["dx"])
+    else:
+        av.averis_gemm_vanilla(dq, wd, out_dtype=torch.bfloat16, out=ws["dx"], ws=ws["g"])
+
+
+def run_dgrad(L, d, wd, t, vanilla, pending=None):
+    """The dgrad pass of a dense linear (split or plain quant of D, GEMM).
+    pending: (join event, quantized D, rank-one row) of a split already
+    issued on the side stream; the GEMM waits for it."""
+    if pending is not None:
+        join, dq, rho_d = pending
+        torch.cuda.current_stream().wait_event(join)
+        gemm_d(L, dq, rho_d, wd, vanilla)
+        return
     if t:
         t.start(L.name + "/split_d")
-    if not vanilla:
-        dr, _, _, rho_d = av.averis_split_quant_rank1(d, wd, seed=1, ws=ws["sq_d"],
-                                                      rho=ws["rho_d"])
-    else:
-        dq = av.averis_quant(d, seed=1, ws=ws["sq_d"])
+    dq, rho_d = split_d(L, d, wd, vanilla)
     if t:
         t.stop(L.name + "/split_d")
         t.start(L.name + "/gemm_dgrad")
-    if not vanilla:
-        av.averis_gemm_rank1(dr, rho_d, wd, out_dtype=torch.bfloat16, out=ws["dx"])
-    else:
-        av.averis_gemm_vanilla(dq, wd, out_dtype=torch.bfloat16, out=ws["dx"], ws=ws["g"])
+    gemm_d(L, dq, rho_d, wd, vanilla)
     if t:
         t.stop(L.name + "/gemm_dgrad")
 
@@ -314,7 +353,7 @@ def block_weights(linears):
     return len(linears) > 1 and all(L.offsets is None and L.w.dim() == 2 for L in linears)
 
 
-def run_step(linears, i, t=None, vanilla=False, shared=False):
+def run_step(linears, i, t=None, vanilla=False, shared=False, side=None):
     wq = [None] * len(linears)
     if block_weights(linears):
         # both copies of every weight of the block in two launches
@@ -327,7 +366,7 @@ def run_step(linears, i, t=None, vanilla=False, shared=False):
     for L, w in zip(linears, wq):
         L.cur_w = w
     for L, w in zip(linears, wq):
-        run_linear(L, i, t, vanilla, shared, w)
+        run_linear(L, i, t, vanilla, shared, w, side)
 
 
 _SLEEP_CYCLES_PER_MS = None
@@ -352,7 +391,7 @@ def pct(v, q):
     return float(np.percentile(v, q)) if len(v) else float("nan")
 
 
-def timed(linears, steps, warmup, vanilla, shared=False, per_call=True):
+def timed(linears, steps, warmup, vanilla, shared=False, per_call=True, side=None):
     """Step time three ways (ms/step), the per-step device times of the
     queued run, and a per-call event timer.
 
@@ -361,14 +400,18 @@ def timed(linears, steps, warmup, vanilla, shared=False, per_call=True):
     queued: the eager launches queued behind a spin kernel and timed with
             events on the launch stream: the device's own step time, with the
             host's launch cost taken out (an event between steps gives each
-            step's own time)."""
+            step's own time; the median step, and p10 / p90; queued_mean is
+            first event to last over the steps, which a stall of the host
+            feeding a full launch queue can lengthen).
+    side: the second stream of the dgrad splits (not for the per-call timer,
+    whose calls run one after another on the launch stream)."""
     ncopy = max(len(L.xs) for L in linears)
     for i in range(warmup):
-        run_step(linears, i, None, vanilla, shared)
+        run_step(linears, i, None, vanilla, shared, side)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        run_step(linears, i, None, vanilla, shared)
+        run_step(linears, i, None, vanilla, shared, side)
     enqueue_ms = (time.perf_counter() - t0) * 1e3
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / steps
@@ -378,7 +421,7 @@ def timed(linears, steps, warmup, vanilla, shared=False, per_call=True):
     for i in range(ncopy):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, pool=pool):
-            run_step(linears, i, None, vanilla, shared)
+            run_step(linears, i, None, vanilla, shared, side)
         pool = g.pool()
         graphs.append(g)
     torch.cuda.synchronize()
@@ -398,12 +441,13 @@ def timed(linears, steps, warmup, vanilla, shared=False, per_call=True):
     t0 = time.perf_counter()
     for i in range(steps):
         evs[i].record()
-        run_step(linears, i, None, vanilla, shared)
+        run_step(linears, i, None, vanilla, shared, side)
     evs[steps].record()
     queued_enqueue_ms = (time.perf_counter() - t0) * 1e3
     torch.cuda.synchronize()
     per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
-    queued_ms = evs[0].elapsed_time(evs[steps]) / steps
+    queued_mean_ms = evs[0].elapsed_time(evs[steps]) / steps
+    queued_ms = float(np.median(per_step))
     if queued_enqueue_ms > 0.8 * hold:
         log("bench: warning: enqueue took %.2f ms of a %.2f ms hold" % (queued_enqueue_ms, hold))
 
@@ -415,7 +459,7 @@ def timed(linears, steps, warmup, vanilla, shared=False, per_call=True):
         for i in range(steps):
             run_step(linears, i, t, vanilla, shared)
         torch.cuda.synchronize()
-    return dict(eager=eager_ms, graph=graph_ms, queued=queued_ms,
+    return dict(eager=eager_ms, graph=graph_ms, queued=queued_ms, queued_mean=queued_mean_ms,
                 queued_p10=pct(per_step, 10), queued_p90=pct(per_step, 90)), t
 
 
@@ -423,7 +467,7 @@ def stats(v):
     return dict(ms=float(np.median(v)), p10=pct(v, 10), p90=pct(v, 90))
 
 
-def measure(cfg, linears, steps, warmup):
+def measure(cfg, linears, steps, warmup, streams=2):
     """Both arms of one workload; returns the summary dict and the timers."""
     act = sum(L.act_bytes() for L in linears)
     copies = max(1, int(np.ceil(ROTATE_BYTES / act)))
@@ -431,8 +475,9 @@ def measure(cfg, linears, steps, warmup):
         L.rotate(copies)
     log("bench: config %d: %d linear(s), %.0f MB of activations per step, %d rotating copies"
         % (cfg, len(linears), act / 1e6, copies))
-    ta_ms, ta = timed(linears, steps, warmup, vanilla=False)
-    tv_ms, tv = timed(linears, steps, warmup, vanilla=True)
+    side = torch.cuda.Stream() if streams == 2 else None
+    ta_ms, ta = timed(linears, steps, warmup, vanilla=False, side=side)
+    tv_ms, tv = timed(linears, steps, warmup, vanilla=True, side=side)
     log("bench: config %d: averis %s | vanilla %s (ms/step)" % (
         cfg, " ".join("%s %.4f" % kv for kv in ta_ms.items()),
         " ".join("%s %.4f" % kv for kv in tv_ms.items())))
@@ -475,6 +520,8 @@ def measure(cfg, linears, steps, warmup):
     A, V = tot["averis"], tot["vanilla"]
     summary = dict(
         workload=WORKLOAD_NAMES[cfg],
+        schedule=("each dense linear's dgrad split on a second stream, beside its forward pass"
+                  if side is not None else "every op in order on the launch stream"),
         ms_per_step=ta_ms["queued"], vanilla_ms_per_step=tv_ms["queued"],
         step_p10_p90_ms=[ta_ms["queued_p10"], ta_ms["queued_p90"]],
         vanilla_step_p10_p90_ms=[tv_ms["queued_p10"], tv_ms["queued_p90"]],
@@ -510,8 +557,10 @@ def measure(cfg, linears, steps, warmup):
         # the same step with each shared input split (or quantized) once: k
         # and v reuse q's, up reuses gate's; the one split forms the rank-one
         # rows of all the GEMMs that take it
-        sa, _ = timed(linears, steps, warmup, vanilla=False, shared=True, per_call=False)
-        sv, _ = timed(linears, steps, warmup, vanilla=True, shared=True, per_call=False)
+        sa, _ = timed(linears, steps, warmup, vanilla=False, shared=True, per_call=False,
+                      side=side)
+        sv, _ = timed(linears, steps, warmup, vanilla=True, shared=True, per_call=False,
+                      side=side)
         log("bench: config %d, shared inputs: averis %.4f | vanilla %.4f (ms/step)"
             % (cfg, sa["queued"], sv["queued"]))
         summary["shared_input_once"] = dict(
@@ -806,7 +855,7 @@ def main():
     cfg = args.config
     log("bench: generating config %d" % cfg)
     linears = make_linears(cfg)
-    head, ta, flops_step = measure(cfg, linears, args.steps, args.warmup)
+    head, ta, flops_step = measure(cfg, linears, args.steps, args.warmup, args.streams)
 
     # roofline of the dominant kernel: k_gemm_win, the Averis GEMM (the
     # NVFP4 NT GEMM with the codes staged in LDS, adding the split's rank-one
@@ -861,7 +910,7 @@ def main():
             torch.cuda.empty_cache()
             log("bench: generating config %d" % c)
             linears = make_linears(c)
-            others[str(c)] = measure(c, linears, args.steps, args.warmup)[0]
+            others[str(c)] = measure(c, linears, args.steps, args.warmup, args.streams)[0]
         out["other_configs"] = others
         # the (f) rows on one linear of the headline workload
         for L in linears:

@@ -227,11 +227,12 @@ def averis_split_quant_grouped(a, offsets, seed=0, rnd=SR, ws=None):
     return res, mean, mu
 
 
-def averis_quant(a, transpose=False, seed=0, rnd=SR, sr_stream=STREAM_ACT, ws=None):
-    """Plain Q4.  transpose=True quantizes a^T (blocks along a's rows)."""
+def averis_quant(a, transpose=False, seed=0, rnd=SR, sr_stream=STREAM_ACT, ws=None, out=None):
+    """Plain Q4.  transpose=True quantizes a^T (blocks along a's rows).  out:
+    an NVFP4 of the output's shape to write into (else a new one)."""
     srows, scols = a.shape
     rows, cols = (scols, srows) if transpose else (srows, scols)
-    out = NVFP4.empty(rows, cols, 1, a.device)
+    out = out if out is not None else NVFP4.empty(rows, cols, 1, a.device)
     need = workspace_bytes(OP_QUANT, rows, cols)
     ws = ws if ws is not None else _workspace(need, a.device)
     o = out.c()
@@ -439,13 +440,17 @@ def averis_split_quant_ratio(a, seed=0, rnd=SR, offsets=None, ws=None):
     return res, mean, mu, ratio
 
 
-def averis_split_quant_rank1(a, b, seed=0, rnd=SR, ws=None, rho=None):
+def averis_split_quant_rank1(a, b, seed=0, rnd=SR, ws=None, rho=None, out=None):
     """averis_split_quant plus the rank-one row rho = deq(mean) deq(b)^T for
-    the GEMM's B operand b; returns (residual, mean, mu_f32, rho)."""
+    the GEMM's B operand b; returns (residual, mean, mu_f32, rho).  out:
+    (residual, mean, mu_f32) to write into (else new ones)."""
     rows, cols = a.shape
-    res = NVFP4.empty(rows, cols, 1, a.device)
-    mean = NVFP4.empty(1, cols, 1, a.device)
-    mu = torch.empty((cols,), dtype=torch.float32, device=a.device)
+    if out is not None:
+        res, mean, mu = out
+    else:
+        res = NVFP4.empty(rows, cols, 1, a.device)
+        mean = NVFP4.empty(1, cols, 1, a.device)
+        mu = torch.empty((cols,), dtype=torch.float32, device=a.device)
     rho = rho if rho is not None else torch.empty((b.rows,), dtype=torch.float32, device=a.device)
     need = workspace_bytes(OP_SPLIT_QUANT, rows, cols)
     ws = ws if ws is not None else _workspace(need, a.device)

@@ -80,6 +80,82 @@ def test_graph_replays_match_eager(l, m, n, mode):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("vanilla", [False, True])
+def test_two_stream_step_replays_match_eager(vanilla):
+    """The step with the dgrad split on a second stream (forked from and
+    joined back to the capturing stream by events, its outputs preallocated):
+    each replay equals the one-stream eager step bit for bit."""
+    cfg = workloads.up_proj(l=2048, m=1024, n=3072)
+    x, w, d = cfg["x"].cuda(), cfg["w"].cuda(), cfg["d"].cuda()
+    rank1 = not vanilla
+    ref = [t.clone() for t in step(x, w, d, vanilla, rank1)]
+    side = torch.cuda.Stream()
+    l, n = d.shape
+    d_res, d_mean = av.NVFP4.empty(l, n), av.NVFP4.empty(1, n)
+    d_mu = torch.empty((n,), dtype=torch.float32, device="cuda")
+    d_rho = torch.empty((w.shape[0],), dtype=torch.float32, device="cuda")
+    d_q = av.NVFP4.empty(l, n)
+
+    def step2():
+        wt, wd = av.averis_quant_pair(w, rnd=av.RN)
+        fork = torch.cuda.Event()
+        fork.record()
+        side.wait_event(fork)
+        with torch.cuda.stream(side):
+            if vanilla:
+                dq, rd = av.averis_quant(d, seed=1, out=d_q), None
+            else:
+                dq, _, _, rd = av.averis_split_quant_rank1(d, wd, seed=1, rho=d_rho,
+                                                           out=(d_res, d_mean, d_mu))
+            join = torch.cuda.Event()
+            join.record()
+        if vanilla:
+            xq = av.averis_quant(x, seed=0)
+            y = av.averis_gemm_vanilla(xq, wt, out_dtype=torch.bfloat16)
+            quants, extra = [wt, wd, xq], []
+        else:
+            xr, xm, xmu, rx = av.averis_split_quant_rank1(x, wt, seed=0)
+            y = av.averis_gemm_rank1(xr, rx, wt, out_dtype=torch.bfloat16)
+            quants, extra = [wt, wd, xr, xm], [xmu, rx]
+        torch.cuda.current_stream().wait_event(join)
+        if vanilla:
+            dx = av.averis_gemm_vanilla(dq, wd, out_dtype=torch.bfloat16)
+            quants, extra = quants + [dq], extra
+        else:
+            dx = av.averis_gemm_rank1(dq, rd, wd, out_dtype=torch.bfloat16)
+            quants, extra = quants + [dq, d_mean], extra + [d_mu, rd]
+        flat = [t for q in quants for t in (q.codes, q.scales, q.tscale)]
+        return flat + extra + [y, dx]
+
+    eager2 = [t.clone() for t in step2()]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = step2()
+    torch.cuda.synchronize()
+    # step lists [wt, wd, xq, dq] (vanilla) or [wt, wd, xr, xm, dr, dm] and
+    # [xmu, dmu, rx, rd]; step2 the same quantized tensors and [xmu, rx, dmu, rd]
+    if vanilla:
+        order = list(range(12)) + [12, 13]
+    else:
+        order = list(range(18)) + [18, 20, 19, 21] + [22, 23]
+    mapped = [eager2[i] for i in order]
+    assert len(mapped) == len(ref)
+    for i, (a, b) in enumerate(zip(mapped, ref)):
+        assert torch.equal(a, b), "two-stream eager output %d differs from the one-stream step" % i
+    for rep in range(3):
+        av.averis_split_quant(workloads.up_proj(l=256, m=1024, n=3072)["x"].cuda(), seed=rep)
+        torch.cuda.synchronize()
+        for t in outs:
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, eager2)):
+            assert torch.equal(a, b), "replay %d, output %d differs from the eager step" % (rep, i)
+    del g
+    torch.cuda.synchronize()
+
+
 def test_wgrad_graph_replays_match_eager():
     # the transposed residual quants and the split-K wgrad (partials + reduce)
     cfg = workloads.up_proj(l=2048, m=320, n=192)
