@@ -277,14 +277,16 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
 
 // ---------------------------------------------------------------------------
 // The correctly rounded sum of column j of one segment whose fp64 running sum
-// is not certified (certificate below).  The chunks' fp64 partial sums that
-// are exact by their own certificate (a chunk spans far fewer rows and
-// usually a far narrower range of values) are added exactly, the rows of the
-// other chunks one by one, into a 320-bit integer in units of 2^-149
-// (exact_sum.hpp), which is rounded once to the nearest double.  Chunk c of
-// the segment goes to thread c mod 256; the block then adds the accumulators
-// pairwise and thread 0 gets the result.  Kept out of line: the finalize
-// pass calls it only for a column that fails the certificate.
+// is not certified (certificate below), by one wavefront (all 64 lanes, in
+// wave-uniform control flow).  The chunks' fp64 partial sums that are exact
+// by their own certificate (a chunk spans far fewer rows and usually a far
+// narrower range of values) are added exactly, the rows of the other chunks
+// one by one, into a 320-bit integer in units of 2^-149 (exact_sum.hpp),
+// which is rounded once to the nearest double.  Chunk c of the segment goes
+// to lane c mod 64; the lanes' accumulators are then added by a butterfly of
+// shuffles (exact, so the order is free) and every lane gets the result.
+// Kept out of line: the finalize passes call it only for a column that fails
+// the certificate.
 // ---------------------------------------------------------------------------
 
 // Certificate of an fp64 sum of n values of one column: every value is a
@@ -305,12 +307,12 @@ __device__ __noinline__ double exact_column_sum(const void* a, bool bf16, int64_
                                                 const double* __restrict__ psum,
                                                 const float* __restrict__ pmax,
                                                 const float* __restrict__ pmin,
-                                                const float* __restrict__ pmnz,
-                                                uint32_t (*red)[kWideWords]) {
+                                                const float* __restrict__ pmnz) {
+  const int lane = threadIdx.x & 63;
   uint32_t acc[kWideWords];
 #pragma unroll
   for (int i = 0; i < kWideWords; ++i) acc[i] = 0u;
-  for (int64_t c = c0 + threadIdx.x; c < c1; c += 256) {
+  for (int64_t c = c0 + lane; c < c1; c += 64) {
     const int64_t r0 = seg_r0 + (c - c0) * ch;
     const int64_t r1 = r0 + ch < seg_r1 ? r0 + ch : seg_r1;
     const int64_t o = c * cols + j;
@@ -325,16 +327,14 @@ __device__ __noinline__ double exact_column_sum(const void* a, bool bf16, int64_
       }
     }
   }
-  for (int stride = 128; stride > 0; stride >>= 1) {
-    if ((int)threadIdx.x >= stride && (int)threadIdx.x < 2 * stride) {
+  // butterfly over the wavefront: every lane ends with the total
+  for (int d = 32; d > 0; d >>= 1) {
+    uint32_t other[kWideWords];
 #pragma unroll
-      for (int i = 0; i < kWideWords; ++i) red[threadIdx.x - stride][i] = acc[i];
-    }
-    __syncthreads();
-    if ((int)threadIdx.x < stride) wide_add(acc, red[threadIdx.x]);
-    __syncthreads();
+    for (int i = 0; i < kWideWords; ++i) other[i] = __shfl_xor(acc[i], d, 64);
+    wide_add(acc, other);
   }
-  return threadIdx.x == 0 ? wide_to_double(acc) : 0.0;
+  return wide_to_double(acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -394,7 +394,6 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
   __shared__ float lx[NQ][NC], ln[NQ][NC], lz[NQ][NC];
   __shared__ uint32_t need_mask;   // bit c: column c of the tile failed the certificate
   __shared__ double exact_s[NC];
-  __shared__ uint32_t wide_red[128][kWideWords];
   ls[q][jl] = s;
   lq[q][jl] = s2;
   lx[q][jl] = m1;
@@ -432,12 +431,18 @@ __global__ __launch_bounds__(256) void k_finalize(const void* a, bool a_bf16, in
   }
   __syncthreads();
   const uint32_t mask = need_mask;   // uniform
-  for (uint32_t mrest = mask; mrest != 0; mrest &= mrest - 1) {
-    const int cidx = __builtin_ctz(mrest);
-    const double v = exact_column_sum(a, a_bf16, lda, cols, sr.seg_r0, sr.seg_r1, sr.c0, sr.c1,
-                                      ch, (int64_t)blockIdx.x * NC + cidx, psum, pmax, pmin, pmnz,
-                                      wide_red);
-    if (threadIdx.x == 0) exact_s[cidx] = v;
+  // the failing columns' exact sums, the k-th of them by wave k mod 4
+  {
+    const int wv = threadIdx.x >> 6;
+    int k = 0;
+    for (uint32_t mrest = mask; mrest != 0; mrest &= mrest - 1, ++k) {
+      if ((k & 3) != wv) continue;   // wave-uniform
+      const int cidx = __builtin_ctz(mrest);
+      const double v = exact_column_sum(a, a_bf16, lda, cols, sr.seg_r0, sr.seg_r1, sr.c0, sr.c1,
+                                        ch, (int64_t)blockIdx.x * NC + cidx, psum, pmax, pmin,
+                                        pmnz);
+      if ((threadIdx.x & 63) == 0) exact_s[cidx] = v;
+    }
   }
   if (mask) __syncthreads();
   if (q == 0 && j < cols) {
@@ -503,7 +508,6 @@ __global__ __launch_bounds__(256) void k_finalize_seg(const void* a, bool a_bf16
   __shared__ SegRange srs[4];
   __shared__ uint64_t fail_mask[4];
   __shared__ double exact_s[4][64];
-  __shared__ uint32_t wide_red[128][kWideWords];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int seg_w = (int)blockIdx.y * 4 + wave;
   if (seg_w < nseg) {   // wave-uniform
@@ -556,19 +560,15 @@ __global__ __launch_bounds__(256) void k_finalize_seg(const void* a, bool a_bf16
   const uint64_t bal = __ballot(fail);
   if (lane == 0) fail_mask[wave] = bal;
   __syncthreads();
-  bool any = false;
-  for (int w = 0; w < 4; ++w) {
-    const SegRange sw = srs[w];
-    for (uint64_t mrest = fail_mask[w]; mrest != 0; mrest &= mrest - 1) {
-      const int cidx = __builtin_ctzll(mrest);
-      const double v = exact_column_sum(a, a_bf16, lda, cols, sw.seg_r0, sw.seg_r1, sw.c0, sw.c1,
-                                        ch, (int64_t)blockIdx.x * 64 + cidx, psum, pmax, pmin,
-                                        pmnz, wide_red);
-      if (threadIdx.x == 0) exact_s[w][cidx] = v;
-      any = true;
-    }
+  // each wave its own segment's failing columns
+  for (uint64_t mrest = fail_mask[wave]; mrest != 0; mrest &= mrest - 1) {   // wave-uniform
+    const int cidx = __builtin_ctzll(mrest);
+    const double v = exact_column_sum(a, a_bf16, lda, cols, sr.seg_r0, sr.seg_r1, sr.c0, sr.c1,
+                                      ch, (int64_t)blockIdx.x * 64 + cidx, psum, pmax, pmin,
+                                      pmnz);
+    if (lane == 0) exact_s[wave][cidx] = v;
   }
-  if (any) __syncthreads();
+  if ((fail_mask[0] | fail_mask[1] | fail_mask[2] | fail_mask[3]) != 0) __syncthreads();
   float rmax = 0.0f, amu = 0.0f;
   double mu2 = 0.0;
   if (live) {
