@@ -131,11 +131,12 @@ class Linear:
             rho_x=torch.empty((self.nseg * n,), dtype=torch.float32, device=dev),
             rho_d=torch.empty((self.nseg * m,), dtype=torch.float32, device=dev),
         )
-        if offsets is None:
-            # the dgrad split's outputs (written on the side stream)
-            self.ws.update(d_res=av.NVFP4.empty(l, n, 1, dev), d_mean=av.NVFP4.empty(1, n, 1, dev),
-                           d_mu=torch.empty((n,), dtype=torch.float32, device=dev),
-                           d_q=av.NVFP4.empty(l, n, 1, dev))
+        # the dgrad split's outputs (written on the side stream)
+        nsg = self.nseg
+        self.ws.update(d_res=av.NVFP4.empty(l, n, nsg, dev), d_mean=av.NVFP4.empty(nsg, n, nsg, dev),
+                       d_mu=torch.empty((n,) if offsets is None else (nsg, n), dtype=torch.float32,
+                                        device=dev),
+                       d_q=av.NVFP4.empty(l, n, nsg, dev))
         self.xs, self.ds = [self.x0], [self.d0]
 
     def act_bytes(self):
@@ -226,7 +227,7 @@ def run_linear(L, i, t, vanilla, shared=False, wq=None, side=None):
     else:
         wt, wd = wq
     pending = None
-    if side is not None and L.offsets is None:
+    if side is not None and L.offsets is None:   # (grouped: below)
         fork = torch.cuda.Event()
         fork.record()
         side.wait_event(fork)
@@ -276,6 +277,37 @@ def run_linear(L, i, t, vanilla, shared=False, wq=None, side=None):
         run_dgrad(L, d, wd, t, vanilla, pending)
         return
     offs = L.offsets
+    if side is not None:
+        # the grouped dgrad split on the second stream, beside the forward pass
+        fork = torch.cuda.Event()
+        fork.record()
+        side.wait_event(fork)
+        with torch.cuda.stream(side):
+            if not vanilla:
+                dq, _, _, rho_d = av.averis_split_quant_grouped_rank1(
+                    d, offs, wd, seed=1, ws=ws["sq_d"], rho=ws["rho_d"],
+                    out=(ws["d_res"], ws["d_mean"], ws["d_mu"]))
+            else:
+                dq = av.averis_quant_grouped(d, offs, seed=1, ws=ws["sq_d"], out=ws["d_q"])
+            join = torch.cuda.Event()
+            join.record()
+        if not vanilla:
+            xr, _, _, rho_x = av.averis_split_quant_grouped_rank1(x, offs, wt, seed=0,
+                                                                  ws=ws["sq_x"])
+            av.averis_gemm_grouped_rank1(xr, rho_x, wt, offs, out_dtype=torch.bfloat16,
+                                         out=ws["y"])
+        else:
+            xq = av.averis_quant_grouped(x, offs, seed=0, ws=ws["sq_x"])
+            av.averis_gemm_grouped(xq, None, wt, offs, out_dtype=torch.bfloat16, out=ws["y"],
+                                   ws=ws["g"])
+        torch.cuda.current_stream().wait_event(join)
+        if not vanilla:
+            av.averis_gemm_grouped_rank1(dq, rho_d, wd, offs, out_dtype=torch.bfloat16,
+                                         out=ws["dx"])
+        else:
+            av.averis_gemm_grouped(dq, None, wd, offs, out_dtype=torch.bfloat16, out=ws["dx"],
+                                   ws=ws["g"])
+        return
     if not vanilla:
         tic("split_x")
         xr, _, _, rho_x = av.averis_split_quant_grouped_rank1(x, offs, wt, seed=0, ws=ws["sq_x"])
@@ -520,7 +552,7 @@ def measure(cfg, linears, steps, warmup, streams=2):
     A, V = tot["averis"], tot["vanilla"]
     summary = dict(
         workload=WORKLOAD_NAMES[cfg],
-        schedule=("each dense linear's dgrad split on a second stream, beside its forward pass"
+        schedule=("each linear's dgrad split on a second stream, beside its forward pass"
                   if side is not None else "every op in order on the launch stream"),
         ms_per_step=ta_ms["queued"], vanilla_ms_per_step=tv_ms["queued"],
         step_p10_p90_ms=[ta_ms["queued_p10"], ta_ms["queued_p90"]],

@@ -330,10 +330,12 @@ def averis_quant_pair_2d(w, seed=0, rnd=RN, sr_stream=STREAM_WEIGHT, ws=None):
     return wt, wd
 
 
-def averis_quant_grouped(a, offsets, seed=0, rnd=SR, sr_stream=STREAM_ACT, ws=None):
+def averis_quant_grouped(a, offsets, seed=0, rnd=SR, sr_stream=STREAM_ACT, ws=None, out=None):
+    """Grouped plain Q4, one tensor scale per segment.  out: an NVFP4 of the
+    output's shape (nseg tensor scales) to write into (else a new one)."""
     rows, cols = a.shape
     nseg = offsets.numel() - 1
-    out = NVFP4.empty(rows, cols, nseg, a.device)
+    out = out if out is not None else NVFP4.empty(rows, cols, nseg, a.device)
     need = workspace_bytes(OP_QUANT, rows, cols, 0, nseg)
     ws = ws if ws is not None else _workspace(need, a.device)
     o = out.c()
@@ -498,15 +500,19 @@ def averis_gemm_rank1(a, rho, b, out_dtype=torch.float32, out=None):
     return c
 
 
-def averis_split_quant_grouped_rank1(a, offsets, b, seed=0, rnd=SR, ws=None):
+def averis_split_quant_grouped_rank1(a, offsets, b, seed=0, rnd=SR, ws=None, out=None, rho=None):
     """Grouped split-quant plus rho[s] = deq(mean_s) deq(b_s)^T per segment
-    (b: nseg stacked matrices); returns (residual, mean, mu_f32, rho)."""
+    (b: nseg stacked matrices); returns (residual, mean, mu_f32, rho).  out:
+    (residual, mean, mu_f32) and rho: buffers to write into (else new ones)."""
     rows, cols = a.shape
     nseg = offsets.numel() - 1
-    res = NVFP4.empty(rows, cols, nseg, a.device)
-    mean = NVFP4.empty(nseg, cols, nseg, a.device)
-    mu = torch.empty((nseg, cols), dtype=torch.float32, device=a.device)
-    rho = torch.empty((b.rows,), dtype=torch.float32, device=a.device)
+    if out is not None:
+        res, mean, mu = out
+    else:
+        res = NVFP4.empty(rows, cols, nseg, a.device)
+        mean = NVFP4.empty(nseg, cols, nseg, a.device)
+        mu = torch.empty((nseg, cols), dtype=torch.float32, device=a.device)
+    rho = rho if rho is not None else torch.empty((b.rows,), dtype=torch.float32, device=a.device)
     need = workspace_bytes(OP_SPLIT_QUANT, rows, cols, 0, nseg)
     ws = ws if ws is not None else _workspace(need, a.device)
     r, m, cb = res.c(), mean.c(), b.c()
