@@ -1139,14 +1139,33 @@ __device__ __forceinline__ void pair_tile(const T* __restrict__ base, int64_t ro
   constexpr int NCH = kPairTile / VE;              // 16-byte chunks per tile row
   constexpr int PER = kPairTile * NCH / 256;       // chunks per thread
   __shared__ float tile[kPairTile][kPairLd];
+  __shared__ float red[4];
   const int tid = threadIdx.x;
+  uint4 wv[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int idx = tid + 256 * i;
     const int lr = idx / NCH, ch = idx % NCH;
     const int64_t r = r0 + lr, c = c0 + (int64_t)ch * VE;
-    uint4 w = {0u, 0u, 0u, 0u};
-    if (r < rows && c < cols) w = *reinterpret_cast<const uint4*>(base + r * lda + c);
+    // (outside the matrix: a clamped load, its value replaced by zeros, so
+    // that no branch stands between these loads and the partials' below)
+    const bool in = r < rows && c < cols;
+    const int64_t rc = r < rows ? r : rows - 1, cc = c < cols ? c : cols - VE;
+    const uint4 w = *reinterpret_cast<const uint4*>(base + rc * lda + cc);
+    wv[i] = in ? w : uint4{0u, 0u, 0u, 0u};
+  }
+  // the thread's share of the tensor's amax partials, loaded while the tile
+  // is in flight (npart <= kAmaxBlocks: at most four a thread)
+  float pq[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) pq[u] = tid + 256 * u < npart ? part[tid + 256 * u] : 0.0f;
+  float pm = __builtin_fmaxf(__builtin_fmaxf(pq[0], pq[1]), __builtin_fmaxf(pq[2], pq[3]));
+  for (int64_t i = tid + 1024; i < npart; i += 256) pm = __builtin_fmaxf(pm, part[i]);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = tid + 256 * i;
+    const int lr = idx / NCH, ch = idx % NCH;
+    const uint4 w = wv[i];
     float* dst = &tile[lr][ch * VE];
     if (sizeof(T) == 2) {
       const uint32_t x[4] = {w.x, w.y, w.z, w.w};
@@ -1162,9 +1181,9 @@ __device__ __forceinline__ void pair_tile(const T* __restrict__ base, int64_t ro
       dst[3] = __uint_as_float(w.w);
     }
   }
-  // the tensor scale (reduce_partials synchronizes the block, which also
+  // the tensor scale (block_max synchronizes the block, which also
   // publishes the tile)
-  const float am = reduce_partials(part, npart);
+  const float am = block_max(pm, red);
   float s_enc, s_dec;
   tensor_scales(am, s_enc, s_dec);
   if (r0 == 0 && c0 == 0 && tid == 0) {
