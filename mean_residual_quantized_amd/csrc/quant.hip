@@ -1128,7 +1128,8 @@ constexpr int kPairLd = kPairTile + 4;   // padded LDS row (floats), 16-byte ali
 
 // the 64 x 64 tile at (r0, c0) of the stored rows x cols matrix W_b at base:
 // global rows of out and out_t from matrix index bt; the tensor scale from
-// W_b's npart amax partials at part (written by the tile at (0, 0))
+// W_b's npart amax partials at part (written by the tile at (0, 0)); every
+// launch caps npart at kAmaxBlocks, four partials a thread at most
 template <typename T, bool SR>
 __device__ __forceinline__ void pair_tile(const T* __restrict__ base, int64_t rows, int64_t cols,
                                           int64_t lda, int bt, int64_t r0, int64_t c0,
@@ -1138,6 +1139,7 @@ __device__ __forceinline__ void pair_tile(const T* __restrict__ base, int64_t ro
   constexpr int VE = 16 / (int)sizeof(T);
   constexpr int NCH = kPairTile / VE;              // 16-byte chunks per tile row
   constexpr int PER = kPairTile * NCH / 256;       // chunks per thread
+  static_assert(kAmaxBlocks <= 4 * 256, "amax partials: four loads a thread");
   __shared__ float tile[kPairTile][kPairLd];
   __shared__ float red[4];
   const int tid = threadIdx.x;
@@ -1155,12 +1157,14 @@ __device__ __forceinline__ void pair_tile(const T* __restrict__ base, int64_t ro
     wv[i] = in ? w : uint4{0u, 0u, 0u, 0u};
   }
   // the thread's share of the tensor's amax partials, loaded while the tile
-  // is in flight (npart <= kAmaxBlocks: at most four a thread)
+  // is in flight; an index past the last partial (npart >= 1) reads the last
+  // one again, which leaves the maximum unchanged and needs no branch
   float pq[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) pq[u] = tid + 256 * u < npart ? part[tid + 256 * u] : 0.0f;
-  float pm = __builtin_fmaxf(__builtin_fmaxf(pq[0], pq[1]), __builtin_fmaxf(pq[2], pq[3]));
-  for (int64_t i = tid + 1024; i < npart; i += 256) pm = __builtin_fmaxf(pm, part[i]);
+  for (int u = 0; u < 4; ++u) {
+    const int64_t j = tid + 256 * u;
+    pq[u] = part[j < npart ? j : npart - 1];
+  }
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int idx = tid + 256 * i;
@@ -1183,6 +1187,7 @@ __device__ __forceinline__ void pair_tile(const T* __restrict__ base, int64_t ro
   }
   // the tensor scale (block_max synchronizes the block, which also
   // publishes the tile)
+  const float pm = __builtin_fmaxf(__builtin_fmaxf(pq[0], pq[1]), __builtin_fmaxf(pq[2], pq[3]));
   const float am = block_max(pm, red);
   float s_enc, s_dec;
   tensor_scales(am, s_enc, s_dec);
@@ -1307,6 +1312,7 @@ __global__ __launch_bounds__(256) void k_pair2d(const T* __restrict__ a, int64_t
   constexpr int VE = 16 / (int)sizeof(T);
   constexpr int NCH = kPairTile / VE;              // 16-byte chunks per tile row
   constexpr int PER = kPairTile * NCH / 256;       // chunks per thread
+  static_assert(kAmaxBlocks <= 4 * 256, "amax partials: four loads a thread");
   __shared__ float tile[kPairTile][kPairLd];
   // codes of the tile transposed, one byte each: ct[column][row]
   __shared__ __attribute__((aligned(16))) uint8_t ct[kPairTile][kPairTile + 16];
