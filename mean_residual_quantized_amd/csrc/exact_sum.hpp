@@ -149,4 +149,43 @@ AVERIS_HD inline double wide_to_double(uint32_t (&a)[kWideWords]) {
   return neg ? -r : r;
 }
 
+// ---------------------------------------------------------------------------
+// A narrower exact path for a column whose values all lie on one grid: every
+// value is a multiple of 2^gexp (gexp from the column's smallest nonzero
+// magnitude) and every partial sum is below 2^62 units of it, so the sum in
+// units of 2^gexp is exact in a signed 64-bit integer, in any order.
+// ---------------------------------------------------------------------------
+
+// exponent of the grid that every value of a column lies on, from its
+// smallest nonzero magnitude mnz (p = 7 for bf16 values, 23 for fp32): a
+// value with binary exponent e (in [2^(e-1), 2^e)) and p fraction bits is a
+// multiple of 2^(e - 1 - p), and e >= that of mnz
+AVERIS_HD inline int value_grid_exp(float mnz, int p) {
+  int e;
+  (void)__builtin_frexp((double)mnz, &e);
+  return e - 1 - p;
+}
+
+// whether n values of magnitude <= amax on the grid 2^gexp sum exactly in a
+// signed 64-bit integer (a margin of one bit for the rounding of n * amax)
+AVERIS_HD inline bool grid_sum_fits(double n, double amax, int gexp) {
+  return n * amax <= __builtin_ldexp(1.0, 61 + gexp);
+}
+
+// v / 2^gexp as an integer (v an exact multiple of 2^gexp, |v / 2^gexp| < 2^62)
+AVERIS_HD inline int64_t grid_int64(double v, int gexp) {
+  const double t = __builtin_ldexp(v, -gexp);                 // an integer-valued double
+  const double hi = __builtin_floor(t * 0x1p-32);             // exact
+  const double lo = t - hi * 0x1p32;                          // exact, in [0, 2^32)
+  return (int64_t)((uint64_t)(int64_t)(int32_t)hi << 32) + (int64_t)(uint32_t)lo;
+}
+
+// n 2^gexp rounded once to the nearest double, ties to even (the scale by
+// 2^gexp is exact: the results here are far from the fp64 range's ends)
+AVERIS_HD inline double grid_int64_to_double(int64_t n, int gexp) {
+  const double hi = (double)(int32_t)(n >> 32) * 0x1p32;      // exact
+  const double lo = (double)(uint32_t)(uint64_t)n;            // exact
+  return __builtin_ldexp(hi + lo, gexp);                      // one rounding
+}
+
 }  // namespace averis

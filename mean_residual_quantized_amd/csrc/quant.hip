@@ -281,10 +281,13 @@ __global__ __launch_bounds__(256) void k_stats(const T* __restrict__ a, int64_t 
 // wave-uniform control flow).  The chunks' fp64 partial sums that are exact
 // by their own certificate (a chunk spans far fewer rows and usually a far
 // narrower range of values) are added exactly, the rows of the other chunks
-// one by one, into a 320-bit integer in units of 2^-149 (exact_sum.hpp),
-// which is rounded once to the nearest double.  Chunk c of the segment goes
-// to lane c mod 64; the lanes' accumulators are then added by a butterfly of
-// shuffles (exact, so the order is free) and every lane gets the result.
+// one by one, into a signed 64-bit integer in units of the grid every value
+// of the column lies on (2^gexp, from its smallest nonzero magnitude) when the
+// column's sum stays below 2^62 of them, else into a 320-bit integer in units
+// of 2^-149 (exact_sum.hpp); either is rounded once to the nearest double.
+// Chunk c of the segment goes to lane c mod 64; the lanes' accumulators are
+// then added by a butterfly of shuffles (exact, so the order is free) and
+// every lane gets the result.
 // Kept out of line: the finalize passes call it only for a column that fails
 // the certificate.
 // ---------------------------------------------------------------------------
@@ -309,6 +312,48 @@ __device__ __noinline__ double exact_column_sum(const void* a, bool bf16, int64_
                                                 const float* __restrict__ pmin,
                                                 const float* __restrict__ pmnz) {
   const int lane = threadIdx.x & 63;
+  // The column's largest and smallest nonzero magnitude over its chunks: when
+  // its values, all on the grid 2^gexp of the smallest, sum to below 2^62
+  // grid units, a signed 64-bit integer holds the exact sum (in any order)
+  // and one rounding gives the correctly rounded double; else the 320-bit sum.
+  {
+    float am = 0.0f, mz = __builtin_inff();
+    for (int64_t c = c0 + lane; c < c1; c += 64) {
+      const int64_t o = c * cols + j;
+      am = __builtin_fmaxf(am, __builtin_fmaxf(__builtin_fabsf(pmax[o]), __builtin_fabsf(pmin[o])));
+      mz = __builtin_fminf(mz, pmnz[o]);
+    }
+    for (int d = 32; d > 0; d >>= 1) {
+      am = __builtin_fmaxf(am, __shfl_xor(am, d, 64));
+      mz = __builtin_fminf(mz, __shfl_xor(mz, d, 64));
+    }
+    if (!(mz < __builtin_inff())) return 0.0;   // no nonzero value
+    const int gexp = value_grid_exp(mz, bf16 ? 7 : 23);
+    if (grid_sum_fits((double)(seg_r1 - seg_r0), (double)am, gexp)) {   // uniform
+      int64_t n = 0;
+      for (int64_t c = c0 + lane; c < c1; c += 64) {
+        const int64_t r0 = seg_r0 + (c - c0) * ch;
+        const int64_t r1 = r0 + ch < seg_r1 ? r0 + ch : seg_r1;
+        const int64_t o = c * cols + j;
+        const double cam = __builtin_fmax(__builtin_fabs((double)pmax[o]), __builtin_fabs((double)pmin[o]));
+        if (sum_certified((double)(r1 - r0), cam, pmnz[o], bf16)) {
+          n += grid_int64(psum[o], gexp);   // an exact sum of values on the grid
+        } else {
+          for (int64_t r = r0; r < r1; ++r) {
+            const float v = bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(a)[r * lda + j] << 16)
+                                 : static_cast<const float*>(a)[r * lda + j];
+            n += grid_int64((double)v, gexp);
+          }
+        }
+      }
+      for (int d = 32; d > 0; d >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)(uint64_t)n, d, 64);
+        const uint32_t hi = __shfl_xor((uint32_t)((uint64_t)n >> 32), d, 64);
+        n += (int64_t)(((uint64_t)hi << 32) | lo);
+      }
+      return grid_int64_to_double(n, gexp);
+    }
+  }
   uint32_t acc[kWideWords];
 #pragma unroll
   for (int i = 0; i < kWideWords; ++i) acc[i] = 0u;

@@ -149,6 +149,14 @@ def adversarial_columns(rows, cols, seed):
     large = rng.integers(-100, 100, rows) * np.float32(2.0 ** 40)
     x[:, 6] = np.where(i < 128, small, large).astype(np.float32)
     x[:, 7] = np.where((i // 128) % 2 == 0, large, small).astype(np.float32)
+    # not certified, but every value on one grid narrow enough for an exact
+    # 64-bit sum in its units (column 8 as bf16, column 9 as fp32): the
+    # fallback's integer path, with a total that needs rounding to a double
+    k = rng.integers(1, 65, rows).astype(np.float32)
+    m = rng.integers(129, 256, rows).astype(np.float32) * np.where(i % 2, 1, -1)
+    x[:, 8] = np.where(i % 7 == 0, k * np.float32(2.0 ** 12), m * np.float32(2.0 ** -29))
+    x[:, 9] = np.where(i % 7 == 0, k * np.float32(2.0 ** 10),
+                       ((0.5 + rng.random(rows) / 2) * 2.0 ** -8 * np.where(i % 2, 1, -1)).astype(np.float32))
     return x
 
 
